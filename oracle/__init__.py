@@ -1,0 +1,158 @@
+"""CPU oracle for the sum-pooled Tensor-Train embedding gather.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product (the HIP library and its
+Python binding) never imports, links or calls anything here, and nothing here
+imports the product: the two share no code. Both sides only share the seeded
+input generators in `workloads`, which hold none of the method's arithmetic.
+
+Contents:
+  tt_oracle.c  plain C, fp64: per-lookup TT chain, sum pooling, core gradients
+  planner.py   NumPy: index split, stable prefix-key sort, groups, chunks
+  this file    ctypes loader and NumPy-facing wrappers; SGD by its definition
+
+Parity status of each function (pins live in tests/, marked "not gpu"):
+  forward      pinned: brute-force table materialisation in another
+               contraction order, rank-1 Kronecker closed form, gauge
+               invariance, multilinearity and pooling additivity
+  backward     pinned: exact adjoint identity against the forward oracle,
+               brute-force chain rule on tiny shapes, rank-1 closed form
+  sgd          pinned by its arithmetic definition on hand-made values
+  planner      pinned: exact digit identity over every row of a table,
+               pure-Python brute-force stable sort on small inputs, and the
+               partition invariants of groups and chunks
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import planner  # noqa: F401  (re-exported)
+from .planner import PlanError, plan, plan_problem  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tt_oracle.c")
+_LIB = os.path.join(_HERE, "libtt_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+OK, BAD_ARG, BAD_INDEX, BAD_OFFSETS, NO_MEMORY = 0, -1, -2, -3, -4
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile tt_oracle.c with gcc (-O2, OpenMP) into oracle/libtt_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                        "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            i32, i64 = ctypes.c_int32, ctypes.c_int64
+            lib.tto_forward.argtypes = [i32, P, P, P, P, P, P, P, P, P, P, i64, i64, P, i64, P]
+            lib.tto_forward.restype = ctypes.c_int
+            lib.tto_backward.argtypes = [i32, P, P, P, P, P, P, P, P, P, P, i64, i64, P, P,
+                                         P, i64, P, i64, P, i64]
+            lib.tto_backward.restype = ctypes.c_int
+            lib.tto_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
+    return int(_load().tto_num_threads())
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _tables(tables) -> Tuple[np.ndarray, ...]:
+    N = np.ascontiguousarray([t.num_rows for t in tables], dtype=np.int64)
+    m = np.ascontiguousarray([t.m for t in tables], dtype=np.int64).reshape(-1)
+    n = np.ascontiguousarray([t.n for t in tables], dtype=np.int64).reshape(-1)
+    R = np.ascontiguousarray([t.rank for t in tables], dtype=np.int64)
+    return N, m, n, R
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise OracleError(f"{what}: oracle returned {rc}")
+
+
+def forward(tables: Sequence, g1, g2, g3, goff, indices, offsets, B: int,
+            bags: Optional[np.ndarray] = None) -> np.ndarray:
+    """Pooled outputs (float64) of the listed bags (all bags if None)."""
+    lib = _load()
+    N, m, n, R = _tables(tables)
+    goff = np.ascontiguousarray(goff, dtype=np.int64).reshape(-1)
+    g1, g2, g3 = (np.ascontiguousarray(x, dtype=np.float32) for x in (g1, g2, g3))
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    D = tables[0].n[0] * tables[0].n[1] * tables[0].n[2]
+    if bags is not None:
+        bags = np.ascontiguousarray(bags, dtype=np.int64)
+        nb = bags.size
+    else:
+        nb = len(tables) * B
+    out = np.empty((nb, D), dtype=np.float64)
+    rc = lib.tto_forward(len(tables), _ptr(N), _ptr(m), _ptr(n), _ptr(R), _ptr(goff),
+                         _ptr(g1), _ptr(g2), _ptr(g3), _ptr(idx), _ptr(off), idx.size, B,
+                         _ptr(bags), nb, _ptr(out))
+    _check(rc, "forward")
+    return out
+
+
+def backward(tables: Sequence, g1, g2, g3, goff, indices, offsets, B: int, grad_out,
+             mask: Optional[np.ndarray] = None):
+    """(dG1, dG2, dG3) in float64, same packing as the cores; only lookups
+    with mask[l] != 0 contribute (all if mask is None)."""
+    lib = _load()
+    N, m, n, R = _tables(tables)
+    goff = np.ascontiguousarray(goff, dtype=np.int64).reshape(-1)
+    g1, g2, g3 = (np.ascontiguousarray(x, dtype=np.float32) for x in (g1, g2, g3))
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    go = np.ascontiguousarray(grad_out, dtype=np.float32)
+    mk = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    d1 = np.empty(g1.size, np.float64)
+    d2 = np.empty(g2.size, np.float64)
+    d3 = np.empty(g3.size, np.float64)
+    rc = lib.tto_backward(len(tables), _ptr(N), _ptr(m), _ptr(n), _ptr(R), _ptr(goff),
+                          _ptr(g1), _ptr(g2), _ptr(g3), _ptr(idx), _ptr(off), idx.size, B,
+                          _ptr(go), _ptr(mk), _ptr(d1), d1.size, _ptr(d2), d2.size,
+                          _ptr(d3), d3.size)
+    _check(rc, "backward")
+    return d1, d2, d3
+
+
+def sgd(g: np.ndarray, dg: np.ndarray, lr: float) -> np.ndarray:
+    """Plain SGD step G <- G - lr * dG, in float64."""
+    return np.asarray(g, dtype=np.float64) - float(lr) * np.asarray(dg, dtype=np.float64)
+
+
+def forward_problem(p, bags=None) -> np.ndarray:
+    return forward(p.tables, p.g1, p.g2, p.g3, p.goff, p.indices, p.offsets, p.batch, bags)
+
+
+def backward_problem(p, mask=None):
+    return backward(p.tables, p.g1, p.g2, p.g3, p.goff, p.indices, p.offsets, p.batch,
+                    p.grad_out, mask)
