@@ -1,0 +1,174 @@
+/*
+ * tt_emb.h — C ABI of the MI355X (gfx950) TT-EmbeddingBag library, libtt_emb.so.
+ *
+ * The operation: an embedding table of N rows x D columns is stored as three
+ * Tensor-Train cores, and a batch of lookups is answered by contracting, for
+ * every requested row, the chain of core slices picked by the row's digits,
+ * then summing the rows of each bag. The pages describe the lookup as a chain
+ * of tensor contractions across TT cores (FlowTT summary card, problem
+ * statement), the table as replaced by a sequence of matrix products whose
+ * embedding vectors become a TT-core multiplication (the TT-Rec news article,
+ * method paragraph), the pooled kernel by its name, TT-EmbeddingBag (TT-Rec
+ * abstract), and the fast path as prefix-based grouping of lookups that share
+ * high-order core indices, a fused chain that keeps the shared partial product
+ * on chip, and persistent threads with chunk-based work stealing (FlowTT
+ * abstract; summary card, key innovations). Training through the lookup is
+ * part of both pages' evaluations (FlowTT abstract: training latency).
+ *
+ * Conventions (the pages give no formulas; these are this library's):
+ *   row index       idx = (i1*m2 + i2)*m3 + i3, 0 <= idx < N <= m1*m2*m3
+ *   cores (fp32)    G1[m1][n1][R], G2[m2][R][n2][R], G3[m3][R][n3], row-major;
+ *                   the slices are 1 x n1 x R, R x n2 x R and R x n3 x 1 with
+ *                   the unit boundary ranks dropped
+ *   row vector      E[(j1*n2 + j2)*n3 + j3] =
+ *                       sum_{r1,r2} G1[i1][j1][r1] G2[i2][r1][j2][r2] G3[i3][r2][j3]
+ *   bags            CSR: T tables x B bags each, bag q = t*B + b holds lookups
+ *                   offsets[q] .. offsets[q+1]-1; out[q] = sum of its rows
+ *                   (sum pooling; an empty bag gives a zero row)
+ *   gradients       of the loss <grad_out, out> with respect to each core
+ *
+ * Memory: every device buffer is owned by the caller (cores, indices,
+ * offsets, outputs, gradients and the planning workspace). The library
+ * allocates no device memory; the plan handle is a small host object.
+ * Several tables are served by one call: their cores are packed one after
+ * another in three flat buffers (one per core kind), located by g_offset.
+ *
+ * Streams: every call that takes `stream` enqueues its kernels on that HIP
+ * stream (a hipStream_t passed as void*; NULL is the null stream) and returns
+ * without waiting, except tt_emb_get_error and tt_emb_plan_counts, which
+ * synchronise that stream. Calls on one plan must be ordered on one stream.
+ *
+ * Errors: every call returns a tt_status. Arguments that can be checked on
+ * the host (null pointers, non-positive or inconsistent dims, sizes beyond
+ * int32, a workspace that is too small, unsupported shapes) are rejected
+ * before any launch. Data errors found on the device (an index outside
+ * [0, N_t), offsets that are not non-decreasing from 0 to L) set a flag in
+ * the workspace; the results of that plan are then unspecified, and
+ * tt_emb_get_error reports the flag.
+ */
+#ifndef TT_EMB_H
+#define TT_EMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TT_OK = 0,
+    TT_ERR_INVALID_ARG = -1,  /* null pointer, bad dims, inconsistent sizes          */
+    TT_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits (see below)   */
+    TT_ERR_WORKSPACE = -3,    /* workspace smaller than tt_emb_workspace_bytes      */
+    TT_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed          */
+    TT_ERR_DEVICE_FLAG = -5   /* returned by tt_emb_get_error when the flag is set   */
+} tt_status;
+
+/* Device error flag bits (tt_emb_get_error). */
+#define TT_FLAG_BAD_INDEX 1   /* some index outside [0, N_t)                         */
+#define TT_FLAG_BAD_OFFSETS 2 /* offsets[0] != 0, offsets[T*B] != L or a decrease   */
+
+/* Limits of this build: N_t < 2^31, L < 2^31, T*B < 2^31, sum over tables of
+ * m1*m2 < 2^30, R <= 64, n1*n2 <= 64, n3 <= 16, D <= 1024, T <= 4096. */
+
+/* One table (host memory). All tables of a call must have the same D. */
+typedef struct {
+    int64_t num_rows;    /* N: valid indices are [0, N)                              */
+    int32_t m[3];        /* row radices (m1, m2, m3), m1*m2*m3 >= N                  */
+    int32_t n[3];        /* dim factors (n1, n2, n3), D = n1*n2*n3                   */
+    int32_t rank;        /* R, the two internal TT ranks                              */
+    int32_t reserved;    /* must be 0                                                 */
+    int64_t g_offset[3]; /* element offset of this table's G1, G2, G3 in the packed  */
+                         /* core buffers (and in the matching gradient buffers)       */
+} tt_emb_table;
+
+typedef struct tt_emb_plan_s* tt_emb_plan_t;  /* opaque, host-side, library-owned */
+
+/* Bytes of device workspace tt_emb_plan needs for these tables, L lookups,
+ * B bags per table and chunk size `chunk` (>= 1). Returns 0 when the
+ * arguments are invalid or unsupported. Pure host computation. */
+size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L, int64_t B,
+                              int32_t chunk);
+
+/* Planning: index split, prefix grouping and chunking, all on the device.
+ *   tables    host array of T descriptors (copied; may be freed after return)
+ *   indices   device int64[L]
+ *   offsets   device int64[T*B + 1]
+ *   chunk     maximum lookups per chunk (work unit); groups larger than this
+ *             are cut into several chunks
+ *   workspace device buffer of at least tt_emb_workspace_bytes(...) bytes,
+ *             256-byte aligned; it holds the plan's tables and stays in use
+ *             until the plan is destroyed
+ * On success *plan_out receives a new handle. The plan keeps pointers to
+ * `workspace` only (indices and offsets are read by the enqueued kernels and
+ * may be reused once they have run).
+ *
+ * Planner output, all int32 in the workspace (tt_emb_plan_view):
+ *   key[l]      = base_t + i2*m1 + i1 (base_t = sum of m1*m2 over earlier tables)
+ *   i3[l], bag_of[l]
+ *   perm        stable sort of lookups by key (equal keys keep increasing l)
+ *   groups      maximal runs of equal key in sorted order: group_key[g],
+ *               group_start[g] (and group_start[U] = L)
+ *   chunks      each group cut into consecutive pieces of exactly `chunk`
+ *               lookups, the last possibly shorter; no chunk spans groups  */
+tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                      const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      tt_emb_plan_t* plan_out);
+
+/* Forward: out (device float[T*B][D]) is fully overwritten with the pooled
+ * rows. g1/g2/g3 are the packed device cores. */
+tt_status tt_emb_forward(tt_emb_plan_t plan, const float* g1, const float* g2,
+                         const float* g3, float* out, void* stream);
+
+/* Backward: dg1/dg2/dg3 (device, same packing and sizes as the cores) are
+ * fully overwritten with the gradients of <grad_out, out>; slices that no
+ * lookup touches are zero. grad_out is device float[T*B][D]. */
+tt_status tt_emb_backward(tt_emb_plan_t plan, const float* g1, const float* g2,
+                          const float* g3, const float* grad_out, float* dg1, float* dg2,
+                          float* dg3, void* stream);
+
+/* SGD step on every core element: G <- G - lr * dG (device buffers). */
+tt_status tt_emb_sgd(tt_emb_plan_t plan, float* g1, float* g2, float* g3, const float* dg1,
+                     const float* dg2, const float* dg3, float lr, void* stream);
+
+/* Synchronises `stream` and reads the device error flag of the plan into
+ * *flag_out (0, or TT_FLAG_* bits). Returns TT_OK when the flag is clear and
+ * TT_ERR_DEVICE_FLAG when it is set. */
+tt_status tt_emb_get_error(tt_emb_plan_t plan, int32_t* flag_out, void* stream);
+
+/* Device pointers to the planner's tables inside the workspace (no copy). */
+typedef struct {
+    const int32_t* key;          /* [L] original lookup order                  */
+    const int32_t* i3;           /* [L]                                        */
+    const int32_t* bag_of;       /* [L]                                        */
+    const int32_t* perm;         /* [L] sorted position -> lookup              */
+    const int32_t* sorted_i3;    /* [L] i3[perm[s]]                            */
+    const int32_t* sorted_bag;   /* [L] bag_of[perm[s]]                        */
+    const int32_t* group_key;    /* [num_groups]                               */
+    const int32_t* group_start;  /* [num_groups + 1]                           */
+    const int32_t* chunk_group;  /* [num_chunks]                               */
+    const int32_t* chunk_begin;  /* [num_chunks] sorted positions              */
+    const int32_t* chunk_end;    /* [num_chunks]                               */
+    int64_t max_groups;          /* capacity of the group arrays               */
+    int64_t max_chunks;          /* capacity of the chunk arrays               */
+} tt_emb_plan_view;
+
+tt_status tt_emb_plan_get_view(tt_emb_plan_t plan, tt_emb_plan_view* view);
+
+/* Synchronises `stream` and reads the number of groups and chunks. */
+tt_status tt_emb_plan_counts(tt_emb_plan_t plan, int64_t* num_groups, int64_t* num_chunks,
+                             void* stream);
+
+/* Frees the host handle (the workspace stays the caller's). NULL is a no-op. */
+tt_status tt_emb_plan_destroy(tt_emb_plan_t plan);
+
+/* Human-readable name of a status code (static storage). */
+const char* tt_emb_status_string(tt_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_EMB_H */

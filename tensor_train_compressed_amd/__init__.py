@@ -1,0 +1,255 @@
+"""Python binding of libtt_emb.so, the MI355X TT-EmbeddingBag library.
+
+Argument marshalling only: every step of the lookup (planning, forward,
+backward, SGD) runs in the library's HIP kernels. PyTorch supplies device
+memory and the stream; tensors are passed by data_ptr(). The function names
+are those of the C ABI in include/tt_emb.h, whose comments state argument
+meaning, layouts, ownership and errors.
+
+If libtt_emb.so has not been built, importing the functions works but the
+first call raises TTEmbLibraryMissing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+__all__ = [
+    "TTEmbError", "TTEmbLibraryMissing", "TT_OK", "TT_FLAG_BAD_INDEX", "TT_FLAG_BAD_OFFSETS",
+    "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
+    "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd", "tt_emb_get_error",
+    "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy", "Plan", "EXPORTS",
+]
+
+TT_OK = 0
+TT_ERR_DEVICE_FLAG = -5
+TT_FLAG_BAD_INDEX = 1
+TT_FLAG_BAD_OFFSETS = 2
+
+# Every symbol include/tt_emb.h declares.
+EXPORTS = (
+    "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd",
+    "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
+    "tt_emb_status_string",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lock = threading.Lock()
+_lib = None
+
+
+class TTEmbError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} ({status})")
+
+
+class TTEmbLibraryMissing(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libtt_emb.so")
+
+
+class _Table(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int64), ("m", ctypes.c_int32 * 3),
+                ("n", ctypes.c_int32 * 3), ("rank", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("g_offset", ctypes.c_int64 * 3)]
+
+
+class _View(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "key", "i3", "bag_of", "perm", "sorted_i3", "sorted_bag", "group_key", "group_start",
+        "chunk_group", "chunk_begin", "chunk_end")] + [
+        ("max_groups", ctypes.c_int64), ("max_chunks", ctypes.c_int64)]
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libtt_emb.so from the package directory (no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise TTEmbLibraryMissing(
+                f"{path} is not built; run `python -m tensor_train_compressed_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.tt_emb_workspace_bytes.argtypes = [P, i32, i64, i64, i32]
+        lib.tt_emb_workspace_bytes.restype = ctypes.c_size_t
+        lib.tt_emb_plan.argtypes = [P, i32, P, P, i64, i64, i32, P, ctypes.c_size_t, P,
+                                    ctypes.POINTER(P)]
+        lib.tt_emb_forward.argtypes = [P, P, P, P, P, P]
+        lib.tt_emb_backward.argtypes = [P, P, P, P, P, P, P, P, P]
+        lib.tt_emb_sgd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P]
+        lib.tt_emb_get_error.argtypes = [P, ctypes.POINTER(i32), P]
+        lib.tt_emb_plan_get_view.argtypes = [P, ctypes.POINTER(_View)]
+        lib.tt_emb_plan_counts.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64), P]
+        lib.tt_emb_plan_destroy.argtypes = [P]
+        lib.tt_emb_status_string.argtypes = [ctypes.c_int]
+        lib.tt_emb_status_string.restype = ctypes.c_char_p
+        for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd",
+                     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts",
+                     "tt_emb_plan_destroy"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().tt_emb_status_string(int(status)).decode()
+    except Exception:
+        return "status"
+
+
+def _check(status: int, what: str):
+    if status != TT_OK:
+        raise TTEmbError(status, what)
+
+
+def make_tables(tables: Sequence, g_offsets) -> ctypes.Array:
+    """C array of tt_emb_table from objects with num_rows, m, n, rank and a
+    [T][3] sequence of core element offsets."""
+    arr = (_Table * len(tables))()
+    for i, t in enumerate(tables):
+        arr[i].num_rows = int(t.num_rows)
+        for k in range(3):
+            arr[i].m[k] = int(t.m[k])
+            arr[i].n[k] = int(t.n[k])
+            arr[i].g_offset[k] = int(g_offsets[i][k])
+        arr[i].rank = int(t.rank)
+        arr[i].reserved = 0
+    return arr
+
+
+def _dev_ptr(t, dtype_name: str, what: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if str(t.dtype) != f"torch.{dtype_name}":
+        raise ValueError(f"{what} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """Owns a tt_emb_plan_t; keeps the workspace tensor alive alongside it."""
+
+    def __init__(self, handle: int, workspace, L: int, TB: int, D: int):
+        self.handle = handle
+        self.workspace = workspace
+        self.L, self.TB, self.D = L, TB, D
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                load_library().tt_emb_plan_destroy(ctypes.c_void_p(self.handle))
+            except Exception:
+                pass
+            self.handle = None
+
+
+def tt_emb_workspace_bytes(tables_c, L: int, B: int, chunk: int) -> int:
+    return int(load_library().tt_emb_workspace_bytes(tables_c, len(tables_c), L, B, chunk))
+
+
+def tt_emb_plan(tables_c, indices, offsets, B: int, chunk: int, workspace=None,
+                stream=None) -> Plan:
+    """Plan a batch. `tables_c` from make_tables; indices int64[L] and offsets
+    int64[T*B+1] device tensors; workspace a uint8 device tensor (allocated
+    here with torch if None)."""
+    lib = load_library()
+    L = int(indices.numel())
+    need = tt_emb_workspace_bytes(tables_c, L, B, chunk)
+    if need == 0:
+        raise TTEmbError(-1, "tt_emb_workspace_bytes")
+    if workspace is None:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=indices.device)
+    h = ctypes.c_void_p()
+    st = lib.tt_emb_plan(tables_c, len(tables_c), _dev_ptr(indices, "int64", "indices"),
+                         _dev_ptr(offsets, "int64", "offsets"), L, B, chunk,
+                         _dev_ptr(workspace, "uint8", "workspace"), workspace.numel(),
+                         _stream(stream), ctypes.byref(h))
+    _check(st, "tt_emb_plan")
+    D = int(tables_c[0].n[0] * tables_c[0].n[1] * tables_c[0].n[2])
+    return Plan(h.value, workspace, L, len(tables_c) * B, D)
+
+
+def tt_emb_forward(plan: Plan, g1, g2, g3, out, stream=None):
+    _check(load_library().tt_emb_forward(
+        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
+        _dev_ptr(g3, "float32", "g3"), _dev_ptr(out, "float32", "out"), _stream(stream)),
+        "tt_emb_forward")
+
+
+def tt_emb_backward(plan: Plan, g1, g2, g3, grad_out, dg1, dg2, dg3, stream=None):
+    _check(load_library().tt_emb_backward(
+        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
+        _dev_ptr(g3, "float32", "g3"), _dev_ptr(grad_out, "float32", "grad_out"),
+        _dev_ptr(dg1, "float32", "dg1"), _dev_ptr(dg2, "float32", "dg2"),
+        _dev_ptr(dg3, "float32", "dg3"), _stream(stream)), "tt_emb_backward")
+
+
+def tt_emb_sgd(plan: Plan, g1, g2, g3, dg1, dg2, dg3, lr: float, stream=None):
+    _check(load_library().tt_emb_sgd(
+        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
+        _dev_ptr(g3, "float32", "g3"), _dev_ptr(dg1, "float32", "dg1"),
+        _dev_ptr(dg2, "float32", "dg2"), _dev_ptr(dg3, "float32", "dg3"), float(lr),
+        _stream(stream)), "tt_emb_sgd")
+
+
+def tt_emb_get_error(plan: Plan, stream=None) -> int:
+    """Device error flag (0 or TT_FLAG_* bits); synchronises the stream."""
+    f = ctypes.c_int32(0)
+    st = load_library().tt_emb_get_error(plan.handle, ctypes.byref(f), _stream(stream))
+    if st not in (TT_OK, TT_ERR_DEVICE_FLAG):
+        _check(st, "tt_emb_get_error")
+    return int(f.value)
+
+
+def tt_emb_plan_get_view(plan: Plan) -> dict:
+    """Device addresses of the planner's int32 tables plus their capacities."""
+    v = _View()
+    _check(load_library().tt_emb_plan_get_view(plan.handle, ctypes.byref(v)), "tt_emb_plan_get_view")
+    return {name: getattr(v, name) for name, _ in _View._fields_}
+
+
+def tt_emb_plan_counts(plan: Plan, stream=None):
+    """(num_groups, num_chunks); synchronises the stream."""
+    g, c = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(load_library().tt_emb_plan_counts(plan.handle, ctypes.byref(g), ctypes.byref(c),
+                                             _stream(stream)), "tt_emb_plan_counts")
+    return int(g.value), int(c.value)
+
+
+def tt_emb_plan_destroy(plan: Plan):
+    if plan.handle:
+        _check(load_library().tt_emb_plan_destroy(plan.handle), "tt_emb_plan_destroy")
+        plan.handle = None
+
+
+def plan_table(plan: Plan, name: str, n: int):
+    """int32 tensor view (no copy) of one planner table inside the plan's
+    workspace tensor; `name` is a tt_emb_plan_view field, `n` its length."""
+    addr = tt_emb_plan_get_view(plan)[name]
+    off = addr - plan.workspace.data_ptr()
+    if off < 0 or off + 4 * n > plan.workspace.numel():
+        raise ValueError(f"{name}[{n}] is outside the workspace")
+    return plan.workspace[off:off + 4 * n].view(dtype=__import__("torch").int32)

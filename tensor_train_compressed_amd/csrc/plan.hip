@@ -1,0 +1,656 @@
+// Planning pass of the TT-EmbeddingBag library: index split, prefix grouping
+// and chunking, all on the GPU.
+//
+// The pages' task-formation step groups lookups that share high-order TT core
+// indices so that the shared part of the contraction chain is done once per
+// group, and cuts skewed groups into chunks that persistent threads take and
+// steal ("FlowTT: Exploiting Computation Flow Reuse in Irregular Tensor-Train
+// Embedding": summary card, key innovations; abstract). The pages fix which
+// lookups share a group; the order and chunk shape used here are this
+// library's (see include/tt_emb.h): groups are ordered by key
+// base_t + i2*m1 + i1, so that groups that read the same G2 slice are
+// adjacent, and lookups keep their input order inside a group.
+//
+// Kernels, in stream order:
+//   k_write_desc      table descriptors into the workspace
+//   k_split           offsets check, bag search, digit split, prefix key
+//   k_radix_hist      \  stable LSD radix sort of the keys, 8 bits per pass:
+//   scan (1 or 3)      | per-tile digit counts, one exclusive scan over
+//   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
+//   k_gather          sorted i3 / bag, first and last position of each key
+//   k_key_flags       per key: present flag and chunk count
+//   scan              group id and first chunk of every present key
+//   k_groups          group tables, counts into the control words
+//   k_chunks          chunk table (one thread per chunk, search over groups)
+#include "tt_internal.h"
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+namespace tt {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K) {
+    Layout y{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
+    y.K = K;
+    y.n_tiles = (L + kSortTile - 1) / kSortTile;
+    y.Gmax = std::min<int64_t>(L, K);
+    y.Cmax = L == 0 ? 0 : std::min<int64_t>(L, y.Gmax + (L + chunk - 1) / chunk);
+    int bits = 0;
+    while ((int64_t(1) << bits) < K) ++bits;
+    y.passes = std::max(1, (bits + kRadixBits - 1) / kRadixBits);
+    (void)B;
+    y.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
+    y.desc = take(sizeof(TabDev) * (size_t)T);
+    const size_t l4 = sizeof(int32_t) * (size_t)L;
+    y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
+    y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
+    y.skey = take(l4);
+    // The radix passes ping-pong between (skey, perm) and a temporary pair that
+    // reuses sorted_i3 / sorted_bag, which are written only after the sort.
+    y.sort_k0 = y.sorted_i3; y.sort_v0 = y.sorted_bag;
+    y.sort_k1 = y.skey; y.sort_v1 = y.perm;
+    const int64_t nhist = (int64_t)kRadixBins * y.n_tiles;
+    y.hist = take(sizeof(uint32_t) * (size_t)nhist);
+    y.key_start = take(sizeof(int32_t) * (size_t)K);
+    y.key_end = take(sizeof(int32_t) * (size_t)K);
+    y.key_scan = take(sizeof(uint64_t) * (size_t)K);
+    y.group_key = take(sizeof(int32_t) * (size_t)y.Gmax);
+    y.group_start = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
+    y.group_cbase = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
+    y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
+    y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
+    y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
+    const int64_t nscan = std::max<int64_t>(nhist, K);
+    y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
+    y.total = off;
+    return y;
+}
+
+// ---------------------------------------------------------------------------
+// small utilities
+
+__global__ void k_fill32(uint32_t* p, uint32_t v, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) p[i] = v;
+}
+
+tt_status fill32(void* p, uint32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return TT_OK;
+    unsigned g = std::min<unsigned>(grid_for(n, 256), 4096u);
+    hipLaunchKernelGGL(k_fill32, dim3(g), dim3(256), 0, s, (uint32_t*)p, v, n);
+    TT_LAUNCH_CHECK();
+    return TT_OK;
+}
+
+struct DescBatch {
+    int32_t first, count;
+    TabDev d[16];
+};
+
+__global__ void k_write_desc(TabDev* out, DescBatch b) {
+    int i = threadIdx.x;
+    if (i < b.count) out[b.first + i] = b.d[i];
+}
+
+// 64-lane match: mask of valid lanes whose 8-bit digit equals this lane's.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t valid) {
+    uint64_t peers = valid;
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+        const uint64_t bal = __ballot((d >> b) & 1u);
+        peers &= ((d >> b) & 1u) ? bal : ~bal;
+    }
+    return peers;
+}
+
+__device__ __forceinline__ uint32_t popc_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// ---------------------------------------------------------------------------
+// split
+
+__global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
+                                               const int64_t* __restrict__ off, int64_t L,
+                                               int64_t TB, int64_t B,
+                                               const TabDev* __restrict__ desc,
+                                               int32_t* __restrict__ key, int32_t* __restrict__ i3o,
+                                               int32_t* __restrict__ bag_of, int32_t* ctrl) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i <= TB) {
+        const int64_t a = off[i];
+        bool bad = (i == 0 && a != 0) || (i == TB && a != L) || (i < TB && off[i + 1] < a);
+        if (bad) atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_OFFSETS);
+    }
+    if (i >= L) return;
+    // last bag q in [0, TB) with off[q] <= i; stays in range for any offsets
+    int64_t lo = 0, hi = TB;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (off[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int64_t q = lo;
+    const TabDev d = desc[q / B];
+    int64_t x = idx[i];
+    if (x < 0 || x >= d.N) {
+        atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_INDEX);
+        x = 0;
+    }
+    const uint32_t xi = (uint32_t)x;
+    const uint32_t r3 = xi % (uint32_t)d.m3;
+    const uint32_t p = xi / (uint32_t)d.m3;
+    const uint32_t r2 = p % (uint32_t)d.m2;
+    const uint32_t r1 = p / (uint32_t)d.m2;
+    key[i] = d.key_base + (int32_t)(r2 * (uint32_t)d.m1 + r1);
+    i3o[i] = (int32_t)r3;
+    bag_of[i] = (int32_t)q;
+}
+
+// ---------------------------------------------------------------------------
+// stable LSD radix sort
+
+__global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t* __restrict__ keys,
+                                                             int64_t L, int shift, int64_t n_tiles,
+                                                             uint32_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[kRadixBins];
+    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t tile = blockIdx.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / 4);
+#pragma unroll 4
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t e = base + slot * 64 + lane;
+        const bool valid = e < L;
+        const uint32_t d = valid ? ((uint32_t)keys[e] >> shift) & (kRadixBins - 1) : 0u;
+        const uint64_t peers = match_digit(d, __ballot(valid));
+        if (valid && popc_below(peers) == 0) atomicAdd(&cnt[d], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) hist[(int64_t)i * n_tiles + tile] = cnt[i];
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
+    const int32_t* __restrict__ kin, const int32_t* __restrict__ vin, int64_t L, int shift,
+    int64_t n_tiles, const uint32_t* __restrict__ hist_scan, int32_t* __restrict__ kout,
+    int32_t* __restrict__ vout) {
+    __shared__ uint32_t cnt[4][kRadixBins];
+    __shared__ uint32_t gbase[kRadixBins];
+    const int64_t tile = blockIdx.x;
+    for (int i = threadIdx.x; i < 4 * kRadixBins; i += kSortThreads) (&cnt[0][0])[i] = 0;
+    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) gbase[i] = hist_scan[(int64_t)i * n_tiles + tile];
+    __syncthreads();
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / 4);
+    int32_t kk[kSortItems], vv[kSortItems];
+    uint32_t rk[kSortItems];
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t e = base + slot * 64 + lane;
+        const bool valid = e < L;
+        kk[slot] = valid ? kin[e] : 0;
+        vv[slot] = valid ? (vin ? vin[e] : (int32_t)e) : 0;
+        const uint32_t d = ((uint32_t)kk[slot] >> shift) & (kRadixBins - 1);
+        const uint64_t peers = match_digit(d, __ballot(valid));
+        const uint32_t below = popc_below(peers);
+        uint32_t pre = 0;
+        if (valid) pre = cnt[w][d];
+        if (valid && below == 0) cnt[w][d] = pre + (uint32_t)__popcll(peers);
+        rk[slot] = pre + below;
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < kRadixBins; d += kSortThreads) {
+        uint32_t run = 0;
+        for (int ww = 0; ww < 4; ++ww) {
+            const uint32_t c = cnt[ww][d];
+            cnt[ww][d] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t e = base + slot * 64 + lane;
+        if (e < L) {
+            const uint32_t d = ((uint32_t)kk[slot] >> shift) & (kRadixBins - 1);
+            const uint32_t pos = gbase[d] + cnt[w][d] + rk[slot];
+            kout[pos] = kk[slot];
+            vout[pos] = vv[slot];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// device-wide exclusive scan (single block for short arrays, else 3 kernels)
+
+template <class V>
+__device__ V block_exclusive_scan(V x, V* wsum, V* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    V inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const V y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        const V v = lane < nw ? wsum[lane] : V(0);
+        V s = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const V y = __shfl_up(s, o, 64);
+            if (lane >= o) s += y;
+        }
+        if (lane < nw) wsum[lane] = s - v;
+        if (lane == nw - 1) wsum[16] = s;
+    }
+    __syncthreads();
+    const V r = wsum[w] + inc - x;
+    *total = wsum[16];
+    __syncthreads();
+    return r;
+}
+
+template <class V>
+__global__ __launch_bounds__(kScanThreads) void k_scan_single(V* data, int64_t n, V* total_out) {
+    __shared__ V wsum[17];
+    V carry = 0;
+    for (int64_t base = 0; base < n; base += kScanTile) {
+        const int64_t i0 = base + (int64_t)threadIdx.x * kScanItems;
+        V v[kScanItems];
+        V s = 0;
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            v[k] = (i0 + k < n) ? data[i0 + k] : V(0);
+            s += v[k];
+        }
+        V tot;
+        V run = carry + block_exclusive_scan<V>(s, wsum, &tot);
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            if (i0 + k < n) data[i0 + k] = run;
+            run += v[k];
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0 && total_out) *total_out = carry;
+}
+
+template <class V>
+__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const V* data, int64_t n, V* part) {
+    __shared__ V wsum[17];
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    V s = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+        if (i0 + k < n) s += data[i0 + k];
+    V tot;
+    (void)block_exclusive_scan<V>(s, wsum, &tot);
+    if (threadIdx.x == 0) part[blockIdx.x] = tot;
+}
+
+template <class V>
+__global__ __launch_bounds__(kScanThreads) void k_scan_down(V* data, int64_t n, const V* part) {
+    __shared__ V wsum[17];
+    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    V v[kScanItems];
+    V s = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        v[k] = (i0 + k < n) ? data[i0 + k] : V(0);
+        s += v[k];
+    }
+    V tot;
+    V run = part[blockIdx.x] + block_exclusive_scan<V>(s, wsum, &tot);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        if (i0 + k < n) data[i0 + k] = run;
+        run += v[k];
+    }
+}
+
+template <class V>
+static tt_status scan_exclusive(V* data, int64_t n, V* part, V* total_out, hipStream_t s) {
+    if (n <= 4 * (int64_t)kScanTile) {
+        hipLaunchKernelGGL(k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, data, n, total_out);
+        TT_LAUNCH_CHECK();
+        return TT_OK;
+    }
+    const int64_t nb = (n + kScanTile - 1) / kScanTile;
+    hipLaunchKernelGGL(k_scan_reduce<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n, part);
+    TT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, part, nb, total_out);
+    TT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_scan_down<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n, part);
+    TT_LAUNCH_CHECK();
+    return TT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// groups and chunks
+
+__global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm,
+                                                const int32_t* __restrict__ skey,
+                                                const int32_t* __restrict__ i3,
+                                                const int32_t* __restrict__ bag_of, int64_t L,
+                                                int32_t* __restrict__ sorted_i3,
+                                                int32_t* __restrict__ sorted_bag,
+                                                int32_t* __restrict__ key_start,
+                                                int32_t* __restrict__ key_end) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= L) return;
+    const int32_t l = perm[s];
+    const int32_t k = skey[s];
+    sorted_i3[s] = i3[l];
+    sorted_bag[s] = bag_of[l];
+    if (s == 0 || skey[s - 1] != k) key_start[k] = (int32_t)s;
+    if (s == L - 1 || skey[s + 1] != k) key_end[k] = (int32_t)(s + 1);
+}
+
+__global__ __launch_bounds__(256) void k_key_flags(const int32_t* __restrict__ key_start,
+                                                   const int32_t* __restrict__ key_end, int64_t K,
+                                                   int32_t chunk, uint64_t* __restrict__ out) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= K) return;
+    const int32_t st = key_start[k];
+    uint64_t v = 0;
+    if (st >= 0) {
+        const uint32_t nch = (uint32_t)((key_end[k] - st + chunk - 1) / chunk);
+        v = (uint64_t(1) << 32) | nch;
+    }
+    out[k] = v;
+}
+
+__global__ __launch_bounds__(256) void k_groups(const int32_t* __restrict__ key_start,
+                                                const uint64_t* __restrict__ scan, int64_t K,
+                                                int64_t L, int32_t* __restrict__ group_key,
+                                                int32_t* __restrict__ group_start,
+                                                int32_t* __restrict__ group_cbase, int32_t* ctrl) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k == 0) {
+        const uint64_t tot = *reinterpret_cast<const uint64_t*>(ctrl + CTRL_SCAN_TOTAL);
+        const int32_t U = (int32_t)(tot >> 32), NC = (int32_t)(tot & 0xffffffffu);
+        ctrl[CTRL_NUM_GROUPS] = U;
+        ctrl[CTRL_NUM_CHUNKS] = NC;
+        group_start[U] = (int32_t)L;
+        group_cbase[U] = NC;
+    }
+    if (k >= K) return;
+    const int32_t st = key_start[k];
+    if (st < 0) return;
+    const uint64_t v = scan[k];
+    const int32_t g = (int32_t)(v >> 32);
+    group_key[g] = (int32_t)k;
+    group_start[g] = st;
+    group_cbase[g] = (int32_t)(v & 0xffffffffu);
+}
+
+__global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
+                                                const int32_t* __restrict__ group_cbase,
+                                                int64_t Cmax, int32_t chunk, const int32_t* ctrl,
+                                                int32_t* __restrict__ chunk_group,
+                                                int32_t* __restrict__ chunk_begin,
+                                                int32_t* __restrict__ chunk_end) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
+    const int32_t U = ctrl[CTRL_NUM_GROUPS];
+    if (c >= Cmax || c >= NC) return;
+    int32_t lo = 0, hi = U;   // last g in [0, U) with cbase[g] <= c
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (group_cbase[mid] <= c) lo = mid; else hi = mid;
+    }
+    const int32_t g = lo;
+    const int32_t b = group_start[g] + (int32_t)(c - group_cbase[g]) * chunk;
+    chunk_group[c] = g;
+    chunk_begin[c] = b;
+    chunk_end[c] = min(b + chunk, group_start[g + 1]);
+}
+
+}  // namespace tt
+
+using namespace tt;
+
+// ---------------------------------------------------------------------------
+// host side
+
+static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out) {
+    if (!tables || T < 1) return TT_ERR_INVALID_ARG;
+    if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
+    int64_t K = 0;
+    int32_t D = -1;
+    for (int32_t t = 0; t < T; ++t) {
+        const tt_emb_table& x = tables[t];
+        if (x.reserved != 0) return TT_ERR_INVALID_ARG;
+        if (x.num_rows < 1 || x.rank < 1) return TT_ERR_INVALID_ARG;
+        for (int k = 0; k < 3; ++k)
+            if (x.m[k] < 1 || x.n[k] < 1 || x.g_offset[k] < 0) return TT_ERR_INVALID_ARG;
+        const int64_t rows = (int64_t)x.m[0] * x.m[1] * x.m[2];
+        if (rows < x.num_rows) return TT_ERR_INVALID_ARG;
+        if (x.num_rows >= (int64_t(1) << 31)) return TT_ERR_UNSUPPORTED;
+        const int64_t d = (int64_t)x.n[0] * x.n[1] * x.n[2];
+        if (D >= 0 && d != D) return TT_ERR_INVALID_ARG;
+        if (x.rank > kMaxR || (int64_t)x.n[0] * x.n[1] > kMaxN12 || x.n[2] > kMaxN3 || d > kMaxD)
+            return TT_ERR_UNSUPPORTED;
+        D = (int32_t)d;
+        K += (int64_t)x.m[0] * x.m[1];
+        if (K >= kMaxKeys) return TT_ERR_UNSUPPORTED;
+    }
+    *K_out = K;
+    *D_out = D;
+    return TT_OK;
+}
+
+static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
+    if (L < 0 || B < 0 || chunk < 1) return TT_ERR_INVALID_ARG;
+    if (L >= (int64_t(1) << 31) - 1) return TT_ERR_UNSUPPORTED;
+    if ((int64_t)T * B >= (int64_t(1) << 31) - 1) return TT_ERR_UNSUPPORTED;
+    if ((int64_t)T * B == 0 && L != 0) return TT_ERR_INVALID_ARG;
+    return TT_OK;
+}
+
+extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
+                                         int64_t B, int32_t chunk) {
+    int64_t K = 0;
+    int32_t D = 0;
+    if (check_tables(tables, T, &K, &D) != TT_OK) return 0;
+    if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
+    return make_layout(T, L, B, chunk, K).total;
+}
+
+extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                                 const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 tt_emb_plan_t* plan_out) {
+    if (!plan_out) return TT_ERR_INVALID_ARG;
+    *plan_out = nullptr;
+    int64_t K = 0;
+    int32_t D = 0;
+    tt_status st = check_tables(tables, T, &K, &D);
+    if (st != TT_OK) return st;
+    st = check_sizes(T, L, B, chunk);
+    if (st != TT_OK) return st;
+    if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
+    const Layout lay = make_layout(T, L, B, chunk, K);
+    if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
+
+    tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
+    if (!p) return TT_ERR_INVALID_ARG;
+    p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;
+    p->ws = (char*)workspace;
+    p->lay = lay;
+    p->tables.assign(tables, tables + T);
+    p->uniform = true;
+    p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
+    for (int k = 0; k < 3; ++k) p->extent[k] = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        const tt_emb_table& x = tables[t];
+        if (x.n[0] != p->n1 || x.n[1] != p->n2 || x.n[2] != p->n3 || x.rank != p->R) p->uniform = false;
+        const int64_t R = x.rank;
+        const int64_t sz[3] = {(int64_t)x.m[0] * x.n[0] * R, (int64_t)x.m[1] * R * x.n[1] * R,
+                               (int64_t)x.m[2] * R * x.n[2]};
+        for (int k = 0; k < 3; ++k) p->extent[k] = std::max(p->extent[k], x.g_offset[k] + sz[k]);
+    }
+    hipStream_t s = (hipStream_t)stream;
+
+    auto fail = [&](tt_status e) { delete p; return e; };
+    // control words and descriptors
+    if (fill32(p->ctrl(), 0u, CTRL_WORDS, s) != TT_OK) return fail(TT_ERR_HIP);
+    int32_t kb = 0;
+    for (int32_t first = 0; first < T; first += 16) {
+        DescBatch b{};
+        b.first = first;
+        b.count = std::min<int32_t>(16, T - first);
+        for (int i = 0; i < b.count; ++i) {
+            const tt_emb_table& x = tables[first + i];
+            TabDev& d = b.d[i];
+            d.N = (int32_t)x.num_rows;
+            d.m1 = x.m[0]; d.m2 = x.m[1]; d.m3 = x.m[2];
+            d.n1 = x.n[0]; d.n2 = x.n[1]; d.n3 = x.n[2]; d.R = x.rank;
+            d.o1 = x.g_offset[0]; d.o2 = x.g_offset[1]; d.o3 = x.g_offset[2];
+            d.key_base = kb;
+            d.key_count = x.m[0] * x.m[1];
+            kb += d.key_count;
+        }
+        hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
+        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+    }
+
+    int32_t* ctrl = p->ctrl();
+    int32_t* key = p->at<int32_t>(lay.key);
+    int32_t* i3 = p->at<int32_t>(lay.i3);
+    int32_t* bag = p->at<int32_t>(lay.bag_of);
+    // split (also checks the offsets; one thread per lookup and per offset)
+    {
+        const int64_t n = std::max<int64_t>(L, p->TB + 1);
+        hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
+                           p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag, ctrl);
+        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+    }
+    // stable radix sort: key -> (skey, perm)
+    if (L > 0) {
+        const int P = lay.passes;
+        uint32_t* hist = p->at<uint32_t>(lay.hist);
+        uint64_t* part = p->at<uint64_t>(lay.scan_tmp);
+        const int32_t* kin = key;
+        const int32_t* vin = nullptr;
+        for (int pass = 0; pass < P; ++pass) {
+            // the last pass lands in (skey, perm); earlier passes alternate so that it does
+            const bool to_final = ((P - 1 - pass) % 2) == 0;
+            int32_t* kout = p->at<int32_t>(to_final ? lay.sort_k1 : lay.sort_k0);
+            int32_t* vout = p->at<int32_t>(to_final ? lay.sort_v1 : lay.sort_v0);
+            const int shift = pass * kRadixBits;
+            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
+                               kin, L, shift, lay.n_tiles, hist);
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (scan_exclusive<uint32_t>(hist, (int64_t)kRadixBins * lay.n_tiles,
+                                         reinterpret_cast<uint32_t*>(part), nullptr, s) != TT_OK)
+                return fail(TT_ERR_HIP);
+            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
+                               s, kin, vin, L, shift, lay.n_tiles, hist, kout, vout);
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            kin = kout;
+            vin = vout;
+        }
+    }
+    // groups and chunks
+    {
+        int32_t* key_start = p->at<int32_t>(lay.key_start);
+        int32_t* key_end = p->at<int32_t>(lay.key_end);
+        uint64_t* kscan = p->at<uint64_t>(lay.key_scan);
+        if (fill32(key_start, 0xffffffffu, K, s) != TT_OK) return fail(TT_ERR_HIP);
+        if (L > 0) {
+            hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
+                               p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
+                               p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
+                               key_start, key_end);
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        }
+        hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
+                           key_end, K, chunk, kscan);
+        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (scan_exclusive<uint64_t>(kscan, K, p->at<uint64_t>(lay.scan_tmp),
+                                     reinterpret_cast<uint64_t*>(ctrl + CTRL_SCAN_TOTAL), s) != TT_OK)
+            return fail(TT_ERR_HIP);
+        hipLaunchKernelGGL(k_groups, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start, kscan, K,
+                           L, p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
+                           p->at<int32_t>(lay.group_cbase), ctrl);
+        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (lay.Cmax > 0) {
+            hipLaunchKernelGGL(k_chunks, dim3(grid_for(lay.Cmax, 256)), dim3(256), 0, s,
+                               p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
+                               lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
+                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        }
+    }
+    *plan_out = p;
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_get_error(tt_emb_plan_t p, int32_t* flag_out, void* stream) {
+    if (!p || !flag_out) return TT_ERR_INVALID_ARG;
+    int32_t f = 0;
+    hipStream_t s = (hipStream_t)stream;
+    TT_HIP_CHECK(hipMemcpyAsync(&f, p->ctrl() + CTRL_FLAG, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    TT_HIP_CHECK(hipStreamSynchronize(s));
+    *flag_out = f;
+    return f ? TT_ERR_DEVICE_FLAG : TT_OK;
+}
+
+extern "C" tt_status tt_emb_plan_get_view(tt_emb_plan_t p, tt_emb_plan_view* v) {
+    if (!p || !v) return TT_ERR_INVALID_ARG;
+    const Layout& y = p->lay;
+    v->key = p->at<int32_t>(y.key);
+    v->i3 = p->at<int32_t>(y.i3);
+    v->bag_of = p->at<int32_t>(y.bag_of);
+    v->perm = p->at<int32_t>(y.perm);
+    v->sorted_i3 = p->at<int32_t>(y.sorted_i3);
+    v->sorted_bag = p->at<int32_t>(y.sorted_bag);
+    v->group_key = p->at<int32_t>(y.group_key);
+    v->group_start = p->at<int32_t>(y.group_start);
+    v->chunk_group = p->at<int32_t>(y.chunk_group);
+    v->chunk_begin = p->at<int32_t>(y.chunk_begin);
+    v->chunk_end = p->at<int32_t>(y.chunk_end);
+    v->max_groups = y.Gmax;
+    v->max_chunks = y.Cmax;
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_plan_counts(tt_emb_plan_t p, int64_t* num_groups, int64_t* num_chunks,
+                                        void* stream) {
+    if (!p || !num_groups || !num_chunks) return TT_ERR_INVALID_ARG;
+    int32_t c[3] = {0, 0, 0};
+    hipStream_t s = (hipStream_t)stream;
+    TT_HIP_CHECK(hipMemcpyAsync(c, p->ctrl(), sizeof(c), hipMemcpyDeviceToHost, s));
+    TT_HIP_CHECK(hipStreamSynchronize(s));
+    *num_groups = c[CTRL_NUM_GROUPS];
+    *num_chunks = c[CTRL_NUM_CHUNKS];
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_plan_destroy(tt_emb_plan_t p) {
+    delete p;
+    return TT_OK;
+}
+
+extern "C" const char* tt_emb_status_string(tt_status s) {
+    switch (s) {
+        case TT_OK: return "ok";
+        case TT_ERR_INVALID_ARG: return "invalid argument";
+        case TT_ERR_UNSUPPORTED: return "unsupported (outside this build's limits)";
+        case TT_ERR_WORKSPACE: return "workspace too small";
+        case TT_ERR_HIP: return "HIP runtime error";
+        case TT_ERR_DEVICE_FLAG: return "device error flag set (bad index or offsets)";
+    }
+    return "unknown status";
+}

@@ -1,0 +1,114 @@
+// Internal definitions shared by the HIP sources of libtt_emb.so (not part of
+// the C ABI). Written for gfx950 (CDNA4): wave64, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tt_emb.h"
+
+namespace tt {
+
+// Per-table descriptor as the kernels read it (device copy in the workspace).
+struct alignas(16) TabDev {
+    int32_t N, m1, m2, m3;      // rows and radices
+    int32_t n1, n2, n3, R;      // dim factors and rank
+    int64_t o1, o2, o3;         // element offsets of this table's G1/G2/G3
+    int32_t key_base;           // first prefix key of this table
+    int32_t key_count;          // m1*m2
+};
+static_assert(sizeof(TabDev) == 64, "TabDev layout");
+
+// Control words at the head of the workspace (int32 slots).
+enum CtrlSlot : int {
+    CTRL_FLAG = 0,        // TT_FLAG_* bits
+    CTRL_NUM_GROUPS = 1,
+    CTRL_NUM_CHUNKS = 2,
+    CTRL_WORK_FWD = 3,    // persistent forward: next task to claim
+    CTRL_WORK_BWD = 4,    // persistent backward: next task to claim
+    CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
+    CTRL_WORDS = 64
+};
+
+constexpr int kRadixBits = 8;
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kSortThreads = 256;                        // 4 waves
+constexpr int kSortItems = 16;                           // per thread
+constexpr int kSortTile = kSortThreads * kSortItems;     // 4096 lookups per tile
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 4;
+constexpr int kScanTile = kScanThreads * kScanItems;     // 4096 per scan tile
+
+// Limits (mirrored in the public header's comment).
+constexpr int kMaxR = 64;
+constexpr int kMaxN12 = 64;
+constexpr int kMaxN3 = 16;
+constexpr int kMaxD = 1024;
+constexpr int kMaxTables = 4096;
+constexpr int64_t kMaxKeys = int64_t(1) << 30;
+
+// Carving of the caller's workspace. Every array starts on a 256-byte boundary.
+struct Layout {
+    size_t ctrl, desc;
+    size_t key, i3, bag_of;                  // [L]
+    size_t perm, sorted_i3, sorted_bag;      // [L]
+    size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
+    size_t hist;                             // [kRadixBins * n_tiles] uint32
+    size_t key_start, key_end;               // [K] int32
+    size_t key_scan;                         // [K] uint64
+    size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
+    size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
+    size_t scan_tmp;                         // uint64 partials of the multi-block scan
+    size_t total;
+    int64_t n_tiles, K, Gmax, Cmax;
+    int passes;
+};
+
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K);
+
+}  // namespace tt
+
+// Host-side plan handle.
+struct tt_emb_plan_s {
+    int32_t T;
+    int64_t L, B, TB;
+    int32_t chunk;
+    int32_t D;
+    int64_t K;
+    bool uniform;             // all tables share (n1, n2, n3, R)
+    int32_t n1, n2, n3, R;    // the shared shape when uniform
+    int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
+    char* ws;                 // workspace base (device)
+    tt::Layout lay;
+    std::vector<tt_emb_table> tables;
+
+    template <class P>
+    P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+    int32_t* ctrl() const { return at<int32_t>(lay.ctrl); }
+    const tt::TabDev* desc() const { return at<tt::TabDev>(lay.desc); }
+};
+
+#define TT_HIP_CHECK(expr)                                  \
+    do {                                                    \
+        hipError_t _e = (expr);                             \
+        if (_e != hipSuccess) return TT_ERR_HIP;            \
+    } while (0)
+
+#define TT_LAUNCH_CHECK()                                   \
+    do {                                                    \
+        hipError_t _e = hipGetLastError();                  \
+        if (_e != hipSuccess) return TT_ERR_HIP;            \
+    } while (0)
+
+namespace tt {
+inline unsigned grid_for(int64_t n, int threads) {
+    int64_t g = (n + threads - 1) / threads;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+// Fill `n` 32-bit words at `p` with `v` (stream-ordered, capture-safe).
+tt_status fill32(void* p, uint32_t v, int64_t n, hipStream_t s);
+}  // namespace tt

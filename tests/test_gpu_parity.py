@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Planner tables must match bit for bit. Floats must satisfy
+|gpu - ref| <= 1e-4 * (1 + |ref|) elementwise, ref being the fp64 oracle.
+Small cases compare every output; the full-size workloads compare sampled
+bags (forward) and sampled core slices (backward), which the oracle computes
+one by one, in the launch configuration the benchmark times.
+"""
+import json
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.test_oracle_forward import GOLDEN
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from tests.gpu_helpers import DevProblem, assert_close, say  # noqa: E402
+
+PLAN_KEYS = ("key", "i3", "bag_of", "perm", "sorted_i3", "sorted_bag", "group_key",
+             "group_start", "chunk_group", "chunk_begin", "chunk_end")
+
+
+def check_plan(dp, label):
+    got = dp.plan_tables()
+    ref = oracle.plan_problem(dp.p, dp.chunk)
+    for k in PLAN_KEYS:
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=f"{label}: {k}")
+    return got
+
+
+def run_forward_check(p, label, chunk=256, bags=None):
+    say(label, f"L={p.L} bags={p.T * p.batch} chunk={chunk}")
+    dp = DevProblem(p, chunk)
+    out = dp.forward().cpu().numpy()
+    assert dp.plan is not None
+    from tensor_train_compressed_amd import tt_emb_get_error
+    assert tt_emb_get_error(dp.plan) == 0
+    if bags is None:
+        ref = oracle.forward_problem(p)
+        err = assert_close(out, ref, f"{label} forward")
+    else:
+        ref = oracle.forward_problem(p, bags=bags)
+        err = assert_close(out[bags], ref, f"{label} forward (sampled)")
+    say(label, f"max rel err {err:.2e}")
+    return dp, out
+
+
+# ---------------------------------------------------------------------------
+# planner
+
+def test_plan_hand_worked():
+    g = json.load(open(GOLDEN))
+    t = wl.Table(g["table"]["num_rows"], tuple(g["table"]["m"]), tuple(g["table"]["n"]),
+                 g["table"]["rank"])
+    p = wl.Problem("golden", [t], g["batch"], np.array(g["g1"], np.float32).ravel(),
+                   np.array(g["g2"], np.float32).ravel(), np.array(g["g3"], np.float32).ravel(),
+                   np.zeros((1, 3), np.int64), np.array(g["indices"], np.int64),
+                   np.array(g["offsets"], np.int64), np.array(g["grad_out"], np.float32), g["lr"])
+    dp = DevProblem(p, g["plan_chunk"])
+    dp.make_plan()
+    got = dp.plan_tables()
+    for k in PLAN_KEYS:
+        np.testing.assert_array_equal(got[k], np.array(g["plan"][k], np.int32), err_msg=k)
+    out = dp.forward().cpu().numpy()
+    np.testing.assert_allclose(out, np.array(g["out"], np.float64), rtol=0, atol=1e-5)
+    d1, d2, d3 = (x.cpu().numpy() for x in dp.backward())
+    np.testing.assert_allclose(d1, np.array(g["dg1"], np.float64).ravel(), atol=1e-5)
+    np.testing.assert_allclose(d2, np.array(g["dg2"], np.float64).ravel(), atol=1e-5)
+    np.testing.assert_allclose(d3, np.array(g["dg3"], np.float64).ravel(), atol=1e-5)
+
+
+@pytest.mark.parametrize("name,kw,chunk", [
+    ("tiny", {}, 256), ("tiny", {}, 1), ("table1m", {}, 256), ("skew11m", {}, 256),
+    ("skew11m", {"permuted": True}, 128), ("multi26", {}, 256)])
+def test_plan_bit_exact_full_size(name, kw, chunk):
+    p = wl.make(name, **kw)
+    say("plan", name, kw, f"L={p.L}")
+    dp = DevProblem(p, chunk)
+    dp.make_plan()
+    check_plan(dp, f"{name}{kw}")
+    # repeat: identical tables
+    first = dp.plan_tables()
+    dp.make_plan()
+    again = dp.plan_tables()
+    for k in PLAN_KEYS:
+        np.testing.assert_array_equal(first[k], again[k], err_msg=f"repeat {k}")
+
+
+def test_plan_edge_cases():
+    t = wl.Table(1000, (10, 10, 10), (2, 2, 4), 4)
+    cases = {
+        "empty bags": wl.make_custom([t], np.array([0, 0, 3, 0, 5, 0]), seed=1),
+        "one giant group": wl.make_custom([t], np.full(40, 200), seed=2),
+        "all lookups empty": wl.make_custom([t], np.zeros(7, np.int64), seed=3),
+    }
+    cases["one giant group"].indices[:] = 7          # every lookup -> same (i1, i2)
+    cases["empty bags"].indices[-1] = 999            # largest index
+    for label, p in cases.items():
+        for chunk in (1, 3, 256):
+            say("plan edge", label, chunk)
+            dp = DevProblem(p, chunk)
+            dp.make_plan()
+            check_plan(dp, f"{label} chunk={chunk}")
+
+
+def test_plan_ragged_multitable():
+    tabs = [wl.Table(97, (5, 4, 5), (2, 2, 2), 3), wl.Table(1, (1, 1, 1), (1, 8, 1), 2),
+            wl.Table(5000, (17, 18, 17), (4, 2, 1), 5)]
+    p = wl.make_custom(tabs, np.random.default_rng(0).integers(0, 9, 3 * 700), seed=4)
+    for chunk in (1, 7, 64):
+        dp = DevProblem(p, chunk)
+        dp.make_plan()
+        check_plan(dp, f"ragged chunk={chunk}")
+
+
+def test_device_error_flags():
+    from tensor_train_compressed_amd import TT_FLAG_BAD_INDEX, TT_FLAG_BAD_OFFSETS, tt_emb_get_error
+    t = wl.Table(1000, (10, 10, 10), (2, 2, 4), 4)
+    p = wl.make_custom([t], np.array([2, 3, 1]), seed=5)
+    p.indices[3] = 1000
+    dp = DevProblem(p)
+    dp.make_plan()
+    assert tt_emb_get_error(dp.plan) == TT_FLAG_BAD_INDEX
+    p = wl.make_custom([t], np.array([2, 3, 1]), seed=5)
+    p.indices[0] = -4
+    dp = DevProblem(p)
+    dp.make_plan()
+    assert tt_emb_get_error(dp.plan) == TT_FLAG_BAD_INDEX
+    p = wl.make_custom([t], np.array([2, 3, 1]), seed=5)
+    p.offsets[1], p.offsets[2] = 4, 3                 # decreasing
+    dp = DevProblem(p)
+    dp.make_plan()
+    assert tt_emb_get_error(dp.plan) & TT_FLAG_BAD_OFFSETS
+    dp.forward()                                      # still runs, in bounds
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# forward
+
+def test_forward_tiny_materialised():
+    p = wl.make("tiny")
+    run_forward_check(p, "tiny")
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 256])
+def test_forward_small_all_bags(chunk):
+    run_forward_check(wl.make("skew11m", batch=512), f"skew11m B=512", chunk=chunk)
+
+
+def test_forward_table1m_full():
+    run_forward_check(wl.make("table1m"), "table1m")
+
+
+def test_forward_multitable_small_all_bags():
+    run_forward_check(wl.make("multi26", batch=128), "multi26 B=128")
+
+
+def test_forward_ragged_shapes():
+    tabs = [wl.Table(97, (5, 4, 5), (2, 2, 2), 3), wl.Table(1, (1, 1, 1), (1, 8, 1), 2),
+            wl.Table(5000, (17, 18, 17), (4, 2, 1), 5)]
+    p = wl.make_custom(tabs, np.random.default_rng(0).integers(0, 9, 3 * 300), seed=4)
+    for chunk in (1, 3, 64):
+        run_forward_check(p, f"ragged chunk={chunk}", chunk=chunk)
+
+
+def _sample_bags(p, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    lens = np.diff(p.offsets)
+    big = np.argsort(lens)[-8:]
+    picks = np.concatenate([[0, p.T * p.batch - 1], big, rng.integers(0, p.T * p.batch, n)])
+    return np.unique(picks)
+
+
+@pytest.mark.parametrize("name", ["skew11m", "multi26"])
+def test_forward_full_size_sampled(name):
+    p = wl.make(name)
+    run_forward_check(p, f"{name} full", chunk=256, bags=_sample_bags(p))
+
+
+# ---------------------------------------------------------------------------
+# backward + SGD
+
+def _check_backward(p, label, chunk=256, mask=None, slices=None):
+    say(label, f"backward L={p.L} chunk={chunk}")
+    dp = DevProblem(p, chunk)
+    d = [x.cpu().numpy() for x in dp.backward()]
+    ref = oracle.backward_problem(p, mask=mask)
+    names = ("dG1", "dG2", "dG3")
+    for k in range(3):
+        if slices is None:
+            assert_close(d[k], ref[k], f"{label} {names[k]}")
+        else:
+            sel = slices[k]
+            assert_close(d[k][sel], ref[k][sel], f"{label} {names[k]} (sampled)")
+    # SGD on the GPU from the GPU gradients, against the oracle's update
+    from tensor_train_compressed_amd import tt_emb_sgd
+    dg = dp.backward()
+    g = [dp.g1.clone(), dp.g2.clone(), dp.g3.clone()]
+    tt_emb_sgd(dp.plan, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr)
+    cores = (p.g1, p.g2, p.g3)
+    for k in range(3):
+        want = oracle.sgd(cores[k], ref[k], p.lr)
+        got = g[k].cpu().numpy()
+        sel = slice(None) if slices is None else slices[k]
+        assert_close(got[sel], want[sel], f"{label} SGD core {k + 1}")
+
+
+def test_backward_small_all():
+    p = wl.make("train11m", batch=256)
+    for chunk in (1, 256):
+        _check_backward(p, f"train11m B=256", chunk=chunk)
+
+
+def test_backward_multitable_small():
+    p = wl.make("multi26", batch=32, tables=6)
+    p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
+    p.lr = 0.01
+    _check_backward(p, "multi26 6 tables B=32")
+
+
+def test_backward_ragged():
+    tabs = [wl.Table(97, (5, 4, 5), (2, 2, 2), 3), wl.Table(1, (1, 1, 1), (1, 8, 1), 2),
+            wl.Table(5000, (17, 18, 17), (4, 2, 1), 5)]
+    p = wl.make_custom(tabs, np.random.default_rng(0).integers(0, 9, 3 * 100), seed=4,
+                       with_grad=True)
+    for chunk in (1, 64):
+        _check_backward(p, f"ragged chunk={chunk}", chunk=chunk)
+
+
+def _slice_mask(p, pl, which, picks):
+    """Mask of lookups whose core-`which` digit is in picks (single table)."""
+    t = p.tables[0]
+    key = pl["key"].astype(np.int64)
+    i1 = key % t.m[0]
+    i2 = key // t.m[0]
+    i3 = pl["i3"].astype(np.int64)
+    dig = {1: i1, 2: i2, 3: i3}[which]
+    return np.isin(dig, picks)
+
+
+def test_backward_full_size_sampled():
+    """train11m at full size: compare gradients of sampled slices; the oracle
+    sums only the lookups that touch them (which is exact for those slices)."""
+    p = wl.make("train11m")
+    t = p.tables[0]
+    R, (n1, n2, n3) = t.rank, t.n
+    pl = oracle.plan_problem(p, 256)
+    i1s = np.array([3, 57, 199]); i2s = np.array([100, 150, 219]); i3s = np.array([17, 131, 249])
+    mask = (_slice_mask(p, pl, 1, i1s) | _slice_mask(p, pl, 2, i2s) |
+            _slice_mask(p, pl, 3, i3s)).astype(np.uint8)
+    say("sampled backward lookups", int(mask.sum()))
+    s1 = np.concatenate([np.arange(i * n1 * R, (i + 1) * n1 * R) for i in i1s])
+    s2 = np.concatenate([np.arange(i * R * n2 * R, (i + 1) * R * n2 * R) for i in i2s])
+    s3 = np.concatenate([np.arange(i * R * n3, (i + 1) * R * n3) for i in i3s])
+    _check_backward(p, "train11m full", chunk=256, mask=mask, slices=(s1, s2, s3))
