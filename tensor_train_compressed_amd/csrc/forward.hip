@@ -64,6 +64,253 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core path for the common shapes (all tables share n1, n2, n3, R).
+//
+// One wave per chunk. The prefix P = G1[i1] x G2[i2] is formed once per chunk
+// (VALU, into LDS) and held in registers as the A operand of
+// v_mfma_f32_16x16x4_f32 for the whole chunk. A tile is 16 output columns =
+// (16/n3 lookups) x (n3 columns of G3), so a chunk of any length wastes at most
+// 16/n3 - 1 lookup slots. Rows leave the matrix cores through LDS, are summed
+// along runs of equal bag (lookups of one bag are adjacent inside a group), and
+// every run is written once, as a whole row, to its slot in the stage buffer
+// (the slot of the run's first lookup). k_pool then adds each bag's runs in
+// input order and writes the bag's output row: no atomics, and the same bits
+// on every run.
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct FwdArgs {
+    const TabDev* desc;
+    int32_t T;
+    const int32_t* ctrl;
+    const int32_t* group_key;
+    const int32_t* chunk_group;
+    const int32_t* chunk_begin;
+    const int32_t* chunk_end;
+    const int32_t* sorted_i3;
+    const int32_t* sorted_bag;
+    const int32_t* perm;
+    const float* g1;
+    const float* g2;
+    const float* g3;
+    float* stage;
+};
+
+// Orders this wave's LDS writes before its later LDS reads (LDS executes a
+// wave's operations in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int N1, int N2, int R, int N3>
+struct FwdShape {
+    static constexpr int NP = N1 * N2;      // rows of P
+    static constexpr int D = NP * N3;       // output width
+    static constexpr int KS = R / 4;        // k-steps of 16x16x4 per tile
+    static constexpr int MT = NP / 16;      // 16-row blocks of P
+    static constexpr int LK = 16 / N3;      // lookups per tile
+    static constexpr int TPB = 4;           // tiles per batch
+    static constexpr int BL = LK * TPB;     // lookups per batch
+    static constexpr int RS = D + 4;        // LDS row stride (floats)
+    static constexpr int HG = 64 / R;       // lanes groups sharing an r2 in the P build
+    static constexpr int PE = NP * R / 64;  // P elements per lane
+    static constexpr int DL = D / 64;       // output floats per lane
+    static_assert(NP % 16 == 0 && R % 4 == 0 && 16 % N3 == 0 && D % 64 == 0, "shape");
+    static_assert(64 % R == 0 && N2 % HG == 0 && DL <= 4, "shape");
+};
+
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
+    using S = FwdShape<N1, N2, R, N3>;
+    constexpr int NP = S::NP, D = S::D, KS = S::KS, MT = S::MT, LK = S::LK, TPB = S::TPB;
+    constexpr int BL = S::BL, RS = S::RS, HG = S::HG, PE = S::PE, DL = S::DL;
+    __shared__ float sP[4][NP * R];
+    __shared__ float sRow[4][BL * RS];
+    __shared__ float sG1[4][N1 * R];
+
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int32_t c = (int32_t)blockIdx.x * 4 + w;
+    if (c >= a.ctrl[CTRL_NUM_CHUNKS]) return;
+
+    const int32_t g = a.chunk_group[c];
+    const int32_t key = a.group_key[g];
+    const TabDev d = a.desc[find_table(a.desc, a.T, key)];
+    const int32_t local = key - d.key_base;
+    const int32_t i2 = local / d.m1, i1 = local % d.m1;
+
+    // ---- prefix P[p][r2] = sum_r1 G1[i1][j1][r1] G2[i2][r1][j2][r2], p = j1*N2 + j2
+    {
+        const float* A = a.g1 + d.o1 + (int64_t)i1 * N1 * R;
+        for (int e = lane; e < N1 * R; e += 64) sG1[w][e] = A[e];
+        wave_lds_sync();
+        const float* Bc = a.g2 + d.o2 + (int64_t)i2 * R * N2 * R;
+        const int r2 = lane % R, h = lane / R;
+        constexpr int J2N = N2 / HG;   // distinct j2 per lane
+        float acc[PE];
+#pragma unroll
+        for (int k = 0; k < PE; ++k) acc[k] = 0.f;
+#pragma unroll 4
+        for (int r1 = 0; r1 < R; ++r1) {
+            float b2[J2N];
+#pragma unroll
+            for (int jj = 0; jj < J2N; ++jj) b2[jj] = Bc[(r1 * N2 + h + HG * jj) * R + r2];
+#pragma unroll
+            for (int k = 0; k < PE; ++k) {
+                // p = h + HG*k  ->  j2 = h + HG*(k % J2N), j1 = k / J2N
+                acc[k] = fmaf(sG1[w][(k / J2N) * R + r1], b2[k % J2N], acc[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PE; ++k) sP[w][(h + HG * k) * R + r2] = acc[k];
+        wave_lds_sync();
+    }
+    // A operand: lane (i = lane%16, q = lane/16) holds P[16*mt + i][KS*q + s]
+    float afr[MT][KS];
+    {
+        const int i = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[w][(16 * mt + i) * R + KS * q + s2];
+    }
+
+    const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
+    const float* G3 = a.g3 + d.o3;
+    const int col = lane & 15, q = lane >> 4;
+    const int lk = col / N3, j3 = col % N3;
+
+    bool have = false;
+    int32_t rbag = -1, rhead = 0;
+    float racc[DL];
+#pragma unroll
+    for (int k = 0; k < DL; ++k) racc[k] = 0.f;
+
+    for (int32_t sb = s0; sb < s1; sb += BL) {
+        const int nb = min(BL, s1 - sb);
+        // bag and original position of the batch's lookups, lane r holds row r
+        int32_t bagv = 0, permv = 0;
+        if (lane < nb) {
+            bagv = a.sorted_bag[sb + lane];
+            permv = a.perm[sb + lane];
+        }
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+            const int32_t sl = sb + t * LK + lk;
+            const int32_t i3 = (sl < s1) ? a.sorted_i3[sl] : 0;
+            const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
+            float bv[KS];
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+                    cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
+                // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
+                const int rr = t * LK + lk;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
+            }
+        }
+        wave_lds_sync();
+        for (int r = 0; r < nb; ++r) {
+            const int32_t bag = __builtin_amdgcn_readlane(bagv, r);
+            if (have && bag != rbag) {
+                float* dst = a.stage + (int64_t)rhead * D + lane * DL;
+#pragma unroll
+                for (int k = 0; k < DL; ++k) dst[k] = racc[k];
+                have = false;
+            }
+            if (!have) {
+                have = true;
+                rbag = bag;
+                rhead = __builtin_amdgcn_readlane(permv, r);
+#pragma unroll
+                for (int k = 0; k < DL; ++k) racc[k] = 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < DL; ++k) racc[k] += sRow[w][r * RS + lane * DL + k];
+        }
+        wave_lds_sync();
+    }
+    if (have) {
+        float* dst = a.stage + (int64_t)rhead * D + lane * DL;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) dst[k] = racc[k];
+    }
+}
+
+// One wave per bag: sum the bag's run rows (run heads in input order) and write
+// the bag's output row. Empty bags get zeros.
+template <int DL>
+__global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
+                                              const uint8_t* __restrict__ run_head,
+                                              const float* __restrict__ stage,
+                                              float* __restrict__ out) {
+    constexpr int D = 64 * DL;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t q = (int64_t)blockIdx.x * 4 + w;
+    if (q >= TB) return;
+    const int32_t b0 = bag_start[q];
+    const int32_t b1 = max(b0, bag_start[q + 1]);
+    float acc[DL];
+#pragma unroll
+    for (int k = 0; k < DL; ++k) acc[k] = 0.f;
+    for (int32_t base = b0; base < b1; base += 64) {
+        const int32_t l = base + lane;
+        uint64_t m = __ballot(l < b1 && run_head[l] != 0);
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const float* src = stage + (int64_t)(base + j) * D + lane * DL;
+#pragma unroll
+            for (int k = 0; k < DL; ++k) acc[k] += src[k];
+        }
+    }
+    float* dst = out + q * D + lane * DL;
+#pragma unroll
+    for (int k = 0; k < DL; ++k) dst[k] = acc[k];
+}
+
+template <int N1, int N2, int R, int N3>
+static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
+                                 const float* g3, float* out, hipStream_t s) {
+    FwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
+              p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
+              p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
+              p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.perm), g1, g2, g3,
+              p->at<float>(p->lay.stage)};
+    if (p->lay.Cmax > 0) {
+        hipLaunchKernelGGL((k_fwd_mfma<N1, N2, R, N3>), dim3(grid_for(p->lay.Cmax, 4)), dim3(256), 0,
+                           s, a);
+        TT_LAUNCH_CHECK();
+    }
+    constexpr int DL = FwdShape<N1, N2, R, N3>::DL;
+    if (p->TB > 0) {
+        hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
+                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<uint8_t>(p->lay.run_head),
+                           p->at<float>(p->lay.stage), out);
+        TT_LAUNCH_CHECK();
+    }
+    return TT_OK;
+}
+
+// Returns true (and launches) when the plan's shape has a matrix-core kernel.
+static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
+                         float* out, hipStream_t s, tt_status* st) {
+    if (!p->uniform) return false;
+    const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
+    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, s); return true; }
+    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, s); return true; }
+    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 16) { *st = launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, s); return true; }
+    return false;
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -72,7 +319,9 @@ extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const floa
                                     const float* g3, float* out, void* stream) {
     if (!p || !g1 || !g2 || !g3 || (!out && p->TB > 0)) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    tt_status st = fill32(out, 0u, p->TB * p->D, s);
+    tt_status st = TT_OK;
+    if (try_fwd_mfma(p, g1, g2, g3, out, s, &st)) return st;
+    st = fill32(out, 0u, p->TB * p->D, s);
     if (st != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;

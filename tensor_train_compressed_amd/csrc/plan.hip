@@ -32,7 +32,7 @@ namespace tt {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K) {
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -43,11 +43,13 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K) {
     int bits = 0;
     while ((int64_t(1) << bits) < K) ++bits;
     y.passes = std::max(1, (bits + kRadixBits - 1) / kRadixBits);
-    (void)B;
     y.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
     y.desc = take(sizeof(TabDev) * (size_t)T);
     const size_t l4 = sizeof(int32_t) * (size_t)L;
     y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
+    y.bag_start = take(sizeof(int32_t) * (size_t)((int64_t)T * B + 1));
+    y.run_head = take((size_t)L);
+    y.stage = take(sizeof(float) * (size_t)L * (size_t)D);
     y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
     y.skey = take(l4);
     // The radix passes ping-pong between (skey, perm) and a temporary pair that
@@ -121,10 +123,12 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
                                                int64_t TB, int64_t B,
                                                const TabDev* __restrict__ desc,
                                                int32_t* __restrict__ key, int32_t* __restrict__ i3o,
-                                               int32_t* __restrict__ bag_of, int32_t* ctrl) {
+                                               int32_t* __restrict__ bag_of,
+                                               int32_t* __restrict__ bag_start, int32_t* ctrl) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i <= TB) {
         const int64_t a = off[i];
+        bag_start[i] = (int32_t)(a < 0 ? 0 : (a > L ? L : a));
         bool bad = (i == 0 && a != 0) || (i == TB && a != L) || (i < TB && off[i + 1] < a);
         if (bad) atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_OFFSETS);
     }
@@ -344,13 +348,18 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
                                                 int32_t* __restrict__ sorted_i3,
                                                 int32_t* __restrict__ sorted_bag,
                                                 int32_t* __restrict__ key_start,
-                                                int32_t* __restrict__ key_end) {
+                                                int32_t* __restrict__ key_end,
+                                                uint8_t* __restrict__ run_head) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
     const int32_t l = perm[s];
     const int32_t k = skey[s];
+    const int32_t b = bag_of[l];
     sorted_i3[s] = i3[l];
-    sorted_bag[s] = bag_of[l];
+    sorted_bag[s] = b;
+    // a run is a maximal stretch of one key and one bag in sorted order (chunk
+    // starts also open a run; k_chunks marks those)
+    run_head[l] = (s == 0 || skey[s - 1] != k || bag_of[perm[s - 1]] != b) ? 1 : 0;
     if (s == 0 || skey[s - 1] != k) key_start[k] = (int32_t)s;
     if (s == L - 1 || skey[s + 1] != k) key_end[k] = (int32_t)(s + 1);
 }
@@ -398,7 +407,9 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
                                                 int64_t Cmax, int32_t chunk, const int32_t* ctrl,
                                                 int32_t* __restrict__ chunk_group,
                                                 int32_t* __restrict__ chunk_begin,
-                                                int32_t* __restrict__ chunk_end) {
+                                                int32_t* __restrict__ chunk_end,
+                                                const int32_t* __restrict__ perm,
+                                                uint8_t* __restrict__ run_head) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
@@ -413,6 +424,7 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     chunk_group[c] = g;
     chunk_begin[c] = b;
     chunk_end[c] = min(b + chunk, group_start[g + 1]);
+    run_head[perm[b]] = 1;
 }
 
 }  // namespace tt
@@ -463,7 +475,7 @@ extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, 
     int32_t D = 0;
     if (check_tables(tables, T, &K, &D) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K).total;
+    return make_layout(T, L, B, chunk, K, D).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -480,7 +492,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K);
+    const Layout lay = make_layout(T, L, B, chunk, K, D);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
@@ -533,7 +545,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     {
         const int64_t n = std::max<int64_t>(L, p->TB + 1);
         hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
-                           p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag, ctrl);
+                           p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
+                           p->at<int32_t>(lay.bag_start), ctrl);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
     }
     // stable radix sort: key -> (skey, perm)
@@ -572,7 +585,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
                                p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
-                               key_start, key_end);
+                               key_start, key_end, p->at<uint8_t>(lay.run_head));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
@@ -589,7 +602,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_chunks, dim3(grid_for(lay.Cmax, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
-                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
+                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
+                               p->at<int32_t>(lay.perm), p->at<uint8_t>(lay.run_head));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

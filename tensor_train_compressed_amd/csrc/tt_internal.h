@@ -55,6 +55,9 @@ constexpr int64_t kMaxKeys = int64_t(1) << 30;
 struct Layout {
     size_t ctrl, desc;
     size_t key, i3, bag_of;                  // [L]
+    size_t bag_start;                        // [TB+1] int32 copy of the offsets
+    size_t run_head;                         // [L] uint8: lookup starts a (chunk, bag) run
+    size_t stage;                            // [L][D] float: one row per run, at its head
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
     size_t hist;                             // [kRadixBins * n_tiles] uint32
@@ -68,7 +71,7 @@ struct Layout {
     int passes;
 };
 
-Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K);
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D);
 
 }  // namespace tt
 
