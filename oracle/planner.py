@@ -18,7 +18,11 @@ unique:
   key      base_t + i2*m1 + i1, base_t = sum over earlier tables of m1*m2:
            one key per (table, i1, i2) prefix; groups sharing a G2 slice
            (same table and i2) get adjacent keys
-  order    stable sort of lookups by key (ties keep increasing lookup id)
+  order    lookups sorted by (key, i3), ties kept in increasing lookup id:
+           inside a group, lookups of the same table row are adjacent, so a
+           row that occurs several times is contracted once (the pages' point
+           that prefix grouping removes redundant core operations extends to
+           the last core when whole rows repeat)
   groups   maximal runs of equal key in sorted order
   chunks   each group, in order, cut into consecutive pieces of exactly C
            lookups; only a group's last piece may be shorter; no piece spans
@@ -70,7 +74,8 @@ def plan(radices: Sequence[Tuple[int, int, int]], num_rows: Sequence[int], B: in
     base = np.concatenate([[0], np.cumsum(m[:, 0] * m[:, 1])])
     key = base[t] + i2 * m1 + i1
 
-    perm = np.argsort(key, kind="stable")
+    M3 = int(m[:, 2].max())
+    perm = np.argsort(key * M3 + i3, kind="stable")
     skey = key[perm]
     if L:
         first = np.concatenate([[True], skey[1:] != skey[:-1]])

@@ -66,10 +66,13 @@ def test_against_bruteforce(inp):
 def check_invariants(p, L, chunk):
     perm = p["perm"].astype(np.int64)
     assert np.array_equal(np.sort(perm), np.arange(L))
-    skey = p["key"][perm]
+    skey = p["key"][perm].astype(np.int64)
+    si3 = p["i3"][perm].astype(np.int64)
     assert np.all(np.diff(skey) >= 0)
-    ties = np.diff(skey) == 0
-    assert np.all(np.diff(perm)[ties] > 0)               # stable
+    same_key = np.diff(skey) == 0
+    assert np.all(np.diff(si3)[same_key] >= 0)            # i3 ascending inside a group
+    ties = same_key & (np.diff(si3) == 0)
+    assert np.all(np.diff(perm)[ties] > 0)               # stable on equal (key, i3)
     gs = p["group_start"].astype(np.int64)
     assert gs[0] == 0 and gs[-1] == L and np.all(np.diff(gs) > 0)
     assert np.all(skey[gs[:-1]] == p["group_key"])

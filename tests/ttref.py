@@ -72,7 +72,7 @@ def grads_bruteforce(p):
 
 def plan_bruteforce(radices, num_rows, B, indices, offsets, chunk):
     """Planner tables by plain Python: digits by repeated division, order by
-    Python's sorted() on (key, l) tuples, groups and chunks by walking."""
+    Python's sorted() on (key, i3, l) tuples, groups and chunks by walking."""
     L = len(indices)
     bag = []
     for q in range(len(offsets) - 1):
@@ -92,7 +92,7 @@ def plan_bruteforce(radices, num_rows, B, indices, offsets, chunk):
         i1 = x // m2
         i1s.append(i1); i2s.append(i2); i3s.append(i3)
         keys.append(base[t] + i2 * m1 + i1)
-    order = [l for (_k, l) in sorted((keys[l], l) for l in range(L))]
+    order = [l for (_k, _i, l) in sorted((keys[l], i3s[l], l) for l in range(L))]
     gk, gs = [], []
     for s, l in enumerate(order):
         if s == 0 or keys[l] != keys[order[s - 1]]:
