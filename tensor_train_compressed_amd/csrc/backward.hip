@@ -7,18 +7,9 @@
 // is recomputed on chip; each lookup adds to dP (kept in LDS for the whole
 // chunk) and to its dG3 slice; the chunk then turns dP into its dG1 and dG2
 // contributions.
-#include "tt_internal.h"
+#include "tt_device.h"
 
 namespace tt {
-
-__device__ __forceinline__ int find_table_b(const TabDev* __restrict__ desc, int32_t T, int32_t key) {
-    int lo = 0, hi = T;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (desc[mid].key_base <= key) lo = mid; else hi = mid;
-    }
-    return lo;
-}
 
 __global__ __launch_bounds__(256) void k_bwd_generic(
     const TabDev* __restrict__ desc, int32_t T, const int32_t* __restrict__ ctrl,
@@ -33,7 +24,7 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     if (c >= ctrl[CTRL_NUM_CHUNKS]) return;
     const int32_t g = chunk_group[c];
     const int32_t key = group_key[g];
-    const TabDev d = desc[find_table_b(desc, T, key)];
+    const TabDev d = desc[find_table(desc, T, key)];
     const int32_t local = key - d.key_base;
     const int32_t i2 = local / d.m1, i1 = local % d.m1;
     const int32_t R = d.R, n1 = d.n1, n2 = d.n2, n3 = d.n3;
@@ -102,6 +93,365 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
     for (; i < n; i += stride) g[i] = fmaf(-lr, dg[i], g[i]);
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core backward for the common shapes (n1 = 4, n3 = 4, shared by all
+// tables). Three kernels:
+//
+// k_bwd_prep    zeroes dG1, dG3 and the dL/dP rows of groups cut into several
+//               chunks (the only targets that are accumulated with atomics)
+// k_bwd_runs    one wave per chunk. Recomputes P, then walks the chunk's runs
+//               (one run per distinct table row). For a run, S = sum of the
+//               grad_out rows of its lookups; then, on the matrix cores,
+//                 dG3[i3] += P^T S          (R x n3, added with atomics)
+//                 dP      += S G3[i3]^T     (n1*n2 x R, kept in registers)
+//               dP of the chunk goes to the group's dL/dP row (plain store, or
+//               atomics when the group has several chunks).
+// k_bwd_prefix  one workgroup per (table, i2) slice. Groups of one slice are
+//               adjacent in key order; for each,
+//                 dG2[i2] += G1[i1]^T dP    (accumulated in registers, stored
+//                                            once: no atomics)
+//                 dG1[i1] += dP G2[i2]^T    (four groups per matrix-core tile,
+//                                            added with atomics)
+
+struct BwdArgs {
+    const TabDev* desc;
+    int32_t T;
+    const int32_t* ctrl;
+    const int32_t* group_key;
+    const int32_t* group_cbase;
+    const int32_t* chunk_group;
+    const int32_t* chunk_begin;
+    const int32_t* chunk_end;
+    const int32_t* sorted_i3;
+    const int32_t* sorted_bag;
+    const uint8_t* run_head;
+    const float* g1;
+    const float* g2;
+    const float* g3;
+    const float* gout;
+    float* dg1;
+    float* dg3;
+    float* dpg;
+};
+
+template <int N1, int N2, int R, int N3>
+struct BwdShape {
+    static constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R;
+    static constexpr int MT = NP / 16;      // 16-row blocks of P / dP
+    static constexpr int RT = R / 16;       // 16-row blocks of P^T, 16-col blocks of dP
+    static constexpr int KSP = NP / 4;      // k-steps over p
+    static constexpr int LK = 16 / N3;      // runs per dG3 tile
+    static constexpr int RB = 2 * LK;       // runs buffered before a matrix-core pass
+    static constexpr int RS = D + 4;        // LDS row stride of S
+    static constexpr int CN = R * N3;       // dG3 slice width
+    static constexpr int CS = CN + 4;
+    static constexpr int DL = D / 64, CL = CN / 64;
+    static_assert(N1 == 4 && N3 == 4 && NP % 16 == 0 && R % 16 == 0, "shape");
+    static_assert(D % 64 == 0 && CN % 64 == 0 && 64 % R == 0, "shape");
+};
+
+__global__ __launch_bounds__(256) void k_bwd_prep(float* __restrict__ dg1, int64_t n1,
+                                                  float* __restrict__ dg3, int64_t n3,
+                                                  float* __restrict__ dpg, int32_t PR,
+                                                  const int32_t* __restrict__ group_cbase,
+                                                  const int32_t* __restrict__ ctrl) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.f;
+    for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.f;
+    const int32_t U = ctrl[CTRL_NUM_GROUPS];
+    const int lane = threadIdx.x & 63;
+    for (int64_t g = tid >> 6; g < U; g += nth >> 6) {
+        if (group_cbase[g + 1] - group_cbase[g] > 1)
+            for (int e = lane; e < PR; e += 64) dpg[g * PR + e] = 0.f;
+    }
+}
+
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(256) void k_bwd_runs(BwdArgs a) {
+    using S = BwdShape<N1, N2, R, N3>;
+    constexpr int NP = S::NP, D = S::D, PR = S::PR, MT = S::MT, RT = S::RT, KSP = S::KSP;
+    constexpr int LK = S::LK, RB = S::RB, RS = S::RS, CN = S::CN, CS = S::CS, DL = S::DL, CL = S::CL;
+    __shared__ float sP[4][PR];
+    __shared__ float sG1[4][N1 * R];
+    __shared__ float sS[4][RB * RS];
+    __shared__ float sC[4][LK * CS];
+    __shared__ int32_t sI3[4][RB];
+
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int32_t c = (int32_t)blockIdx.x * 4 + w;
+    if (c >= a.ctrl[CTRL_NUM_CHUNKS]) return;
+
+    const int32_t g = a.chunk_group[c];
+    const bool multi = (a.group_cbase[g + 1] - a.group_cbase[g]) > 1;
+    const int32_t key = a.group_key[g];
+    const TabDev d = a.desc[find_table(a.desc, a.T, key)];
+    const int32_t local = key - d.key_base;
+    const int32_t i2 = local / d.m1, i1 = local % d.m1;
+    build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
+                            a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
+    const int col = lane & 15, q = lane >> 4;
+    // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
+    float afT[RT][KSP];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[w][(KSP * q + s2) * R + 16 * rt + col];
+
+    floatx4 dacc[MT][RT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const float* G3 = a.g3 + d.o3;
+    float* dG3 = a.dg3 + d.o3;
+    int nrun = 0;
+    bool have = false;
+    int32_t cur_i3 = 0;
+    float sacc[DL];
+#pragma unroll
+    for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+
+    // matrix-core pass over the nrun buffered runs
+    auto flush = [&]() {
+        wave_lds_sync();
+        // dG3[i3] += P^T S: tiles of LK runs x N3 columns
+        for (int t0 = 0; t0 < nrun; t0 += LK) {
+            const int lk = col / N3, j3 = col % N3;
+            float bv[KSP];
+#pragma unroll
+            for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = sS[w][(t0 + lk) * RS + (KSP * q + s2) * N3 + j3];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KSP; ++s2)
+                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], bv[s2], cc, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) sC[w][lk * CS + (16 * rt + 4 * q + v) * N3 + j3] = cc[v];
+            }
+            wave_lds_sync();
+            const int nr = min(LK, nrun - t0);
+            for (int r = 0; r < nr; ++r) {
+                float* dst = dG3 + (int64_t)sI3[w][t0 + r] * CN + lane * CL;
+#pragma unroll
+                for (int k = 0; k < CL; ++k) atomicAdd(dst + k, sC[w][r * CS + lane * CL + k]);
+            }
+            wave_lds_sync();
+        }
+        // dP += S G3[i3]^T: one k-step per run (k = j3)
+        for (int r = 0; r < nrun; ++r) {
+            const float* gb = G3 + (int64_t)sI3[w][r] * CN;
+            float av[MT], bv[RT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) av[mt] = sS[w][r * RS + (16 * mt + col) * N3 + q];
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) bv[nt] = gb[(16 * nt + col) * N3 + q];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < RT; ++nt)
+                    dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], dacc[mt][nt], 0, 0, 0);
+        }
+        wave_lds_sync();
+        nrun = 0;
+    };
+    auto finish_run = [&]() {
+#pragma unroll
+        for (int k = 0; k < DL; ++k) sS[w][nrun * RS + lane * DL + k] = sacc[k];
+        if (lane == 0) sI3[w][nrun] = cur_i3;
+        ++nrun;
+        if (nrun == RB) flush();
+    };
+
+    const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
+    for (int32_t sb = s0; sb < s1; sb += 64) {
+        const int n = min(64, s1 - sb);
+        const int32_t sl = sb + lane;
+        const bool valid = lane < n;
+        const uint64_t m = __ballot(valid && a.run_head[sl] != 0);
+        const int32_t bagv = valid ? a.sorted_bag[sl] : 0;
+        const int32_t i3v = valid ? a.sorted_i3[sl] : 0;
+        for (int r = 0; r < n; ++r) {
+            if ((m >> r) & 1ull) {
+                if (have) finish_run();
+                have = true;
+                cur_i3 = __builtin_amdgcn_readlane(i3v, r);
+#pragma unroll
+                for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+            }
+            const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, r) * D + lane * DL;
+#pragma unroll
+            for (int k = 0; k < DL; ++k) sacc[k] += row[k];
+        }
+    }
+    if (have) finish_run();
+    if (nrun > 0) flush();
+
+    // dP of this chunk -> the group's dL/dP row, [p][r2]
+    float* dst = a.dpg + (int64_t)g * PR;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float* e = dst + (16 * mt + 4 * q + v) * R + 16 * nt + col;
+                if (multi) atomicAdd(e, dacc[mt][nt][v]);
+                else *e = dacc[mt][nt][v];
+            }
+}
+
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
+                                                    const int32_t* __restrict__ ctrl, int64_t K,
+                                                    const uint64_t* __restrict__ key_scan,
+                                                    const int32_t* __restrict__ group_key,
+                                                    const float* __restrict__ dpg,
+                                                    const float* __restrict__ g1,
+                                                    const float* __restrict__ g2,
+                                                    float* __restrict__ dg1, float* __restrict__ dg2) {
+    constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, RT = R / 16;
+    constexpr int NTN = N2R / 16;           // 16-col tiles of dG2
+    constexpr int NTW = NTN / 4;            // tiles per wave
+    constexpr int GS = N2R + 4;             // LDS row stride of G2 and dP rows
+    constexpr int KS1 = N2R / 4;            // k-steps of the dG1 product
+    static_assert(N1 == 4 && NTN % 4 == 0 && RT == 2, "shape");
+    __shared__ float sG2[R * GS];
+    __shared__ float sD[4 * N1 * GS];       // dP of four groups, rows (g, j1)
+    __shared__ float sA[4 * N1 * R];        // G1 of four groups
+    __shared__ float sRed[2][64][4];
+    __shared__ int32_t sI1[4];
+
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+    const int32_t bi = blockIdx.x;
+    int t = 0;
+    {
+        int lo = 0, hi = T;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (desc[mid].i2_base <= bi) lo = mid; else hi = mid;
+        }
+        t = lo;
+    }
+    const TabDev d = desc[t];
+    const int32_t i2 = bi - d.i2_base;
+    const int64_t kb = (int64_t)d.key_base + (int64_t)i2 * d.m1;
+    const int64_t ke = kb + d.m1;
+    const int32_t U = ctrl[CTRL_NUM_GROUPS];
+    const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
+    const int32_t g1e = ke < K ? (int32_t)(key_scan[ke] >> 32) : U;
+
+    const float* G2s = g2 + d.o2 + (int64_t)i2 * R * N2R;
+    for (int e = threadIdx.x; e < R * N2R; e += 256) sG2[(e / N2R) * GS + e % N2R] = G2s[e];
+
+    floatx4 acc2[RT][NTW];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc2[rt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int nt1 = w & 1, kh = w >> 1;
+    for (int32_t gs = g0; gs < g1e; gs += 4) {
+        const int ng = min(4, g1e - gs);
+        __syncthreads();
+        for (int e = threadIdx.x; e < 4 * NP * R; e += 256) {
+            const int gi = e / PR, r = e % PR;
+            sD[(gi * N1 + r / N2R) * GS + r % N2R] = gi < ng ? dpg[(int64_t)(gs + gi) * PR + r] : 0.f;
+        }
+        if (threadIdx.x < 4) sI1[threadIdx.x] = threadIdx.x < ng ? (int32_t)(group_key[gs + threadIdx.x] - kb) : 0;
+        __syncthreads();
+        for (int e = threadIdx.x; e < 4 * N1 * R; e += 256) {
+            const int gi = e / (N1 * R);
+            sA[e] = gi < ng ? g1[d.o1 + (int64_t)sI1[gi] * N1 * R + e % (N1 * R)] : 0.f;
+        }
+        __syncthreads();
+        // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c], one k-step (j1) per group
+        for (int gi = 0; gi < ng; ++gi) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float av = sA[gi * N1 * R + q * R + 16 * rt + col];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const float bv = sD[(gi * N1 + q) * GS + 16 * (w * NTW + j) + col];
+                    acc2[rt][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc2[rt][j], 0, 0, 0);
+                }
+            }
+        }
+        // dG1 rows (g, j1) = dP rows x G2^T: wave (nt1, kh) takes r1 tile nt1, half of K
+        floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s2 = kh * (KS1 / 2); s2 < (kh + 1) * (KS1 / 2); ++s2) {
+            const float av = sD[col * GS + 4 * s2 + q];
+            const float bv = sG2[(16 * nt1 + col) * GS + 4 * s2 + q];
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
+        }
+        if (kh == 1) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sRed[nt1][lane][v] = acc1[v];
+        }
+        __syncthreads();
+        if (kh == 0 && q < ng) {
+            // lane holds rows 4q+v = (group q, j1 v), column r1 = 16*nt1 + col
+            float* dst = dg1 + d.o1 + (int64_t)sI1[q] * N1 * R + 16 * nt1 + col;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, acc1[v] + sRed[nt1][lane][v]);
+        }
+    }
+    // dG2[i2] is owned by this workgroup: plain stores (zeros when no group)
+    float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                D2[(16 * rt + 4 * q + v) * N2R + 16 * (w * NTW + j) + col] = acc2[rt][j][v];
+}
+
+template <int N1, int N2, int R, int N3>
+static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
+                                 const float* g3, const float* gout, float* dg1, float* dg2,
+                                 float* dg3, hipStream_t s) {
+    constexpr int PR = N1 * N2 * R;
+    if (!p->packed) {
+        tt_status st = fill32(dg2, 0u, p->extent[1], s);
+        if (st != TT_OK) return st;
+    }
+    hipLaunchKernelGGL(k_bwd_prep, dim3(1024), dim3(256), 0, s, dg1, p->extent[0], dg3, p->extent[2],
+                       p->at<float>(p->lay.dpg), PR, p->at<int32_t>(p->lay.group_cbase), p->ctrl());
+    TT_LAUNCH_CHECK();
+    if (p->lay.Cmax > 0) {
+        BwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
+                  p->at<int32_t>(p->lay.group_cbase), p->at<int32_t>(p->lay.chunk_group),
+                  p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_end),
+                  p->at<int32_t>(p->lay.sorted_i3), p->at<int32_t>(p->lay.sorted_bag),
+                  p->at<uint8_t>(p->lay.run_head), g1, g2, g3, gout, dg1, dg3,
+                  p->at<float>(p->lay.dpg)};
+        hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(grid_for(p->lay.Cmax, 4)), dim3(256), 0,
+                           s, a);
+        TT_LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)p->n_i2), dim3(256), 0, s,
+                       p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+                       p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, dg1,
+                       dg2);
+    TT_LAUNCH_CHECK();
+    return TT_OK;
+}
+
+static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
+                         const float* gout, float* dg1, float* dg2, float* dg3, hipStream_t s,
+                         tt_status* st) {
+    if (!p->uniform) return false;
+    const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
+    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
+    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
+    return false;
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -112,7 +462,8 @@ extern "C" tt_status tt_emb_backward(tt_emb_plan_t p, const float* g1, const flo
     if (!p || !g1 || !g2 || !g3 || !dg1 || !dg2 || !dg3 || (!grad_out && p->TB > 0))
         return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    tt_status st;
+    tt_status st = TT_OK;
+    if (try_bwd_mfma(p, g1, g2, g3, grad_out, dg1, dg2, dg3, s, &st)) return st;
     if ((st = fill32(dg1, 0u, p->extent[0], s)) != TT_OK) return st;
     if ((st = fill32(dg2, 0u, p->extent[1], s)) != TT_OK) return st;
     if ((st = fill32(dg3, 0u, p->extent[2], s)) != TT_OK) return st;

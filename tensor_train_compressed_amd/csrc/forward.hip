@@ -8,18 +8,9 @@
 // grouping and flow-aligned on-chip execution; problem statement: the shared
 // part of the chain is otherwise recomputed and intermediates round-trip
 // through off-chip memory).
-#include "tt_internal.h"
+#include "tt_device.h"
 
 namespace tt {
-
-__device__ __forceinline__ int find_table(const TabDev* __restrict__ desc, int32_t T, int32_t key) {
-    int lo = 0, hi = T;  // last t with key_base <= key
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (desc[mid].key_base <= key) lo = mid; else hi = mid;
-    }
-    return lo;
-}
 
 // Generic shapes: one workgroup per chunk. P lives in LDS; each thread forms
 // output elements of the chunk's lookups and adds them to the bag's row.
@@ -70,16 +61,15 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 //
 // One wave per chunk. The prefix P = G1[i1] x G2[i2] is formed once per chunk
 // (VALU, into LDS) and held in registers as the A operand of
-// v_mfma_f32_16x16x4_f32 for the whole chunk. A tile is 16 output columns =
-// (16/n3 lookups) x (n3 columns of G3), so a chunk of any length wastes at most
-// 16/n3 - 1 lookup slots. Rows leave the matrix cores through LDS, are summed
-// along runs of equal bag (lookups of one bag are adjacent inside a group), and
-// every run is written once, as a whole row, to its slot in the stage buffer
-// (the slot of the run's first lookup). k_pool then adds each bag's runs in
-// input order and writes the bag's output row: no atomics, and the same bits
-// on every run.
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+// v_mfma_f32_16x16x4_f32 for the whole chunk. Inside a group the planner has
+// put repeats of one table row next to each other, so the chunk is a list of
+// runs, one per distinct row; the last contraction P x G3[i3] is done once per
+// run. A tile is 16 output columns = (16/n3 runs) x (n3 columns of G3), so a
+// chunk wastes at most 16/n3 - 1 run slots. Each run's row leaves the matrix
+// cores through LDS and is written once, as a whole row, to the stage buffer
+// at the run's first sorted position; every lookup records that position in
+// row_of. k_pool then sums each bag's rows in input order and writes the
+// bag's output row: no atomics, and the same bits on every run.
 
 struct FwdArgs {
     const TabDev* desc;
@@ -90,21 +80,14 @@ struct FwdArgs {
     const int32_t* chunk_begin;
     const int32_t* chunk_end;
     const int32_t* sorted_i3;
-    const int32_t* sorted_bag;
     const int32_t* perm;
+    const uint8_t* run_head;
     const float* g1;
     const float* g2;
     const float* g3;
     float* stage;
+    int32_t* row_of;
 };
-
-// Orders this wave's LDS writes before its later LDS reads (LDS executes a
-// wave's operations in order; this keeps the compiler from moving them).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 template <int N1, int N2, int R, int N3>
 struct FwdShape {
@@ -112,25 +95,27 @@ struct FwdShape {
     static constexpr int D = NP * N3;       // output width
     static constexpr int KS = R / 4;        // k-steps of 16x16x4 per tile
     static constexpr int MT = NP / 16;      // 16-row blocks of P
-    static constexpr int LK = 16 / N3;      // lookups per tile
+    static constexpr int LK = 16 / N3;      // runs per tile
     static constexpr int TPB = 4;           // tiles per batch
-    static constexpr int BL = LK * TPB;     // lookups per batch
+    static constexpr int BL = LK * TPB;     // runs per batch
     static constexpr int RS = D + 4;        // LDS row stride (floats)
-    static constexpr int HG = 64 / R;       // lanes groups sharing an r2 in the P build
+    static constexpr int HG = 64 / R;       // lane groups sharing an r2 in the P build
     static constexpr int PE = NP * R / 64;  // P elements per lane
     static constexpr int DL = D / 64;       // output floats per lane
     static_assert(NP % 16 == 0 && R % 4 == 0 && 16 % N3 == 0 && D % 64 == 0, "shape");
-    static_assert(64 % R == 0 && N2 % HG == 0 && DL <= 4, "shape");
+    static_assert(64 % R == 0 && N2 % HG == 0 && DL <= 4 && BL <= 64, "shape");
 };
 
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
     using S = FwdShape<N1, N2, R, N3>;
     constexpr int NP = S::NP, D = S::D, KS = S::KS, MT = S::MT, LK = S::LK, TPB = S::TPB;
-    constexpr int BL = S::BL, RS = S::RS, HG = S::HG, PE = S::PE, DL = S::DL;
+    constexpr int BL = S::BL, RS = S::RS, DL = S::DL;
     __shared__ float sP[4][NP * R];
     __shared__ float sRow[4][BL * RS];
     __shared__ float sG1[4][N1 * R];
+    __shared__ int32_t sHead[4][64];
+    __shared__ int32_t sHeadI3[4][64];
 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int32_t c = (int32_t)blockIdx.x * 4 + w;
@@ -141,33 +126,8 @@ __global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
     const TabDev d = a.desc[find_table(a.desc, a.T, key)];
     const int32_t local = key - d.key_base;
     const int32_t i2 = local / d.m1, i1 = local % d.m1;
-
-    // ---- prefix P[p][r2] = sum_r1 G1[i1][j1][r1] G2[i2][r1][j2][r2], p = j1*N2 + j2
-    {
-        const float* A = a.g1 + d.o1 + (int64_t)i1 * N1 * R;
-        for (int e = lane; e < N1 * R; e += 64) sG1[w][e] = A[e];
-        wave_lds_sync();
-        const float* Bc = a.g2 + d.o2 + (int64_t)i2 * R * N2 * R;
-        const int r2 = lane % R, h = lane / R;
-        constexpr int J2N = N2 / HG;   // distinct j2 per lane
-        float acc[PE];
-#pragma unroll
-        for (int k = 0; k < PE; ++k) acc[k] = 0.f;
-#pragma unroll 4
-        for (int r1 = 0; r1 < R; ++r1) {
-            float b2[J2N];
-#pragma unroll
-            for (int jj = 0; jj < J2N; ++jj) b2[jj] = Bc[(r1 * N2 + h + HG * jj) * R + r2];
-#pragma unroll
-            for (int k = 0; k < PE; ++k) {
-                // p = h + HG*k  ->  j2 = h + HG*(k % J2N), j1 = k / J2N
-                acc[k] = fmaf(sG1[w][(k / J2N) * R + r1], b2[k % J2N], acc[k]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < PE; ++k) sP[w][(h + HG * k) * R + r2] = acc[k];
-        wave_lds_sync();
-    }
+    build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
+                            a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
     // A operand: lane (i = lane%16, q = lane/16) holds P[16*mt + i][KS*q + s]
     float afr[MT][KS];
     {
@@ -182,74 +142,68 @@ __global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
     const float* G3 = a.g3 + d.o3;
     const int col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
+    const uint64_t below_eq = (lane == 63) ? ~0ull : ((2ull << lane) - 1);
+    int32_t carried = s0;   // head of the run that continues into the next batch
 
-    bool have = false;
-    int32_t rbag = -1, rhead = 0;
-    float racc[DL];
-#pragma unroll
-    for (int k = 0; k < DL; ++k) racc[k] = 0.f;
-
-    for (int32_t sb = s0; sb < s1; sb += BL) {
-        const int nb = min(BL, s1 - sb);
-        // bag and original position of the batch's lookups, lane r holds row r
-        int32_t bagv = 0, permv = 0;
-        if (lane < nb) {
-            bagv = a.sorted_bag[sb + lane];
-            permv = a.perm[sb + lane];
+    for (int32_t sb = s0; sb < s1; sb += 64) {
+        const int32_t sl = sb + lane;
+        const bool valid = sl < s1;
+        const bool head = valid && (a.run_head[sl] != 0);
+        const uint64_t m = __ballot(head);
+        // every lookup records its run head
+        if (valid) {
+            const uint64_t le = m & below_eq;
+            const int32_t hp = le ? sb + 63 - __builtin_clzll(le) : carried;
+            a.row_of[a.perm[sl]] = hp;
         }
-#pragma unroll
-        for (int t = 0; t < TPB; ++t) {
-            const int32_t sl = sb + t * LK + lk;
-            const int32_t i3 = (sl < s1) ? a.sorted_i3[sl] : 0;
-            const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
-            float bv[KS];
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2)
-                    cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
-                // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
-                const int rr = t * LK + lk;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
-            }
+        if (head) {
+            const int rk = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            sHead[w][rk] = sl;
+            sHeadI3[w][rk] = a.sorted_i3[sl];
         }
+        if (m) carried = sb + 63 - __builtin_clzll(m);
         wave_lds_sync();
-        for (int r = 0; r < nb; ++r) {
-            const int32_t bag = __builtin_amdgcn_readlane(bagv, r);
-            if (have && bag != rbag) {
-                float* dst = a.stage + (int64_t)rhead * D + lane * DL;
+        const int nh = __popcll(m);
+        for (int r0 = 0; r0 < nh; r0 += BL) {
+            const int nr = min(BL, nh - r0);
 #pragma unroll
-                for (int k = 0; k < DL; ++k) dst[k] = racc[k];
-                have = false;
+            for (int t = 0; t < TPB; ++t) {
+                const int ri = r0 + t * LK + lk;
+                const int32_t i3 = (ri < nh) ? sHeadI3[w][ri] : 0;
+                const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
+                float bv[KS];
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2)
+                        cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
+                    // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
+                    const int rr = t * LK + lk;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
+                }
             }
-            if (!have) {
-                have = true;
-                rbag = bag;
-                rhead = __builtin_amdgcn_readlane(permv, r);
+            wave_lds_sync();
+            for (int r = 0; r < nr; ++r) {
+                const int32_t hs = sHead[w][r0 + r];
+                float* dst = a.stage + (int64_t)hs * D + lane * DL;
 #pragma unroll
-                for (int k = 0; k < DL; ++k) racc[k] = 0.f;
+                for (int k = 0; k < DL; ++k) dst[k] = sRow[w][r * RS + lane * DL + k];
             }
-#pragma unroll
-            for (int k = 0; k < DL; ++k) racc[k] += sRow[w][r * RS + lane * DL + k];
+            wave_lds_sync();
         }
-        wave_lds_sync();
-    }
-    if (have) {
-        float* dst = a.stage + (int64_t)rhead * D + lane * DL;
-#pragma unroll
-        for (int k = 0; k < DL; ++k) dst[k] = racc[k];
     }
 }
 
-// One wave per bag: sum the bag's run rows (run heads in input order) and write
-// the bag's output row. Empty bags get zeros.
+// One wave per bag: sum the rows of the bag's lookups (in input order) from
+// the stage buffer and write the bag's output row. Empty bags get zeros.
 template <int DL>
 __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
-                                              const uint8_t* __restrict__ run_head,
+                                              const int32_t* __restrict__ row_of,
                                               const float* __restrict__ stage,
                                               float* __restrict__ out) {
     constexpr int D = 64 * DL;
@@ -262,12 +216,11 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 #pragma unroll
     for (int k = 0; k < DL; ++k) acc[k] = 0.f;
     for (int32_t base = b0; base < b1; base += 64) {
-        const int32_t l = base + lane;
-        uint64_t m = __ballot(l < b1 && run_head[l] != 0);
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1;
-            const float* src = stage + (int64_t)(base + j) * D + lane * DL;
+        const int n = min(64, b1 - base);
+        const int32_t rv = (lane < n) ? row_of[base + lane] : 0;
+        for (int j = 0; j < n; ++j) {
+            const int32_t slot = __builtin_amdgcn_readlane(rv, j);
+            const float* src = stage + (int64_t)slot * D + lane * DL;
 #pragma unroll
             for (int k = 0; k < DL; ++k) acc[k] += src[k];
         }
@@ -283,8 +236,8 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     FwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
               p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
               p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
-              p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.perm), g1, g2, g3,
-              p->at<float>(p->lay.stage)};
+              p->at<int32_t>(p->lay.perm), p->at<uint8_t>(p->lay.run_head), g1, g2, g3,
+              p->at<float>(p->lay.stage), p->at<int32_t>(p->lay.row_of)};
     if (p->lay.Cmax > 0) {
         hipLaunchKernelGGL((k_fwd_mfma<N1, N2, R, N3>), dim3(grid_for(p->lay.Cmax, 4)), dim3(256), 0,
                            s, a);
@@ -293,7 +246,7 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     constexpr int DL = FwdShape<N1, N2, R, N3>::DL;
     if (p->TB > 0) {
         hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
-                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<uint8_t>(p->lay.run_head),
+                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.row_of),
                            p->at<float>(p->lay.stage), out);
         TT_LAUNCH_CHECK();
     }

@@ -9,15 +9,16 @@
 // lookups share a group; the order and chunk shape used here are this
 // library's (see include/tt_emb.h): groups are ordered by key
 // base_t + i2*m1 + i1, so that groups that read the same G2 slice are
-// adjacent, and lookups keep their input order inside a group.
+// adjacent; inside a group lookups are ordered by i3 (ties in input order), so
+// repeats of one table row are adjacent and that row is contracted once.
 //
 // Kernels, in stream order:
 //   k_write_desc      table descriptors into the workspace
 //   k_split           offsets check, bag search, digit split, prefix key
-//   k_radix_hist      \  stable LSD radix sort of the keys, 8 bits per pass:
+//   k_radix_hist      \  stable LSD radix sort of key*M3 + i3, 8 bits per pass:
 //   scan (1 or 3)      | per-tile digit counts, one exclusive scan over
 //   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
-//   k_gather          sorted i3 / bag, first and last position of each key
+//   k_gather          sorted i3 / bag, run heads, first and last position of each key
 //   k_key_flags       per key: present flag and chunk count
 //   scan              group id and first chunk of every present key
 //   k_groups          group tables, counts into the control words
@@ -32,7 +33,8 @@ namespace tt {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D) {
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
+                   int64_t M3, int64_t PR) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -41,14 +43,16 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.Gmax = std::min<int64_t>(L, K);
     y.Cmax = L == 0 ? 0 : std::min<int64_t>(L, y.Gmax + (L + chunk - 1) / chunk);
     int bits = 0;
-    while ((int64_t(1) << bits) < K) ++bits;
+    while ((int64_t(1) << bits) < K * M3) ++bits;
     y.passes = std::max(1, (bits + kRadixBits - 1) / kRadixBits);
     y.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
     y.desc = take(sizeof(TabDev) * (size_t)T);
     const size_t l4 = sizeof(int32_t) * (size_t)L;
     y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
+    y.ckey = take(l4);
     y.bag_start = take(sizeof(int32_t) * (size_t)((int64_t)T * B + 1));
     y.run_head = take((size_t)L);
+    y.row_of = take(l4);
     y.stage = take(sizeof(float) * (size_t)L * (size_t)D);
     y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
     y.skey = take(l4);
@@ -69,6 +73,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
     const int64_t nscan = std::max<int64_t>(nhist, K);
     y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
+    // dL/dP per group, only for shapes the matrix-core backward serves
+    y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.total = off;
     return y;
 }
@@ -124,7 +130,9 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
                                                const TabDev* __restrict__ desc,
                                                int32_t* __restrict__ key, int32_t* __restrict__ i3o,
                                                int32_t* __restrict__ bag_of,
-                                               int32_t* __restrict__ bag_start, int32_t* ctrl) {
+                                               int32_t* __restrict__ bag_start,
+                                               int32_t* __restrict__ ckey, int32_t M3,
+                                               int32_t* ctrl) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i <= TB) {
         const int64_t a = off[i];
@@ -151,7 +159,9 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
     const uint32_t p = xi / (uint32_t)d.m3;
     const uint32_t r2 = p % (uint32_t)d.m2;
     const uint32_t r1 = p / (uint32_t)d.m2;
-    key[i] = d.key_base + (int32_t)(r2 * (uint32_t)d.m1 + r1);
+    const int32_t k = d.key_base + (int32_t)(r2 * (uint32_t)d.m1 + r1);
+    key[i] = k;
+    ckey[i] = k * M3 + (int32_t)r3;
     i3o[i] = (int32_t)r3;
     bag_of[i] = (int32_t)q;
 }
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
                                                 const int32_t* __restrict__ skey,
                                                 const int32_t* __restrict__ i3,
                                                 const int32_t* __restrict__ bag_of, int64_t L,
-                                                int32_t* __restrict__ sorted_i3,
+                                                int32_t M3, int32_t* __restrict__ sorted_i3,
                                                 int32_t* __restrict__ sorted_bag,
                                                 int32_t* __restrict__ key_start,
                                                 int32_t* __restrict__ key_end,
@@ -353,15 +363,15 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
     const int32_t l = perm[s];
-    const int32_t k = skey[s];
-    const int32_t b = bag_of[l];
+    const int32_t ck = skey[s];
+    const int32_t k = ck / M3;
     sorted_i3[s] = i3[l];
-    sorted_bag[s] = b;
-    // a run is a maximal stretch of one key and one bag in sorted order (chunk
-    // starts also open a run; k_chunks marks those)
-    run_head[l] = (s == 0 || skey[s - 1] != k || bag_of[perm[s - 1]] != b) ? 1 : 0;
-    if (s == 0 || skey[s - 1] != k) key_start[k] = (int32_t)s;
-    if (s == L - 1 || skey[s + 1] != k) key_end[k] = (int32_t)(s + 1);
+    sorted_bag[s] = bag_of[l];
+    // a run is a maximal stretch of one (key, i3) row in sorted order; chunk
+    // starts also open a run (k_chunks marks those)
+    run_head[s] = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
+    if (s == 0 || skey[s - 1] / M3 != k) key_start[k] = (int32_t)s;
+    if (s == L - 1 || skey[s + 1] / M3 != k) key_end[k] = (int32_t)(s + 1);
 }
 
 __global__ __launch_bounds__(256) void k_key_flags(const int32_t* __restrict__ key_start,
@@ -408,7 +418,6 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
                                                 int32_t* __restrict__ chunk_group,
                                                 int32_t* __restrict__ chunk_begin,
                                                 int32_t* __restrict__ chunk_end,
-                                                const int32_t* __restrict__ perm,
                                                 uint8_t* __restrict__ run_head) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     chunk_group[c] = g;
     chunk_begin[c] = b;
     chunk_end[c] = min(b + chunk, group_start[g + 1]);
-    run_head[perm[b]] = 1;
+    run_head[b] = 1;
 }
 
 }  // namespace tt
@@ -434,11 +443,12 @@ using namespace tt;
 // ---------------------------------------------------------------------------
 // host side
 
-static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out) {
+static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
+                              int32_t* M3_out, int64_t* PR_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
-    int64_t K = 0;
-    int32_t D = -1;
+    int64_t K = 0, PR = 1;
+    int32_t D = -1, M3 = 1;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
         if (x.reserved != 0) return TT_ERR_INVALID_ARG;
@@ -455,9 +465,14 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         D = (int32_t)d;
         K += (int64_t)x.m[0] * x.m[1];
         if (K >= kMaxKeys) return TT_ERR_UNSUPPORTED;
+        M3 = std::max(M3, x.m[2]);
+        PR = std::max<int64_t>(PR, (int64_t)x.n[0] * x.n[1] * x.rank);
     }
+    if (K * M3 >= (int64_t(1) << 31)) return TT_ERR_UNSUPPORTED;
     *K_out = K;
     *D_out = D;
+    *M3_out = M3;
+    *PR_out = PR;
     return TT_OK;
 }
 
@@ -471,11 +486,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 
 extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
                                          int64_t B, int32_t chunk) {
-    int64_t K = 0;
-    int32_t D = 0;
-    if (check_tables(tables, T, &K, &D) != TT_OK) return 0;
+    int64_t K = 0, PR = 1;
+    int32_t D = 0, M3 = 1;
+    if (check_tables(tables, T, &K, &D, &M3, &PR) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -484,40 +499,47 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                  tt_emb_plan_t* plan_out) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
-    int64_t K = 0;
-    int32_t D = 0;
-    tt_status st = check_tables(tables, T, &K, &D);
+    int64_t K = 0, PR = 1;
+    int32_t D = 0, M3 = 1;
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
     if (!p) return TT_ERR_INVALID_ARG;
     p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;
+    p->M3 = M3;
+    p->n_i2 = 0;
+    for (int32_t t = 0; t < T; ++t) p->n_i2 += tables[t].m[1];
     p->ws = (char*)workspace;
     p->lay = lay;
     p->tables.assign(tables, tables + T);
     p->uniform = true;
     p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
     for (int k = 0; k < 3; ++k) p->extent[k] = 0;
+    p->packed = true;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
         if (x.n[0] != p->n1 || x.n[1] != p->n2 || x.n[2] != p->n3 || x.rank != p->R) p->uniform = false;
         const int64_t R = x.rank;
         const int64_t sz[3] = {(int64_t)x.m[0] * x.n[0] * R, (int64_t)x.m[1] * R * x.n[1] * R,
                                (int64_t)x.m[2] * R * x.n[2]};
-        for (int k = 0; k < 3; ++k) p->extent[k] = std::max(p->extent[k], x.g_offset[k] + sz[k]);
+        for (int k = 0; k < 3; ++k) {
+            if (x.g_offset[k] != p->extent[k]) p->packed = false;
+            p->extent[k] = std::max(p->extent[k], x.g_offset[k] + sz[k]);
+        }
     }
     hipStream_t s = (hipStream_t)stream;
 
     auto fail = [&](tt_status e) { delete p; return e; };
     // control words and descriptors
     if (fill32(p->ctrl(), 0u, CTRL_WORDS, s) != TT_OK) return fail(TT_ERR_HIP);
-    int32_t kb = 0;
+    int32_t kb = 0, i2b = 0;
     for (int32_t first = 0; first < T; first += 16) {
         DescBatch b{};
         b.first = first;
@@ -530,8 +552,9 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             d.n1 = x.n[0]; d.n2 = x.n[1]; d.n3 = x.n[2]; d.R = x.rank;
             d.o1 = x.g_offset[0]; d.o2 = x.g_offset[1]; d.o3 = x.g_offset[2];
             d.key_base = kb;
-            d.key_count = x.m[0] * x.m[1];
-            kb += d.key_count;
+            d.i2_base = i2b;
+            i2b += x.m[1];
+            kb += x.m[0] * x.m[1];
         }
         hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
@@ -546,7 +569,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         const int64_t n = std::max<int64_t>(L, p->TB + 1);
         hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
                            p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
-                           p->at<int32_t>(lay.bag_start), ctrl);
+                           p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
+                           ctrl);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
     }
     // stable radix sort: key -> (skey, perm)
@@ -554,7 +578,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         const int P = lay.passes;
         uint32_t* hist = p->at<uint32_t>(lay.hist);
         uint64_t* part = p->at<uint64_t>(lay.scan_tmp);
-        const int32_t* kin = key;
+        const int32_t* kin = p->at<int32_t>(lay.ckey);
         const int32_t* vin = nullptr;
         for (int pass = 0; pass < P; ++pass) {
             // the last pass lands in (skey, perm); earlier passes alternate so that it does
@@ -584,7 +608,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         if (L > 0) {
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
-                               p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
+                               p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
                                key_start, key_end, p->at<uint8_t>(lay.run_head));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
@@ -603,7 +627,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<int32_t>(lay.perm), p->at<uint8_t>(lay.run_head));
+                               p->at<uint8_t>(lay.run_head));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

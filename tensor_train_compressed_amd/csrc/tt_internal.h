@@ -19,7 +19,7 @@ struct alignas(16) TabDev {
     int32_t n1, n2, n3, R;      // dim factors and rank
     int64_t o1, o2, o3;         // element offsets of this table's G1/G2/G3
     int32_t key_base;           // first prefix key of this table
-    int32_t key_count;          // m1*m2
+    int32_t i2_base;            // first (table, i2) slice index of this table
 };
 static_assert(sizeof(TabDev) == 64, "TabDev layout");
 
@@ -55,8 +55,11 @@ constexpr int64_t kMaxKeys = int64_t(1) << 30;
 struct Layout {
     size_t ctrl, desc;
     size_t key, i3, bag_of;                  // [L]
+    size_t ckey;                             // [L] sort key = key * M3 + i3
     size_t bag_start;                        // [TB+1] int32 copy of the offsets
-    size_t run_head;                         // [L] uint8: lookup starts a (chunk, bag) run
+    size_t run_head;                         // [L] uint8, sorted order: position starts a run
+                                             //     (a new (key, i3) row, or a chunk start)
+    size_t row_of;                           // [L] int32: sorted position of the lookup's run head
     size_t stage;                            // [L][D] float: one row per run, at its head
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
@@ -66,12 +69,14 @@ struct Layout {
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
     size_t scan_tmp;                         // uint64 partials of the multi-block scan
+    size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
     size_t total;
     int64_t n_tiles, K, Gmax, Cmax;
     int passes;
 };
 
-Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D);
+Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
+                   int64_t M3, int64_t PR);
 
 }  // namespace tt
 
@@ -82,9 +87,12 @@ struct tt_emb_plan_s {
     int32_t chunk;
     int32_t D;
     int64_t K;
+    int32_t M3;               // largest m3 over the tables
+    int64_t n_i2;             // sum over tables of m2 (number of (table, i2) slices)
     bool uniform;             // all tables share (n1, n2, n3, R)
     int32_t n1, n2, n3, R;    // the shared shape when uniform
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
+    bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
     char* ws;                 // workspace base (device)
     tt::Layout lay;
     std::vector<tt_emb_table> tables;
