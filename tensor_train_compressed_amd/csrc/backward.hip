@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 struct BwdArgs {
     const TabDev* desc;
     int32_t T;
-    const int32_t* ctrl;
+    int32_t* ctrl;
+    const int32_t* task_start;
     const int32_t* group_key;
     const int32_t* group_cbase;
     const int32_t* chunk_group;
@@ -173,160 +174,191 @@ __global__ __launch_bounds__(256) void k_bwd_runs(BwdArgs a) {
     using S = BwdShape<N1, N2, R, N3>;
     constexpr int NP = S::NP, D = S::D, PR = S::PR, MT = S::MT, RT = S::RT, KSP = S::KSP;
     constexpr int LK = S::LK, RB = S::RB, RS = S::RS, CN = S::CN, CS = S::CS, DL = S::DL, CL = S::CL;
-    __shared__ float sP[4][PR];
+    __shared__ __attribute__((aligned(16))) float sP[4][PR];
     __shared__ float sG1[4][N1 * R];
     __shared__ float sS[4][RB * RS];
     __shared__ float sC[4][LK * CS];
     __shared__ int32_t sI3[4][RB];
 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int32_t c = (int32_t)blockIdx.x * 4 + w;
-    if (c >= a.ctrl[CTRL_NUM_CHUNKS]) return;
-
-    const int32_t g = a.chunk_group[c];
-    const bool multi = (a.group_cbase[g + 1] - a.group_cbase[g]) > 1;
-    const int32_t key = a.group_key[g];
-    const TabDev d = a.desc[find_table(a.desc, a.T, key)];
-    const int32_t local = key - d.key_base;
-    const int32_t i2 = local / d.m1, i1 = local % d.m1;
-    build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
-                            a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
     const int col = lane & 15, q = lane >> 4;
-    // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
-    float afT[RT][KSP];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[w][(KSP * q + s2) * R + 16 * rt + col];
+    TaskQueues tq = make_queues(a.ctrl, 1);
 
+    int32_t cur_g = -1;
+    bool multi = false;
+    TabDev d{};
+    float afT[RT][KSP];
     floatx4 dacc[MT][RT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const float* G3 = a.g3 + d.o3;
-    float* dG3 = a.dg3 + d.o3;
-    int nrun = 0;
-    bool have = false;
-    int32_t cur_i3 = 0;
-    float sacc[DL];
+    // dP of the current group -> its dL/dP row, [p][r2] (atomics when the
+    // group is cut into several chunks, which other waves may hold)
+    auto flush_dp = [&]() {
+        float* dst = a.dpg + (int64_t)cur_g * PR;
 #pragma unroll
-    for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
-
-    // matrix-core pass over the nrun buffered runs
-    auto flush = [&]() {
-        wave_lds_sync();
-        // dG3[i3] += P^T S: tiles of LK runs x N3 columns
-        for (int t0 = 0; t0 < nrun; t0 += LK) {
-            const int lk = col / N3, j3 = col % N3;
-            float bv[KSP];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = sS[w][(t0 + lk) * RS + (KSP * q + s2) * N3 + j3];
+            for (int nt = 0; nt < RT; ++nt) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                floatx4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s2 = 0; s2 < KSP; ++s2)
-                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], bv[s2], cc, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) sC[w][lk * CS + (16 * rt + 4 * q + v) * N3 + j3] = cc[v];
+                for (int v = 0; v < 4; ++v) {
+                    float* e = dst + (16 * mt + 4 * q + v) * R + 16 * nt + col;
+                    if (multi) atomicAdd(e, dacc[mt][nt][v]);
+                    else *e = dacc[mt][nt][v];
+                }
+                dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
-            wave_lds_sync();
-            const int nr = min(LK, nrun - t0);
-            for (int r = 0; r < nr; ++r) {
-                float* dst = dG3 + (int64_t)sI3[w][t0 + r] * CN + lane * CL;
-#pragma unroll
-                for (int k = 0; k < CL; ++k) atomicAdd(dst + k, sC[w][r * CS + lane * CL + k]);
-            }
-            wave_lds_sync();
-        }
-        // dP += S G3[i3]^T: one k-step per run (k = j3)
-        for (int r = 0; r < nrun; ++r) {
-            const float* gb = G3 + (int64_t)sI3[w][r] * CN;
-            float av[MT], bv[RT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) av[mt] = sS[w][r * RS + (16 * mt + col) * N3 + q];
-#pragma unroll
-            for (int nt = 0; nt < RT; ++nt) bv[nt] = gb[(16 * nt + col) * N3 + q];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt)
-                    dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], dacc[mt][nt], 0, 0, 0);
-        }
-        wave_lds_sync();
-        nrun = 0;
-    };
-    auto finish_run = [&]() {
-#pragma unroll
-        for (int k = 0; k < DL; ++k) sS[w][nrun * RS + lane * DL + k] = sacc[k];
-        if (lane == 0) sI3[w][nrun] = cur_i3;
-        ++nrun;
-        if (nrun == RB) flush();
     };
 
-    const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
-    for (int32_t sb = s0; sb < s1; sb += 64) {
-        const int n = min(64, s1 - sb);
-        const int32_t sl = sb + lane;
-        const bool valid = lane < n;
-        const uint64_t m = __ballot(valid && a.run_head[sl] != 0);
-        const int32_t bagv = valid ? a.sorted_bag[sl] : 0;
-        const int32_t i3v = valid ? a.sorted_i3[sl] : 0;
-        for (int r = 0; r < n; ++r) {
-            if ((m >> r) & 1ull) {
-                if (have) finish_run();
-                have = true;
-                cur_i3 = __builtin_amdgcn_readlane(i3v, r);
+    for (int32_t t = next_task(tq); t >= 0; t = next_task(tq)) {
+        const int32_t cA = a.task_start[t], cB = a.task_start[t + 1];
+        for (int32_t c = cA; c < cB; ++c) {
+            const int32_t g = a.chunk_group[c];
+            if (g != cur_g) {
+                if (cur_g >= 0) flush_dp();
+                cur_g = g;
+                multi = (a.group_cbase[g + 1] - a.group_cbase[g]) > 1;
+                const int32_t key = a.group_key[g];
+                d = a.desc[find_table(a.desc, a.T, key)];
+                const int32_t local = key - d.key_base;
+                const int32_t i2 = local / d.m1, i1 = local % d.m1;
+                build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
+                                        a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
+                // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
 #pragma unroll
-                for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[w][(KSP * q + s2) * R + 16 * rt + col];
             }
-            const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, r) * D + lane * DL;
+            const float* G3 = a.g3 + d.o3;
+            float* dG3 = a.dg3 + d.o3;
+            int nrun = 0;
+            bool have = false;
+            int32_t cur_i3 = 0;
+            float sacc[DL];
 #pragma unroll
-            for (int k = 0; k < DL; ++k) sacc[k] += row[k];
+            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+
+            // matrix-core pass over the nrun buffered runs
+            auto flush = [&]() {
+                wave_lds_sync();
+                // dG3[i3] += P^T S: tiles of LK runs x N3 columns
+                for (int t0 = 0; t0 < nrun; t0 += LK) {
+                    const int lk = col / N3, j3 = col % N3;
+                    float bv[KSP];
+#pragma unroll
+                    for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = sS[w][(t0 + lk) * RS + (KSP * q + s2) * N3 + j3];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        floatx4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < KSP; ++s2)
+                            cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], bv[s2], cc, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) sC[w][lk * CS + (16 * rt + 4 * q + v) * N3 + j3] = cc[v];
+                    }
+                    wave_lds_sync();
+                    const int nr = min(LK, nrun - t0);
+                    for (int r = 0; r < nr; ++r) {
+                        float* dst = dG3 + (int64_t)sI3[w][t0 + r] * CN + lane * CL;
+#pragma unroll
+                        for (int k = 0; k < CL; ++k) atomicAdd(dst + k, sC[w][r * CS + lane * CL + k]);
+                    }
+                    wave_lds_sync();
+                }
+                // dP += S G3[i3]^T: one k-step per run (k = j3)
+                for (int r = 0; r < nrun; ++r) {
+                    const float* gb = G3 + (int64_t)sI3[w][r] * CN;
+                    float av[MT], bv[RT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) av[mt] = sS[w][r * RS + (16 * mt + col) * N3 + q];
+#pragma unroll
+                    for (int nt = 0; nt < RT; ++nt) bv[nt] = gb[(16 * nt + col) * N3 + q];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < RT; ++nt)
+                            dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], dacc[mt][nt], 0, 0, 0);
+                }
+                wave_lds_sync();
+                nrun = 0;
+            };
+            auto finish_run = [&]() {
+#pragma unroll
+                for (int k = 0; k < DL; ++k) sS[w][nrun * RS + lane * DL + k] = sacc[k];
+                if (lane == 0) sI3[w][nrun] = cur_i3;
+                ++nrun;
+                if (nrun == RB) flush();
+            };
+
+            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
+            for (int32_t sb = s0; sb < s1; sb += 64) {
+                const int n = min(64, s1 - sb);
+                const int32_t sl = sb + lane;
+                const bool valid = lane < n;
+                const uint64_t m = __ballot(valid && a.run_head[sl] != 0);
+                const int32_t bagv = valid ? a.sorted_bag[sl] : a.sorted_bag[sb];
+                const int32_t i3v = valid ? a.sorted_i3[sl] : 0;
+                // grad_out rows of 8 positions in flight, then walk them in order
+                for (int r0 = 0; r0 < n; r0 += 8) {
+                    float v[8][DL];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) v[u][k] = row[k];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = r0 + u;
+                        if (r >= n) break;
+                        if ((m >> r) & 1ull) {
+                            if (have) finish_run();
+                            have = true;
+                            cur_i3 = __builtin_amdgcn_readlane(i3v, r);
+#pragma unroll
+                            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+                        }
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) sacc[k] += v[u][k];
+                    }
+                }
+            }
+            if (have) finish_run();
+            if (nrun > 0) flush();
         }
     }
-    if (have) finish_run();
-    if (nrun > 0) flush();
-
-    // dP of this chunk -> the group's dL/dP row, [p][r2]
-    float* dst = a.dpg + (int64_t)g * PR;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < RT; ++nt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float* e = dst + (16 * mt + 4 * q + v) * R + 16 * nt + col;
-                if (multi) atomicAdd(e, dacc[mt][nt][v]);
-                else *e = dacc[mt][nt][v];
-            }
+    if (cur_g >= 0) flush_dp();
 }
 
+// One workgroup per ((table, i2) slice, 64-column block of the N2*R columns).
+// Groups of the slice are taken eight at a time (a slab); wave w owns
+//   dG2 tiles (r1 block w & 1) x (column blocks 2*(w >> 1), +1), K = j1 per group
+//   dG1 tile  (groups 4*(w >> 1)..+3 x j1) x (r1 block w & 1), K = the 64 columns
+// so dG2 needs no reduction and dG1 only atomics across column blocks.
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
-                                                    const int32_t* __restrict__ ctrl, int64_t K,
+                                                    int32_t* ctrl, int64_t K,
                                                     const uint64_t* __restrict__ key_scan,
                                                     const int32_t* __restrict__ group_key,
                                                     const float* __restrict__ dpg,
                                                     const float* __restrict__ g1,
                                                     const float* __restrict__ g2,
                                                     float* __restrict__ dg1, float* __restrict__ dg2) {
-    constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, RT = R / 16;
-    constexpr int NTN = N2R / 16;           // 16-col tiles of dG2
-    constexpr int NTW = NTN / 4;            // tiles per wave
-    constexpr int GS = N2R + 4;             // LDS row stride of G2 and dP rows
-    constexpr int KS1 = N2R / 4;            // k-steps of the dG1 product
-    static_assert(N1 == 4 && NTN % 4 == 0 && RT == 2, "shape");
-    __shared__ float sG2[R * GS];
-    __shared__ float sD[4 * N1 * GS];       // dP of four groups, rows (g, j1)
-    __shared__ float sA[4 * N1 * R];        // G1 of four groups
-    __shared__ float sRed[2][64][4];
-    __shared__ int32_t sI1[4];
+    constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, QN = N2R / 64;
+    constexpr int SG = 8;                   // groups per slab
+    constexpr int DS = 64 + 4;              // LDS row stride of the dP / G2 column block
+    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32, "shape");
+    __shared__ float sG2[R * DS];           // G2[i2][r1][cols]
+    __shared__ float sD[SG * N1 * DS];      // dP rows (g, j1), this block's columns
+    __shared__ float sA[SG * N1 * R];       // G1[i1(g)] of the slab
+    __shared__ int32_t sI1[SG];
 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int32_t bi = blockIdx.x;
+    reset_queues(ctrl, 1);
+    const int32_t bi = blockIdx.x / QN, qn = blockIdx.x % QN;
     int t = 0;
     {
         int lo = 0, hi = T;
@@ -343,72 +375,70 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
     const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
     const int32_t g1e = ke < K ? (int32_t)(key_scan[ke] >> 32) : U;
+    const int c0 = 64 * qn;
 
     const float* G2s = g2 + d.o2 + (int64_t)i2 * R * N2R;
-    for (int e = threadIdx.x; e < R * N2R; e += 256) sG2[(e / N2R) * GS + e % N2R] = G2s[e];
+    for (int e = threadIdx.x; e < R * 64; e += 256) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
 
-    floatx4 acc2[RT][NTW];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) acc2[rt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int rt = w & 1, ch = w >> 1;      // dG2: r1 block, column pair; dG1: group quad, r1 block
+    floatx4 acc2[2];
+    acc2[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc2[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int nt1 = w & 1, kh = w >> 1;
-    for (int32_t gs = g0; gs < g1e; gs += 4) {
-        const int ng = min(4, g1e - gs);
+    for (int32_t gs = g0; gs < g1e; gs += SG) {
+        const int ng = min(SG, g1e - gs);
         __syncthreads();
-        for (int e = threadIdx.x; e < 4 * NP * R; e += 256) {
-            const int gi = e / PR, r = e % PR;
-            sD[(gi * N1 + r / N2R) * GS + r % N2R] = gi < ng ? dpg[(int64_t)(gs + gi) * PR + r] : 0.f;
+        // dP rows of the slab, this block's 64 columns (one float4 per thread)
+#pragma unroll
+        for (int it = 0; it < SG * N1 / 16; ++it) {
+            const int row = (threadIdx.x >> 4) + 16 * it, c4 = (threadIdx.x & 15) * 4;  // row = (g, j1)
+            const int gi = row / N1, j1 = row % N1;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (gi < ng)
+                v = *reinterpret_cast<const float4*>(dpg + (int64_t)(gs + gi) * PR + j1 * N2R + c0 + c4);
+            float* dst = sD + row * DS + c4;
+            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
         }
-        if (threadIdx.x < 4) sI1[threadIdx.x] = threadIdx.x < ng ? (int32_t)(group_key[gs + threadIdx.x] - kb) : 0;
+        if (threadIdx.x < SG) sI1[threadIdx.x] = threadIdx.x < ng ? (int32_t)(group_key[gs + threadIdx.x] - kb) : 0;
         __syncthreads();
-        for (int e = threadIdx.x; e < 4 * N1 * R; e += 256) {
+        for (int e = threadIdx.x; e < SG * N1 * R; e += 256) {
             const int gi = e / (N1 * R);
             sA[e] = gi < ng ? g1[d.o1 + (int64_t)sI1[gi] * N1 * R + e % (N1 * R)] : 0.f;
         }
         __syncthreads();
-        // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c], one k-step (j1) per group
+        // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c]: one k-step per group
         for (int gi = 0; gi < ng; ++gi) {
+            const float av = sA[gi * N1 * R + q * R + 16 * rt + col];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const float av = sA[gi * N1 * R + q * R + 16 * rt + col];
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) {
-                    const float bv = sD[(gi * N1 + q) * GS + 16 * (w * NTW + j) + col];
-                    acc2[rt][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc2[rt][j], 0, 0, 0);
-                }
+            for (int j = 0; j < 2; ++j) {
+                const float bv = sD[(gi * N1 + q) * DS + 16 * (2 * ch + j) + col];
+                acc2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc2[j], 0, 0, 0);
             }
         }
-        // dG1 rows (g, j1) = dP rows x G2^T: wave (nt1, kh) takes r1 tile nt1, half of K
-        floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s2 = kh * (KS1 / 2); s2 < (kh + 1) * (KS1 / 2); ++s2) {
-            const float av = sD[col * GS + 4 * s2 + q];
-            const float bv = sG2[(16 * nt1 + col) * GS + 4 * s2 + q];
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
-        }
-        if (kh == 1) {
+        // dG1 rows (g, j1) of group quad ch, r1 block rt, K = 64 columns
+        if (4 * ch < ng) {
+            floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sRed[nt1][lane][v] = acc1[v];
-        }
-        __syncthreads();
-        if (kh == 0 && q < ng) {
-            // lane holds rows 4q+v = (group q, j1 v), column r1 = 16*nt1 + col
-            float* dst = dg1 + d.o1 + (int64_t)sI1[q] * N1 * R + 16 * nt1 + col;
+            for (int s2 = 0; s2 < 16; ++s2) {
+                const float av = sD[(16 * ch + col) * DS + 4 * s2 + q];
+                const float bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
+            }
+            // lane holds rows 4q+v = (group 4ch+q, j1 v), column r1 = 16*rt + col
+            const int gi = 4 * ch + q;
+            if (gi < ng) {
+                float* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, acc1[v] + sRed[nt1][lane][v]);
+                for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, acc1[v]);
+            }
         }
     }
-    // dG2[i2] is owned by this workgroup: plain stores (zeros when no group)
-    float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R;
+    // dG2[i2][:, block columns] is owned by this workgroup: plain stores
+    float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R + c0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                D2[(16 * rt + 4 * q + v) * N2R + 16 * (w * NTW + j) + col] = acc2[rt][j][v];
+        for (int v = 0; v < 4; ++v) D2[(16 * rt + 4 * q + v) * N2R + 16 * (2 * ch + j) + col] = acc2[j][v];
 }
 
 template <int N1, int N2, int R, int N3>
@@ -424,17 +454,18 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                        p->at<float>(p->lay.dpg), PR, p->at<int32_t>(p->lay.group_cbase), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->lay.Cmax > 0) {
-        BwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
+        BwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.task_start),
+                  p->at<int32_t>(p->lay.group_key),
                   p->at<int32_t>(p->lay.group_cbase), p->at<int32_t>(p->lay.chunk_group),
                   p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_end),
                   p->at<int32_t>(p->lay.sorted_i3), p->at<int32_t>(p->lay.sorted_bag),
                   p->at<uint8_t>(p->lay.run_head), g1, g2, g3, gout, dg1, dg3,
                   p->at<float>(p->lay.dpg)};
-        hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(grid_for(p->lay.Cmax, 4)), dim3(256), 0,
-                           s, a);
+        hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, a);
         TT_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)p->n_i2), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
+                       dim3(256), 0, s,
                        p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
                        p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, dg1,
                        dg2);
@@ -445,7 +476,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                          const float* gout, float* dg1, float* dg2, float* dg3, hipStream_t s,
                          tt_status* st) {
-    if (!p->uniform) return false;
+    // the prefix build reads G2 rows as float4
+    if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
     if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
     if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }

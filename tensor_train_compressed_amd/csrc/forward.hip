@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 struct FwdArgs {
     const TabDev* desc;
     int32_t T;
-    const int32_t* ctrl;
+    int32_t* ctrl;
+    const int32_t* task_start;
     const int32_t* group_key;
     const int32_t* chunk_group;
     const int32_t* chunk_begin;
@@ -111,90 +112,94 @@ __global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
     using S = FwdShape<N1, N2, R, N3>;
     constexpr int NP = S::NP, D = S::D, KS = S::KS, MT = S::MT, LK = S::LK, TPB = S::TPB;
     constexpr int BL = S::BL, RS = S::RS, DL = S::DL;
-    __shared__ float sP[4][NP * R];
+    __shared__ __attribute__((aligned(16))) float sP[4][NP * R];
     __shared__ float sRow[4][BL * RS];
     __shared__ float sG1[4][N1 * R];
     __shared__ int32_t sHead[4][64];
     __shared__ int32_t sHeadI3[4][64];
 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int32_t c = (int32_t)blockIdx.x * 4 + w;
-    if (c >= a.ctrl[CTRL_NUM_CHUNKS]) return;
-
-    const int32_t g = a.chunk_group[c];
-    const int32_t key = a.group_key[g];
-    const TabDev d = a.desc[find_table(a.desc, a.T, key)];
-    const int32_t local = key - d.key_base;
-    const int32_t i2 = local / d.m1, i1 = local % d.m1;
-    build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
-                            a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
-    // A operand: lane (i = lane%16, q = lane/16) holds P[16*mt + i][KS*q + s]
-    float afr[MT][KS];
-    {
-        const int i = lane & 15, q = lane >> 4;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[w][(16 * mt + i) * R + KS * q + s2];
-    }
-
-    const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
-    const float* G3 = a.g3 + d.o3;
     const int col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
     const uint64_t below_eq = (lane == 63) ? ~0ull : ((2ull << lane) - 1);
-    int32_t carried = s0;   // head of the run that continues into the next batch
+    int32_t cur_key = -1;
+    TabDev d{};
+    float afr[MT][KS];
 
-    for (int32_t sb = s0; sb < s1; sb += 64) {
-        const int32_t sl = sb + lane;
-        const bool valid = sl < s1;
-        const bool head = valid && (a.run_head[sl] != 0);
-        const uint64_t m = __ballot(head);
-        // every lookup records its run head
-        if (valid) {
-            const uint64_t le = m & below_eq;
-            const int32_t hp = le ? sb + 63 - __builtin_clzll(le) : carried;
-            a.row_of[a.perm[sl]] = hp;
-        }
-        if (head) {
-            const int rk = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            sHead[w][rk] = sl;
-            sHeadI3[w][rk] = a.sorted_i3[sl];
-        }
-        if (m) carried = sb + 63 - __builtin_clzll(m);
-        wave_lds_sync();
-        const int nh = __popcll(m);
-        for (int r0 = 0; r0 < nh; r0 += BL) {
-            const int nr = min(BL, nh - r0);
+    {
+        const int32_t c = span_chunk(a.ctrl[CTRL_NUM_CHUNKS], w);
+        if (c >= 0) {
+            const int32_t key = a.group_key[a.chunk_group[c]];
+            if (key != cur_key) {
+                // new group: rebuild P and reload the A operand
+                cur_key = key;
+                d = a.desc[find_table(a.desc, a.T, key)];
+                const int32_t local = key - d.key_base;
+                const int32_t i2 = local / d.m1, i1 = local % d.m1;
+                build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
+                                        a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
+                // A operand: lane (i = lane%16, q) holds P[16*mt + i][KS*q + s]
 #pragma unroll
-            for (int t = 0; t < TPB; ++t) {
-                const int ri = r0 + t * LK + lk;
-                const int32_t i3 = (ri < nh) ? sHeadI3[w][ri] : 0;
-                const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
-                float bv[KS];
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
+                    for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[w][(16 * mt + col) * R + KS * q + s2];
+            }
+            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
+            const float* G3 = a.g3 + d.o3;
+            int32_t carried = s0;   // head of the run that continues into the next batch
+            for (int32_t sb = s0; sb < s1; sb += 64) {
+                const int32_t sl = sb + lane;
+                const bool valid = sl < s1;
+                const bool head = valid && (a.run_head[sl] != 0);
+                const uint64_t m = __ballot(head);
+                // every lookup records its run head
+                if (valid) {
+                    const uint64_t le = m & below_eq;
+                    const int32_t hp = le ? sb + 63 - __builtin_clzll(le) : carried;
+                    a.row_of[a.perm[sl]] = hp;
+                }
+                if (head) {
+                    const int rk = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    sHead[w][rk] = sl;
+                    sHeadI3[w][rk] = a.sorted_i3[sl];
+                }
+                if (m) carried = sb + 63 - __builtin_clzll(m);
+                wave_lds_sync();
+                const int nh = __popcll(m);
+                for (int r0 = 0; r0 < nh; r0 += BL) {
+                    const int nr = min(BL, nh - r0);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+                    for (int tt = 0; tt < TPB; ++tt) {
+                        const int ri = r0 + tt * LK + lk;
+                        const int32_t i3 = (ri < nh) ? sHeadI3[w][ri] : 0;
+                        const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
+                        float bv[KS];
 #pragma unroll
-                    for (int s2 = 0; s2 < KS; ++s2)
-                        cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
-                    // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
-                    const int rr = t * LK + lk;
+                        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
+                        for (int mt = 0; mt < MT; ++mt) {
+                            floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s2 = 0; s2 < KS; ++s2)
+                                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
+                            // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
+                            const int rr = tt * LK + lk;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
+                        }
+                    }
+                    wave_lds_sync();
+                    for (int r = 0; r < nr; ++r) {
+                        const int32_t hs = sHead[w][r0 + r];
+                        float* dst = a.stage + (int64_t)hs * D + lane * DL;
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) dst[k] = sRow[w][r * RS + lane * DL + k];
+                    }
+                    wave_lds_sync();
                 }
             }
-            wave_lds_sync();
-            for (int r = 0; r < nr; ++r) {
-                const int32_t hs = sHead[w][r0 + r];
-                float* dst = a.stage + (int64_t)hs * D + lane * DL;
-#pragma unroll
-                for (int k = 0; k < DL; ++k) dst[k] = sRow[w][r * RS + lane * DL + k];
-            }
-            wave_lds_sync();
         }
     }
 }
@@ -205,8 +210,9 @@ template <int DL>
 __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
                                               const int32_t* __restrict__ row_of,
                                               const float* __restrict__ stage,
-                                              float* __restrict__ out) {
+                                              float* __restrict__ out, int32_t* ctrl) {
     constexpr int D = 64 * DL;
+    reset_queues(ctrl, 0);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t q = (int64_t)blockIdx.x * 4 + w;
     if (q >= TB) return;
@@ -217,12 +223,22 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
     for (int k = 0; k < DL; ++k) acc[k] = 0.f;
     for (int32_t base = b0; base < b1; base += 64) {
         const int n = min(64, b1 - base);
-        const int32_t rv = (lane < n) ? row_of[base + lane] : 0;
-        for (int j = 0; j < n; ++j) {
-            const int32_t slot = __builtin_amdgcn_readlane(rv, j);
-            const float* src = stage + (int64_t)slot * D + lane * DL;
+        const int32_t rv = (lane < n) ? row_of[base + lane] : row_of[b0];
+        // 8 rows in flight; rows past n re-read a valid row and are not added
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            float v[8][DL];
 #pragma unroll
-            for (int k = 0; k < DL; ++k) acc[k] += src[k];
+            for (int u = 0; u < 8; ++u) {
+                const int32_t slot = __builtin_amdgcn_readlane(rv, min(j0 + u, 63));
+                const float* src = stage + (int64_t)slot * D + lane * DL;
+#pragma unroll
+                for (int k = 0; k < DL; ++k) v[u][k] = src[k];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u < n)
+#pragma unroll
+                    for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
         }
     }
     float* dst = out + q * D + lane * DL;
@@ -233,21 +249,21 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 template <int N1, int N2, int R, int N3>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, hipStream_t s) {
-    FwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
+    FwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.task_start),
+              p->at<int32_t>(p->lay.group_key),
               p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
               p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
               p->at<int32_t>(p->lay.perm), p->at<uint8_t>(p->lay.run_head), g1, g2, g3,
               p->at<float>(p->lay.stage), p->at<int32_t>(p->lay.row_of)};
     if (p->lay.Cmax > 0) {
-        hipLaunchKernelGGL((k_fwd_mfma<N1, N2, R, N3>), dim3(grid_for(p->lay.Cmax, 4)), dim3(256), 0,
-                           s, a);
+        hipLaunchKernelGGL((k_fwd_mfma<N1, N2, R, N3>), dim3(span_grid(p->lay.Cmax)), dim3(256), 0, s, a);
         TT_LAUNCH_CHECK();
     }
     constexpr int DL = FwdShape<N1, N2, R, N3>::DL;
     if (p->TB > 0) {
         hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.row_of),
-                           p->at<float>(p->lay.stage), out);
+                           p->at<float>(p->lay.stage), out, p->ctrl());
         TT_LAUNCH_CHECK();
     }
     return TT_OK;
@@ -256,7 +272,8 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 // Returns true (and launches) when the plan's shape has a matrix-core kernel.
 static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                          float* out, hipStream_t s, tt_status* st) {
-    if (!p->uniform) return false;
+    // the prefix build reads G2 rows as float4
+    if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
     if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, s); return true; }
     if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, s); return true; }

@@ -71,6 +71,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
+    y.Tmax = (L + (int64_t)kChunkCost * y.Cmax) / kTaskCost + 2;
+    y.task_start = take(sizeof(int32_t) * (size_t)(y.Tmax + 1));
     const int64_t nscan = std::max<int64_t>(nhist, K);
     y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
@@ -412,28 +414,49 @@ __global__ __launch_bounds__(256) void k_groups(const int32_t* __restrict__ key_
     group_cbase[g] = (int32_t)(v & 0xffffffffu);
 }
 
-__global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
-                                                const int32_t* __restrict__ group_cbase,
-                                                int64_t Cmax, int32_t chunk, const int32_t* ctrl,
-                                                int32_t* __restrict__ chunk_group,
-                                                int32_t* __restrict__ chunk_begin,
-                                                int32_t* __restrict__ chunk_end,
-                                                uint8_t* __restrict__ run_head) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
-    const int32_t U = ctrl[CTRL_NUM_GROUPS];
-    if (c >= Cmax || c >= NC) return;
+__device__ __forceinline__ int32_t group_of_chunk(const int32_t* __restrict__ group_cbase, int32_t U,
+                                                 int64_t c) {
     int32_t lo = 0, hi = U;   // last g in [0, U) with cbase[g] <= c
     while (hi - lo > 1) {
         const int32_t mid = (lo + hi) >> 1;
         if (group_cbase[mid] <= c) lo = mid; else hi = mid;
     }
-    const int32_t g = lo;
+    return lo;
+}
+
+// Chunk table, run heads at chunk starts, and the task table: chunk c starts
+// at modelled cost begin(c) + kChunkCost*c; task t holds the chunks whose
+// start lies in [t*kTaskCost, (t+1)*kTaskCost) (some tasks may be empty).
+__global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
+                                                const int32_t* __restrict__ group_cbase,
+                                                int64_t Cmax, int32_t chunk, int32_t* ctrl,
+                                                int32_t* __restrict__ chunk_group,
+                                                int32_t* __restrict__ chunk_begin,
+                                                int32_t* __restrict__ chunk_end,
+                                                uint8_t* __restrict__ run_head,
+                                                int32_t* __restrict__ task_start) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
+    const int32_t U = ctrl[CTRL_NUM_GROUPS];
+    if (c >= Cmax || c >= NC) return;
+    const int32_t g = group_of_chunk(group_cbase, U, c);
     const int32_t b = group_start[g] + (int32_t)(c - group_cbase[g]) * chunk;
     chunk_group[c] = g;
     chunk_begin[c] = b;
     chunk_end[c] = min(b + chunk, group_start[g + 1]);
     run_head[b] = 1;
+    const int64_t tc = ((int64_t)b + (int64_t)kChunkCost * c) / kTaskCost;
+    int64_t tp = -1;
+    if (c > 0) {
+        const int32_t gp = group_of_chunk(group_cbase, U, c - 1);
+        const int32_t bp = group_start[gp] + (int32_t)(c - 1 - group_cbase[gp]) * chunk;
+        tp = ((int64_t)bp + (int64_t)kChunkCost * (c - 1)) / kTaskCost;
+    }
+    for (int64_t t = tp + 1; t <= tc; ++t) task_start[t] = (int32_t)c;
+    if (c == NC - 1) {
+        task_start[tc + 1] = NC;
+        ctrl[CTRL_NUM_TASKS] = (int32_t)(tc + 1);
+    }
 }
 
 }  // namespace tt
@@ -523,7 +546,9 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
     for (int k = 0; k < 3; ++k) p->extent[k] = 0;
     p->packed = true;
+    p->off4 = true;
     for (int32_t t = 0; t < T; ++t) {
+        if (tables[t].g_offset[1] % 4 != 0) p->off4 = false;
         const tt_emb_table& x = tables[t];
         if (x.n[0] != p->n1 || x.n[1] != p->n2 || x.n[2] != p->n3 || x.rank != p->R) p->uniform = false;
         const int64_t R = x.rank;
@@ -627,7 +652,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<uint8_t>(lay.run_head));
+                               p->at<uint8_t>(lay.run_head), p->at<int32_t>(lay.task_start));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

@@ -25,29 +25,112 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // P[p][r2] = sum_r1 G1[i1][j1][r1] G2[i2][r1][j2][r2] (p = j1*N2 + j2) into
-// sP, one wave, VALU. Lane owns r2 = lane % R and rows p = h + HG*k.
+// sP ([p][r2], row-major), one wave, VALU. Row r1 of the G2 slice is N2*R
+// contiguous floats; lane owns the float4 "quad" qd = lane % Q of that row
+// (j2 = 4*qd / R, r2 = 4*qd % R .. +3) and the j1 values j1 = lane / Q + (64/Q)*k,
+// so every load is one coalesced dwordx4 row read and 16 loads are in flight.
 template <int N1, int N2, int R>
 __device__ __forceinline__ void build_prefix(const float* __restrict__ A, const float* __restrict__ Bc,
-                                             float* sG1, float* sP, int lane) {
-    constexpr int NP = N1 * N2, HG = 64 / R, PE = NP * R / 64, J2N = N2 / HG;
-    for (int e = lane; e < N1 * R; e += 64) sG1[e] = A[e];
+                                             float* sG1T, float* sP, int lane) {
+    constexpr int N2R = N2 * R, Q = N2R / 4, LG = 64 / Q, J1L = N1 / LG;
+    static_assert(N2R % 4 == 0 && 64 % Q == 0 && N1 % LG == 0, "prefix shape");
+    // G1 slice transposed to [r1][j1] so that one r1 gives the N1 values together
+    for (int e = lane; e < N1 * R; e += 64) sG1T[(e % R) * N1 + e / R] = A[e];
     wave_lds_sync();
-    const int r2 = lane % R, h = lane / R;
-    float acc[PE];
+    const int qd = lane % Q, jg = lane / Q;
+    const float4* Bq = reinterpret_cast<const float4*>(Bc) + qd;
+    float4 acc[J1L];
 #pragma unroll
-    for (int k = 0; k < PE; ++k) acc[k] = 0.f;
-#pragma unroll 4
+    for (int k = 0; k < J1L; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 16
     for (int r1 = 0; r1 < R; ++r1) {
-        float b2[J2N];
+        const float4 b = Bq[r1 * Q];
 #pragma unroll
-        for (int jj = 0; jj < J2N; ++jj) b2[jj] = Bc[(r1 * N2 + h + HG * jj) * R + r2];
-#pragma unroll
-        for (int k = 0; k < PE; ++k)  // p = h + HG*k: j2 = h + HG*(k % J2N), j1 = k / J2N
-            acc[k] = fmaf(sG1[(k / J2N) * R + r1], b2[k % J2N], acc[k]);
+        for (int k = 0; k < J1L; ++k) {
+            const float a = sG1T[r1 * N1 + jg + LG * k];
+            acc[k].x = fmaf(a, b.x, acc[k].x);
+            acc[k].y = fmaf(a, b.y, acc[k].y);
+            acc[k].z = fmaf(a, b.z, acc[k].z);
+            acc[k].w = fmaf(a, b.w, acc[k].w);
+        }
     }
 #pragma unroll
-    for (int k = 0; k < PE; ++k) sP[(h + HG * k) * R + r2] = acc[k];
+    for (int k = 0; k < J1L; ++k) {
+        const int j1 = jg + LG * k;
+        // element (j1, j2, r2) sits at ((j1*N2 + j2)*R + r2) = j1*N2R + 4*qd
+        *reinterpret_cast<float4*>(sP + j1 * N2R + 4 * qd) = acc[k];
+    }
     wave_lds_sync();
 }
+
+// Persistent scheduling. Block b runs on XCD b % 8 (workgroups are handed to
+// the XCDs round-robin), and its waves first take tasks from that XCD's queue:
+// the queues are contiguous eighths of the key-ordered task list, so a run of
+// i2 values (and their G2 slices) stays in one XCD's L2. A wave whose queue is
+// empty steals from the next queues in turn. One returning atomic per task,
+// issued by lane 0; counters only grow, so a plain read tells an empty queue
+// without an atomic. Every wave ends after at most 8 empty probes.
+struct TaskQueues {
+    int32_t* ctr;    // 8 counters, CTRL_QSTRIDE words apart
+    int32_t nt;      // number of tasks
+    int home;
+    int probe;
+};
+
+__device__ __forceinline__ TaskQueues make_queues(int32_t* ctrl, int kind) {
+    TaskQueues q;
+    q.ctr = ctrl + CTRL_QUEUE + kind * kXcds * CTRL_QSTRIDE;
+    q.nt = ctrl[CTRL_NUM_TASKS];
+    q.home = (int)(blockIdx.x % kXcds);
+    q.probe = 0;
+    return q;
+}
+
+__device__ __forceinline__ int32_t next_task(TaskQueues& q) {
+    while (q.probe < kXcds) {
+        const int x = (q.home + q.probe) % kXcds;
+        const int32_t lo = (int32_t)(((int64_t)x * q.nt) / kXcds);
+        const int32_t hi = (int32_t)(((int64_t)(x + 1) * q.nt) / kXcds);
+        int32_t* ctr = q.ctr + x * CTRL_QSTRIDE;
+        const int32_t seen = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (lo + seen < hi) {
+            int32_t t = 0;
+            if ((threadIdx.x & 63) == 0) t = lo + atomicAdd(ctr, 1);
+            t = __builtin_amdgcn_readfirstlane(t);
+            if (t < hi) return t;
+        }
+        ++q.probe;
+    }
+    return -1;
+}
+
+// Zeroes the 8 queue counters of `kind` (run by a later kernel in the stream).
+__device__ __forceinline__ void reset_queues(int32_t* ctrl, int kind) {
+    if (blockIdx.x == 0 && threadIdx.x < kXcds)
+        ctrl[CTRL_QUEUE + (kind * kXcds + threadIdx.x) * CTRL_QSTRIDE] = 0;
+}
+
+// Non-persistent chunk mapping: consecutive spans of kSpan chunks go to one XCD,
+// spans rotate over the 8 XCDs (block b runs on XCD b % 8). Groups that share
+// an i2 are adjacent in chunk order, so a G2 slice is read by few XCDs, while
+// a huge group's chunks still spread over all of them. -1 past the end.
+constexpr int kSpan = 64;
+__device__ __forceinline__ int32_t span_chunk(int32_t nchunks, int w) {
+    const int32_t x = (int32_t)(blockIdx.x % kXcds), j = (int32_t)(blockIdx.x / kXcds);
+    const int32_t idx = 4 * j + w;                  // this XCD's idx-th chunk
+    const int32_t c = ((idx / kSpan) * kXcds + x) * kSpan + idx % kSpan;
+    return c < nchunks ? c : -1;
+}
+inline unsigned span_grid(int64_t max_chunks) {
+    // enough blocks that every XCD covers every span it could own
+    const int64_t spans = (max_chunks + kSpan - 1) / kSpan;
+    const int64_t per_xcd = (spans + kXcds - 1) / kXcds * kSpan;   // chunks per XCD
+    const int64_t blocks = kXcds * ((per_xcd + 3) / 4);
+    return (unsigned)(blocks > 0 ? blocks : kXcds);
+}
+
+// Persistent grid: blocks per CU times the CU count.
+inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blocks_per_cu); }
 
 }  // namespace tt

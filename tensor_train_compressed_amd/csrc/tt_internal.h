@@ -28,11 +28,20 @@ enum CtrlSlot : int {
     CTRL_FLAG = 0,        // TT_FLAG_* bits
     CTRL_NUM_GROUPS = 1,
     CTRL_NUM_CHUNKS = 2,
-    CTRL_WORK_FWD = 3,    // persistent forward: next task to claim
-    CTRL_WORK_BWD = 4,    // persistent backward: next task to claim
+    CTRL_NUM_TASKS = 3,
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
-    CTRL_WORDS = 64
+    CTRL_QUEUE = 64,      // task-queue counters, one per 256-byte line:
+                          // forward queues 0..7, backward queues 8..15
+    CTRL_QSTRIDE = 64,
+    CTRL_WORDS = CTRL_QUEUE + 16 * CTRL_QSTRIDE
 };
+
+// Work units of the persistent kernels. A task is a run of consecutive chunks
+// whose modelled cost (lookups + kChunkCost per chunk, the prefix build) is
+// about kTaskCost; the task list is cut into 8 contiguous queues, one per XCD.
+constexpr int kTaskCost = 512;
+constexpr int kChunkCost = 32;
+constexpr int kXcds = 8;
 
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
@@ -68,10 +77,11 @@ struct Layout {
     size_t key_scan;                         // [K] uint64
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
+    size_t task_start;                       // [Tmax+1] first chunk of each task
     size_t scan_tmp;                         // uint64 partials of the multi-block scan
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
     size_t total;
-    int64_t n_tiles, K, Gmax, Cmax;
+    int64_t n_tiles, K, Gmax, Cmax, Tmax;
     int passes;
 };
 
@@ -93,6 +103,7 @@ struct tt_emb_plan_s {
     int32_t n1, n2, n3, R;    // the shared shape when uniform
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
     bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
+    bool off4;                // every table's G2 offset is a multiple of 4 floats
     char* ws;                 // workspace base (device)
     tt::Layout lay;
     std::vector<tt_emb_table> tables;
