@@ -57,158 +57,217 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 
 
 // ---------------------------------------------------------------------------
-// Matrix-core path for the common shapes (all tables share n1, n2, n3, R).
+// Matrix-core path for the common shapes (n1 = 4, n3 = 4, shared n2 and R).
 //
-// One wave per chunk. The prefix P = G1[i1] x G2[i2] is formed once per chunk
-// (VALU, into LDS) and held in registers as the A operand of
-// v_mfma_f32_16x16x4_f32 for the whole chunk. Inside a group the planner has
-// put repeats of one table row next to each other, so the chunk is a list of
-// runs, one per distinct row; the last contraction P x G3[i3] is done once per
-// run. A tile is 16 output columns = (16/n3 runs) x (n3 columns of G3), so a
-// chunk wastes at most 16/n3 - 1 run slots. Each run's row leaves the matrix
-// cores through LDS and is written once, as a whole row, to the stage buffer
-// at the run's first sorted position; every lookup records that position in
-// row_of. k_pool then sums each bag's rows in input order and writes the
-// bag's output row: no atomics, and the same bits on every run.
+// One workgroup (8 waves) per batch of up to kFwdBatch prefix groups of one
+// (table, i2) slice: groups that share a G2 slice are adjacent in key order.
+// The workgroup reads the G2 slice into LDS once and forms the batch's prefixes
+// P_g = G1[i1(g)] x G2[i2] together, as one (4*batch) x (n2*R) x R product on
+// the matrix cores (v_mfma_f32_16x16x4_f32), keeping all of them in LDS.
+// Inside a group the planner has put repeats of one table row next to each
+// other, so a group is a list of runs, one per distinct row; the last contraction P_g x G3[i3] is done once per run, in tiles
+// of 16 output columns = 4 runs x 4 columns of G3. Each run's row is written
+// once to the stage buffer at its run id; k_pool then sums every bag's rows in
+// input order and writes the bag's output row: no atomics, and the same bits
+// on every run.
 
 struct FwdArgs {
     const TabDev* desc;
     int32_t T;
-    int32_t* ctrl;
-    const int32_t* task_start;
+    const int32_t* ctrl;
+    int64_t K;
+    const uint64_t* key_scan;
     const int32_t* group_key;
-    const int32_t* chunk_group;
-    const int32_t* chunk_begin;
-    const int32_t* chunk_end;
-    const int32_t* sorted_i3;
-    const int32_t* perm;
-    const uint8_t* run_head;
+    const int32_t* group_rbase;
+    const int32_t* run_i3;
     const float* g1;
     const float* g2;
     const float* g3;
     float* stage;
-    int32_t* row_of;
 };
 
 template <int N1, int N2, int R, int N3>
 struct FwdShape {
     static constexpr int NP = N1 * N2;      // rows of P
+    static constexpr int N2R = N2 * R;      // columns of a G2 slice row
     static constexpr int D = NP * N3;       // output width
-    static constexpr int KS = R / 4;        // k-steps of 16x16x4 per tile
-    static constexpr int MT = NP / 16;      // 16-row blocks of P
-    static constexpr int LK = 16 / N3;      // runs per tile
-    static constexpr int TPB = 4;           // tiles per batch
-    static constexpr int BL = LK * TPB;     // runs per batch
-    static constexpr int RS = D + 4;        // LDS row stride (floats)
-    static constexpr int HG = 64 / R;       // lane groups sharing an r2 in the P build
-    static constexpr int PE = NP * R / 64;  // P elements per lane
-    static constexpr int DL = D / 64;       // output floats per lane
-    static_assert(NP % 16 == 0 && R % 4 == 0 && 16 % N3 == 0 && D % 64 == 0, "shape");
-    static_assert(64 % R == 0 && N2 % HG == 0 && DL <= 4 && BL <= 64, "shape");
+    static constexpr int SG = kFwdBatch;    // groups per batch
+    static constexpr int MR = SG * N1;      // rows of the batched prefix product
+    static constexpr int MTP = MR / 16;     // row tiles of the prefix product
+    static constexpr int NT2 = N2R / 16;    // column tiles of the prefix product
+    static constexpr int KS = R / 4;        // k-steps over r
+    static constexpr int MT = NP / 16;      // row tiles of P
+    static constexpr int LK = 16 / N3;      // runs per suffix tile
+    static constexpr int GS = N2R + 16;     // LDS row stride of G2
+    static constexpr int AS = R + 4;        // LDS row stride of P rows
+    static constexpr int WAVES = 8;
+    static constexpr int NTW = NT2 * MTP / WAVES;   // prefix tiles per wave
+    static_assert(N1 == 4 && N3 == 4 && NP % 16 == 0 && N2R % 32 == 0 && R % 4 == 0, "shape");
+    static_assert(WAVES % MTP == 0 && (NT2 * MTP) % WAVES == 0, "wave split");
 };
 
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256) void k_fwd_mfma(FwdArgs a) {
+__global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a) {
     using S = FwdShape<N1, N2, R, N3>;
-    constexpr int NP = S::NP, D = S::D, KS = S::KS, MT = S::MT, LK = S::LK, TPB = S::TPB;
-    constexpr int BL = S::BL, RS = S::RS, DL = S::DL;
-    __shared__ __attribute__((aligned(16))) float sP[4][NP * R];
-    __shared__ float sRow[4][BL * RS];
-    __shared__ float sG1[4][N1 * R];
-    __shared__ int32_t sHead[4][64];
-    __shared__ int32_t sHeadI3[4][64];
+    constexpr int NP = S::NP, N2R = S::N2R, D = S::D, SG = S::SG, MTP = S::MTP, NTW = S::NTW;
+    constexpr int KS = S::KS, MT = S::MT, LK = S::LK, GS = S::GS, AS = S::AS, WAVES = S::WAVES;
+    __shared__ __attribute__((aligned(16))) float sG2[R * GS];
+    __shared__ float sP[SG * NP * AS];
+    __shared__ int32_t sRb[SG + 1];
+    __shared__ int32_t sTp[SG + 1];
 
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 15, q = lane >> 4;
-    const int lk = col / N3, j3 = col % N3;
-    const uint64_t below_eq = (lane == 63) ? ~0ull : ((2ull << lane) - 1);
-    int32_t cur_key = -1;
-    TabDev d{};
-    float afr[MT][KS];
-
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
+    // batch -> table, slice, group range
+    const int32_t b = blockIdx.x;
+    int t = 0;
     {
-        const int32_t c = span_chunk(a.ctrl[CTRL_NUM_CHUNKS], w);
-        if (c >= 0) {
-            const int32_t key = a.group_key[a.chunk_group[c]];
-            if (key != cur_key) {
-                // new group: rebuild P and reload the A operand
-                cur_key = key;
-                d = a.desc[find_table(a.desc, a.T, key)];
-                const int32_t local = key - d.key_base;
-                const int32_t i2 = local / d.m1, i1 = local % d.m1;
-                build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
-                                        a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
-                // A operand: lane (i = lane%16, q) holds P[16*mt + i][KS*q + s]
+        int lo = 0, hi = a.T;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.desc[mid].fb_base <= b) lo = mid; else hi = mid;
+        }
+        t = lo;
+    }
+    const TabDev* dp = a.desc + t;
+    const int32_t m1 = dp->m1, fb = dp->fb_base;
+    const int64_t o1 = dp->o1, o2 = dp->o2, o3 = dp->o3;
+    const int32_t nb = (m1 + SG - 1) / SG;
+    const int32_t i2 = (b - fb) / nb, jb = (b - fb) % nb;
+    const int64_t kb = (int64_t)dp->key_base + (int64_t)i2 * m1;
+    const int64_t ke = kb + m1;
+    const int32_t gs0 = (int32_t)(a.key_scan[kb] >> 32);
+    const int32_t gs1 = ke < a.K ? (int32_t)(a.key_scan[ke] >> 32) : a.ctrl[CTRL_NUM_GROUPS];
+    const int32_t g0 = gs0 + SG * jb;
+    if (g0 >= gs1) return;
+    const int ng = min(SG, gs1 - g0);
+
+    // ---- G2 slice into LDS; prefix A operand (G1 rows) straight into registers
+    {
+        const float4* G2s = reinterpret_cast<const float4*>(a.g2 + o2 + (int64_t)i2 * R * N2R);
+        constexpr int NQ = R * N2R / 4, NV = (NQ + 64 * WAVES - 1) / (64 * WAVES);
+        float4 v[NV];
+        constexpr bool even = NQ % (64 * WAVES) == 0;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+        for (int k = 0; k < NV; ++k) {
+            const int e4 = tid + 64 * WAVES * k;
+            v[k] = (even || e4 < NQ) ? G2s[even ? e4 : min(e4, NQ - 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-                    for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[w][(16 * mt + col) * R + KS * q + s2];
-            }
-            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
-            const float* G3 = a.g3 + d.o3;
-            int32_t carried = s0;   // head of the run that continues into the next batch
-            for (int32_t sb = s0; sb < s1; sb += 64) {
-                const int32_t sl = sb + lane;
-                const bool valid = sl < s1;
-                const bool head = valid && (a.run_head[sl] != 0);
-                const uint64_t m = __ballot(head);
-                // every lookup records its run head
-                if (valid) {
-                    const uint64_t le = m & below_eq;
-                    const int32_t hp = le ? sb + 63 - __builtin_clzll(le) : carried;
-                    a.row_of[a.perm[sl]] = hp;
-                }
-                if (head) {
-                    const int rk = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    sHead[w][rk] = sl;
-                    sHeadI3[w][rk] = a.sorted_i3[sl];
-                }
-                if (m) carried = sb + 63 - __builtin_clzll(m);
-                wave_lds_sync();
-                const int nh = __popcll(m);
-                for (int r0 = 0; r0 < nh; r0 += BL) {
-                    const int nr = min(BL, nh - r0);
+        for (int k = 0; k < NV; ++k) {
+            const int e4 = tid + 64 * WAVES * k;
+            if (even || e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
+        }
+        if (tid <= ng) sRb[tid] = a.group_rbase[g0 + tid];
+    }
+    const int mtp = w % MTP;                  // prefix row tile: groups 4*mtp .. 4*mtp+3
+    const int gA = 4 * mtp + col / N1;        // group of this lane's A row (col = 4*(g%4) + j1)
+    float af[KS];
+    {
+        const bool live = gA < ng;
+        const int32_t i1 = live ? (int32_t)(a.group_key[g0 + gA] - kb) : 0;
+        const float* G1r = a.g1 + o1 + (int64_t)i1 * N1 * R + (col % N1) * R;
 #pragma unroll
-                    for (int tt = 0; tt < TPB; ++tt) {
-                        const int ri = r0 + tt * LK + lk;
-                        const int32_t i3 = (ri < nh) ? sHeadI3[w][ri] : 0;
-                        const float* gb = G3 + (int64_t)i3 * R * N3 + j3 + KS * q * N3;
-                        float bv[KS];
+        for (int s2 = 0; s2 < KS; ++s2) af[s2] = live ? G1r[4 * s2 + q] : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t acc = 0;
+        sTp[0] = 0;
+        for (int gi = 0; gi < ng; ++gi) {
+            acc += (sRb[gi + 1] - sRb[gi] + LK - 1) / LK;
+            sTp[gi + 1] = acc;
+        }
+    }
+
+    // ---- batched prefix: rows (g, j1) of the G1 stack x G2 slice -> P_g[(j1, j2)][r2]
+    if (4 * mtp < ng) {
 #pragma unroll
-                        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
+        for (int k = 0; k < NTW; ++k) {
+            const int nt = w / MTP + (WAVES / MTP) * k;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+            for (int s2 = 0; s2 < KS; ++s2)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s2], sG2[(4 * s2 + q) * GS + 16 * nt + col],
+                                                           acc, 0, 0, 0);
+            // C row 4q+v = (group 4*mtp+q, j1 v); column c = 16nt + col = (j2, r2)
+            const int gi = 4 * mtp + q, c = 16 * nt + col;
 #pragma unroll
-                            for (int s2 = 0; s2 < KS; ++s2)
-                                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
-                            // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
-                            const int rr = tt * LK + lk;
+            for (int v = 0; v < 4; ++v) sP[(gi * NP + v * N2 + c / R) * AS + c % R] = acc[v];
+        }
+    }
+    __syncthreads();
+
+    // ---- runs: tiles of LK runs of one group, spread over the waves; the
+    // next tile's run index and G3 operand are fetched before this tile's math
+    const int ntile = sTp[ng];
+    const int lk = col / N3, j3 = col % N3;
+    const float* G3 = a.g3 + o3 + j3 + KS * q * N3;
+    int cur = -1, gnext = 0;
+    float afr[MT][KS];
+    int tau = w;
+    int32_t r = 0;
+    bool valid = false;
+    float bv[KS];
 #pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                sRow[w][rr * RS + (16 * mt + 4 * q + v) * N3 + j3] = cacc[v];
-                        }
-                    }
-                    wave_lds_sync();
-                    for (int r = 0; r < nr; ++r) {
-                        const int32_t hs = sHead[w][r0 + r];
-                        float* dst = a.stage + (int64_t)hs * D + lane * DL;
+    for (int s2 = 0; s2 < KS; ++s2) bv[s2] = 0.f;
+    if (tau < ntile) {
+        while (sTp[gnext + 1] <= tau) ++gnext;
+        r = sRb[gnext] + LK * (tau - sTp[gnext]) + lk;
+        valid = r < sRb[gnext + 1];
+        const float* gb = G3 + (int64_t)(valid ? a.run_i3[r] : 0) * R * N3;
 #pragma unroll
-                        for (int k = 0; k < DL; ++k) dst[k] = sRow[w][r * RS + lane * DL + k];
-                    }
-                    wave_lds_sync();
-                }
+        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
+    }
+    for (; tau < ntile; tau += WAVES) {
+        const int gi = gnext;
+        if (gi != cur) {
+            cur = gi;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[(gi * NP + 16 * mt + col) * AS + KS * q + s2];
+        }
+        // prefetch the next tile
+        const int tn = tau + WAVES;
+        int32_t rn = 0;
+        bool vn = false;
+        float bn[KS];
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) bn[s2] = 0.f;
+        if (tn < ntile) {
+            while (sTp[gnext + 1] <= tn) ++gnext;
+            rn = sRb[gnext] + LK * (tn - sTp[gnext]) + lk;
+            vn = rn < sRb[gnext + 1];
+            const float* gb = G3 + (int64_t)(vn ? a.run_i3[rn] : 0) * R * N3;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) bn[s2] = gb[s2 * N3];
+        }
+        float* dst = a.stage + (int64_t)r * D + j3;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
+            // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
+            if (valid) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dst[(16 * mt + 4 * q + v) * N3] = cacc[v];
             }
         }
+        r = rn;
+        valid = vn;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = bn[s2];
     }
 }
 
 // One wave per bag: sum the rows of the bag's lookups (in input order) from
-// the stage buffer and write the bag's output row. Empty bags get zeros.
+// the stage buffer (one row per run id) and write the bag's output row. Empty
+// bags get zeros.
 template <int DL>
 __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
-                                              const int32_t* __restrict__ row_of,
+                                              const int32_t* __restrict__ run_of,
                                               const float* __restrict__ stage,
                                               float* __restrict__ out, int32_t* ctrl) {
     constexpr int D = 64 * DL;
@@ -223,7 +282,7 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
     for (int k = 0; k < DL; ++k) acc[k] = 0.f;
     for (int32_t base = b0; base < b1; base += 64) {
         const int n = min(64, b1 - base);
-        const int32_t rv = (lane < n) ? row_of[base + lane] : row_of[b0];
+        const int32_t rv = (lane < n) ? run_of[base + lane] : run_of[b0];
         // 8 rows in flight; rows past n re-read a valid row and are not added
         for (int j0 = 0; j0 < n; j0 += 8) {
             float v[8][DL];
@@ -249,20 +308,17 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 template <int N1, int N2, int R, int N3>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, hipStream_t s) {
-    FwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.task_start),
-              p->at<int32_t>(p->lay.group_key),
-              p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
-              p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
-              p->at<int32_t>(p->lay.perm), p->at<uint8_t>(p->lay.run_head), g1, g2, g3,
-              p->at<float>(p->lay.stage), p->at<int32_t>(p->lay.row_of)};
-    if (p->lay.Cmax > 0) {
-        hipLaunchKernelGGL((k_fwd_mfma<N1, N2, R, N3>), dim3(span_grid(p->lay.Cmax)), dim3(256), 0, s, a);
+    FwdArgs a{p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+              p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.group_rbase),
+              p->at<int32_t>(p->lay.run_i3), g1, g2, g3, p->at<float>(p->lay.stage)};
+    if (p->L > 0 && p->n_fb > 0) {
+        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(512), 0, s, a);
         TT_LAUNCH_CHECK();
     }
-    constexpr int DL = FwdShape<N1, N2, R, N3>::DL;
+    constexpr int DL = FwdShape<N1, N2, R, N3>::D / 64;
     if (p->TB > 0) {
         hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
-                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.row_of),
+                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
                            p->at<float>(p->lay.stage), out, p->ctrl());
         TT_LAUNCH_CHECK();
     }

@@ -52,7 +52,10 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.ckey = take(l4);
     y.bag_start = take(sizeof(int32_t) * (size_t)((int64_t)T * B + 1));
     y.run_head = take((size_t)L);
-    y.row_of = take(l4);
+    y.rid = take(l4);
+    y.run_start = take(l4);
+    y.run_i3 = take(l4);
+    y.run_of = take(l4);
     y.stage = take(sizeof(float) * (size_t)L * (size_t)D);
     y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
     y.skey = take(l4);
@@ -68,12 +71,13 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.group_key = take(sizeof(int32_t) * (size_t)y.Gmax);
     y.group_start = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
     y.group_cbase = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
+    y.group_rbase = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
     y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.Tmax = (L + (int64_t)kChunkCost * y.Cmax) / kTaskCost + 2;
     y.task_start = take(sizeof(int32_t) * (size_t)(y.Tmax + 1));
-    const int64_t nscan = std::max<int64_t>(nhist, K);
+    const int64_t nscan = std::max<int64_t>(std::max<int64_t>(nhist, K), L);
     y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
@@ -361,7 +365,8 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
                                                 int32_t* __restrict__ sorted_bag,
                                                 int32_t* __restrict__ key_start,
                                                 int32_t* __restrict__ key_end,
-                                                uint8_t* __restrict__ run_head) {
+                                                uint8_t* __restrict__ run_head,
+                                                int32_t* __restrict__ rid) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
     const int32_t l = perm[s];
@@ -369,9 +374,11 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
     const int32_t k = ck / M3;
     sorted_i3[s] = i3[l];
     sorted_bag[s] = bag_of[l];
-    // a run is a maximal stretch of one (key, i3) row in sorted order; chunk
-    // starts also open a run (k_chunks marks those)
-    run_head[s] = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
+    // a run is a maximal stretch of one (key, i3) row in sorted order; for the
+    // backward's run_head, chunk starts also open a run (k_chunks marks those)
+    const int32_t h = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
+    run_head[s] = (uint8_t)h;
+    rid[s] = h;
     if (s == 0 || skey[s - 1] / M3 != k) key_start[k] = (int32_t)s;
     if (s == L - 1 || skey[s + 1] / M3 != k) key_end[k] = (int32_t)(s + 1);
 }
@@ -459,6 +466,37 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     }
 }
 
+// Row runs (maximal stretches of one (key, i3) row in sorted order; unlike the
+// backward's run_head flags, chunk starts do not cut them) from the scanned
+// head flags: rid[s] is now the number of row-run heads before position s.
+__global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
+                                              const int32_t* __restrict__ perm,
+                                              const int32_t* __restrict__ skey,
+                                              const int32_t* __restrict__ sorted_i3,
+                                              const uint64_t* __restrict__ key_scan, int64_t L,
+                                              int32_t M3, int32_t* ctrl,
+                                              int32_t* __restrict__ run_start,
+                                              int32_t* __restrict__ run_i3,
+                                              int32_t* __restrict__ run_of,
+                                              int32_t* __restrict__ group_rbase) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= L) return;
+    const int32_t r0 = rid[s];
+    const int32_t h = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
+    if (h) {
+        run_start[r0] = (int32_t)s;
+        run_i3[r0] = sorted_i3[s];
+    }
+    run_of[perm[s]] = r0 + h - 1;
+    const int32_t k = skey[s] / M3;
+    if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = r0;
+    if (s == L - 1) {
+        const int32_t nr = r0 + h;
+        ctrl[CTRL_NUM_RUNS] = nr;
+        group_rbase[ctrl[CTRL_NUM_GROUPS]] = nr;
+    }
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -538,7 +576,11 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;
     p->M3 = M3;
     p->n_i2 = 0;
-    for (int32_t t = 0; t < T; ++t) p->n_i2 += tables[t].m[1];
+    p->n_fb = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        p->n_i2 += tables[t].m[1];
+        p->n_fb += (int64_t)tables[t].m[1] * ((tables[t].m[0] + kFwdBatch - 1) / kFwdBatch);
+    }
     p->ws = (char*)workspace;
     p->lay = lay;
     p->tables.assign(tables, tables + T);
@@ -564,7 +606,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     auto fail = [&](tt_status e) { delete p; return e; };
     // control words and descriptors
     if (fill32(p->ctrl(), 0u, CTRL_WORDS, s) != TT_OK) return fail(TT_ERR_HIP);
-    int32_t kb = 0, i2b = 0;
+    int32_t kb = 0, i2b = 0, fbb = 0;
     for (int32_t first = 0; first < T; first += 16) {
         DescBatch b{};
         b.first = first;
@@ -579,6 +621,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             d.key_base = kb;
             d.i2_base = i2b;
             i2b += x.m[1];
+            d.fb_base = fbb;
+            fbb += x.m[1] * ((x.m[0] + kFwdBatch - 1) / kFwdBatch);
             kb += x.m[0] * x.m[1];
         }
         hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
@@ -634,7 +678,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
                                p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
-                               key_start, key_end, p->at<uint8_t>(lay.run_head));
+                               key_start, key_end, p->at<uint8_t>(lay.run_head), p->at<int32_t>(lay.rid));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
@@ -653,6 +697,17 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
                                p->at<uint8_t>(lay.run_head), p->at<int32_t>(lay.task_start));
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            // run ids: exclusive scan of the head flags, then the run tables
+            if (scan_exclusive<uint32_t>(p->at<uint32_t>(lay.rid), L,
+                                         reinterpret_cast<uint32_t*>(p->at<uint64_t>(lay.scan_tmp)),
+                                         nullptr, s) != TT_OK)
+                return fail(TT_ERR_HIP);
+            hipLaunchKernelGGL(k_runs, dim3(grid_for(L, 256)), dim3(256), 0, s,
+                               p->at<int32_t>(lay.rid), p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
+                               p->at<int32_t>(lay.sorted_i3), p->at<uint64_t>(lay.key_scan), L, p->M3,
+                               ctrl, p->at<int32_t>(lay.run_start), p->at<int32_t>(lay.run_i3),
+                               p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.group_rbase));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

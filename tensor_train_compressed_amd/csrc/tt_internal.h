@@ -20,8 +20,10 @@ struct alignas(16) TabDev {
     int64_t o1, o2, o3;         // element offsets of this table's G1/G2/G3
     int32_t key_base;           // first prefix key of this table
     int32_t i2_base;            // first (table, i2) slice index of this table
+    int32_t fb_base;            // first forward batch (kFwdBatch groups of one slice) of this table
+    int32_t pad_[3];
 };
-static_assert(sizeof(TabDev) == 64, "TabDev layout");
+static_assert(sizeof(TabDev) == 80, "TabDev layout");
 
 // Control words at the head of the workspace (int32 slots).
 enum CtrlSlot : int {
@@ -29,6 +31,7 @@ enum CtrlSlot : int {
     CTRL_NUM_GROUPS = 1,
     CTRL_NUM_CHUNKS = 2,
     CTRL_NUM_TASKS = 3,
+    CTRL_NUM_RUNS = 4,
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
     CTRL_QUEUE = 64,      // task-queue counters, one per 256-byte line:
                           // forward queues 0..7, backward queues 8..15
@@ -42,6 +45,8 @@ enum CtrlSlot : int {
 constexpr int kTaskCost = 512;
 constexpr int kChunkCost = 32;
 constexpr int kXcds = 8;
+// Forward work unit: up to this many prefix groups of one (table, i2) slice.
+constexpr int kFwdBatch = 8;
 
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
@@ -68,8 +73,12 @@ struct Layout {
     size_t bag_start;                        // [TB+1] int32 copy of the offsets
     size_t run_head;                         // [L] uint8, sorted order: position starts a run
                                              //     (a new (key, i3) row, or a chunk start)
-    size_t row_of;                           // [L] int32: sorted position of the lookup's run head
-    size_t stage;                            // [L][D] float: one row per run, at its head
+    size_t rid;                              // [L] int32, sorted order: row-run id (exclusive count of heads)
+    size_t run_start;                        // [L] int32: first sorted position of each run
+    size_t run_i3;                           // [L] int32: i3 of each run
+    size_t run_of;                           // [L] int32, input order: run id of each lookup
+    size_t group_rbase;                      // [Gmax+1] int32: first run of each group
+    size_t stage;                            // [L][D] float: one row per run (indexed by run id)
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
     size_t hist;                             // [kRadixBins * n_tiles] uint32
@@ -99,6 +108,7 @@ struct tt_emb_plan_s {
     int64_t K;
     int32_t M3;               // largest m3 over the tables
     int64_t n_i2;             // sum over tables of m2 (number of (table, i2) slices)
+    int64_t n_fb;             // forward batches: sum over tables of m2 * ceil(m1 / kFwdBatch)
     bool uniform;             // all tables share (n1, n2, n3, R)
     int32_t n1, n2, n3, R;    // the shared shape when uniform
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
