@@ -86,6 +86,15 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     }
 }
 
+__global__ __launch_bounds__(256) void k_bwd_finish(const double* __restrict__ a1, float* __restrict__ dg1,
+                                                    int64_t n1, const double* __restrict__ a3,
+                                                    float* __restrict__ dg3, int64_t n3) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = tid; i < n1; i += nth) dg1[i] = (float)a1[i];
+    for (int64_t i = tid; i < n3; i += nth) dg3[i] = (float)a3[i];
+}
+
 __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float* __restrict__ dg,
                                              float lr, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -96,241 +105,272 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 
 // ---------------------------------------------------------------------------
 // Matrix-core backward for the common shapes (n1 = 4, n3 = 4, shared by all
-// tables). Three kernels:
+// tables). Four kernels, all on row runs (one run per distinct table row of a
+// group, the same runs the forward contracts):
 //
-// k_bwd_prep    zeroes dG1, dG3 and the dL/dP rows of groups cut into several
-//               chunks (the only targets that are accumulated with atomics)
-// k_bwd_runs    one wave per chunk. Recomputes P, then walks the chunk's runs
-//               (one run per distinct table row). For a run, S = sum of the
-//               grad_out rows of its lookups; then, on the matrix cores,
+// k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
+//               with atomics; fp64 keeps a sum of many cancelling terms within
+//               the fp32 tolerance) and the S rows of the runs that cross a
+//               chunk start (summed piece by piece)
+// k_bwd_sum     persistent waves over cost-balanced chunk tasks (per-XCD
+//               queues, stealing): for every run, S = sum of the grad_out rows
+//               of its lookups. A run inside one chunk is stored once; the
+//               pieces of a run cut by chunk starts are added with atomics.
+//               Memory-bound.
+// k_bwd_batch   one workgroup per (slice, 8-group batch): forms the batch's
+//               prefixes P like the forward, then per run, on the matrix cores,
 //                 dG3[i3] += P^T S          (R x n3, added with atomics)
-//                 dP      += S G3[i3]^T     (n1*n2 x R, kept in registers)
-//               dP of the chunk goes to the group's dL/dP row (plain store, or
-//               atomics when the group has several chunks).
-// k_bwd_prefix  one workgroup per (table, i2) slice. Groups of one slice are
-//               adjacent in key order; for each,
-//                 dG2[i2] += G1[i1]^T dP    (accumulated in registers, stored
-//                                            once: no atomics)
-//                 dG1[i1] += dP G2[i2]^T    (four groups per matrix-core tile,
-//                                            added with atomics)
+//                 dP_g    += S G3[i3]^T     (n1*n2 x R, reduced in LDS)
+//               and stores each group's dL/dP row once.
+// k_bwd_prefix  one workgroup per ((table, i2) slice, 64-column block):
+//                 dG2[i2] += G1[i1]^T dP    (plain stores, owned)
+//                 dG1[i1] += dP G2[i2]^T    (atomics across column blocks)
+// k_bwd_finish  dG1, dG3 <- their fp64 accumulators, rounded to fp32
+
+__device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64_t s) {
+    return s == 0 || skey[s - 1] != skey[s];
+}
+
+template <int DL>
+__global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
+                                                  double* __restrict__ dg3, int64_t n3,
+                                                  float* __restrict__ S,
+                                                  const int32_t* __restrict__ chunk_begin,
+                                                  const int32_t* __restrict__ skey,
+                                                  const int32_t* __restrict__ rid,
+                                                  const int32_t* __restrict__ ctrl) {
+    constexpr int D = 64 * DL;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
+    for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
+    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
+    const int lane = threadIdx.x & 63;
+    for (int64_t c = tid >> 6; c < NC; c += nth >> 6) {
+        const int32_t b = chunk_begin[c];
+        if (!row_head(skey, b)) {
+            float* dst = S + (int64_t)(rid[b] - 1) * D + lane * DL;
+#pragma unroll
+            for (int k = 0; k < DL; ++k) dst[k] = 0.f;
+        }
+    }
+}
+
+struct SumArgs {
+    int32_t* ctrl;
+    const int32_t* task_start;
+    const int32_t* chunk_begin;
+    const int32_t* chunk_end;
+    const int32_t* sorted_bag;
+    const int32_t* skey;
+    const int32_t* rid;
+    int64_t L;
+    const float* gout;
+    float* S;
+};
+
+template <int DL>
+__global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
+    constexpr int D = 64 * DL, FL = 32;   // grad_out rows in flight
+    const int lane = threadIdx.x & 63;
+    TaskQueues tq = make_queues(a.ctrl, 1);
+    for (int32_t t = next_task(tq); t >= 0; t = next_task(tq)) {
+        const int32_t cA = a.task_start[t], cB = a.task_start[t + 1];
+        for (int32_t c = cA; c < cB; ++c) {
+            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
+            const bool tail_whole = (s1 == a.L) || row_head(a.skey, s1);
+            int32_t cur = 0;
+            bool cur_head = false;
+            float sacc[DL];
+#pragma unroll
+            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+            auto flush = [&](bool whole) {
+                float* dst = a.S + (int64_t)cur * D + lane * DL;
+                if (whole) {
+#pragma unroll
+                    for (int k = 0; k < DL; ++k) dst[k] = sacc[k];
+                } else {
+#pragma unroll
+                    for (int k = 0; k < DL; ++k) atomicAdd(dst + k, sacc[k]);
+                }
+            };
+            for (int32_t sb = s0; sb < s1; sb += 64) {
+                const int n = min(64, s1 - sb);
+                const int32_t sl = sb + lane;
+                const bool valid = lane < n;
+                const bool hr = valid && row_head(a.skey, sl);
+                const uint64_t m = __ballot(hr);
+                const int32_t bagv = valid ? a.sorted_bag[sl] : a.sorted_bag[sb];
+                const int32_t rrv = valid ? a.rid[sl] + (hr ? 1 : 0) - 1 : 0;
+                for (int r0 = 0; r0 < n; r0 += FL) {
+                    float v[FL][DL];
+#pragma unroll
+                    for (int u = 0; u < FL; ++u) {
+                        const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) v[u][k] = row[k];
+                    }
+#pragma unroll
+                    for (int u = 0; u < FL; ++u) {
+                        const int r = r0 + u;
+                        if (r < n) {
+                            const bool first = (sb + r == s0);
+                            if (first || ((m >> r) & 1ull)) {
+                                if (!first) flush(cur_head);   // the previous piece ends at a row head
+                                cur = __builtin_amdgcn_readlane(rrv, r);
+                                cur_head = ((m >> r) & 1ull) != 0;
+#pragma unroll
+                                for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+                            }
+#pragma unroll
+                            for (int k = 0; k < DL; ++k) sacc[k] += v[u][k];
+                        }
+                    }
+                }
+            }
+            flush(cur_head && tail_whole);
+        }
+    }
+}
 
 struct BwdArgs {
     const TabDev* desc;
     int32_t T;
-    int32_t* ctrl;
-    const int32_t* task_start;
+    const int32_t* ctrl;
+    int64_t K;
+    const uint64_t* key_scan;
     const int32_t* group_key;
-    const int32_t* group_cbase;
-    const int32_t* chunk_group;
-    const int32_t* chunk_begin;
-    const int32_t* chunk_end;
-    const int32_t* sorted_i3;
-    const int32_t* sorted_bag;
-    const uint8_t* run_head;
+    const int32_t* group_rbase;
+    const int32_t* run_i3;
     const float* g1;
     const float* g2;
     const float* g3;
-    const float* gout;
-    float* dg1;
-    float* dg3;
+    const float* S;
+    double* dg3;
     float* dpg;
 };
 
 template <int N1, int N2, int R, int N3>
-struct BwdShape {
-    static constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R;
-    static constexpr int MT = NP / 16;      // 16-row blocks of P / dP
-    static constexpr int RT = R / 16;       // 16-row blocks of P^T, 16-col blocks of dP
-    static constexpr int KSP = NP / 4;      // k-steps over p
-    static constexpr int LK = 16 / N3;      // runs per dG3 tile
-    static constexpr int RB = 2 * LK;       // runs buffered before a matrix-core pass
-    static constexpr int RS = D + 4;        // LDS row stride of S
-    static constexpr int CN = R * N3;       // dG3 slice width
-    static constexpr int CS = CN + 4;
-    static constexpr int DL = D / 64, CL = CN / 64;
-    static_assert(N1 == 4 && N3 == 4 && NP % 16 == 0 && R % 16 == 0, "shape");
-    static_assert(D % 64 == 0 && CN % 64 == 0 && 64 % R == 0, "shape");
-};
+__global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
+    using B = PrefixBatch<N1, N2, R>;
+    constexpr int NP = B::NP, D = NP * N3, PR = NP * R, SG = B::SG, AS = B::AS, WAVES = B::WAVES;
+    constexpr int MT = NP / 16, RT = R / 16, KSP = NP / 4, LK = 16 / N3, CN = R * N3;
+    static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0, "shape");
+    constexpr int U_FLOATS = B::G2_FLOATS > SG * PR ? B::G2_FLOATS : SG * PR;
+    __shared__ __attribute__((aligned(16))) float sU[U_FLOATS];   // G2 slice, then dP of the batch
+    __shared__ float sP[B::P_FLOATS];
+    __shared__ int32_t sRb[SG + 1];
+    __shared__ int32_t sTp[SG + 1];
 
-__global__ __launch_bounds__(256) void k_bwd_prep(float* __restrict__ dg1, int64_t n1,
-                                                  float* __restrict__ dg3, int64_t n3,
-                                                  float* __restrict__ dpg, int32_t PR,
-                                                  const int32_t* __restrict__ group_cbase,
-                                                  const int32_t* __restrict__ ctrl) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.f;
-    for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.f;
-    const int32_t U = ctrl[CTRL_NUM_GROUPS];
-    const int lane = threadIdx.x & 63;
-    for (int64_t g = tid >> 6; g < U; g += nth >> 6) {
-        if (group_cbase[g + 1] - group_cbase[g] > 1)
-            for (int e = lane; e < PR; e += 64) dpg[g * PR + e] = 0.f;
-    }
-}
+    BatchCtx c;
+    if (!batch_setup(a.desc, a.T, a.K, a.key_scan, a.ctrl, c)) return;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
+    if (tid <= c.ng) sRb[tid] = a.group_rbase[c.g0 + tid];
+    batch_prefix<N1, N2, R>(c, a.group_key, a.g1, a.g2, sU, sP);
+    batch_tiles(sRb, sTp, c.ng, LK);
+    float* sDP = sU;
+    for (int e = tid; e < SG * PR; e += 64 * WAVES) sDP[e] = 0.f;
+    __syncthreads();
 
-template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256) void k_bwd_runs(BwdArgs a) {
-    using S = BwdShape<N1, N2, R, N3>;
-    constexpr int NP = S::NP, D = S::D, PR = S::PR, MT = S::MT, RT = S::RT, KSP = S::KSP;
-    constexpr int LK = S::LK, RB = S::RB, RS = S::RS, CN = S::CN, CS = S::CS, DL = S::DL, CL = S::CL;
-    __shared__ __attribute__((aligned(16))) float sP[4][PR];
-    __shared__ float sG1[4][N1 * R];
-    __shared__ float sS[4][RB * RS];
-    __shared__ float sC[4][LK * CS];
-    __shared__ int32_t sI3[4][RB];
-
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 15, q = lane >> 4;
-    TaskQueues tq = make_queues(a.ctrl, 1);
-
-    int32_t cur_g = -1;
-    bool multi = false;
-    TabDev d{};
+    const int ntile = sTp[c.ng];
+    const int lk = col / N3, j3 = col % N3;
+    const float* G3 = a.g3 + c.o3;
+    double* dG3 = a.dg3 + c.o3;
+    int cur = -1;
     float afT[RT][KSP];
     floatx4 dacc[MT][RT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // dP of the current group -> its dL/dP row, [p][r2] (atomics when the
-    // group is cut into several chunks, which other waves may hold)
-    auto flush_dp = [&]() {
-        float* dst = a.dpg + (int64_t)cur_g * PR;
+    auto flush = [&]() {
+        // lane holds dP[p = 16mt + 4q + v][r2 = 16nt + col]
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float* e = dst + (16 * mt + 4 * q + v) * R + 16 * nt + col;
-                    if (multi) atomicAdd(e, dacc[mt][nt][v]);
-                    else *e = dacc[mt][nt][v];
-                }
+                for (int v = 0; v < 4; ++v)
+                    atomicAdd(&sDP[cur * PR + (16 * mt + 4 * q + v) * R + 16 * nt + col], dacc[mt][nt][v]);
                 dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
     };
-
-    for (int32_t t = next_task(tq); t >= 0; t = next_task(tq)) {
-        const int32_t cA = a.task_start[t], cB = a.task_start[t + 1];
-        for (int32_t c = cA; c < cB; ++c) {
-            const int32_t g = a.chunk_group[c];
-            if (g != cur_g) {
-                if (cur_g >= 0) flush_dp();
-                cur_g = g;
-                multi = (a.group_cbase[g + 1] - a.group_cbase[g]) > 1;
-                const int32_t key = a.group_key[g];
-                d = a.desc[find_table(a.desc, a.T, key)];
-                const int32_t local = key - d.key_base;
-                const int32_t i2 = local / d.m1, i1 = local % d.m1;
-                build_prefix<N1, N2, R>(a.g1 + d.o1 + (int64_t)i1 * N1 * R,
-                                        a.g2 + d.o2 + (int64_t)i2 * R * N2 * R, sG1[w], sP[w], lane);
-                // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
+    // per-tile operands, fetched one tile ahead
+    struct TileOps {
+        int gi;
+        int32_t rbase, rend, i3;
+        bool valid;
+        float bv[KSP];
+    };
+    auto fetch = [&](int tt, int& g, TileOps& o) {
+        while (sTp[g + 1] <= tt) ++g;
+        o.gi = g;
+        o.rbase = sRb[g] + LK * (tt - sTp[g]);
+        o.rend = sRb[g + 1];
+        const int32_t r = o.rbase + lk;
+        o.valid = r < o.rend;
+        o.i3 = o.valid ? a.run_i3[r] : 0;
+        const float* Sb = a.S + (int64_t)(o.valid ? r : o.rbase) * D + j3;
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
+        for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = o.valid ? Sb[(KSP * q + s2) * N3] : 0.f;
+    };
+    // wave w takes a contiguous range of tiles, so consecutive tiles mostly
+    // share a group and the dP flush and P reload happen once per group
+    const int per = (ntile + WAVES - 1) / WAVES;
+    const int t0 = min(ntile, w * per), t1 = min(ntile, t0 + per);
+    TileOps cu, nx;
+    int gsearch = 0;
+    if (t0 < t1) fetch(t0, gsearch, cu);
+    for (int tau = t0; tau < t1; ++tau) {
+        if (tau + 1 < t1) fetch(tau + 1, gsearch, nx);
+        if (cu.gi != cur) {
+            if (cur >= 0) flush();
+            cur = cu.gi;
+            // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
 #pragma unroll
-                    for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[w][(KSP * q + s2) * R + 16 * rt + col];
-            }
-            const float* G3 = a.g3 + d.o3;
-            float* dG3 = a.dg3 + d.o3;
-            int nrun = 0;
-            bool have = false;
-            int32_t cur_i3 = 0;
-            float sacc[DL];
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
-
-            // matrix-core pass over the nrun buffered runs
-            auto flush = [&]() {
-                wave_lds_sync();
-                // dG3[i3] += P^T S: tiles of LK runs x N3 columns
-                for (int t0 = 0; t0 < nrun; t0 += LK) {
-                    const int lk = col / N3, j3 = col % N3;
-                    float bv[KSP];
-#pragma unroll
-                    for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = sS[w][(t0 + lk) * RS + (KSP * q + s2) * N3 + j3];
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        floatx4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s2 = 0; s2 < KSP; ++s2)
-                            cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], bv[s2], cc, 0, 0, 0);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) sC[w][lk * CS + (16 * rt + 4 * q + v) * N3 + j3] = cc[v];
-                    }
-                    wave_lds_sync();
-                    const int nr = min(LK, nrun - t0);
-                    for (int r = 0; r < nr; ++r) {
-                        float* dst = dG3 + (int64_t)sI3[w][t0 + r] * CN + lane * CL;
-#pragma unroll
-                        for (int k = 0; k < CL; ++k) atomicAdd(dst + k, sC[w][r * CS + lane * CL + k]);
-                    }
-                    wave_lds_sync();
-                }
-                // dP += S G3[i3]^T: one k-step per run (k = j3)
-                for (int r = 0; r < nrun; ++r) {
-                    const float* gb = G3 + (int64_t)sI3[w][r] * CN;
-                    float av[MT], bv[RT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) av[mt] = sS[w][r * RS + (16 * mt + col) * N3 + q];
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt) bv[nt] = gb[(16 * nt + col) * N3 + q];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int nt = 0; nt < RT; ++nt)
-                            dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bv[nt], dacc[mt][nt], 0, 0, 0);
-                }
-                wave_lds_sync();
-                nrun = 0;
-            };
-            auto finish_run = [&]() {
-#pragma unroll
-                for (int k = 0; k < DL; ++k) sS[w][nrun * RS + lane * DL + k] = sacc[k];
-                if (lane == 0) sI3[w][nrun] = cur_i3;
-                ++nrun;
-                if (nrun == RB) flush();
-            };
-
-            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
-            for (int32_t sb = s0; sb < s1; sb += 64) {
-                const int n = min(64, s1 - sb);
-                const int32_t sl = sb + lane;
-                const bool valid = lane < n;
-                const uint64_t m = __ballot(valid && a.run_head[sl] != 0);
-                const int32_t bagv = valid ? a.sorted_bag[sl] : a.sorted_bag[sb];
-                const int32_t i3v = valid ? a.sorted_i3[sl] : 0;
-                // grad_out rows of 8 positions in flight, then walk them in order
-                for (int r0 = 0; r0 < n; r0 += 8) {
-                    float v[8][DL];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
-#pragma unroll
-                        for (int k = 0; k < DL; ++k) v[u][k] = row[k];
-                    }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int r = r0 + u;
-                        if (r >= n) break;
-                        if ((m >> r) & 1ull) {
-                            if (have) finish_run();
-                            have = true;
-                            cur_i3 = __builtin_amdgcn_readlane(i3v, r);
-#pragma unroll
-                            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
-                        }
-#pragma unroll
-                        for (int k = 0; k < DL; ++k) sacc[k] += v[u][k];
-                    }
-                }
-            }
-            if (have) finish_run();
-            if (nrun > 0) flush();
+                for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[(cur * NP + KSP * q + s2) * AS + 16 * rt + col];
         }
+        // dG3[i3] += P^T S: column (run lk, j3), rows r2
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            floatx4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < KSP; ++s2)
+                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], cu.bv[s2], cc, 0, 0, 0);
+            if (cu.valid) {
+                double* dst = dG3 + (int64_t)cu.i3 * CN + j3;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) atomicAdd(dst + (16 * rt + 4 * q + v) * N3, (double)cc[v]);
+            }
+        }
+        // dP += S G3[i3]^T: one k-step (k = j3) per run of the tile
+#pragma unroll
+        for (int ru = 0; ru < LK; ++ru) {
+            const int32_t rr = cu.rbase + ru;
+            if (rr < cu.rend) {
+                const int32_t i3r = __builtin_amdgcn_readlane(cu.i3, ru * N3);
+                const float* Sr = a.S + (int64_t)rr * D;
+                const float* gb = G3 + (int64_t)i3r * CN;
+                float av[MT], bq[RT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) av[mt] = Sr[(16 * mt + col) * N3 + q];
+#pragma unroll
+                for (int nt = 0; nt < RT; ++nt) bq[nt] = gb[(16 * nt + col) * N3 + q];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < RT; ++nt)
+                        dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bq[nt], dacc[mt][nt], 0, 0, 0);
+            }
+        }
+        cu = nx;
     }
-    if (cur_g >= 0) flush_dp();
+    if (cur >= 0) flush();
+    __syncthreads();
+    // each group of the batch owns its dL/dP row: plain stores
+    for (int e = tid; e < c.ng * PR; e += 64 * WAVES) a.dpg[(int64_t)c.g0 * PR + e] = sDP[e];
 }
 
 // One workgroup per ((table, i2) slice, 64-column block of the N2*R columns).
@@ -346,7 +386,7 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
                                                     const float* __restrict__ dpg,
                                                     const float* __restrict__ g1,
                                                     const float* __restrict__ g2,
-                                                    float* __restrict__ dg1, float* __restrict__ dg2) {
+                                                    double* __restrict__ dg1, float* __restrict__ dg2) {
     constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, QN = N2R / 64;
     constexpr int SG = 8;                   // groups per slab
     constexpr int DS = 64 + 4;              // LDS row stride of the dP / G2 column block
@@ -427,9 +467,9 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
             // lane holds rows 4q+v = (group 4ch+q, j1 v), column r1 = 16*rt + col
             const int gi = 4 * ch + q;
             if (gi < ng) {
-                float* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
+                double* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, acc1[v]);
+                for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, (double)acc1[v]);
             }
         }
     }
@@ -445,30 +485,37 @@ template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
                                  float* dg3, hipStream_t s) {
-    constexpr int PR = N1 * N2 * R;
     if (!p->packed) {
         tt_status st = fill32(dg2, 0u, p->extent[1], s);
         if (st != TT_OK) return st;
     }
-    hipLaunchKernelGGL(k_bwd_prep, dim3(1024), dim3(256), 0, s, dg1, p->extent[0], dg3, p->extent[2],
-                       p->at<float>(p->lay.dpg), PR, p->at<int32_t>(p->lay.group_cbase), p->ctrl());
+    constexpr int DL = N1 * N2 * N3 / 64;
+    double* acc1 = p->at<double>(p->lay.acc1);
+    double* acc3 = p->at<double>(p->lay.acc3);
+    hipLaunchKernelGGL(k_bwd_prep<DL>, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
+                       p->at<float>(p->lay.stage), p->at<int32_t>(p->lay.chunk_begin),
+                       p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid), p->ctrl());
     TT_LAUNCH_CHECK();
-    if (p->lay.Cmax > 0) {
-        BwdArgs a{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.task_start),
-                  p->at<int32_t>(p->lay.group_key),
-                  p->at<int32_t>(p->lay.group_cbase), p->at<int32_t>(p->lay.chunk_group),
-                  p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_end),
-                  p->at<int32_t>(p->lay.sorted_i3), p->at<int32_t>(p->lay.sorted_bag),
-                  p->at<uint8_t>(p->lay.run_head), g1, g2, g3, gout, dg1, dg3,
+    if (p->L > 0) {
+        SumArgs sa{p->ctrl(), p->at<int32_t>(p->lay.task_start), p->at<int32_t>(p->lay.chunk_begin),
+                   p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_bag),
+                   p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid), p->L, gout,
+                   p->at<float>(p->lay.stage)};
+        hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
+        TT_LAUNCH_CHECK();
+        BwdArgs a{p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+                  p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.group_rbase),
+                  p->at<int32_t>(p->lay.run_i3), g1, g2, g3, p->at<float>(p->lay.stage), acc3,
                   p->at<float>(p->lay.dpg)};
-        hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_bwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), 0, s, a);
         TT_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
-                       dim3(256), 0, s,
-                       p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
-                       p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, dg1,
-                       dg2);
+                       dim3(256), 0, s, p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+                       p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, acc1, dg2);
+    TT_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
+                       p->extent[2]);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }

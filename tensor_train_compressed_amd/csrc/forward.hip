@@ -87,130 +87,42 @@ struct FwdArgs {
 };
 
 template <int N1, int N2, int R, int N3>
-struct FwdShape {
-    static constexpr int NP = N1 * N2;      // rows of P
-    static constexpr int N2R = N2 * R;      // columns of a G2 slice row
-    static constexpr int D = NP * N3;       // output width
-    static constexpr int SG = kFwdBatch;    // groups per batch
-    static constexpr int MR = SG * N1;      // rows of the batched prefix product
-    static constexpr int MTP = MR / 16;     // row tiles of the prefix product
-    static constexpr int NT2 = N2R / 16;    // column tiles of the prefix product
-    static constexpr int KS = R / 4;        // k-steps over r
-    static constexpr int MT = NP / 16;      // row tiles of P
-    static constexpr int LK = 16 / N3;      // runs per suffix tile
-    static constexpr int GS = N2R + 16;     // LDS row stride of G2
-    static constexpr int AS = R + 4;        // LDS row stride of P rows
-    static constexpr int WAVES = 8;
-    static constexpr int NTW = NT2 * MTP / WAVES;   // prefix tiles per wave
-    static_assert(N1 == 4 && N3 == 4 && NP % 16 == 0 && N2R % 32 == 0 && R % 4 == 0, "shape");
-    static_assert(WAVES % MTP == 0 && (NT2 * MTP) % WAVES == 0, "wave split");
-};
-
-template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a) {
-    using S = FwdShape<N1, N2, R, N3>;
-    constexpr int NP = S::NP, N2R = S::N2R, D = S::D, SG = S::SG, MTP = S::MTP, NTW = S::NTW;
-    constexpr int KS = S::KS, MT = S::MT, LK = S::LK, GS = S::GS, AS = S::AS, WAVES = S::WAVES;
-    __shared__ __attribute__((aligned(16))) float sG2[R * GS];
-    __shared__ float sP[SG * NP * AS];
+__global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
+    using B = PrefixBatch<N1, N2, R>;
+    constexpr int NP = B::NP, D = NP * N3, SG = B::SG, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
+    constexpr int MT = NP / 16, LK = 16 / N3;
+    static_assert(N3 == 4 && NP % 16 == 0, "shape");
+    __shared__ __attribute__((aligned(16))) float sG2[B::G2_FLOATS];
+    __shared__ float sP[B::P_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sTp[SG + 1];
 
+    BatchCtx c;
+    if (!batch_setup(a.desc, a.T, a.K, a.key_scan, a.ctrl, c)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    // batch -> table, slice, group range
-    const int32_t b = blockIdx.x;
-    int t = 0;
-    {
-        int lo = 0, hi = a.T;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (a.desc[mid].fb_base <= b) lo = mid; else hi = mid;
-        }
-        t = lo;
-    }
-    const TabDev* dp = a.desc + t;
-    const int32_t m1 = dp->m1, fb = dp->fb_base;
-    const int64_t o1 = dp->o1, o2 = dp->o2, o3 = dp->o3;
-    const int32_t nb = (m1 + SG - 1) / SG;
-    const int32_t i2 = (b - fb) / nb, jb = (b - fb) % nb;
-    const int64_t kb = (int64_t)dp->key_base + (int64_t)i2 * m1;
-    const int64_t ke = kb + m1;
-    const int32_t gs0 = (int32_t)(a.key_scan[kb] >> 32);
-    const int32_t gs1 = ke < a.K ? (int32_t)(a.key_scan[ke] >> 32) : a.ctrl[CTRL_NUM_GROUPS];
-    const int32_t g0 = gs0 + SG * jb;
-    if (g0 >= gs1) return;
-    const int ng = min(SG, gs1 - g0);
-
-    // ---- G2 slice into LDS; prefix A operand (G1 rows) straight into registers
-    {
-        const float4* G2s = reinterpret_cast<const float4*>(a.g2 + o2 + (int64_t)i2 * R * N2R);
-        constexpr int NQ = R * N2R / 4, NV = (NQ + 64 * WAVES - 1) / (64 * WAVES);
-        float4 v[NV];
-        constexpr bool even = NQ % (64 * WAVES) == 0;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int e4 = tid + 64 * WAVES * k;
-            v[k] = (even || e4 < NQ) ? G2s[even ? e4 : min(e4, NQ - 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int e4 = tid + 64 * WAVES * k;
-            if (even || e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
-        }
-        if (tid <= ng) sRb[tid] = a.group_rbase[g0 + tid];
-    }
-    const int mtp = w % MTP;                  // prefix row tile: groups 4*mtp .. 4*mtp+3
-    const int gA = 4 * mtp + col / N1;        // group of this lane's A row (col = 4*(g%4) + j1)
-    float af[KS];
-    {
-        const bool live = gA < ng;
-        const int32_t i1 = live ? (int32_t)(a.group_key[g0 + gA] - kb) : 0;
-        const float* G1r = a.g1 + o1 + (int64_t)i1 * N1 * R + (col % N1) * R;
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) af[s2] = live ? G1r[4 * s2 + q] : 0.f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int32_t acc = 0;
-        sTp[0] = 0;
-        for (int gi = 0; gi < ng; ++gi) {
-            acc += (sRb[gi + 1] - sRb[gi] + LK - 1) / LK;
-            sTp[gi + 1] = acc;
-        }
-    }
-
-    // ---- batched prefix: rows (g, j1) of the G1 stack x G2 slice -> P_g[(j1, j2)][r2]
-    if (4 * mtp < ng) {
-#pragma unroll
-        for (int k = 0; k < NTW; ++k) {
-            const int nt = w / MTP + (WAVES / MTP) * k;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s2], sG2[(4 * s2 + q) * GS + 16 * nt + col],
-                                                           acc, 0, 0, 0);
-            // C row 4q+v = (group 4*mtp+q, j1 v); column c = 16nt + col = (j2, r2)
-            const int gi = 4 * mtp + q, c = 16 * nt + col;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sP[(gi * NP + v * N2 + c / R) * AS + c % R] = acc[v];
-        }
-    }
+    if (tid <= c.ng) sRb[tid] = a.group_rbase[c.g0 + tid];
+    batch_prefix<N1, N2, R>(c, a.group_key, a.g1, a.g2, sG2, sP);
+    batch_tiles(sRb, sTp, c.ng, LK);
     __syncthreads();
 
     // ---- runs: tiles of LK runs of one group, spread over the waves; the
     // next tile's run index and G3 operand are fetched before this tile's math
-    const int ntile = sTp[ng];
+    const int ntile = sTp[c.ng];
     const int lk = col / N3, j3 = col % N3;
-    const float* G3 = a.g3 + o3 + j3 + KS * q * N3;
+    const float* G3 = a.g3 + c.o3 + j3 + KS * q * N3;
+    // wave w takes a contiguous range of tiles (consecutive tiles mostly share
+    // a group, so P is reloaded once per group)
+    const int per = (ntile + WAVES - 1) / WAVES;
+    const int t0 = min(ntile, w * per), t1 = min(ntile, t0 + per);
     int cur = -1, gnext = 0;
     float afr[MT][KS];
-    int tau = w;
+    int tau = t0;
     int32_t r = 0;
     bool valid = false;
     float bv[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) bv[s2] = 0.f;
-    if (tau < ntile) {
+    if (tau < t1) {
         while (sTp[gnext + 1] <= tau) ++gnext;
         r = sRb[gnext] + LK * (tau - sTp[gnext]) + lk;
         valid = r < sRb[gnext + 1];
@@ -218,7 +130,7 @@ __global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a) {
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
     }
-    for (; tau < ntile; tau += WAVES) {
+    for (; tau < t1; ++tau) {
         const int gi = gnext;
         if (gi != cur) {
             cur = gi;
@@ -228,13 +140,13 @@ __global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a) {
                 for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[(gi * NP + 16 * mt + col) * AS + KS * q + s2];
         }
         // prefetch the next tile
-        const int tn = tau + WAVES;
+        const int tn = tau + 1;
         int32_t rn = 0;
         bool vn = false;
         float bn[KS];
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) bn[s2] = 0.f;
-        if (tn < ntile) {
+        if (tn < t1) {
             while (sTp[gnext + 1] <= tn) ++gnext;
             rn = sRb[gnext] + LK * (tn - sTp[gnext]) + lk;
             vn = rn < sRb[gnext + 1];
@@ -312,10 +224,10 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
               p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.group_rbase),
               p->at<int32_t>(p->lay.run_i3), g1, g2, g3, p->at<float>(p->lay.stage)};
     if (p->L > 0 && p->n_fb > 0) {
-        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), 0, s, a);
         TT_LAUNCH_CHECK();
     }
-    constexpr int DL = FwdShape<N1, N2, R, N3>::D / 64;
+    constexpr int DL = N1 * N2 * N3 / 64;
     if (p->TB > 0) {
         hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),

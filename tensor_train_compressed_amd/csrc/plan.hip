@@ -18,11 +18,12 @@
 //   k_radix_hist      \  stable LSD radix sort of key*M3 + i3, 8 bits per pass:
 //   scan (1 or 3)      | per-tile digit counts, one exclusive scan over
 //   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
-//   k_gather          sorted i3 / bag, run heads, first and last position of each key
+//   k_gather          sorted i3 / bag, row-run heads, first and last position of each key
 //   k_key_flags       per key: present flag and chunk count
 //   scan              group id and first chunk of every present key
 //   k_groups          group tables, counts into the control words
-//   k_chunks          chunk table (one thread per chunk, search over groups)
+//   k_chunks          chunk table and cost-balanced task table (one thread per chunk)
+//   scan, k_runs      row-run ids (a row run = one (key, i3) row), run tables
 #include "tt_internal.h"
 
 #include <algorithm>
@@ -34,7 +35,7 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR) {
+                   int64_t M3, int64_t PR, int64_t E1, int64_t E3) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -51,9 +52,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
     y.ckey = take(l4);
     y.bag_start = take(sizeof(int32_t) * (size_t)((int64_t)T * B + 1));
-    y.run_head = take((size_t)L);
     y.rid = take(l4);
-    y.run_start = take(l4);
     y.run_i3 = take(l4);
     y.run_of = take(l4);
     y.stage = take(sizeof(float) * (size_t)L * (size_t)D);
@@ -81,6 +80,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
+    y.acc1 = take(sizeof(double) * (size_t)E1);
+    y.acc3 = take(sizeof(double) * (size_t)E3);
     y.total = off;
     return y;
 }
@@ -365,7 +366,6 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
                                                 int32_t* __restrict__ sorted_bag,
                                                 int32_t* __restrict__ key_start,
                                                 int32_t* __restrict__ key_end,
-                                                uint8_t* __restrict__ run_head,
                                                 int32_t* __restrict__ rid) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
@@ -374,11 +374,8 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
     const int32_t k = ck / M3;
     sorted_i3[s] = i3[l];
     sorted_bag[s] = bag_of[l];
-    // a run is a maximal stretch of one (key, i3) row in sorted order; for the
-    // backward's run_head, chunk starts also open a run (k_chunks marks those)
-    const int32_t h = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
-    run_head[s] = (uint8_t)h;
-    rid[s] = h;
+    // a row run is a maximal stretch of one (key, i3) row in sorted order
+    rid[s] = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
     if (s == 0 || skey[s - 1] / M3 != k) key_start[k] = (int32_t)s;
     if (s == L - 1 || skey[s + 1] / M3 != k) key_end[k] = (int32_t)(s + 1);
 }
@@ -431,7 +428,7 @@ __device__ __forceinline__ int32_t group_of_chunk(const int32_t* __restrict__ gr
     return lo;
 }
 
-// Chunk table, run heads at chunk starts, and the task table: chunk c starts
+// Chunk table and the task table: chunk c starts
 // at modelled cost begin(c) + kChunkCost*c; task t holds the chunks whose
 // start lies in [t*kTaskCost, (t+1)*kTaskCost) (some tasks may be empty).
 __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
@@ -440,7 +437,6 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
                                                 int32_t* __restrict__ chunk_group,
                                                 int32_t* __restrict__ chunk_begin,
                                                 int32_t* __restrict__ chunk_end,
-                                                uint8_t* __restrict__ run_head,
                                                 int32_t* __restrict__ task_start) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
@@ -451,7 +447,6 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     chunk_group[c] = g;
     chunk_begin[c] = b;
     chunk_end[c] = min(b + chunk, group_start[g + 1]);
-    run_head[b] = 1;
     const int64_t tc = ((int64_t)b + (int64_t)kChunkCost * c) / kTaskCost;
     int64_t tp = -1;
     if (c > 0) {
@@ -466,34 +461,29 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     }
 }
 
-// Row runs (maximal stretches of one (key, i3) row in sorted order; unlike the
-// backward's run_head flags, chunk starts do not cut them) from the scanned
-// head flags: rid[s] is now the number of row-run heads before position s.
+// Row-run tables from the scanned head flags. A row run is a maximal stretch
+// of one (key, i3) row in sorted order; after the scan, rid[s] holds the
+// number of row-run heads before sorted position s.
 __global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
                                               const int32_t* __restrict__ perm,
                                               const int32_t* __restrict__ skey,
                                               const int32_t* __restrict__ sorted_i3,
                                               const uint64_t* __restrict__ key_scan, int64_t L,
                                               int32_t M3, int32_t* ctrl,
-                                              int32_t* __restrict__ run_start,
                                               int32_t* __restrict__ run_i3,
                                               int32_t* __restrict__ run_of,
                                               int32_t* __restrict__ group_rbase) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
-    const int32_t r0 = rid[s];
-    const int32_t h = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
-    if (h) {
-        run_start[r0] = (int32_t)s;
-        run_i3[r0] = sorted_i3[s];
-    }
-    run_of[perm[s]] = r0 + h - 1;
+    const int32_t rr = rid[s];
+    const int32_t hr = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
+    if (hr) run_i3[rr] = sorted_i3[s];
+    run_of[perm[s]] = rr + hr - 1;
     const int32_t k = skey[s] / M3;
-    if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = r0;
+    if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = rr;
     if (s == L - 1) {
-        const int32_t nr = r0 + h;
-        ctrl[CTRL_NUM_RUNS] = nr;
-        group_rbase[ctrl[CTRL_NUM_GROUPS]] = nr;
+        ctrl[CTRL_NUM_RUNS] = rr + hr;
+        group_rbase[ctrl[CTRL_NUM_GROUPS]] = rr + hr;
     }
 }
 
@@ -505,10 +495,10 @@ using namespace tt;
 // host side
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
-                              int32_t* M3_out, int64_t* PR_out) {
+                              int32_t* M3_out, int64_t* PR_out, int64_t* E1_out, int64_t* E3_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
-    int64_t K = 0, PR = 1;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
     int32_t D = -1, M3 = 1;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
@@ -528,12 +518,16 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         if (K >= kMaxKeys) return TT_ERR_UNSUPPORTED;
         M3 = std::max(M3, x.m[2]);
         PR = std::max<int64_t>(PR, (int64_t)x.n[0] * x.n[1] * x.rank);
+        E1 = std::max<int64_t>(E1, x.g_offset[0] + (int64_t)x.m[0] * x.n[0] * x.rank);
+        E3 = std::max<int64_t>(E3, x.g_offset[2] + (int64_t)x.m[2] * x.rank * x.n[2]);
     }
     if (K * M3 >= (int64_t(1) << 31)) return TT_ERR_UNSUPPORTED;
     *K_out = K;
     *D_out = D;
     *M3_out = M3;
     *PR_out = PR;
+    *E1_out = E1;
+    *E3_out = E3;
     return TT_OK;
 }
 
@@ -547,11 +541,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 
 extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
                                          int64_t B, int32_t chunk) {
-    int64_t K = 0, PR = 1;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
     int32_t D = 0, M3 = 1;
-    if (check_tables(tables, T, &K, &D, &M3, &PR) != TT_OK) return 0;
+    if (check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -560,15 +554,15 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                  tt_emb_plan_t* plan_out) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
-    int64_t K = 0, PR = 1;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
     int32_t D = 0, M3 = 1;
-    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR);
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
@@ -678,7 +672,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
                                p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
-                               key_start, key_end, p->at<uint8_t>(lay.run_head), p->at<int32_t>(lay.rid));
+                               key_start, key_end, p->at<int32_t>(lay.rid));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
@@ -696,9 +690,9 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<uint8_t>(lay.run_head), p->at<int32_t>(lay.task_start));
+                               p->at<int32_t>(lay.task_start));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-            // run ids: exclusive scan of the head flags, then the run tables
+            // row-run ids: exclusive scan of the head flags, then the run tables
             if (scan_exclusive<uint32_t>(p->at<uint32_t>(lay.rid), L,
                                          reinterpret_cast<uint32_t*>(p->at<uint64_t>(lay.scan_tmp)),
                                          nullptr, s) != TT_OK)
@@ -706,8 +700,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_runs, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.rid), p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
                                p->at<int32_t>(lay.sorted_i3), p->at<uint64_t>(lay.key_scan), L, p->M3,
-                               ctrl, p->at<int32_t>(lay.run_start), p->at<int32_t>(lay.run_i3),
-                               p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.group_rbase));
+                               ctrl, p->at<int32_t>(lay.run_i3), p->at<int32_t>(lay.run_of),
+                               p->at<int32_t>(lay.group_rbase));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

@@ -31,7 +31,7 @@ enum CtrlSlot : int {
     CTRL_NUM_GROUPS = 1,
     CTRL_NUM_CHUNKS = 2,
     CTRL_NUM_TASKS = 3,
-    CTRL_NUM_RUNS = 4,
+    CTRL_NUM_RUNS = 4,    // row runs
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
     CTRL_QUEUE = 64,      // task-queue counters, one per 256-byte line:
                           // forward queues 0..7, backward queues 8..15
@@ -71,14 +71,12 @@ struct Layout {
     size_t key, i3, bag_of;                  // [L]
     size_t ckey;                             // [L] sort key = key * M3 + i3
     size_t bag_start;                        // [TB+1] int32 copy of the offsets
-    size_t run_head;                         // [L] uint8, sorted order: position starts a run
-                                             //     (a new (key, i3) row, or a chunk start)
-    size_t rid;                              // [L] int32, sorted order: row-run id (exclusive count of heads)
-    size_t run_start;                        // [L] int32: first sorted position of each run
+    size_t rid;                              // [L] int32, sorted order: number of row-run heads before s
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
-    size_t group_rbase;                      // [Gmax+1] int32: first run of each group
-    size_t stage;                            // [L][D] float: one row per run (indexed by run id)
+    size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
+    size_t stage;                            // [L][D] float, one row per row run: forward, the
+                                             //     run's embedding row; backward, its grad-row sum
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
     size_t hist;                             // [kRadixBins * n_tiles] uint32
@@ -89,13 +87,15 @@ struct Layout {
     size_t task_start;                       // [Tmax+1] first chunk of each task
     size_t scan_tmp;                         // uint64 partials of the multi-block scan
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
+    size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
+                                             //     dG3 accumulated in fp64 by the backward
     size_t total;
     int64_t n_tiles, K, Gmax, Cmax, Tmax;
     int passes;
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR);
+                   int64_t M3, int64_t PR, int64_t E1, int64_t E3);
 
 }  // namespace tt
 
