@@ -234,13 +234,7 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
 }
 
 struct BwdArgs {
-    const TabDev* desc;
-    int32_t T;
-    const int32_t* ctrl;
-    int64_t K;
-    const uint64_t* key_scan;
-    const int32_t* group_key;
-    const int32_t* group_rbase;
+    const BatchRec* recs;
     const int32_t* run_i3;
     const float* g1;
     const float* g2;
@@ -261,12 +255,11 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     __shared__ float sP[B::P_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sTp[SG + 1];
+    extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     BatchCtx c;
-    if (!batch_setup(a.desc, a.T, a.K, a.key_scan, a.ctrl, c)) return;
+    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sP, sRb, sI3, c)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    if (tid <= c.ng) sRb[tid] = a.group_rbase[c.g0 + tid];
-    batch_prefix<N1, N2, R>(c, a.group_key, a.g1, a.g2, sU, sP);
     batch_tiles(sRb, sTp, c.ng, LK);
     float* sDP = sU;
     for (int e = tid; e < SG * PR; e += 64 * WAVES) sDP[e] = 0.f;
@@ -277,7 +270,6 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     const float* G3 = a.g3 + c.o3;
     double* dG3 = a.dg3 + c.o3;
     int cur = -1;
-    float afT[RT][KSP];
     floatx4 dacc[MT][RT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -295,77 +287,110 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
                 dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
     };
-    // per-tile operands, fetched one tile ahead
-    struct TileOps {
-        int gi;
-        int32_t rbase, rend, i3;
-        bool valid;
-        float bv[KSP];
-    };
-    auto fetch = [&](int tt, int& g, TileOps& o) {
-        while (sTp[g + 1] <= tt) ++g;
-        o.gi = g;
-        o.rbase = sRb[g] + LK * (tt - sTp[g]);
-        o.rend = sRb[g + 1];
-        const int32_t r = o.rbase + lk;
-        o.valid = r < o.rend;
-        o.i3 = o.valid ? a.run_i3[r] : 0;
-        const float* Sb = a.S + (int64_t)(o.valid ? r : o.rbase) * D + j3;
-#pragma unroll
-        for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = o.valid ? Sb[(KSP * q + s2) * N3] : 0.f;
-    };
-    // wave w takes a contiguous range of tiles, so consecutive tiles mostly
-    // share a group and the dP flush and P reload happen once per group
+    // Wave w takes a contiguous range of tiles, so consecutive tiles mostly
+    // share a group and the dP flush and P reload happen once per group.
+    // A tile's S and G3 operands are loaded one tile ahead, before the
+    // current tile's dG3 atomics: loads and atomics share one in-order
+    // completion counter, so a load can only be waited for alone if every
+    // memory access issued after it is certain to have been issued. The loop
+    // body therefore holds no conditional load (the look-ahead tile is clamped
+    // to the last one, run i3 values come from LDS), it is unrolled by two with
+    // ping-pong operand sets, and no register that a load is still filling is
+    // ever copied.
     const int per = (ntile + WAVES - 1) / WAVES;
-    const int t0 = min(ntile, w * per), t1 = min(ntile, t0 + per);
-    TileOps cu, nx;
-    int gsearch = 0;
-    if (t0 < t1) fetch(t0, gsearch, cu);
-    for (int tau = t0; tau < t1; ++tau) {
-        if (tau + 1 < t1) fetch(tau + 1, gsearch, nx);
-        if (cu.gi != cur) {
-            if (cur >= 0) flush();
-            cur = cu.gi;
-            // A operand of P^T: lane (i, q) holds P[KSP*q + s][16*rt + i]
+    const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
+    struct Ids {
+        int g;
+        int32_t rbase, rend, i3;   // absolute run ids; i3 of this lane's run (run rbase's past the end)
+        bool ok;
+    };
+    struct Ops {
+        int g;
+        int32_t rbase, rend;
+        bool ok;
+        double* dst;          // dG3 slice of this lane's run, column j3
+        float bv[KSP];        // S of this lane's run, K = p (dG3 product)
+        float av[LK][MT];     // S of run ru, K = j3 (dP product)
+        float bq[LK][RT];     // G3[i3 of run ru], K = j3
+    };
+    int gs = 0;               // walks forward over the batch's groups
+    auto ids_of = [&](int k, Ids& o) {
+        const int tt = t0 + k;
+        while (sTp[gs + 1] <= tt) ++gs;
+        o.g = gs;
+        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]), re = sRb[gs + 1];   // relative to rb0
+        o.ok = rb + lk < re;
+        o.i3 = sI3[o.ok ? rb + lk : rb];
+        o.rbase = c.rb0 + rb;
+        o.rend = c.rb0 + re;
+    };
+    auto load_ops = [&](const Ids& o, Ops& x) {
+        x.g = o.g; x.rbase = o.rbase; x.rend = o.rend; x.ok = o.ok;
+        x.dst = dG3 + (int64_t)o.i3 * CN + j3;
+        const int32_t r = o.ok ? o.rbase + lk : o.rbase;
+        const float* Sb = a.S + (int64_t)r * D + j3;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+        for (int s2 = 0; s2 < KSP; ++s2) x.bv[s2] = Sb[(KSP * q + s2) * N3];
 #pragma unroll
-                for (int s2 = 0; s2 < KSP; ++s2) afT[rt][s2] = sP[(cur * NP + KSP * q + s2) * AS + 16 * rt + col];
+        for (int ru = 0; ru < LK; ++ru) {
+            const bool okr = o.rbase + ru < o.rend;
+            const int32_t i3r = __builtin_amdgcn_readlane(o.i3, ru * N3);
+            const float* Sr = a.S + (int64_t)(okr ? o.rbase + ru : o.rbase) * D;
+            const float* gb = G3 + (int64_t)i3r * CN;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) x.av[ru][mt] = Sr[(16 * mt + col) * N3 + q];
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) x.bq[ru][nt] = gb[(16 * nt + col) * N3 + q];
         }
-        // dG3[i3] += P^T S: column (run lk, j3), rows r2
+    };
+    auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
+        ids_of(min(k + 2, n - 1), Inew);
+        load_ops(Inext, Nx);
+        if (C.g != cur) {
+            if (cur >= 0) flush();
+            cur = C.g;
+        }
+        // dP += S G3[i3]^T: one k-step (k = j3) per run of the tile
+#pragma unroll
+        for (int ru = 0; ru < LK; ++ru) {
+            if (C.rbase + ru < C.rend) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < RT; ++nt)
+                        dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(C.av[ru][mt], C.bq[ru][nt], dacc[mt][nt], 0, 0, 0);
+            }
+        }
+        // dG3[i3] += P^T S: column (run lk, j3), rows r2. The A operand of P^T
+        // comes from LDS: lane (i, q) takes P[KSP*q + s][16*rt + i].
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             floatx4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KSP; ++s2)
-                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(afT[rt][s2], cu.bv[s2], cc, 0, 0, 0);
-            if (cu.valid) {
-                double* dst = dG3 + (int64_t)cu.i3 * CN + j3;
+                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(cur * NP + KSP * q + s2) * AS + 16 * rt + col],
+                                                          C.bv[s2], cc, 0, 0, 0);
+            // lanes past the group's last run add nothing (adding zeros
+            // instead measured slower: the extra atomics cost more than the
+            // conservative waits the branch brings)
+            if (C.ok) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) atomicAdd(dst + (16 * rt + 4 * q + v) * N3, (double)cc[v]);
+                for (int v = 0; v < 4; ++v) atomicAdd(C.dst + (16 * rt + 4 * q + v) * N3, (double)cc[v]);
             }
         }
-        // dP += S G3[i3]^T: one k-step (k = j3) per run of the tile
-#pragma unroll
-        for (int ru = 0; ru < LK; ++ru) {
-            const int32_t rr = cu.rbase + ru;
-            if (rr < cu.rend) {
-                const int32_t i3r = __builtin_amdgcn_readlane(cu.i3, ru * N3);
-                const float* Sr = a.S + (int64_t)rr * D;
-                const float* gb = G3 + (int64_t)i3r * CN;
-                float av[MT], bq[RT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) av[mt] = Sr[(16 * mt + col) * N3 + q];
-#pragma unroll
-                for (int nt = 0; nt < RT; ++nt) bq[nt] = gb[(16 * nt + col) * N3 + q];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt)
-                        dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mt], bq[nt], dacc[mt][nt], 0, 0, 0);
-            }
+    };
+    if (n > 0) {
+        Ids IA, IB;
+        Ops OA, OB;
+        ids_of(0, IA);
+        load_ops(IA, OA);
+        ids_of(min(1, n - 1), IB);
+        int k = 0;
+        for (; k + 1 < n; k += 2) {
+            step(k, OA, OB, IA, IB);
+            step(k + 1, OB, OA, IB, IA);
         }
-        cu = nx;
+        if (k < n) step(k, OA, OB, IA, IB);
     }
     if (cur >= 0) flush();
     __syncthreads();
@@ -503,11 +528,11 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                    p->at<float>(p->lay.stage)};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
-        BwdArgs a{p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
-                  p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.group_rbase),
-                  p->at<int32_t>(p->lay.run_i3), g1, g2, g3, p->at<float>(p->lay.stage), acc3,
-                  p->at<float>(p->lay.dpg)};
-        hipLaunchKernelGGL((k_bwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), 0, s, a);
+        BwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
+                  p->at<float>(p->lay.stage), acc3, p->at<float>(p->lay.dpg)};
+        const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
+        hipLaunchKernelGGL((k_bwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb),
+                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a);
         TT_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
@@ -525,6 +550,8 @@ static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
                          tt_status* st) {
     // the prefix build reads G2 rows as float4
     if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
+    // the batch's run i3 list is staged in LDS
+    if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
     if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
     if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }

@@ -72,18 +72,13 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 // on every run.
 
 struct FwdArgs {
-    const TabDev* desc;
-    int32_t T;
-    const int32_t* ctrl;
-    int64_t K;
-    const uint64_t* key_scan;
-    const int32_t* group_key;
-    const int32_t* group_rbase;
+    const BatchRec* recs;
     const int32_t* run_i3;
     const float* g1;
     const float* g2;
     const float* g3;
     float* stage;
+    int64_t L;             // first spare stage row
 };
 
 template <int N1, int N2, int R, int N3>
@@ -96,82 +91,92 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
     __shared__ float sP[B::P_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sTp[SG + 1];
+    extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     BatchCtx c;
-    if (!batch_setup(a.desc, a.T, a.K, a.key_scan, a.ctrl, c)) return;
+    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sG2, sP, sRb, sI3, c)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    if (tid <= c.ng) sRb[tid] = a.group_rbase[c.g0 + tid];
-    batch_prefix<N1, N2, R>(c, a.group_key, a.g1, a.g2, sG2, sP);
     batch_tiles(sRb, sTp, c.ng, LK);
     __syncthreads();
 
-    // ---- runs: tiles of LK runs of one group, spread over the waves; the
-    // next tile's run index and G3 operand are fetched before this tile's math
+    // ---- runs: tiles of LK runs of one group. Wave w takes a contiguous range
+    // of tiles (consecutive tiles mostly share a group, so P is reloaded once
+    // per group). A tile's G3 operand is loaded one tile ahead, before the
+    // current tile's stores: loads and stores share one in-order completion
+    // counter, so a load can only be waited for alone if every memory access
+    // issued after it is certain to have been issued. The loop body therefore
+    // holds no conditional access (inactive lanes store to a spare row, the
+    // look-ahead tile is clamped to the last one, run i3 values come from
+    // LDS), it is unrolled by two with ping-pong operand sets, and no register
+    // that a load is still filling is ever copied.
     const int ntile = sTp[c.ng];
+    const int per = (ntile + WAVES - 1) / WAVES;
+    const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
+    if (n <= 0) return;
     const int lk = col / N3, j3 = col % N3;
     const float* G3 = a.g3 + c.o3 + j3 + KS * q * N3;
-    // wave w takes a contiguous range of tiles (consecutive tiles mostly share
-    // a group, so P is reloaded once per group)
-    const int per = (ntile + WAVES - 1) / WAVES;
-    const int t0 = min(ntile, w * per), t1 = min(ntile, t0 + per);
-    int cur = -1, gnext = 0;
+    struct Ids {
+        int g;
+        int32_t r, i3;     // this lane's stage row (its run, or a spare row) and an i3 to read
+        bool ok;
+    };
+    struct Ops {
+        int g;
+        int32_t r;
+        float bv[KS];      // G3[i3] operand, K = r2
+    };
+    int gs = 0;            // walks forward over the batch's groups
+    auto ids_of = [&](int k, Ids& o) {
+        const int tt = t0 + k;
+        while (sTp[gs + 1] <= tt) ++gs;
+        o.g = gs;
+        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]);   // relative to rb0
+        const int32_t r = rb + lk;
+        o.ok = r < sRb[gs + 1];
+        o.r = o.ok ? c.rb0 + r : (int32_t)a.L + lk;
+        o.i3 = sI3[o.ok ? r : rb];
+    };
+    auto load_ops = [&](const Ids& o, Ops& x) {
+        x.g = o.g; x.r = o.r;
+        const float* gb = G3 + (int64_t)o.i3 * R * N3;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) x.bv[s2] = gb[s2 * N3];
+    };
+    int cur = -1;
     float afr[MT][KS];
-    int tau = t0;
-    int32_t r = 0;
-    bool valid = false;
-    float bv[KS];
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) bv[s2] = 0.f;
-    if (tau < t1) {
-        while (sTp[gnext + 1] <= tau) ++gnext;
-        r = sRb[gnext] + LK * (tau - sTp[gnext]) + lk;
-        valid = r < sRb[gnext + 1];
-        const float* gb = G3 + (int64_t)(valid ? a.run_i3[r] : 0) * R * N3;
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = gb[s2 * N3];
-    }
-    for (; tau < t1; ++tau) {
-        const int gi = gnext;
-        if (gi != cur) {
-            cur = gi;
+    auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
+        ids_of(min(k + 2, n - 1), Inew);
+        load_ops(Inext, Nx);
+        if (C.g != cur) {
+            cur = C.g;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[(gi * NP + 16 * mt + col) * AS + KS * q + s2];
+                for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
         }
-        // prefetch the next tile
-        const int tn = tau + 1;
-        int32_t rn = 0;
-        bool vn = false;
-        float bn[KS];
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) bn[s2] = 0.f;
-        if (tn < t1) {
-            while (sTp[gnext + 1] <= tn) ++gnext;
-            rn = sRb[gnext] + LK * (tn - sTp[gnext]) + lk;
-            vn = rn < sRb[gnext + 1];
-            const float* gb = G3 + (int64_t)(vn ? a.run_i3[rn] : 0) * R * N3;
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2) bn[s2] = gb[s2 * N3];
-        }
-        float* dst = a.stage + (int64_t)r * D + j3;
+        float* dst = a.stage + (int64_t)C.r * D + j3;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
-                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], bv[s2], cacc, 0, 0, 0);
+                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], C.bv[s2], cacc, 0, 0, 0);
             // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
-            if (valid) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dst[(16 * mt + 4 * q + v) * N3] = cacc[v];
-            }
+            for (int v = 0; v < 4; ++v) dst[(16 * mt + 4 * q + v) * N3] = cacc[v];
         }
-        r = rn;
-        valid = vn;
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) bv[s2] = bn[s2];
+    };
+    Ids IA, IB;
+    Ops OA, OB;
+    ids_of(0, IA);
+    load_ops(IA, OA);
+    ids_of(min(1, n - 1), IB);
+    int k = 0;
+    for (; k + 1 < n; k += 2) {
+        step(k, OA, OB, IA, IB);
+        step(k + 1, OB, OA, IB, IA);
     }
+    if (k < n) step(k, OA, OB, IA, IB);
 }
 
 // One wave per bag: sum the rows of the bag's lookups (in input order) from
@@ -220,11 +225,12 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 template <int N1, int N2, int R, int N3>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, hipStream_t s) {
-    FwdArgs a{p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
-              p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.group_rbase),
-              p->at<int32_t>(p->lay.run_i3), g1, g2, g3, p->at<float>(p->lay.stage)};
+    FwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
+              p->at<float>(p->lay.stage), p->L};
     if (p->L > 0 && p->n_fb > 0) {
-        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), 0, s, a);
+        const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
+        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb),
+                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a);
         TT_LAUNCH_CHECK();
     }
     constexpr int DL = N1 * N2 * N3 / 64;
@@ -242,6 +248,8 @@ static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
                          float* out, hipStream_t s, tt_status* st) {
     // the prefix build reads G2 rows as float4
     if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
+    // the batch's run i3 list is staged in LDS
+    if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
     if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, s); return true; }
     if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, s); return true; }

@@ -24,6 +24,7 @@
 //   k_groups          group tables, counts into the control words
 //   k_chunks          chunk table and cost-balanced task table (one thread per chunk)
 //   scan, k_runs      row-run ids (a row run = one (key, i3) row), run tables
+//   k_batches         one record per forward batch (kFwdBatch groups of one slice)
 #include "tt_internal.h"
 
 #include <algorithm>
@@ -35,7 +36,7 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t E1, int64_t E3) {
+                   int64_t M3, int64_t PR, int64_t E1, int64_t E3, int64_t NFB) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -55,7 +56,9 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.rid = take(l4);
     y.run_i3 = take(l4);
     y.run_of = take(l4);
-    y.stage = take(sizeof(float) * (size_t)L * (size_t)D);
+    // one row per row run, plus kStageSpare rows that take the writes of
+    // inactive lanes (kept branch-free) in the forward
+    y.stage = take(sizeof(float) * ((size_t)L + kStageSpare) * (size_t)D);
     y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
     y.skey = take(l4);
     // The radix passes ping-pong between (skey, perm) and a temporary pair that
@@ -82,6 +85,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);
+    y.NFB = NFB;
+    y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
     return y;
 }
@@ -487,6 +492,46 @@ __global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
     }
 }
 
+// One thread per forward batch slot (table t, i2, j): the j-th run of
+// kFwdBatch groups among the groups of slice (t, i2), which are consecutive in
+// key order. Writes the batch's record; ng = 0 when the slot has no group.
+__global__ __launch_bounds__(256) void k_batches(const TabDev* __restrict__ desc, int32_t T, int64_t K,
+                                                 int64_t NFB, const uint64_t* __restrict__ key_scan,
+                                                 const int32_t* __restrict__ group_key,
+                                                 const int32_t* __restrict__ group_rbase,
+                                                 const int32_t* __restrict__ ctrl,
+                                                 BatchRec* __restrict__ rec) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= NFB) return;
+    int lo = 0, hi = T;   // last table with fb_base <= b
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
+    }
+    const TabDev d = desc[lo];
+    const int32_t nb = (d.m1 + kFwdBatch - 1) / kFwdBatch;
+    const int32_t i2 = (int32_t)((b - d.fb_base) / nb), jb = (int32_t)((b - d.fb_base) % nb);
+    const int64_t kb = (int64_t)d.key_base + (int64_t)i2 * d.m1, ke = kb + d.m1;
+    const int32_t gs0 = (int32_t)(key_scan[kb] >> 32);
+    const int32_t gs1 = ke < K ? (int32_t)(key_scan[ke] >> 32) : ctrl[CTRL_NUM_GROUPS];
+    BatchRec r;
+    memset(&r, 0, sizeof(r));
+    r.g0 = gs0 + kFwdBatch * jb;
+    r.ng = max(0, min(kFwdBatch, gs1 - r.g0));
+    r.i2 = i2;
+    r.o1 = d.o1; r.o2 = d.o2; r.o3 = d.o3;
+    if (r.ng > 0) {
+        r.rb0 = group_rbase[r.g0];
+        for (int j = 0; j < kFwdBatch; ++j) {
+            if (j < r.ng) r.i1[j] = (int32_t)(group_key[r.g0 + j] - kb);
+            r.rbase[j] = group_rbase[r.g0 + min(j, r.ng)] - r.rb0;
+        }
+        r.nr = group_rbase[r.g0 + r.ng] - r.rb0;
+        r.rbase[kFwdBatch] = r.nr;
+    }
+    rec[b] = r;
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -495,10 +540,11 @@ using namespace tt;
 // host side
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
-                              int32_t* M3_out, int64_t* PR_out, int64_t* E1_out, int64_t* E3_out) {
+                              int32_t* M3_out, int64_t* PR_out, int64_t* E1_out, int64_t* E3_out,
+                              int64_t* NFB_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = -1, M3 = 1;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
@@ -517,6 +563,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         K += (int64_t)x.m[0] * x.m[1];
         if (K >= kMaxKeys) return TT_ERR_UNSUPPORTED;
         M3 = std::max(M3, x.m[2]);
+        NFB += (int64_t)x.m[1] * ((x.m[0] + kFwdBatch - 1) / kFwdBatch);
         PR = std::max<int64_t>(PR, (int64_t)x.n[0] * x.n[1] * x.rank);
         E1 = std::max<int64_t>(E1, x.g_offset[0] + (int64_t)x.m[0] * x.n[0] * x.rank);
         E3 = std::max<int64_t>(E3, x.g_offset[2] + (int64_t)x.m[2] * x.rank * x.n[2]);
@@ -528,6 +575,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
     *PR_out = PR;
     *E1_out = E1;
     *E3_out = E3;
+    *NFB_out = NFB;
     return TT_OK;
 }
 
@@ -541,11 +589,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 
 extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
                                          int64_t B, int32_t chunk) {
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = 0, M3 = 1;
-    if (check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3) != TT_OK) return 0;
+    if (check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3, &NFB) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3, NFB).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -554,15 +602,15 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                  tt_emb_plan_t* plan_out) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0;
+    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = 0, M3 = 1;
-    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3);
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3, &NFB);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3, NFB);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
@@ -702,6 +750,12 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.sorted_i3), p->at<uint64_t>(lay.key_scan), L, p->M3,
                                ctrl, p->at<int32_t>(lay.run_i3), p->at<int32_t>(lay.run_of),
                                p->at<int32_t>(lay.group_rbase));
+            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        }
+        if (lay.NFB > 0) {
+            hipLaunchKernelGGL(k_batches, dim3(grid_for(lay.NFB, 256)), dim3(256), 0, s, p->desc(), T, K,
+                               lay.NFB, kscan, p->at<int32_t>(lay.group_key),
+                               p->at<int32_t>(lay.group_rbase), ctrl, p->at<BatchRec>(lay.batch));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
     }

@@ -135,42 +135,16 @@ inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blo
 
 // ---------------------------------------------------------------------------
 // Prefix batches: up to kFwdBatch groups of one (table, i2) slice, one
-// workgroup. batch_setup maps blockIdx to the batch; batch_prefix reads the G2
-// slice into LDS and forms every group's P = G1[i1] x G2[i2] as one
-// (4*batch) x (n2*R) x R product on the matrix cores, into sP[g][p][AS].
+// workgroup, described by the planner's BatchRec. batch_begin reads the record,
+// then issues every load the batch needs at once (G2 slice, G1 rows, the run
+// i3 list), so the prologue costs two dependent round trips; it stages the G2
+// slice and the run i3 list in LDS and forms every group's P = G1[i1] x G2[i2]
+// as one (4*batch) x (n2*R) x R product on the matrix cores, into sP[g][p][AS].
 
 struct BatchCtx {
-    int32_t i2, g0, ng;
-    int64_t kb, o1, o2, o3;
+    int32_t g0, ng, rb0, nr;
+    int64_t o3;
 };
-
-__device__ __forceinline__ bool batch_setup(const TabDev* __restrict__ desc, int32_t T, int64_t K,
-                                            const uint64_t* __restrict__ key_scan,
-                                            const int32_t* __restrict__ ctrl, BatchCtx& c) {
-    const int32_t b = blockIdx.x;
-    int t = 0;
-    {
-        int lo = 0, hi = T;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
-        }
-        t = lo;
-    }
-    const TabDev* dp = desc + t;
-    const int32_t m1 = dp->m1, fb = dp->fb_base;
-    c.o1 = dp->o1; c.o2 = dp->o2; c.o3 = dp->o3;
-    const int32_t nb = (m1 + kFwdBatch - 1) / kFwdBatch;
-    c.i2 = (b - fb) / nb;
-    const int32_t jb = (b - fb) % nb;
-    c.kb = (int64_t)dp->key_base + (int64_t)c.i2 * m1;
-    const int64_t ke = c.kb + m1;
-    const int32_t gs0 = (int32_t)(key_scan[c.kb] >> 32);
-    const int32_t gs1 = ke < K ? (int32_t)(key_scan[ke] >> 32) : ctrl[CTRL_NUM_GROUPS];
-    c.g0 = gs0 + kFwdBatch * jb;
-    c.ng = min(kFwdBatch, gs1 - c.g0);
-    return c.g0 < gs1;
-}
 
 template <int N1, int N2, int R>
 struct PrefixBatch {
@@ -185,46 +159,55 @@ struct PrefixBatch {
     static_assert(WAVES % MTP == 0, "prefix batch wave split");
 };
 
-// Called by all WAVES waves; ends with the block synchronised and sP complete.
+// Called by all WAVES waves of the block. Returns false (for the whole block)
+// when the batch holds no group; otherwise sRb[0..ng] = the groups' first row
+// runs relative to rb0, sI3[0..nr) = the batch's run i3 values, sP is complete
+// and the block is synchronised.
 template <int N1, int N2, int R>
-__device__ __forceinline__ void batch_prefix(const BatchCtx& c, const int32_t* __restrict__ group_key,
-                                             const float* __restrict__ g1, const float* __restrict__ g2,
-                                             float* sG2, float* sP) {
+__device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs,
+                                            const int32_t* __restrict__ run_i3,
+                                            const float* __restrict__ g1, const float* __restrict__ g2,
+                                            float* sG2, float* sP, int32_t* sRb, int32_t* sI3,
+                                            BatchCtx& c) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int NP = B::NP, N2R = B::N2R, MTP = B::MTP, KS = B::KS, GS = B::GS, AS = B::AS;
     constexpr int WAVES = B::WAVES, NT2 = B::NT2;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    {
-        const float4* G2s = reinterpret_cast<const float4*>(g2 + c.o2 + (int64_t)c.i2 * R * N2R);
-        constexpr int NQ = R * N2R / 4, NV = (NQ + 64 * WAVES - 1) / (64 * WAVES);
-        constexpr bool even = NQ % (64 * WAVES) == 0;
-        float4 v[NV];
+    const BatchRec* rec = recs + blockIdx.x;
+    c.ng = rec->ng;
+    if (c.ng <= 0) return false;
+    c.g0 = rec->g0; c.rb0 = rec->rb0; c.nr = rec->nr; c.o3 = rec->o3;
+    // the G2 slice: R rows of N2*R floats, read as float4
+    constexpr int NQ = R * N2R / 4, NV = (NQ + 64 * WAVES - 1) / (64 * WAVES);
+    constexpr bool even = NQ % (64 * WAVES) == 0;
+    const float4* G2s = reinterpret_cast<const float4*>(g2 + rec->o2 + (int64_t)rec->i2 * R * N2R);
+    float4 v[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int e4 = tid + 64 * WAVES * k;
-            v[k] = (even || e4 < NQ) ? G2s[even ? e4 : min(e4, NQ - 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int e4 = tid + 64 * WAVES * k;
-            if (even || e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
-        }
+    for (int k = 0; k < NV; ++k) {
+        const int e4 = tid + 64 * WAVES * k;
+        v[k] = (even || e4 < NQ) ? G2s[even ? e4 : min(e4, NQ - 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const int mtp = w % MTP;                  // prefix row tile: groups 4*mtp .. 4*mtp+3
     const int gA = 4 * mtp + col / N1;        // group of this lane's A row (col = 4*(g%4) + j1)
     float af[KS];
     {
-        const bool live = gA < c.ng;
-        const int32_t i1 = live ? (int32_t)(group_key[c.g0 + gA] - c.kb) : 0;
-        const float* G1r = g1 + c.o1 + (int64_t)i1 * N1 * R + (col % N1) * R;
+        const float* G1r = g1 + rec->o1 + (int64_t)rec->i1[gA] * N1 * R + (col % N1) * R;
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) af[s2] = live ? G1r[4 * s2 + q] : 0.f;
+        for (int s2 = 0; s2 < KS; ++s2) af[s2] = G1r[4 * s2 + q];   // zero rows: see below
+    }
+    if (tid <= kFwdBatch) sRb[tid] = rec->rbase[tid];
+    for (int e = tid; e < c.nr; e += 64 * WAVES) sI3[e] = run_i3[c.rb0 + e];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int e4 = tid + 64 * WAVES * k;
+        if (even || e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
     }
     __syncthreads();
     if (4 * mtp < c.ng) {
-        // output tiles t = w, w + WAVES, ...: row tile t % MTP (= mtp), column tile t / MTP
-        for (int t = w; t < NT2 * MTP; t += WAVES) {
-            const int nt = t / MTP;
+        // rows of groups past ng hold G1[0] (the record's i1 is 0 there); their
+        // P rows are written but never read
+        for (int t2 = w; t2 < NT2 * MTP; t2 += WAVES) {
+            const int nt = t2 / MTP;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
@@ -233,10 +216,11 @@ __device__ __forceinline__ void batch_prefix(const BatchCtx& c, const int32_t* _
             // C row 4q+v = (group 4*mtp+q, j1 v); column c = 16nt + col = (j2, r2)
             const int gi = 4 * mtp + q, cc = 16 * nt + col;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sP[(gi * NP + v * N2 + cc / R) * AS + cc % R] = acc[v];
+            for (int v2 = 0; v2 < 4; ++v2) sP[(gi * NP + v2 * N2 + cc / R) * AS + cc % R] = acc[v2];
         }
     }
     __syncthreads();
+    return true;
 }
 
 // Tile prefix over the batch's groups: sTp[g+1] - sTp[g] = ceil(runs(g) / per).

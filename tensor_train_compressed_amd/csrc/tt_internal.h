@@ -47,6 +47,28 @@ constexpr int kChunkCost = 32;
 constexpr int kXcds = 8;
 // Forward work unit: up to this many prefix groups of one (table, i2) slice.
 constexpr int kFwdBatch = 8;
+// Spare stage rows after the L run rows (targets of inactive lanes' stores).
+constexpr int kStageSpare = 4;
+// LDS the batch kernels may spend on the run i3 list of one batch
+// (kFwdBatch * largest m3 int32 values); larger m3 takes the generic kernels.
+constexpr int kMaxBatchI3Bytes = 32768;
+
+// One forward batch as the planner describes it to the batch kernels: up to
+// kFwdBatch groups of one (table, i2) slice, consecutive in key order.
+struct alignas(16) BatchRec {
+    int32_t ng;                    // groups in the batch (0: nothing to do)
+    int32_t g0;                    // first group
+    int32_t i2;                    // slice index inside the table
+    int32_t rb0;                   // first row run of the batch
+    int32_t nr;                    // row runs of the batch
+    int32_t pad0[3];
+    int64_t o1, o2, o3;            // the table's core offsets
+    int32_t pad1[2];
+    int32_t i1[kFwdBatch];         // i1 of each group (0 past ng)
+    int32_t rbase[kFwdBatch + 1];  // first row run of each group, relative to rb0; then nr
+    int32_t pad2[7];
+};
+static_assert(sizeof(BatchRec) == 160, "BatchRec layout");
 
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
@@ -75,7 +97,7 @@ struct Layout {
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
     size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
-    size_t stage;                            // [L][D] float, one row per row run: forward, the
+    size_t stage;                            // [L + kStageSpare][D] float, one row per row run: forward, the
                                              //     run's embedding row; backward, its grad-row sum
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
@@ -89,13 +111,14 @@ struct Layout {
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
+    size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, K, Gmax, Cmax, Tmax;
+    int64_t n_tiles, K, Gmax, Cmax, Tmax, NFB;
     int passes;
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t E1, int64_t E3);
+                   int64_t M3, int64_t PR, int64_t E1, int64_t E3, int64_t NFB);
 
 }  // namespace tt
 
