@@ -250,18 +250,17 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     constexpr int NP = B::NP, D = NP * N3, PR = NP * R, SG = B::SG, AS = B::AS, WAVES = B::WAVES;
     constexpr int MT = NP / 16, RT = R / 16, KSP = NP / 4, LK = 16 / N3, CN = R * N3;
     static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0, "shape");
-    constexpr int U_FLOATS = B::G2_FLOATS > SG * PR ? B::G2_FLOATS : SG * PR;
-    __shared__ __attribute__((aligned(16))) float sU[U_FLOATS];   // G2 slice, then dP of the batch
-    __shared__ float sP[B::P_FLOATS];
+    __shared__ float sDP[SG * PR];   // dP of the batch's groups
+    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sTp[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     BatchCtx c;
-    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sP, sRb, sI3, c)) return;
+    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
+    const float* sP = sU;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
     batch_tiles(sRb, sTp, c.ng, LK);
-    float* sDP = sU;
     for (int e = tid; e < SG * PR; e += 64 * WAVES) sDP[e] = 0.f;
     __syncthreads();
 
@@ -548,8 +547,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                          const float* gout, float* dg1, float* dg2, float* dg3, hipStream_t s,
                          tt_status* st) {
-    // the prefix build reads G2 rows as float4
-    if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
+    // the prologue reads G1 rows and the G2 slice as 16-byte vectors
+    if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;

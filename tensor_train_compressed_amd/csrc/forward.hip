@@ -87,28 +87,33 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
     constexpr int NP = B::NP, D = NP * N3, SG = B::SG, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
     constexpr int MT = NP / 16, LK = 16 / N3;
     static_assert(N3 == 4 && NP % 16 == 0, "shape");
-    __shared__ __attribute__((aligned(16))) float sG2[B::G2_FLOATS];
-    __shared__ float sP[B::P_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sTp[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     BatchCtx c;
-    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sG2, sP, sRb, sI3, c)) return;
+    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
+    const float* sP = sU;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
     batch_tiles(sRb, sTp, c.ng, LK);
     __syncthreads();
 
-    // ---- runs: tiles of LK runs of one group. Wave w takes a contiguous range
-    // of tiles (consecutive tiles mostly share a group, so P is reloaded once
-    // per group). A tile's G3 operand is loaded one tile ahead, before the
-    // current tile's stores: loads and stores share one in-order completion
-    // counter, so a load can only be waited for alone if every memory access
-    // issued after it is certain to have been issued. The loop body therefore
-    // holds no conditional access (inactive lanes store to a spare row, the
-    // look-ahead tile is clamped to the last one, run i3 values come from
-    // LDS), it is unrolled by two with ping-pong operand sets, and no register
-    // that a load is still filling is ever copied.
+    // ---- runs: tiles of LK = 4 runs of one group. The suffix product of a
+    // tile is E^T = G3[i3]^T P^T: rows (run, j3), columns p, K = r2. Lane
+    // (col, q) feeds G3 of run col/4 as the A operand and P row 16mt + col as
+    // the B operand, and receives E[run q][p = 16mt + col][j3 = 0..3]: four
+    // consecutive floats of that run's row, written with one 16-byte store.
+    // Wave w takes a contiguous range of tiles (consecutive tiles mostly share
+    // a group, so P is reloaded once per group). A tile's G3 operand is loaded
+    // one tile ahead, before the current tile's stores: loads and stores share
+    // one in-order completion counter, so a load can only be waited for alone
+    // if every memory access issued after it is certain to have been issued.
+    // The loop body therefore holds no conditional access (lanes past the
+    // group's last run store to a spare row, the look-ahead tile is clamped to
+    // the last one, run i3 values come from LDS), it is unrolled by two with
+    // ping-pong operand sets, and no register that a load is still filling is
+    // ever copied.
     const int ntile = sTp[c.ng];
     const int per = (ntile + WAVES - 1) / WAVES;
     const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
@@ -117,24 +122,22 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
     const float* G3 = a.g3 + c.o3 + j3 + KS * q * N3;
     struct Ids {
         int g;
-        int32_t r, i3;     // this lane's stage row (its run, or a spare row) and an i3 to read
-        bool ok;
+        int32_t r;         // stage row of run q of the tile (a spare row past the group's end)
+        int32_t i3;        // i3 of run lk of the tile (run 0's past the end)
     };
     struct Ops {
         int g;
         int32_t r;
-        float bv[KS];      // G3[i3] operand, K = r2
+        float bv[KS];      // G3[i3 of run lk][r2][j3], K = r2
     };
     int gs = 0;            // walks forward over the batch's groups
     auto ids_of = [&](int k, Ids& o) {
         const int tt = t0 + k;
         while (sTp[gs + 1] <= tt) ++gs;
         o.g = gs;
-        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]);   // relative to rb0
-        const int32_t r = rb + lk;
-        o.ok = r < sRb[gs + 1];
-        o.r = o.ok ? c.rb0 + r : (int32_t)a.L + lk;
-        o.i3 = sI3[o.ok ? r : rb];
+        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]), re = sRb[gs + 1];   // relative to rb0
+        o.r = rb + q < re ? c.rb0 + rb + q : (int32_t)a.L + q;
+        o.i3 = sI3[rb + lk < re ? rb + lk : rb];
     };
     auto load_ops = [&](const Ids& o, Ops& x) {
         x.g = o.g; x.r = o.r;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
         for (int s2 = 0; s2 < KS; ++s2) x.bv[s2] = gb[s2 * N3];
     };
     int cur = -1;
-    float afr[MT][KS];
+    float bp[MT][KS];      // P[16mt + col][KS*q + s2]
     auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
         ids_of(min(k + 2, n - 1), Inew);
         load_ops(Inext, Nx);
@@ -152,18 +155,16 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) afr[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
+                for (int s2 = 0; s2 < KS; ++s2) bp[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
         }
-        float* dst = a.stage + (int64_t)C.r * D + j3;
+        float* dst = a.stage + (int64_t)C.r * D + col * N3;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+            floatx4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
-                cacc = __builtin_amdgcn_mfma_f32_16x16x4f32(afr[mt][s2], C.bv[s2], cacc, 0, 0, 0);
-            // C[i][j]: lane holds rows 4q+v of column col -> p = 16mt + 4q + v
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dst[(16 * mt + 4 * q + v) * N3] = cacc[v];
+                e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2], bp[mt][s2], e, 0, 0, 0);
+            *reinterpret_cast<floatx4*>(dst + 16 * mt * N3) = e;
         }
     };
     Ids IA, IB;
@@ -246,8 +247,8 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 // Returns true (and launches) when the plan's shape has a matrix-core kernel.
 static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                          float* out, hipStream_t s, tt_status* st) {
-    // the prefix build reads G2 rows as float4
-    if (!p->uniform || !p->off4 || ((uintptr_t)g2 & 15) != 0) return false;
+    // the prologue reads G1 rows and the G2 slice as 16-byte vectors
+    if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;

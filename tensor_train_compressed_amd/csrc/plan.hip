@@ -632,7 +632,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     p->packed = true;
     p->off4 = true;
     for (int32_t t = 0; t < T; ++t) {
-        if (tables[t].g_offset[1] % 4 != 0) p->off4 = false;
+        if (tables[t].g_offset[0] % 4 != 0 || tables[t].g_offset[1] % 4 != 0) p->off4 = false;
         const tt_emb_table& x = tables[t];
         if (x.n[0] != p->n1 || x.n[1] != p->n2 || x.n[2] != p->n3 || x.rank != p->R) p->uniform = false;
         const int64_t R = x.rank;

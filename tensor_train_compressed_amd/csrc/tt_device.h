@@ -136,10 +136,11 @@ inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blo
 // ---------------------------------------------------------------------------
 // Prefix batches: up to kFwdBatch groups of one (table, i2) slice, one
 // workgroup, described by the planner's BatchRec. batch_begin reads the record,
-// then issues every load the batch needs at once (G2 slice, G1 rows, the run
-// i3 list), so the prologue costs two dependent round trips; it stages the G2
-// slice and the run i3 list in LDS and forms every group's P = G1[i1] x G2[i2]
-// as one (4*batch) x (n2*R) x R product on the matrix cores, into sP[g][p][AS].
+// then issues every load the batch needs at once (G2 slice and G1 rows as
+// coalesced 16-byte loads, the run i3 list), so the prologue costs two
+// dependent round trips. The G2 slice and the G1 rows go to LDS; every group's
+// P = G1[i1] x G2[i2] is then formed as one (4*batch) x (n2*R) x R product on
+// the matrix cores, and P is written over the same LDS (sP[g][p][AS]).
 
 struct BatchCtx {
     int32_t g0, ng, rb0, nr;
@@ -151,72 +152,101 @@ struct PrefixBatch {
     static constexpr int NP = N1 * N2, N2R = N2 * R, SG = kFwdBatch;
     static constexpr int MR = SG * N1, MTP = MR / 16, NT2 = N2R / 16, KS = R / 4;
     static constexpr int GS = N2R + 16;      // LDS row stride of the G2 slice
-    static constexpr int AS = R + 4;         // LDS row stride of P rows
+    static constexpr int AS = R + 4;         // LDS row stride of G1 rows and of P rows
     static constexpr int WAVES = 8;
+    static constexpr int NTW = (NT2 + WAVES - 1) / WAVES;   // column tiles per wave
     static constexpr int G2_FLOATS = R * GS;
+    static constexpr int G1_FLOATS = MR * AS;
     static constexpr int P_FLOATS = SG * NP * AS;
-    static_assert(N1 == 4 && MR % 16 == 0 && N2R % 32 == 0 && R % 4 == 0, "prefix batch shape");
-    static_assert(WAVES % MTP == 0, "prefix batch wave split");
+    // LDS of the prologue: G2 slice then G1 rows; P is written over them
+    static constexpr int U_FLOATS = (G2_FLOATS + G1_FLOATS) > P_FLOATS ? (G2_FLOATS + G1_FLOATS) : P_FLOATS;
+    static_assert(N1 == 4 && MR % 16 == 0 && N2R % 16 == 0 && R % 4 == 0, "prefix batch shape");
 };
 
 // Called by all WAVES waves of the block. Returns false (for the whole block)
 // when the batch holds no group; otherwise sRb[0..ng] = the groups' first row
-// runs relative to rb0, sI3[0..nr) = the batch's run i3 values, sP is complete
-// and the block is synchronised.
+// runs relative to rb0, sI3[0..nr) = the batch's run i3 values, sU holds P
+// (row (g*NP + p) at stride AS) and the block is synchronised.
 template <int N1, int N2, int R>
 __device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs,
                                             const int32_t* __restrict__ run_i3,
                                             const float* __restrict__ g1, const float* __restrict__ g2,
-                                            float* sG2, float* sP, int32_t* sRb, int32_t* sI3,
-                                            BatchCtx& c) {
+                                            float* sU, int32_t* sRb, int32_t* sI3, BatchCtx& c) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int NP = B::NP, N2R = B::N2R, MTP = B::MTP, KS = B::KS, GS = B::GS, AS = B::AS;
-    constexpr int WAVES = B::WAVES, NT2 = B::NT2;
+    constexpr int WAVES = B::WAVES, NT2 = B::NT2, NTW = B::NTW, NT = 64 * WAVES;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
     const BatchRec* rec = recs + blockIdx.x;
     c.ng = rec->ng;
     if (c.ng <= 0) return false;
     c.g0 = rec->g0; c.rb0 = rec->rb0; c.nr = rec->nr; c.o3 = rec->o3;
-    // the G2 slice: R rows of N2*R floats, read as float4
-    constexpr int NQ = R * N2R / 4, NV = (NQ + 64 * WAVES - 1) / (64 * WAVES);
-    constexpr bool even = NQ % (64 * WAVES) == 0;
+    // G2 slice: R rows of N2*R floats
+    constexpr int NQ = R * N2R / 4, NV = (NQ + NT - 1) / NT;
     const float4* G2s = reinterpret_cast<const float4*>(g2 + rec->o2 + (int64_t)rec->i2 * R * N2R);
     float4 v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        const int e4 = tid + 64 * WAVES * k;
-        v[k] = (even || e4 < NQ) ? G2s[even ? e4 : min(e4, NQ - 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int e4 = min(tid + NT * k, NQ - 1);
+        v[k] = G2s[e4];
     }
-    const int mtp = w % MTP;                  // prefix row tile: groups 4*mtp .. 4*mtp+3
-    const int gA = 4 * mtp + col / N1;        // group of this lane's A row (col = 4*(g%4) + j1)
-    float af[KS];
-    {
-        const float* G1r = g1 + rec->o1 + (int64_t)rec->i1[gA] * N1 * R + (col % N1) * R;
+    // G1 rows of the batch's groups: N1*R floats each (groups past ng read G1[0]:
+    // the record's i1 is 0 there; their P rows are written but never read)
+    constexpr int NQ1 = kFwdBatch * N1 * R / 4, NV1 = (NQ1 + NT - 1) / NT, Q1 = N1 * R / 4;
+    float4 u[NV1];
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) af[s2] = G1r[4 * s2 + q];   // zero rows: see below
+    for (int k = 0; k < NV1; ++k) {
+        const int f = min(tid + NT * k, NQ1 - 1);
+        u[k] = reinterpret_cast<const float4*>(g1 + rec->o1 + (int64_t)rec->i1[f / Q1] * N1 * R)[f % Q1];
     }
     if (tid <= kFwdBatch) sRb[tid] = rec->rbase[tid];
-    for (int e = tid; e < c.nr; e += 64 * WAVES) sI3[e] = run_i3[c.rb0 + e];
+    for (int e = tid; e < c.nr; e += NT) sI3[e] = run_i3[c.rb0 + e];
+    float* sG2 = sU;
+    float* sG1 = sU + B::G2_FLOATS;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        const int e4 = tid + 64 * WAVES * k;
-        if (even || e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
+        const int e4 = tid + NT * k;
+        if (e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NV1; ++k) {
+        const int f = tid + NT * k;   // group f / Q1, element 4*(f % Q1) = (j1, r1)
+        if (f < NQ1) {
+            const int e = 4 * (f % Q1);
+            *reinterpret_cast<float4*>(sG1 + ((f / Q1) * N1 + e / R) * AS + e % R) = u[k];
+        }
     }
     __syncthreads();
-    if (4 * mtp < c.ng) {
-        // rows of groups past ng hold G1[0] (the record's i1 is 0 there); their
-        // P rows are written but never read
-        for (int t2 = w; t2 < NT2 * MTP; t2 += WAVES) {
-            const int nt = t2 / MTP;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // wave w: column tiles nt = w + WAVES*k, every row tile mt (row 16mt + i =
+    // group 4mt + i/N1, j1 = i%N1); K = r1
+    floatx4 acc[NTW][MTP];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+        const int nt = min(w + WAVES * k, NT2 - 1);
+        float bf[KS];
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) bf[s2] = sG2[(4 * s2 + q) * GS + 16 * nt + col];
+#pragma unroll
+        for (int mt = 0; mt < MTP; ++mt) {
+            acc[k][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[s2], sG2[(4 * s2 + q) * GS + 16 * nt + col],
-                                                           acc, 0, 0, 0);
-            // C row 4q+v = (group 4*mtp+q, j1 v); column c = 16nt + col = (j2, r2)
-            const int gi = 4 * mtp + q, cc = 16 * nt + col;
+                acc[k][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sG1[(16 * mt + col) * AS + 4 * s2 + q], bf[s2],
+                                                                  acc[k][mt], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    float* sP = sU;
 #pragma unroll
-            for (int v2 = 0; v2 < 4; ++v2) sP[(gi * NP + v2 * N2 + cc / R) * AS + cc % R] = acc[v2];
+    for (int k = 0; k < NTW; ++k) {
+        const int nt = w + WAVES * k;
+        if (nt < NT2) {
+#pragma unroll
+            for (int mt = 0; mt < MTP; ++mt) {
+                // C row 4q+v2 = (group 4mt+q, j1 v2); column cc = 16nt + col = (j2, r2)
+                const int gi = 4 * mt + q, cc = 16 * nt + col;
+#pragma unroll
+                for (int v2 = 0; v2 < 4; ++v2) sP[(gi * NP + v2 * N2 + cc / R) * AS + cc % R] = acc[k][mt][v2];
+            }
         }
     }
     __syncthreads();

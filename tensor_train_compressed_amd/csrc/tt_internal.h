@@ -136,7 +136,7 @@ struct tt_emb_plan_s {
     int32_t n1, n2, n3, R;    // the shared shape when uniform
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
     bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
-    bool off4;                // every table's G2 offset is a multiple of 4 floats
+    bool off4;                // every table's G1 and G2 offsets are multiples of 4 floats
     char* ws;                 // workspace base (device)
     tt::Layout lay;
     std::vector<tt_emb_table> tables;
