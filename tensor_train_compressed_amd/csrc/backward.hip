@@ -235,6 +235,7 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
 
 struct BwdArgs {
     const BatchRec* recs;
+    int64_t nb;
     const int32_t* run_i3;
     const float* g1;
     const float* g2;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     BatchCtx c;
-    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
+    if (!batch_begin<N1, N2, R>(a.recs, a.nb, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
     const float* sP = sU;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
     batch_tiles(sRb, sTp, c.ng, LK);
@@ -527,7 +528,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                    p->at<float>(p->lay.stage)};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
-        BwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
+        BwdArgs a{p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
                   p->at<float>(p->lay.stage), acc3, p->at<float>(p->lay.dpg)};
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         hipLaunchKernelGGL((k_bwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb),

@@ -81,39 +81,27 @@ struct FwdArgs {
     int64_t L;             // first spare stage row
 };
 
+// The runs of one batch: tiles of LK = 4 runs of one group. The suffix
+// product of a tile is E^T = G3[i3]^T P^T: rows (run, j3), columns p, K = r2.
+// Lane (col, q) feeds G3 of run col/4 as the A operand and P row 16mt + col as
+// the B operand, and receives E[run q][p = 16mt + col][j3 = 0..3]: four
+// consecutive floats of that run's row, written with one 16-byte store.
+// Wave w takes a contiguous range of tiles (consecutive tiles mostly share a
+// group, so P is reloaded once per group). A tile's G3 operand is loaded one
+// tile ahead, before the current tile's stores: loads and stores share one
+// in-order completion counter, so a load can only be waited for alone if every
+// memory access issued after it is certain to have been issued. The loop body
+// therefore holds no conditional access (lanes past the group's last run store
+// to a spare row, the look-ahead tile is clamped to the last one, run i3 values
+// come from LDS), it is unrolled by two with ping-pong operand sets, and no
+// register that a load is still filling is ever copied.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
+__device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, const float* sP,
+                                          const int32_t* sRb, const int32_t* sTp, const int32_t* sI3) {
     using B = PrefixBatch<N1, N2, R>;
-    constexpr int NP = B::NP, D = NP * N3, SG = B::SG, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
+    constexpr int NP = B::NP, D = NP * N3, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
     constexpr int MT = NP / 16, LK = 16 / N3;
-    static_assert(N3 == 4 && NP % 16 == 0, "shape");
-    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
-    __shared__ int32_t sRb[SG + 1];
-    __shared__ int32_t sTp[SG + 1];
-    extern __shared__ int32_t sI3[];   // the batch's run i3 list
-
-    BatchCtx c;
-    if (!batch_begin<N1, N2, R>(a.recs, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
-    const float* sP = sU;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    batch_tiles(sRb, sTp, c.ng, LK);
-    __syncthreads();
-
-    // ---- runs: tiles of LK = 4 runs of one group. The suffix product of a
-    // tile is E^T = G3[i3]^T P^T: rows (run, j3), columns p, K = r2. Lane
-    // (col, q) feeds G3 of run col/4 as the A operand and P row 16mt + col as
-    // the B operand, and receives E[run q][p = 16mt + col][j3 = 0..3]: four
-    // consecutive floats of that run's row, written with one 16-byte store.
-    // Wave w takes a contiguous range of tiles (consecutive tiles mostly share
-    // a group, so P is reloaded once per group). A tile's G3 operand is loaded
-    // one tile ahead, before the current tile's stores: loads and stores share
-    // one in-order completion counter, so a load can only be waited for alone
-    // if every memory access issued after it is certain to have been issued.
-    // The loop body therefore holds no conditional access (lanes past the
-    // group's last run store to a spare row, the look-ahead tile is clamped to
-    // the last one, run i3 values come from LDS), it is unrolled by two with
-    // ping-pong operand sets, and no register that a load is still filling is
-    // ever copied.
     const int ntile = sTp[c.ng];
     const int per = (ntile + WAVES - 1) / WAVES;
     const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
@@ -180,47 +168,91 @@ __global__ __launch_bounds__(1024) void k_fwd_batch(FwdArgs a) {
     if (k < n) step(k, OA, OB, IA, IB);
 }
 
+// Persistent workgroups (a few per CU) walk the batch slots b = blockIdx.x,
+// blockIdx.x + gridDim.x, ... . While a workgroup runs the tiles of one batch,
+// the loads of its next batch (G2 slice, G1 rows, run i3 list) are in flight,
+// and the records of the next two batches are already in registers, so a
+// batch's prologue costs no exposed memory round trip; slots without a group
+// cost a record read.
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a, int64_t nb) {
+    using B = PrefixBatch<N1, N2, R>;
+    constexpr int SG = B::SG, LK = 16 / N3;
+    static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 512, "shape");
+    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
+    __shared__ int32_t sRb[SG + 1];
+    __shared__ int32_t sTp[SG + 1];
+    extern __shared__ int32_t sI3[];   // the batch's run i3 list
+
+    const int64_t G = gridDim.x;
+    int64_t b = blockIdx.x;
+    int32_t rwA = rec_word(a.recs, b, nb);
+    int32_t rwB = rec_word(a.recs, b + G, nb);
+    BatchPf<N1, N2, R> f;
+    batch_fetch<N1, N2, R>(rwA, a.run_i3, a.g1, a.g2, f);
+    for (; b < nb; b += G) {
+        const int32_t rwC = rec_word(a.recs, b + 2 * G, nb);
+        BatchCtx c;
+        const bool live = rec_field(rwA, RW_NG) > 0;
+        if (live) {
+            batch_prefix<N1, N2, R>(rwA, a.run_i3, f, sU, sRb, sI3, c);
+            batch_tiles(sRb, sTp, c.ng, LK);
+        }
+        batch_fetch<N1, N2, R>(rwB, a.run_i3, a.g1, a.g2, f);
+        if (live) {
+            __syncthreads();
+            fwd_tiles<N1, N2, R, N3>(a, c, sU, sRb, sTp, sI3);
+            __syncthreads();
+        }
+        rwA = rwB;
+        rwB = rwC;
+    }
+}
+
 // One wave per bag: sum the rows of the bag's lookups (in input order) from
 // the stage buffer (one row per run id) and write the bag's output row. Empty
-// bags get zeros.
-template <int DL>
+// bags get zeros. Rows are read as 16-byte vectors, LPR = D/4 lanes per row,
+// so one load instruction covers RPI = 64/LPR rows; lane group h takes rows
+// h, h + RPI, ... of the bag and the RPI partial sums are added at the end.
+template <int D>
 __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
                                               const int32_t* __restrict__ run_of,
                                               const float* __restrict__ stage,
                                               float* __restrict__ out, int32_t* ctrl) {
-    constexpr int D = 64 * DL;
+    constexpr int LPR = D / 4, RPI = 64 / LPR, U = 8;   // U loads in flight
+    static_assert(D % 4 == 0 && 64 % LPR == 0, "row shape");
     reset_queues(ctrl, 0);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane / LPR, c4 = 4 * (lane % LPR);
     const int64_t q = (int64_t)blockIdx.x * 4 + w;
     if (q >= TB) return;
     const int32_t b0 = bag_start[q];
     const int32_t b1 = max(b0, bag_start[q + 1]);
-    float acc[DL];
-#pragma unroll
-    for (int k = 0; k < DL; ++k) acc[k] = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int32_t base = b0; base < b1; base += 64) {
         const int n = min(64, b1 - base);
-        const int32_t rv = (lane < n) ? run_of[base + lane] : run_of[b0];
-        // 8 rows in flight; rows past n re-read a valid row and are not added
-        for (int j0 = 0; j0 < n; j0 += 8) {
-            float v[8][DL];
+        const int32_t rv = (lane < n) ? run_of[base + lane] : 0;
+        for (int j0 = 0; j0 < n; j0 += RPI * U) {
+            floatx4 v[U];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int32_t slot = __builtin_amdgcn_readlane(rv, min(j0 + u, 63));
-                const float* src = stage + (int64_t)slot * D + lane * DL;
-#pragma unroll
-                for (int k = 0; k < DL; ++k) v[u][k] = src[k];
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + RPI * u + h;
+                const int32_t slot = __shfl(rv, min(j, n - 1));
+                v[u] = *reinterpret_cast<const floatx4*>(stage + (int64_t)slot * D + c4);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (j0 + u < n)
-#pragma unroll
-                    for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
+            for (int u = 0; u < U; ++u)
+                if (j0 + RPI * u + h < n) acc += v[u];
         }
     }
-    float* dst = out + q * D + lane * DL;
 #pragma unroll
-    for (int k = 0; k < DL; ++k) dst[k] = acc[k];
+    for (int m = LPR; m < 64; m *= 2) {
+        floatx4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __shfl_xor(acc[e], m);
+        acc += o;
+    }
+    if (h == 0) *reinterpret_cast<floatx4*>(out + q * D + c4) = acc;
 }
 
 template <int N1, int N2, int R, int N3>
@@ -230,13 +262,13 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
               p->at<float>(p->lay.stage), p->L};
     if (p->L > 0 && p->n_fb > 0) {
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
-        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb),
-                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a);
+        const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
+        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)grid),
+                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
         TT_LAUNCH_CHECK();
     }
-    constexpr int DL = N1 * N2 * N3 / 64;
     if (p->TB > 0) {
-        hipLaunchKernelGGL(k_pool<DL>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
+        hipLaunchKernelGGL(k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
                            p->at<float>(p->lay.stage), out, p->ctrl());
         TT_LAUNCH_CHECK();

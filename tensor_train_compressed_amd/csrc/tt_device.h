@@ -3,6 +3,8 @@
 
 #include "tt_internal.h"
 
+#include <cstddef>
+
 namespace tt {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -163,58 +165,109 @@ struct PrefixBatch {
     static_assert(N1 == 4 && MR % 16 == 0 && N2R % 16 == 0 && R % 4 == 0, "prefix batch shape");
 };
 
-// Called by all WAVES waves of the block. Returns false (for the whole block)
-// when the batch holds no group; otherwise sRb[0..ng] = the groups' first row
-// runs relative to rb0, sI3[0..nr) = the batch's run i3 values, sU holds P
-// (row (g*NP + p) at stride AS) and the block is synchronised.
+// The record of batch b as one word per lane (lane k holds word k of the
+// BatchRec; lanes past it hold word 0); all zero (ng = 0) for b >= nb.
+constexpr int kRecWords = (int)(sizeof(BatchRec) / 4);
+static_assert(kRecWords <= 64, "BatchRec fits one wave");
+__device__ __forceinline__ int32_t rec_word(const BatchRec* __restrict__ recs, int64_t b, int64_t nb) {
+    const int lane = threadIdx.x & 63;
+    const int32_t* w = reinterpret_cast<const int32_t*>(recs + (b < nb ? b : 0));
+    const int32_t x = w[lane < kRecWords ? lane : 0];
+    return b < nb ? x : 0;
+}
+__device__ __forceinline__ int32_t rec_field(int32_t rw, int k) { return __builtin_amdgcn_readlane(rw, k); }
+__device__ __forceinline__ int64_t rec_field64(int32_t rw, int k) {
+    return (int64_t)(uint32_t)__builtin_amdgcn_readlane(rw, k) |
+           ((int64_t)__builtin_amdgcn_readlane(rw, k + 1) << 32);
+}
+// word offsets of the BatchRec fields
+enum RecWord : int { RW_NG = 0, RW_G0 = 1, RW_I2 = 2, RW_RB0 = 3, RW_NR = 4, RW_O1 = 8, RW_O2 = 10,
+                     RW_O3 = 12, RW_I1 = 16, RW_RBASE = 24 };
+static_assert(offsetof(BatchRec, o1) == 4 * RW_O1 && offsetof(BatchRec, o3) == 4 * RW_O3 &&
+              offsetof(BatchRec, i1) == 4 * RW_I1 && offsetof(BatchRec, rbase) == 4 * RW_RBASE &&
+              offsetof(BatchRec, nr) == 4 * RW_NR, "BatchRec words");
+
+// Registers that carry one batch's operands from their loads to LDS.
 template <int N1, int N2, int R>
-__device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs,
-                                            const int32_t* __restrict__ run_i3,
-                                            const float* __restrict__ g1, const float* __restrict__ g2,
-                                            float* sU, int32_t* sRb, int32_t* sI3, BatchCtx& c) {
+struct BatchPf {
     using B = PrefixBatch<N1, N2, R>;
+    static constexpr int NT = 64 * B::WAVES;
+    static constexpr int NQ = R * B::N2R / 4, NV = (NQ + NT - 1) / NT;          // G2 slice, float4
+    static constexpr int Q1 = N1 * R / 4, NQ1 = kFwdBatch * Q1, NV1 = (NQ1 + NT - 1) / NT;   // G1 rows
+    static constexpr int NI = 4;                                                // run i3 values
+    floatx4 v[NV];
+    floatx4 u[NV1];
+    int32_t i3[NI];
+};
+
+// Issues the loads of batch `rw` (all threads; nothing when ng = 0). Groups
+// past ng read G1[0] (the record's i1 is 0 there); their P rows are written
+// but never read.
+template <int N1, int N2, int R>
+__device__ __forceinline__ void batch_fetch(int32_t rw, const int32_t* __restrict__ run_i3,
+                                            const float* __restrict__ g1, const float* __restrict__ g2,
+                                            BatchPf<N1, N2, R>& f) {
+    using F = BatchPf<N1, N2, R>;
+    constexpr int N2R = N2 * R, NT = F::NT;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const floatx4* G2s = reinterpret_cast<const floatx4*>(g2 + rec_field64(rw, RW_O2) +
+                                                        (int64_t)rec_field(rw, RW_I2) * R * N2R);
+#pragma unroll
+    for (int k = 0; k < F::NV; ++k) f.v[k] = G2s[min(tid + NT * k, F::NQ - 1)];
+    const float* G1b = g1 + rec_field64(rw, RW_O1);
+#pragma unroll
+    for (int k = 0; k < F::NV1; ++k) {
+        const int e = min(tid + NT * k, F::NQ1 - 1);
+        const int32_t i1 = __shfl(rw, RW_I1 + e / F::Q1);
+        f.u[k] = reinterpret_cast<const floatx4*>(G1b + (int64_t)i1 * N1 * R)[e % F::Q1];
+    }
+    const int32_t rb0 = rec_field(rw, RW_RB0), nr = rec_field(rw, RW_NR);
+#pragma unroll
+    for (int j = 0; j < F::NI; ++j) {
+        const int e = tid + NT * j;
+        f.i3[j] = run_i3[rb0 + max(0, min(e, nr - 1))];
+    }
+    (void)lane;
+}
+
+// Moves a fetched batch into LDS and forms its prefixes. All WAVES waves call
+// it (only for ng > 0); it ends with the block synchronised, sU holding P (row
+// g*NP + p at stride AS), sRb[0..kFwdBatch] the groups' first row runs relative
+// to rb0 and sI3[0..nr) the batch's run i3 values.
+template <int N1, int N2, int R>
+__device__ __forceinline__ void batch_prefix(int32_t rw, const int32_t* __restrict__ run_i3,
+                                             const BatchPf<N1, N2, R>& f, float* sU, int32_t* sRb,
+                                             int32_t* sI3, BatchCtx& c) {
+    using B = PrefixBatch<N1, N2, R>;
+    using F = BatchPf<N1, N2, R>;
     constexpr int NP = B::NP, N2R = B::N2R, MTP = B::MTP, KS = B::KS, GS = B::GS, AS = B::AS;
-    constexpr int WAVES = B::WAVES, NT2 = B::NT2, NTW = B::NTW, NT = 64 * WAVES;
+    constexpr int WAVES = B::WAVES, NT2 = B::NT2, NTW = B::NTW, NT = F::NT;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    const BatchRec* rec = recs + blockIdx.x;
-    c.ng = rec->ng;
-    if (c.ng <= 0) return false;
-    c.g0 = rec->g0; c.rb0 = rec->rb0; c.nr = rec->nr; c.o3 = rec->o3;
-    // G2 slice: R rows of N2*R floats
-    constexpr int NQ = R * N2R / 4, NV = (NQ + NT - 1) / NT;
-    const float4* G2s = reinterpret_cast<const float4*>(g2 + rec->o2 + (int64_t)rec->i2 * R * N2R);
-    float4 v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int e4 = min(tid + NT * k, NQ - 1);
-        v[k] = G2s[e4];
-    }
-    // G1 rows of the batch's groups: N1*R floats each (groups past ng read G1[0]:
-    // the record's i1 is 0 there; their P rows are written but never read)
-    constexpr int NQ1 = kFwdBatch * N1 * R / 4, NV1 = (NQ1 + NT - 1) / NT, Q1 = N1 * R / 4;
-    float4 u[NV1];
-#pragma unroll
-    for (int k = 0; k < NV1; ++k) {
-        const int f = min(tid + NT * k, NQ1 - 1);
-        u[k] = reinterpret_cast<const float4*>(g1 + rec->o1 + (int64_t)rec->i1[f / Q1] * N1 * R)[f % Q1];
-    }
-    if (tid <= kFwdBatch) sRb[tid] = rec->rbase[tid];
-    for (int e = tid; e < c.nr; e += NT) sI3[e] = run_i3[c.rb0 + e];
+    c.ng = rec_field(rw, RW_NG); c.g0 = rec_field(rw, RW_G0);
+    c.rb0 = rec_field(rw, RW_RB0); c.nr = rec_field(rw, RW_NR); c.o3 = rec_field64(rw, RW_O3);
     float* sG2 = sU;
     float* sG1 = sU + B::G2_FLOATS;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
+    for (int k = 0; k < F::NV; ++k) {
         const int e4 = tid + NT * k;
-        if (e4 < NQ) *reinterpret_cast<float4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = v[k];
+        if (e4 < F::NQ) *reinterpret_cast<floatx4*>(sG2 + ((4 * e4) / N2R) * GS + (4 * e4) % N2R) = f.v[k];
     }
 #pragma unroll
-    for (int k = 0; k < NV1; ++k) {
-        const int f = tid + NT * k;   // group f / Q1, element 4*(f % Q1) = (j1, r1)
-        if (f < NQ1) {
-            const int e = 4 * (f % Q1);
-            *reinterpret_cast<float4*>(sG1 + ((f / Q1) * N1 + e / R) * AS + e % R) = u[k];
+    for (int k = 0; k < F::NV1; ++k) {
+        const int e = tid + NT * k;   // group e / Q1, element 4*(e % Q1) = (j1, r1)
+        if (e < F::NQ1) {
+            const int x = 4 * (e % F::Q1);
+            *reinterpret_cast<floatx4*>(sG1 + ((e / F::Q1) * N1 + x / R) * AS + x % R) = f.u[k];
         }
     }
+#pragma unroll
+    for (int j = 0; j < F::NI; ++j) {
+        const int e = tid + NT * j;
+        if (e < c.nr) sI3[e] = f.i3[j];
+    }
+    for (int e = tid + NT * F::NI; e < c.nr; e += NT) sI3[e] = run_i3[c.rb0 + e];
+    const int32_t rbw = __shfl(rw, RW_RBASE + min(lane, kFwdBatch));
+    if (tid <= kFwdBatch) sRb[tid] = rbw;
     __syncthreads();
     // wave w: column tiles nt = w + WAVES*k, every row tile mt (row 16mt + i =
     // group 4mt + i/N1, j1 = i%N1); K = r1
@@ -250,6 +303,20 @@ __device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs,
         }
     }
     __syncthreads();
+}
+
+// One batch per workgroup (blockIdx): fetch and prefix. Returns false (for the
+// whole block) when the batch holds no group.
+template <int N1, int N2, int R>
+__device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs, int64_t nb,
+                                            const int32_t* __restrict__ run_i3,
+                                            const float* __restrict__ g1, const float* __restrict__ g2,
+                                            float* sU, int32_t* sRb, int32_t* sI3, BatchCtx& c) {
+    const int32_t rw = rec_word(recs, blockIdx.x, nb);
+    if (rec_field(rw, RW_NG) <= 0) return false;
+    BatchPf<N1, N2, R> f;
+    batch_fetch<N1, N2, R>(rw, run_i3, g1, g2, f);
+    batch_prefix<N1, N2, R>(rw, run_i3, f, sU, sRb, sI3, c);
     return true;
 }
 

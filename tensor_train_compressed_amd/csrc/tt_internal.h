@@ -49,6 +49,9 @@ constexpr int kXcds = 8;
 constexpr int kFwdBatch = 8;
 // Spare stage rows after the L run rows (targets of inactive lanes' stores).
 constexpr int kStageSpare = 4;
+// Workgroups of the persistent forward batch kernel: two per CU (the kernel's
+// registers allow two 8-wave workgroups on a CU).
+constexpr int kFwdPersistBlocks = 2 * 256;
 // LDS the batch kernels may spend on the run i3 list of one batch
 // (kFwdBatch * largest m3 int32 values); larger m3 takes the generic kernels.
 constexpr int kMaxBatchI3Bytes = 32768;
