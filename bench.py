@@ -5,16 +5,27 @@ Workload: one 11,000,000-row table (radices 200x220x250), dim 128 (4x8x4),
 TT rank 32, fp32 cores; a batch of 32,768 bags with Poisson(20) lengths
 clipped to [1,100] and unpermuted Zipf(1.1) indices; grad_out ~ N(0,1) and an
 SGD step with lr 0.01. One step is the whole path on one batch: plan (split,
-prefix grouping, chunking), forward, backward, SGD, with every input already
-resident in HBM.
+prefix grouping, chunking, row runs), forward, backward, SGD, with every input
+already resident in HBM.
 
-Prints one JSON line: whole-step pooled bags/s as `value`, plus per-phase
-times from HIP events, the forward kernel's roofline figures, and the CPU
-oracle timed on a bounded sample of the same batch as `cpu_baseline`.
+Prints one JSON line: whole-step pooled bags/s as `value`; per-call times of
+each phase (HIP events around back-to-back calls on the stream the kernels run
+on); the forward call's roofline figures; and the CPU oracle timed on a
+bounded sample of the same batch as `cpu_baseline`.
+
+Roofline of the forward call (the planner's output is an input to it): the
+work counted is the work the kernels execute. The forward contracts each
+distinct table row of a prefix group once, so its FLOP count is
+U * 2*n1*n2*R^2 (prefixes) + U_row * 2*n1*n2*n3*R (suffixes of distinct rows)
++ L * D (pooling adds); the per-lookup count of the plain method (every lookup
+contracted) is reported beside it as context. HBM traffic per call comes from
+rocprofv3 counter passes kept under profiles/ and is reported only while the
+kernel sources still match the hash recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,8 +34,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP32_TFLOPS = 157.3      # MI355X published dense FP32 (vector and matrix)
+PEAK_FP32_TFLOPS = 157.3      # MI355X published dense FP32 (matrix cores and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_traffic_skew11m.json")
+FORWARD_SOURCES = ("forward.hip", "tt_device.h", "tt_internal.h")
 
 
 def parse():
@@ -33,10 +46,33 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--chunk", type=int, default=256)
-    ap.add_argument("--cpu-bags", type=int, default=256,
+    ap.add_argument("--cpu-bags", type=int, default=6144,
                     help="bags of the batch the CPU oracle baseline runs on (0: skip)")
-    ap.add_argument("--phase-reps", type=int, default=20)
+    ap.add_argument("--phase-reps", type=int, default=50)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of 256 MiB (reference for HBM counters)")
     return ap.parse_args()
+
+
+def forward_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in FORWARD_SOURCES:
+        with open(os.path.join(ROOT, "tensor_train_compressed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def forward_traffic():
+    """HBM bytes per forward call from the committed counter passes, or None
+    when the forward kernels changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != forward_source_hash():
+        return None
+    return rec.get("bytes_per_call")
 
 
 def main():
@@ -60,8 +96,7 @@ def main():
     R, D = t.rank, t.dim
     B, L = p.batch, p.L
     tabs = tte.make_tables(p.tables, p.goff)
-    g_init = [torch.from_numpy(x).to(dev) for x in (p.g1, p.g2, p.g3)]
-    g = [x.clone() for x in g_init]
+    g = [torch.from_numpy(x).to(dev) for x in (p.g1, p.g2, p.g3)]
     dg = [torch.empty_like(x) for x in g]
     idx = torch.from_numpy(p.indices).to(dev)
     off = torch.from_numpy(p.offsets).to(dev)
@@ -71,8 +106,11 @@ def main():
                      device=dev)
     stream = torch.cuda.current_stream()
 
+    def plan():
+        return tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream)
+
     def step():
-        pl = tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream)
+        pl = plan()
         tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream)
         tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
         tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr, stream=stream)
@@ -84,6 +122,7 @@ def main():
     assert tte.tt_emb_get_error(pl) == 0
     U, NC = tte.tt_emb_plan_counts(pl)
 
+    # the timed region: exactly `steps` whole steps, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -93,31 +132,49 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     bags_per_s = B * args.steps / elapsed
 
-    # per-phase HIP events on the stream the kernels run on
-    reps = args.phase_reps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
-    for r in range(reps):
-        e = ev[r]
-        e[0].record(stream)
-        pl = tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream)
-        e[1].record(stream)
-        tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream)
-        e[2].record(stream)
-        tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
-        e[3].record(stream)
-        tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr, stream=stream)
-        e[4].record(stream)
-    torch.cuda.synchronize()
-    ph = np.array([[ev[r][k].elapsed_time(ev[r][k + 1]) for k in range(4)] for r in range(reps)])
-    plan_ms, fwd_ms, bwd_ms, sgd_ms = (float(np.median(ph[:, k])) for k in range(4))
+    # per-call phase times: HIP events on the kernels' stream around
+    # back-to-back calls (host launch gaps overlap the GPU work)
+    def per_call_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
-    # algorithmic work of one forward launch (prefix per group, suffix + pool per lookup)
-    fwd_flop = U * 2 * n1 * n2 * R * R + L * (2 * n1 * n2 * n3 * R + D)
-    touched = len(np.unique(p.indices // t.m[2]))  # not used for flops; cores are tiny
+    reps = args.phase_reps
+    plan_ms = per_call_ms(plan, reps)
+    pl = plan()
+    fwd_ms = per_call_ms(lambda: tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream), reps)
+    bwd_ms = per_call_ms(lambda: tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1],
+                                                     dg[2], stream=stream), reps)
+    sgd_ms = per_call_ms(lambda: tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr,
+                                                stream=stream), reps)
+    torch.cuda.synchronize()
+
+    # executed work of one forward call (distinct rows of a group contracted once)
+    key_i3 = np.unique(p.indices)            # one table: a distinct index is a distinct (key, i3) row
+    U_row = int(key_i3.size)
+    fwd_flop = U * 2 * n1 * n2 * R * R + U_row * 2 * n1 * n2 * n3 * R + L * D
+    fwd_flop_per_lookup = U * 2 * n1 * n2 * R * R + L * (2 * n1 * n2 * n3 * R + D)
     core_bytes = 4 * (p.g1.size + p.g2.size + p.g3.size)
     fwd_bytes = 8 * L + 8 * (B + 1) + core_bytes + 4 * B * D
     achieved_tflops = fwd_flop / (fwd_ms * 1e-3) / 1e12
-    del touched
+    traffic = forward_traffic()
+
+    if args.calibrate_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter values
+        # scale the counters of the forward kernels to bytes
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_bags > 0:
@@ -138,20 +195,23 @@ def main():
         "data": "synthetic (seeded Zipf/Poisson indices, Gaussian cores)",
         "config": {"workload": "skew11m-train: 11M rows 200x220x250, dim 128=4x8x4, rank 32, "
                                "B=32768 Poisson(20) clip[1,100], Zipf(1.1) unpermuted, "
-                               "fwd+bwd+SGD lr 0.01",
-                   "global_batch": B, "lookups": L, "prefix_groups": U, "chunks": NC,
-                   "chunk": args.chunk},
-        "phases_ms": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4),
-                      "backward": round(bwd_ms, 4), "sgd": round(sgd_ms, 4)},
+                               "plan+fwd+bwd+SGD lr 0.01",
+                   "global_batch": B, "lookups": L, "prefix_groups": U, "distinct_rows": U_row,
+                   "chunks": NC, "chunk": args.chunk},
+        "phases_ms_per_call": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4),
+                               "backward": round(bwd_ms, 4), "sgd": round(sgd_ms, 4)},
         "forward_bags_per_s": round(B / (fwd_ms * 1e-3), 1),
         "plan_forward_bags_per_s": round(B / ((plan_ms + fwd_ms) * 1e-3), 1),
         "forward_rows_per_s": round(L / (fwd_ms * 1e-3), 1),
-        "roofline": {"kernel": "tt_emb_forward (output zero-fill + k_fwd)",
-                     "bound": "alu", "achieved": round(achieved_tflops, 3),
+        "roofline": {"kernel": "tt_emb_forward call (k_fwd_batch + k_pool)",
+                     "bound": "mfma", "achieved": round(achieved_tflops, 3),
                      "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                     "algorithmic_flop": int(fwd_flop), "algorithmic_bytes": int(fwd_bytes),
-                     "traffic": None},
+                     "traffic": traffic,
+                     "flop_per_call": int(fwd_flop),
+                     "flop_per_call_if_every_lookup_contracted": int(fwd_flop_per_lookup),
+                     "algorithmic_bytes_per_call": int(fwd_bytes),
+                     "hbm_frac_algorithmic": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -160,15 +220,13 @@ def main():
 def cpu_baseline(p, nbags: int, chunk: int):
     """The CPU oracle (plan, forward, backward, SGD) on the first `nbags` bags
     of the same batch; bags/s over that sample."""
-    import numpy as np
-
     import oracle
     import workloads as wl
 
     nb = min(nbags, p.batch)
     Ls = int(p.offsets[nb])
-    sub = wl.Problem(p.name, p.tables, nb, p.g1, p.g2, p.g3, p.goff, p.indices[:Ls],
-                     p.offsets[:nb + 1].copy(), p.grad_out[:nb], p.lr)
+    sub = wl.Problem(p.name, p.tables, nb, p.g1.copy(), p.g2.copy(), p.g3.copy(), p.goff,
+                     p.indices[:Ls], p.offsets[:nb + 1].copy(), p.grad_out[:nb], p.lr)
     t0 = time.perf_counter()
     oracle.plan_problem(sub, chunk)
     oracle.forward_problem(sub)
