@@ -107,7 +107,9 @@ size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L, 
  * Planner output, all int32 in the workspace (tt_emb_plan_view):
  *   key[l]      = base_t + i2*m1 + i1 (base_t = sum of m1*m2 over earlier tables)
  *   i3[l], bag_of[l]
- *   perm        stable sort of lookups by key (equal keys keep increasing l)
+ *   perm        stable sort of lookups by (key, i3): groups in key order, inside a
+ *               group by i3, equal (key, i3) keeping increasing l (repeats of one
+ *               table row are adjacent and contracted once)
  *   groups      maximal runs of equal key in sorted order: group_key[g],
  *               group_start[g] (and group_start[U] = L)
  *   chunks      each group cut into consecutive pieces of exactly `chunk`
