@@ -309,7 +309,7 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
         int32_t rbase, rend;
         bool ok;
         double* dst;          // dG3 slice of this lane's run, column j3
-        float bv[KSP];        // S of this lane's run, K = p (dG3 product)
+        float bv[KSP];        // S of this lane's run, K = p = 4*s2 + q (dG3 product)
         float av[LK][MT];     // S of run ru, K = j3 (dP product)
         float bq[LK][RT];     // G3[i3 of run ru], K = j3
     };
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
         const int32_t r = o.ok ? o.rbase + lk : o.rbase;
         const float* Sb = a.S + (int64_t)r * D + j3;
 #pragma unroll
-        for (int s2 = 0; s2 < KSP; ++s2) x.bv[s2] = Sb[(KSP * q + s2) * N3];
+        for (int s2 = 0; s2 < KSP; ++s2) x.bv[s2] = Sb[(4 * s2 + q) * N3];
 #pragma unroll
         for (int ru = 0; ru < LK; ++ru) {
             const bool okr = o.rbase + ru < o.rend;
@@ -362,13 +362,14 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
             }
         }
         // dG3[i3] += P^T S: column (run lk, j3), rows r2. The A operand of P^T
-        // comes from LDS: lane (i, q) takes P[KSP*q + s][16*rt + i].
+        // comes from LDS: lane (i, q) takes P[4*s2 + q][16*rt + i]; K = p runs
+        // as 4*s2 + q so that each S load reads 64 consecutive bytes per run.
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             floatx4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s2 = 0; s2 < KSP; ++s2)
-                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(cur * NP + KSP * q + s2) * AS + 16 * rt + col],
+                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(cur * NP + 4 * s2 + q) * AS + 16 * rt + col],
                                                           C.bv[s2], cc, 0, 0, 0);
             // lanes past the group's last run add nothing (adding zeros
             // instead measured slower: the extra atomics cost more than the
@@ -398,11 +399,15 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     for (int e = tid; e < c.ng * PR; e += 64 * WAVES) a.dpg[(int64_t)c.g0 * PR + e] = sDP[e];
 }
 
-// One workgroup per ((table, i2) slice, 64-column block of the N2*R columns).
-// Groups of the slice are taken eight at a time (a slab); wave w owns
-//   dG2 tiles (r1 block w & 1) x (column blocks 2*(w >> 1), +1), K = j1 per group
-//   dG1 tile  (groups 4*(w >> 1)..+3 x j1) x (r1 block w & 1), K = the 64 columns
-// so dG2 needs no reduction and dG1 only atomics across column blocks.
+// One workgroup (4 waves) per ((table, i2) slice, 64-column block of the N2*R
+// columns). The slice's groups are taken 32 at a time (a slab); wave w owns
+//   dG2 tiles (r1 block w & 1) x (column tiles 2*(w >> 1), +1), K = j1 per group
+//   dG1 tiles (r1 block w & 1) x (row tiles (w >> 1) + 2m, m < 4), rows = (group, j1),
+//            K = the block's 64 columns
+// so dG2 needs no reduction and dG1 only atomics across the column blocks.
+// Loads run ahead: the next slab's dP rows and G1 rows and the group keys two
+// slabs ahead are issued before the current slab's math and its dG1 atomics,
+// so a slab costs its math and barriers, not memory round trips.
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
                                                     int32_t* ctrl, int64_t K,
@@ -413,15 +418,19 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
                                                     const float* __restrict__ g2,
                                                     double* __restrict__ dg1, float* __restrict__ dg2) {
     constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, QN = N2R / 64;
-    constexpr int SG = 8;                   // groups per slab
+    constexpr int SG = 32;                  // groups per slab
+    constexpr int MR = SG * N1;             // slab rows (group, j1)
     constexpr int DS = 64 + 4;              // LDS row stride of the dP / G2 column block
-    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32, "shape");
-    __shared__ float sG2[R * DS];           // G2[i2][r1][cols]
-    __shared__ float sD[SG * N1 * DS];      // dP rows (g, j1), this block's columns
+    constexpr int NDP = MR * 16 / 256;      // float4 of dP rows per thread
+    constexpr int NG1 = SG * N1 * R / 4 / 256;   // float4 of G1 rows per thread
+    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32 && NDP * 256 == MR * 16 && NG1 * 256 * 4 == SG * N1 * R,
+                  "shape");
+    __shared__ float sG2[R * DS];           // G2[i2][r1][block columns]
+    __shared__ float sD[MR * DS];           // dP rows (g, j1), block columns
     __shared__ float sA[SG * N1 * R];       // G1[i1(g)] of the slab
     __shared__ int32_t sI1[SG];
 
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
     reset_queues(ctrl, 1);
     const int32_t bi = blockIdx.x / QN, qn = blockIdx.x % QN;
     int t = 0;
@@ -439,37 +448,69 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     const int64_t ke = kb + d.m1;
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
     const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
-    const int32_t g1e = ke < K ? (int32_t)(key_scan[ke] >> 32) : U;
+    const int32_t ge = ke < K ? (int32_t)(key_scan[ke] >> 32) : U;
     const int c0 = 64 * qn;
+    const float* G1t = g1 + d.o1;
+
+    // loads of slab gs: dP rows (zero past the slice's groups) and G1 rows of
+    // the groups whose i1 lane k of `i1v` holds (k < SG)
+    auto load_dp = [&](int32_t gs, floatx4 (&v)[NDP]) {
+#pragma unroll
+        for (int k = 0; k < NDP; ++k) {
+            const int f = tid + 256 * k, row = f / 16, c4 = 4 * (f % 16);   // row = (g, j1)
+            const int32_t g = gs + row / N1;
+            const floatx4* src = reinterpret_cast<const floatx4*>(
+                dpg + (int64_t)min(g, ge - 1) * PR + (row % N1) * N2R + c0 + c4);
+            v[k] = *src;
+            if (g >= ge) v[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto load_i1 = [&](int32_t gs) -> int32_t {   // lane k < SG: i1 of group gs + k (0 past the end)
+        const int32_t g = gs + (lane & (SG - 1));
+        return g < ge ? (int32_t)(group_key[g] - kb) : 0;
+    };
+    auto load_g1 = [&](int32_t i1v, floatx4 (&u)[NG1]) {
+#pragma unroll
+        for (int k = 0; k < NG1; ++k) {
+            const int f = tid + 256 * k, gi = f / (N1 * R / 4);   // float4 f of the slab's G1 rows
+            const int32_t i1 = __shfl(i1v, gi);
+            u[k] = reinterpret_cast<const floatx4*>(G1t + (int64_t)i1 * N1 * R)[f % (N1 * R / 4)];
+        }
+    };
 
     const float* G2s = g2 + d.o2 + (int64_t)i2 * R * N2R;
-    for (int e = threadIdx.x; e < R * 64; e += 256) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
+    for (int e = tid; e < R * 64; e += 256) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
 
-    const int rt = w & 1, ch = w >> 1;      // dG2: r1 block, column pair; dG1: group quad, r1 block
+    const int rt = w & 1, ch = w >> 1;
     floatx4 acc2[2];
     acc2[0] = floatx4{0.f, 0.f, 0.f, 0.f};
     acc2[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    for (int32_t gs = g0; gs < g1e; gs += SG) {
-        const int ng = min(SG, g1e - gs);
-        __syncthreads();
-        // dP rows of the slab, this block's 64 columns (one float4 per thread)
+    floatx4 dpv[NDP], g1v[NG1];
+    int32_t i1c = 0, i1n = 0;
+    if (g0 < ge) {   // (the slab loads clamp rows to [g0, ge - 1])
+        i1c = load_i1(g0);
+        i1n = load_i1(g0 + SG);
+        load_dp(g0, dpv);
+        load_g1(i1c, g1v);
+    }
+    for (int32_t gs = g0; gs < ge; gs += SG) {
+        const int ng = min(SG, ge - gs);
+        __syncthreads();   // the previous slab's math is done with sD / sA / sI1
 #pragma unroll
-        for (int it = 0; it < SG * N1 / 16; ++it) {
-            const int row = (threadIdx.x >> 4) + 16 * it, c4 = (threadIdx.x & 15) * 4;  // row = (g, j1)
-            const int gi = row / N1, j1 = row % N1;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (gi < ng)
-                v = *reinterpret_cast<const float4*>(dpg + (int64_t)(gs + gi) * PR + j1 * N2R + c0 + c4);
-            float* dst = sD + row * DS + c4;
-            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+        for (int k = 0; k < NDP; ++k) {
+            const int f = tid + 256 * k;
+            *reinterpret_cast<floatx4*>(sD + (f / 16) * DS + 4 * (f % 16)) = dpv[k];
         }
-        if (threadIdx.x < SG) sI1[threadIdx.x] = threadIdx.x < ng ? (int32_t)(group_key[gs + threadIdx.x] - kb) : 0;
-        __syncthreads();
-        for (int e = threadIdx.x; e < SG * N1 * R; e += 256) {
-            const int gi = e / (N1 * R);
-            sA[e] = gi < ng ? g1[d.o1 + (int64_t)sI1[gi] * N1 * R + e % (N1 * R)] : 0.f;
-        }
+#pragma unroll
+        for (int k = 0; k < NG1; ++k) *reinterpret_cast<floatx4*>(sA + 4 * (tid + 256 * k)) = g1v[k];
+        if (tid < SG) sI1[tid] = i1c;
+        // the next slab's loads, then the group keys of the one after
+        const int32_t i1nn = load_i1(gs + 2 * SG);
+        load_dp(gs + SG, dpv);
+        load_g1(i1n, g1v);
+        i1c = i1n;
+        i1n = i1nn;
         __syncthreads();
         // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c]: one k-step per group
         for (int gi = 0; gi < ng; ++gi) {
@@ -480,21 +521,25 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
                 acc2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc2[j], 0, 0, 0);
             }
         }
-        // dG1 rows (g, j1) of group quad ch, r1 block rt, K = 64 columns
-        if (4 * ch < ng) {
-            floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
+        // dG1 rows (g, j1) of row tiles ch + 2m, r1 block rt, K = 64 columns
 #pragma unroll
-            for (int s2 = 0; s2 < 16; ++s2) {
-                const float av = sD[(16 * ch + col) * DS + 4 * s2 + q];
-                const float bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
-            }
-            // lane holds rows 4q+v = (group 4ch+q, j1 v), column r1 = 16*rt + col
-            const int gi = 4 * ch + q;
-            if (gi < ng) {
-                double* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
+        for (int m = 0; m < MR / 32; ++m) {
+            const int rtile = ch + 2 * m;
+            if (4 * rtile < ng) {
+                floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, (double)acc1[v]);
+                for (int s2 = 0; s2 < 16; ++s2) {
+                    const float av = sD[(16 * rtile + col) * DS + 4 * s2 + q];
+                    const float bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
+                }
+                // lane holds rows 4q+v = (group 4*rtile+q, j1 v), column r1 = 16*rt + col
+                const int gi = 4 * rtile + q;
+                if (gi < ng) {
+                    double* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, (double)acc1[v]);
+                }
             }
         }
     }
