@@ -68,6 +68,7 @@ typedef enum {
 /* Device error flag bits (tt_emb_get_error). */
 #define TT_FLAG_BAD_INDEX 1   /* some index outside [0, N_t)                         */
 #define TT_FLAG_BAD_OFFSETS 2 /* offsets[0] != 0, offsets[T*B] != L or a decrease   */
+#define TT_FLAG_INTERNAL 4    /* a scan's wait for an earlier tile hit its bound     */
 
 /* Limits of this build: N_t < 2^31, L < 2^31, T*B < 2^31, sum over tables of
  * m1*m2 < 2^30, R <= 64, n1*n2 <= 64, n3 <= 16, D <= 1024, T <= 4096. */

@@ -13,10 +13,10 @@
 // repeats of one table row are adjacent and that row is contracted once.
 //
 // Kernels, in stream order:
-//   k_write_desc      table descriptors into the workspace
-//   k_split           offsets check, bag search, digit split, prefix key
+//   k_init            clears the control words, writes the table descriptors
+//   k_split           offsets check, bag search, digit split, prefix key; marks keys absent
 //   k_radix_hist      \  stable LSD radix sort of key*M3 + i3, 8 bits per pass:
-//   scan (1 or 3)      | per-tile digit counts, one exclusive scan over
+//   scan               | per-tile digit counts, one exclusive scan over
 //   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
 //   k_gather          sorted i3 / bag, row-run heads, first and last position of each key
 //   k_key_flags       per key: present flag and chunk count
@@ -48,6 +48,12 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     while ((int64_t(1) << bits) < K * M3) ++bits;
     y.passes = std::max(1, (bits + kRadixBits - 1) / kRadixBits);
     y.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
+    {
+        const int64_t nh = (int64_t)kRadixBins * ((L + kSortTile - 1) / kSortTile);
+        const int64_t nscan = std::max<int64_t>(std::max<int64_t>(nh, K), L);
+        y.scan_tiles = (nscan + kScanTile - 1) / kScanTile + 1;
+        y.scan_st = take(sizeof(ScanTileStatus) * (size_t)y.scan_tiles);
+    }
     y.desc = take(sizeof(TabDev) * (size_t)T);
     const size_t l4 = sizeof(int32_t) * (size_t)L;
     y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
@@ -79,8 +85,6 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.Tmax = (L + (int64_t)kChunkCost * y.Cmax) / kTaskCost + 2;
     y.task_start = take(sizeof(int32_t) * (size_t)(y.Tmax + 1));
-    const int64_t nscan = std::max<int64_t>(std::max<int64_t>(nhist, K), L);
-    y.scan_tmp = take(sizeof(uint64_t) * (size_t)((nscan + kScanTile - 1) / kScanTile + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
@@ -118,7 +122,16 @@ __global__ void k_write_desc(TabDev* out, DescBatch b) {
     if (i < b.count) out[b.first + i] = b.d[i];
 }
 
-// 64-lane match: mask of valid lanes whose 8-bit digit equals this lane's.
+// Clears `nzero` words from `zero` (the control words and the scans' status
+// words) and writes the first batch of table descriptors.
+__global__ __launch_bounds__(256) void k_init(uint32_t* __restrict__ zero, int64_t nzero,
+                                              TabDev* __restrict__ out, DescBatch b) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = t; i < nzero; i += (int64_t)gridDim.x * blockDim.x) zero[i] = 0u;
+    if (t < b.count) out[b.first + t] = b.d[t];
+}
+
+// 64-lane match: mask of valid lanes whose digit equals this lane's.
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t valid) {
     uint64_t peers = valid;
 #pragma unroll
@@ -144,8 +157,10 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
                                                int32_t* __restrict__ bag_of,
                                                int32_t* __restrict__ bag_start,
                                                int32_t* __restrict__ ckey, int32_t M3,
-                                               int32_t* ctrl) {
+                                               int32_t* ctrl, int32_t* __restrict__ key_start,
+                                               int64_t K) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < K) key_start[i] = -1;   // k_gather records each present key's first position
     if (i <= TB) {
         const int64_t a = off[i];
         bag_start[i] = (int32_t)(a < 0 ? 0 : (a > L ? L : a));
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
 }
 
 // ---------------------------------------------------------------------------
-// device-wide exclusive scan (single block for short arrays, else 3 kernels)
+// device-wide exclusive scan (single block for short arrays, else single-pass look-back)
 
 template <class V>
 __device__ V block_exclusive_scan(V x, V* wsum, V* total) {
@@ -310,32 +325,85 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_single(V* data, int64_t n
     if (threadIdx.x == 0 && total_out) *total_out = carry;
 }
 
-template <class V>
-__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const V* data, int64_t n, V* part) {
-    __shared__ V wsum[17];
-    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-    V s = 0;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k)
-        if (i0 + k < n) s += data[i0 + k];
-    V tot;
-    (void)block_exclusive_scan<V>(s, wsum, &tot);
-    if (threadIdx.x == 0) part[blockIdx.x] = tot;
-}
+// Single-pass scan of arrays longer than one block's share: decoupled look-back
+// (Merrill and Garland, "Single-pass Parallel Prefix Scan with Decoupled
+// Look-back"). A workgroup claims the next tile from a counter, scans it,
+// publishes the tile's total, then walks back over the earlier tiles' status
+// words 64 at a time (one wave, one word per lane), adding totals until it
+// meets a tile whose inclusive prefix is known, and publishes its own
+// inclusive prefix. Status words carry the scan's epoch
+// (one per scan of a plan) so they need no clearing between scans; the plan's
+// control-word fill clears them once. Each wait is bounded: past the bound the
+// workgroup raises TT_FLAG_INTERNAL and goes on (wrong sums, never a hang).
+constexpr int kLookbackSpins = 1 << 20;
 
 template <class V>
-__global__ __launch_bounds__(kScanThreads) void k_scan_down(V* data, int64_t n, const V* part) {
+__global__ __launch_bounds__(kScanThreads) void k_scan_lookback(V* data, int64_t n, ScanTileStatus* st,
+                                                                uint32_t* tile_ctr, uint32_t epoch,
+                                                                V* total_out, int32_t* ctrl) {
     __shared__ V wsum[17];
-    const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    __shared__ uint32_t s_tile;
+    __shared__ V s_prefix;
+    if (threadIdx.x == 0) s_tile = atomicAdd(tile_ctr, 1u);
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const int64_t i0 = (int64_t)tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
     V v[kScanItems];
-    V s = 0;
+    V sum = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         v[k] = (i0 + k < n) ? data[i0 + k] : V(0);
-        s += v[k];
+        sum += v[k];
     }
     V tot;
-    V run = part[blockIdx.x] + block_exclusive_scan<V>(s, wsum, &tot);
+    V run = block_exclusive_scan<V>(sum, wsum, &tot);
+    if (threadIdx.x < 64) {
+        // wave 0: publish the tile's total, then look back 64 tiles at a time
+        const int lane = threadIdx.x;
+        auto publish = [&](uint32_t state, V x) {
+            if (state == 2u) st[tile].incl = (uint64_t)x; else st[tile].agg = (uint64_t)x;
+            __hip_atomic_store(&st[tile].flag, (epoch << 2) | state, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        V prefix = 0;
+        if (tile > 0) {
+            if (lane == 0) publish(1u, tot);
+            int64_t top = (int64_t)tile - 1;   // nearest tile of the window
+            int spins = 0;
+            while (true) {
+                const int64_t j = top - lane;
+                uint32_t f = 0;
+                if (j >= 0) f = __hip_atomic_load(&st[j].flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                const bool mine = (f >> 2) == epoch;
+                const uint32_t state = mine ? (f & 3u) : 0u;
+                const uint64_t incl = __ballot(j >= 0 && state == 2u);
+                const int first = incl ? __ffsll((unsigned long long)incl) - 1 : 64;   // nearest inclusive
+                const uint64_t need = first == 64 ? ~0ull : ((1ull << first) - 1ull);
+                const uint64_t waiting = __ballot(j >= 0 && state == 0u) & need;
+                if (waiting) {
+                    if (++spins > kLookbackSpins) {
+                        if (lane == 0) atomicOr(ctrl + CTRL_FLAG, TT_FLAG_INTERNAL);
+                        break;
+                    }
+                    continue;
+                }
+                V c = 0;
+                if (j >= 0 && lane < first) c = (V)st[j].agg;
+                if (lane == first) c = (V)st[j].incl;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+                prefix += c;
+                if (first < 64 || top < 64) break;
+                top -= 64;
+            }
+        }
+        if (lane == 0) {
+            publish(2u, prefix + tot);
+            s_prefix = prefix;
+            if (total_out && (int64_t)(tile + 1) * kScanTile >= n) *total_out = prefix + tot;
+        }
+    }
+    __syncthreads();
+    run += s_prefix;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         if (i0 + k < n) data[i0 + k] = run;
@@ -343,19 +411,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(V* data, int64_t n, 
     }
 }
 
+// Exclusive scan in place, one launch: one workgroup for short arrays, the
+// single-pass scan otherwise. `seq` numbers the plan's scans from 1.
 template <class V>
-static tt_status scan_exclusive(V* data, int64_t n, V* part, V* total_out, hipStream_t s) {
+static tt_status scan_exclusive(const tt_emb_plan_s* p, int seq, V* data, int64_t n, V* total_out,
+                                hipStream_t s) {
     if (n <= 4 * (int64_t)kScanTile) {
         hipLaunchKernelGGL(k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, data, n, total_out);
         TT_LAUNCH_CHECK();
         return TT_OK;
     }
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
-    hipLaunchKernelGGL(k_scan_reduce<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n, part);
-    TT_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, part, nb, total_out);
-    TT_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_scan_down<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n, part);
+    if (seq < 1 || seq >= CTRL_SCAN_MAX || nb > p->lay.scan_tiles) return TT_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_scan_lookback<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n,
+                       p->at<ScanTileStatus>(p->lay.scan_st),
+                       reinterpret_cast<uint32_t*>(p->ctrl() + CTRL_SCAN_CTR + seq), (uint32_t)seq,
+                       total_out, p->ctrl());
     TT_LAUNCH_CHECK();
     return TT_OK;
 }
@@ -647,7 +718,10 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
 
     auto fail = [&](tt_status e) { delete p; return e; };
     // control words and descriptors
-    if (fill32(p->ctrl(), 0u, CTRL_WORDS, s) != TT_OK) return fail(TT_ERR_HIP);
+    // control words and the scans' tile status words (adjacent in the workspace)
+    // are cleared by the launch that writes the first descriptors
+    const int64_t nzero = (int64_t)((lay.scan_st - lay.ctrl) + sizeof(ScanTileStatus) * lay.scan_tiles) / 4;
+    int nscan = 0;   // scans issued so far (each gets its own epoch and tile counter)
     int32_t kb = 0, i2b = 0, fbb = 0;
     for (int32_t first = 0; first < T; first += 16) {
         DescBatch b{};
@@ -667,7 +741,11 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             fbb += x.m[1] * ((x.m[0] + kFwdBatch - 1) / kFwdBatch);
             kb += x.m[0] * x.m[1];
         }
-        hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
+        if (first == 0)
+            hipLaunchKernelGGL(k_init, dim3(std::min<unsigned>(grid_for(nzero, 256), 64u)), dim3(256), 0, s,
+                               reinterpret_cast<uint32_t*>(p->ctrl()), nzero, p->at<TabDev>(lay.desc), b);
+        else
+            hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
     }
 
@@ -675,20 +753,20 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     int32_t* key = p->at<int32_t>(lay.key);
     int32_t* i3 = p->at<int32_t>(lay.i3);
     int32_t* bag = p->at<int32_t>(lay.bag_of);
-    // split (also checks the offsets; one thread per lookup and per offset)
+    // split (also checks the offsets and marks every key absent; one thread per
+    // lookup, per offset and per key)
     {
-        const int64_t n = std::max<int64_t>(L, p->TB + 1);
+        const int64_t n = std::max<int64_t>(std::max<int64_t>(L, p->TB + 1), K);
         hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
                            p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
                            p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
-                           ctrl);
+                           ctrl, p->at<int32_t>(lay.key_start), K);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
     }
     // stable radix sort: key -> (skey, perm)
     if (L > 0) {
         const int P = lay.passes;
         uint32_t* hist = p->at<uint32_t>(lay.hist);
-        uint64_t* part = p->at<uint64_t>(lay.scan_tmp);
         const int32_t* kin = p->at<int32_t>(lay.ckey);
         const int32_t* vin = nullptr;
         for (int pass = 0; pass < P; ++pass) {
@@ -700,8 +778,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
                                kin, L, shift, lay.n_tiles, hist);
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-            if (scan_exclusive<uint32_t>(hist, (int64_t)kRadixBins * lay.n_tiles,
-                                         reinterpret_cast<uint32_t*>(part), nullptr, s) != TT_OK)
+            if (scan_exclusive<uint32_t>(p, ++nscan, hist, (int64_t)kRadixBins * lay.n_tiles, nullptr, s) != TT_OK)
                 return fail(TT_ERR_HIP);
             hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                s, kin, vin, L, shift, lay.n_tiles, hist, kout, vout);
@@ -715,7 +792,6 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         int32_t* key_start = p->at<int32_t>(lay.key_start);
         int32_t* key_end = p->at<int32_t>(lay.key_end);
         uint64_t* kscan = p->at<uint64_t>(lay.key_scan);
-        if (fill32(key_start, 0xffffffffu, K, s) != TT_OK) return fail(TT_ERR_HIP);
         if (L > 0) {
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
@@ -726,8 +802,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
                            key_end, K, chunk, kscan);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-        if (scan_exclusive<uint64_t>(kscan, K, p->at<uint64_t>(lay.scan_tmp),
-                                     reinterpret_cast<uint64_t*>(ctrl + CTRL_SCAN_TOTAL), s) != TT_OK)
+        if (scan_exclusive<uint64_t>(p, ++nscan, kscan, K, reinterpret_cast<uint64_t*>(ctrl + CTRL_SCAN_TOTAL),
+                                     s) != TT_OK)
             return fail(TT_ERR_HIP);
         hipLaunchKernelGGL(k_groups, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start, kscan, K,
                            L, p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
@@ -741,9 +817,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.task_start));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
             // row-run ids: exclusive scan of the head flags, then the run tables
-            if (scan_exclusive<uint32_t>(p->at<uint32_t>(lay.rid), L,
-                                         reinterpret_cast<uint32_t*>(p->at<uint64_t>(lay.scan_tmp)),
-                                         nullptr, s) != TT_OK)
+            if (scan_exclusive<uint32_t>(p, ++nscan, p->at<uint32_t>(lay.rid), L, nullptr, s) != TT_OK)
                 return fail(TT_ERR_HIP);
             hipLaunchKernelGGL(k_runs, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.rid), p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),

@@ -33,6 +33,8 @@ enum CtrlSlot : int {
     CTRL_NUM_TASKS = 3,
     CTRL_NUM_RUNS = 4,    // row runs
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
+    CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
+    CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
     CTRL_QUEUE = 64,      // task-queue counters, one per 256-byte line:
                           // forward queues 0..7, backward queues 8..15
     CTRL_QSTRIDE = 64,
@@ -90,9 +92,20 @@ constexpr int kMaxD = 1024;
 constexpr int kMaxTables = 4096;
 constexpr int64_t kMaxKeys = int64_t(1) << 30;
 
+// Tile status of the single-pass scans: flag = (epoch << 2) | state, state 1
+// when `agg` (the tile's total) is published, 2 when `incl` (the sum through
+// the tile) is.
+struct alignas(32) ScanTileStatus {
+    uint32_t flag;
+    uint32_t pad_;
+    uint64_t agg;
+    uint64_t incl;
+};
+
 // Carving of the caller's workspace. Every array starts on a 256-byte boundary.
 struct Layout {
-    size_t ctrl, desc;
+    size_t ctrl, scan_st, desc;               // scan_st: tile status words of the single-pass
+                                             //     scans, right after ctrl (cleared with it)
     size_t key, i3, bag_of;                  // [L]
     size_t ckey;                             // [L] sort key = key * M3 + i3
     size_t bag_start;                        // [TB+1] int32 copy of the offsets
@@ -110,13 +123,12 @@ struct Layout {
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
     size_t task_start;                       // [Tmax+1] first chunk of each task
-    size_t scan_tmp;                         // uint64 partials of the multi-block scan
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
     size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, K, Gmax, Cmax, Tmax, NFB;
+    int64_t n_tiles, K, Gmax, Cmax, Tmax, NFB, scan_tiles;
     int passes;
 };
 
