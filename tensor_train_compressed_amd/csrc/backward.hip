@@ -110,13 +110,16 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 //
 // k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
 //               with atomics; fp64 keeps a sum of many cancelling terms within
-//               the fp32 tolerance) and the S rows of the runs that cross a
+//               the fp32 tolerance) and the fp64 sums of the runs that cross a
 //               chunk start (summed piece by piece)
 // k_bwd_sum     persistent waves over cost-balanced chunk tasks (per-XCD
 //               queues, stealing): for every run, S = sum of the grad_out rows
-//               of its lookups. A run inside one chunk is stored once; the
-//               pieces of a run cut by chunk starts are added with atomics.
-//               Memory-bound.
+//               of its lookups, accumulated in fp64. A run inside one chunk is
+//               stored once, rounded to fp32; the pieces of a run cut by chunk
+//               starts are added with fp64 atomics to its slot. Memory-bound.
+// k_bwd_cross   rounds the fp64 sums of the cut runs into their S rows
+//               (a hot row's run spans many chunks: an fp32 sum of its pieces
+//               would lose the fp32 tolerance on the slices it feeds)
 // k_bwd_batch   one workgroup per (slice, 8-group batch): forms the batch's
 //               prefixes P like the forward, then per run, on the matrix cores,
 //                 dG3[i3] += P^T S          (R x n3, added with atomics)
@@ -131,29 +134,82 @@ __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64
     return s == 0 || skey[s - 1] != skey[s];
 }
 
+// Where chunks cut row runs. Chunks of a group are `chunk` lookups apart, so
+// the chunk holding sorted position x, seen from chunk c that begins at b, is
+// c + floor((x - b) / chunk). A run cut by chunk starts is summed in the slot
+// of its first cutting chunk c_f (the chunk after the one holding its head):
+// slot = c_f - g - 1 for c_f in group g, unique and below ceil(L / chunk).
+struct CrossRef {
+    const int32_t* chunk_begin;
+    const int32_t* chunk_group;
+    const int32_t* skey;
+    const int32_t* rid;
+    const int32_t* run_start;
+    int32_t chunk;
+};
+
+__device__ __forceinline__ int32_t floor_div(int32_t x, int32_t n) {
+    return x >= 0 ? x / n : -((n - 1 - x) / n);
+}
+
+// slot of run `run` (cut by chunk starts) seen from a piece in chunk c
+__device__ __forceinline__ int64_t cross_slot(const CrossRef& x, int64_t c, int32_t run) {
+    const int32_t cf = (int32_t)c + floor_div(x.run_start[run] - x.chunk_begin[c], x.chunk) + 1;
+    return (int64_t)cf - x.chunk_group[c] - 1;
+}
+
+// run cut by the start of chunk c when c is that run's first cutting chunk,
+// else -1
+__device__ __forceinline__ int32_t first_cut_run(const CrossRef& x, int64_t c) {
+    const int32_t b = x.chunk_begin[c];
+    if (row_head(x.skey, b)) return -1;
+    const int32_t run = x.rid[b] - 1;
+    return x.run_start[run] >= b - x.chunk ? run : -1;
+}
+
+// visit(run, slot, part) for every first cutting chunk and every 4-element
+// part of its row: one thread per (chunk, part), so the few hundred slots of
+// a step are converted in parallel rather than one after another.
+template <int D, class F>
+__device__ __forceinline__ void for_each_first_cut(const CrossRef& x, int32_t NC, F visit) {
+    constexpr int D4 = D / 4;
+    const int64_t n = (int64_t)NC * D4;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += nth) {
+        const int64_t c = t / D4;
+        const int part = (int)(t - c * D4);
+        const int32_t run = first_cut_run(x, c);
+        if (run >= 0) visit(run, c - x.chunk_group[c] - 1, part);
+    }
+}
+
 template <int DL>
 __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
                                                   double* __restrict__ dg3, int64_t n3,
-                                                  float* __restrict__ S,
-                                                  const int32_t* __restrict__ chunk_begin,
-                                                  const int32_t* __restrict__ skey,
-                                                  const int32_t* __restrict__ rid,
+                                                  double* __restrict__ xsum, CrossRef x,
                                                   const int32_t* __restrict__ ctrl) {
     constexpr int D = 64 * DL;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
-    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
-    const int lane = threadIdx.x & 63;
-    for (int64_t c = tid >> 6; c < NC; c += nth >> 6) {
-        const int32_t b = chunk_begin[c];
-        if (!row_head(skey, b)) {
-            float* dst = S + (int64_t)(rid[b] - 1) * D + lane * DL;
+    for_each_first_cut<D>(x, ctrl[CTRL_NUM_CHUNKS], [&](int32_t, int64_t slot, int part) {
+        double* dst = xsum + slot * D + 4 * part;
 #pragma unroll
-            for (int k = 0; k < DL; ++k) dst[k] = 0.f;
-        }
-    }
+        for (int k = 0; k < 4; ++k) dst[k] = 0.0;
+    });
+}
+
+template <int DL>
+__global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xsum, CrossRef x,
+                                                   float* __restrict__ S,
+                                                   const int32_t* __restrict__ ctrl) {
+    constexpr int D = 64 * DL;
+    for_each_first_cut<D>(x, ctrl[CTRL_NUM_CHUNKS], [&](int32_t run, int64_t slot, int part) {
+        const double* src = xsum + slot * D + 4 * part;
+        *reinterpret_cast<floatx4*>(S + (int64_t)run * D + 4 * part) =
+            floatx4{(float)src[0], (float)src[1], (float)src[2], (float)src[3]};
+    });
 }
 
 struct SumArgs {
@@ -167,6 +223,8 @@ struct SumArgs {
     int64_t L;
     const float* gout;
     float* S;
+    double* xsum;
+    CrossRef x;
 };
 
 template <int DL>
@@ -181,15 +239,16 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
             const bool tail_whole = (s1 == a.L) || row_head(a.skey, s1);
             int32_t cur = 0;
             bool cur_head = false;
-            float sacc[DL];
+            double sacc[DL];
 #pragma unroll
-            for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+            for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
             auto flush = [&](bool whole) {
-                float* dst = a.S + (int64_t)cur * D + lane * DL;
                 if (whole) {
+                    float* dst = a.S + (int64_t)cur * D + lane * DL;
 #pragma unroll
-                    for (int k = 0; k < DL; ++k) dst[k] = sacc[k];
+                    for (int k = 0; k < DL; ++k) dst[k] = (float)sacc[k];
                 } else {
+                    double* dst = a.xsum + cross_slot(a.x, c, cur) * D + lane * DL;
 #pragma unroll
                     for (int k = 0; k < DL; ++k) atomicAdd(dst + k, sacc[k]);
                 }
@@ -220,10 +279,10 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
                                 cur = __builtin_amdgcn_readlane(rrv, r);
                                 cur_head = ((m >> r) & 1ull) != 0;
 #pragma unroll
-                                for (int k = 0; k < DL; ++k) sacc[k] = 0.f;
+                                for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
                             }
 #pragma unroll
-                            for (int k = 0; k < DL; ++k) sacc[k] += v[u][k];
+                            for (int k = 0; k < DL; ++k) sacc[k] += (double)v[u][k];
                         }
                     }
                 }
@@ -270,21 +329,25 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
     const float* G3 = a.g3 + c.o3;
     double* dG3 = a.dg3 + c.o3;
     int cur = -1;
-    floatx4 dacc[MT][RT];
+    // dP sums a group's runs (up to m3 of them, each a sum of up to tens of
+    // thousands of grad rows): fp64 matrix-core products and accumulators keep
+    // it within the fp32 tolerance of the fp64 reference (fp32 accumulation
+    // over the runs does not)
+    doublex4 dacc[MT][RT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
     auto flush = [&]() {
-        // lane holds dP[p = 16mt + 4q + v][r2 = 16nt + col]
+        // the fp64 product's lane holds dP[p = 16mt + q + 4v][r2 = 16nt + col]
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    atomicAdd(&sDP[cur * PR + (16 * mt + 4 * q + v) * R + 16 * nt + col], dacc[mt][nt][v]);
-                dacc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    atomicAdd(&sDP[cur * PR + (16 * mt + q + 4 * v) * R + 16 * nt + col], (float)dacc[mt][nt][v]);
+                dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
             }
     };
     // Wave w takes a contiguous range of tiles, so consecutive tiles mostly
@@ -358,7 +421,8 @@ __global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < RT; ++nt)
-                        dacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(C.av[ru][mt], C.bq[ru][nt], dacc[mt][nt], 0, 0, 0);
+                        dacc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)C.av[ru][mt], (double)C.bq[ru][nt],
+                                                                            dacc[mt][nt], 0, 0, 0);
             }
         }
         // dG3[i3] += P^T S: column (run lk, j3), rows r2. The A operand of P^T
@@ -482,9 +546,13 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     for (int e = tid; e < R * 64; e += 256) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
 
     const int rt = w & 1, ch = w >> 1;
-    floatx4 acc2[2];
-    acc2[0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc2[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // dG1 and dG2 are sums over every lookup of the slice (hundreds of
+    // thousands for the hot ones) with heavy cancellation: their products run
+    // on the fp64 matrix cores (fp32 operands convert exactly), so the only
+    // fp32 rounding left is that of the stored result
+    doublex4 acc2[2];
+    acc2[0] = doublex4{0.0, 0.0, 0.0, 0.0};
+    acc2[1] = doublex4{0.0, 0.0, 0.0, 0.0};
 
     floatx4 dpv[NDP], g1v[NG1];
     int32_t i1c = 0, i1n = 0;
@@ -514,11 +582,11 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
         __syncthreads();
         // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c]: one k-step per group
         for (int gi = 0; gi < ng; ++gi) {
-            const float av = sA[gi * N1 * R + q * R + 16 * rt + col];
+            const double av = sA[gi * N1 * R + q * R + 16 * rt + col];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float bv = sD[(gi * N1 + q) * DS + 16 * (2 * ch + j) + col];
-                acc2[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc2[j], 0, 0, 0);
+                const double bv = sD[(gi * N1 + q) * DS + 16 * (2 * ch + j) + col];
+                acc2[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc2[j], 0, 0, 0);
             }
         }
         // dG1 rows (g, j1) of row tiles ch + 2m, r1 block rt, K = 64 columns
@@ -526,29 +594,30 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
         for (int m = 0; m < MR / 32; ++m) {
             const int rtile = ch + 2 * m;
             if (4 * rtile < ng) {
-                floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
+                doublex4 acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
                 for (int s2 = 0; s2 < 16; ++s2) {
-                    const float av = sD[(16 * rtile + col) * DS + 4 * s2 + q];
-                    const float bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc1, 0, 0, 0);
+                    const double av = sD[(16 * rtile + col) * DS + 4 * s2 + q];
+                    const double bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
+                    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc1, 0, 0, 0);
                 }
-                // lane holds rows 4q+v = (group 4*rtile+q, j1 v), column r1 = 16*rt + col
-                const int gi = 4 * rtile + q;
-                if (gi < ng) {
-                    double* dst = dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + 16 * rt + col;
+                // the fp64 product's lane holds rows q + 4v = (group 4*rtile + v,
+                // j1 = q), column r1 = 16*rt + col
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) atomicAdd(dst + v * R, (double)acc1[v]);
+                for (int v = 0; v < 4; ++v) {
+                    const int gi = 4 * rtile + v;
+                    if (gi < ng) atomicAdd(dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + q * R + 16 * rt + col, acc1[v]);
                 }
             }
         }
     }
-    // dG2[i2][:, block columns] is owned by this workgroup: plain stores
+    // dG2[i2][:, block columns] is owned by this workgroup: plain stores (the
+    // fp64 product's lane holds rows q + 4v of the tile)
     float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R + c0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) D2[(16 * rt + 4 * q + v) * N2R + 16 * (2 * ch + j) + col] = acc2[j][v];
+        for (int v = 0; v < 4; ++v) D2[(16 * rt + q + 4 * v) * N2R + 16 * (2 * ch + j) + col] = (float)acc2[j][v];
 }
 
 template <int N1, int N2, int R, int N3>
@@ -562,16 +631,25 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     constexpr int DL = N1 * N2 * N3 / 64;
     double* acc1 = p->at<double>(p->lay.acc1);
     double* acc3 = p->at<double>(p->lay.acc3);
-    hipLaunchKernelGGL(k_bwd_prep<DL>, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
-                       p->at<float>(p->lay.stage), p->at<int32_t>(p->lay.chunk_begin),
-                       p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid), p->ctrl());
+    double* xsum = p->at<double>(p->lay.xsum);
+    const CrossRef xr{p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_group),
+                      p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
+                      p->at<int32_t>(p->lay.run_start), p->chunk};
+    hipLaunchKernelGGL(k_bwd_prep<DL>,
+                       dim3(std::max(512u, std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u))),
+                       dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
+                       xsum, xr, p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
         SumArgs sa{p->ctrl(), p->at<int32_t>(p->lay.task_start), p->at<int32_t>(p->lay.chunk_begin),
                    p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_bag),
                    p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid), p->L, gout,
-                   p->at<float>(p->lay.stage)};
+                   p->at<float>(p->lay.stage), xsum, xr};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
+        TT_LAUNCH_CHECK();
+        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3(std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u)),
+                           dim3(256), 0, s, xsum, xr,
+                           p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
         BwdArgs a{p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
                   p->at<float>(p->lay.stage), acc3, p->at<float>(p->lay.dpg)};

@@ -62,6 +62,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.rid = take(l4);
     y.run_i3 = take(l4);
     y.run_of = take(l4);
+    y.run_start = take(l4);
     // one row per row run, plus kStageSpare rows that take the writes of
     // inactive lanes (kept branch-free) in the forward
     y.stage = take(sizeof(float) * ((size_t)L + kStageSpare) * (size_t)D);
@@ -89,6 +90,10 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);
+    // a row run cut by chunk starts has a first cutting chunk, which is never
+    // the first chunk of its group; chunk c of group g that is not the first
+    // one of g has slot c - g - 1 < ceil(L / chunk)
+    y.xsum = take(sizeof(double) * (size_t)((L + chunk - 1) / chunk) * (size_t)D);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
@@ -548,12 +553,16 @@ __global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
                                               int32_t M3, int32_t* ctrl,
                                               int32_t* __restrict__ run_i3,
                                               int32_t* __restrict__ run_of,
+                                              int32_t* __restrict__ run_start,
                                               int32_t* __restrict__ group_rbase) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= L) return;
     const int32_t rr = rid[s];
     const int32_t hr = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
-    if (hr) run_i3[rr] = sorted_i3[s];
+    if (hr) {
+        run_i3[rr] = sorted_i3[s];
+        run_start[rr] = (int32_t)s;
+    }
     run_of[perm[s]] = rr + hr - 1;
     const int32_t k = skey[s] / M3;
     if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = rr;
@@ -823,7 +832,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.rid), p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
                                p->at<int32_t>(lay.sorted_i3), p->at<uint64_t>(lay.key_scan), L, p->M3,
                                ctrl, p->at<int32_t>(lay.run_i3), p->at<int32_t>(lay.run_of),
-                               p->at<int32_t>(lay.group_rbase));
+                               p->at<int32_t>(lay.run_start), p->at<int32_t>(lay.group_rbase));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         if (lay.NFB > 0) {

@@ -8,6 +8,7 @@
 namespace tt {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int find_table(const TabDev* __restrict__ desc, int32_t T, int32_t key) {
     int lo = 0, hi = T;  // last t with key_base <= key

@@ -182,6 +182,30 @@ def test_forward_full_size_sampled(name):
     run_forward_check(p, f"{name} full", chunk=256, bags=_sample_bags(p))
 
 
+def test_forward_permuted_full_size_sampled():
+    # the skewed table with its rows permuted: far more, smaller prefix groups
+    p = wl.make("skew11m", permuted=True)
+    run_forward_check(p, "skew11m permuted full", chunk=256, bags=_sample_bags(p))
+
+
+def test_repeat_runs():
+    # the forward sums every bag in a fixed order: the same bits on every run;
+    # the backward's fp64 accumulation order varies between runs, its fp32
+    # result stays within the tolerance of itself
+    p = wl.make("train11m")
+    dp = DevProblem(p, 256)
+    a = dp.forward().cpu().numpy()
+    b = dp.forward().cpu().numpy()
+    np.testing.assert_array_equal(a, b, err_msg="forward repeat")
+    dp2 = DevProblem(p, 256)
+    c = dp2.forward().cpu().numpy()
+    np.testing.assert_array_equal(a, c, err_msg="forward with a fresh plan")
+    d1 = [x.cpu().numpy() for x in dp.backward()]
+    d2 = [x.cpu().numpy() for x in dp.backward()]
+    for k in range(3):
+        assert_close(d2[k], d1[k].astype(np.float64), f"backward repeat dG{k + 1}")
+
+
 # ---------------------------------------------------------------------------
 # backward + SGD
 
@@ -212,7 +236,7 @@ def _check_backward(p, label, chunk=256, mask=None, slices=None):
 
 def test_backward_small_all():
     p = wl.make("train11m", batch=256)
-    for chunk in (1, 256):
+    for chunk in (1, 7, 256):
         _check_backward(p, f"train11m B=256", chunk=chunk)
 
 
@@ -250,7 +274,9 @@ def test_backward_full_size_sampled():
     t = p.tables[0]
     R, (n1, n2, n3) = t.rank, t.n
     pl = oracle.plan_problem(p, 256)
-    i1s = np.array([3, 57, 199]); i2s = np.array([100, 150, 219]); i3s = np.array([17, 131, 249])
+    # the Zipf head is unpermuted: i2 = 1 and i3 = 1 pick up hot rows (row 1
+    # sits in the largest prefix group), while keeping the masked oracle short
+    i1s = np.array([3, 57, 199]); i2s = np.array([1, 100, 219]); i3s = np.array([1, 131, 249])
     mask = (_slice_mask(p, pl, 1, i1s) | _slice_mask(p, pl, 2, i2s) |
             _slice_mask(p, pl, 3, i3s)).astype(np.uint8)
     say("sampled backward lookups", int(mask.sum()))
