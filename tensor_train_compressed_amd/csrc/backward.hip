@@ -86,11 +86,13 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     }
 }
 
+// dG1 (and dG3 when n3 > 0) from their fp64 accumulators.
 __global__ __launch_bounds__(256) void k_bwd_finish(const double* __restrict__ a1, float* __restrict__ dg1,
                                                     int64_t n1, const double* __restrict__ a3,
-                                                    float* __restrict__ dg3, int64_t n3) {
+                                                    float* __restrict__ dg3, int64_t n3, int32_t* ctrl) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    if (tid == 0) ctrl[CTRL_NUM_XPIECES] = 0;   // the next backward on this plan appends from 0
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = (float)a1[i];
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = (float)a3[i];
 }
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 
 // ---------------------------------------------------------------------------
 // Matrix-core backward for the common shapes (n1 = 4, n3 = 4, shared by all
-// tables). Four kernels, all on row runs (one run per distinct table row of a
+// tables). Seven kernels, all on row runs (one run per distinct table row of a
 // group, the same runs the forward contracts):
 //
 // k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
@@ -120,11 +122,15 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 // k_bwd_cross   rounds the fp64 sums of the cut runs into their S rows
 //               (a hot row's run spans many chunks: an fp32 sum of its pieces
 //               would lose the fp32 tolerance on the slices it feeds)
-// k_bwd_batch   one workgroup per (slice, 8-group batch): forms the batch's
-//               prefixes P like the forward, then per run, on the matrix cores,
-//                 dG3[i3] += P^T S          (R x n3, added with atomics)
-//                 dP_g    += S G3[i3]^T     (n1*n2 x R, reduced in LDS)
-//               and stores each group's dL/dP row once.
+// k_bwd_pfx     recomputes P of every group (persistent workgroups over the
+//               planner's prefix batches, as the forward) into a global buffer
+// k_bwd_runs    one wave per piece of up to kRunRange runs of one group, the
+//               group's P in registers;
+//               per run, on the matrix cores,
+//                 dG3[i3] += P^T S          (R x n3, added with fp64 atomics)
+//                 dP_g    += S G3[i3]^T     (n1*n2 x R, summed in registers)
+//               and stores each group's dL/dP row once (atomics only for the
+//               few groups large enough to be split into pieces)
 // k_bwd_prefix  one workgroup per ((table, i2) slice, 64-column block):
 //                 dG2[i2] += G1[i1]^T dP    (plain stores, owned)
 //                 dG1[i1] += dP G2[i2]^T    (atomics across column blocks)
@@ -183,16 +189,38 @@ __device__ __forceinline__ void for_each_first_cut(const CrossRef& x, int32_t NC
     }
 }
 
-template <int DL>
+template <int DL, int PR>
 __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
                                                   double* __restrict__ dg3, int64_t n3,
                                                   double* __restrict__ xsum, CrossRef x,
-                                                  const int32_t* __restrict__ ctrl) {
-    constexpr int D = 64 * DL;
+                                                  float* __restrict__ dpg,
+                                                  const int32_t* __restrict__ group_rbase,
+                                                  int32_t* __restrict__ xpiece, int32_t* ctrl) {
+    constexpr int D = 64 * DL, PR4 = PR / 4;
+    static_assert(PR % 4 == 0, "shape");
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
+    // groups of more than kRunRange runs are split into pieces of kRunRange
+    // runs: zero their dP rows (the pieces add to them) and list every piece
+    // but the first (the run kernel's wave g takes piece 0 of group g)
+    const int64_t U = ctrl[CTRL_NUM_GROUPS];
+    for (int64_t i = tid; i < U * PR4; i += nth) {
+        const int64_t g = i / PR4;
+        if (group_rbase[g + 1] - group_rbase[g] > kRunRange)
+            reinterpret_cast<floatx4*>(dpg + g * PR)[i % PR4] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int64_t g = tid; g < U; g += nth) {
+        const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
+        if (np > 1) {
+            const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np - 1);
+            for (int32_t k = 1; k < np; ++k) {
+                xpiece[2 * (base + k - 1)] = (int32_t)g;
+                xpiece[2 * (base + k - 1) + 1] = k;
+            }
+        }
+    }
     for_each_first_cut<D>(x, ctrl[CTRL_NUM_CHUNKS], [&](int32_t, int64_t slot, int part) {
         double* dst = xsum + slot * D + 4 * part;
 #pragma unroll
@@ -292,175 +320,235 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
     }
 }
 
-struct BwdArgs {
-    const BatchRec* recs;
-    int64_t nb;
+// P of every group, for the run kernel. Persistent workgroups walk the
+// planner's prefix batches like the forward (the next batch's loads are in
+// flight while the current one is formed) and store each group's P in the
+// lane order the run kernel reads it: float4 number x = ((rt*KQ + h)*4 + q)*16
+// + col of a group holds P[4*(4h + u) + q][16*rt + col], u = 0..3, so that a
+// lane (col, q) loads its whole matrix-core operand as RT*KQ float4.
+template <int N1, int N2, int R>
+__global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t nb,
+                                                 const int32_t* __restrict__ run_i3,
+                                                 const float* __restrict__ g1, const float* __restrict__ g2,
+                                                 float* __restrict__ pbuf) {
+    using B = PrefixBatch<N1, N2, R>;
+    constexpr int NP = B::NP, AS = B::AS, SG = B::SG, KQ = NP / 16, PF4 = NP * R / 4;
+    static_assert(NP % 16 == 0 && R % 16 == 0 && 64 * B::WAVES == 512, "shape");
+    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];
+    __shared__ int32_t sRb[SG + 1];
+    extern __shared__ int32_t sI3[];
+    const int tid = threadIdx.x;
+    const int64_t G = gridDim.x;
+    int64_t b = blockIdx.x;
+    int32_t rwA = rec_word(recs, b, nb);
+    int32_t rwB = rec_word(recs, b + G, nb);
+    BatchPf<N1, N2, R> f;
+    batch_fetch<N1, N2, R>(rwA, run_i3, g1, g2, f);
+    for (; b < nb; b += G) {
+        const int32_t rwC = rec_word(recs, b + 2 * G, nb);
+        BatchCtx c;
+        const bool live = rec_field(rwA, RW_NG) > 0;
+        if (live) batch_prefix<N1, N2, R>(rwA, run_i3, f, sU, sRb, sI3, c);
+        batch_fetch<N1, N2, R>(rwB, run_i3, g1, g2, f);
+        if (live) {
+            const float* sP = sU;
+            for (int e4 = tid; e4 < c.ng * PF4; e4 += 512) {
+                const int gi = e4 / PF4, x = e4 % PF4;
+                const int col = x & 15, q = (x >> 4) & 3, h = (x >> 6) % KQ, rt = (x >> 6) / KQ;
+                const float* src = sP + (gi * NP + 16 * h + q) * AS + 16 * rt + col;
+                const floatx4 v = {src[0], src[4 * AS], src[8 * AS], src[12 * AS]};
+                *reinterpret_cast<floatx4*>(pbuf + ((int64_t)(c.g0 + gi) * PF4 + x) * 4) = v;
+            }
+            __syncthreads();
+        }
+        rwA = rwB;
+        rwB = rwC;
+    }
+}
+
+// Run pieces: piece 0 of group g is handed to wave g, the further pieces of
+// the groups with more than kRunRange runs come from the list the prep kernel
+// wrote. A piece is the group's runs [kRunRange*k, kRunRange*(k+1)).
+struct RunsArgs {
+    const TabDev* desc;
+    int32_t T;
+    const int32_t* ctrl;
+    const int32_t* xpiece;
+    const int32_t* group_rbase;
+    const int32_t* group_key;
     const int32_t* run_i3;
-    const float* g1;
-    const float* g2;
-    const float* g3;
     const float* S;
+    const float* pbuf;
+    const float* g3;
     double* dg3;
     float* dpg;
 };
 
-template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(1024) void k_bwd_batch(BwdArgs a) {
-    using B = PrefixBatch<N1, N2, R>;
-    constexpr int NP = B::NP, D = NP * N3, PR = NP * R, SG = B::SG, AS = B::AS, WAVES = B::WAVES;
-    constexpr int MT = NP / 16, RT = R / 16, KSP = NP / 4, LK = 16 / N3, CN = R * N3;
-    static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0, "shape");
-    __shared__ float sDP[SG * PR];   // dP of the batch's groups
-    __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
-    __shared__ int32_t sRb[SG + 1];
-    __shared__ int32_t sTp[SG + 1];
-    extern __shared__ int32_t sI3[];   // the batch's run i3 list
-
-    BatchCtx c;
-    if (!batch_begin<N1, N2, R>(a.recs, a.nb, a.run_i3, a.g1, a.g2, sU, sRb, sI3, c)) return;
-    const float* sP = sU;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    batch_tiles(sRb, sTp, c.ng, LK);
-    for (int e = tid; e < SG * PR; e += 64 * WAVES) sDP[e] = 0.f;
-    __syncthreads();
-
-    const int ntile = sTp[c.ng];
+// One wave per piece (persistent, static stride), the group's P in registers;
+// four runs at a time (lane group q takes run t0 + q):
+//   dG3[i3] += P^T S          fp32 products over p, added to the fp64 dG3
+//                              accumulator with atomics
+//   dP      += S G3[i3]^T     fp64 products and sums over the piece
+// then dP goes to the group's row: a plain store, or fp32 atomics when the
+// group has several pieces (its row was zeroed first).
+template <int N1, int N2, int R, int N3, class Add3>
+__device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
+    constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R, MT = NP / 16, RT = R / 16, KSP = NP / 4;
+    constexpr int KQ = KSP / 4, CN = R * N3, W = kRunRange;
+    static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64, "shape");
+    const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
-    const float* G3 = a.g3 + c.o3;
-    double* dG3 = a.dg3 + c.o3;
-    int cur = -1;
-    // dP sums a group's runs (up to m3 of them, each a sum of up to tens of
-    // thousands of grad rows): fp64 matrix-core products and accumulators keep
-    // it within the fp32 tolerance of the fp64 reference (fp32 accumulation
-    // over the runs does not)
-    doublex4 dacc[MT][RT];
+    const int32_t U = a.ctrl[CTRL_NUM_GROUPS];
+    const int64_t npieces = (int64_t)U + a.ctrl[CTRL_NUM_XPIECES];
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; k < npieces; k += nw) {
+        int64_t g = k;
+        int32_t part = 0;
+        if (k >= U) {
+            g = a.xpiece[2 * (k - U)];
+            part = a.xpiece[2 * (k - U) + 1];
+        }
+        const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
+        const bool split = ge - gs > W;
+        const int32_t s = gs + W * part, e = min(ge, s + W);
+        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
+        const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
+        floatx4 preg[RT][KQ];
+        const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
-    auto flush = [&]() {
-        // the fp64 product's lane holds dP[p = 16mt + q + 4v][r2 = 16nt + col]
+            for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
+        doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < RT; ++nt) {
+            for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
+        for (int32_t t0 = s; t0 < e; t0 += 4) {
+            const bool okq = t0 + q < e;
+            const int32_t rq = okq ? t0 + q : t0;
+            const int32_t i3q = __shfl(i3l, rq - s);
+            const float* Sq = a.S + (int64_t)rq * D;
+            const float* G3q = a.g3 + o3 + (int64_t)i3q * CN;
+            floatx4 av[MT], bq[RT];
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    atomicAdd(&sDP[cur * PR + (16 * mt + q + 4 * v) * R + 16 * nt + col], (float)dacc[mt][nt][v]);
-                dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
+            for (int mt = 0; mt < MT; ++mt) av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
+            const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
+            float bv[KSP];
+#pragma unroll
+            for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = Sl[(4 * s2 + q) * N3];
+            // dG3: rows (run t0 + lk, j3) of P^T S; lane (col, q) gets run
+            // t0 + q, r2 = 16rt + col, j3 = v
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KSP; ++s2)
+                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
+                if (okq) add3(o3 + (int64_t)i3q * CN, (16 * rt + col) * N3, rq, cc);
             }
-    };
-    // Wave w takes a contiguous range of tiles, so consecutive tiles mostly
-    // share a group and the dP flush and P reload happen once per group.
-    // A tile's S and G3 operands are loaded one tile ahead, before the
-    // current tile's dG3 atomics: loads and atomics share one in-order
-    // completion counter, so a load can only be waited for alone if every
-    // memory access issued after it is certain to have been issued. The loop
-    // body therefore holds no conditional load (the look-ahead tile is clamped
-    // to the last one, run i3 values come from LDS), it is unrolled by two with
-    // ping-pong operand sets, and no register that a load is still filling is
-    // ever copied.
-    const int per = (ntile + WAVES - 1) / WAVES;
-    const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
-    struct Ids {
-        int g;
-        int32_t rbase, rend, i3;   // absolute run ids; i3 of this lane's run (run rbase's past the end)
-        bool ok;
-    };
-    struct Ops {
-        int g;
-        int32_t rbase, rend;
-        bool ok;
-        double* dst;          // dG3 slice of this lane's run, column j3
-        float bv[KSP];        // S of this lane's run, K = p = 4*s2 + q (dG3 product)
-        float av[LK][MT];     // S of run ru, K = j3 (dP product)
-        float bq[LK][RT];     // G3[i3 of run ru], K = j3
-    };
-    int gs = 0;               // walks forward over the batch's groups
-    auto ids_of = [&](int k, Ids& o) {
-        const int tt = t0 + k;
-        while (sTp[gs + 1] <= tt) ++gs;
-        o.g = gs;
-        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]), re = sRb[gs + 1];   // relative to rb0
-        o.ok = rb + lk < re;
-        o.i3 = sI3[o.ok ? rb + lk : rb];
-        o.rbase = c.rb0 + rb;
-        o.rend = c.rb0 + re;
-    };
-    auto load_ops = [&](const Ids& o, Ops& x) {
-        x.g = o.g; x.rbase = o.rbase; x.rend = o.rend; x.ok = o.ok;
-        x.dst = dG3 + (int64_t)o.i3 * CN + j3;
-        const int32_t r = o.ok ? o.rbase + lk : o.rbase;
-        const float* Sb = a.S + (int64_t)r * D + j3;
+            // dP: K = (run q, j3 = step), fp64 products and sums (a hot
+            // group's dP adds up hundreds of runs of large S); a run past the
+            // piece adds zeros
 #pragma unroll
-        for (int s2 = 0; s2 < KSP; ++s2) x.bv[s2] = Sb[(4 * s2 + q) * N3];
+            for (int mt = 0; mt < MT; ++mt) {
+                if (!okq) av[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ru = 0; ru < LK; ++ru) {
-            const bool okr = o.rbase + ru < o.rend;
-            const int32_t i3r = __builtin_amdgcn_readlane(o.i3, ru * N3);
-            const float* Sr = a.S + (int64_t)(okr ? o.rbase + ru : o.rbase) * D;
-            const float* gb = G3 + (int64_t)i3r * CN;
+                for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) x.av[ru][mt] = Sr[(16 * mt + col) * N3 + q];
-#pragma unroll
-            for (int nt = 0; nt < RT; ++nt) x.bq[ru][nt] = gb[(16 * nt + col) * N3 + q];
-        }
-    };
-    auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
-        ids_of(min(k + 2, n - 1), Inew);
-        load_ops(Inext, Nx);
-        if (C.g != cur) {
-            if (cur >= 0) flush();
-            cur = C.g;
-        }
-        // dP += S G3[i3]^T: one k-step (k = j3) per run of the tile
-#pragma unroll
-        for (int ru = 0; ru < LK; ++ru) {
-            if (C.rbase + ru < C.rend) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < RT; ++nt)
-                        dacc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)C.av[ru][mt], (double)C.bq[ru][nt],
+                    for (int st = 0; st < 4; ++st)
+                        dacc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[mt][st], (double)bq[nt][st],
                                                                             dacc[mt][nt], 0, 0, 0);
             }
         }
-        // dG3[i3] += P^T S: column (run lk, j3), rows r2. The A operand of P^T
-        // comes from LDS: lane (i, q) takes P[4*s2 + q][16*rt + i]; K = p runs
-        // as 4*s2 + q so that each S load reads 64 consecutive bytes per run.
+        // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col]
+        float* dst = a.dpg + g * PR;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            floatx4 cc = {0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int s2 = 0; s2 < KSP; ++s2)
-                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(cur * NP + 4 * s2 + q) * AS + 16 * rt + col],
-                                                          C.bv[s2], cc, 0, 0, 0);
-            // lanes past the group's last run add nothing (adding zeros
-            // instead measured slower: the extra atomics cost more than the
-            // conservative waits the branch brings)
-            if (C.ok) {
+            for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) atomicAdd(C.dst + (16 * rt + 4 * q + v) * N3, (double)cc[v]);
+                for (int v = 0; v < 4; ++v) {
+                    const int idx = (16 * mt + q + 4 * v) * R + 16 * nt + col;
+                    if (split) atomicAdd(dst + idx, (float)dacc[mt][nt][v]);
+                    else dst[idx] = (float)dacc[mt][nt][v];
+                }
+    }
+}
+
+// dG3 added straight to the fp64 accumulator with device atomics (tables
+// sharing their G3 slices' rows make this the general path)
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
+    runs_body<N1, N2, R, N3>(a, [&](int64_t row, int within, int32_t, const floatx4& c) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) atomicAdd(a.dg3 + row + within + v, (double)c[v]);
+    });
+}
+
+// One table: each run's dG3 term P^T S is stored as its own row (c3[run]),
+// and k_bwd_dg3 sums them per G3 slice. Device atomics from every CU on the
+// same few hundred G3 slices saturate the memory-side atomic units, and LDS
+// float atomics are slow on the CU; plain stores avoid both.
+template <int N1, int N2, int R, int N3>
+__global__ __launch_bounds__(256) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3) {
+    constexpr int CN = R * N3;
+    runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
+        *reinterpret_cast<floatx4*>(c3 + (int64_t)run * CN + within) = c;
+    });
+}
+
+// dG3[i3] = sum of c3[run] over the runs with that i3, in fp64: one workgroup
+// per G3 slice i3 scans the run i3 list (16-byte loads, UNR of them in flight
+// per lane) and gathers the matching rows; the 16 waves' sums are added in LDS.
+template <int CN>
+__global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ run_i3,
+                                                  const int32_t* __restrict__ ctrl,
+                                                  const float* __restrict__ c3, float* __restrict__ dg3) {
+    constexpr int PL = CN / 64, UNR = 8, WAVES = 16, SPAN = 256 * UNR;
+    static_assert(CN % 64 == 0, "shape");
+    __shared__ double red[WAVES][CN];
+    const int32_t row = blockIdx.x;
+    const int64_t NR = ctrl[CTRL_NUM_RUNS];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    double acc[PL];
+#pragma unroll
+    for (int k = 0; k < PL; ++k) acc[k] = 0.0;
+    for (int64_t base = (int64_t)w * SPAN; base < NR; base += (int64_t)WAVES * SPAN) {
+        int32_t v[UNR][4];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int64_t r = base + 256 * u + 4 * lane;
+            if (r + 3 < NR) {
+                const int4 x = *reinterpret_cast<const int4*>(run_i3 + r);
+                v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[u][c] = r + c < NR ? run_i3[r + c] : -1;
             }
         }
-    };
-    if (n > 0) {
-        Ids IA, IB;
-        Ops OA, OB;
-        ids_of(0, IA);
-        load_ops(IA, OA);
-        ids_of(min(1, n - 1), IB);
-        int k = 0;
-        for (; k + 1 < n; k += 2) {
-            step(k, OA, OB, IA, IB);
-            step(k + 1, OB, OA, IB, IA);
-        }
-        if (k < n) step(k, OA, OB, IA, IB);
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                for (uint64_t m = __ballot(v[u][c] == row); m; m &= m - 1) {
+                    const int64_t r = base + 256 * u + 4 * __builtin_ctzll(m) + c;
+                    const float* src = c3 + r * CN + lane * PL;
+#pragma unroll
+                    for (int k = 0; k < PL; ++k) acc[k] += (double)src[k];
+                }
     }
-    if (cur >= 0) flush();
+#pragma unroll
+    for (int k = 0; k < PL; ++k) red[w][lane * PL + k] = acc[k];
     __syncthreads();
-    // each group of the batch owns its dL/dP row: plain stores
-    for (int e = tid; e < c.ng * PR; e += 64 * WAVES) a.dpg[(int64_t)c.g0 * PR + e] = sDP[e];
+    for (int e = threadIdx.x; e < CN; e += 1024) {
+        double x = 0.0;
+#pragma unroll
+        for (int k = 0; k < WAVES; ++k) x += red[k][e];
+        dg3[(int64_t)row * CN + e] = (float)x;
+    }
 }
 
 // One workgroup (4 waves) per ((table, i2) slice, 64-column block of the N2*R
@@ -624,8 +712,12 @@ template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
                                  float* dg3, hipStream_t s) {
+    // one table: dG3 reduced per slice from per-run terms
+    const bool scan3 = p->T == 1 && p->tables[0].m[2] <= kMaxScanSlices3;
     if (!p->packed) {
+        // elements outside every table's slices are zero in the gradients
         tt_status st = fill32(dg2, 0u, p->extent[1], s);
+        if (st == TT_OK && scan3) st = fill32(dg3, 0u, p->extent[2], s);
         if (st != TT_OK) return st;
     }
     constexpr int DL = N1 * N2 * N3 / 64;
@@ -635,10 +727,12 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     const CrossRef xr{p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_group),
                       p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                       p->at<int32_t>(p->lay.run_start), p->chunk};
-    hipLaunchKernelGGL(k_bwd_prep<DL>,
+    constexpr int PR = N1 * N2 * R;
+    hipLaunchKernelGGL((k_bwd_prep<DL, PR>),
                        dim3(std::max(512u, std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u))),
-                       dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
-                       xsum, xr, p->ctrl());
+                       dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2], xsum, xr,
+                       p->at<float>(p->lay.dpg), p->at<int32_t>(p->lay.group_rbase),
+                       p->at<int32_t>(p->lay.xpiece), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
         SumArgs sa{p->ctrl(), p->at<int32_t>(p->lay.task_start), p->at<int32_t>(p->lay.chunk_begin),
@@ -648,14 +742,28 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
         hipLaunchKernelGGL(k_bwd_cross<DL>, dim3(std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u)),
-                           dim3(256), 0, s, xsum, xr,
-                           p->at<float>(p->lay.stage), p->ctrl());
+                           dim3(256), 0, s, xsum, xr, p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
-        BwdArgs a{p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
-                  p->at<float>(p->lay.stage), acc3, p->at<float>(p->lay.dpg)};
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
-        hipLaunchKernelGGL((k_bwd_batch<N1, N2, R, N3>), dim3((unsigned)p->n_fb),
-                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a);
+        const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
+        hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(512), lds, s,
+                           p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
+                           p->at<float>(p->lay.pbuf));
+        TT_LAUNCH_CHECK();
+        RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece),
+                    p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
+                    p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
+                    acc3, p->at<float>(p->lay.dpg)};
+        if (scan3) {
+            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
+                               p->at<float>(p->lay.c3));
+            TT_LAUNCH_CHECK();
+            hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->tables[0].m[2]), dim3(1024), 0, s,
+                               p->at<int32_t>(p->lay.run_i3), p->ctrl(), p->at<float>(p->lay.c3),
+                               dg3 + p->tables[0].g_offset[2]);
+        } else {
+            hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
+        }
         TT_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
@@ -663,7 +771,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                        p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, acc1, dg2);
     TT_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
-                       p->extent[2]);
+                       (scan3 && p->L > 0) ? 0 : p->extent[2], p->ctrl());
     TT_LAUNCH_CHECK();
     return TT_OK;
 }

@@ -36,7 +36,7 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t E1, int64_t E3, int64_t NFB) {
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -63,6 +63,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_i3 = take(l4);
     y.run_of = take(l4);
     y.run_start = take(l4);
+    y.xpiece = take(sizeof(int32_t) * 2 * (size_t)(L / kRunRange + 1));
     // one row per row run, plus kStageSpare rows that take the writes of
     // inactive lanes (kept branch-free) in the forward
     y.stage = take(sizeof(float) * ((size_t)L + kStageSpare) * (size_t)D);
@@ -88,8 +89,11 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.task_start = take(sizeof(int32_t) * (size_t)(y.Tmax + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
+    y.pbuf = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);
+    // per run, P^T S (the run's dG3 term), for the single-table reduction of dG3
+    y.c3 = take(T == 1 ? sizeof(float) * (size_t)L * (size_t)CN : 0);
     // a row run cut by chunk starts has a first cutting chunk, which is never
     // the first chunk of its group; chunk c of group g that is not the first
     // one of g has slot c - g - 1 < ceil(L / chunk)
@@ -559,12 +563,12 @@ __global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
     if (s >= L) return;
     const int32_t rr = rid[s];
     const int32_t hr = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
+    const int32_t k = skey[s] / M3;
     if (hr) {
         run_i3[rr] = sorted_i3[s];
         run_start[rr] = (int32_t)s;
     }
     run_of[perm[s]] = rr + hr - 1;
-    const int32_t k = skey[s] / M3;
     if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = rr;
     if (s == L - 1) {
         ctrl[CTRL_NUM_RUNS] = rr + hr;
@@ -620,11 +624,11 @@ using namespace tt;
 // host side
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
-                              int32_t* M3_out, int64_t* PR_out, int64_t* E1_out, int64_t* E3_out,
-                              int64_t* NFB_out) {
+                              int32_t* M3_out, int64_t* PR_out, int64_t* CN_out, int64_t* E1_out,
+                              int64_t* E3_out, int64_t* NFB_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = -1, M3 = 1;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
@@ -645,6 +649,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         M3 = std::max(M3, x.m[2]);
         NFB += (int64_t)x.m[1] * ((x.m[0] + kFwdBatch - 1) / kFwdBatch);
         PR = std::max<int64_t>(PR, (int64_t)x.n[0] * x.n[1] * x.rank);
+        CN = std::max<int64_t>(CN, (int64_t)x.rank * x.n[2]);
         E1 = std::max<int64_t>(E1, x.g_offset[0] + (int64_t)x.m[0] * x.n[0] * x.rank);
         E3 = std::max<int64_t>(E3, x.g_offset[2] + (int64_t)x.m[2] * x.rank * x.n[2]);
     }
@@ -653,6 +658,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
     *D_out = D;
     *M3_out = M3;
     *PR_out = PR;
+    *CN_out = CN;
     *E1_out = E1;
     *E3_out = E3;
     *NFB_out = NFB;
@@ -669,11 +675,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 
 extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
                                          int64_t B, int32_t chunk) {
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = 0, M3 = 1;
-    if (check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3, &NFB) != TT_OK) return 0;
+    if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3, NFB).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -682,15 +688,15 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                  tt_emb_plan_t* plan_out) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
-    int64_t K = 0, PR = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
     int32_t D = 0, M3 = 1;
-    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &E1, &E3, &NFB);
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, E1, E3, NFB);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();

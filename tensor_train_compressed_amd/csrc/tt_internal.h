@@ -32,6 +32,7 @@ enum CtrlSlot : int {
     CTRL_NUM_CHUNKS = 2,
     CTRL_NUM_TASKS = 3,
     CTRL_NUM_RUNS = 4,    // row runs
+    CTRL_NUM_XPIECES = 5, // backward: extra run pieces of the groups split over several waves
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
     CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
     CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
@@ -54,6 +55,13 @@ constexpr int kStageSpare = 4;
 // Workgroups of the persistent forward batch kernel: two per CU (the kernel's
 // registers allow two 8-wave workgroups on a CU).
 constexpr int kFwdPersistBlocks = 2 * 256;
+// The backward's run kernel hands out row runs in ranges of about this many
+// (a group of more runs is split; smaller groups are never split).
+constexpr int kRunRange = 32;
+// With one table of at most this many G3 slices, dG3 is reduced per slice
+// from per-run terms (one workgroup per slice scans the run list) instead of
+// with device atomics.
+constexpr int kMaxScanSlices3 = 1024;
 // LDS the batch kernels may spend on the run i3 list of one batch
 // (kFwdBatch * largest m3 int32 values); larger m3 takes the generic kernels.
 constexpr int kMaxBatchI3Bytes = 32768;
@@ -113,6 +121,7 @@ struct Layout {
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
     size_t run_start;                        // [L] int32: first sorted position of each row run
+    size_t xpiece;                           // [L/kRunRange + 1] int32 pairs: (group, piece) (backward)
     size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
     size_t stage;                            // [L + kStageSpare][D] float, one row per row run: forward, the
                                              //     run's embedding row; backward, its grad-row sum
@@ -125,6 +134,9 @@ struct Layout {
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
     size_t task_start;                       // [Tmax+1] first chunk of each task
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
+    size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group (backward),
+                                             //     in the lane order of the matrix-core operands
+    size_t c3;                               // [L][R*n3] float, one table only: P^T S per run
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
     size_t xsum;                             // [ceil(L/chunk)][D] double: S of the row runs
@@ -136,7 +148,7 @@ struct Layout {
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t E1, int64_t E3, int64_t NFB);
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB);
 
 }  // namespace tt
 

@@ -284,3 +284,24 @@ def test_backward_full_size_sampled():
     s2 = np.concatenate([np.arange(i * R * n2 * R, (i + 1) * R * n2 * R) for i in i2s])
     s3 = np.concatenate([np.arange(i * R * n3, (i + 1) * R * n3) for i in i3s])
     _check_backward(p, "train11m full", chunk=256, mask=mask, slices=(s1, s2, s3))
+
+
+def test_backward_hot_slices_full_size():
+    """train11m at full size, the hottest slices (i1 = 0, i2 = 0, i3 = 0):
+    against the fp64 oracle's values stored by
+    tests/golden/make_train11m_hot_slices.py (the oracle on these slices takes
+    about a minute, too long to rerun here). Two runs: the fp64 accumulation
+    order differs between them."""
+    from tests.golden.make_train11m_hot_slices import OUT, fingerprint
+    g = np.load(OUT)
+    p = wl.make("train11m")
+    assert str(g["fingerprint"]) == fingerprint(p), \
+        "train11m inputs changed: rerun tests/golden/make_train11m_hot_slices.py"
+    t = p.tables[0]
+    R, (n1, n2, n3) = t.rank, t.n
+    dp = DevProblem(p, 256)
+    for run in range(2):
+        d = [x.cpu().numpy() for x in dp.backward()]
+        assert_close(d[0][:n1 * R], g["dg1_i1_0"], f"hot dG1[i1=0] run {run}")
+        assert_close(d[1][:R * n2 * R], g["dg2_i2_0"], f"hot dG2[i2=0] run {run}")
+        assert_close(d[2][:R * n3], g["dg3_i3_0"], f"hot dG3[i3=0] run {run}")

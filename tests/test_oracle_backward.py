@@ -90,3 +90,18 @@ def test_mask_partition_sums_to_full():
     b = oracle.backward_problem(p, mask=1 - mask)
     for f, x, y in zip(full, a, b):
         np.testing.assert_allclose(x + y, f, rtol=1e-12, atol=1e-12)
+
+
+def test_hot_slice_fixture_inputs_current():
+    """The stored hot-slice gradients (tests/golden/train11m_hot_slices.npz,
+    written by the oracle) belong to the inputs the generator draws today."""
+    import workloads as wl
+    from tests.golden.make_train11m_hot_slices import OUT, fingerprint
+    g = np.load(OUT)
+    p = wl.make("train11m")
+    assert str(g["fingerprint"]) == fingerprint(p)
+    t = p.tables[0]
+    R, (n1, n2, n3) = t.rank, t.n
+    assert g["dg1_i1_0"].shape == (n1 * R,)
+    assert g["dg2_i2_0"].shape == (R * n2 * R,)
+    assert g["dg3_i3_0"].shape == (R * n3,)
