@@ -203,8 +203,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
     // groups of more than kRunRange runs are split into pieces of kRunRange
-    // runs: zero their dP rows (the pieces add to them) and list every piece
-    // but the first (the run kernel's wave g takes piece 0 of group g)
+    // runs: zero their dP rows (the pieces add to them) and list their pieces
+    // (the run kernel takes these first, then one piece per other group)
     const int64_t U = ctrl[CTRL_NUM_GROUPS];
     for (int64_t i = tid; i < U * PR4; i += nth) {
         const int64_t g = i / PR4;
@@ -214,10 +214,10 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
     for (int64_t g = tid; g < U; g += nth) {
         const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
         if (np > 1) {
-            const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np - 1);
-            for (int32_t k = 1; k < np; ++k) {
-                xpiece[2 * (base + k - 1)] = (int32_t)g;
-                xpiece[2 * (base + k - 1) + 1] = k;
+            const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np);
+            for (int32_t k = 0; k < np; ++k) {
+                xpiece[2 * (base + k)] = (int32_t)g;
+                xpiece[2 * (base + k) + 1] = k;
             }
         }
     }
@@ -366,9 +366,10 @@ __global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ re
     }
 }
 
-// Run pieces: piece 0 of group g is handed to wave g, the further pieces of
-// the groups with more than kRunRange runs come from the list the prep kernel
-// wrote. A piece is the group's runs [kRunRange*k, kRunRange*(k+1)).
+// Run pieces. A piece is a group's runs [kRunRange*k, kRunRange*(k+1)). The
+// pieces of the groups with more than kRunRange runs come first, from the
+// list the prep kernel wrote (X of them; the longest work starts first), then
+// piece X + g is group g whole, or nothing if g was split.
 struct RunsArgs {
     const TabDev* desc;
     int32_t T;
@@ -386,8 +387,8 @@ struct RunsArgs {
 
 // One wave per piece (persistent, static stride), the group's P in registers;
 // four runs at a time (lane group q takes run t0 + q):
-//   dG3[i3] += P^T S          fp32 products over p, added to the fp64 dG3
-//                              accumulator with atomics
+//   dG3[i3] += P^T S          fp32 products over p, handed to add3 (device
+//                              atomics, or a row per run reduced later)
 //   dP      += S G3[i3]^T     fp64 products and sums over the piece
 // then dP goes to the group's row: a plain store, or fp32 atomics when the
 // group has several pieces (its row was zeroed first).
@@ -398,27 +399,29 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
-    const int32_t U = a.ctrl[CTRL_NUM_GROUPS];
-    const int64_t npieces = (int64_t)U + a.ctrl[CTRL_NUM_XPIECES];
+    const int32_t U = a.ctrl[CTRL_NUM_GROUPS], X = a.ctrl[CTRL_NUM_XPIECES];
+    const int64_t npieces = (int64_t)X + U;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
     for (int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; k < npieces; k += nw) {
-        int64_t g = k;
+        int64_t g = k - X;
         int32_t part = 0;
-        if (k >= U) {
-            g = a.xpiece[2 * (k - U)];
-            part = a.xpiece[2 * (k - U) + 1];
+        if (k < X) {
+            g = a.xpiece[2 * k];
+            part = a.xpiece[2 * k + 1];
         }
-        const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
-        const bool split = ge - gs > W;
-        const int32_t s = gs + W * part, e = min(ge, s + W);
-        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
-        const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
+        // P first: its address needs only g
         floatx4 preg[RT][KQ];
         const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
+        const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
+        const bool split = ge - gs > W;
+        if (split && k >= X) continue;   // done piece by piece from the list
+        const int32_t s = gs + W * part, e = min(ge, s + W);
+        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
+        const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
         doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
 // same few hundred G3 slices saturate the memory-side atomic units, and LDS
 // float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3) {
+__global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3) {
     constexpr int CN = R * N3;
     runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)run * CN + within) = c;
@@ -501,18 +504,22 @@ __global__ __launch_bounds__(256) void k_bwd_runs_c3(RunsArgs a, float* __restri
 }
 
 // dG3[i3] = sum of c3[run] over the runs with that i3, in fp64: one workgroup
-// per G3 slice i3 scans the run i3 list (16-byte loads, UNR of them in flight
-// per lane) and gathers the matching rows; the 16 waves' sums are added in LDS.
+// per G3 slice i3. Each wave scans its share of the run i3 list a span of
+// SPAN runs at a time (16-byte loads, all of the span's in flight), lists the
+// matching runs in LDS, then gathers their rows GB at a time; the 16 waves'
+// sums are added in LDS at the end.
 template <int CN>
 __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ run_i3,
                                                   const int32_t* __restrict__ ctrl,
                                                   const float* __restrict__ c3, float* __restrict__ dg3) {
-    constexpr int PL = CN / 64, UNR = 8, WAVES = 16, SPAN = 256 * UNR;
+    constexpr int PL = CN / 64, UNR = 8, WAVES = 16, SPAN = 256 * UNR, GB = 8;
     static_assert(CN % 64 == 0, "shape");
     __shared__ double red[WAVES][CN];
+    __shared__ int32_t list[WAVES][SPAN];
     const int32_t row = blockIdx.x;
     const int64_t NR = ctrl[CTRL_NUM_RUNS];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int32_t* my = list[w];
     double acc[PL];
 #pragma unroll
     for (int k = 0; k < PL; ++k) acc[k] = 0.0;
@@ -529,16 +536,37 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ ru
                 for (int c = 0; c < 4; ++c) v[u][c] = r + c < NR ? run_i3[r + c] : -1;
             }
         }
+        // list this span's matches (span offsets), in any order
+        int n = 0;
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                for (uint64_t m = __ballot(v[u][c] == row); m; m &= m - 1) {
-                    const int64_t r = base + 256 * u + 4 * __builtin_ctzll(m) + c;
-                    const float* src = c3 + r * CN + lane * PL;
+            for (int c = 0; c < 4; ++c) {
+                const bool hit = v[u][c] == row;
+                const uint64_t m = __ballot(hit);
+                if (hit) my[n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+                    256 * u + 4 * lane + c;
+                n += __builtin_popcountll(m);
+            }
+        wave_lds_sync();
+        for (int j0 = 0; j0 < n; j0 += GB) {
+            float x[GB][PL];
 #pragma unroll
-                    for (int k = 0; k < PL; ++k) acc[k] += (double)src[k];
+            for (int j = 0; j < GB; ++j) {
+                const int32_t off = my[min(j0 + j, n - 1)];
+                const float* src = c3 + (base + off) * CN + lane * PL;
+#pragma unroll
+                for (int k = 0; k < PL; ++k) x[j][k] = src[k];
+            }
+#pragma unroll
+            for (int j = 0; j < GB; ++j)
+                if (j0 + j < n) {
+#pragma unroll
+                    for (int k = 0; k < PL; ++k) acc[k] += (double)x[j][k];
                 }
+        }
+        wave_lds_sync();
     }
 #pragma unroll
     for (int k = 0; k < PL; ++k) red[w][lane * PL + k] = acc[k];
