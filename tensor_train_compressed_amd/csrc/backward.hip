@@ -579,17 +579,17 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ ru
     }
 }
 
-// One workgroup (4 waves) per ((table, i2) slice, 64-column block of the N2*R
+// One workgroup (8 waves) per ((table, i2) slice, 64-column block of the N2*R
 // columns). The slice's groups are taken 32 at a time (a slab); wave w owns
-//   dG2 tiles (r1 block w & 1) x (column tiles 2*(w >> 1), +1), K = j1 per group
-//   dG1 tiles (r1 block w & 1) x (row tiles (w >> 1) + 2m, m < 4), rows = (group, j1),
+//   dG2 tile (r1 block w & 1) x (column tile w >> 1), K = j1 per group
+//   dG1 tiles (r1 block w & 1) x (row tiles (w >> 1) + 4m, m < 2), rows = (group, j1),
 //            K = the block's 64 columns
 // so dG2 needs no reduction and dG1 only atomics across the column blocks.
 // Loads run ahead: the next slab's dP rows and G1 rows and the group keys two
 // slabs ahead are issued before the current slab's math and its dG1 atomics,
 // so a slab costs its math and barriers, not memory round trips.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
+__global__ __launch_bounds__(512) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
                                                     int32_t* ctrl, int64_t K,
                                                     const uint64_t* __restrict__ key_scan,
                                                     const int32_t* __restrict__ group_key,
@@ -601,9 +601,10 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     constexpr int SG = 32;                  // groups per slab
     constexpr int MR = SG * N1;             // slab rows (group, j1)
     constexpr int DS = 64 + 4;              // LDS row stride of the dP / G2 column block
-    constexpr int NDP = MR * 16 / 256;      // float4 of dP rows per thread
-    constexpr int NG1 = SG * N1 * R / 4 / 256;   // float4 of G1 rows per thread
-    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32 && NDP * 256 == MR * 16 && NG1 * 256 * 4 == SG * N1 * R,
+    constexpr int NT = 512;                 // threads
+    constexpr int NDP = MR * 16 / NT;       // float4 of dP rows per thread
+    constexpr int NG1 = SG * N1 * R / 4 / NT;   // float4 of G1 rows per thread
+    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32 && NDP * NT == MR * 16 && NG1 * NT * 4 == SG * N1 * R,
                   "shape");
     __shared__ float sG2[R * DS];           // G2[i2][r1][block columns]
     __shared__ float sD[MR * DS];           // dP rows (g, j1), block columns
@@ -637,7 +638,7 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     auto load_dp = [&](int32_t gs, floatx4 (&v)[NDP]) {
 #pragma unroll
         for (int k = 0; k < NDP; ++k) {
-            const int f = tid + 256 * k, row = f / 16, c4 = 4 * (f % 16);   // row = (g, j1)
+            const int f = tid + NT * k, row = f / 16, c4 = 4 * (f % 16);   // row = (g, j1)
             const int32_t g = gs + row / N1;
             const floatx4* src = reinterpret_cast<const floatx4*>(
                 dpg + (int64_t)min(g, ge - 1) * PR + (row % N1) * N2R + c0 + c4);
@@ -652,23 +653,21 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     auto load_g1 = [&](int32_t i1v, floatx4 (&u)[NG1]) {
 #pragma unroll
         for (int k = 0; k < NG1; ++k) {
-            const int f = tid + 256 * k, gi = f / (N1 * R / 4);   // float4 f of the slab's G1 rows
+            const int f = tid + NT * k, gi = f / (N1 * R / 4);   // float4 f of the slab's G1 rows
             const int32_t i1 = __shfl(i1v, gi);
             u[k] = reinterpret_cast<const floatx4*>(G1t + (int64_t)i1 * N1 * R)[f % (N1 * R / 4)];
         }
     };
 
     const float* G2s = g2 + d.o2 + (int64_t)i2 * R * N2R;
-    for (int e = tid; e < R * 64; e += 256) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
+    for (int e = tid; e < R * 64; e += NT) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
 
     const int rt = w & 1, ch = w >> 1;
     // dG1 and dG2 are sums over every lookup of the slice (hundreds of
     // thousands for the hot ones) with heavy cancellation: their products run
     // on the fp64 matrix cores (fp32 operands convert exactly), so the only
     // fp32 rounding left is that of the stored result
-    doublex4 acc2[2];
-    acc2[0] = doublex4{0.0, 0.0, 0.0, 0.0};
-    acc2[1] = doublex4{0.0, 0.0, 0.0, 0.0};
+    doublex4 acc2 = {0.0, 0.0, 0.0, 0.0};
 
     floatx4 dpv[NDP], g1v[NG1];
     int32_t i1c = 0, i1n = 0;
@@ -683,11 +682,11 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
         __syncthreads();   // the previous slab's math is done with sD / sA / sI1
 #pragma unroll
         for (int k = 0; k < NDP; ++k) {
-            const int f = tid + 256 * k;
+            const int f = tid + NT * k;
             *reinterpret_cast<floatx4*>(sD + (f / 16) * DS + 4 * (f % 16)) = dpv[k];
         }
 #pragma unroll
-        for (int k = 0; k < NG1; ++k) *reinterpret_cast<floatx4*>(sA + 4 * (tid + 256 * k)) = g1v[k];
+        for (int k = 0; k < NG1; ++k) *reinterpret_cast<floatx4*>(sA + 4 * (tid + NT * k)) = g1v[k];
         if (tid < SG) sI1[tid] = i1c;
         // the next slab's loads, then the group keys of the one after
         const int32_t i1nn = load_i1(gs + 2 * SG);
@@ -699,16 +698,13 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
         // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c]: one k-step per group
         for (int gi = 0; gi < ng; ++gi) {
             const double av = sA[gi * N1 * R + q * R + 16 * rt + col];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const double bv = sD[(gi * N1 + q) * DS + 16 * (2 * ch + j) + col];
-                acc2[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc2[j], 0, 0, 0);
-            }
+            const double bv = sD[(gi * N1 + q) * DS + 16 * ch + col];
+            acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc2, 0, 0, 0);
         }
-        // dG1 rows (g, j1) of row tiles ch + 2m, r1 block rt, K = 64 columns
+        // dG1 rows (g, j1) of row tiles ch + 4m, r1 block rt, K = 64 columns
 #pragma unroll
-        for (int m = 0; m < MR / 32; ++m) {
-            const int rtile = ch + 2 * m;
+        for (int m = 0; m < MR / 64; ++m) {
+            const int rtile = ch + 4 * m;
             if (4 * rtile < ng) {
                 doublex4 acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -731,9 +727,7 @@ __global__ __launch_bounds__(256) void k_bwd_prefix(const TabDev* __restrict__ d
     // fp64 product's lane holds rows q + 4v of the tile)
     float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R + c0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) D2[(16 * rt + q + 4 * v) * N2R + 16 * (2 * ch + j) + col] = (float)acc2[j][v];
+    for (int v = 0; v < 4; ++v) D2[(16 * rt + q + 4 * v) * N2R + 16 * ch + col] = (float)acc2[v];
 }
 
 template <int N1, int N2, int R, int N3>
@@ -795,7 +789,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         TT_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
-                       dim3(256), 0, s, p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+                       dim3(512), 0, s, p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
                        p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, acc1, dg2);
     TT_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
