@@ -112,16 +112,16 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float*
 //
 // k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
 //               with atomics; fp64 keeps a sum of many cancelling terms within
-//               the fp32 tolerance) and the fp64 sums of the runs that cross a
-//               chunk start (summed piece by piece)
-// k_bwd_sum     persistent waves over cost-balanced chunk tasks (per-XCD
-//               queues, stealing): for every run, S = sum of the grad_out rows
-//               of its lookups, accumulated in fp64. A run inside one chunk is
-//               stored once, rounded to fp32; the pieces of a run cut by chunk
-//               starts are added with fp64 atomics to its slot. Memory-bound.
-// k_bwd_cross   rounds the fp64 sums of the cut runs into their S rows
-//               (a hot row's run spans many chunks: an fp32 sum of its pieces
-//               would lose the fp32 tolerance on the slices it feeds)
+//               the fp32 tolerance) and lists the pieces of the large groups
+// k_bwd_sum     one wave per window of 64 sorted positions: for every run,
+//               S = sum of the grad_out rows of its lookups, accumulated in
+//               fp64. A run inside one window is stored once, rounded to fp32;
+//               the pieces of a run cut by window ends go to fp64 slots, one
+//               per piece. Memory-bound.
+// k_bwd_cross   adds up the pieces of the cut runs in fp64 and rounds them
+//               into their S rows (a hot row's run spans many windows: an
+//               fp32 sum of its pieces would lose the fp32 tolerance on the
+//               slices it feeds)
 // k_bwd_pfx     recomputes P of every group (persistent workgroups over the
 //               planner's prefix batches, as the forward) into a global buffer
 // k_bwd_runs    one wave per piece of up to kRunRange runs of one group, the
@@ -140,77 +140,40 @@ __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64
     return s == 0 || skey[s - 1] != skey[s];
 }
 
-// Where chunks cut row runs. Chunks of a group are `chunk` lookups apart, so
-// the chunk holding sorted position x, seen from chunk c that begins at b, is
-// c + floor((x - b) / chunk). A run cut by chunk starts is summed in the slot
-// of its first cutting chunk c_f (the chunk after the one holding its head):
-// slot = c_f - g - 1 for c_f in group g, unique and below ceil(L / chunk).
+// The grad-row sums run over fixed windows of kWin sorted positions (one
+// wave each). A row run that crosses a window end is summed piece by piece:
+// the piece of window w that starts at w's first position (when that is not a
+// run head) goes to fp64 slot 2w, the piece that starts at a head inside w and
+// runs past w's end goes to slot 2w + 1. No two pieces share a slot.
+constexpr int kWin = 64;
+
 struct CrossRef {
-    const int32_t* chunk_begin;
-    const int32_t* chunk_group;
     const int32_t* skey;
     const int32_t* rid;
     const int32_t* run_start;
-    int32_t chunk;
+    int64_t L;
 };
 
-__device__ __forceinline__ int32_t floor_div(int32_t x, int32_t n) {
-    return x >= 0 ? x / n : -((n - 1 - x) / n);
+// The run cut by the end of window w when its head lies in w, else -1.
+__device__ __forceinline__ int32_t first_cut_run(const CrossRef& x, int64_t w) {
+    const int64_t e = (w + 1) * kWin;
+    if (e >= x.L || row_head(x.skey, e)) return -1;
+    const int32_t run = x.rid[e] - 1;
+    return x.run_start[run] >= e - kWin ? run : -1;
 }
 
-// slot of run `run` (cut by chunk starts) seen from a piece in chunk c
-__device__ __forceinline__ int64_t cross_slot(const CrossRef& x, int64_t c, int32_t run) {
-    const int32_t cf = (int32_t)c + floor_div(x.run_start[run] - x.chunk_begin[c], x.chunk) + 1;
-    return (int64_t)cf - x.chunk_group[c] - 1;
-}
-
-// run cut by the start of chunk c when c is that run's first cutting chunk,
-// else -1
-__device__ __forceinline__ int32_t first_cut_run(const CrossRef& x, int64_t c) {
-    const int32_t b = x.chunk_begin[c];
-    if (row_head(x.skey, b)) return -1;
-    const int32_t run = x.rid[b] - 1;
-    return x.run_start[run] >= b - x.chunk ? run : -1;
-}
-
-// visit(run, slot, part) for every first cutting chunk and every 4-element
-// part of its row: one thread per (chunk, part), so the few hundred slots of
-// a step are converted in parallel rather than one after another.
-template <int D, class F>
-__device__ __forceinline__ void for_each_first_cut(const CrossRef& x, int32_t NC, F visit) {
-    constexpr int D4 = D / 4;
-    const int64_t n = (int64_t)NC * D4;
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += nth) {
-        const int64_t c = t / D4;
-        const int part = (int)(t - c * D4);
-        const int32_t run = first_cut_run(x, c);
-        if (run >= 0) visit(run, c - x.chunk_group[c] - 1, part);
-    }
-}
-
-template <int DL, int PR>
 __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
                                                   double* __restrict__ dg3, int64_t n3,
-                                                  double* __restrict__ xsum, CrossRef x,
-                                                  float* __restrict__ dpg,
                                                   const int32_t* __restrict__ group_rbase,
                                                   int32_t* __restrict__ xpiece, int32_t* ctrl) {
-    constexpr int D = 64 * DL, PR4 = PR / 4;
-    static_assert(PR % 4 == 0, "shape");
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
     // groups of more than kRunRange runs are split into pieces of kRunRange
-    // runs: zero their dP rows (the pieces add to them) and list their pieces
-    // (the run kernel takes these first, then one piece per other group)
+    // runs: list their pieces, a group's pieces together and in order (the
+    // run kernel takes these first, then one piece per other group)
     const int64_t U = ctrl[CTRL_NUM_GROUPS];
-    for (int64_t i = tid; i < U * PR4; i += nth) {
-        const int64_t g = i / PR4;
-        if (group_rbase[g + 1] - group_rbase[g] > kRunRange)
-            reinterpret_cast<floatx4*>(dpg + g * PR)[i % PR4] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
     for (int64_t g = tid; g < U; g += nth) {
         const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
         if (np > 1) {
@@ -221,102 +184,134 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
             }
         }
     }
-    for_each_first_cut<D>(x, ctrl[CTRL_NUM_CHUNKS], [&](int32_t, int64_t slot, int part) {
-        double* dst = xsum + slot * D + 4 * part;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = 0.0;
-    });
 }
 
+// S of the cut runs: workgroup w takes the run whose head lies in window w
+// and that runs past its end (if any), and adds its end piece and the start
+// pieces of the windows up to the one holding its last lookup, in fp64 (the
+// four waves take every fourth window, eight loads in flight each).
 template <int DL>
-__global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xsum, CrossRef x,
-                                                   float* __restrict__ S,
-                                                   const int32_t* __restrict__ ctrl) {
-    constexpr int D = 64 * DL;
-    for_each_first_cut<D>(x, ctrl[CTRL_NUM_CHUNKS], [&](int32_t run, int64_t slot, int part) {
-        const double* src = xsum + slot * D + 4 * part;
-        *reinterpret_cast<floatx4*>(S + (int64_t)run * D + 4 * part) =
-            floatx4{(float)src[0], (float)src[1], (float)src[2], (float)src[3]};
-    });
+__global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xpart, CrossRef x,
+                                                   float* __restrict__ S, const int32_t* __restrict__ ctrl) {
+    constexpr int D = 64 * DL, UNR = 8;
+    __shared__ double red[4][D];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t nwin = (x.L + kWin - 1) / kWin;
+    const int32_t NR = ctrl[CTRL_NUM_RUNS];
+    for (int64_t w = blockIdx.x; w < nwin; w += gridDim.x) {
+        const int32_t run = first_cut_run(x, w);
+        if (run < 0) continue;
+        const int64_t run_end = run + 1 < NR ? x.run_start[run + 1] : x.L;
+        const int64_t last = (run_end - 1) / kWin;
+        double acc[DL];
+#pragma unroll
+        for (int k = 0; k < DL; ++k) acc[k] = wv == 0 ? xpart[(2 * w + 1) * D + lane * DL + k] : 0.0;
+        for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += 4 * UNR) {
+            double v[UNR][DL];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int64_t j = min(j0 + 4 * u, last);
+#pragma unroll
+                for (int k = 0; k < DL; ++k) v[u][k] = xpart[2 * j * D + lane * DL + k];
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (j0 + 4 * u <= last) {
+#pragma unroll
+                    for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = acc[k];
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int k = 0; k < DL; ++k) {
+                const int e = lane * DL + k;
+                S[(int64_t)run * D + e] = (float)(red[0][e] + red[1][e] + red[2][e] + red[3][e]);
+            }
+        }
+        __syncthreads();
+    }
 }
 
 struct SumArgs {
-    int32_t* ctrl;
-    const int32_t* task_start;
-    const int32_t* chunk_begin;
-    const int32_t* chunk_end;
     const int32_t* sorted_bag;
     const int32_t* skey;
     const int32_t* rid;
+    const int32_t* run_start;
     int64_t L;
     const float* gout;
     float* S;
-    double* xsum;
-    CrossRef x;
+    double* xpart;
 };
 
+// S[run] = sum of the grad rows of the run's lookups, in fp64. One wave per
+// window of kWin sorted positions (fixed stride over the windows): the
+// window's bag ids, run ids and run heads come in one round of loads, then its
+// grad rows FL at a time, added in order; a run is stored (rounded to fp32)
+// when it starts and ends in the window, otherwise its piece goes to its
+// fp64 slot (no atomics: every slot has one writer).
 template <int DL>
 __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
     constexpr int D = 64 * DL, FL = 32;   // grad_out rows in flight
     const int lane = threadIdx.x & 63;
-    TaskQueues tq = make_queues(a.ctrl, 1);
-    for (int32_t t = next_task(tq); t >= 0; t = next_task(tq)) {
-        const int32_t cA = a.task_start[t], cB = a.task_start[t + 1];
-        for (int32_t c = cA; c < cB; ++c) {
-            const int32_t s0 = a.chunk_begin[c], s1 = a.chunk_end[c];
-            const bool tail_whole = (s1 == a.L) || row_head(a.skey, s1);
-            int32_t cur = 0;
-            bool cur_head = false;
-            double sacc[DL];
+    const int64_t nwin = (a.L + kWin - 1) / kWin;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t w = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; w < nwin; w += nw) {
+        const int64_t s0 = w * kWin;
+        const int n = (int)min((int64_t)kWin, a.L - s0);
+        const int64_t s1 = s0 + n;
+        const bool tail_whole = (s1 == a.L) || row_head(a.skey, s1);
+        const int64_t sl = s0 + lane;
+        const bool valid = lane < n;
+        const bool hr = valid && row_head(a.skey, sl);
+        const uint64_t m = __ballot(hr);
+        const int32_t bagv = a.sorted_bag[valid ? sl : s0];
+        const int32_t rrv = valid ? a.rid[sl] + (hr ? 1 : 0) - 1 : 0;
+        int32_t cur = 0;
+        bool cur_head = false;
+        double sacc[DL];
 #pragma unroll
-            for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
-            auto flush = [&](bool whole) {
-                if (whole) {
-                    float* dst = a.S + (int64_t)cur * D + lane * DL;
+        for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
+        // a piece that starts at a head and ends inside the window (or at its
+        // end, the next window starting a new run) is the whole run
+        auto flush = [&](bool ends_here) {
+            if (cur_head && ends_here) {
+                float* dst = a.S + (int64_t)cur * D + lane * DL;
 #pragma unroll
-                    for (int k = 0; k < DL; ++k) dst[k] = (float)sacc[k];
-                } else {
-                    double* dst = a.xsum + cross_slot(a.x, c, cur) * D + lane * DL;
+                for (int k = 0; k < DL; ++k) dst[k] = (float)sacc[k];
+            } else {
+                double* dst = a.xpart + (2 * w + (cur_head ? 1 : 0)) * D + lane * DL;
 #pragma unroll
-                    for (int k = 0; k < DL; ++k) atomicAdd(dst + k, sacc[k]);
-                }
-            };
-            for (int32_t sb = s0; sb < s1; sb += 64) {
-                const int n = min(64, s1 - sb);
-                const int32_t sl = sb + lane;
-                const bool valid = lane < n;
-                const bool hr = valid && row_head(a.skey, sl);
-                const uint64_t m = __ballot(hr);
-                const int32_t bagv = valid ? a.sorted_bag[sl] : a.sorted_bag[sb];
-                const int32_t rrv = valid ? a.rid[sl] + (hr ? 1 : 0) - 1 : 0;
-                for (int r0 = 0; r0 < n; r0 += FL) {
-                    float v[FL][DL];
+                for (int k = 0; k < DL; ++k) dst[k] = sacc[k];
+            }
+        };
+        for (int r0 = 0; r0 < n; r0 += FL) {
+            float v[FL][DL];
 #pragma unroll
-                    for (int u = 0; u < FL; ++u) {
-                        const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
+            for (int u = 0; u < FL; ++u) {
+                const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
 #pragma unroll
-                        for (int k = 0; k < DL; ++k) v[u][k] = row[k];
+                for (int k = 0; k < DL; ++k) v[u][k] = row[k];
+            }
+#pragma unroll
+            for (int u = 0; u < FL; ++u) {
+                const int r = r0 + u;
+                if (r < n) {
+                    if (r == 0 || ((m >> r) & 1ull)) {
+                        if (r != 0) flush(true);   // the previous piece ends at a row head
+                        cur = __builtin_amdgcn_readlane(rrv, r);
+                        cur_head = ((m >> r) & 1ull) != 0;
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
                     }
 #pragma unroll
-                    for (int u = 0; u < FL; ++u) {
-                        const int r = r0 + u;
-                        if (r < n) {
-                            const bool first = (sb + r == s0);
-                            if (first || ((m >> r) & 1ull)) {
-                                if (!first) flush(cur_head);   // the previous piece ends at a row head
-                                cur = __builtin_amdgcn_readlane(rrv, r);
-                                cur_head = ((m >> r) & 1ull) != 0;
-#pragma unroll
-                                for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
-                            }
-#pragma unroll
-                            for (int k = 0; k < DL; ++k) sacc[k] += (double)v[u][k];
-                        }
-                    }
+                    for (int k = 0; k < DL; ++k) sacc[k] += (double)v[u][k];
                 }
             }
-            flush(cur_head && tail_whole);
         }
+        flush(tail_whole);
     }
 }
 
@@ -383,6 +378,7 @@ struct RunsArgs {
     const float* g3;
     double* dg3;
     float* dpg;
+    double* dpart;
 };
 
 // One wave per piece (persistent, static stride), the group's P in registers;
@@ -390,8 +386,8 @@ struct RunsArgs {
 //   dG3[i3] += P^T S          fp32 products over p, handed to add3 (device
 //                              atomics, or a row per run reduced later)
 //   dP      += S G3[i3]^T     fp64 products and sums over the piece
-// then dP goes to the group's row: a plain store, or fp32 atomics when the
-// group has several pieces (its row was zeroed first).
+// then dP goes to the group's row (rounded to fp32), or, for a piece of a
+// split group, to the piece's own fp64 slot, which k_bwd_dpsum adds up.
 template <int N1, int N2, int R, int N3, class Add3>
 __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R, MT = NP / 16, RT = R / 16, KSP = NP / 4;
@@ -466,8 +462,10 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
                                                                             dacc[mt][nt], 0, 0, 0);
             }
         }
-        // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col]
+        // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col];
+        // a piece of a split group keeps its fp64 partial in its own slot
         float* dst = a.dpg + g * PR;
+        double* dpp = a.dpart + k * PR;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -475,7 +473,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int idx = (16 * mt + q + 4 * v) * R + 16 * nt + col;
-                    if (split) atomicAdd(dst + idx, (float)dacc[mt][nt][v]);
+                    if (split) dpp[idx] = dacc[mt][nt][v];
                     else dst[idx] = (float)dacc[mt][nt][v];
                 }
     }
@@ -501,6 +499,36 @@ __global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __res
     runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)run * CN + within) = c;
     });
+}
+
+// dP rows of the split groups: the fp64 sum of their pieces' slots, rounded
+// once. One thread per (listed piece 0, element); a group's pieces are listed
+// together and in order. Eight piece loads in flight per thread.
+template <int PR>
+__global__ __launch_bounds__(256) void k_bwd_dpsum(const int32_t* __restrict__ xpiece,
+                                                   const int32_t* __restrict__ group_rbase,
+                                                   const int32_t* __restrict__ ctrl,
+                                                   const double* __restrict__ dpart, float* __restrict__ dpg) {
+    constexpr int UNR = 8;
+    const int64_t X = ctrl[CTRL_NUM_XPIECES];
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < X * PR; t += nth) {
+        const int64_t k = t / PR;
+        const int e = (int)(t - k * PR);
+        if (xpiece[2 * k + 1] != 0) continue;
+        const int32_t g = xpiece[2 * k];
+        const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
+        double acc = 0.0;
+        for (int32_t j0 = 0; j0 < np; j0 += UNR) {
+            double v[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) v[u] = dpart[(k + min(j0 + u, np - 1)) * PR + e];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (j0 + u < np) acc += v[u];
+        }
+        dpg[(int64_t)g * PR + e] = (float)acc;
+    }
 }
 
 // dG3[i3] = sum of c3[run] over the runs with that i3, in fp64: one workgroup
@@ -745,26 +773,21 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     constexpr int DL = N1 * N2 * N3 / 64;
     double* acc1 = p->at<double>(p->lay.acc1);
     double* acc3 = p->at<double>(p->lay.acc3);
-    double* xsum = p->at<double>(p->lay.xsum);
-    const CrossRef xr{p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_group),
-                      p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
-                      p->at<int32_t>(p->lay.run_start), p->chunk};
+    double* xpart = p->at<double>(p->lay.xsum);
+    const CrossRef xr{p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
+                      p->at<int32_t>(p->lay.run_start), p->L};
     constexpr int PR = N1 * N2 * R;
-    hipLaunchKernelGGL((k_bwd_prep<DL, PR>),
-                       dim3(std::max(512u, std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u))),
-                       dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2], xsum, xr,
-                       p->at<float>(p->lay.dpg), p->at<int32_t>(p->lay.group_rbase),
-                       p->at<int32_t>(p->lay.xpiece), p->ctrl());
+    const int64_t nwin = (p->L + kWin - 1) / kWin;
+    hipLaunchKernelGGL(k_bwd_prep, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
+                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
-        SumArgs sa{p->ctrl(), p->at<int32_t>(p->lay.task_start), p->at<int32_t>(p->lay.chunk_begin),
-                   p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_bag),
-                   p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid), p->L, gout,
-                   p->at<float>(p->lay.stage), xsum, xr};
+        SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
+                   p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
-        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3(std::min<unsigned>(grid_for(p->lay.Cmax * (DL * 16), 256), 4096u)),
-                           dim3(256), 0, s, xsum, xr, p->at<float>(p->lay.stage), p->ctrl());
+        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>(nwin, 1), 8192)),
+                           dim3(256), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
@@ -775,7 +798,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece),
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
-                    acc3, p->at<float>(p->lay.dpg)};
+                    acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart)};
         if (scan3) {
             hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
                                p->at<float>(p->lay.c3));
@@ -786,6 +809,10 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         } else {
             hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
+        TT_LAUNCH_CHECK();
+        hipLaunchKernelGGL((k_bwd_dpsum<PR>), dim3(2048), dim3(256), 0, s, p->at<int32_t>(p->lay.xpiece),
+                           p->at<int32_t>(p->lay.group_rbase), p->ctrl(), p->at<double>(p->lay.dpart),
+                           p->at<float>(p->lay.dpg));
         TT_LAUNCH_CHECK();
     }
     hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),

@@ -63,7 +63,11 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_i3 = take(l4);
     y.run_of = take(l4);
     y.run_start = take(l4);
-    y.xpiece = take(sizeof(int32_t) * 2 * (size_t)(L / kRunRange + 1));
+    // pieces of the groups with more than kRunRange row runs: a group of n > W
+    // runs has ceil(n / W) < 2n / W of them, so fewer than 2L / W in all
+    const size_t xcap = 2 * (size_t)(L / kRunRange) + 1;
+    y.xpiece = take(sizeof(int32_t) * 2 * xcap);
+    y.dpart = take(sizeof(double) * xcap * (size_t)PR);
     // one row per row run, plus kStageSpare rows that take the writes of
     // inactive lanes (kept branch-free) in the forward
     y.stage = take(sizeof(float) * ((size_t)L + kStageSpare) * (size_t)D);
@@ -94,10 +98,9 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.acc3 = take(sizeof(double) * (size_t)E3);
     // per run, P^T S (the run's dG3 term), for the single-table reduction of dG3
     y.c3 = take(T == 1 ? sizeof(float) * (size_t)L * (size_t)CN : 0);
-    // a row run cut by chunk starts has a first cutting chunk, which is never
-    // the first chunk of its group; chunk c of group g that is not the first
-    // one of g has slot c - g - 1 < ceil(L / chunk)
-    y.xsum = take(sizeof(double) * (size_t)((L + chunk - 1) / chunk) * (size_t)D);
+    // fp64 pieces of the row runs cut by the backward's 64-position windows:
+    // two slots per window (its start piece and its end piece)
+    y.xsum = take(sizeof(double) * 2 * (size_t)((L + 63) / 64) * (size_t)D);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;

@@ -121,7 +121,8 @@ struct Layout {
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
     size_t run_start;                        // [L] int32: first sorted position of each row run
-    size_t xpiece;                           // [L/kRunRange + 1] int32 pairs: (group, piece) (backward)
+    size_t xpiece;                           // [2*(L/kRunRange) + 1] int32 pairs: (group, piece) (backward)
+    size_t dpart;                            // [2*(L/kRunRange) + 1][n1*n2*R] double: dP of each listed piece
     size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
     size_t stage;                            // [L + kStageSpare][D] float, one row per row run: forward, the
                                              //     run's embedding row; backward, its grad-row sum
@@ -139,8 +140,8 @@ struct Layout {
     size_t c3;                               // [L][R*n3] float, one table only: P^T S per run
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
-    size_t xsum;                             // [ceil(L/chunk)][D] double: S of the row runs
-                                             //     cut by chunk starts, summed piece by piece
+    size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
+                                             //     cut by the backward's windows
     size_t batch;                            // [NFB] BatchRec
     size_t total;
     int64_t n_tiles, K, Gmax, Cmax, Tmax, NFB, scan_tiles;
