@@ -189,12 +189,13 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
 // S of the cut runs: workgroup w takes the run whose head lies in window w
 // and that runs past its end (if any), and adds its end piece and the start
 // pieces of the windows up to the one holding its last lookup, in fp64 (the
-// four waves take every fourth window, eight loads in flight each).
+// WV waves take every WV-th window, UNR loads in flight each; a hot row's run
+// spans hundreds of windows).
 template <int DL>
-__global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xpart, CrossRef x,
-                                                   float* __restrict__ S, const int32_t* __restrict__ ctrl) {
-    constexpr int D = 64 * DL, UNR = 8;
-    __shared__ double red[4][D];
+__global__ __launch_bounds__(1024) void k_bwd_cross(const double* __restrict__ xpart, CrossRef x,
+                                                    float* __restrict__ S, const int32_t* __restrict__ ctrl) {
+    constexpr int D = 64 * DL, UNR = 8, WV = 16;
+    __shared__ double red[WV][D];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t nwin = (x.L + kWin - 1) / kWin;
     const int32_t NR = ctrl[CTRL_NUM_RUNS];
@@ -206,17 +207,17 @@ __global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xp
         double acc[DL];
 #pragma unroll
         for (int k = 0; k < DL; ++k) acc[k] = wv == 0 ? xpart[(2 * w + 1) * D + lane * DL + k] : 0.0;
-        for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += 4 * UNR) {
+        for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += WV * UNR) {
             double v[UNR][DL];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int64_t j = min(j0 + 4 * u, last);
+                const int64_t j = min(j0 + WV * u, last);
 #pragma unroll
                 for (int k = 0; k < DL; ++k) v[u][k] = xpart[2 * j * D + lane * DL + k];
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u)
-                if (j0 + 4 * u <= last) {
+                if (j0 + WV * u <= last) {
 #pragma unroll
                     for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
                 }
@@ -224,12 +225,11 @@ __global__ __launch_bounds__(256) void k_bwd_cross(const double* __restrict__ xp
 #pragma unroll
         for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = acc[k];
         __syncthreads();
-        if (wv == 0) {
+        for (int e = threadIdx.x; e < D; e += 64 * WV) {
+            double t = 0.0;
 #pragma unroll
-            for (int k = 0; k < DL; ++k) {
-                const int e = lane * DL + k;
-                S[(int64_t)run * D + e] = (float)(red[0][e] + red[1][e] + red[2][e] + red[3][e]);
-            }
+            for (int k = 0; k < WV; ++k) t += red[k][e];
+            S[(int64_t)run * D + e] = (float)t;
         }
         __syncthreads();
     }
@@ -786,8 +786,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                    p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
-        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>(nwin, 1), 8192)),
-                           dim3(256), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
+        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>(nwin, 1), 2048)),
+                           dim3(1024), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
