@@ -125,6 +125,18 @@ tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indi
 tt_status tt_emb_forward(tt_emb_plan_t plan, const float* g1, const float* g2,
                          const float* g3, float* out, void* stream);
 
+/* Forward for training: the same result as tt_emb_forward, and the plan
+ * also keeps each prefix group's shared partial product P = G1[i1] x G2[i2]
+ * in its workspace, so that the next tt_emb_backward on this plan reuses it
+ * instead of forming it again (the FlowTT pages' inter-block sharing of
+ * reusable intermediates through checkpoint buffers: summary card, key
+ * innovations; abstract). The kept products are used by tt_emb_backward only
+ * when it is given the same g1 and g2 pointers; the caller must not change
+ * the contents of G1 or G2 between the two calls (tt_emb_sgd on this plan
+ * discards them). Shapes without the matrix-core path keep nothing. */
+tt_status tt_emb_forward_train(tt_emb_plan_t plan, const float* g1, const float* g2,
+                               const float* g3, float* out, void* stream);
+
 /* Backward: dg1/dg2/dg3 (device, same packing and sizes as the cores) are
  * fully overwritten with the gradients of <grad_out, out>; slices that no
  * lookup touches are zero. grad_out is device float[T*B][D]. */

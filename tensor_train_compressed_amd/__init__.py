@@ -19,7 +19,7 @@ from typing import Optional, Sequence
 __all__ = [
     "TTEmbError", "TTEmbLibraryMissing", "TT_OK", "TT_FLAG_BAD_INDEX", "TT_FLAG_BAD_OFFSETS",
     "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
-    "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd", "tt_emb_get_error",
+    "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_sgd", "tt_emb_get_error",
     "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy", "Plan", "EXPORTS",
 ]
 
@@ -30,7 +30,8 @@ TT_FLAG_BAD_OFFSETS = 2
 
 # Every symbol include/tt_emb.h declares.
 EXPORTS = (
-    "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd",
+    "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train",
+    "tt_emb_backward", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
     "tt_emb_status_string",
 )
@@ -84,6 +85,7 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_plan.argtypes = [P, i32, P, P, i64, i64, i32, P, ctypes.c_size_t, P,
                                     ctypes.POINTER(P)]
         lib.tt_emb_forward.argtypes = [P, P, P, P, P, P]
+        lib.tt_emb_forward_train.argtypes = [P, P, P, P, P, P]
         lib.tt_emb_backward.argtypes = [P, P, P, P, P, P, P, P, P]
         lib.tt_emb_sgd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P]
         lib.tt_emb_get_error.argtypes = [P, ctypes.POINTER(i32), P]
@@ -92,7 +94,7 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_plan_destroy.argtypes = [P]
         lib.tt_emb_status_string.argtypes = [ctypes.c_int]
         lib.tt_emb_status_string.restype = ctypes.c_char_p
-        for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_backward", "tt_emb_sgd",
+        for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_sgd",
                      "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts",
                      "tt_emb_plan_destroy"):
             getattr(lib, name).restype = ctypes.c_int
@@ -197,6 +199,14 @@ def tt_emb_forward(plan: Plan, g1, g2, g3, out, stream=None):
         plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
         _dev_ptr(g3, "float32", "g3"), _dev_ptr(out, "float32", "out"), _stream(stream)),
         "tt_emb_forward")
+
+
+def tt_emb_forward_train(plan: Plan, g1, g2, g3, out, stream=None):
+    """Forward that also keeps the prefix products for the next backward on the plan."""
+    _check(load_library().tt_emb_forward_train(
+        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
+        _dev_ptr(g3, "float32", "g3"), _dev_ptr(out, "float32", "out"), _stream(stream)),
+        "tt_emb_forward_train")
 
 
 def tt_emb_backward(plan: Plan, g1, g2, g3, grad_out, dg1, dg2, dg3, stream=None):

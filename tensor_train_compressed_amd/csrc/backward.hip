@@ -318,21 +318,19 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
 // P of every group, for the run kernel. Persistent workgroups walk the
 // planner's prefix batches like the forward (the next batch's loads are in
 // flight while the current one is formed) and store each group's P in the
-// lane order the run kernel reads it: float4 number x = ((rt*KQ + h)*4 + q)*16
-// + col of a group holds P[4*(4h + u) + q][16*rt + col], u = 0..3, so that a
-// lane (col, q) loads its whole matrix-core operand as RT*KQ float4.
+// lane order the run kernel reads it (store_prefix_lanes). Skipped when the
+// forward kept P on this plan for the same G1 and G2.
 template <int N1, int N2, int R>
 __global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t nb,
                                                  const int32_t* __restrict__ run_i3,
                                                  const float* __restrict__ g1, const float* __restrict__ g2,
                                                  float* __restrict__ pbuf) {
     using B = PrefixBatch<N1, N2, R>;
-    constexpr int NP = B::NP, AS = B::AS, SG = B::SG, KQ = NP / 16, PF4 = NP * R / 4;
-    static_assert(NP % 16 == 0 && R % 16 == 0 && 64 * B::WAVES == 512, "shape");
+    constexpr int SG = B::SG;
+    static_assert(64 * B::WAVES == 512, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];
-    const int tid = threadIdx.x;
     const int64_t G = gridDim.x;
     int64_t b = blockIdx.x;
     int32_t rwA = rec_word(recs, b, nb);
@@ -346,14 +344,7 @@ __global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ re
         if (live) batch_prefix<N1, N2, R>(rwA, run_i3, f, sU, sRb, sI3, c);
         batch_fetch<N1, N2, R>(rwB, run_i3, g1, g2, f);
         if (live) {
-            const float* sP = sU;
-            for (int e4 = tid; e4 < c.ng * PF4; e4 += 512) {
-                const int gi = e4 / PF4, x = e4 % PF4;
-                const int col = x & 15, q = (x >> 4) & 3, h = (x >> 6) % KQ, rt = (x >> 6) / KQ;
-                const float* src = sP + (gi * NP + 16 * h + q) * AS + 16 * rt + col;
-                const floatx4 v = {src[0], src[4 * AS], src[8 * AS], src[12 * AS]};
-                *reinterpret_cast<floatx4*>(pbuf + ((int64_t)(c.g0 + gi) * PF4 + x) * 4) = v;
-            }
+            store_prefix_lanes<N1, N2, R, 512>(sU, c.g0, c.ng, pbuf);
             __syncthreads();
         }
         rwA = rwB;
@@ -782,6 +773,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                        p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
+        const bool kept = p->p_kept && p->kept_g1 == g1 && p->kept_g2 == g2;
         SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                    p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
@@ -789,12 +781,14 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>(nwin, 1), 2048)),
                            dim3(1024), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
-        const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
-        const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
-        hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(512), lds, s,
-                           p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
-                           p->at<float>(p->lay.pbuf));
-        TT_LAUNCH_CHECK();
+        if (!kept) {
+            const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
+            const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
+            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(512), lds, s,
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
+                               p->at<float>(p->lay.pbuf));
+            TT_LAUNCH_CHECK();
+        }
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece),
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
@@ -872,6 +866,7 @@ extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3
                                 void* stream) {
     if (!p || !g1 || !g2 || !g3 || !dg1 || !dg2 || !dg3) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
+    p->p_kept = false;   // the cores change: a kept P no longer matches them
     float* gs[3] = {g1, g2, g3};
     const float* ds[3] = {dg1, dg2, dg3};
     for (int k = 0; k < 3; ++k) {

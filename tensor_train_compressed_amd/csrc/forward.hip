@@ -79,6 +79,7 @@ struct FwdArgs {
     const float* g3;
     float* stage;
     int64_t L;             // first spare stage row
+    float* pbuf;           // when set, each group's P is also kept here (for the backward)
 };
 
 // The runs of one batch: tiles of LK = 4 runs of one group. The suffix
@@ -174,8 +175,8 @@ __device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, c
 // and the records of the next two batches are already in registers, so a
 // batch's prologue costs no exposed memory round trip; slots without a group
 // cost a record read.
-template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a, int64_t nb) {
+template <int N1, int N2, int R, int N3, bool KEEP>
+__global__ __launch_bounds__(512, 4) void k_fwd_batch(FwdArgs a, int64_t nb) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int SG = B::SG, LK = 16 / N3;
     static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 512, "shape");
@@ -200,6 +201,7 @@ __global__ __launch_bounds__(512) void k_fwd_batch(FwdArgs a, int64_t nb) {
         }
         batch_fetch<N1, N2, R>(rwB, a.run_i3, a.g1, a.g2, f);
         if (live) {
+            if (KEEP) store_prefix_lanes<N1, N2, R, 512>(sU, c.g0, c.ng, a.pbuf);
             __syncthreads();
             fwd_tiles<N1, N2, R, N3>(a, c, sU, sRb, sTp, sI3);
             __syncthreads();
@@ -257,14 +259,18 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 
 template <int N1, int N2, int R, int N3>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
-                                 const float* g3, float* out, hipStream_t s) {
+                                 const float* g3, float* out, bool keep, hipStream_t s) {
     FwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
-              p->at<float>(p->lay.stage), p->L};
+              p->at<float>(p->lay.stage), p->L, keep ? p->at<float>(p->lay.pbuf) : nullptr};
     if (p->L > 0 && p->n_fb > 0) {
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
-        hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3>), dim3((unsigned)grid),
-                           dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
+        if (keep)
+            hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
+                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
+        else
+            hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3, false>), dim3((unsigned)grid),
+                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
         TT_LAUNCH_CHECK();
     }
     if (p->TB > 0) {
@@ -278,15 +284,15 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 
 // Returns true (and launches) when the plan's shape has a matrix-core kernel.
 static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
-                         float* out, hipStream_t s, tt_status* st) {
+                         float* out, bool keep, hipStream_t s, tt_status* st) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
-    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, s); return true; }
-    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, s); return true; }
-    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 16) { *st = launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, s); return true; }
+    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, keep, s); return true; }
+    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, keep, s); return true; }
+    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 16) { *st = launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, false, s); return true; }
     return false;
 }
 
@@ -294,12 +300,20 @@ static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
 
 using namespace tt;
 
-extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const float* g2,
-                                    const float* g3, float* out, void* stream) {
+static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3, float* out,
+                              bool keep, void* stream) {
     if (!p || !g1 || !g2 || !g3 || (!out && p->TB > 0)) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     tt_status st = TT_OK;
-    if (try_fwd_mfma(p, g1, g2, g3, out, s, &st)) return st;
+    if (try_fwd_mfma(p, g1, g2, g3, out, keep, s, &st)) {
+        // the backward's shapes (R = 32) are the ones whose prefix lanes are kept
+        if (keep && st == TT_OK && p->R == 32 && p->L > 0) {
+            p->p_kept = true;
+            p->kept_g1 = g1;
+            p->kept_g2 = g2;
+        }
+        return st;
+    }
     st = fill32(out, 0u, p->TB * p->D, s);
     if (st != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
@@ -313,4 +327,14 @@ extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const floa
                        p->at<int32_t>(p->lay.sorted_bag), g1, g2, g3, out, p->D);
     TT_LAUNCH_CHECK();
     return TT_OK;
+}
+
+extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const float* g2,
+                                    const float* g3, float* out, void* stream) {
+    return forward_impl(p, g1, g2, g3, out, false, stream);
+}
+
+extern "C" tt_status tt_emb_forward_train(tt_emb_plan_t p, const float* g1, const float* g2,
+                                          const float* g3, float* out, void* stream) {
+    return forward_impl(p, g1, g2, g3, out, true, stream);
 }

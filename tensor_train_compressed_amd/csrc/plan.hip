@@ -719,6 +719,9 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
     for (int k = 0; k < 3; ++k) p->extent[k] = 0;
     p->packed = true;
+    p->p_kept = false;
+    p->kept_g1 = nullptr;
+    p->kept_g2 = nullptr;
     p->off4 = true;
     for (int32_t t = 0; t < T; ++t) {
         if (tables[t].g_offset[0] % 4 != 0 || tables[t].g_offset[1] % 4 != 0) p->off4 = false;

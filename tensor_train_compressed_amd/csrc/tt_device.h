@@ -321,6 +321,25 @@ __device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs, i
     return true;
 }
 
+// Stores the batch's P (in LDS, row gi*NP + p at stride AS) to pbuf in the
+// lane order of the backward run kernel's matrix-core operand: float4 number
+// x = ((rt*KQ + h)*4 + q)*16 + col of a group holds P[4*(4h + u) + q][16*rt +
+// col], u = 0..3 (KQ = n1*n2/16), so that lane (col, q) reads its whole
+// operand as RT*KQ float4. All NT threads of the workgroup call it.
+template <int N1, int N2, int R, int NT>
+__device__ __forceinline__ void store_prefix_lanes(const float* sP, int32_t g0, int ng, float* __restrict__ pbuf) {
+    using B = PrefixBatch<N1, N2, R>;
+    constexpr int NP = B::NP, AS = B::AS, KQ = NP / 16, PF4 = NP * R / 4;
+    static_assert(NP % 16 == 0 && R % 16 == 0, "shape");
+    for (int e4 = threadIdx.x; e4 < ng * PF4; e4 += NT) {
+        const int gi = e4 / PF4, x = e4 % PF4;
+        const int col = x & 15, q = (x >> 4) & 3, h = (x >> 6) % KQ, rt = (x >> 6) / KQ;
+        const float* src = sP + (gi * NP + 16 * h + q) * AS + 16 * rt + col;
+        const floatx4 v = {src[0], src[4 * AS], src[8 * AS], src[12 * AS]};
+        *reinterpret_cast<floatx4*>(pbuf + ((int64_t)(g0 + gi) * PF4 + x) * 4) = v;
+    }
+}
+
 // Tile prefix over the batch's groups: sTp[g+1] - sTp[g] = ceil(runs(g) / per).
 __device__ __forceinline__ void batch_tiles(const int32_t* sRb, int32_t* sTp, int ng, int per) {
     if (threadIdx.x == 0) {

@@ -240,6 +240,33 @@ def test_backward_small_all():
         _check_backward(p, f"train11m B=256", chunk=chunk)
 
 
+def test_forward_train_keeps_prefix():
+    """tt_emb_forward_train gives the forward's output bit for bit and keeps
+    P for the next backward, which must match the oracle; tt_emb_sgd then
+    discards the kept P, so a backward on the updated cores (same pointers)
+    matches the oracle on those cores."""
+    import tensor_train_compressed_amd as tte
+    p = wl.make("train11m", batch=1024)
+    dp = DevProblem(p, 256)
+    want_out = dp.forward().cpu().numpy()
+    out = torch.empty_like(torch.from_numpy(want_out)).to("cuda:0")
+    tte.tt_emb_forward_train(dp.plan, dp.g1, dp.g2, dp.g3, out)
+    np.testing.assert_array_equal(out.cpu().numpy(), want_out, err_msg="forward_train output")
+    d = [x.cpu().numpy() for x in dp.backward()]
+    ref = oracle.backward_problem(p)
+    for k in range(3):
+        assert_close(d[k], ref[k], f"backward after forward_train dG{k + 1}")
+    # an SGD step on the plan's cores, in place, then the backward again
+    dg = dp.backward()
+    tte.tt_emb_sgd(dp.plan, dp.g1, dp.g2, dp.g3, dg[0], dg[1], dg[2], p.lr)
+    p2 = wl.Problem(p.name, p.tables, p.batch, dp.g1.cpu().numpy(), dp.g2.cpu().numpy(),
+                    dp.g3.cpu().numpy(), p.goff, p.indices, p.offsets, p.grad_out, p.lr)
+    d2 = [x.cpu().numpy() for x in dp.backward()]
+    ref2 = oracle.backward_problem(p2)
+    for k in range(3):
+        assert_close(d2[k], ref2[k], f"backward after SGD dG{k + 1}")
+
+
 def test_backward_multitable_small():
     p = wl.make("multi26", batch=32, tables=6)
     p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
