@@ -97,11 +97,36 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const double* __restrict__ a
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = (float)a3[i];
 }
 
-__global__ __launch_bounds__(256) void k_sgd(float* __restrict__ g, const float* __restrict__ dg,
-                                             float lr, int64_t n) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// G_k <- G_k - lr * dG_k for the three cores in one launch (16-byte accesses
+// where both buffers allow them).
+struct SgdArgs {
+    float* g[3];
+    const float* dg[3];
+    int64_t n[3];
+};
+
+__global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (; i < n; i += stride) g[i] = fmaf(-lr, dg[i], g[i]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        float* g = a.g[k];
+        const float* dg = a.dg[k];
+        const int64_t n = a.n[k];
+        int64_t done = 0;
+        if ((((uintptr_t)g | (uintptr_t)dg) & 15) == 0) {
+            const int64_t n4 = n / 4;
+            floatx4* g4 = reinterpret_cast<floatx4*>(g);
+            const floatx4* d4 = reinterpret_cast<const floatx4*>(dg);
+            for (int64_t i = t0; i < n4; i += stride) {
+                const floatx4 x = g4[i], d = d4[i];
+                g4[i] = floatx4{fmaf(-lr, d[0], x[0]), fmaf(-lr, d[1], x[1]), fmaf(-lr, d[2], x[2]),
+                                fmaf(-lr, d[3], x[3])};
+            }
+            done = 4 * n4;
+        }
+        for (int64_t i = done + t0; i < n; i += stride) g[i] = fmaf(-lr, dg[i], g[i]);
+    }
 }
 
 
@@ -631,7 +656,6 @@ __global__ __launch_bounds__(512) void k_bwd_prefix(const TabDev* __restrict__ d
     __shared__ int32_t sI1[SG];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    reset_queues(ctrl, 1);
     const int32_t bi = blockIdx.x / QN, qn = blockIdx.x % QN;
     int t = 0;
     {
@@ -867,14 +891,10 @@ extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3
     if (!p || !g1 || !g2 || !g3 || !dg1 || !dg2 || !dg3) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     p->p_kept = false;   // the cores change: a kept P no longer matches them
-    float* gs[3] = {g1, g2, g3};
-    const float* ds[3] = {dg1, dg2, dg3};
-    for (int k = 0; k < 3; ++k) {
-        const int64_t n = p->extent[k];
-        if (n <= 0) continue;
-        hipLaunchKernelGGL(k_sgd, dim3(std::min<unsigned>(grid_for(n, 256), 8192u)), dim3(256), 0,
-                           s, gs[k], ds[k], lr, n);
-        TT_LAUNCH_CHECK();
-    }
+    const SgdArgs a{{g1, g2, g3}, {dg1, dg2, dg3}, {p->extent[0], p->extent[1], p->extent[2]}};
+    const int64_t nmax = std::max(p->extent[0], std::max(p->extent[1], p->extent[2]));
+    if (nmax <= 0) return TT_OK;
+    hipLaunchKernelGGL(k_sgd, dim3(std::min<unsigned>(grid_for(nmax / 4 + 1, 256), 2048u)), dim3(256), 0, s, a, lr);
+    TT_LAUNCH_CHECK();
     return TT_OK;
 }

@@ -3,9 +3,9 @@
 //
 // The pages' task-formation step groups lookups that share high-order TT core
 // indices so that the shared part of the contraction chain is done once per
-// group, and cuts skewed groups into chunks that persistent threads take and
-// steal ("FlowTT: Exploiting Computation Flow Reuse in Irregular Tensor-Train
-// Embedding": summary card, key innovations; abstract). The pages fix which
+// group, and cuts skewed groups into chunks for load balance ("FlowTT:
+// Exploiting Computation Flow Reuse in Irregular Tensor-Train Embedding":
+// summary card, key innovations; abstract). The pages fix which
 // lookups share a group; the order and chunk shape used here are this
 // library's (see include/tt_emb.h): groups are ordered by key
 // base_t + i2*m1 + i1, so that groups that read the same G2 slice are
@@ -22,7 +22,7 @@
 //   k_key_flags       per key: present flag and chunk count
 //   scan              group id and first chunk of every present key
 //   k_groups          group tables, counts into the control words
-//   k_chunks          chunk table and cost-balanced task table (one thread per chunk)
+//   k_chunks          chunk table (one thread per chunk)
 //   scan, k_runs      row-run ids (a row run = one (key, i3) row), run tables
 //   k_batches         one record per forward batch (kFwdBatch groups of one slice)
 #include "tt_internal.h"
@@ -89,8 +89,6 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
-    y.Tmax = (L + (int64_t)kChunkCost * y.Cmax) / kTaskCost + 2;
-    y.task_start = take(sizeof(int32_t) * (size_t)(y.Tmax + 1));
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.pbuf = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
@@ -516,16 +514,14 @@ __device__ __forceinline__ int32_t group_of_chunk(const int32_t* __restrict__ gr
     return lo;
 }
 
-// Chunk table and the task table: chunk c starts
-// at modelled cost begin(c) + kChunkCost*c; task t holds the chunks whose
-// start lies in [t*kTaskCost, (t+1)*kTaskCost) (some tasks may be empty).
+// Chunk table: chunk c of group g starts `chunk` lookups after the previous
+// one of g (the group's first chunk at the group's start).
 __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
                                                 const int32_t* __restrict__ group_cbase,
                                                 int64_t Cmax, int32_t chunk, int32_t* ctrl,
                                                 int32_t* __restrict__ chunk_group,
                                                 int32_t* __restrict__ chunk_begin,
-                                                int32_t* __restrict__ chunk_end,
-                                                int32_t* __restrict__ task_start) {
+                                                int32_t* __restrict__ chunk_end) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
@@ -535,18 +531,6 @@ __global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ grou
     chunk_group[c] = g;
     chunk_begin[c] = b;
     chunk_end[c] = min(b + chunk, group_start[g + 1]);
-    const int64_t tc = ((int64_t)b + (int64_t)kChunkCost * c) / kTaskCost;
-    int64_t tp = -1;
-    if (c > 0) {
-        const int32_t gp = group_of_chunk(group_cbase, U, c - 1);
-        const int32_t bp = group_start[gp] + (int32_t)(c - 1 - group_cbase[gp]) * chunk;
-        tp = ((int64_t)bp + (int64_t)kChunkCost * (c - 1)) / kTaskCost;
-    }
-    for (int64_t t = tp + 1; t <= tc; ++t) task_start[t] = (int32_t)c;
-    if (c == NC - 1) {
-        task_start[tc + 1] = NC;
-        ctrl[CTRL_NUM_TASKS] = (int32_t)(tc + 1);
-    }
 }
 
 // Row-run tables from the scanned head flags. A row run is a maximal stretch
@@ -834,8 +818,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_chunks, dim3(grid_for(lay.Cmax, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
                                lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
-                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<int32_t>(lay.task_start));
+                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
             // row-run ids: exclusive scan of the head flags, then the run tables
             if (scan_exclusive<uint32_t>(p, ++nscan, p->at<uint32_t>(lay.rid), L, nullptr, s) != TT_OK)

@@ -66,73 +66,6 @@ __device__ __forceinline__ void build_prefix(const float* __restrict__ A, const 
     wave_lds_sync();
 }
 
-// Persistent scheduling. Block b runs on XCD b % 8 (workgroups are handed to
-// the XCDs round-robin), and its waves first take tasks from that XCD's queue:
-// the queues are contiguous eighths of the key-ordered task list, so a run of
-// i2 values (and their G2 slices) stays in one XCD's L2. A wave whose queue is
-// empty steals from the next queues in turn. One returning atomic per task,
-// issued by lane 0; counters only grow, so a plain read tells an empty queue
-// without an atomic. Every wave ends after at most 8 empty probes.
-struct TaskQueues {
-    int32_t* ctr;    // 8 counters, CTRL_QSTRIDE words apart
-    int32_t nt;      // number of tasks
-    int home;
-    int probe;
-};
-
-__device__ __forceinline__ TaskQueues make_queues(int32_t* ctrl, int kind) {
-    TaskQueues q;
-    q.ctr = ctrl + CTRL_QUEUE + kind * kXcds * CTRL_QSTRIDE;
-    q.nt = ctrl[CTRL_NUM_TASKS];
-    q.home = (int)(blockIdx.x % kXcds);
-    q.probe = 0;
-    return q;
-}
-
-__device__ __forceinline__ int32_t next_task(TaskQueues& q) {
-    while (q.probe < kXcds) {
-        const int x = (q.home + q.probe) % kXcds;
-        const int32_t lo = (int32_t)(((int64_t)x * q.nt) / kXcds);
-        const int32_t hi = (int32_t)(((int64_t)(x + 1) * q.nt) / kXcds);
-        int32_t* ctr = q.ctr + x * CTRL_QSTRIDE;
-        const int32_t seen = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (lo + seen < hi) {
-            int32_t t = 0;
-            if ((threadIdx.x & 63) == 0) t = lo + atomicAdd(ctr, 1);
-            t = __builtin_amdgcn_readfirstlane(t);
-            if (t < hi) return t;
-        }
-        ++q.probe;
-    }
-    return -1;
-}
-
-// Zeroes the 8 queue counters of `kind` (run by a later kernel in the stream).
-__device__ __forceinline__ void reset_queues(int32_t* ctrl, int kind) {
-    if (blockIdx.x == 0 && threadIdx.x < kXcds)
-        ctrl[CTRL_QUEUE + (kind * kXcds + threadIdx.x) * CTRL_QSTRIDE] = 0;
-}
-
-// Non-persistent chunk mapping: consecutive spans of kSpan chunks go to one XCD,
-// spans rotate over the 8 XCDs (block b runs on XCD b % 8). Groups that share
-// an i2 are adjacent in chunk order, so a G2 slice is read by few XCDs, while
-// a huge group's chunks still spread over all of them. -1 past the end.
-constexpr int kSpan = 64;
-__device__ __forceinline__ int32_t span_chunk(int32_t nchunks, int w) {
-    const int32_t x = (int32_t)(blockIdx.x % kXcds), j = (int32_t)(blockIdx.x / kXcds);
-    const int32_t idx = 4 * j + w;                  // this XCD's idx-th chunk
-    const int32_t c = ((idx / kSpan) * kXcds + x) * kSpan + idx % kSpan;
-    return c < nchunks ? c : -1;
-}
-inline unsigned span_grid(int64_t max_chunks) {
-    // enough blocks that every XCD covers every span it could own
-    const int64_t spans = (max_chunks + kSpan - 1) / kSpan;
-    const int64_t per_xcd = (spans + kXcds - 1) / kXcds * kSpan;   // chunks per XCD
-    const int64_t blocks = kXcds * ((per_xcd + 3) / 4);
-    return (unsigned)(blocks > 0 ? blocks : kXcds);
-}
-
 // Persistent grid: blocks per CU times the CU count.
 inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blocks_per_cu); }
 

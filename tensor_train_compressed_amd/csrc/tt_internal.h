@@ -30,23 +30,14 @@ enum CtrlSlot : int {
     CTRL_FLAG = 0,        // TT_FLAG_* bits
     CTRL_NUM_GROUPS = 1,
     CTRL_NUM_CHUNKS = 2,
-    CTRL_NUM_TASKS = 3,
     CTRL_NUM_RUNS = 4,    // row runs
     CTRL_NUM_XPIECES = 5, // backward: extra run pieces of the groups split over several waves
     CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
     CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
     CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
-    CTRL_QUEUE = 64,      // task-queue counters, one per 256-byte line:
-                          // forward queues 0..7, backward queues 8..15
-    CTRL_QSTRIDE = 64,
-    CTRL_WORDS = CTRL_QUEUE + 16 * CTRL_QSTRIDE
+    CTRL_WORDS = 64
 };
 
-// Work units of the persistent kernels. A task is a run of consecutive chunks
-// whose modelled cost (lookups + kChunkCost per chunk, the prefix build) is
-// about kTaskCost; the task list is cut into 8 contiguous queues, one per XCD.
-constexpr int kTaskCost = 512;
-constexpr int kChunkCost = 32;
 constexpr int kXcds = 8;
 // Forward work unit: up to this many prefix groups of one (table, i2) slice.
 constexpr int kFwdBatch = 8;
@@ -133,7 +124,6 @@ struct Layout {
     size_t key_scan;                         // [K] uint64
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
-    size_t task_start;                       // [Tmax+1] first chunk of each task
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
     size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group (backward),
                                              //     in the lane order of the matrix-core operands
@@ -144,7 +134,7 @@ struct Layout {
                                              //     cut by the backward's windows
     size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, K, Gmax, Cmax, Tmax, NFB, scan_tiles;
+    int64_t n_tiles, K, Gmax, Cmax, NFB, scan_tiles;
     int passes;
 };
 
