@@ -211,52 +211,60 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
     }
 }
 
-// S of the cut runs: workgroup w takes the run whose head lies in window w
-// and that runs past its end (if any), and adds its end piece and the start
-// pieces of the windows up to the one holding its last lookup, in fp64 (the
-// WV waves take every WV-th window, UNR loads in flight each; a hot row's run
-// spans hundreds of windows).
+// S of the cut runs. A workgroup takes WV consecutive windows: wave v checks
+// window WV*b + v for a run that starts in it and runs past its end (all
+// checks at once), then the workgroup sums each found run in turn: its end
+// piece and the start pieces of the windows up to the one holding its last
+// lookup, in fp64 (the WV waves take every WV-th window, UNR loads in flight
+// each; a hot row's run spans hundreds of windows).
 template <int DL>
 __global__ __launch_bounds__(1024) void k_bwd_cross(const double* __restrict__ xpart, CrossRef x,
                                                     float* __restrict__ S, const int32_t* __restrict__ ctrl) {
     constexpr int D = 64 * DL, UNR = 8, WV = 16;
     __shared__ double red[WV][D];
+    __shared__ int32_t s_run[WV];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t nwin = (x.L + kWin - 1) / kWin;
     const int32_t NR = ctrl[CTRL_NUM_RUNS];
-    for (int64_t w = blockIdx.x; w < nwin; w += gridDim.x) {
-        const int32_t run = first_cut_run(x, w);
-        if (run < 0) continue;
-        const int64_t run_end = run + 1 < NR ? x.run_start[run + 1] : x.L;
-        const int64_t last = (run_end - 1) / kWin;
-        double acc[DL];
+    for (int64_t w0 = (int64_t)blockIdx.x * WV; w0 < nwin; w0 += (int64_t)gridDim.x * WV) {
+        if (lane == 0) s_run[wv] = w0 + wv < nwin ? first_cut_run(x, w0 + wv) : -1;
+        __syncthreads();
+        for (int i = 0; i < WV; ++i) {
+            const int32_t run = s_run[i];
+            if (run < 0) continue;
+            const int64_t w = w0 + i;
+            const int64_t run_end = run + 1 < NR ? x.run_start[run + 1] : x.L;
+            const int64_t last = (run_end - 1) / kWin;
+            double acc[DL];
 #pragma unroll
-        for (int k = 0; k < DL; ++k) acc[k] = wv == 0 ? xpart[(2 * w + 1) * D + lane * DL + k] : 0.0;
-        for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += WV * UNR) {
-            double v[UNR][DL];
+            for (int k = 0; k < DL; ++k) acc[k] = wv == 0 ? xpart[(2 * w + 1) * D + lane * DL + k] : 0.0;
+            for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += WV * UNR) {
+                double v[UNR][DL];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int64_t j = min(j0 + WV * u, last);
+                for (int u = 0; u < UNR; ++u) {
+                    const int64_t j = min(j0 + WV * u, last);
 #pragma unroll
-                for (int k = 0; k < DL; ++k) v[u][k] = xpart[2 * j * D + lane * DL + k];
+                    for (int k = 0; k < DL; ++k) v[u][k] = xpart[2 * j * D + lane * DL + k];
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u)
+                    if (j0 + WV * u <= last) {
+#pragma unroll
+                        for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
+                    }
             }
 #pragma unroll
-            for (int u = 0; u < UNR; ++u)
-                if (j0 + WV * u <= last) {
+            for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = acc[k];
+            __syncthreads();
+            for (int e = threadIdx.x; e < D; e += 64 * WV) {
+                double t = 0.0;
 #pragma unroll
-                    for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
-                }
+                for (int k = 0; k < WV; ++k) t += red[k][e];
+                S[(int64_t)run * D + e] = (float)t;
+            }
+            __syncthreads();
         }
-#pragma unroll
-        for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = acc[k];
-        __syncthreads();
-        for (int e = threadIdx.x; e < D; e += 64 * WV) {
-            double t = 0.0;
-#pragma unroll
-            for (int k = 0; k < WV; ++k) t += red[k][e];
-            S[(int64_t)run * D + e] = (float)t;
-        }
-        __syncthreads();
+        __syncthreads();   // every wave is done with s_run before it is rewritten
     }
 }
 
@@ -802,7 +810,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                    p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
-        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>(nwin, 1), 2048)),
+        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024)),
                            dim3(1024), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
         TT_LAUNCH_CHECK();
         if (!kept) {

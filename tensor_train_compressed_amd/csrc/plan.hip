@@ -14,7 +14,7 @@
 //
 // Kernels, in stream order:
 //   k_init            clears the control words, writes the table descriptors
-//   k_split           offsets check, bag search, digit split, prefix key; marks keys absent
+//   k_split           offsets check, bag labels, digit split, prefix key; marks keys absent
 //   k_radix_hist      \  stable LSD radix sort of key*M3 + i3, 8 bits per pass:
 //   scan               | per-tile digit counts, one exclusive scan over
 //   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
@@ -177,15 +177,22 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
         bool bad = (i == 0 && a != 0) || (i == TB && a != L) || (i < TB && off[i + 1] < a);
         if (bad) atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_OFFSETS);
     }
+    if (i < TB) {
+        // bag i labels its own lookups (clamped: bad offsets may leave some
+        // unlabelled; their readers clamp the label into [0, TB))
+        const int64_t a = min(max(off[i], (int64_t)0), L);
+        const int64_t b = min(max(off[i + 1], a), L);
+        for (int64_t l = a; l < b; ++l) bag_of[l] = (int32_t)i;
+    }
     if (i >= L) return;
-    // last bag q in [0, TB) with off[q] <= i; stays in range for any offsets
-    int64_t lo = 0, hi = TB;
+    // table of lookup i: last t with off[t*B] <= i (in range for any offsets)
+    const int64_t T = TB / B;
+    int64_t lo = 0, hi = T;
     while (hi - lo > 1) {
         const int64_t mid = (lo + hi) >> 1;
-        if (off[mid] <= i) lo = mid; else hi = mid;
+        if (off[mid * B] <= i) lo = mid; else hi = mid;
     }
-    const int64_t q = lo;
-    const TabDev d = desc[q / B];
+    const TabDev d = desc[lo];
     int64_t x = idx[i];
     if (x < 0 || x >= d.N) {
         atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_INDEX);
@@ -200,7 +207,6 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
     key[i] = k;
     ckey[i] = k * M3 + (int32_t)r3;
     i3o[i] = (int32_t)r3;
-    bag_of[i] = (int32_t)q;
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
                                                 const int32_t* __restrict__ skey,
                                                 const int32_t* __restrict__ i3,
                                                 const int32_t* __restrict__ bag_of, int64_t L,
-                                                int32_t M3, int32_t* __restrict__ sorted_i3,
+                                                int32_t TB, int32_t M3, int32_t* __restrict__ sorted_i3,
                                                 int32_t* __restrict__ sorted_bag,
                                                 int32_t* __restrict__ key_start,
                                                 int32_t* __restrict__ key_end,
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm
     const int32_t ck = skey[s];
     const int32_t k = ck / M3;
     sorted_i3[s] = i3[l];
-    sorted_bag[s] = bag_of[l];
+    sorted_bag[s] = min(max(bag_of[l], 0), TB - 1);
     // a row run is a maximal stretch of one (key, i3) row in sorted order
     rid[s] = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
     if (s == 0 || skey[s - 1] / M3 != k) key_start[k] = (int32_t)s;
@@ -800,7 +806,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         if (L > 0) {
             hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
                                p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
-                               p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
+                               (int32_t)p->TB, p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
                                key_start, key_end, p->at<int32_t>(lay.rid));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
