@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core backward for the common shapes (n1 = 4, n3 = 4, shared by all
-// tables). Seven kernels, all on row runs (one run per distinct table row of a
+// tables). The kernels, all on row runs (one run per distinct table row of a
 // group, the same runs the forward contracts):
 //
 // k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
@@ -156,9 +156,11 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 //                 dP_g    += S G3[i3]^T     (n1*n2 x R, summed in registers)
 //               and stores each group's dL/dP row once (atomics only for the
 //               few groups large enough to be split into pieces)
-// k_bwd_prefix  one workgroup per ((table, i2) slice, 64-column block):
-//                 dG2[i2] += G1[i1]^T dP    (plain stores, owned)
-//                 dG1[i1] += dP G2[i2]^T    (atomics across column blocks)
+// k_bwd_dg2     one wave per (slice, 16x16 tile of dG2[i2]):
+//                 dG2[i2] += G1[i1]^T dP    (fp64 products, plain stores, owned)
+// k_bwd_dg1     one wave per (4 groups of a slice, 16 r1 columns):
+//                 dG1[i1] += dP G2[i2]^T    (fp64 products, one fp64 atomic
+//                                            per element and group)
 // k_bwd_finish  dG1, dG3 <- their fp64 accumulators, rounded to fp32
 
 __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64_t s) {
@@ -631,40 +633,26 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ ru
     }
 }
 
-// One workgroup (8 waves) per ((table, i2) slice, 64-column block of the N2*R
-// columns). The slice's groups are taken 32 at a time (a slab); wave w owns
-//   dG2 tile (r1 block w & 1) x (column tile w >> 1), K = j1 per group
-//   dG1 tiles (r1 block w & 1) x (row tiles (w >> 1) + 4m, m < 2), rows = (group, j1),
-//            K = the block's 64 columns
-// so dG2 needs no reduction and dG1 only atomics across the column blocks.
-// Loads run ahead: the next slab's dP rows and G1 rows and the group keys two
-// slabs ahead are issued before the current slab's math and its dG1 atomics,
-// so a slab costs its math and barriers, not memory round trips.
-template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(512) void k_bwd_prefix(const TabDev* __restrict__ desc, int32_t T,
-                                                    int32_t* ctrl, int64_t K,
-                                                    const uint64_t* __restrict__ key_scan,
-                                                    const int32_t* __restrict__ group_key,
-                                                    const float* __restrict__ dpg,
-                                                    const float* __restrict__ g1,
-                                                    const float* __restrict__ g2,
-                                                    double* __restrict__ dg1, float* __restrict__ dg2) {
-    constexpr int NP = N1 * N2, PR = NP * R, N2R = N2 * R, QN = N2R / 64;
-    constexpr int SG = 32;                  // groups per slab
-    constexpr int MR = SG * N1;             // slab rows (group, j1)
-    constexpr int DS = 64 + 4;              // LDS row stride of the dP / G2 column block
-    constexpr int NT = 512;                 // threads
-    constexpr int NDP = MR * 16 / NT;       // float4 of dP rows per thread
-    constexpr int NG1 = SG * N1 * R / 4 / NT;   // float4 of G1 rows per thread
-    static_assert(N1 == 4 && N2R % 64 == 0 && R == 32 && NDP * NT == MR * 16 && NG1 * NT * 4 == SG * N1 * R,
-                  "shape");
-    __shared__ float sG2[R * DS];           // G2[i2][r1][block columns]
-    __shared__ float sD[MR * DS];           // dP rows (g, j1), block columns
-    __shared__ float sA[SG * N1 * R];       // G1[i1(g)] of the slab
-    __shared__ int32_t sI1[SG];
-
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
-    const int32_t bi = blockIdx.x / QN, qn = blockIdx.x % QN;
+// dG2[i2] = sum over the slice's groups of G1[i1]^T dP_g, one wave per
+// (slice, 16-column tile of the n2*R columns), every r1 tile: K = j1, one
+// fp64 matrix-core step per group and r1 tile, operands read straight from
+// memory (each dP element once; the next UNR groups' loads issued before the
+// current ones' products), no LDS and no barrier. The wave owns its columns:
+// plain stores.
+template <int N1, int N2, int R>
+__global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc, int32_t T,
+                                                 const int32_t* __restrict__ ctrl, int64_t K,
+                                                 const uint64_t* __restrict__ key_scan,
+                                                 const int32_t* __restrict__ group_key,
+                                                 const float* __restrict__ dpg, const float* __restrict__ g1,
+                                                 float* __restrict__ dg2, int64_t n_i2) {
+    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, CT = N2R / 16, UNR = 8;
+    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0, "shape");
+    const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+    const int64_t task = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if (task >= n_i2 * CT) return;
+    const int32_t bi = (int32_t)(task / CT);
+    const int ct = (int)(task % CT);
     int t = 0;
     {
         int lo = 0, hi = T;
@@ -677,108 +665,120 @@ __global__ __launch_bounds__(512) void k_bwd_prefix(const TabDev* __restrict__ d
     const TabDev d = desc[t];
     const int32_t i2 = bi - d.i2_base;
     const int64_t kb = (int64_t)d.key_base + (int64_t)i2 * d.m1;
-    const int64_t ke = kb + d.m1;
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
     const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
-    const int32_t ge = ke < K ? (int32_t)(key_scan[ke] >> 32) : U;
-    const int c0 = 64 * qn;
-    const float* G1t = g1 + d.o1;
-
-    // loads of slab gs: dP rows (zero past the slice's groups) and G1 rows of
-    // the groups whose i1 lane k of `i1v` holds (k < SG)
-    auto load_dp = [&](int32_t gs, floatx4 (&v)[NDP]) {
+    const int32_t ge = kb + d.m1 < K ? (int32_t)(key_scan[kb + d.m1] >> 32) : U;
+    const float* G1c = g1 + d.o1 + q * R + col;               // + i1*N1*R + 16*rt: G1[i1][j1 = q][r1]
+    const float* dPc = dpg + q * N2R + 16 * ct + col;          // + g * PR: dP_g[j1 = q][c]
+    doublex4 acc[RT];
 #pragma unroll
-        for (int k = 0; k < NDP; ++k) {
-            const int f = tid + NT * k, row = f / 16, c4 = 4 * (f % 16);   // row = (g, j1)
-            const int32_t g = gs + row / N1;
-            const floatx4* src = reinterpret_cast<const floatx4*>(
-                dpg + (int64_t)min(g, ge - 1) * PR + (row % N1) * N2R + c0 + c4);
-            v[k] = *src;
-            if (g >= ge) v[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-    auto load_i1 = [&](int32_t gs) -> int32_t {   // lane k < SG: i1 of group gs + k (0 past the end)
-        const int32_t g = gs + (lane & (SG - 1));
-        return g < ge ? (int32_t)(group_key[g] - kb) : 0;
-    };
-    auto load_g1 = [&](int32_t i1v, floatx4 (&u)[NG1]) {
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = doublex4{0.0, 0.0, 0.0, 0.0};
+    for (int32_t gb = g0; gb < ge; gb += 64) {
+        const int32_t i1l = group_key[min(gb + lane, ge - 1)] - (int32_t)kb;   // lane j: i1 of group gb + j
+        const int n = min(64, ge - gb);
+        float av[2][UNR][RT], bv[2][UNR];
+        auto load = [&](int j0, float (&a)[UNR][RT], float (&b)[UNR]) {
 #pragma unroll
-        for (int k = 0; k < NG1; ++k) {
-            const int f = tid + NT * k, gi = f / (N1 * R / 4);   // float4 f of the slab's G1 rows
-            const int32_t i1 = __shfl(i1v, gi);
-            u[k] = reinterpret_cast<const floatx4*>(G1t + (int64_t)i1 * N1 * R)[f % (N1 * R / 4)];
-        }
-    };
-
-    const float* G2s = g2 + d.o2 + (int64_t)i2 * R * N2R;
-    for (int e = tid; e < R * 64; e += NT) sG2[(e >> 6) * DS + (e & 63)] = G2s[(e >> 6) * N2R + c0 + (e & 63)];
-
-    const int rt = w & 1, ch = w >> 1;
-    // dG1 and dG2 are sums over every lookup of the slice (hundreds of
-    // thousands for the hot ones) with heavy cancellation: their products run
-    // on the fp64 matrix cores (fp32 operands convert exactly), so the only
-    // fp32 rounding left is that of the stored result
-    doublex4 acc2 = {0.0, 0.0, 0.0, 0.0};
-
-    floatx4 dpv[NDP], g1v[NG1];
-    int32_t i1c = 0, i1n = 0;
-    if (g0 < ge) {   // (the slab loads clamp rows to [g0, ge - 1])
-        i1c = load_i1(g0);
-        i1n = load_i1(g0 + SG);
-        load_dp(g0, dpv);
-        load_g1(i1c, g1v);
-    }
-    for (int32_t gs = g0; gs < ge; gs += SG) {
-        const int ng = min(SG, ge - gs);
-        __syncthreads();   // the previous slab's math is done with sD / sA / sI1
+            for (int u = 0; u < UNR; ++u) {
+                const int j = min(j0 + u, n - 1);
+                const float* ga = G1c + (int64_t)__builtin_amdgcn_readlane(i1l, j) * N1 * R;
 #pragma unroll
-        for (int k = 0; k < NDP; ++k) {
-            const int f = tid + NT * k;
-            *reinterpret_cast<floatx4*>(sD + (f / 16) * DS + 4 * (f % 16)) = dpv[k];
-        }
-#pragma unroll
-        for (int k = 0; k < NG1; ++k) *reinterpret_cast<floatx4*>(sA + 4 * (tid + NT * k)) = g1v[k];
-        if (tid < SG) sI1[tid] = i1c;
-        // the next slab's loads, then the group keys of the one after
-        const int32_t i1nn = load_i1(gs + 2 * SG);
-        load_dp(gs + SG, dpv);
-        load_g1(i1n, g1v);
-        i1c = i1n;
-        i1n = i1nn;
-        __syncthreads();
-        // dG2[r1][c] += sum_j1 G1[j1][r1] dP[j1][c]: one k-step per group
-        for (int gi = 0; gi < ng; ++gi) {
-            const double av = sA[gi * N1 * R + q * R + 16 * rt + col];
-            const double bv = sD[(gi * N1 + q) * DS + 16 * ch + col];
-            acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc2, 0, 0, 0);
-        }
-        // dG1 rows (g, j1) of row tiles ch + 4m, r1 block rt, K = 64 columns
-#pragma unroll
-        for (int m = 0; m < MR / 64; ++m) {
-            const int rtile = ch + 4 * m;
-            if (4 * rtile < ng) {
-                doublex4 acc1 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                for (int s2 = 0; s2 < 16; ++s2) {
-                    const double av = sD[(16 * rtile + col) * DS + 4 * s2 + q];
-                    const double bv = sG2[(16 * rt + col) * DS + 4 * s2 + q];
-                    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc1, 0, 0, 0);
-                }
-                // the fp64 product's lane holds rows q + 4v = (group 4*rtile + v,
-                // j1 = q), column r1 = 16*rt + col
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int gi = 4 * rtile + v;
-                    if (gi < ng) atomicAdd(dg1 + d.o1 + (int64_t)sI1[gi] * N1 * R + q * R + 16 * rt + col, acc1[v]);
-                }
+                for (int rt = 0; rt < RT; ++rt) a[u][rt] = ga[16 * rt];
+                b[u] = dPc[(int64_t)(gb + j) * PR];
             }
+        };
+        auto math = [&](int j0, const float (&a)[UNR][RT], const float (&b)[UNR]) {
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (j0 + u < n) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][rt], (double)b[u], acc[rt], 0, 0, 0);
+                }
+        };
+        load(0, av[0], bv[0]);
+        for (int j0 = 0;; j0 += 2 * UNR) {
+            load(min(j0 + UNR, n - 1), av[1], bv[1]);
+            math(j0, av[0], bv[0]);
+            if (j0 + UNR >= n) break;
+            load(min(j0 + 2 * UNR, n - 1), av[0], bv[0]);
+            math(j0 + UNR, av[1], bv[1]);
+            if (j0 + 2 * UNR >= n) break;
         }
     }
-    // dG2[i2][:, block columns] is owned by this workgroup: plain stores (the
-    // fp64 product's lane holds rows q + 4v of the tile)
-    float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R + c0;
+    // the fp64 product's lane (col, q) holds rows r1 = 16rt + q + 4v, column c = 16ct + col
+    float* D2 = dg2 + d.o2 + (int64_t)i2 * R * N2R + 16 * ct + col;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) D2[(16 * rt + q + 4 * v) * N2R + 16 * ch + col] = (float)acc2[v];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) D2[(int64_t)(16 * rt + q + 4 * v) * N2R] = (float)acc[rt][v];
+}
+
+// dG1[i1] += dP_g G2[i2]^T, one wave per half of a prefix batch (4 groups of
+// one slice), every r1 tile: rows (group, j1), K = the n2*R columns, taken 16
+// at a time as 16-byte loads per lane (dP once, G2 per r1 tile) feeding four
+// fp64 matrix-core steps. A group's sum over K is complete in the wave, so
+// each dG1 element takes one fp64 atomic per group (groups of every slice add
+// to the same i1).
+template <int N1, int N2, int R>
+__global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ recs, int64_t nb,
+                                                 const float* __restrict__ dpg, const float* __restrict__ g2,
+                                                 double* __restrict__ dg1) {
+    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2;
+    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0, "shape");
+    const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+    const int64_t task = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if (task >= nb * 2) return;
+    const int64_t b = task / 2;
+    const int h = (int)(task % 2);
+    const int32_t rw = rec_word(recs, b, nb);
+    const int ng = rec_field(rw, RW_NG) - 4 * h;
+    if (ng <= 0) return;
+    const int32_t g0 = rec_field(rw, RW_G0) + 4 * h;
+    // A row i = (group i / 4, j1 = i % 4) of the tile: lane (col, q) reads row col
+    const int32_t ga = g0 + min(col / 4, ng - 1);
+    const floatx4* A = reinterpret_cast<const floatx4*>(dpg + (int64_t)ga * PR + (col % 4) * N2R) + q;
+    const floatx4* Bm = reinterpret_cast<const floatx4*>(g2 + rec_field64(rw, RW_O2) +
+                                                          (int64_t)rec_field(rw, RW_I2) * R * N2R +
+                                                          (int64_t)col * N2R) + q;   // + 16*rt rows
+    doublex4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = doublex4{0.0, 0.0, 0.0, 0.0};
+    floatx4 a4[2][UNR], b4[2][UNR][RT];
+    auto load = [&](int s0, floatx4 (&a)[UNR], floatx4 (&bb)[UNR][RT]) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            a[u] = A[4 * (s0 + u)];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) bb[u][rt] = Bm[(16 * rt) * (N2R / 4) + 4 * (s0 + u)];
+        }
+    };
+    auto math = [&](const floatx4 (&a)[UNR], const floatx4 (&bb)[UNR][RT]) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][e], (double)bb[u][rt][e], acc[rt], 0, 0, 0);
+    };
+    load(0, a4[0], b4[0]);
+#pragma unroll
+    for (int s0 = 0; s0 < KS; s0 += 2 * UNR) {
+        load(s0 + UNR, a4[1], b4[1]);
+        math(a4[0], b4[0]);
+        if (s0 + 2 * UNR < KS) load(s0 + 2 * UNR, a4[0], b4[0]);
+        math(a4[1], b4[1]);
+    }
+    // the fp64 product's lane (col, q) holds rows q + 4v = (group v, j1 = q), column r1 = 16rt + col
+    double* D1 = dg1 + rec_field64(rw, RW_O1) + q * R + col;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        if (v < ng) {
+            double* dst = D1 + (int64_t)__builtin_amdgcn_readlane(rw, RW_I1 + 4 * h + v) * N1 * R;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[rt][v]);
+        }
 }
 
 template <int N1, int N2, int R, int N3>
@@ -841,10 +841,19 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                            p->at<float>(p->lay.dpg));
         TT_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL((k_bwd_prefix<N1, N2, R, N3>), dim3((unsigned)(p->n_i2 * (N2 * R / 64))),
-                       dim3(512), 0, s, p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
-                       p->at<int32_t>(p->lay.group_key), p->at<float>(p->lay.dpg), g1, g2, acc1, dg2);
-    TT_LAUNCH_CHECK();
+    {
+        const int64_t w2 = p->n_i2 * (N2 * R / 16);
+        hipLaunchKernelGGL((k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(), p->T,
+                           p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key),
+                           p->at<float>(p->lay.dpg), g1, dg2, p->n_i2);
+        TT_LAUNCH_CHECK();
+        const int64_t w1 = p->n_fb * 2;
+        if (w1 > 0) {
+            hipLaunchKernelGGL((k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<float>(p->lay.dpg), g2, acc1);
+            TT_LAUNCH_CHECK();
+        }
+    }
     hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
                        (scan3 && p->L > 0) ? 0 : p->extent[2], p->ctrl());
     TT_LAUNCH_CHECK();
