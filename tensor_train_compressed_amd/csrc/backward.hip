@@ -670,9 +670,13 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
     const int32_t ge = kb + d.m1 < K ? (int32_t)(key_scan[kb + d.m1] >> 32) : U;
     const float* G1c = g1 + d.o1 + q * R + col;               // + i1*N1*R + 16*rt: G1[i1][j1 = q][r1]
     const float* dPc = dpg + q * N2R + 16 * ct + col;          // + g * PR: dP_g[j1 = q][c]
-    doublex4 acc[RT];
+    // two accumulator sets (even and odd steps of a group pair) keep two
+    // independent product chains per r1 tile in flight
+    doublex4 acc[2][RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = doublex4{0.0, 0.0, 0.0, 0.0};
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[x][rt] = doublex4{0.0, 0.0, 0.0, 0.0};
     for (int32_t gb = g0; gb < ge; gb += 64) {
         const int32_t i1l = group_key[min(gb + lane, ge - 1)] - (int32_t)kb;   // lane j: i1 of group gb + j
         const int n = min(64, ge - gb);
@@ -693,7 +697,8 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
                 if (j0 + u < n) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
-                        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][rt], (double)b[u], acc[rt], 0, 0, 0);
+                        acc[u & 1][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][rt], (double)b[u],
+                                                                             acc[u & 1][rt], 0, 0, 0);
                 }
         };
         load(0, av[0], bv[0]);
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) D2[(int64_t)(16 * rt + q + 4 * v) * N2R] = (float)acc[rt][v];
+        for (int v = 0; v < 4; ++v) D2[(int64_t)(16 * rt + q + 4 * v) * N2R] = (float)(acc[0][rt][v] + acc[1][rt][v]);
 }
 
 // dG1[i1] += dP_g G2[i2]^T, one wave per half of a prefix batch (4 groups of
@@ -741,9 +746,11 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
     const floatx4* Bm = reinterpret_cast<const floatx4*>(g2 + rec_field64(rw, RW_O2) +
                                                           (int64_t)rec_field(rw, RW_I2) * R * N2R +
                                                           (int64_t)col * N2R) + q;   // + 16*rt rows
-    doublex4 acc[RT];
+    doublex4 acc[2][RT];   // two sets (even and odd columns): independent chains
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = doublex4{0.0, 0.0, 0.0, 0.0};
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[x][rt] = doublex4{0.0, 0.0, 0.0, 0.0};
     floatx4 a4[2][UNR], b4[2][UNR][RT];
     auto load = [&](int s0, floatx4 (&a)[UNR], floatx4 (&bb)[UNR][RT]) {
 #pragma unroll
@@ -760,7 +767,8 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][e], (double)bb[u][rt][e], acc[rt], 0, 0, 0);
+                    acc[e & 1][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][e], (double)bb[u][rt][e],
+                                                                         acc[e & 1][rt], 0, 0, 0);
     };
     load(0, a4[0], b4[0]);
 #pragma unroll
@@ -777,7 +785,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
         if (v < ng) {
             double* dst = D1 + (int64_t)__builtin_amdgcn_readlane(rw, RW_I1 + 4 * h + v) * N1 * R;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[rt][v]);
+            for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[0][rt][v] + acc[1][rt][v]);
         }
 }
 
