@@ -16,15 +16,16 @@
 //   k_init            clears the control words, writes the table descriptors
 //   k_split           offsets check, bag labels, digit split, prefix key; marks keys absent
 //   k_radix_hist      \  stable LSD radix sort of key*M3 + i3, 8 bits per pass:
-//   scan               | per-tile digit counts, one exclusive scan over
-//   k_radix_scatter   /  (digit, tile), wave-ballot stable ranks inside a tile
-//   k_gather          sorted i3 / bag, row-run heads, first and last position of each key
-//   k_key_flags       per key: present flag and chunk count
-//   scan              group id and first chunk of every present key
-//   k_groups          group tables, counts into the control words
-//   k_chunks          chunk table (one thread per chunk)
-//   scan, k_runs      row-run ids (a row run = one (key, i3) row), run tables
+//   k_radix_scatter   /  per-tile digit counts, then wave-ballot stable ranks inside a
+//                        tile, staged in LDS and written out in digit runs
+//   k_gather          sorted i3, first and last position of each key, row-run heads
+//                     per tile (the sorted bags come out of the sort)
+//   k_key_tiles       present keys and chunks per tile of keys
+//   k_groups          key scan (group id and first chunk of every key), group tables
+//   k_runs            row-run ids and tables, chunk table
 //   k_batches         one record per forward batch (kFwdBatch groups of one slice)
+// A device-wide scan of the tile totals runs before k_radix_scatter, k_groups
+// or k_runs only when there are more than kDirectTiles tiles.
 #include "tt_internal.h"
 
 #include <algorithm>
@@ -42,6 +43,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
     y.K = K;
     y.n_tiles = (L + kSortTile - 1) / kSortTile;
+    y.hstride = (y.n_tiles + 15) & ~int64_t(15);   // rows of whole 64-byte lines (padding kept zero)
     y.Gmax = std::min<int64_t>(L, K);
     y.Cmax = L == 0 ? 0 : std::min<int64_t>(L, y.Gmax + (L + chunk - 1) / chunk);
     int bits = 0;
@@ -49,7 +51,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.passes = std::max(1, (bits + kRadixBits - 1) / kRadixBits);
     y.ctrl = take(sizeof(int32_t) * CTRL_WORDS);
     {
-        const int64_t nh = (int64_t)kRadixBins * ((L + kSortTile - 1) / kSortTile);
+        const int64_t nh = (int64_t)kRadixBins * y.hstride;
         const int64_t nscan = std::max<int64_t>(std::max<int64_t>(nh, K), L);
         y.scan_tiles = (nscan + kScanTile - 1) / kScanTile + 1;
         y.scan_st = take(sizeof(ScanTileStatus) * (size_t)y.scan_tiles);
@@ -73,15 +75,19 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.stage = take(sizeof(float) * ((size_t)L + kStageSpare) * (size_t)D);
     y.perm = take(l4); y.sorted_i3 = take(l4); y.sorted_bag = take(l4);
     y.skey = take(l4);
-    // The radix passes ping-pong between (skey, perm) and a temporary pair that
-    // reuses sorted_i3 / sorted_bag, which are written only after the sort.
-    y.sort_k0 = y.sorted_i3; y.sort_v0 = y.sorted_bag;
-    y.sort_k1 = y.skey; y.sort_v1 = y.perm;
-    const int64_t nhist = (int64_t)kRadixBins * y.n_tiles;
+    // The radix passes move (sort key, lookup, bag) and ping-pong between
+    // (skey, perm, sorted_bag) and a temporary triple that reuses sorted_i3,
+    // rid and run_start, which are written only after the sort.
+    y.sort_k0 = y.sorted_i3; y.sort_v0 = y.rid; y.sort_b0 = y.run_start;
+    y.sort_k1 = y.skey; y.sort_v1 = y.perm; y.sort_b1 = y.sorted_bag;
+    const int64_t nhist = (int64_t)kRadixBins * y.hstride;
     y.hist = take(sizeof(uint32_t) * (size_t)nhist);
     y.key_start = take(sizeof(int32_t) * (size_t)K);
     y.key_end = take(sizeof(int32_t) * (size_t)K);
     y.key_scan = take(sizeof(uint64_t) * (size_t)K);
+    y.n_ktiles = (K + kSortTile - 1) / kSortTile;
+    y.run_tiles = take(sizeof(uint32_t) * (size_t)y.n_tiles);
+    y.key_tiles = take(sizeof(uint64_t) * (size_t)y.n_ktiles);
     y.group_key = take(sizeof(int32_t) * (size_t)y.Gmax);
     y.group_start = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
     y.group_cbase = take(sizeof(int32_t) * (size_t)(y.Gmax + 1));
@@ -211,49 +217,128 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
 
 // ---------------------------------------------------------------------------
 // stable LSD radix sort
+//
+// A tile is kSortTile consecutive elements; wave w of its workgroup takes the
+// w-th sixteenth, 64 at a time, so ranks in (wave, slot, lane) order are ranks
+// in sequence order. Digit counts are kept per wave (no LDS atomics: in a
+// slot, one leader lane per distinct digit adds its peers' count).
 
-__global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t* __restrict__ keys,
-                                                             int64_t L, int shift, int64_t n_tiles,
-                                                             uint32_t* __restrict__ hist) {
-    __shared__ uint32_t cnt[kRadixBins];
-    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) cnt[i] = 0;
-    __syncthreads();
-    const int64_t tile = blockIdx.x;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / 4);
-#pragma unroll 4
-    for (int slot = 0; slot < kSortItems; ++slot) {
-        const int64_t e = base + slot * 64 + lane;
-        const bool valid = e < L;
-        const uint32_t d = valid ? ((uint32_t)keys[e] >> shift) & (kRadixBins - 1) : 0u;
-        const uint64_t peers = match_digit(d, __ballot(valid));
-        if (valid && popc_below(peers) == 0) atomicAdd(&cnt[d], (uint32_t)__popcll(peers));
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) hist[(int64_t)i * n_tiles + tile] = cnt[i];
+__device__ __forceinline__ uint32_t sort_digit(int32_t k, int shift) {
+    return ((uint32_t)k >> shift) & (kRadixBins - 1);
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
-    const int32_t* __restrict__ kin, const int32_t* __restrict__ vin, int64_t L, int shift,
-    int64_t n_tiles, const uint32_t* __restrict__ hist_scan, int32_t* __restrict__ kout,
-    int32_t* __restrict__ vout) {
-    __shared__ uint32_t cnt[4][kRadixBins];
-    __shared__ uint32_t gbase[kRadixBins];
-    const int64_t tile = blockIdx.x;
-    for (int i = threadIdx.x; i < 4 * kRadixBins; i += kSortThreads) (&cnt[0][0])[i] = 0;
-    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) gbase[i] = hist_scan[(int64_t)i * n_tiles + tile];
-    __syncthreads();
+// Per-tile digit counts: hist[d * hstride + tile]; the last tile also zeroes
+// the padding columns [n_tiles, hstride).
+__global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t* __restrict__ keys,
+                                                             int64_t L, int shift, int64_t n_tiles,
+                                                             int64_t hstride, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[kSortWaves][kRadixBins];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / 4);
-    int32_t kk[kSortItems], vv[kSortItems];
-    uint32_t rk[kSortItems];
+    for (int i = lane; i < kRadixBins; i += 64) cnt[w][i] = 0;   // own row, so no barrier
+    const int64_t tile = blockIdx.x;
+    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / kSortWaves);
+    uint32_t d[kSortItems];
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t e = base + slot * 64 + lane;
+        d[slot] = e < L ? sort_digit(keys[e], shift) : 0u;
+    }
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const bool valid = base + slot * 64 + lane < L;
+        const uint64_t peers = match_digit(d[slot], __ballot(valid));
+        if (valid && popc_below(peers) == 0) cnt[w][d[slot]] += (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) c += cnt[ww][i];
+        hist[(int64_t)i * hstride + tile] = c;
+    }
+    if (tile == n_tiles - 1) {
+        const int64_t pad = hstride - n_tiles;
+        for (int64_t i = threadIdx.x; i < pad * kRadixBins; i += kSortThreads)
+            hist[(i / pad) * hstride + n_tiles + i % pad] = 0u;
+    }
+}
+
+// Scatter of one tile. The tile's elements are first placed in LDS in their
+// output order (by digit, stable), then written out with consecutive threads
+// on consecutive output positions, so each digit's run is one coalesced
+// stretch. DIRECT: the workgroup forms its digits' global bases from the raw
+// per-tile counts (digit start = counts of all smaller digits, plus this
+// digit's counts in earlier tiles); otherwise hist holds the exclusive scan of
+// the counts in digit-major order.
+//
+// Each element carries its lookup and its bag. The first pass (vin null)
+// takes the lookup from the position and the bag from bin = bag_of, clamped
+// into [0, TB) (bad offsets can leave lookups unlabelled).
+template <bool DIRECT>
+__global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
+    const int32_t* __restrict__ kin, const int32_t* __restrict__ vin, const int32_t* __restrict__ bin,
+    int64_t L, int32_t TB, int shift, int64_t hstride, const uint32_t* __restrict__ hist,
+    int32_t* __restrict__ kout, int32_t* __restrict__ vout, int32_t* __restrict__ bout) {
+    __shared__ uint32_t cnt[kSortWaves][kRadixBins];
+    __shared__ int32_t sk[kSortTile], sv[kSortTile], sb[kSortTile];
+    __shared__ uint32_t gpre[kRadixBins];    // digit's count in earlier tiles (DIRECT) or global base
+    __shared__ uint32_t gtot[kRadixBins];    // digit's count in all tiles (DIRECT)
+    __shared__ uint32_t lbase[kRadixBins];   // digit's first position in the tile's output order
+    __shared__ int32_t delta[kRadixBins];    // global position - tile position, per digit
+    __shared__ uint32_t wsum[2][kRadixBins / 64];
+    const int64_t tile = blockIdx.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = lane; i < kRadixBins; i += 64) cnt[w][i] = 0;
+    // this tile's elements, all loads in flight at once
+    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / kSortWaves);
+    int32_t kk[kSortItems], vv[kSortItems], bb[kSortItems];
 #pragma unroll
     for (int slot = 0; slot < kSortItems; ++slot) {
         const int64_t e = base + slot * 64 + lane;
         const bool valid = e < L;
         kk[slot] = valid ? kin[e] : 0;
         vv[slot] = valid ? (vin ? vin[e] : (int32_t)e) : 0;
-        const uint32_t d = ((uint32_t)kk[slot] >> shift) & (kRadixBins - 1);
+        bb[slot] = valid ? bin[e] : 0;
+        if (!vin) bb[slot] = min(max(bb[slot], 0), TB - 1);
+    }
+    if (DIRECT) {
+        // four lanes per digit, each sums a quarter of the digit's row
+        const int dg = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const uint4* row = reinterpret_cast<const uint4*>(hist + (int64_t)dg * hstride);
+        const int64_t n4 = hstride / 4;
+        uint32_t pre = 0, tot = 0;
+        for (int64_t v0 = part; v0 < n4; v0 += 32) {   // eight loads in flight per lane
+            uint4 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = v0 + 4 * u < n4 ? row[v0 + 4 * u] : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t t0 = 4 * (v0 + 4 * u);
+                const uint32_t c[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    tot += c[j];
+                    if (t0 + j < tile) pre += c[j];
+                }
+            }
+        }
+        pre += __shfl_xor(pre, 1);
+        pre += __shfl_xor(pre, 2);
+        tot += __shfl_xor(tot, 1);
+        tot += __shfl_xor(tot, 2);
+        if (part == 0) {
+            gpre[dg] = pre;
+            gtot[dg] = tot;
+        }
+    } else {
+        for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) gpre[i] = hist[(int64_t)i * hstride + tile];
+    }
+    // stable ranks inside the tile, per wave
+    uint32_t rk[kSortItems];
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const bool valid = base + slot * 64 + lane < L;
+        const uint32_t d = sort_digit(kk[slot], shift);
         const uint64_t peers = match_digit(d, __ballot(valid));
         const uint32_t below = popc_below(peers);
         uint32_t pre = 0;
@@ -262,23 +347,69 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
         rk[slot] = pre + below;
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadixBins; d += kSortThreads) {
-        uint32_t run = 0;
-        for (int ww = 0; ww < 4; ++ww) {
-            const uint32_t c = cnt[ww][d];
-            cnt[ww][d] = run;
-            run += c;
+    // per digit (threads 0..255, waves 0..3): exclusive prefix over the waves,
+    // then exclusive scans over the digits of the tile counts and (DIRECT) of
+    // the all-tile counts
+    uint32_t linc = 0, lcnt = 0, tinc = 0, tcnt = 0;
+    if (threadIdx.x < kRadixBins) {
+        const int dg = threadIdx.x;
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) {
+            const uint32_t c = cnt[ww][dg];
+            cnt[ww][dg] = lcnt;
+            lcnt += c;
+        }
+        linc = lcnt;
+        if (DIRECT) tinc = tcnt = gtot[dg];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(linc, o, 64);
+            const uint32_t z = __shfl_up(tinc, o, 64);
+            if (lane >= o) {
+                linc += y;
+                tinc += z;
+            }
+        }
+        if (lane == 63) {
+            wsum[0][w] = linc;
+            wsum[1][w] = tinc;
         }
     }
     __syncthreads();
+    if (threadIdx.x < kRadixBins) {
+        uint32_t lo = 0, to = 0;
+        for (int ww = 0; ww < w; ++ww) {
+            lo += wsum[0][ww];
+            to += wsum[1][ww];
+        }
+        const uint32_t lb = lo + linc - lcnt;
+        const uint32_t gb = DIRECT ? to + tinc - tcnt + gpre[threadIdx.x] : gpre[threadIdx.x];
+        lbase[threadIdx.x] = lb;
+        delta[threadIdx.x] = (int32_t)(gb - lb);
+    }
+    __syncthreads();
+    // place in output order inside the tile
 #pragma unroll
     for (int slot = 0; slot < kSortItems; ++slot) {
-        const int64_t e = base + slot * 64 + lane;
-        if (e < L) {
-            const uint32_t d = ((uint32_t)kk[slot] >> shift) & (kRadixBins - 1);
-            const uint32_t pos = gbase[d] + cnt[w][d] + rk[slot];
-            kout[pos] = kk[slot];
-            vout[pos] = vv[slot];
+        if (base + slot * 64 + lane < L) {
+            const uint32_t d = sort_digit(kk[slot], shift);
+            const uint32_t lp = lbase[d] + cnt[w][d] + rk[slot];
+            if (lp < (uint32_t)kSortTile) {   // always, as above
+                sk[lp] = kk[slot];
+                sv[lp] = vv[slot];
+                sb[lp] = bb[slot];
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t nt = min<int64_t>(kSortTile, L - tile * kSortTile);
+    for (int i = threadIdx.x; i < nt; i += kSortThreads) {
+        const int32_t k = sk[i];
+        const int64_t pos = (int64_t)delta[sort_digit(k, shift)] + i;
+        if (pos >= 0 && pos < L) {   // always, when the counts are consistent
+            kout[pos] = k;
+            vout[pos] = sv[i];
+            bout[pos] = sb[i];
         }
     }
 }
@@ -449,123 +580,223 @@ static tt_status scan_exclusive(const tt_emb_plan_s* p, int seq, V* data, int64_
 
 // ---------------------------------------------------------------------------
 // groups and chunks
+//
+// The position-indexed passes below work on tiles of kSortTile sorted
+// positions (one workgroup each) and the key-indexed ones on tiles of
+// kSortTile keys. A counting pass leaves one total per tile; the pass that
+// needs the exclusive scan adds up the earlier tiles' totals itself (DIRECT,
+// up to kDirectTiles tiles) or reads them from a device-wide scan of the
+// tile totals, and scans inside its tile.
 
-__global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ perm,
-                                                const int32_t* __restrict__ skey,
-                                                const int32_t* __restrict__ i3,
-                                                const int32_t* __restrict__ bag_of, int64_t L,
-                                                int32_t TB, int32_t M3, int32_t* __restrict__ sorted_i3,
-                                                int32_t* __restrict__ sorted_bag,
-                                                int32_t* __restrict__ key_start,
-                                                int32_t* __restrict__ key_end,
-                                                int32_t* __restrict__ rid) {
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= L) return;
-    const int32_t l = perm[s];
-    const int32_t ck = skey[s];
-    const int32_t k = ck / M3;
-    sorted_i3[s] = i3[l];
-    sorted_bag[s] = min(max(bag_of[l], 0), TB - 1);
-    // a row run is a maximal stretch of one (key, i3) row in sorted order
-    rid[s] = (s == 0 || skey[s - 1] != ck) ? 1 : 0;
-    if (s == 0 || skey[s - 1] / M3 != k) key_start[k] = (int32_t)s;
-    if (s == L - 1 || skey[s + 1] / M3 != k) key_end[k] = (int32_t)(s + 1);
-}
-
-__global__ __launch_bounds__(256) void k_key_flags(const int32_t* __restrict__ key_start,
-                                                   const int32_t* __restrict__ key_end, int64_t K,
-                                                   int32_t chunk, uint64_t* __restrict__ out) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
-    const int32_t st = key_start[k];
-    uint64_t v = 0;
-    if (st >= 0) {
-        const uint32_t nch = (uint32_t)((key_end[k] - st + chunk - 1) / chunk);
-        v = (uint64_t(1) << 32) | nch;
+// Sum of tsum[0, tile) (DIRECT, tile <= kDirectTiles) or the scanned tsum[tile],
+// by wave 0, into *out (LDS); the caller synchronises before reading it.
+template <bool DIRECT, class V>
+__device__ __forceinline__ void tile_base(const V* __restrict__ tsum, int64_t tile, V* out) {
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    V x = 0;
+    if (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < (int)(kDirectTiles / 64); ++j) {
+            const int64_t u = lane + 64 * j;
+            if (u < tile) x += tsum[u];
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    } else {
+        x = tsum[tile];
     }
-    out[k] = v;
+    if (lane == 0) *out = x;
 }
 
-__global__ __launch_bounds__(256) void k_groups(const int32_t* __restrict__ key_start,
-                                                const uint64_t* __restrict__ scan, int64_t K,
-                                                int64_t L, int32_t* __restrict__ group_key,
-                                                int32_t* __restrict__ group_start,
-                                                int32_t* __restrict__ group_cbase, int32_t* ctrl) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k == 0) {
-        const uint64_t tot = *reinterpret_cast<const uint64_t*>(ctrl + CTRL_SCAN_TOTAL);
-        const int32_t U = (int32_t)(tot >> 32), NC = (int32_t)(tot & 0xffffffffu);
+// Per sorted position: sorted i3 (from the sort key), first and last
+// position of each key; per tile: the number of row-run heads (a row run is a
+// maximal stretch of one (key, i3) row in sorted order).
+__global__ __launch_bounds__(kSortThreads) void k_gather(const int32_t* __restrict__ skey, int64_t L,
+                                                         int32_t M3, int32_t* __restrict__ sorted_i3,
+                                                         int32_t* __restrict__ key_start,
+                                                         int32_t* __restrict__ key_end,
+                                                         uint32_t* __restrict__ run_tiles) {
+    __shared__ uint32_t wc[kSortWaves];
+    const int64_t tile = blockIdx.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t heads = 0;
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t s = tile * kSortTile + slot * kSortThreads + threadIdx.x;
+        if (s < L) {
+            const int32_t ck = skey[s];
+            const int32_t prev = s > 0 ? skey[s - 1] : -1;
+            const int32_t next = s + 1 < L ? skey[s + 1] : -1;
+            const int32_t k = ck / M3;
+            sorted_i3[s] = ck - k * M3;
+            heads += (s == 0 || prev != ck) ? 1u : 0u;
+            if (s == 0 || prev / M3 != k) key_start[k] = (int32_t)s;
+            if (s + 1 == L || next / M3 != k) key_end[k] = (int32_t)(s + 1);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) heads += __shfl_xor(heads, o);
+    if (lane == 0) wc[w] = heads;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int i = 0; i < kSortWaves; ++i) t += wc[i];
+        run_tiles[tile] = t;
+    }
+}
+
+// Per key: (present << 32) | number of chunks (0 when absent).
+__device__ __forceinline__ uint64_t key_word(const int32_t* __restrict__ key_start,
+                                             const int32_t* __restrict__ key_end, int64_t k, int64_t K,
+                                             int32_t chunk) {
+    if (k >= K) return 0;
+    const int32_t st = key_start[k];
+    if (st < 0) return 0;
+    return (uint64_t(1) << 32) | (uint32_t)((key_end[k] - st + chunk - 1) / chunk);
+}
+
+// Per tile of keys: the sum of the key words (present keys, chunks).
+__global__ __launch_bounds__(kSortThreads) void k_key_tiles(const int32_t* __restrict__ key_start,
+                                                            const int32_t* __restrict__ key_end, int64_t K,
+                                                            int32_t chunk, uint64_t* __restrict__ key_tiles) {
+    __shared__ uint64_t wc[kSortWaves];
+    const int64_t tile = blockIdx.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint64_t v = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j)
+        v += key_word(key_start, key_end, tile * kSortTile + j * kSortThreads + threadIdx.x, K, chunk);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) wc[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int i = 0; i < kSortWaves; ++i) t += wc[i];
+        key_tiles[tile] = t;
+    }
+}
+
+// Per key: key_scan[k] = exclusive scan of the key words (group id << 32 |
+// first chunk); group tables for the present keys; the last tile writes the
+// totals (groups, chunks) and the closing entries of the group tables.
+template <bool DIRECT>
+__global__ __launch_bounds__(kSortThreads) void k_groups(const int32_t* __restrict__ key_start,
+                                                         const int32_t* __restrict__ key_end, int64_t K,
+                                                         int64_t L, int32_t chunk,
+                                                         const uint64_t* __restrict__ key_tiles,
+                                                         uint64_t* __restrict__ key_scan,
+                                                         int32_t* __restrict__ group_key,
+                                                         int32_t* __restrict__ group_start,
+                                                         int32_t* __restrict__ group_cbase, int32_t* ctrl) {
+    __shared__ uint64_t wsum[17];
+    __shared__ uint64_t sbase;
+    const int64_t tile = blockIdx.x;
+    tile_base<DIRECT, uint64_t>(key_tiles, tile, &sbase);
+    // thread t takes keys 4t .. 4t+3 of the tile
+    const int64_t k0 = tile * kSortTile + (int64_t)threadIdx.x * kSortItems;
+    uint64_t v[kSortItems];
+    uint64_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        v[j] = key_word(key_start, key_end, k0 + j, K, chunk);
+        sum += v[j];
+    }
+    uint64_t tot;
+    uint64_t run = block_exclusive_scan<uint64_t>(sum, wsum, &tot);   // synchronises
+    run += sbase;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const int64_t k = k0 + j;
+        if (k < K) {
+            key_scan[k] = run;
+            if (v[j]) {
+                const int32_t g = (int32_t)(run >> 32);
+                const int32_t c0 = (int32_t)(run & 0xffffffffu);
+                group_key[g] = (int32_t)k;
+                group_start[g] = key_start[k];
+                group_cbase[g] = c0;
+            }
+        }
+        run += v[j];
+    }
+    if (tile == (int64_t)gridDim.x - 1 && threadIdx.x == 0) {
+        const uint64_t all = sbase + tot;
+        const int32_t U = (int32_t)(all >> 32), NC = (int32_t)(all & 0xffffffffu);
         ctrl[CTRL_NUM_GROUPS] = U;
         ctrl[CTRL_NUM_CHUNKS] = NC;
         group_start[U] = (int32_t)L;
         group_cbase[U] = NC;
     }
-    if (k >= K) return;
-    const int32_t st = key_start[k];
-    if (st < 0) return;
-    const uint64_t v = scan[k];
-    const int32_t g = (int32_t)(v >> 32);
-    group_key[g] = (int32_t)k;
-    group_start[g] = st;
-    group_cbase[g] = (int32_t)(v & 0xffffffffu);
 }
 
-__device__ __forceinline__ int32_t group_of_chunk(const int32_t* __restrict__ group_cbase, int32_t U,
-                                                 int64_t c) {
-    int32_t lo = 0, hi = U;   // last g in [0, U) with cbase[g] <= c
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (group_cbase[mid] <= c) lo = mid; else hi = mid;
+// Row-run ids and tables over one tile of sorted positions (rid[s] = number
+// of row-run heads before s), and the chunk table: position s opens a chunk
+// when it lies a multiple of `chunk` past its group's start (chunk c of group
+// g starts `chunk` lookups after the previous one of g).
+template <bool DIRECT>
+__global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ skey,
+                                                       const uint64_t* __restrict__ key_scan,
+                                                       const int32_t* __restrict__ key_start,
+                                                       const int32_t* __restrict__ key_end,
+                                                       const uint32_t* __restrict__ run_tiles,
+                                                       int64_t L, int32_t M3, int32_t chunk, int32_t* ctrl,
+                                                       int32_t* __restrict__ rid,
+                                                       int32_t* __restrict__ run_i3,
+                                                       int32_t* __restrict__ run_of,
+                                                       int32_t* __restrict__ run_start,
+                                                       int32_t* __restrict__ group_rbase,
+                                                       int32_t* __restrict__ chunk_group,
+                                                       int32_t* __restrict__ chunk_begin,
+                                                       int32_t* __restrict__ chunk_end) {
+    const int64_t tile = blockIdx.x;
+    __shared__ uint32_t wsum[17];
+    __shared__ uint32_t sbase;
+    tile_base<DIRECT, uint32_t>(run_tiles, tile, &sbase);
+    // thread t takes positions 4t .. 4t+3 of the tile
+    const int64_t s0 = tile * kSortTile + (int64_t)threadIdx.x * kSortItems;
+    int32_t ck[kSortItems + 1];
+    ck[0] = s0 > 0 && s0 <= L ? skey[s0 - 1] : -1;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) ck[j + 1] = s0 + j < L ? skey[s0 + j] : -1;
+    uint32_t hr[kSortItems], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        hr[j] = (s0 + j < L && (s0 + j == 0 || ck[j] != ck[j + 1])) ? 1u : 0u;
+        sum += hr[j];
     }
-    return lo;
-}
-
-// Chunk table: chunk c of group g starts `chunk` lookups after the previous
-// one of g (the group's first chunk at the group's start).
-__global__ __launch_bounds__(256) void k_chunks(const int32_t* __restrict__ group_start,
-                                                const int32_t* __restrict__ group_cbase,
-                                                int64_t Cmax, int32_t chunk, int32_t* ctrl,
-                                                int32_t* __restrict__ chunk_group,
-                                                int32_t* __restrict__ chunk_begin,
-                                                int32_t* __restrict__ chunk_end) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int32_t NC = ctrl[CTRL_NUM_CHUNKS];
-    const int32_t U = ctrl[CTRL_NUM_GROUPS];
-    if (c >= Cmax || c >= NC) return;
-    const int32_t g = group_of_chunk(group_cbase, U, c);
-    const int32_t b = group_start[g] + (int32_t)(c - group_cbase[g]) * chunk;
-    chunk_group[c] = g;
-    chunk_begin[c] = b;
-    chunk_end[c] = min(b + chunk, group_start[g + 1]);
-}
-
-// Row-run tables from the scanned head flags. A row run is a maximal stretch
-// of one (key, i3) row in sorted order; after the scan, rid[s] holds the
-// number of row-run heads before sorted position s.
-__global__ __launch_bounds__(256) void k_runs(const int32_t* __restrict__ rid,
-                                              const int32_t* __restrict__ perm,
-                                              const int32_t* __restrict__ skey,
-                                              const int32_t* __restrict__ sorted_i3,
-                                              const uint64_t* __restrict__ key_scan, int64_t L,
-                                              int32_t M3, int32_t* ctrl,
-                                              int32_t* __restrict__ run_i3,
-                                              int32_t* __restrict__ run_of,
-                                              int32_t* __restrict__ run_start,
-                                              int32_t* __restrict__ group_rbase) {
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= L) return;
-    const int32_t rr = rid[s];
-    const int32_t hr = (s == 0 || skey[s - 1] != skey[s]) ? 1 : 0;
-    const int32_t k = skey[s] / M3;
-    if (hr) {
-        run_i3[rr] = sorted_i3[s];
-        run_start[rr] = (int32_t)s;
-    }
-    run_of[perm[s]] = rr + hr - 1;
-    if (s == 0 || skey[s - 1] / M3 != k) group_rbase[key_scan[k] >> 32] = rr;
-    if (s == L - 1) {
-        ctrl[CTRL_NUM_RUNS] = rr + hr;
-        group_rbase[ctrl[CTRL_NUM_GROUPS]] = rr + hr;
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan<uint32_t>(sum, wsum, &tot) + sbase;   // synchronises
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const int64_t s = s0 + j;
+        if (s < L) {
+            const int32_t rr = (int32_t)run;   // heads before s
+            rid[s] = rr;
+            const int32_t k = ck[j + 1] / M3;
+            if (hr[j]) {
+                run_i3[rr] = ck[j + 1] - k * M3;
+                run_start[rr] = (int32_t)s;
+            }
+            run_of[perm[s]] = rr + (int32_t)hr[j] - 1;
+            const int32_t off = (int32_t)s - key_start[k];
+            if (off % chunk == 0) {
+                const uint64_t ks = key_scan[k];
+                const int32_t g = (int32_t)(ks >> 32);
+                const int32_t c = (int32_t)(ks & 0xffffffffu) + off / chunk;
+                chunk_group[c] = g;
+                chunk_begin[c] = (int32_t)s;
+                chunk_end[c] = min((int32_t)s + chunk, key_end[k]);
+                if (off == 0) group_rbase[g] = rr;
+            }
+            if (s == L - 1) {
+                ctrl[CTRL_NUM_RUNS] = rr + (int32_t)hr[j];
+                group_rbase[ctrl[CTRL_NUM_GROUPS]] = rr + (int32_t)hr[j];
+            }
+        }
+        run += hr[j];
     }
 }
 
@@ -780,22 +1011,31 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         uint32_t* hist = p->at<uint32_t>(lay.hist);
         const int32_t* kin = p->at<int32_t>(lay.ckey);
         const int32_t* vin = nullptr;
+        const int32_t* bin = bag;
         for (int pass = 0; pass < P; ++pass) {
             // the last pass lands in (skey, perm); earlier passes alternate so that it does
             const bool to_final = ((P - 1 - pass) % 2) == 0;
             int32_t* kout = p->at<int32_t>(to_final ? lay.sort_k1 : lay.sort_k0);
             int32_t* vout = p->at<int32_t>(to_final ? lay.sort_v1 : lay.sort_v0);
+            int32_t* bout = p->at<int32_t>(to_final ? lay.sort_b1 : lay.sort_b0);
             const int shift = pass * kRadixBits;
             hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
-                               kin, L, shift, lay.n_tiles, hist);
+                               kin, L, shift, lay.n_tiles, lay.hstride, hist);
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-            if (scan_exclusive<uint32_t>(p, ++nscan, hist, (int64_t)kRadixBins * lay.n_tiles, nullptr, s) != TT_OK)
-                return fail(TT_ERR_HIP);
-            hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
-                               s, kin, vin, L, shift, lay.n_tiles, hist, kout, vout);
+            if (lay.n_tiles <= kDirectTiles) {
+                hipLaunchKernelGGL(k_radix_scatter<true>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
+                                   s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
+            } else {
+                if (scan_exclusive<uint32_t>(p, ++nscan, hist, (int64_t)kRadixBins * lay.hstride, nullptr, s) !=
+                    TT_OK)
+                    return fail(TT_ERR_HIP);
+                hipLaunchKernelGGL(k_radix_scatter<false>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
+                                   s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
+            }
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
             kin = kout;
             vin = vout;
+            bin = bout;
         }
     }
     // groups and chunks
@@ -803,37 +1043,36 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
         int32_t* key_start = p->at<int32_t>(lay.key_start);
         int32_t* key_end = p->at<int32_t>(lay.key_end);
         uint64_t* kscan = p->at<uint64_t>(lay.key_scan);
+        uint32_t* run_tiles = p->at<uint32_t>(lay.run_tiles);
+        uint64_t* key_tiles = p->at<uint64_t>(lay.key_tiles);
         if (L > 0) {
-            hipLaunchKernelGGL(k_gather, dim3(grid_for(L, 256)), dim3(256), 0, s,
-                               p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey), i3, bag, L,
-                               (int32_t)p->TB, p->M3, p->at<int32_t>(lay.sorted_i3), p->at<int32_t>(lay.sorted_bag),
-                               key_start, key_end, p->at<int32_t>(lay.rid));
+            hipLaunchKernelGGL(k_gather, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
+                               p->at<int32_t>(lay.skey), L, p->M3, p->at<int32_t>(lay.sorted_i3), key_start,
+                               key_end, run_tiles);
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
-        hipLaunchKernelGGL(k_key_flags, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start,
-                           key_end, K, chunk, kscan);
+        hipLaunchKernelGGL(k_key_tiles, dim3((unsigned)lay.n_ktiles), dim3(kSortThreads), 0, s, key_start,
+                           key_end, K, chunk, key_tiles);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-        if (scan_exclusive<uint64_t>(p, ++nscan, kscan, K, reinterpret_cast<uint64_t*>(ctrl + CTRL_SCAN_TOTAL),
-                                     s) != TT_OK)
+        const bool kdirect = lay.n_ktiles <= kDirectTiles;
+        if (!kdirect && scan_exclusive<uint64_t>(p, ++nscan, key_tiles, lay.n_ktiles, nullptr, s) != TT_OK)
             return fail(TT_ERR_HIP);
-        hipLaunchKernelGGL(k_groups, dim3(grid_for(K, 256)), dim3(256), 0, s, key_start, kscan, K,
-                           L, p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
+        hipLaunchKernelGGL(kdirect ? k_groups<true> : k_groups<false>, dim3((unsigned)lay.n_ktiles),
+                           dim3(kSortThreads), 0, s, key_start, key_end, K, L, chunk, key_tiles, kscan,
+                           p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
                            p->at<int32_t>(lay.group_cbase), ctrl);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-        if (lay.Cmax > 0) {
-            hipLaunchKernelGGL(k_chunks, dim3(grid_for(lay.Cmax, 256)), dim3(256), 0, s,
-                               p->at<int32_t>(lay.group_start), p->at<int32_t>(lay.group_cbase),
-                               lay.Cmax, chunk, ctrl, p->at<int32_t>(lay.chunk_group),
-                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
-            // row-run ids: exclusive scan of the head flags, then the run tables
-            if (scan_exclusive<uint32_t>(p, ++nscan, p->at<uint32_t>(lay.rid), L, nullptr, s) != TT_OK)
+        if (L > 0) {
+            const bool rdirect = lay.n_tiles <= kDirectTiles;
+            if (!rdirect && scan_exclusive<uint32_t>(p, ++nscan, run_tiles, lay.n_tiles, nullptr, s) != TT_OK)
                 return fail(TT_ERR_HIP);
-            hipLaunchKernelGGL(k_runs, dim3(grid_for(L, 256)), dim3(256), 0, s,
-                               p->at<int32_t>(lay.rid), p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
-                               p->at<int32_t>(lay.sorted_i3), p->at<uint64_t>(lay.key_scan), L, p->M3,
-                               ctrl, p->at<int32_t>(lay.run_i3), p->at<int32_t>(lay.run_of),
-                               p->at<int32_t>(lay.run_start), p->at<int32_t>(lay.group_rbase));
+            hipLaunchKernelGGL(rdirect ? k_runs<true> : k_runs<false>, dim3((unsigned)lay.n_tiles),
+                               dim3(kSortThreads), 0, s, p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
+                               p->at<uint64_t>(lay.key_scan), key_start, key_end, run_tiles, L, p->M3, chunk,
+                               ctrl, p->at<int32_t>(lay.rid), p->at<int32_t>(lay.run_i3),
+                               p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.run_start),
+                               p->at<int32_t>(lay.group_rbase), p->at<int32_t>(lay.chunk_group),
+                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         if (lay.NFB > 0) {

@@ -32,7 +32,6 @@ enum CtrlSlot : int {
     CTRL_NUM_CHUNKS = 2,
     CTRL_NUM_RUNS = 4,    // row runs
     CTRL_NUM_XPIECES = 5, // backward: extra run pieces of the groups split over several waves
-    CTRL_SCAN_TOTAL = 8,  // 64-bit slot (8..9): total of the last key scan
     CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
     CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
     CTRL_WORDS = 64
@@ -76,9 +75,14 @@ static_assert(sizeof(BatchRec) == 160, "BatchRec layout");
 
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kSortThreads = 256;                        // 4 waves
-constexpr int kSortItems = 16;                           // per thread
+constexpr int kSortThreads = 1024;                       // 16 waves
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortItems = 4;                            // per thread
 constexpr int kSortTile = kSortThreads * kSortItems;     // 4096 lookups per tile
+// Up to this many tiles, each scatter workgroup sums the per-tile digit counts
+// it needs itself; beyond, a device-wide scan of the counts runs between the
+// two kernels of a pass.
+constexpr int64_t kDirectTiles = 512;
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 4;
 constexpr int kScanTile = kScanThreads * kScanItems;     // 4096 per scan tile
@@ -118,10 +122,12 @@ struct Layout {
     size_t stage;                            // [L + kStageSpare][D] float, one row per row run: forward, the
                                              //     run's embedding row; backward, its grad-row sum
     size_t perm, sorted_i3, sorted_bag;      // [L]
-    size_t skey, sort_k0, sort_v0, sort_k1, sort_v1;  // [L] radix ping-pong
-    size_t hist;                             // [kRadixBins * n_tiles] uint32
+    size_t skey, sort_k0, sort_v0, sort_b0, sort_k1, sort_v1, sort_b1;  // [L] radix ping-pong
+    size_t hist;                             // [kRadixBins][hstride] uint32: digit counts per tile
     size_t key_start, key_end;               // [K] int32
     size_t key_scan;                         // [K] uint64
+    size_t run_tiles;                        // [n_tiles] uint32: row-run heads per tile of sorted positions
+    size_t key_tiles;                        // [n_ktiles] uint64: key words per tile of keys
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
@@ -134,7 +140,7 @@ struct Layout {
                                              //     cut by the backward's windows
     size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, K, Gmax, Cmax, NFB, scan_tiles;
+    int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles;
     int passes;
 };
 

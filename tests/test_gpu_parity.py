@@ -117,6 +117,19 @@ def test_plan_ragged_multitable():
         check_plan(dp, f"ragged chunk={chunk}")
 
 
+def test_plan_many_keys():
+    # 2.3M possible prefix keys: more key tiles than one workgroup adds up
+    # itself, so the key-tile totals take the device-wide scan
+    t = wl.Table(2_300_000, (2300, 1000, 1), (1, 2, 2), 2)
+    p = wl.make_custom([t], np.full(64, 40), seed=5)
+    for chunk in (1, 64):
+        say("plan many keys", chunk)
+        dp = DevProblem(p, chunk)
+        dp.make_plan()
+        check_plan(dp, f"many keys chunk={chunk}")
+    run_forward_check(p, "many keys")
+
+
 def test_device_error_flags():
     from tensor_train_compressed_amd import TT_FLAG_BAD_INDEX, TT_FLAG_BAD_OFFSETS, tt_emb_get_error
     t = wl.Table(1000, (10, 10, 10), (2, 2, 4), 4)
