@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 //
 // k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
 //               with atomics; fp64 keeps a sum of many cancelling terms within
-//               the fp32 tolerance) and lists the pieces of the large groups
+//               the fp32 tolerance) and the long-run counters of k_bwd_cross,
+//               and lists the pieces of the large groups
 // k_bwd_sum     one wave per window of 64 sorted positions: for every run,
 //               S = sum of the grad_out rows of its lookups, accumulated in
 //               fp64. A run inside one window is stored once, rounded to fp32;
@@ -181,22 +182,49 @@ struct CrossRef {
     int64_t L;
 };
 
-// The run cut by the end of window w when its head lies in w, else -1.
-__device__ __forceinline__ int32_t first_cut_run(const CrossRef& x, int64_t w) {
-    const int64_t e = (w + 1) * kWin;
-    if (e >= x.L || row_head(x.skey, e)) return -1;
-    const int32_t run = x.rid[e] - 1;
-    return x.run_start[run] >= e - kWin ? run : -1;
-}
-
 __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
                                                   double* __restrict__ dg3, int64_t n3,
+                                                  int32_t* __restrict__ xcnt, int64_t nwin,
+                                                  const int32_t* __restrict__ i3cnt, int32_t m3,
+                                                  int32_t* __restrict__ i3start,
                                                   const int32_t* __restrict__ group_rbase,
                                                   int32_t* __restrict__ xpiece, int32_t* ctrl) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    if (m3 > 0 && blockIdx.x == 0) {
+        // first run slot of each i3 bucket: exclusive scan of the planner's
+        // counts, four per thread (m3 <= 4 * 256)
+        static_assert(kMaxScanSlices3 <= 4 * 256, "one pass");
+        __shared__ int32_t wtot[4];
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        int32_t c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * threadIdx.x + j;
+            c[j] = i < m3 ? i3cnt[(int64_t)i * kI3Pad] : 0;
+            sum += c[j];
+        }
+        int32_t inc = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        int32_t run = inc - sum;
+        for (int ww = 0; ww < w; ++ww) run += wtot[ww];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * threadIdx.x + j;
+            if (i < m3) i3start[i] = run;
+            run += c[j];
+        }
+        if (threadIdx.x == 255) i3start[m3] = run;   // the total
+    }
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
+    for (int64_t i = tid; i < nwin; i += nth) xcnt[i] = 0;
     // groups of more than kRunRange runs are split into pieces of kRunRange
     // runs: list their pieces, a group's pieces together and in order (the
     // run kernel takes these first, then one piece per other group)
@@ -213,60 +241,132 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
     }
 }
 
-// S of the cut runs. A workgroup takes WV consecutive windows: wave v checks
-// window WV*b + v for a run that starts in it and runs past its end (all
-// checks at once), then the workgroup sums each found run in turn: its end
-// piece and the start pieces of the windows up to the one holding its last
-// lookup, in fp64 (the WV waves take every WV-th window, UNR loads in flight
-// each; a hot row's run spans hundreds of windows).
+// S of the cut runs. Windows go in spans of WV = 16 (one workgroup per
+// span, wave v on window 16*span + v). Wave v checks its window for a run that
+// starts in it and runs past its end (the check's loads go out in two
+// rounds). A run whose pieces lie in at most SHORT + 1 windows is summed by
+// that wave alone: its end piece plus the start pieces of the windows up to
+// the one holding its last lookup, all loads in flight at once, in fp64.
+// A longer run (a hot row, spanning up to thousands of windows) is summed by
+// every span it touches: each adds the start pieces of its own windows (one
+// per wave, added across the waves in LDS) into the run's end-piece slot with
+// fp64 device atomics, then counts itself in the run's counter; the span that
+// completes the count rounds the slot into the run's S row. At most one long
+// run starts in a span and at most one enters it from before.
 template <int DL>
-__global__ __launch_bounds__(1024) void k_bwd_cross(const double* __restrict__ xpart, CrossRef x,
-                                                    float* __restrict__ S, const int32_t* __restrict__ ctrl) {
-    constexpr int D = 64 * DL, UNR = 8, WV = 16;
+__global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, int32_t* __restrict__ xcnt,
+                                                    CrossRef x, float* __restrict__ S,
+                                                    const int32_t* __restrict__ ctrl) {
+    constexpr int D = 64 * DL, WV = 16, SHORT = 16;
+    static_assert(SHORT >= WV, "a long run leaves the span it starts in");
     __shared__ double red[WV][D];
-    __shared__ int32_t s_run[WV];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __shared__ int32_t s_run[2];      // long run that starts in the span / enters it (-1: none)
+    __shared__ int64_t s_hw[2], s_lw[2];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwin = (x.L + kWin - 1) / kWin;
     const int32_t NR = ctrl[CTRL_NUM_RUNS];
     for (int64_t w0 = (int64_t)blockIdx.x * WV; w0 < nwin; w0 += (int64_t)gridDim.x * WV) {
-        if (lane == 0) s_run[wv] = w0 + wv < nwin ? first_cut_run(x, w0 + wv) : -1;
-        __syncthreads();
-        for (int i = 0; i < WV; ++i) {
-            const int32_t run = s_run[i];
-            if (run < 0) continue;
-            const int64_t w = w0 + i;
-            const int64_t run_end = run + 1 < NR ? x.run_start[run + 1] : x.L;
-            const int64_t last = (run_end - 1) / kWin;
+        const int64_t w = w0 + wv;
+        const int64_t e = (w + 1) * kWin;   // first position after window w
+        int32_t run = -1;
+        int64_t last = 0;
+        if (e < x.L) {
+            const int32_t k0 = x.skey[e - 1], k1 = x.skey[e];
+            const int32_t r1 = x.rid[e];
+            if (k0 == k1) {   // the run holding position e - 1 continues past the window
+                const int32_t rr = r1 - 1;
+                const int32_t rs = x.run_start[rr];
+                const int64_t re = rr + 1 < NR ? x.run_start[rr + 1] : x.L;
+                if (rs >= e - kWin) {   // ... and starts in it
+                    run = rr;
+                    last = (re - 1) / kWin;
+                }
+            }
+        }
+        if (run >= 0 && last - w <= SHORT) {
+            double v[SHORT + 1][DL];
+#pragma unroll
+            for (int u = 0; u <= SHORT; ++u) {
+                const int64_t slot = u == 0 ? 2 * w + 1 : 2 * min(w + u, last);
+#pragma unroll
+                for (int k = 0; k < DL; ++k) v[u][k] = xpart[slot * D + lane * DL + k];
+            }
             double acc[DL];
 #pragma unroll
-            for (int k = 0; k < DL; ++k) acc[k] = wv == 0 ? xpart[(2 * w + 1) * D + lane * DL + k] : 0.0;
-            for (int64_t j0 = w + 1 + wv; j0 <= last; j0 += WV * UNR) {
-                double v[UNR][DL];
+            for (int k = 0; k < DL; ++k) acc[k] = v[0][k];
 #pragma unroll
-                for (int u = 0; u < UNR; ++u) {
-                    const int64_t j = min(j0 + WV * u, last);
+            for (int u = 1; u <= SHORT; ++u)
+                if (w + u <= last) {
 #pragma unroll
-                    for (int k = 0; k < DL; ++k) v[u][k] = xpart[2 * j * D + lane * DL + k];
+                    for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
                 }
+            float* dst = S + (int64_t)run * D + lane * DL;
 #pragma unroll
-                for (int u = 0; u < UNR; ++u)
-                    if (j0 + WV * u <= last) {
-#pragma unroll
-                        for (int k = 0; k < DL; ++k) acc[k] += v[u][k];
-                    }
+            for (int k = 0; k < DL; ++k) dst[k] = (float)acc[k];
+        }
+        if (wv == 0 && lane == 0) {
+            s_run[0] = -1;
+            s_run[1] = -1;
+            // the run holding the span's first position, when it started in
+            // an earlier span and is long
+            const int64_t f = w0 * kWin;
+            if (f > 0 && x.skey[f - 1] == x.skey[f]) {
+                const int32_t rr = x.rid[f] - 1;
+                const int64_t rs = x.run_start[rr];
+                const int64_t re = rr + 1 < NR ? x.run_start[rr + 1] : x.L;
+                const int64_t hw = rs / kWin, lw = (re - 1) / kWin;
+                if (lw - hw > SHORT) {
+                    s_run[1] = rr;
+                    s_hw[1] = hw;
+                    s_lw[1] = lw;
+                }
             }
+        }
+        __syncthreads();
+        if (run >= 0 && last - w > SHORT && lane == 0) {
+            s_run[0] = run;
+            s_hw[0] = w;
+            s_lw[0] = last;
+        }
+        __syncthreads();
 #pragma unroll
-            for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = acc[k];
+        for (int c = 0; c < 2; ++c) {
+            const int32_t lr = s_run[c];
+            if (lr < 0) continue;
+            const int64_t hw = s_hw[c], lw = s_lw[c];
+            // this span's windows holding start pieces of the run
+            const int64_t j = w0 + wv;
+            const bool mine = j > hw && j <= lw;
+#pragma unroll
+            for (int k = 0; k < DL; ++k) red[wv][lane * DL + k] = mine ? xpart[2 * j * D + lane * DL + k] : 0.0;
             __syncthreads();
-            for (int e = threadIdx.x; e < D; e += 64 * WV) {
-                double t = 0.0;
+            if (wv == 0) {
+                double* accp = xpart + (2 * hw + 1) * D + lane * DL;
 #pragma unroll
-                for (int k = 0; k < WV; ++k) t += red[k][e];
-                S[(int64_t)run * D + e] = (float)t;
+                for (int k = 0; k < DL; ++k) {
+                    double t = 0.0;
+#pragma unroll
+                    for (int i = 0; i < WV; ++i) t += red[i][lane * DL + k];
+                    atomicAdd(accp + k, t);
+                }
+                __threadfence();
+                int32_t done = 0;
+                if (lane == 0) {
+                    const int32_t need = (int32_t)(lw / WV - hw / WV + 1);
+                    done = atomicAdd(xcnt + hw, 1) == need - 1 ? 1 : 0;
+                }
+                if (__builtin_amdgcn_readfirstlane(done)) {
+                    __threadfence();
+                    float* dst = S + (int64_t)lr * D + lane * DL;
+#pragma unroll
+                    for (int k = 0; k < DL; ++k)
+                        dst[k] = (float)__hip_atomic_load(accp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             __syncthreads();
         }
-        __syncthreads();   // every wave is done with s_run before it is rewritten
+        __syncthreads();   // every wave is done with s_run before the next span rewrites it
     }
 }
 
@@ -293,7 +393,10 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t nwin = (a.L + kWin - 1) / kWin;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t w = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; w < nwin; w += nw) {
+    // the wave index is uniform: held in scalar registers, so the window's
+    // control flow below is scalar branches, not lane masks
+    const int64_t w0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t w = w0; w < nwin; w += nw) {
         const int64_t s0 = w * kWin;
         const int n = (int)min((int64_t)kWin, a.L - s0);
         const int64_t s1 = s0 + n;
@@ -410,12 +513,14 @@ struct RunsArgs {
 // One wave per piece (persistent, static stride), the group's P in registers;
 // four runs at a time (lane group q takes run t0 + q):
 //   dG3[i3] += P^T S          fp32 products over p, handed to add3 (device
-//                              atomics, or a row per run reduced later)
+//                              atomics, or a row per run reduced later) with
+//                              the word pre(run, i3) gave for the run at the
+//                              piece's start
 //   dP      += S G3[i3]^T     fp64 products and sums over the piece
 // then dP goes to the group's row (rounded to fp32), or, for a piece of a
 // split group, to the piece's own fp64 slot, which k_bwd_dpsum adds up.
-template <int N1, int N2, int R, int N3, class Add3>
-__device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
+template <int N1, int N2, int R, int N3, class Pre, class Add3>
+__device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3) {
     constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R, MT = NP / 16, RT = R / 16, KSP = NP / 4;
     constexpr int KQ = KSP / 4, CN = R * N3, W = kRunRange;
     static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64, "shape");
@@ -444,6 +549,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         const int32_t s = gs + W * part, e = min(ge, s + W);
         const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
         const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
+        const int32_t xl = pre(min(s + lane, e - 1), i3l);    // lane j: add3's word for run s + j
         doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -453,6 +559,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             const bool okq = t0 + q < e;
             const int32_t rq = okq ? t0 + q : t0;
             const int32_t i3q = __shfl(i3l, rq - s);
+            const int32_t xq = __shfl(xl, rq - s);
             const float* Sq = a.S + (int64_t)rq * D;
             const float* G3q = a.g3 + o3 + (int64_t)i3q * CN;
             floatx4 av[MT], bq[RT];
@@ -472,7 +579,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
 #pragma unroll
                 for (int s2 = 0; s2 < KSP; ++s2)
                     cc = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
-                if (okq) add3(o3 + (int64_t)i3q * CN, (16 * rt + col) * N3, rq, cc);
+                if (okq) add3(o3 + (int64_t)i3q * CN, (16 * rt + col) * N3, xq, cc);
             }
             // dP: K = (run q, j3 = step), fp64 products and sums (a hot
             // group's dP adds up hundreds of runs of large S); a run past the
@@ -509,21 +616,27 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
 // sharing their G3 slices' rows make this the general path)
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
-    runs_body<N1, N2, R, N3>(a, [&](int64_t row, int within, int32_t, const floatx4& c) {
+    runs_body<N1, N2, R, N3>(a, [](int32_t, int32_t) { return 0; },
+                             [&](int64_t row, int within, int32_t, const floatx4& c) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) atomicAdd(a.dg3 + row + within + v, (double)c[v]);
     });
 }
 
-// One table: each run's dG3 term P^T S is stored as its own row (c3[run]),
-// and k_bwd_dg3 sums them per G3 slice. Device atomics from every CU on the
+// One table: each run's dG3 term P^T S is stored as its own row, in the
+// bucket of its i3 (the planner ranked the runs inside their buckets), and
+// k_bwd_dg3 sums each bucket. Device atomics from every CU on the
 // same few hundred G3 slices saturate the memory-side atomic units, and LDS
 // float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3) {
+__global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3,
+                                                        const int32_t* __restrict__ i3start,
+                                                        const int32_t* __restrict__ run_rank) {
     constexpr int CN = R * N3;
-    runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
-        *reinterpret_cast<floatx4*>(c3 + (int64_t)run * CN + within) = c;
+    // add3's word: the run's row in its i3 bucket
+    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t i3) { return i3start[i3] + run_rank[run]; },
+                             [&](int64_t, int within, int32_t slot, const floatx4& c) {
+        *reinterpret_cast<floatx4*>(c3 + (int64_t)slot * CN + within) = c;
     });
 }
 
@@ -557,79 +670,45 @@ __global__ __launch_bounds__(256) void k_bwd_dpsum(const int32_t* __restrict__ x
     }
 }
 
-// dG3[i3] = sum of c3[run] over the runs with that i3, in fp64: one workgroup
-// per G3 slice i3. Each wave scans its share of the run i3 list a span of
-// SPAN runs at a time (16-byte loads, all of the span's in flight), lists the
-// matching runs in LDS, then gathers their rows GB at a time; the 16 waves'
-// sums are added in LDS at the end.
+// dG3[i3] = sum of the c3 rows of bucket i3 (the rows of the runs with that
+// i3, contiguous), in fp64: one workgroup per G3 slice, wave w on rows w,
+// w + 16, ... of the bucket, GB rows in flight; the 16 waves' sums are added
+// in LDS at the end.
 template <int CN>
-__global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ run_i3,
-                                                  const int32_t* __restrict__ ctrl,
+__global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3start,
                                                   const float* __restrict__ c3, float* __restrict__ dg3) {
-    constexpr int PL = CN / 64, UNR = 8, WAVES = 16, SPAN = 256 * UNR, GB = 8;
+    constexpr int PL = CN / 64, WAVES = 16, GB = 16;
     static_assert(CN % 64 == 0, "shape");
     __shared__ double red[WAVES][CN];
-    __shared__ int32_t list[WAVES][SPAN];
     const int32_t row = blockIdx.x;
-    const int64_t NR = ctrl[CTRL_NUM_RUNS];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int32_t* my = list[w];
+    const int32_t b = i3start[row], e = i3start[row + 1];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     double acc[PL];
 #pragma unroll
     for (int k = 0; k < PL; ++k) acc[k] = 0.0;
-    for (int64_t base = (int64_t)w * SPAN; base < NR; base += (int64_t)WAVES * SPAN) {
-        int32_t v[UNR][4];
+    for (int32_t j0 = b + w; j0 < e; j0 += WAVES * GB) {
+        float x[GB][PL];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int64_t r = base + 256 * u + 4 * lane;
-            if (r + 3 < NR) {
-                const int4 x = *reinterpret_cast<const int4*>(run_i3 + r);
-                v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
-            } else {
+        for (int j = 0; j < GB; ++j) {
+            const float* src = c3 + (int64_t)min(j0 + WAVES * j, e - 1) * CN + lane * PL;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v[u][c] = r + c < NR ? run_i3[r + c] : -1;
-            }
+            for (int k = 0; k < PL; ++k) x[j][k] = src[k];
         }
-        // list this span's matches (span offsets), in any order
-        int n = 0;
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
+        for (int j = 0; j < GB; ++j)
+            if (j0 + WAVES * j < e) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool hit = v[u][c] == row;
-                const uint64_t m = __ballot(hit);
-                if (hit) my[n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-                    256 * u + 4 * lane + c;
-                n += __builtin_popcountll(m);
+                for (int k = 0; k < PL; ++k) acc[k] += (double)x[j][k];
             }
-        wave_lds_sync();
-        for (int j0 = 0; j0 < n; j0 += GB) {
-            float x[GB][PL];
-#pragma unroll
-            for (int j = 0; j < GB; ++j) {
-                const int32_t off = my[min(j0 + j, n - 1)];
-                const float* src = c3 + (base + off) * CN + lane * PL;
-#pragma unroll
-                for (int k = 0; k < PL; ++k) x[j][k] = src[k];
-            }
-#pragma unroll
-            for (int j = 0; j < GB; ++j)
-                if (j0 + j < n) {
-#pragma unroll
-                    for (int k = 0; k < PL; ++k) acc[k] += (double)x[j][k];
-                }
-        }
-        wave_lds_sync();
     }
 #pragma unroll
     for (int k = 0; k < PL; ++k) red[w][lane * PL + k] = acc[k];
     __syncthreads();
-    for (int e = threadIdx.x; e < CN; e += 1024) {
+    for (int t = threadIdx.x; t < CN; t += 1024) {
         double x = 0.0;
 #pragma unroll
-        for (int k = 0; k < WAVES; ++k) x += red[k][e];
-        dg3[(int64_t)row * CN + e] = (float)x;
+        for (int k = 0; k < WAVES; ++k) x += red[k][t];
+        dg3[(int64_t)row * CN + t] = (float)x;
     }
 }
 
@@ -810,6 +889,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     constexpr int PR = N1 * N2 * R;
     const int64_t nwin = (p->L + kWin - 1) / kWin;
     hipLaunchKernelGGL(k_bwd_prep, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
+                       p->at<int32_t>(p->lay.xcnt), nwin, p->at<int32_t>(p->lay.i3cnt),
+                       scan3 ? p->tables[0].m[2] : 0, p->at<int32_t>(p->lay.i3start),
                        p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
@@ -819,7 +900,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
         TT_LAUNCH_CHECK();
         hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024)),
-                           dim3(1024), 0, s, xpart, xr, p->at<float>(p->lay.stage), p->ctrl());
+                           dim3(1024), 0, s, xpart, p->at<int32_t>(p->lay.xcnt), xr, p->at<float>(p->lay.stage),
+                           p->ctrl());
         TT_LAUNCH_CHECK();
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
@@ -835,10 +917,11 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart)};
         if (scan3) {
             hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
-                               p->at<float>(p->lay.c3));
+                               p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.i3start),
+                               p->at<int32_t>(p->lay.run_rank));
             TT_LAUNCH_CHECK();
             hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->tables[0].m[2]), dim3(1024), 0, s,
-                               p->at<int32_t>(p->lay.run_i3), p->ctrl(), p->at<float>(p->lay.c3),
+                               p->at<int32_t>(p->lay.i3start), p->at<float>(p->lay.c3),
                                dg3 + p->tables[0].g_offset[2]);
         } else {
             hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);

@@ -22,7 +22,7 @@
 //                     per tile (the sorted bags come out of the sort)
 //   k_key_tiles       present keys and chunks per tile of keys
 //   k_groups          key scan (group id and first chunk of every key), group tables
-//   k_runs            row-run ids and tables, chunk table
+//   k_runs            row-run ids and tables, chunk table; runs per i3 (one table)
 //   k_batches         one record per forward batch (kFwdBatch groups of one slice)
 // A device-wide scan of the tile totals runs before k_radix_scatter, k_groups
 // or k_runs only when there are more than kDirectTiles tiles.
@@ -105,6 +105,10 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     // fp64 pieces of the row runs cut by the backward's 64-position windows:
     // two slots per window (its start piece and its end piece)
     y.xsum = take(sizeof(double) * 2 * (size_t)((L + 63) / 64) * (size_t)D);
+    y.xcnt = take(sizeof(int32_t) * (size_t)((L + 63) / 64));
+    y.i3cnt = take(sizeof(int32_t) * (size_t)M3 * kI3Pad);
+    y.i3start = take(sizeof(int32_t) * (size_t)(M3 + 1));
+    y.run_rank = take(sizeof(int32_t) * (size_t)L);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
@@ -174,9 +178,10 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
                                                int32_t* __restrict__ bag_start,
                                                int32_t* __restrict__ ckey, int32_t M3,
                                                int32_t* ctrl, int32_t* __restrict__ key_start,
-                                               int64_t K) {
+                                               int64_t K, int32_t* __restrict__ i3cnt, int32_t n3cnt) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < K) key_start[i] = -1;   // k_gather records each present key's first position
+    if (i < n3cnt) i3cnt[i * kI3Pad] = 0;   // k_runs counts the runs of each i3
     if (i <= TB) {
         const int64_t a = off[i];
         bag_start[i] = (int32_t)(a < 0 ? 0 : (a > L ? L : a));
@@ -750,7 +755,11 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int32_t* __restrict__ group_rbase,
                                                        int32_t* __restrict__ chunk_group,
                                                        int32_t* __restrict__ chunk_begin,
-                                                       int32_t* __restrict__ chunk_end) {
+                                                       int32_t* __restrict__ chunk_end,
+                                                       int32_t* __restrict__ i3cnt, int32_t n3cnt,
+                                                       int32_t* __restrict__ run_rank) {
+    __shared__ uint32_t sh3[kMaxScanSlices3];
+    for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
     const int64_t tile = blockIdx.x;
     __shared__ uint32_t wsum[17];
     __shared__ uint32_t sbase;
@@ -769,6 +778,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
     }
     uint32_t tot;
     uint32_t run = block_exclusive_scan<uint32_t>(sum, wsum, &tot) + sbase;   // synchronises
+    uint32_t lrank[kSortItems];
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const int64_t s = s0 + j;
@@ -777,8 +787,10 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
             rid[s] = rr;
             const int32_t k = ck[j + 1] / M3;
             if (hr[j]) {
-                run_i3[rr] = ck[j + 1] - k * M3;
+                const int32_t r3 = ck[j + 1] - k * M3;
+                run_i3[rr] = r3;
                 run_start[rr] = (int32_t)s;
+                if (n3cnt) lrank[j] = atomicAdd(&sh3[r3], 1u);   // rank among the tile's runs of r3
             }
             run_of[perm[s]] = rr + (int32_t)hr[j] - 1;
             const int32_t off = (int32_t)s - key_start[k];
@@ -797,6 +809,23 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
             }
         }
         run += hr[j];
+    }
+    if (n3cnt) {
+        // one counter claim per (tile, i3): the tile's runs of i3 take the
+        // next sh3[i3] ranks of the bucket (buckets fill in any tile order)
+        __syncthreads();
+        for (int i = threadIdx.x; i < n3cnt; i += kSortThreads)
+            if (sh3[i]) sh3[i] = (uint32_t)atomicAdd(i3cnt + (int64_t)i * kI3Pad, (int32_t)sh3[i]);
+        __syncthreads();
+        uint32_t r = run - sum;   // heads before this thread's first position
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            if (s0 + j < L && hr[j]) {
+                const int32_t r3 = ck[j + 1] - (ck[j + 1] / M3) * M3;
+                run_rank[r] = (int32_t)(sh3[r3] + lrank[j]);
+            }
+            r += hr[j];
+        }
     }
 }
 
@@ -992,17 +1021,20 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     }
 
     int32_t* ctrl = p->ctrl();
+    // runs per i3 are counted for the backward's dG3 reduction (one table of
+    // at most kMaxScanSlices3 G3 slices)
+    const int32_t n3cnt = (T == 1 && tables[0].m[2] <= kMaxScanSlices3) ? tables[0].m[2] : 0;
     int32_t* key = p->at<int32_t>(lay.key);
     int32_t* i3 = p->at<int32_t>(lay.i3);
     int32_t* bag = p->at<int32_t>(lay.bag_of);
     // split (also checks the offsets and marks every key absent; one thread per
     // lookup, per offset and per key)
     {
-        const int64_t n = std::max<int64_t>(std::max<int64_t>(L, p->TB + 1), K);
+        const int64_t n = std::max<int64_t>(std::max<int64_t>(std::max<int64_t>(L, p->TB + 1), K), n3cnt);
         hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
                            p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
                            p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
-                           ctrl, p->at<int32_t>(lay.key_start), K);
+                           ctrl, p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt);
         if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
     }
     // stable radix sort: key -> (skey, perm)
@@ -1072,7 +1104,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                ctrl, p->at<int32_t>(lay.rid), p->at<int32_t>(lay.run_i3),
                                p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.run_start),
                                p->at<int32_t>(lay.group_rbase), p->at<int32_t>(lay.chunk_group),
-                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end));
+                               p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
+                               p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank));
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         if (lay.NFB > 0) {

@@ -52,6 +52,7 @@ constexpr int kRunRange = 32;
 // from per-run terms (one workgroup per slice scans the run list) instead of
 // with device atomics.
 constexpr int kMaxScanSlices3 = 1024;
+constexpr int kI3Pad = 32;   // int32 words per i3 counter (one 128-byte line each)
 // LDS the batch kernels may spend on the run i3 list of one batch
 // (kFwdBatch * largest m3 int32 values); larger m3 takes the generic kernels.
 constexpr int kMaxBatchI3Bytes = 32768;
@@ -138,6 +139,11 @@ struct Layout {
                                              //     dG3 accumulated in fp64 by the backward
     size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
                                              //     cut by the backward's windows
+    size_t xcnt;                             // [ceil(L/64)] int32: spans done per long cut run
+    // one table with m3 <= kMaxScanSlices3: the backward's c3 rows are bucketed by i3
+    size_t i3cnt;                            // [M3][kI3Pad] int32: runs per i3 (one counter per line)
+    size_t i3start;                          // [M3 + 1] int32: exclusive scan of the counts
+    size_t run_rank;                         // [L] int32: rank of each run inside its i3 bucket
     size_t batch;                            // [NFB] BatchRec
     size_t total;
     int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles;
