@@ -175,6 +175,16 @@ __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64
 // runs past w's end goes to slot 2w + 1. No two pieces share a slot.
 constexpr int kWin = 64;
 
+// Waits until every memory access this wave has issued has completed (for
+// device-scope stores and atomics: performed at the level all XCDs share).
+// Used before a completion count is claimed, in place of a device-scope
+// release fence, which on this chip also writes back the whole L2.
+__device__ __forceinline__ void wait_vmem_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 struct CrossRef {
     const int32_t* skey;
     const int32_t* rid;
@@ -188,7 +198,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
                                                   const int32_t* __restrict__ i3cnt, int32_t m3,
                                                   int32_t* __restrict__ i3start,
                                                   const int32_t* __restrict__ group_rbase,
-                                                  int32_t* __restrict__ xpiece, int32_t* ctrl) {
+                                                  int32_t* __restrict__ xpiece, int32_t* __restrict__ gdone,
+                                                  int32_t* ctrl) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     if (m3 > 0 && blockIdx.x == 0) {
@@ -230,6 +241,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
     // run kernel takes these first, then one piece per other group)
     const int64_t U = ctrl[CTRL_NUM_GROUPS];
     for (int64_t g = tid; g < U; g += nth) {
+        gdone[g] = 0;
         const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
         if (np > 1) {
             const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np);
@@ -350,14 +362,17 @@ __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, 
                     for (int i = 0; i < WV; ++i) t += red[i][lane * DL + k];
                     atomicAdd(accp + k, t);
                 }
-                __threadfence();
+                // counted once the adds have completed (device atomics are
+                // performed at the level all XCDs share; no device-scope
+                // fence, which would write back the whole L2)
+                wait_vmem_done();
                 int32_t done = 0;
                 if (lane == 0) {
                     const int32_t need = (int32_t)(lw / WV - hw / WV + 1);
                     done = atomicAdd(xcnt + hw, 1) == need - 1 ? 1 : 0;
                 }
                 if (__builtin_amdgcn_readfirstlane(done)) {
-                    __threadfence();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     float* dst = S + (int64_t)lr * D + lane * DL;
 #pragma unroll
                     for (int k = 0; k < DL; ++k)
@@ -508,6 +523,7 @@ struct RunsArgs {
     double* dg3;
     float* dpg;
     double* dpart;
+    int32_t* gdone;   // per group: pieces finished (zeroed by k_bwd_prep)
 };
 
 // One wave per piece (persistent, static stride), the group's P in registers;
@@ -518,12 +534,14 @@ struct RunsArgs {
 //                              piece's start
 //   dP      += S G3[i3]^T     fp64 products and sums over the piece
 // then dP goes to the group's row (rounded to fp32), or, for a piece of a
-// split group, to the piece's own fp64 slot, which k_bwd_dpsum adds up.
+// split group, to the piece's own fp64 slot; the group's last piece to finish
+// (a counter per group) adds the group's slots in piece order and rounds the
+// sum into the group's row once.
 template <int N1, int N2, int R, int N3, class Pre, class Add3>
 __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3) {
     constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R, MT = NP / 16, RT = R / 16, KSP = NP / 4;
     constexpr int KQ = KSP / 4, CN = R * N3, W = kRunRange;
-    static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64, "shape");
+    static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64 && PR % 256 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
     const int32_t U = a.ctrl[CTRL_NUM_GROUPS], X = a.ctrl[CTRL_NUM_XPIECES];
@@ -606,9 +624,34 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int idx = (16 * mt + q + 4 * v) * R + 16 * nt + col;
-                    if (split) dpp[idx] = dacc[mt][nt][v];
-                    else dst[idx] = (float)dacc[mt][nt][v];
+                    if (split)   // device-scope stores: written through to the level all XCDs share
+                        __hip_atomic_store(dpp + idx, dacc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        dst[idx] = (float)dacc[mt][nt][v];
                 }
+        if (split) {
+            // count the piece once its slot's stores have completed (a wait,
+            // not a device-scope fence: that one writes back the whole L2)
+            const int32_t np = (ge - gs + W - 1) / W;
+            wait_vmem_done();
+            int32_t done = 0;
+            if (lane == 0) done = atomicAdd(a.gdone + g, 1) == np - 1 ? 1 : 0;
+            if (__builtin_amdgcn_readfirstlane(done)) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                const double* first = a.dpart + (k - part) * PR;   // the group's pieces are listed in order
+                for (int e0 = 0; e0 < PR; e0 += 64 * 4) {
+                    double t[4] = {0.0, 0.0, 0.0, 0.0};
+                    for (int32_t j = 0; j < np; ++j) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            t[u] += __hip_atomic_load(first + (int64_t)j * PR + e0 + 64 * u + lane, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) dst[e0 + 64 * u + lane] = (float)t[u];
+                }
+            }
+        }
     }
 }
 
@@ -638,36 +681,6 @@ __global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __res
                              [&](int64_t, int within, int32_t slot, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)slot * CN + within) = c;
     });
-}
-
-// dP rows of the split groups: the fp64 sum of their pieces' slots, rounded
-// once. One thread per (listed piece 0, element); a group's pieces are listed
-// together and in order. Eight piece loads in flight per thread.
-template <int PR>
-__global__ __launch_bounds__(256) void k_bwd_dpsum(const int32_t* __restrict__ xpiece,
-                                                   const int32_t* __restrict__ group_rbase,
-                                                   const int32_t* __restrict__ ctrl,
-                                                   const double* __restrict__ dpart, float* __restrict__ dpg) {
-    constexpr int UNR = 8;
-    const int64_t X = ctrl[CTRL_NUM_XPIECES];
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < X * PR; t += nth) {
-        const int64_t k = t / PR;
-        const int e = (int)(t - k * PR);
-        if (xpiece[2 * k + 1] != 0) continue;
-        const int32_t g = xpiece[2 * k];
-        const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
-        double acc = 0.0;
-        for (int32_t j0 = 0; j0 < np; j0 += UNR) {
-            double v[UNR];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) v[u] = dpart[(k + min(j0 + u, np - 1)) * PR + e];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u)
-                if (j0 + u < np) acc += v[u];
-        }
-        dpg[(int64_t)g * PR + e] = (float)acc;
-    }
 }
 
 // dG3[i3] = sum of the c3 rows of bucket i3 (the rows of the runs with that
@@ -891,7 +904,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     hipLaunchKernelGGL(k_bwd_prep, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
                        p->at<int32_t>(p->lay.xcnt), nwin, p->at<int32_t>(p->lay.i3cnt),
                        scan3 ? p->tables[0].m[2] : 0, p->at<int32_t>(p->lay.i3start),
-                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->ctrl());
+                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece),
+                       p->at<int32_t>(p->lay.gdone), p->ctrl());
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
         const bool kept = p->p_kept && p->kept_g1 == g1 && p->kept_g2 == g2;
@@ -914,7 +928,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece),
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
-                    acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart)};
+                    acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart), p->at<int32_t>(p->lay.gdone)};
         if (scan3) {
             hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
                                p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.i3start),
@@ -926,10 +940,6 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         } else {
             hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
-        TT_LAUNCH_CHECK();
-        hipLaunchKernelGGL((k_bwd_dpsum<PR>), dim3(2048), dim3(256), 0, s, p->at<int32_t>(p->lay.xpiece),
-                           p->at<int32_t>(p->lay.group_rbase), p->ctrl(), p->at<double>(p->lay.dpart),
-                           p->at<float>(p->lay.dpg));
         TT_LAUNCH_CHECK();
     }
     {

@@ -97,6 +97,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
     // dL/dP per group, only for shapes the matrix-core backward serves
     y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
+    y.gdone = take(sizeof(int32_t) * (size_t)y.Gmax);
     y.pbuf = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);

@@ -132,6 +132,7 @@ struct Layout {
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
     size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
+    size_t gdone;                            // [Gmax] int32: pieces of a split group finished (backward)
     size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group (backward),
                                              //     in the lane order of the matrix-core operands
     size_t c3;                               // [L][R*n3] float, one table only: P^T S per run

@@ -296,6 +296,19 @@ def test_backward_ragged():
         _check_backward(p, f"ragged chunk={chunk}", chunk=chunk)
 
 
+@pytest.mark.parametrize("m3", [1024, 1025])
+def test_backward_i3_bucket_limit(m3):
+    # m3 = 1024: dG3 from the run rows bucketed by i3; 1025: device atomics.
+    # L = 4097 lookups: one full sort tile and a ragged one; Zipf indices so
+    # rows repeat inside groups.
+    t = wl.Table(4 * 5 * m3, (4, 5, m3), (4, 8, 4), 32)
+    lens = np.full(97, 42, np.int64)
+    lens[-1] += 4097 - int(lens.sum())
+    p = wl.make_custom([t], lens, seed=6, zipf_alpha=1.05, with_grad=True)
+    assert p.L == 4097
+    _check_backward(p, f"m3={m3} L=4097", chunk=64)
+
+
 def _slice_mask(p, pl, which, picks):
     """Mask of lookups whose core-`which` digit is in picks (single table)."""
     t = p.tables[0]
