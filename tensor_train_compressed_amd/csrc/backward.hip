@@ -135,10 +135,11 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 // tables). The kernels, all on row runs (one run per distinct table row of a
 // group, the same runs the forward contracts):
 //
-// k_bwd_prep    zeroes the fp64 accumulators of dG1 and dG3 (the targets added
-//               with atomics; fp64 keeps a sum of many cancelling terms within
-//               the fp32 tolerance) and the long-run counters of k_bwd_cross,
-//               and lists the pieces of the large groups
+// bwd_prep      (the first workgroups of the k_bwd_sum launch) zeroes the
+//               fp64 accumulators of dG1 and dG3 (the targets added with
+//               atomics; fp64 keeps a sum of many cancelling terms within the
+//               fp32 tolerance) and the completion counters, scans the runs
+//               per i3, and lists the pieces of the large groups
 // k_bwd_sum     one wave per window of 64 sorted positions: for every run,
 //               S = sum of the grad_out rows of its lookups, accumulated in
 //               fp64. A run inside one window is stored once, rounded to fp32;
@@ -192,17 +193,35 @@ struct CrossRef {
     int64_t L;
 };
 
-__global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int64_t n1,
-                                                  double* __restrict__ dg3, int64_t n3,
-                                                  int32_t* __restrict__ xcnt, int64_t nwin,
-                                                  const int32_t* __restrict__ i3cnt, int32_t m3,
-                                                  int32_t* __restrict__ i3start,
-                                                  const int32_t* __restrict__ group_rbase,
-                                                  int32_t* __restrict__ xpiece, int32_t* __restrict__ gdone,
-                                                  int32_t* ctrl) {
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    if (m3 > 0 && blockIdx.x == 0) {
+struct PrepArgs {
+    double* dg1;
+    int64_t n1;
+    double* dg3;
+    int64_t n3;
+    int32_t* xcnt;
+    int64_t nwin;
+    const int32_t* i3cnt;
+    int32_t m3;
+    int32_t* i3start;
+    const int32_t* group_rbase;
+    int32_t* xpiece;
+    int32_t* gdone;
+    int32_t* ctrl;
+};
+
+// The backward's set-up, run by the first kPrepBlocks workgroups of the
+// grad-sum launch (nothing it writes is read before the kernels after it).
+constexpr int kPrepBlocks = 256;
+
+__device__ __forceinline__ void bwd_prep(const PrepArgs& pa, int64_t blk) {
+    double* __restrict__ dg1 = pa.dg1;
+    double* __restrict__ dg3 = pa.dg3;
+    const int64_t n1 = pa.n1, n3 = pa.n3, nwin = pa.nwin;
+    const int32_t m3 = pa.m3;
+    int32_t* ctrl = pa.ctrl;
+    const int64_t tid = blk * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)kPrepBlocks * blockDim.x;
+    if (m3 > 0 && blk == 0) {
         // first run slot of each i3 bucket: exclusive scan of the planner's
         // counts, four per thread (m3 <= 4 * 256)
         static_assert(kMaxScanSlices3 <= 4 * 256, "one pass");
@@ -212,7 +231,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = 4 * threadIdx.x + j;
-            c[j] = i < m3 ? i3cnt[(int64_t)i * kI3Pad] : 0;
+            c[j] = i < m3 ? pa.i3cnt[(int64_t)i * kI3Pad] : 0;
             sum += c[j];
         }
         int32_t inc = sum;
@@ -228,26 +247,26 @@ __global__ __launch_bounds__(256) void k_bwd_prep(double* __restrict__ dg1, int6
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = 4 * threadIdx.x + j;
-            if (i < m3) i3start[i] = run;
+            if (i < m3) pa.i3start[i] = run;
             run += c[j];
         }
-        if (threadIdx.x == 255) i3start[m3] = run;   // the total
+        if (threadIdx.x == 255) pa.i3start[m3] = run;   // the total
     }
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
-    for (int64_t i = tid; i < nwin; i += nth) xcnt[i] = 0;
+    for (int64_t i = tid; i < nwin; i += nth) pa.xcnt[i] = 0;
     // groups of more than kRunRange runs are split into pieces of kRunRange
     // runs: list their pieces, a group's pieces together and in order (the
     // run kernel takes these first, then one piece per other group)
     const int64_t U = ctrl[CTRL_NUM_GROUPS];
     for (int64_t g = tid; g < U; g += nth) {
-        gdone[g] = 0;
-        const int32_t np = (group_rbase[g + 1] - group_rbase[g] + kRunRange - 1) / kRunRange;
+        pa.gdone[g] = 0;
+        const int32_t np = (pa.group_rbase[g + 1] - pa.group_rbase[g] + kRunRange - 1) / kRunRange;
         if (np > 1) {
             const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np);
             for (int32_t k = 0; k < np; ++k) {
-                xpiece[2 * (base + k)] = (int32_t)g;
-                xpiece[2 * (base + k) + 1] = k;
+                pa.xpiece[2 * (base + k)] = (int32_t)g;
+                pa.xpiece[2 * (base + k) + 1] = k;
             }
         }
     }
@@ -403,14 +422,19 @@ struct SumArgs {
 // when it starts and ends in the window, otherwise its piece goes to its
 // fp64 slot (no atomics: every slot has one writer).
 template <int DL>
-__global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a) {
+__global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
     constexpr int D = 64 * DL, FL = 32;   // grad_out rows in flight
+    if (blockIdx.x < kPrepBlocks) {
+        bwd_prep(pa, blockIdx.x);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const int64_t nwin = (a.L + kWin - 1) / kWin;
-    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t nw = ((int64_t)(gridDim.x - kPrepBlocks) * blockDim.x) >> 6;
     // the wave index is uniform: held in scalar registers, so the window's
     // control flow below is scalar branches, not lane masks
-    const int64_t w0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t w0 = (int64_t)(blockIdx.x - kPrepBlocks) * (blockDim.x >> 6) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int64_t w = w0; w < nwin; w += nw) {
         const int64_t s0 = w * kWin;
         const int n = (int)min((int64_t)kWin, a.L - s0);
@@ -523,7 +547,7 @@ struct RunsArgs {
     double* dg3;
     float* dpg;
     double* dpart;
-    int32_t* gdone;   // per group: pieces finished (zeroed by k_bwd_prep)
+    int32_t* gdone;   // per group: pieces finished (zeroed by bwd_prep)
 };
 
 // One wave per piece (persistent, static stride), the group's P in registers;
@@ -901,18 +925,18 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                       p->at<int32_t>(p->lay.run_start), p->L};
     constexpr int PR = N1 * N2 * R;
     const int64_t nwin = (p->L + kWin - 1) / kWin;
-    hipLaunchKernelGGL(k_bwd_prep, dim3(512), dim3(256), 0, s, acc1, p->extent[0], acc3, p->extent[2],
-                       p->at<int32_t>(p->lay.xcnt), nwin, p->at<int32_t>(p->lay.i3cnt),
-                       scan3 ? p->tables[0].m[2] : 0, p->at<int32_t>(p->lay.i3start),
-                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece),
-                       p->at<int32_t>(p->lay.gdone), p->ctrl());
+    // set-up (first kPrepBlocks workgroups) and the grad-row sums in one launch
+    const PrepArgs pa{acc1, p->extent[0], acc3, p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
+                      p->at<int32_t>(p->lay.i3cnt), scan3 ? p->tables[0].m[2] : 0, p->at<int32_t>(p->lay.i3start),
+                      p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece),
+                      p->at<int32_t>(p->lay.gdone), p->ctrl()};
+    const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
+                     p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
+    hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
+                       sa, pa);
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
         const bool kept = p->p_kept && p->kept_g1 == g1 && p->kept_g2 == g2;
-        SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
-                   p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
-        hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(persistent_grid(4)), dim3(256), 0, s, sa);
-        TT_LAUNCH_CHECK();
         hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024)),
                            dim3(1024), 0, s, xpart, p->at<int32_t>(p->lay.xcnt), xr, p->at<float>(p->lay.stage),
                            p->ctrl());
