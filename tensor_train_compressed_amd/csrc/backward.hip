@@ -222,35 +222,41 @@ __device__ __forceinline__ void bwd_prep(const PrepArgs& pa, int64_t blk) {
     const int64_t tid = blk * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)kPrepBlocks * blockDim.x;
     if (m3 > 0 && blk == 0) {
-        // first run slot of each i3 bucket: exclusive scan of the planner's
-        // counts, four per thread (m3 <= 4 * 256)
-        static_assert(kMaxScanSlices3 <= 4 * 256, "one pass");
+        // first run slot of each dG3 bucket: exclusive scan of the planner's
+        // counts, 1024 at a time (four per thread)
         __shared__ int32_t wtot[4];
+        __shared__ int32_t carry;
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        int32_t c[4], sum = 0;
+        if (threadIdx.x == 0) carry = 0;
+        for (int base = 0; base < m3; base += 4 * 256) {
+            int32_t c[4], sum = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * threadIdx.x + j;
-            c[j] = i < m3 ? pa.i3cnt[(int64_t)i * kI3Pad] : 0;
-            sum += c[j];
-        }
-        int32_t inc = sum;
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + 4 * threadIdx.x + j;
+                c[j] = i < m3 ? pa.i3cnt[(int64_t)i * kI3Pad] : 0;
+                sum += c[j];
+            }
+            int32_t inc = sum;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int32_t y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        if (lane == 63) wtot[w] = inc;
-        __syncthreads();
-        int32_t run = inc - sum;
-        for (int ww = 0; ww < w; ++ww) run += wtot[ww];
+            for (int o = 1; o < 64; o <<= 1) {
+                const int32_t y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            if (lane == 63) wtot[w] = inc;
+            __syncthreads();
+            int32_t run = carry + inc - sum;
+            for (int ww = 0; ww < w; ++ww) run += wtot[ww];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * threadIdx.x + j;
-            if (i < m3) pa.i3start[i] = run;
-            run += c[j];
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + 4 * threadIdx.x + j;
+                if (i < m3) pa.i3start[i] = run;
+                run += c[j];
+            }
+            __syncthreads();   // every thread has read carry and wtot
+            if (threadIdx.x == 255) carry = run;
+            __syncthreads();
         }
-        if (threadIdx.x == 255) pa.i3start[m3] = run;   // the total
+        if (threadIdx.x == 0) pa.i3start[m3] = carry;   // the total
     }
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
@@ -591,7 +597,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
         const int32_t s = gs + W * part, e = min(ge, s + W);
         const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
         const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
-        const int32_t xl = pre(min(s + lane, e - 1), i3l);    // lane j: add3's word for run s + j
+        const int32_t xl = pre(min(s + lane, e - 1), (int32_t)(o3 / CN) + i3l);   // lane j: add3's word for run s + j
         doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -700,8 +706,8 @@ __global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __res
                                                         const int32_t* __restrict__ i3start,
                                                         const int32_t* __restrict__ run_rank) {
     constexpr int CN = R * N3;
-    // add3's word: the run's row in its i3 bucket
-    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t i3) { return i3start[i3] + run_rank[run]; },
+    // add3's word: the run's row in the bucket of its G3 row
+    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t b3) { return i3start[b3] + run_rank[run]; },
                              [&](int64_t, int within, int32_t slot, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)slot * CN + within) = c;
     });
@@ -909,12 +915,13 @@ template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
                                  float* dg3, hipStream_t s) {
-    // one table: dG3 reduced per slice from per-run terms
-    const bool scan3 = p->T == 1 && p->tables[0].m[2] <= kMaxScanSlices3;
+    // dG3 reduced per G3 row from per-run terms (k_bwd_dg3 writes every row
+    // of the buffer, gaps included), unless some table's G3 rows are not
+    // aligned to R*n3: then device atomics into an fp64 accumulator
+    const bool bucket3 = p->nb3 > 0 && p->L > 0;
     if (!p->packed) {
         // elements outside every table's slices are zero in the gradients
         tt_status st = fill32(dg2, 0u, p->extent[1], s);
-        if (st == TT_OK && scan3) st = fill32(dg3, 0u, p->extent[2], s);
         if (st != TT_OK) return st;
     }
     constexpr int DL = N1 * N2 * N3 / 64;
@@ -926,8 +933,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     constexpr int PR = N1 * N2 * R;
     const int64_t nwin = (p->L + kWin - 1) / kWin;
     // set-up (first kPrepBlocks workgroups) and the grad-row sums in one launch
-    const PrepArgs pa{acc1, p->extent[0], acc3, p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
-                      p->at<int32_t>(p->lay.i3cnt), scan3 ? p->tables[0].m[2] : 0, p->at<int32_t>(p->lay.i3start),
+    const PrepArgs pa{acc1, p->extent[0], acc3, bucket3 ? 0 : p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
+                      p->at<int32_t>(p->lay.i3cnt), bucket3 ? p->nb3 : 0, p->at<int32_t>(p->lay.i3start),
                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece),
                       p->at<int32_t>(p->lay.gdone), p->ctrl()};
     const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
@@ -953,14 +960,13 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
                     acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart), p->at<int32_t>(p->lay.gdone)};
-        if (scan3) {
+        if (bucket3) {
             hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
                                p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.i3start),
                                p->at<int32_t>(p->lay.run_rank));
             TT_LAUNCH_CHECK();
-            hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->tables[0].m[2]), dim3(1024), 0, s,
-                               p->at<int32_t>(p->lay.i3start), p->at<float>(p->lay.c3),
-                               dg3 + p->tables[0].g_offset[2]);
+            hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
+                               p->at<int32_t>(p->lay.i3start), p->at<float>(p->lay.c3), dg3);
         } else {
             hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
@@ -980,7 +986,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         }
     }
     hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
-                       (scan3 && p->L > 0) ? 0 : p->extent[2], p->ctrl());
+                       bucket3 ? 0 : p->extent[2], p->ctrl());
     TT_LAUNCH_CHECK();
     return TT_OK;
 }

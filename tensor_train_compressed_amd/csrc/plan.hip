@@ -22,7 +22,7 @@
 //                     per tile (the sorted bags come out of the sort)
 //   k_key_tiles       present keys and chunks per tile of keys
 //   k_groups          key scan (group id and first chunk of every key), group tables
-//   k_runs            row-run ids and tables, chunk table; runs per i3 (one table)
+//   k_runs            row-run ids and tables, chunk table; runs per G3 row
 //   k_batches         one record per forward batch (kFwdBatch groups of one slice)
 // A device-wide scan of the tile totals runs before k_radix_scatter, k_groups
 // or k_runs only when there are more than kDirectTiles tiles.
@@ -37,7 +37,7 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB) {
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3) {
     Layout y{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
@@ -102,13 +102,14 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);
     // per run, P^T S (the run's dG3 term), for the single-table reduction of dG3
-    y.c3 = take(T == 1 ? sizeof(float) * (size_t)L * (size_t)CN : 0);
+    y.c3 = take(NB3 > 0 ? sizeof(float) * (size_t)L * (size_t)CN : 0);
     // fp64 pieces of the row runs cut by the backward's 64-position windows:
     // two slots per window (its start piece and its end piece)
     y.xsum = take(sizeof(double) * 2 * (size_t)((L + 63) / 64) * (size_t)D);
     y.xcnt = take(sizeof(int32_t) * (size_t)((L + 63) / 64));
-    y.i3cnt = take(sizeof(int32_t) * (size_t)M3 * kI3Pad);
-    y.i3start = take(sizeof(int32_t) * (size_t)(M3 + 1));
+    y.NB3 = NB3;
+    y.i3cnt = take(sizeof(int32_t) * (size_t)NB3 * kI3Pad);
+    y.i3start = take(sizeof(int32_t) * (size_t)(NB3 + 1));
     y.run_rank = take(sizeof(int32_t) * (size_t)L);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
@@ -737,6 +738,17 @@ __global__ __launch_bounds__(kSortThreads) void k_groups(const int32_t* __restri
     }
 }
 
+// G3 row of a run of key k and digit i3: its table's first G3 row plus i3.
+__device__ __forceinline__ int32_t bucket3(const TabDev* __restrict__ desc, int32_t T, int32_t CN, int32_t k,
+                                           int32_t i3) {
+    int lo = 0, hi = T;   // last table with key_base <= k
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (desc[mid].key_base <= k) lo = mid; else hi = mid;
+    }
+    return (int32_t)(desc[lo].o3 / CN) + i3;
+}
+
 // Row-run ids and tables over one tile of sorted positions (rid[s] = number
 // of row-run heads before s), and the chunk table: position s opens a chunk
 // when it lies a multiple of `chunk` past its group's start (chunk c of group
@@ -758,8 +770,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int32_t* __restrict__ chunk_begin,
                                                        int32_t* __restrict__ chunk_end,
                                                        int32_t* __restrict__ i3cnt, int32_t n3cnt,
-                                                       int32_t* __restrict__ run_rank) {
-    __shared__ uint32_t sh3[kMaxScanSlices3];
+                                                       int32_t* __restrict__ run_rank,
+                                                       const TabDev* __restrict__ desc, int32_t T, int32_t CN) {
+    __shared__ uint32_t sh3[kMaxBuckets3];
     for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
     const int64_t tile = blockIdx.x;
     __shared__ uint32_t wsum[17];
@@ -791,7 +804,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                 const int32_t r3 = ck[j + 1] - k * M3;
                 run_i3[rr] = r3;
                 run_start[rr] = (int32_t)s;
-                if (n3cnt) lrank[j] = atomicAdd(&sh3[r3], 1u);   // rank among the tile's runs of r3
+                if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3)], 1u);   // rank in the tile
             }
             run_of[perm[s]] = rr + (int32_t)hr[j] - 1;
             const int32_t off = (int32_t)s - key_start[k];
@@ -822,8 +835,8 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             if (s0 + j < L && hr[j]) {
-                const int32_t r3 = ck[j + 1] - (ck[j + 1] / M3) * M3;
-                run_rank[r] = (int32_t)(sh3[r3] + lrank[j]);
+                const int32_t k = ck[j + 1] / M3;
+                run_rank[r] = (int32_t)(sh3[bucket3(desc, T, CN, k, ck[j + 1] - k * M3)] + lrank[j]);
             }
             r += hr[j];
         }
@@ -879,7 +892,7 @@ using namespace tt;
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
                               int32_t* M3_out, int64_t* PR_out, int64_t* CN_out, int64_t* E1_out,
-                              int64_t* E3_out, int64_t* NFB_out) {
+                              int64_t* E3_out, int64_t* NFB_out, int64_t* NB3_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
     int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
@@ -908,6 +921,11 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         E3 = std::max<int64_t>(E3, x.g_offset[2] + (int64_t)x.m[2] * x.rank * x.n[2]);
     }
     if (K * M3 >= (int64_t(1) << 31)) return TT_ERR_UNSUPPORTED;
+    // dG3 buckets: every table's G3 rows R*n3 long and aligned to that length
+    bool rows3 = E3 % CN == 0 && E3 / CN <= kMaxBuckets3;
+    for (int32_t t = 0; t < T && rows3; ++t)
+        rows3 = (int64_t)tables[t].rank * tables[t].n[2] == CN && tables[t].g_offset[2] % CN == 0;
+    *NB3_out = rows3 ? E3 / CN : 0;
     *K_out = K;
     *D_out = D;
     *M3_out = M3;
@@ -929,11 +947,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 
 extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
                                          int64_t B, int32_t chunk) {
-    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
-    if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB) != TT_OK) return 0;
+    if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3).total;
 }
 
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
@@ -942,21 +960,23 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                  tt_emb_plan_t* plan_out) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
-    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
-    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB);
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
     if (!p) return TT_ERR_INVALID_ARG;
     p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;
     p->M3 = M3;
+    p->nb3 = (int32_t)NB3;
+    p->cn = CN;
     p->n_i2 = 0;
     p->n_fb = 0;
     for (int32_t t = 0; t < T; ++t) {
@@ -1022,9 +1042,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     }
 
     int32_t* ctrl = p->ctrl();
-    // runs per i3 are counted for the backward's dG3 reduction (one table of
-    // at most kMaxScanSlices3 G3 slices)
-    const int32_t n3cnt = (T == 1 && tables[0].m[2] <= kMaxScanSlices3) ? tables[0].m[2] : 0;
+    // runs per G3 row are counted for the backward's dG3 reduction
+    const int32_t n3cnt = (int32_t)NB3;
     int32_t* key = p->at<int32_t>(lay.key);
     int32_t* i3 = p->at<int32_t>(lay.i3);
     int32_t* bag = p->at<int32_t>(lay.bag_of);
@@ -1106,7 +1125,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.run_start),
                                p->at<int32_t>(lay.group_rbase), p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank));
+                               p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank), p->desc(), T,
+                               (int32_t)CN);
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         if (lay.NFB > 0) {

@@ -51,7 +51,7 @@ constexpr int kRunRange = 32;
 // With one table of at most this many G3 slices, dG3 is reduced per slice
 // from per-run terms (one workgroup per slice scans the run list) instead of
 // with device atomics.
-constexpr int kMaxScanSlices3 = 1024;
+constexpr int kMaxBuckets3 = 8192;   // G3 rows whose runs the planner counts (see Layout::i3cnt)
 constexpr int kI3Pad = 32;   // int32 words per i3 counter (one 128-byte line each)
 // LDS the batch kernels may spend on the run i3 list of one batch
 // (kFwdBatch * largest m3 int32 values); larger m3 takes the generic kernels.
@@ -135,24 +135,26 @@ struct Layout {
     size_t gdone;                            // [Gmax] int32: pieces of a split group finished (backward)
     size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group (backward),
                                              //     in the lane order of the matrix-core operands
-    size_t c3;                               // [L][R*n3] float, one table only: P^T S per run
+    size_t c3;                               // [L][R*n3] float (NB3 > 0): P^T S per run, by bucket
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
     size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
                                              //     cut by the backward's windows
     size_t xcnt;                             // [ceil(L/64)] int32: spans done per long cut run
-    // one table with m3 <= kMaxScanSlices3: the backward's c3 rows are bucketed by i3
-    size_t i3cnt;                            // [M3][kI3Pad] int32: runs per i3 (one counter per line)
-    size_t i3start;                          // [M3 + 1] int32: exclusive scan of the counts
-    size_t run_rank;                         // [L] int32: rank of each run inside its i3 bucket
+    // the backward's c3 rows, bucketed by G3 row (table's G3 offset / (R*n3) + i3),
+    // when every table's G3 offset is a whole number of rows and there are at
+    // most kMaxBuckets3 rows (NB3 of them; else NB3 = 0 and dG3 takes atomics)
+    size_t i3cnt;                            // [NB3][kI3Pad] int32: runs per bucket (one counter per line)
+    size_t i3start;                          // [NB3 + 1] int32: exclusive scan of the counts
+    size_t run_rank;                         // [L] int32: rank of each run inside its bucket
     size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles;
+    int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles, NB3;
     int passes;
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB);
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3);
 
 }  // namespace tt
 
@@ -164,6 +166,8 @@ struct tt_emb_plan_s {
     int32_t D;
     int64_t K;
     int32_t M3;               // largest m3 over the tables
+    int32_t nb3;              // G3 rows of the dG3 buckets (0: dG3 by device atomics)
+    int64_t cn;               // R*n3 (the G3 row length) when nb3 > 0
     int64_t n_i2;             // sum over tables of m2 (number of (table, i2) slices)
     int64_t n_fb;             // forward batches: sum over tables of m2 * ceil(m1 / kFwdBatch)
     bool uniform;             // all tables share (n1, n2, n3, R)

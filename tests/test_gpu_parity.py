@@ -296,17 +296,55 @@ def test_backward_ragged():
         _check_backward(p, f"ragged chunk={chunk}", chunk=chunk)
 
 
-@pytest.mark.parametrize("m3", [1024, 1025])
-def test_backward_i3_bucket_limit(m3):
-    # m3 = 1024: dG3 from the run rows bucketed by i3; 1025: device atomics.
-    # L = 4097 lookups: one full sort tile and a ragged one; Zipf indices so
-    # rows repeat inside groups.
+@pytest.mark.parametrize("m3,pad3", [(1024, 0), (1025, 0), (1024, 4)])
+def test_backward_g3_buckets(m3, pad3):
+    # dG3 from the run rows bucketed by G3 row; with the table's G3 placed 4
+    # floats into its buffer (rows not aligned to R*n3) it takes the device
+    # atomics instead. L = 4097 lookups: one full sort tile and a ragged one;
+    # Zipf indices so rows repeat inside groups.
     t = wl.Table(4 * 5 * m3, (4, 5, m3), (4, 8, 4), 32)
     lens = np.full(97, 42, np.int64)
     lens[-1] += 4097 - int(lens.sum())
     p = wl.make_custom([t], lens, seed=6, zipf_alpha=1.05, with_grad=True)
     assert p.L == 4097
-    _check_backward(p, f"m3={m3} L=4097", chunk=64)
+    if pad3:
+        p.g3 = np.concatenate([np.zeros(pad3, np.float32), p.g3])
+        p.goff = p.goff.copy()
+        p.goff[0, 2] = pad3
+    _check_backward(p, f"m3={m3} G3 at {pad3} L=4097", chunk=64)
+
+
+def test_backward_multitable_full_size_sampled():
+    """The 26-table batch at full size (8.5 M lookups): dG3 through buckets of
+    2,391 G3 rows, the planner's scans past 512 tiles. In each of the three
+    largest tables one slice of each core (cold under the unpermuted Zipf
+    head) is compared, against the oracle run on the lookups touching them
+    (exact for those slices)."""
+    p = wl.make("multi26")
+    p.grad_out = np.random.default_rng(2).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
+    p.lr = 0.01
+    pl = oracle.plan_problem(p, 256)
+    kb = np.cumsum([0] + [t.m[0] * t.m[1] for t in p.tables])
+    key = pl["key"].astype(np.int64)
+    i3 = pl["i3"].astype(np.int64)
+    tab = np.searchsorted(kb, key, side="right") - 1
+    m1 = np.array([t.m[0] for t in p.tables])
+    i1 = (key - kb[tab]) % m1[tab]
+    i2 = (key - kb[tab]) // m1[tab]
+    mask = np.zeros(p.L, bool)
+    s1, s2, s3 = [], [], []
+    for t in np.argsort([-t.num_rows for t in p.tables])[:3]:
+        tb = p.tables[t]
+        R, (n1, n2, n3) = tb.rank, tb.n
+        a1, a2, a3 = tb.m[0] - 1, tb.m[1] // 2, tb.m[2] // 3
+        mask |= (tab == t) & ((i1 == a1) | (i2 == a2) | (i3 == a3))
+        o1, o2, o3 = p.goff[t]
+        s1.append(np.arange(o1 + a1 * n1 * R, o1 + (a1 + 1) * n1 * R))
+        s2.append(np.arange(o2 + a2 * R * n2 * R, o2 + (a2 + 1) * R * n2 * R))
+        s3.append(np.arange(o3 + a3 * R * n3, o3 + (a3 + 1) * R * n3))
+    say("sampled multitable backward lookups", int(mask.sum()))
+    _check_backward(p, "multi26 full (sampled)", chunk=256, mask=mask.astype(np.uint8),
+                    slices=(np.concatenate(s1), np.concatenate(s2), np.concatenate(s3)))
 
 
 def _slice_mask(p, pl, which, picks):
