@@ -176,15 +176,6 @@ __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64
 // runs past w's end goes to slot 2w + 1. No two pieces share a slot.
 constexpr int kWin = 64;
 
-// Waits until every memory access this wave has issued has completed (for
-// device-scope stores and atomics: performed at the level all XCDs share).
-// Used before a completion count is claimed, in place of a device-scope
-// release fence, which on this chip also writes back the whole L2.
-__device__ __forceinline__ void wait_vmem_done() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 struct CrossRef {
     const int32_t* skey;

@@ -514,9 +514,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_lookback(V* data, int64_t
     if (threadIdx.x < 64) {
         // wave 0: publish the tile's total, then look back 64 tiles at a time
         const int lane = threadIdx.x;
+        // the value goes out as a device-scope store and has completed before
+        // the flag does (a wait, not a device-scope release fence, which
+        // would write back the whole L2)
         auto publish = [&](uint32_t state, V x) {
-            if (state == 2u) st[tile].incl = (uint64_t)x; else st[tile].agg = (uint64_t)x;
-            __hip_atomic_store(&st[tile].flag, (epoch << 2) | state, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(state == 2u ? &st[tile].incl : &st[tile].agg, (uint64_t)x, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            wait_vmem_done();
+            __hip_atomic_store(&st[tile].flag, (epoch << 2) | state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
         V prefix = 0;
         if (tile > 0) {
@@ -526,7 +531,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_lookback(V* data, int64_t
             while (true) {
                 const int64_t j = top - lane;
                 uint32_t f = 0;
-                if (j >= 0) f = __hip_atomic_load(&st[j].flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                if (j >= 0) f = __hip_atomic_load(&st[j].flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const bool mine = (f >> 2) == epoch;
                 const uint32_t state = mine ? (f & 3u) : 0u;
                 const uint64_t incl = __ballot(j >= 0 && state == 2u);
@@ -540,9 +545,12 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_lookback(V* data, int64_t
                     }
                     continue;
                 }
+                // values read after their flags (device-scope loads)
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 V c = 0;
-                if (j >= 0 && lane < first) c = (V)st[j].agg;
-                if (lane == first) c = (V)st[j].incl;
+                if (j >= 0 && lane < first)
+                    c = (V)__hip_atomic_load(&st[j].agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == first) c = (V)__hip_atomic_load(&st[j].incl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
                 for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
                 prefix += c;

@@ -201,6 +201,17 @@ struct tt_emb_plan_s {
     } while (0)
 
 namespace tt {
+// Waits until every memory access this wave has issued has completed (for
+// device-scope stores and atomics: performed at the level all XCDs share).
+// Used before a completion count or a ready flag is published, in place of a
+// device-scope release fence, which on this chip also writes back the whole
+// L2 of the XCD.
+__device__ __forceinline__ void wait_vmem_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 inline unsigned grid_for(int64_t n, int threads) {
     int64_t g = (n + threads - 1) / threads;
     return (unsigned)(g < 1 ? 1 : g);
