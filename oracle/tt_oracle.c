@@ -218,6 +218,25 @@ static void contrib_dg3(const tto_tab* x, const float* g1, const float* g2, cons
         }
 }
 
+/* 1 when two tables' core `which` (1, 2 or 3) occupy overlapping elements of
+ * the packed buffer (tables may share a core); their slices then write the
+ * same gradient elements and must not be accumulated concurrently. */
+static int cores_overlap(int32_t T, const tto_tab* tabs, int which) {
+    for (int32_t a = 0; a < T; ++a)
+        for (int32_t b = a + 1; b < T; ++b) {
+            const tto_tab* x = &tabs[a];
+            const tto_tab* y = &tabs[b];
+            const int64_t ox = which == 1 ? x->o1 : which == 2 ? x->o2 : x->o3;
+            const int64_t oy = which == 1 ? y->o1 : which == 2 ? y->o2 : y->o3;
+            const int64_t sx = which == 1 ? x->m1 * x->n1 * x->R
+                               : which == 2 ? x->m2 * x->R * x->n2 * x->R : x->m3 * x->R * x->n3;
+            const int64_t sy = which == 1 ? y->m1 * y->n1 * y->R
+                               : which == 2 ? y->m2 * y->R * y->n2 * y->R : y->m3 * y->R * y->n3;
+            if (ox < oy + sy && oy < ox + sx) return 1;
+        }
+    return 0;
+}
+
 /* Bucket the selected lookups by (table, slice) of core `which` (1, 2 or 3):
  * CSR over the global slice id, lookups in increasing l inside each bucket. */
 static int bucket(int32_t T, const tto_tab* tabs, const tto_lk* lk, const unsigned char* sel,
@@ -287,7 +306,9 @@ int tto_backward(int32_t T, const int64_t* num_rows, const int64_t* m, const int
         int64_t *start = NULL, *list = NULL, *tbase = NULL, S = 0;
         rc = bucket(T, tabs, lk, sel, L, which, &start, &list, &tbase, &S);
         if (rc != TTO_OK) break;
-#pragma omp parallel for schedule(dynamic, 1)
+        /* slices in parallel, unless slices of two tables share elements */
+        const int shared = cores_overlap(T, tabs, which);
+#pragma omp parallel for schedule(dynamic, 1) if (!shared)
         for (int64_t s = 0; s < S; ++s) {
             if (start[s] == start[s + 1]) continue;
             int32_t t = 0;

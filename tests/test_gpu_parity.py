@@ -314,6 +314,22 @@ def test_backward_g3_buckets(m3, pad3):
     _check_backward(p, f"m3={m3} G3 at {pad3} L=4097", chunk=64)
 
 
+def test_backward_shared_g3_and_empty():
+    # two tables reading one G3 (same offset): both tables' runs land in the
+    # same dG3 buckets and the slices get both sums
+    t1 = wl.Table(4 * 5 * 300, (4, 5, 300), (4, 8, 4), 32)
+    t2 = wl.Table(3 * 6 * 300, (3, 6, 300), (4, 8, 4), 32)
+    p = wl.make_custom([t1, t2], np.full(2 * 60, 7), seed=7, zipf_alpha=1.1, with_grad=True)
+    p.g3 = p.g3[:300 * 32 * 4].copy()
+    p.goff = p.goff.copy()
+    p.goff[1, 2] = 0
+    _check_backward(p, "shared G3", chunk=32)
+    # no lookups at all: every gradient is zero
+    q = wl.make_custom([t1], np.zeros(16, np.int64), seed=8, with_grad=True)
+    assert q.L == 0
+    _check_backward(q, "no lookups", chunk=32)
+
+
 def test_backward_multitable_full_size_sampled():
     """The 26-table batch at full size (8.5 M lookups): dG3 through buckets of
     2,391 G3 rows, the planner's scans past 512 tiles. In each of the three

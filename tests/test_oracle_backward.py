@@ -105,3 +105,29 @@ def test_hot_slice_fixture_inputs_current():
     assert g["dg1_i1_0"].shape == (n1 * R,)
     assert g["dg2_i2_0"].shape == (R * n2 * R,)
     assert g["dg3_i3_0"].shape == (R * n3,)
+
+
+def test_shared_core_is_the_sum_of_its_tables():
+    """Two tables reading one G3 (same offset): the gradient of the shared G3
+    is the sum of what each table alone gives it, and G1, G2 split by table.
+    (The per-slice accumulation runs in parallel; slices of tables that share
+    elements must not, and this is the case where they would collide.)"""
+    t1 = wl.Table(4 * 5 * 300, (4, 5, 300), (4, 8, 4), 8)
+    t2 = wl.Table(3 * 6 * 300, (3, 6, 300), (4, 8, 4), 8)
+    p = wl.make_custom([t1, t2], np.full(2 * 60, 7), seed=7, zipf_alpha=1.1, with_grad=True)
+    g3 = p.g3[:300 * 8 * 4].copy()
+    goff = p.goff.copy()
+    goff[1, 2] = 0
+    shared = wl.Problem("shared", p.tables, p.batch, p.g1, p.g2, g3, goff, p.indices, p.offsets,
+                        p.grad_out, p.lr)
+    B, L1 = p.batch, int(p.offsets[p.batch])
+    parts = []
+    for t, (lo, hi) in enumerate([(0, L1), (L1, p.L)]):
+        off = p.offsets[t * B:(t + 1) * B + 1] - p.offsets[t * B]
+        q = wl.Problem("one", [p.tables[t]], B, p.g1, p.g2, g3, goff[t:t + 1], p.indices[lo:hi],
+                       off, p.grad_out[t * B:(t + 1) * B], p.lr)
+        parts.append(oracle.backward_problem(q))
+    for _ in range(5):   # a collision between threads shows up only now and then
+        d = oracle.backward_problem(shared)
+        for k in range(3):
+            np.testing.assert_allclose(d[k], parts[0][k] + parts[1][k], rtol=1e-12, atol=1e-12)
