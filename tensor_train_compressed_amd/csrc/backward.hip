@@ -281,11 +281,26 @@ __device__ __forceinline__ void bwd_prep(const PrepArgs& pa, int64_t blk) {
 // fp64 device atomics, then counts itself in the run's counter; the span that
 // completes the count rounds the slot into the run's S row. At most one long
 // run starts in a span and at most one enters it from before.
+struct SlotArgs {
+    const int32_t* i3start;
+    const int32_t* run_bkt;
+    const int32_t* run_rank;
+    int32_t* run_slot;
+};
+
+// Workgroups past the first nspan (when sl.run_slot is set): each run's c3
+// row, its bucket's start plus its rank in the bucket, for the run kernel.
 template <int DL>
 __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, int32_t* __restrict__ xcnt,
                                                     CrossRef x, float* __restrict__ S,
-                                                    const int32_t* __restrict__ ctrl) {
+                                                    const int32_t* __restrict__ ctrl, int64_t nspan,
+                                                    SlotArgs sl) {
     constexpr int D = 64 * DL, WV = 16, SHORT = 16;
+    if ((int64_t)blockIdx.x >= nspan) {
+        const int64_t r = ((int64_t)blockIdx.x - nspan) * blockDim.x + threadIdx.x;
+        if (r < ctrl[CTRL_NUM_RUNS]) sl.run_slot[r] = sl.i3start[sl.run_bkt[r]] + sl.run_rank[r];
+        return;
+    }
     static_assert(SHORT >= WV, "a long run leaves the span it starts in");
     __shared__ double red[WV][D];
     __shared__ int32_t s_run[2];      // long run that starts in the span / enters it (-1: none)
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, 
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwin = (x.L + kWin - 1) / kWin;
     const int32_t NR = ctrl[CTRL_NUM_RUNS];
-    for (int64_t w0 = (int64_t)blockIdx.x * WV; w0 < nwin; w0 += (int64_t)gridDim.x * WV) {
+    for (int64_t w0 = (int64_t)blockIdx.x * WV; w0 < nwin; w0 += nspan * WV) {
         const int64_t w = w0 + wv;
         const int64_t e = (w + 1) * kWin;   // first position after window w
         int32_t run = -1;
@@ -568,27 +583,51 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
     const int32_t U = a.ctrl[CTRL_NUM_GROUPS], X = a.ctrl[CTRL_NUM_XPIECES];
     const int64_t npieces = (int64_t)X + U;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; k < npieces; k += nw) {
-        int64_t g = k - X;
-        int32_t part = 0;
-        if (k < X) {
-            g = a.xpiece[2 * k];
-            part = a.xpiece[2 * k + 1];
+    // A piece's words (group, part, its group's runs) and, per lane j, the i3
+    // and add3 word of its run s + j are fetched during the piece before it:
+    // the words at that piece's start, the run words after its tiles.
+    struct Words {
+        int64_t g;
+        int32_t part, gs, ge;
+    };
+    auto words_of = [&](int64_t kk, Words& w) {
+        w.g = kk - X;
+        w.part = 0;
+        if (kk < X) {
+            w.g = a.xpiece[2 * kk];
+            w.part = a.xpiece[2 * kk + 1];
         }
-        // P first: its address needs only g
+        w.gs = a.group_rbase[w.g];
+        w.ge = a.group_rbase[w.g + 1];
+    };
+    auto run_words = [&](const Words& w, int32_t& i3w, int32_t& xw) {
+        const int32_t s = w.gs + W * w.part, e = min(w.ge, s + W);
+        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[w.g])].o3;
+        i3w = a.run_i3[min(s + lane, e - 1)];
+        xw = pre(min(s + lane, e - 1), (int32_t)(o3 / CN) + i3w);
+    };
+    int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (k >= npieces) return;
+    Words cur;
+    int32_t i3l, xl;   // lane j: i3 and add3's word of run s + j of the current piece
+    words_of(k, cur);
+    run_words(cur, i3l, xl);
+    for (; k < npieces; k += nw) {
+        Words nxt;
+        words_of(min(k + nw, npieces - 1), nxt);
+        const int64_t g = cur.g;
+        // P: its address needs only g
         floatx4 preg[RT][KQ];
         const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
-        const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
+        const int32_t gs = cur.gs, ge = cur.ge, part = cur.part;
         const bool split = ge - gs > W;
-        if (split && k >= X) continue;   // done piece by piece from the list
+        if (!split || k < X) {   // a split group is done piece by piece from the list
         const int32_t s = gs + W * part, e = min(ge, s + W);
         const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
-        const int32_t i3l = a.run_i3[min(s + lane, e - 1)];   // lane j: i3 of run s + j
-        const int32_t xl = pre(min(s + lane, e - 1), (int32_t)(o3 / CN) + i3l);   // lane j: add3's word for run s + j
         doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -673,6 +712,9 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
                 }
             }
         }
+        }
+        run_words(nxt, i3l, xl);
+        cur = nxt;
     }
 }
 
@@ -694,11 +736,10 @@ __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
 // float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3,
-                                                        const int32_t* __restrict__ i3start,
-                                                        const int32_t* __restrict__ run_rank) {
+                                                        const int32_t* __restrict__ run_slot) {
     constexpr int CN = R * N3;
-    // add3's word: the run's row in the bucket of its G3 row
-    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t b3) { return i3start[b3] + run_rank[run]; },
+    // add3's word: the run's c3 row in the bucket of its G3 row
+    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t) { return run_slot[run]; },
                              [&](int64_t, int within, int32_t slot, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)slot * CN + within) = c;
     });
@@ -935,9 +976,13 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
         const bool kept = p->p_kept && p->kept_g1 == g1 && p->kept_g2 == g2;
-        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024)),
-                           dim3(1024), 0, s, xpart, p->at<int32_t>(p->lay.xcnt), xr, p->at<float>(p->lay.stage),
-                           p->ctrl());
+        // cut-run sums (nspan workgroups) and, with buckets, the runs' c3 rows
+        const int64_t nspan = std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024);
+        const SlotArgs sl{p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.run_bkt),
+                          p->at<int32_t>(p->lay.run_rank), p->at<int32_t>(p->lay.run_slot)};
+        const int64_t nslot = bucket3 ? (p->L + 1023) / 1024 : 0;
+        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)(nspan + nslot)), dim3(1024), 0, s, xpart,
+                           p->at<int32_t>(p->lay.xcnt), xr, p->at<float>(p->lay.stage), p->ctrl(), nspan, sl);
         TT_LAUNCH_CHECK();
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
@@ -953,8 +998,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart), p->at<int32_t>(p->lay.gdone)};
         if (bucket3) {
             hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
-                               p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.i3start),
-                               p->at<int32_t>(p->lay.run_rank));
+                               p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.run_slot));
             TT_LAUNCH_CHECK();
             hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
                                p->at<int32_t>(p->lay.i3start), p->at<float>(p->lay.c3), dg3);

@@ -111,6 +111,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.i3cnt = take(sizeof(int32_t) * (size_t)NB3 * kI3Pad);
     y.i3start = take(sizeof(int32_t) * (size_t)(NB3 + 1));
     y.run_rank = take(sizeof(int32_t) * (size_t)L);
+    y.run_bkt = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
+    y.run_slot = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
@@ -779,6 +781,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int32_t* __restrict__ chunk_end,
                                                        int32_t* __restrict__ i3cnt, int32_t n3cnt,
                                                        int32_t* __restrict__ run_rank,
+                                                       int32_t* __restrict__ run_bkt,
                                                        const TabDev* __restrict__ desc, int32_t T, int32_t CN) {
     __shared__ uint32_t sh3[kMaxBuckets3];
     for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
@@ -844,7 +847,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
         for (int j = 0; j < kSortItems; ++j) {
             if (s0 + j < L && hr[j]) {
                 const int32_t k = ck[j + 1] / M3;
-                run_rank[r] = (int32_t)(sh3[bucket3(desc, T, CN, k, ck[j + 1] - k * M3)] + lrank[j]);
+                const int32_t b = bucket3(desc, T, CN, k, ck[j + 1] - k * M3);
+                run_rank[r] = (int32_t)(sh3[b] + lrank[j]);
+                run_bkt[r] = b;
             }
             r += hr[j];
         }
@@ -1133,8 +1138,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.run_of), p->at<int32_t>(lay.run_start),
                                p->at<int32_t>(lay.group_rbase), p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
-                               p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank), p->desc(), T,
-                               (int32_t)CN);
+                               p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank),
+                               p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN);
             if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
         }
         if (lay.NFB > 0) {

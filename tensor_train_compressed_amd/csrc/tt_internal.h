@@ -147,6 +147,8 @@ struct Layout {
     size_t i3cnt;                            // [NB3][kI3Pad] int32: runs per bucket (one counter per line)
     size_t i3start;                          // [NB3 + 1] int32: exclusive scan of the counts
     size_t run_rank;                         // [L] int32: rank of each run inside its bucket
+    size_t run_bkt;                          // [L] int32: bucket (G3 row) of each run
+    size_t run_slot;                         // [L] int32: backward: each run's c3 row (start + rank)
     size_t batch;                            // [NFB] BatchRec
     size_t total;
     int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles, NB3;
