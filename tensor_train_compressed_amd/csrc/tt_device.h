@@ -27,45 +27,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// P[p][r2] = sum_r1 G1[i1][j1][r1] G2[i2][r1][j2][r2] (p = j1*N2 + j2) into
-// sP ([p][r2], row-major), one wave, VALU. Row r1 of the G2 slice is N2*R
-// contiguous floats; lane owns the float4 "quad" qd = lane % Q of that row
-// (j2 = 4*qd / R, r2 = 4*qd % R .. +3) and the j1 values j1 = lane / Q + (64/Q)*k,
-// so every load is one coalesced dwordx4 row read and 16 loads are in flight.
-template <int N1, int N2, int R>
-__device__ __forceinline__ void build_prefix(const float* __restrict__ A, const float* __restrict__ Bc,
-                                             float* sG1T, float* sP, int lane) {
-    constexpr int N2R = N2 * R, Q = N2R / 4, LG = 64 / Q, J1L = N1 / LG;
-    static_assert(N2R % 4 == 0 && 64 % Q == 0 && N1 % LG == 0, "prefix shape");
-    // G1 slice transposed to [r1][j1] so that one r1 gives the N1 values together
-    for (int e = lane; e < N1 * R; e += 64) sG1T[(e % R) * N1 + e / R] = A[e];
-    wave_lds_sync();
-    const int qd = lane % Q, jg = lane / Q;
-    const float4* Bq = reinterpret_cast<const float4*>(Bc) + qd;
-    float4 acc[J1L];
-#pragma unroll
-    for (int k = 0; k < J1L; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 16
-    for (int r1 = 0; r1 < R; ++r1) {
-        const float4 b = Bq[r1 * Q];
-#pragma unroll
-        for (int k = 0; k < J1L; ++k) {
-            const float a = sG1T[r1 * N1 + jg + LG * k];
-            acc[k].x = fmaf(a, b.x, acc[k].x);
-            acc[k].y = fmaf(a, b.y, acc[k].y);
-            acc[k].z = fmaf(a, b.z, acc[k].z);
-            acc[k].w = fmaf(a, b.w, acc[k].w);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < J1L; ++k) {
-        const int j1 = jg + LG * k;
-        // element (j1, j2, r2) sits at ((j1*N2 + j2)*R + r2) = j1*N2R + 4*qd
-        *reinterpret_cast<float4*>(sP + j1 * N2R + 4 * qd) = acc[k];
-    }
-    wave_lds_sync();
-}
-
 // Persistent grid: blocks per CU times the CU count.
 inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blocks_per_cu); }
 
