@@ -803,7 +803,9 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, CT = N2R / 16, UNR = 8;
     static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int64_t task = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    // wave-uniform task: the group loop is scalar control flow (no exec-mask
+    // loop, whose head waits for every load in flight)
+    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (task >= n_i2 * CT) return;
     const int32_t bi = (int32_t)(task / CT);
     const int ct = (int)(task % CT);
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2;
     static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int64_t task = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (task >= nb * 2) return;
     const int64_t b = task / 2;
     const int h = (int)(task % 2);

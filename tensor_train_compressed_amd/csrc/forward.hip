@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
                                               float* __restrict__ out, int32_t* ctrl) {
     constexpr int LPR = D / 4, RPI = 64 / LPR, U = 8;   // U loads in flight
     static_assert(D % 4 == 0 && 64 % LPR == 0, "row shape");
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform bag: its loops are scalar control flow
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int h = lane / LPR, c4 = 4 * (lane % LPR);
     const int64_t q = (int64_t)blockIdx.x * 4 + w;
     if (q >= TB) return;

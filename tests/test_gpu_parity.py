@@ -253,6 +253,25 @@ def test_backward_small_all():
         _check_backward(p, f"train11m B=256", chunk=chunk)
 
 
+def test_backward_unaligned_dg2():
+    """dG2 written through a pointer 4 bytes past a 16-byte boundary (the
+    library takes any 4-byte-aligned output): the result still matches the
+    oracle."""
+    import tensor_train_compressed_amd as tte
+    p = wl.make("train11m", batch=256)
+    dp = DevProblem(p, 256)
+    dp.make_plan()
+    d1 = torch.empty_like(dp.g1)
+    d3 = torch.empty_like(dp.g3)
+    buf = torch.empty(dp.g2.numel() + 4, dtype=torch.float32, device="cuda:0")
+    d2 = buf[1:1 + dp.g2.numel()]
+    assert d2.data_ptr() % 16 == 4
+    tte.tt_emb_backward(dp.plan, dp.g1, dp.g2, dp.g3, dp.gout, d1, d2, d3)
+    ref = oracle.backward_problem(p)
+    for k, x in enumerate((d1, d2, d3)):
+        assert_close(x.cpu().numpy(), ref[k], f"unaligned dG2: dG{k + 1}")
+
+
 def test_forward_train_keeps_prefix():
     """tt_emb_forward_train gives the forward's output bit for bit and keeps
     P for the next backward, which must match the oracle; tt_emb_sgd then
