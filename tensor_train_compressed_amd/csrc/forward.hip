@@ -102,7 +102,8 @@ __device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, c
     using B = PrefixBatch<N1, N2, R>;
     constexpr int NP = B::NP, D = NP * N3, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
     constexpr int MT = NP / 16, LK = 16 / N3;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
+              q = lane >> 4;   // w wave-uniform: branches and loops on it are scalar
     const int ntile = sTp[c.ng];
     const int per = (ntile + WAVES - 1) / WAVES;
     const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;

@@ -137,7 +137,8 @@ __device__ __forceinline__ void batch_prefix(int32_t rw, const int32_t* __restri
     using F = BatchPf<N1, N2, R>;
     constexpr int NP = B::NP, N2R = B::N2R, MTP = B::MTP, KS = B::KS, GS = B::GS, AS = B::AS;
     constexpr int WAVES = B::WAVES, NT2 = B::NT2, NTW = B::NTW, NT = F::NT;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, col = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
+              q = lane >> 4;   // w wave-uniform: branches and loops on it are scalar
     c.ng = rec_field(rw, RW_NG); c.g0 = rec_field(rw, RW_G0);
     c.rb0 = rec_field(rw, RW_RB0); c.nr = rec_field(rw, RW_NR); c.o3 = rec_field64(rw, RW_O3);
     float* sG2 = sU;
