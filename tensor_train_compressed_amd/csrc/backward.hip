@@ -875,56 +875,62 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
         for (int v = 0; v < 4; ++v) D2[(int64_t)(16 * rt + q + 4 * v) * N2R] = (float)(acc[0][rt][v] + acc[1][rt][v]);
 }
 
-// dG1[i1] += dP_g G2[i2]^T, one wave per half of a prefix batch (4 groups of
-// one slice), every r1 tile: rows (group, j1), K = the n2*R columns, taken 16
-// at a time as 16-byte loads per lane (dP once, G2 per r1 tile) feeding four
-// fp64 matrix-core steps. A group's sum over K is complete in the wave, so
-// each dG1 element takes one fp64 atomic per group (groups of every slice add
-// to the same i1).
+// dG1[i1] += dP_g G2[i2]^T, one wave per prefix batch (up to 8 groups of one
+// slice: two row tiles of 4 groups), every r1 tile: rows (group, j1), K = the
+// n2*R columns, taken 16 at a time as 16-byte loads per lane (dP once, G2 once
+// per r1 tile for both row tiles) feeding four fp64 matrix-core steps per row
+// and r1 tile. A group's sum over K is complete in the wave, so each dG1
+// element takes one fp64 atomic per group (groups of every slice add to the
+// same i1). A wave per half batch read the 32 KB G2 slice twice per batch,
+// and that L2 traffic set its time.
 template <int N1, int N2, int R>
 __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ recs, int64_t nb,
                                                  const float* __restrict__ dpg, const float* __restrict__ g2,
                                                  double* __restrict__ dg1) {
-    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2;
-    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0, "shape");
+    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2, MT = kFwdBatch / 4;
+    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0 && MT == 2, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (task >= nb * 2) return;
-    const int64_t b = task / 2;
-    const int h = (int)(task % 2);
+    const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (b >= nb) return;
     const int32_t rw = rec_word(recs, b, nb);
-    const int ng = rec_field(rw, RW_NG) - 4 * h;
+    const int ng = rec_field(rw, RW_NG);
     if (ng <= 0) return;
-    const int32_t g0 = rec_field(rw, RW_G0) + 4 * h;
-    // A row i = (group i / 4, j1 = i % 4) of the tile: lane (col, q) reads row col
-    const int32_t ga = g0 + min(col / 4, ng - 1);
-    const floatx4* A = reinterpret_cast<const floatx4*>(dpg + (int64_t)ga * PR + (col % 4) * N2R) + q;
+    const int32_t g0 = rec_field(rw, RW_G0);
+    // A row i of row tile mt = (group 4mt + i / 4, j1 = i % 4): lane (col, q) reads row col
+    const floatx4* A[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        A[mt] = reinterpret_cast<const floatx4*>(dpg + (int64_t)(g0 + min(4 * mt + col / 4, ng - 1)) * PR +
+                                                 (col % 4) * N2R) + q;
     const floatx4* Bm = reinterpret_cast<const floatx4*>(g2 + rec_field64(rw, RW_O2) +
                                                           (int64_t)rec_field(rw, RW_I2) * R * N2R +
                                                           (int64_t)col * N2R) + q;   // + 16*rt rows
-    doublex4 acc[2][RT];   // two sets (even and odd columns): independent chains
+    doublex4 acc[MT][RT];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[x][rt] = doublex4{0.0, 0.0, 0.0, 0.0};
-    floatx4 a4[2][UNR], b4[2][UNR][RT];
-    auto load = [&](int s0, floatx4 (&a)[UNR], floatx4 (&bb)[UNR][RT]) {
+        for (int rt = 0; rt < RT; ++rt) acc[mt][rt] = doublex4{0.0, 0.0, 0.0, 0.0};
+    floatx4 a4[2][UNR][MT], b4[2][UNR][RT];
+    auto load = [&](int s0, floatx4 (&a)[UNR][MT], floatx4 (&bb)[UNR][RT]) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            a[u] = A[4 * (s0 + u)];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) a[u][mt] = A[mt][4 * (s0 + u)];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) bb[u][rt] = Bm[(16 * rt) * (N2R / 4) + 4 * (s0 + u)];
         }
     };
-    auto math = [&](const floatx4 (&a)[UNR], const floatx4 (&bb)[UNR][RT]) {
+    auto math = [&](const floatx4 (&a)[UNR][MT], const floatx4 (&bb)[UNR][RT]) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    acc[e & 1][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][e], (double)bb[u][rt][e],
-                                                                         acc[e & 1][rt], 0, 0, 0);
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc[mt][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][mt][e], (double)bb[u][rt][e],
+                                                                          acc[mt][rt], 0, 0, 0);
     };
     load(0, a4[0], b4[0]);
 #pragma unroll
@@ -934,15 +940,18 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
         if (s0 + 2 * UNR < KS) load(s0 + 2 * UNR, a4[0], b4[0]);
         math(a4[1], b4[1]);
     }
-    // the fp64 product's lane (col, q) holds rows q + 4v = (group v, j1 = q), column r1 = 16rt + col
+    // the fp64 product's lane (col, q) holds rows q + 4v of tile mt = (group 4mt + v, j1 = q),
+    // column r1 = 16rt + col
     double* D1 = dg1 + rec_field64(rw, RW_O1) + q * R + col;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-        if (v < ng) {
-            double* dst = D1 + (int64_t)__builtin_amdgcn_readlane(rw, RW_I1 + 4 * h + v) * N1 * R;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[0][rt][v] + acc[1][rt][v]);
-        }
+        for (int v = 0; v < 4; ++v)
+            if (4 * mt + v < ng) {
+                double* dst = D1 + (int64_t)__builtin_amdgcn_readlane(rw, RW_I1 + 4 * mt + v) * N1 * R;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[mt][rt][v]);
+            }
 }
 
 template <int N1, int N2, int R, int N3>
@@ -1015,7 +1024,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                            p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key),
                            p->at<float>(p->lay.dpg), g1, dg2, p->n_i2);
         TT_LAUNCH_CHECK();
-        const int64_t w1 = p->n_fb * 2;
+        const int64_t w1 = p->n_fb;
         if (w1 > 0) {
             hipLaunchKernelGGL((k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<float>(p->lay.dpg), g2, acc1);
