@@ -311,18 +311,21 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
         if (!vin) bb[slot] = min(max(bb[slot], 0), TB - 1);
     }
     if (DIRECT) {
-        // four lanes per digit, each sums a quarter of the digit's row
-        const int dg = threadIdx.x >> 2, part = threadIdx.x & 3;
+        // LPD lanes per digit, each sums every LPD-th 16-byte piece of the
+        // digit's row
+        constexpr int LPD = kSortThreads / kRadixBins;
+        static_assert(LPD >= 1 && (LPD & (LPD - 1)) == 0 && LPD <= 64, "lanes per digit");
+        const int dg = threadIdx.x / LPD, part = threadIdx.x % LPD;
         const uint4* row = reinterpret_cast<const uint4*>(hist + (int64_t)dg * hstride);
         const int64_t n4 = hstride / 4;
         uint32_t pre = 0, tot = 0;
-        for (int64_t v0 = part; v0 < n4; v0 += 32) {   // eight loads in flight per lane
+        for (int64_t v0 = part; v0 < n4; v0 += 8 * LPD) {   // eight loads in flight per lane
             uint4 x[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = v0 + 4 * u < n4 ? row[v0 + 4 * u] : uint4{0u, 0u, 0u, 0u};
+            for (int u = 0; u < 8; ++u) x[u] = v0 + LPD * u < n4 ? row[v0 + LPD * u] : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int64_t t0 = 4 * (v0 + 4 * u);
+                const int64_t t0 = 4 * (v0 + LPD * u);
                 const uint32_t c[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -331,10 +334,11 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(
                 }
             }
         }
-        pre += __shfl_xor(pre, 1);
-        pre += __shfl_xor(pre, 2);
-        tot += __shfl_xor(tot, 1);
-        tot += __shfl_xor(tot, 2);
+#pragma unroll
+        for (int o = 1; o < LPD; o <<= 1) {
+            pre += __shfl_xor(pre, o);
+            tot += __shfl_xor(tot, o);
+        }
         if (part == 0) {
             gpre[dg] = pre;
             gtot[dg] = tot;
