@@ -633,22 +633,29 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
-        for (int32_t t0 = s; t0 < e; t0 += 4) {
-            const bool okq = t0 + q < e;
-            const int32_t rq = okq ? t0 + q : t0;
-            const int32_t i3q = __shfl(i3l, rq - s);
-            const int32_t xq = __shfl(xl, rq - s);
-            const float* Sq = a.S + (int64_t)rq * D;
-            const float* G3q = a.g3 + o3 + (int64_t)i3q * CN;
+        // a tile's operands (S rows in both layouts, G3 rows of its runs) are
+        // loaded one tile ahead, before the current tile's products and stores
+        struct TileOps {
             floatx4 av[MT], bq[RT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
-#pragma unroll
-            for (int nt = 0; nt < RT; ++nt) bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
-            const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
             float bv[KSP];
+            int32_t i3q, xq;
+        };
+        auto load_tile = [&](int32_t t0, TileOps& o) {
+            const int32_t rq = t0 + q < e ? t0 + q : t0;
+            o.i3q = __shfl(i3l, rq - s);
+            o.xq = __shfl(xl, rq - s);
+            const float* Sq = a.S + (int64_t)rq * D;
+            const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
 #pragma unroll
-            for (int s2 = 0; s2 < KSP; ++s2) bv[s2] = Sl[(4 * s2 + q) * N3];
+            for (int mt = 0; mt < MT; ++mt) o.av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
+#pragma unroll
+            for (int nt = 0; nt < RT; ++nt) o.bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
+            const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
+#pragma unroll
+            for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = Sl[(4 * s2 + q) * N3];
+        };
+        auto tile = [&](int32_t t0, TileOps& o) {
+            const bool okq = t0 + q < e;
             // dG3: rows (run t0 + lk, j3) of P^T S; lane (col, q) gets run
             // t0 + q, r2 = 16rt + col, j3 = v
 #pragma unroll
@@ -656,22 +663,32 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
                 floatx4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < KSP; ++s2)
-                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
-                if (okq) add3(o3 + (int64_t)i3q * CN, (16 * rt + col) * N3, xq, cc);
+                    cc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
+                if (okq) add3(o3 + (int64_t)o.i3q * CN, (16 * rt + col) * N3, o.xq, cc);
             }
             // dP: K = (run q, j3 = step), fp64 products and sums (a hot
             // group's dP adds up hundreds of runs of large S); a run past the
             // piece adds zeros
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                if (!okq) av[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                const floatx4 av = okq ? o.av[mt] : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
                     for (int st = 0; st < 4; ++st)
-                        dacc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[mt][st], (double)bq[nt][st],
+                        dacc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[st], (double)o.bq[nt][st],
                                                                             dacc[mt][nt], 0, 0, 0);
             }
+        };
+        TileOps TA, TB;
+        load_tile(s, TA);
+        for (int32_t t0 = s;; t0 += 8) {
+            load_tile(min(t0 + 4, e - 1), TB);
+            tile(t0, TA);
+            if (t0 + 4 >= e) break;
+            load_tile(min(t0 + 8, e - 1), TA);
+            tile(t0 + 4, TB);
+            if (t0 + 8 >= e) break;
         }
         // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col];
         // a piece of a split group keeps its fp64 partial in its own slot
@@ -735,7 +752,7 @@ __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
 // same few hundred G3 slices saturate the memory-side atomic units, and LDS
 // float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256, 4) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3,
+__global__ __launch_bounds__(256, 3) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3,
                                                         const int32_t* __restrict__ run_slot) {
     constexpr int CN = R * N3;
     // add3's word: the run's c3 row in the bucket of its G3 row
@@ -1008,7 +1025,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
                     acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart), p->at<int32_t>(p->lay.gdone)};
         if (bucket3) {
-            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra,
+            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra,
                                p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.run_slot));
             TT_LAUNCH_CHECK();
             hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
