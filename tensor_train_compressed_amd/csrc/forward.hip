@@ -88,28 +88,24 @@ struct FwdArgs {
 // the B operand, and receives E[run q][p = 16mt + col][j3 = 0..3]: four
 // consecutive floats of that run's row, written with one 16-byte store.
 // Wave w takes a contiguous range of tiles (consecutive tiles mostly share a
-// group, so P is reloaded once per group). A tile's G3 operand is loaded one
-// tile ahead, before the current tile's stores: loads and stores share one
-// in-order completion counter, so a load can only be waited for alone if every
-// memory access issued after it is certain to have been issued. The loop body
-// therefore holds no conditional access (lanes past the group's last run store
-// to a spare row, the look-ahead tile is clamped to the last one, run i3 values
-// come from LDS), it is unrolled by two with ping-pong operand sets, and no
-// register that a load is still filling is ever copied.
+// group, so P is reloaded once per group). Every wave forms the batch's tile
+// prefix itself, in registers (lane g: first tile of group g), so begin() can
+// issue the G3 loads of the wave's first tile straight after the prologue,
+// before the next batch's loads and with no barrier: most batches have one
+// tile per wave, whose operand latency would otherwise be exposed. In run(),
+// a tile's G3 operand is loaded one tile ahead, before the current tile's
+// stores: loads and stores share one in-order completion counter, so a load
+// can only be waited for alone if every memory access issued after it is
+// certain to have been issued. The loop body therefore holds no conditional
+// access (lanes past the group's last run store to a spare row, the
+// look-ahead tile is clamped to the last one, run i3 values come from LDS),
+// it is unrolled by two with ping-pong operand sets, and no register that a
+// load is still filling is ever copied.
 template <int N1, int N2, int R, int N3>
-__device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, const float* sP,
-                                          const int32_t* sRb, const int32_t* sTp, const int32_t* sI3) {
+struct FwdTiles {
     using B = PrefixBatch<N1, N2, R>;
-    constexpr int NP = B::NP, D = NP * N3, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
-    constexpr int MT = NP / 16, LK = 16 / N3;
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, col = lane & 15,
-              q = lane >> 4;   // w wave-uniform: branches and loops on it are scalar
-    const int ntile = sTp[c.ng];
-    const int per = (ntile + WAVES - 1) / WAVES;
-    const int t0 = min(ntile, w * per), n = min(ntile, t0 + per) - t0;
-    if (n <= 0) return;
-    const int lk = col / N3, j3 = col % N3;
-    const float* G3 = a.g3 + c.o3 + j3 + KS * q * N3;
+    static constexpr int NP = B::NP, D = NP * N3, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
+    static constexpr int MT = NP / 16, LK = 16 / N3;
     struct Ids {
         int g;
         int32_t r;         // stage row of run q of the tile (a spare row past the group's end)
@@ -120,55 +116,91 @@ __device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, c
         int32_t r;
         float bv[KS];      // G3[i3 of run lk][r2][j3], K = r2
     };
-    int gs = 0;            // walks forward over the batch's groups
-    auto ids_of = [&](int k, Ids& o) {
-        const int tt = t0 + k;
-        while (sTp[gs + 1] <= tt) ++gs;
-        o.g = gs;
-        const int32_t rb = sRb[gs] + LK * (tt - sTp[gs]), re = sRb[gs + 1];   // relative to rb0
-        o.r = rb + q < re ? c.rb0 + rb + q : (int32_t)a.L + q;
-        o.i3 = sI3[rb + lk < re ? rb + lk : rb];
-    };
-    auto load_ops = [&](const Ids& o, Ops& x) {
-        x.g = o.g; x.r = o.r;
-        const float* gb = G3 + (int64_t)o.i3 * R * N3;
-#pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) x.bv[s2] = gb[s2 * N3];
-    };
-    int cur = -1;
-    float bp[MT][KS];      // P[16mt + col][KS*q + s2]
-    auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
-        ids_of(min(k + 2, n - 1), Inew);
-        load_ops(Inext, Nx);
-        if (C.g != cur) {
-            cur = C.g;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int s2 = 0; s2 < KS; ++s2) bp[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
-        }
-        float* dst = a.stage + (int64_t)C.r * D + col * N3;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            floatx4 e = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s2 = 0; s2 < KS; ++s2)
-                e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2], bp[mt][s2], e, 0, 0, 0);
-            *reinterpret_cast<floatx4*>(dst + 16 * mt * N3) = e;
-        }
-    };
+    int32_t tpl;           // lane g <= ng: the batch's first tile of group g (lane ng: the tile count)
+    int t0, n, gs;
     Ids IA, IB;
     Ops OA, OB;
-    ids_of(0, IA);
-    load_ops(IA, OA);
-    ids_of(min(1, n - 1), IB);
-    int k = 0;
-    for (; k + 1 < n; k += 2) {
-        step(k, OA, OB, IA, IB);
-        step(k + 1, OB, OA, IB, IA);
+
+    __device__ __forceinline__ int tp(int g) const { return __builtin_amdgcn_readlane(tpl, g); }
+
+    __device__ __forceinline__ void ids_of(const FwdArgs& a, const BatchCtx& c, const int32_t* sRb,
+                                           const int32_t* sI3, int k, Ids& o) {
+        const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4, lk = col / N3;
+        const int tt = t0 + k;
+        while (tp(gs + 1) <= tt) ++gs;
+        o.g = gs;
+        const int32_t rb = sRb[gs] + LK * (tt - tp(gs)), re = sRb[gs + 1];   // relative to rb0
+        o.r = rb + q < re ? c.rb0 + rb + q : (int32_t)a.L + q;
+        o.i3 = sI3[rb + lk < re ? rb + lk : rb];
     }
-    if (k < n) step(k, OA, OB, IA, IB);
-}
+    __device__ __forceinline__ void load_ops(const FwdArgs& a, const BatchCtx& c, const Ids& o, Ops& x) {
+        const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4, j3 = col % N3;
+        x.g = o.g; x.r = o.r;
+        const float* gb = a.g3 + c.o3 + j3 + KS * q * N3 + (int64_t)o.i3 * R * N3;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) x.bv[s2] = gb[s2 * N3];
+    }
+
+    // After the prologue (sRb, sI3 and P in LDS, visible to every wave): the
+    // wave's tile range and the loads of its first tile.
+    __device__ __forceinline__ void begin(const FwdArgs& a, const BatchCtx& c, const int32_t* sRb,
+                                          const int32_t* sI3) {
+        const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int gl = min(lane, c.ng - 1);   // c.ng >= 1 here; sRb has kFwdBatch + 1 entries
+        const int32_t cnt = lane < c.ng ? (sRb[gl + 1] - sRb[gl] + LK - 1) / LK : 0;
+        int32_t inc = cnt;
+#pragma unroll
+        for (int o = 1; o <= kFwdBatch; o <<= 1) {
+            const int32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        tpl = inc - cnt;
+        const int ntile = tp(c.ng);
+        const int per = (ntile + WAVES - 1) / WAVES;
+        t0 = min(ntile, w * per);
+        n = min(ntile, t0 + per) - t0;
+        gs = 0;
+        if (n > 0) {
+            ids_of(a, c, sRb, sI3, 0, IA);
+            load_ops(a, c, IA, OA);
+            ids_of(a, c, sRb, sI3, min(1, n - 1), IB);
+        }
+    }
+
+    __device__ __forceinline__ void run(const FwdArgs& a, const BatchCtx& c, const float* sP, const int32_t* sRb,
+                                        const int32_t* sI3) {
+        if (n <= 0) return;
+        const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+        int cur = -1;
+        float bp[MT][KS];      // P[16mt + col][KS*q + s2]
+        auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
+            ids_of(a, c, sRb, sI3, min(k + 2, n - 1), Inew);
+            load_ops(a, c, Inext, Nx);
+            if (C.g != cur) {
+                cur = C.g;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) bp[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
+            }
+            float* dst = a.stage + (int64_t)C.r * D + col * N3;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                floatx4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+                    e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2], bp[mt][s2], e, 0, 0, 0);
+                *reinterpret_cast<floatx4*>(dst + 16 * mt * N3) = e;
+            }
+        };
+        int k = 0;
+        for (; k + 1 < n; k += 2) {
+            step(k, OA, OB, IA, IB);
+            step(k + 1, OB, OA, IB, IA);
+        }
+        if (k < n) step(k, OA, OB, IA, IB);
+    }
+};
 
 // Persistent workgroups (a few per CU) walk the batch slots b = blockIdx.x,
 // blockIdx.x + gridDim.x, ... . While a workgroup runs the tiles of one batch,
@@ -179,11 +211,10 @@ __device__ __forceinline__ void fwd_tiles(const FwdArgs& a, const BatchCtx& c, c
 template <int N1, int N2, int R, int N3, bool KEEP>
 __global__ __launch_bounds__(512, 4) void k_fwd_batch(FwdArgs a, int64_t nb) {
     using B = PrefixBatch<N1, N2, R>;
-    constexpr int SG = B::SG, LK = 16 / N3;
+    constexpr int SG = B::SG;
     static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 512, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
-    __shared__ int32_t sTp[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
     const int64_t G = gridDim.x;
@@ -192,20 +223,20 @@ __global__ __launch_bounds__(512, 4) void k_fwd_batch(FwdArgs a, int64_t nb) {
     int32_t rwB = rec_word(a.recs, b + G, nb);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, a.run_i3, a.g1, a.g2, f);
+    FwdTiles<N1, N2, R, N3> tl;
     for (; b < nb; b += G) {
         const int32_t rwC = rec_word(a.recs, b + 2 * G, nb);
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) {
             batch_prefix<N1, N2, R>(rwA, a.run_i3, f, sU, sRb, sI3, c);
-            batch_tiles(sRb, sTp, c.ng, LK);
+            tl.begin(a, c, sRb, sI3);   // the first tile's G3 loads go out before the next batch's
         }
         batch_fetch<N1, N2, R>(rwB, a.run_i3, a.g1, a.g2, f);
         if (live) {
             if (KEEP) store_prefix_lanes<N1, N2, R, 512>(sU, c.g0, c.ng, a.pbuf);
-            __syncthreads();
-            fwd_tiles<N1, N2, R, N3>(a, c, sU, sRb, sTp, sI3);
-            __syncthreads();
+            tl.run(a, c, sU, sRb, sI3);
+            __syncthreads();   // sU is the next prologue's
         }
         rwA = rwB;
         rwB = rwC;

@@ -235,16 +235,4 @@ __device__ __forceinline__ void store_prefix_lanes(const float* sP, int32_t g0, 
     }
 }
 
-// Tile prefix over the batch's groups: sTp[g+1] - sTp[g] = ceil(runs(g) / per).
-__device__ __forceinline__ void batch_tiles(const int32_t* sRb, int32_t* sTp, int ng, int per) {
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        sTp[0] = 0;
-        for (int gi = 0; gi < ng; ++gi) {
-            acc += (sRb[gi + 1] - sRb[gi] + per - 1) / per;
-            sTp[gi + 1] = acc;
-        }
-    }
-}
-
 }  // namespace tt
