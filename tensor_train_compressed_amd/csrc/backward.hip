@@ -990,7 +990,6 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     double* xpart = p->at<double>(p->lay.xsum);
     const CrossRef xr{p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                       p->at<int32_t>(p->lay.run_start), p->L};
-    constexpr int PR = N1 * N2 * R;
     const int64_t nwin = (p->L + kWin - 1) / kWin;
     // set-up (first kPrepBlocks workgroups) and the grad-row sums in one launch
     const PrepArgs pa{acc1, p->extent[0], acc3, bucket3 ? 0 : p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
