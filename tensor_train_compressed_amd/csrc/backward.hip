@@ -510,13 +510,13 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
 // lane order the run kernel reads it (store_prefix_lanes). Skipped when the
 // forward kept P on this plan for the same G1 and G2.
 template <int N1, int N2, int R>
-__global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t nb,
+__global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t nb,
                                                  const int32_t* __restrict__ run_i3,
                                                  const float* __restrict__ g1, const float* __restrict__ g2,
                                                  float* __restrict__ pbuf) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int SG = B::SG;
-    static_assert(64 * B::WAVES == 512, "shape");
+    static_assert(64 * B::WAVES == 256, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(512) void k_bwd_pfx(const BatchRec* __restrict__ re
         if (live) batch_prefix<N1, N2, R>(rwA, run_i3, f, sU, sRb, sI3, c);
         batch_fetch<N1, N2, R>(rwB, run_i3, g1, g2, f);
         if (live) {
-            store_prefix_lanes<N1, N2, R, 512>(sU, c.g0, c.ng, pbuf);
+            store_prefix_lanes<N1, N2, R, 256>(sU, c.g0, c.ng, pbuf);
             __syncthreads();
         }
         rwA = rwB;
@@ -1014,7 +1014,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
             const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
-            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(512), lds, s,
+            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(256), lds, s,
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
                                p->at<float>(p->lay.pbuf));
             TT_LAUNCH_CHECK();

@@ -209,10 +209,10 @@ struct FwdTiles {
 // batch's prologue costs no exposed memory round trip; slots without a group
 // cost a record read.
 template <int N1, int N2, int R, int N3, bool KEEP>
-__global__ __launch_bounds__(512, 4) void k_fwd_batch(FwdArgs a, int64_t nb) {
+__global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t nb) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int SG = B::SG;
-    static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 512, "shape");
+    static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 256, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512, 4) void k_fwd_batch(FwdArgs a, int64_t nb) {
         }
         batch_fetch<N1, N2, R>(rwB, a.run_i3, a.g1, a.g2, f);
         if (live) {
-            if (KEEP) store_prefix_lanes<N1, N2, R, 512>(sU, c.g0, c.ng, a.pbuf);
+            if (KEEP) store_prefix_lanes<N1, N2, R, 256>(sU, c.g0, c.ng, a.pbuf);
             tl.run(a, c, sU, sRb, sI3);
             __syncthreads();   // sU is the next prologue's
         }

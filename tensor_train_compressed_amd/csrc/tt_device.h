@@ -50,7 +50,7 @@ struct PrefixBatch {
     static constexpr int MR = SG * N1, MTP = MR / 16, NT2 = N2R / 16, KS = R / 4;
     static constexpr int GS = N2R + 16;      // LDS row stride of the G2 slice
     static constexpr int AS = R + 4;         // LDS row stride of G1 rows and of P rows
-    static constexpr int WAVES = 8;
+    static constexpr int WAVES = 4;
     static constexpr int NTW = (NT2 + WAVES - 1) / WAVES;   // column tiles per wave
     static constexpr int G2_FLOATS = R * GS;
     static constexpr int G1_FLOATS = MR * AS;

@@ -44,7 +44,7 @@ constexpr int kFwdBatch = 8;
 constexpr int kStageSpare = 4;
 // Workgroups of the persistent forward batch kernel: two per CU (the kernel's
 // registers allow two 8-wave workgroups on a CU).
-constexpr int kFwdPersistBlocks = 2 * 256;
+constexpr int kFwdPersistBlocks = 3 * 256;
 // The backward's run kernel hands out row runs in ranges of about this many
 // (a group of more runs is split; smaller groups are never split).
 constexpr int kRunRange = 32;
