@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 // ---------------------------------------------------------------------------
 // Matrix-core path for the common shapes (n1 = 4, n3 = 4, shared n2 and R).
 //
-// One workgroup (8 waves) per batch of up to kFwdBatch prefix groups of one
+// One workgroup (4 waves) per batch of up to kFwdBatch prefix groups of one
 // (table, i2) slice: groups that share a G2 slice are adjacent in key order.
 // The workgroup reads the G2 slice into LDS once and forms the batch's prefixes
 // P_g = G1[i1(g)] x G2[i2] together, as one (4*batch) x (n2*R) x R product on

@@ -42,8 +42,8 @@ constexpr int kXcds = 8;
 constexpr int kFwdBatch = 8;
 // Spare stage rows after the L run rows (targets of inactive lanes' stores).
 constexpr int kStageSpare = 4;
-// Workgroups of the persistent forward batch kernel: two per CU (the kernel's
-// registers allow two 8-wave workgroups on a CU).
+// Workgroups (four waves each) of the persistent forward batch kernel: three
+// per CU (the kernel's registers and LDS allow no more).
 constexpr int kFwdPersistBlocks = 3 * 256;
 // The backward's run kernel hands out row runs in ranges of about this many
 // (a group of more runs is split; smaller groups are never split).
