@@ -1014,7 +1014,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
             const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
-            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(256), lds, s,
+            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
                                p->at<float>(p->lay.pbuf));
             TT_LAUNCH_CHECK();
