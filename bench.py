@@ -79,8 +79,8 @@ def forward_traffic():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; "
+              "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
