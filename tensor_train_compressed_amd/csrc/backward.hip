@@ -1058,6 +1058,9 @@ static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
                          tt_status* st) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
+    // k_bwd_dg2 stores each table's slices once: tables sharing G2 take the
+    // general path, which adds every table's terms
+    if (p->g2_overlap) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;

@@ -1023,6 +1023,19 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             p->extent[k] = std::max(p->extent[k], x.g_offset[k] + sz[k]);
         }
     }
+    // tables may share a core; a shared G2 needs a backward that adds the
+    // tables' dG2 terms (the matrix-core dG2 kernel stores each slice once)
+    {
+        std::vector<std::pair<int64_t, int64_t>> r2((size_t)T);
+        for (int32_t t = 0; t < T; ++t) {
+            const tt_emb_table& x = tables[t];
+            r2[t] = {x.g_offset[1], x.g_offset[1] + (int64_t)x.m[1] * x.rank * x.n[1] * x.rank};
+        }
+        std::sort(r2.begin(), r2.end());
+        p->g2_overlap = false;
+        for (size_t t = 1; t < r2.size(); ++t)
+            if (r2[t].first < r2[t - 1].second) p->g2_overlap = true;
+    }
     hipStream_t s = (hipStream_t)stream;
 
     auto fail = [&](tt_status e) { delete p; return e; };

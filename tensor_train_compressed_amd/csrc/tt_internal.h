@@ -177,6 +177,7 @@ struct tt_emb_plan_s {
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
     bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
     bool off4;                // every table's G1 and G2 offsets are multiples of 4 floats
+    bool g2_overlap;          // two tables' G2 ranges overlap (a shared core)
     bool p_kept;              // pbuf holds P of every group for kept_g1/kept_g2 (forward_train)
     const float* kept_g1;
     const float* kept_g2;

@@ -349,6 +349,20 @@ def test_backward_shared_g3_and_empty():
     _check_backward(q, "no lookups", chunk=32)
 
 
+def test_backward_shared_g1_g2():
+    # two tables reading one G1 and one G2 (same offsets), shapes of the
+    # matrix-core path: each shared core's gradient is the sum of both tables'
+    t1 = wl.Table(4 * 6 * 300, (4, 6, 300), (4, 8, 4), 32)
+    t2 = wl.Table(4 * 6 * 200, (4, 6, 200), (4, 8, 4), 32)
+    p = wl.make_custom([t1, t2], np.full(2 * 60, 7), seed=9, zipf_alpha=1.1, with_grad=True)
+    p.g1 = p.g1[:4 * 4 * 32].copy()
+    p.g2 = p.g2[:6 * 32 * 8 * 32].copy()
+    p.goff = p.goff.copy()
+    p.goff[1, 0] = 0
+    p.goff[1, 1] = 0
+    _check_backward(p, "shared G1 and G2", chunk=32)
+
+
 def test_backward_multitable_full_size_sampled():
     """The 26-table batch at full size (8.5 M lookups): dG3 through buckets of
     2,391 G3 rows, the planner's scans past 512 tiles. In each of the three
