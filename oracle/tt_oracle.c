@@ -160,62 +160,69 @@ int tto_forward(int32_t T, const int64_t* num_rows, const int64_t* m, const int6
  *   dG2[i2][r1][j2][r2] += sum_{j1,j3}    G1[i1][j1][r1] g[j1,j2,j3] G3[i3][r2][j3]
  *   dG3[i3][r2][j3]     += sum_{j1,j2,r1} G1[i1][j1][r1] G2[i2][r1][j2][r2] g[j1,j2,j3]
  *
- * Each core is handled in its own pass that walks slice by slice (parallel over
- * slices), visiting that slice's lookups in increasing l.
+ * Each core is handled in its own pass that walks slice by slice, visiting that
+ * slice's lookups in increasing l for each element (parallel over blocks of a
+ * slice's elements, so a slice that most lookups touch is not left to one
+ * thread).
  */
 typedef struct {
     int64_t t, i1, i2, i3, q;
 } tto_lk;
 
+/* The three contributions of one lookup k to elements [e0, e1) of the slice
+ * it touches (element numbering: the slice's own row-major order). Each
+ * element's term is a plain triple sum, added to the running total. */
 static void contrib_dg1(const tto_tab* x, const float* g2, const float* g3, const tto_lk* k,
-                        const float* g, double* d1 /* [n1][R] of slice i1 */) {
-    const int64_t n1 = x->n1, n2 = x->n2, n3 = x->n3, R = x->R;
+                        const float* g, double* d1 /* [n1][R] of slice i1 */, int64_t e0,
+                        int64_t e1) {
+    const int64_t n2 = x->n2, n3 = x->n3, R = x->R;
     const float* b = g2 + x->o2 + k->i2 * R * n2 * R;
     const float* c = g3 + x->o3 + k->i3 * R * n3;
-    for (int64_t j1 = 0; j1 < n1; ++j1)
-        for (int64_t r1 = 0; r1 < R; ++r1) {
-            double s = 0.0;
-            for (int64_t j2 = 0; j2 < n2; ++j2)
-                for (int64_t j3 = 0; j3 < n3; ++j3)
-                    for (int64_t r2 = 0; r2 < R; ++r2)
-                        s += (double)g[(j1 * n2 + j2) * n3 + j3] *
-                             (double)b[(r1 * n2 + j2) * R + r2] * (double)c[r2 * n3 + j3];
-            d1[j1 * R + r1] += s;
-        }
+    for (int64_t e = e0; e < e1; ++e) {
+        const int64_t j1 = e / R, r1 = e % R;
+        double s = 0.0;
+        for (int64_t j2 = 0; j2 < n2; ++j2)
+            for (int64_t j3 = 0; j3 < n3; ++j3)
+                for (int64_t r2 = 0; r2 < R; ++r2)
+                    s += (double)g[(j1 * n2 + j2) * n3 + j3] *
+                         (double)b[(r1 * n2 + j2) * R + r2] * (double)c[r2 * n3 + j3];
+        d1[e] += s;
+    }
 }
 
 static void contrib_dg2(const tto_tab* x, const float* g1, const float* g3, const tto_lk* k,
-                        const float* g, double* d2 /* [R][n2][R] of slice i2 */) {
+                        const float* g, double* d2 /* [R][n2][R] of slice i2 */, int64_t e0,
+                        int64_t e1) {
     const int64_t n1 = x->n1, n2 = x->n2, n3 = x->n3, R = x->R;
     const float* a = g1 + x->o1 + k->i1 * n1 * R;
     const float* c = g3 + x->o3 + k->i3 * R * n3;
-    for (int64_t r1 = 0; r1 < R; ++r1)
-        for (int64_t j2 = 0; j2 < n2; ++j2)
-            for (int64_t r2 = 0; r2 < R; ++r2) {
-                double s = 0.0;
-                for (int64_t j1 = 0; j1 < n1; ++j1)
-                    for (int64_t j3 = 0; j3 < n3; ++j3)
-                        s += (double)a[j1 * R + r1] * (double)g[(j1 * n2 + j2) * n3 + j3] *
-                             (double)c[r2 * n3 + j3];
-                d2[(r1 * n2 + j2) * R + r2] += s;
-            }
+    for (int64_t e = e0; e < e1; ++e) {
+        const int64_t r1 = e / (n2 * R), j2 = (e / R) % n2, r2 = e % R;
+        double s = 0.0;
+        for (int64_t j1 = 0; j1 < n1; ++j1)
+            for (int64_t j3 = 0; j3 < n3; ++j3)
+                s += (double)a[j1 * R + r1] * (double)g[(j1 * n2 + j2) * n3 + j3] *
+                     (double)c[r2 * n3 + j3];
+        d2[e] += s;
+    }
 }
 
 static void contrib_dg3(const tto_tab* x, const float* g1, const float* g2, const tto_lk* k,
-                        const float* g, double* d3 /* [R][n3] of slice i3 */) {
+                        const float* g, double* d3 /* [R][n3] of slice i3 */, int64_t e0,
+                        int64_t e1) {
     const int64_t n1 = x->n1, n2 = x->n2, n3 = x->n3, R = x->R;
     const float* a = g1 + x->o1 + k->i1 * n1 * R;
     const float* b = g2 + x->o2 + k->i2 * R * n2 * R;
-    for (int64_t r2 = 0; r2 < R; ++r2)
-        for (int64_t j3 = 0; j3 < n3; ++j3) {
-            double s = 0.0;
-            for (int64_t j1 = 0; j1 < n1; ++j1)
-                for (int64_t j2 = 0; j2 < n2; ++j2)
-                    for (int64_t r1 = 0; r1 < R; ++r1)
-                        s += (double)a[j1 * R + r1] * (double)b[(r1 * n2 + j2) * R + r2] *
-                             (double)g[(j1 * n2 + j2) * n3 + j3];
-            d3[r2 * n3 + j3] += s;
-        }
+    for (int64_t e = e0; e < e1; ++e) {
+        const int64_t r2 = e / n3, j3 = e % n3;
+        double s = 0.0;
+        for (int64_t j1 = 0; j1 < n1; ++j1)
+            for (int64_t j2 = 0; j2 < n2; ++j2)
+                for (int64_t r1 = 0; r1 < R; ++r1)
+                    s += (double)a[j1 * R + r1] * (double)b[(r1 * n2 + j2) * R + r2] *
+                         (double)g[(j1 * n2 + j2) * n3 + j3];
+        d3[e] += s;
+    }
 }
 
 /* 1 when two tables' core `which` (1, 2 or 3) occupy overlapping elements of
@@ -306,26 +313,48 @@ int tto_backward(int32_t T, const int64_t* num_rows, const int64_t* m, const int
         int64_t *start = NULL, *list = NULL, *tbase = NULL, S = 0;
         rc = bucket(T, tabs, lk, sel, L, which, &start, &list, &tbase, &S);
         if (rc != TTO_OK) break;
-        /* slices in parallel, unless slices of two tables share elements */
+        /* Work items are (slice, block of kEB elements of the slice): every
+         * element is summed by one thread over its slice's lookups in
+         * increasing l, so the result does not depend on the thread count.
+         * Items run in parallel unless slices of two tables share elements. */
         const int shared = cores_overlap(T, tabs, which);
+        const int64_t kEB = 16;
+        int64_t* ibase = (int64_t*)malloc(sizeof(int64_t) * (size_t)(S + 1));
+        if (!ibase) { free(start); free(list); free(tbase); rc = TTO_NO_MEMORY; break; }
+        ibase[0] = 0;
+        for (int64_t s = 0, t = 0; s < S; ++s) {
+            while (tbase[t + 1] <= s) ++t;
+            const tto_tab* x = &tabs[t];
+            const int64_t ne = which == 1 ? x->n1 * x->R : which == 2 ? x->R * x->n2 * x->R : x->R * x->n3;
+            ibase[s + 1] = ibase[s] + (start[s] == start[s + 1] ? 0 : (ne + kEB - 1) / kEB);
+        }
+        const int64_t nitems = ibase[S];
 #pragma omp parallel for schedule(dynamic, 1) if (!shared)
-        for (int64_t s = 0; s < S; ++s) {
-            if (start[s] == start[s + 1]) continue;
+        for (int64_t it = 0; it < nitems; ++it) {
+            int64_t lo = 0, hi = S;   /* the slice s with ibase[s] <= it < ibase[s + 1] */
+            while (hi - lo > 1) {
+                const int64_t mid = (lo + hi) / 2;
+                if (ibase[mid] <= it) lo = mid; else hi = mid;
+            }
+            const int64_t s = lo;
             int32_t t = 0;
             while (tbase[t + 1] <= s) ++t;
             const tto_tab* x = &tabs[t];
             const int64_t local = s - tbase[t];
+            const int64_t ne = which == 1 ? x->n1 * x->R : which == 2 ? x->R * x->n2 * x->R : x->R * x->n3;
+            const int64_t e0 = (it - ibase[s]) * kEB, e1 = e0 + kEB < ne ? e0 + kEB : ne;
             for (int64_t p = start[s]; p < start[s + 1]; ++p) {
                 const tto_lk* k = &lk[list[p]];
                 const float* g = grad_out + k->q * D;
                 if (which == 1)
-                    contrib_dg1(x, g2, g3, k, g, dg1 + x->o1 + local * x->n1 * x->R);
+                    contrib_dg1(x, g2, g3, k, g, dg1 + x->o1 + local * x->n1 * x->R, e0, e1);
                 else if (which == 2)
-                    contrib_dg2(x, g1, g3, k, g, dg2 + x->o2 + local * x->R * x->n2 * x->R);
+                    contrib_dg2(x, g1, g3, k, g, dg2 + x->o2 + local * x->R * x->n2 * x->R, e0, e1);
                 else
-                    contrib_dg3(x, g1, g2, k, g, dg3 + x->o3 + local * x->R * x->n3);
+                    contrib_dg3(x, g1, g2, k, g, dg3 + x->o3 + local * x->R * x->n3, e0, e1);
             }
         }
+        free(ibase);
         free(start); free(list); free(tbase);
     }
     free(tabs); free(lk); free(sel);
