@@ -112,8 +112,8 @@ def main():
 
     def step():
         pl = plan()
-        tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
-        tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
+        tok = tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
+        tte.tt_emb_backward_kept(pl, tok, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
         tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr, stream=stream)
         return pl
 
@@ -153,9 +153,21 @@ def main():
     fwd_ms = per_call_ms(lambda: tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream), reps)
     fwd_train_ms = per_call_ms(lambda: tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream),
                                reps)
-    # the backward as the step runs it: after forward_train, reusing the kept P
-    bwd_ms = per_call_ms(lambda: tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1],
-                                                     dg[2], stream=stream), reps)
+    # the backward as the step runs it: after forward_train, reusing the kept
+    # P (each call consumes the kept products, so every backward follows its
+    # own training forward; events bracket the backward alone)
+    def bwd_after_fwd_train_ms(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            tok = tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
+            e0.record(stream)
+            tte.tt_emb_backward_kept(pl, tok, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
+    bwd_ms = bwd_after_fwd_train_ms(reps)
     sgd_ms = per_call_ms(lambda: tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr,
                                                 stream=stream), reps)
     torch.cuda.synchronize()

@@ -62,7 +62,9 @@ typedef enum {
     TT_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits (see below)   */
     TT_ERR_WORKSPACE = -3,    /* workspace smaller than tt_emb_workspace_bytes      */
     TT_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed          */
-    TT_ERR_DEVICE_FLAG = -5   /* returned by tt_emb_get_error when the flag is set   */
+    TT_ERR_DEVICE_FLAG = -5,  /* returned by tt_emb_get_error when the flag is set   */
+    TT_ERR_STALE = -6         /* tt_emb_backward_kept: the token does not name the   */
+                              /* products the plan holds (see below)                 */
 } tt_status;
 
 /* Device error flag bits (tt_emb_get_error). */
@@ -127,22 +129,39 @@ tt_status tt_emb_forward(tt_emb_plan_t plan, const float* g1, const float* g2,
 
 /* Forward for training: the same result as tt_emb_forward, and the plan
  * also keeps each prefix group's shared partial product P = G1[i1] x G2[i2]
- * in its workspace, so that the next tt_emb_backward on this plan reuses it
- * instead of forming it again (the FlowTT pages' inter-block sharing of
- * reusable intermediates through checkpoint buffers: summary card, key
- * innovations; abstract). The kept products are used by tt_emb_backward only
- * when it is given the same g1 and g2 pointers; the caller must not change
- * the contents of G1 or G2 between the two calls (tt_emb_sgd on this plan
- * discards them). Shapes without the matrix-core path keep nothing. */
+ * in its workspace, for one following tt_emb_backward_kept on this plan
+ * (the FlowTT pages' sharing of reusable intermediates through checkpoint
+ * buffers: summary card, key innovations; abstract).
+ *   kept_token  receives a nonzero token naming the kept products, or 0 when
+ *               the plan's shape has no matrix-core backward and nothing was
+ *               kept (use tt_emb_backward then). May be NULL.
+ * The token stays valid until the next call on this plan that changes or
+ * uses the kept products: tt_emb_forward_train (a new token),
+ * tt_emb_backward or tt_emb_backward_kept (they overwrite them), tt_emb_sgd
+ * (the cores change). tt_emb_forward leaves it valid. */
 tt_status tt_emb_forward_train(tt_emb_plan_t plan, const float* g1, const float* g2,
-                               const float* g3, float* out, void* stream);
+                               const float* g3, float* out, uint64_t* kept_token, void* stream);
 
 /* Backward: dg1/dg2/dg3 (device, same packing and sizes as the cores) are
  * fully overwritten with the gradients of <grad_out, out>; slices that no
- * lookup touches are zero. grad_out is device float[T*B][D]. */
+ * lookup touches are zero. grad_out is device float[T*B][D]. Forms every
+ * prefix product again (it never uses products kept by
+ * tt_emb_forward_train) and ends the validity of any kept token. */
 tt_status tt_emb_backward(tt_emb_plan_t plan, const float* g1, const float* g2,
                           const float* g3, const float* grad_out, float* dg1, float* dg2,
                           float* dg3, void* stream);
+
+/* Backward that reuses the prefix products kept by the tt_emb_forward_train
+ * call that returned `kept_token`, instead of forming them again. Same
+ * results as tt_emb_backward, provided the caller has not changed the
+ * contents of G1 or G2 since that forward (the library cannot see such a
+ * change). Returns TT_ERR_STALE, and launches nothing, when the token is 0,
+ * is not the plan's current token (see tt_emb_forward_train), or g1/g2 are
+ * not the pointers the forward was given. The kept products are consumed:
+ * the token is no longer valid afterwards. */
+tt_status tt_emb_backward_kept(tt_emb_plan_t plan, uint64_t kept_token, const float* g1,
+                               const float* g2, const float* g3, const float* grad_out,
+                               float* dg1, float* dg2, float* dg3, void* stream);
 
 /* SGD step on every core element: G <- G - lr * dG (device buffers). */
 tt_status tt_emb_sgd(tt_emb_plan_t plan, float* g1, float* g2, float* g3, const float* dg1,
@@ -178,6 +197,28 @@ tt_status tt_emb_plan_counts(tt_emb_plan_t plan, int64_t* num_groups, int64_t* n
 
 /* Frees the host handle (the workspace stays the caller's). NULL is a no-op. */
 tt_status tt_emb_plan_destroy(tt_emb_plan_t plan);
+
+/* Which kernels a call on this plan runs (pure host query, no launch).
+ * The matrix-core path serves plans whose tables all share one shape among
+ * those this build instantiates, with G1 and G2 offsets that are multiples
+ * of 4 floats, 16-byte aligned g1 and g2, and m3 <= 1024; the backward's
+ * matrix-core path also needs tables that do not share a G2 core. Other
+ * plans take the generic kernels (scalar FMA, one workgroup per chunk, fp32
+ * atomics whose summation order varies from run to run). */
+#define TT_PATH_MATRIX_CORE 1
+#define TT_PATH_GENERIC 2
+typedef struct {
+    int32_t forward_path;     /* TT_PATH_* of tt_emb_forward / _forward_train        */
+    int32_t backward_path;    /* TT_PATH_* of tt_emb_backward / _backward_kept       */
+    int32_t keeps_prefix;     /* 1: tt_emb_forward_train keeps P (nonzero token)     */
+    int32_t dg3_by_rows;      /* 1: dG3 reduced per G3 row from per-run terms;       */
+                              /* 0: fp64 device atomics (G3 rows not aligned, or     */
+                              /* more than 8192 G3 rows in all)                      */
+    uint64_t workspace_bytes; /* the plan's workspace size (tt_emb_workspace_bytes)  */
+} tt_emb_path_info;
+
+tt_status tt_emb_query_paths(tt_emb_plan_t plan, const float* g1, const float* g2,
+                             tt_emb_path_info* info);
 
 /* Human-readable name of a status code (static storage). */
 const char* tt_emb_status_string(tt_status s);

@@ -19,21 +19,26 @@ from typing import Optional, Sequence
 __all__ = [
     "TTEmbError", "TTEmbLibraryMissing", "TT_OK", "TT_FLAG_BAD_INDEX", "TT_FLAG_BAD_OFFSETS",
     "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
-    "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_sgd", "tt_emb_get_error",
-    "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy", "Plan", "EXPORTS",
+    "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
+    "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
+    "tt_emb_query_paths", "TT_PATH_MATRIX_CORE", "TT_PATH_GENERIC", "TT_ERR_STALE", "Plan", "EXPORTS",
 ]
 
 TT_OK = 0
+TT_ERR_INVALID_ARG = -1
 TT_ERR_DEVICE_FLAG = -5
+TT_ERR_STALE = -6
+TT_PATH_MATRIX_CORE = 1
+TT_PATH_GENERIC = 2
 TT_FLAG_BAD_INDEX = 1
 TT_FLAG_BAD_OFFSETS = 2
 
 # Every symbol include/tt_emb.h declares.
 EXPORTS = (
     "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train",
-    "tt_emb_backward", "tt_emb_sgd",
+    "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
-    "tt_emb_status_string",
+    "tt_emb_query_paths", "tt_emb_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +66,12 @@ class _Table(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("g_offset", ctypes.c_int64 * 3)]
 
 
+class _PathInfo(ctypes.Structure):
+    _fields_ = [("forward_path", ctypes.c_int32), ("backward_path", ctypes.c_int32),
+                ("keeps_prefix", ctypes.c_int32), ("dg3_by_rows", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
 class _View(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "key", "i3", "bag_of", "perm", "sorted_i3", "sorted_bag", "group_key", "group_start",
@@ -85,8 +96,10 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_plan.argtypes = [P, i32, P, P, i64, i64, i32, P, ctypes.c_size_t, P,
                                     ctypes.POINTER(P)]
         lib.tt_emb_forward.argtypes = [P, P, P, P, P, P]
-        lib.tt_emb_forward_train.argtypes = [P, P, P, P, P, P]
+        lib.tt_emb_forward_train.argtypes = [P, P, P, P, P, ctypes.POINTER(ctypes.c_uint64), P]
         lib.tt_emb_backward.argtypes = [P, P, P, P, P, P, P, P, P]
+        lib.tt_emb_backward_kept.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, P, P]
+        lib.tt_emb_query_paths.argtypes = [P, P, P, ctypes.POINTER(_PathInfo)]
         lib.tt_emb_sgd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P]
         lib.tt_emb_get_error.argtypes = [P, ctypes.POINTER(i32), P]
         lib.tt_emb_plan_get_view.argtypes = [P, ctypes.POINTER(_View)]
@@ -94,9 +107,9 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_plan_destroy.argtypes = [P]
         lib.tt_emb_status_string.argtypes = [ctypes.c_int]
         lib.tt_emb_status_string.restype = ctypes.c_char_p
-        for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_sgd",
-                     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts",
-                     "tt_emb_plan_destroy"):
+        for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward",
+                     "tt_emb_backward_kept", "tt_emb_sgd", "tt_emb_get_error", "tt_emb_plan_get_view",
+                     "tt_emb_plan_counts", "tt_emb_plan_destroy", "tt_emb_query_paths"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -129,7 +142,11 @@ def make_tables(tables: Sequence, g_offsets) -> ctypes.Array:
     return arr
 
 
-def _dev_ptr(t, dtype_name: str, what: str) -> Optional[int]:
+def _dev_ptr(t, dtype_name: str, what: str, numel: Optional[int] = None,
+             at_least: bool = False) -> Optional[int]:
+    """data_ptr() of a contiguous device tensor of the given dtype; with
+    `numel`, its element count must equal it (or, with at_least, reach it):
+    the C ABI takes bare pointers and cannot check extents itself."""
     if t is None:
         return None
     if not t.is_cuda:
@@ -138,7 +155,24 @@ def _dev_ptr(t, dtype_name: str, what: str) -> Optional[int]:
         raise ValueError(f"{what} must be {dtype_name}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
+    if numel is not None:
+        n = int(t.numel())
+        if (n < numel) if at_least else (n != numel):
+            raise ValueError(f"{what} has {n} elements, needs {'at least ' if at_least else ''}{numel}")
     return t.data_ptr()
+
+
+def core_extents(tables_c) -> tuple:
+    """Elements of the packed G1, G2, G3 buffers the tables use (the same
+    bound applies to the gradient buffers)."""
+    ext = [0, 0, 0]
+    for t in tables_c:
+        n1, n2, n3 = t.n[0], t.n[1], t.n[2]
+        R = t.rank
+        sizes = (t.m[0] * n1 * R, t.m[1] * R * n2 * R, t.m[2] * R * n3)
+        for k in range(3):
+            ext[k] = max(ext[k], int(t.g_offset[k]) + sizes[k])
+    return tuple(ext)
 
 
 def _stream(stream) -> Optional[int]:
@@ -151,12 +185,14 @@ def _stream(stream) -> Optional[int]:
 
 
 class Plan:
-    """Owns a tt_emb_plan_t; keeps the workspace tensor alive alongside it."""
+    """Owns a tt_emb_plan_t; keeps the workspace tensor alive alongside it,
+    and the sizes the binding checks tensors against."""
 
-    def __init__(self, handle: int, workspace, L: int, TB: int, D: int):
+    def __init__(self, handle: int, workspace, L: int, TB: int, D: int, extents=(0, 0, 0)):
         self.handle = handle
         self.workspace = workspace
         self.L, self.TB, self.D = L, TB, D
+        self.extents = tuple(extents)
 
     def __del__(self):
         if getattr(self, "handle", None):
@@ -165,6 +201,10 @@ class Plan:
             except Exception:
                 pass
             self.handle = None
+
+    def cores(self, g1, g2, g3, names=("g1", "g2", "g3"), dtype="float32"):
+        return tuple(_dev_ptr(x, dtype, nm, e, at_least=True)
+                     for x, nm, e in zip((g1, g2, g3), names, self.extents))
 
 
 def tt_emb_workspace_bytes(tables_c, L: int, B: int, chunk: int) -> int:
@@ -178,6 +218,7 @@ def tt_emb_plan(tables_c, indices, offsets, B: int, chunk: int, workspace=None,
     here with torch if None)."""
     lib = load_library()
     L = int(indices.numel())
+    T = len(tables_c)
     need = tt_emb_workspace_bytes(tables_c, L, B, chunk)
     if need == 0:
         raise TTEmbError(-1, "tt_emb_workspace_bytes")
@@ -185,44 +226,61 @@ def tt_emb_plan(tables_c, indices, offsets, B: int, chunk: int, workspace=None,
         import torch
         workspace = torch.empty(need, dtype=torch.uint8, device=indices.device)
     h = ctypes.c_void_p()
-    st = lib.tt_emb_plan(tables_c, len(tables_c), _dev_ptr(indices, "int64", "indices"),
-                         _dev_ptr(offsets, "int64", "offsets"), L, B, chunk,
+    st = lib.tt_emb_plan(tables_c, T, _dev_ptr(indices, "int64", "indices"),
+                         _dev_ptr(offsets, "int64", "offsets", T * B + 1), L, B, chunk,
                          _dev_ptr(workspace, "uint8", "workspace"), workspace.numel(),
                          _stream(stream), ctypes.byref(h))
     _check(st, "tt_emb_plan")
     D = int(tables_c[0].n[0] * tables_c[0].n[1] * tables_c[0].n[2])
-    return Plan(h.value, workspace, L, len(tables_c) * B, D)
+    return Plan(h.value, workspace, L, T * B, D, core_extents(tables_c))
 
 
 def tt_emb_forward(plan: Plan, g1, g2, g3, out, stream=None):
     _check(load_library().tt_emb_forward(
-        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
-        _dev_ptr(g3, "float32", "g3"), _dev_ptr(out, "float32", "out"), _stream(stream)),
-        "tt_emb_forward")
+        plan.handle, *plan.cores(g1, g2, g3), _dev_ptr(out, "float32", "out", plan.TB * plan.D),
+        _stream(stream)), "tt_emb_forward")
 
 
-def tt_emb_forward_train(plan: Plan, g1, g2, g3, out, stream=None):
-    """Forward that also keeps the prefix products for the next backward on the plan."""
+def tt_emb_forward_train(plan: Plan, g1, g2, g3, out, stream=None) -> int:
+    """Forward that also keeps the prefix products for tt_emb_backward_kept;
+    returns the token naming them (0: nothing kept, use tt_emb_backward)."""
+    tok = ctypes.c_uint64(0)
     _check(load_library().tt_emb_forward_train(
-        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
-        _dev_ptr(g3, "float32", "g3"), _dev_ptr(out, "float32", "out"), _stream(stream)),
-        "tt_emb_forward_train")
+        plan.handle, *plan.cores(g1, g2, g3), _dev_ptr(out, "float32", "out", plan.TB * plan.D),
+        ctypes.byref(tok), _stream(stream)), "tt_emb_forward_train")
+    return int(tok.value)
 
 
 def tt_emb_backward(plan: Plan, g1, g2, g3, grad_out, dg1, dg2, dg3, stream=None):
     _check(load_library().tt_emb_backward(
-        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
-        _dev_ptr(g3, "float32", "g3"), _dev_ptr(grad_out, "float32", "grad_out"),
-        _dev_ptr(dg1, "float32", "dg1"), _dev_ptr(dg2, "float32", "dg2"),
-        _dev_ptr(dg3, "float32", "dg3"), _stream(stream)), "tt_emb_backward")
+        plan.handle, *plan.cores(g1, g2, g3),
+        _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D),
+        *plan.cores(dg1, dg2, dg3, ("dg1", "dg2", "dg3")), _stream(stream)), "tt_emb_backward")
+
+
+def tt_emb_backward_kept(plan: Plan, kept_token: int, g1, g2, g3, grad_out, dg1, dg2, dg3,
+                         stream=None):
+    """Backward reusing the prefix products named by kept_token (raises
+    TTEmbError with status TT_ERR_STALE when they are not the plan's)."""
+    _check(load_library().tt_emb_backward_kept(
+        plan.handle, ctypes.c_uint64(int(kept_token)), *plan.cores(g1, g2, g3),
+        _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D),
+        *plan.cores(dg1, dg2, dg3, ("dg1", "dg2", "dg3")), _stream(stream)), "tt_emb_backward_kept")
 
 
 def tt_emb_sgd(plan: Plan, g1, g2, g3, dg1, dg2, dg3, lr: float, stream=None):
     _check(load_library().tt_emb_sgd(
-        plan.handle, _dev_ptr(g1, "float32", "g1"), _dev_ptr(g2, "float32", "g2"),
-        _dev_ptr(g3, "float32", "g3"), _dev_ptr(dg1, "float32", "dg1"),
-        _dev_ptr(dg2, "float32", "dg2"), _dev_ptr(dg3, "float32", "dg3"), float(lr),
-        _stream(stream)), "tt_emb_sgd")
+        plan.handle, *plan.cores(g1, g2, g3), *plan.cores(dg1, dg2, dg3, ("dg1", "dg2", "dg3")),
+        float(lr), _stream(stream)), "tt_emb_sgd")
+
+
+def tt_emb_query_paths(plan: Plan, g1, g2) -> dict:
+    """Which kernels the plan's calls run with these cores (host query)."""
+    info = _PathInfo()
+    _check(load_library().tt_emb_query_paths(plan.handle, ctypes.c_void_p(g1.data_ptr()),
+                                             ctypes.c_void_p(g2.data_ptr()), ctypes.byref(info)),
+           "tt_emb_query_paths")
+    return {name: int(getattr(info, name)) for name, _ in _PathInfo._fields_}
 
 
 def tt_emb_get_error(plan: Plan, stream=None) -> int:

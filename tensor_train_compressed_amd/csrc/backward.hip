@@ -196,6 +196,7 @@ struct PrepArgs {
     int32_t* i3start;
     const int32_t* group_rbase;
     int32_t* xpiece;
+    int64_t xcap;
     int32_t* gdone;
     int32_t* ctrl;
 };
@@ -255,17 +256,23 @@ __device__ __forceinline__ void bwd_prep(const PrepArgs& pa, int64_t blk) {
     // groups of more than kRunRange runs are split into pieces of kRunRange
     // runs: list their pieces, a group's pieces together and in order (the
     // run kernel takes these first, then one piece per other group)
+    // (at most xcap pieces: a group whose pieces do not all fit is not listed,
+    // gdone = -1, and runs whole; the slots it took below xcap are marked
+    // empty with group -1)
     const int64_t U = ctrl[CTRL_NUM_GROUPS];
     for (int64_t g = tid; g < U; g += nth) {
-        pa.gdone[g] = 0;
+        int32_t gd = 0;
         const int32_t np = (pa.group_rbase[g + 1] - pa.group_rbase[g] + kRunRange - 1) / kRunRange;
         if (np > 1) {
             const int32_t base = atomicAdd(ctrl + CTRL_NUM_XPIECES, np);
-            for (int32_t k = 0; k < np; ++k) {
-                pa.xpiece[2 * (base + k)] = (int32_t)g;
+            const bool fits = (int64_t)base + np <= pa.xcap;
+            if (!fits) gd = -1;
+            for (int32_t k = 0; k < np && (int64_t)base + k < pa.xcap; ++k) {
+                pa.xpiece[2 * (base + k)] = fits ? (int32_t)g : -1;
                 pa.xpiece[2 * (base + k) + 1] = k;
             }
         }
+        pa.gdone[g] = gd;
     }
 }
 
@@ -285,11 +292,12 @@ struct SlotArgs {
     const int32_t* i3start;
     const int32_t* run_bkt;
     const int32_t* run_rank;
-    int32_t* run_slot;
+    int32_t* bucket_runs;
 };
 
-// Workgroups past the first nspan (when sl.run_slot is set): each run's c3
-// row, its bucket's start plus its rank in the bucket, for the run kernel.
+// Workgroups past the first nspan (when bucketing dG3): each run's place in
+// the list of its bucket's runs (its bucket's start plus its rank in the
+// bucket), read by k_bwd_dg3.
 template <int DL>
 __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, int32_t* __restrict__ xcnt,
                                                     CrossRef x, float* __restrict__ S,
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, 
     constexpr int D = 64 * DL, WV = 16, SHORT = 16;
     if ((int64_t)blockIdx.x >= nspan) {
         const int64_t r = ((int64_t)blockIdx.x - nspan) * blockDim.x + threadIdx.x;
-        if (r < ctrl[CTRL_NUM_RUNS]) sl.run_slot[r] = sl.i3start[sl.run_bkt[r]] + sl.run_rank[r];
+        if (r < ctrl[CTRL_NUM_RUNS]) sl.bucket_runs[sl.i3start[sl.run_bkt[r]] + sl.run_rank[r]] = (int32_t)r;
         return;
     }
     static_assert(SHORT >= WV, "a long run leaves the span it starts in");
@@ -541,81 +549,87 @@ __global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ re
     }
 }
 
-// Run pieces. A piece is a group's runs [kRunRange*k, kRunRange*(k+1)). The
-// pieces of the groups with more than kRunRange runs come first, from the
-// list the prep kernel wrote (X of them; the longest work starts first), then
-// piece X + g is group g whole, or nothing if g was split.
+// Run units. A piece is kRunRange consecutive runs of one group. Units
+// 0..X-1 are the listed pieces of the groups with more than kRunRange runs
+// (bwd_prep's list: a group's pieces together and in order, the largest work
+// first; -1 in place of a group that did not fit the list's capacity); unit
+// X + g is group g whole when it has at most kRunRange runs or was not
+// listed, and nothing otherwise.
 struct RunsArgs {
     const TabDev* desc;
     int32_t T;
     const int32_t* ctrl;
     const int32_t* xpiece;
+    int64_t xcap;              // capacity of the piece list
     const int32_t* group_rbase;
     const int32_t* group_key;
     const int32_t* run_i3;
     const float* S;
-    const float* pbuf;
+    float* pbuf;               // P per group; each group's dP is written over it
     const float* g3;
     double* dg3;
-    float* dpg;
     double* dpart;
-    int32_t* gdone;   // per group: pieces finished (zeroed by bwd_prep)
+    int32_t* gdone;            // per group: pieces finished (zeroed by bwd_prep); -1: not listed
 };
 
-// One wave per piece (persistent, static stride), the group's P in registers;
+// One wave per unit (persistent, static stride), the group's P in registers;
 // four runs at a time (lane group q takes run t0 + q):
 //   dG3[i3] += P^T S          fp32 products over p, handed to add3 (device
-//                              atomics, or a row per run reduced later) with
-//                              the word pre(run, i3) gave for the run at the
-//                              piece's start
-//   dP      += S G3[i3]^T     fp64 products and sums over the piece
-// then dP goes to the group's row (rounded to fp32), or, for a piece of a
-// split group, to the piece's own fp64 slot; the group's last piece to finish
-// (a counter per group) adds the group's slots in piece order and rounds the
-// sum into the group's row once.
-template <int N1, int N2, int R, int N3, class Pre, class Add3>
-__device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3) {
+//                              atomics, or the run's own row, reduced later)
+//   dP      += S G3[i3]^T     fp64 products and sums over the unit
+// then dP is written, rounded to fp32, over the group's P (every piece of the
+// group has read P by then), or, for a listed piece, its fp64 partial goes to
+// the piece's own slot and the group's last piece to finish (a counter per
+// group) adds the group's slots in piece order and writes the sum once. A
+// whole group of more than kRunRange runs (one that did not fit the list) is
+// walked kRunRange runs at a time, dP summed across them in registers.
+template <int N1, int N2, int R, int N3, class Add3>
+__device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     constexpr int NP = N1 * N2, D = NP * N3, PR = NP * R, MT = NP / 16, RT = R / 16, KSP = NP / 4;
     constexpr int KQ = KSP / 4, CN = R * N3, W = kRunRange;
     static_assert(N3 == 4 && NP % 16 == 0 && R % 16 == 0 && W <= 64 && PR % 256 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     const int lk = col / N3, j3 = col % N3;
-    const int32_t U = a.ctrl[CTRL_NUM_GROUPS], X = a.ctrl[CTRL_NUM_XPIECES];
-    const int64_t npieces = (int64_t)X + U;
+    const int32_t U = a.ctrl[CTRL_NUM_GROUPS];
+    const int32_t X = (int32_t)min((int64_t)a.ctrl[CTRL_NUM_XPIECES], a.xcap);
+    const int64_t nunits = (int64_t)X + U;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    // A piece's words (group, part, its group's runs) and, per lane j, the i3
-    // and add3 word of its run s + j are fetched during the piece before it:
-    // the words at that piece's start, the run words after its tiles.
+    // A unit's words (group, mode, runs) and, per lane j, the i3 of its run
+    // s + j are fetched during the unit before it: the words at that unit's
+    // start, the run i3 values after its tiles.
     struct Words {
         int64_t g;
-        int32_t part, gs, ge;
+        int32_t mode;          // 0: nothing, 1: a listed piece, 2: the whole group
+        int32_t part, s, e;    // piece number; first run and end of the unit's runs
     };
     auto words_of = [&](int64_t kk, Words& w) {
-        w.g = kk - X;
-        w.part = 0;
+        int64_t g = kk - X;
+        int32_t part = 0, mode = 2;
         if (kk < X) {
-            w.g = a.xpiece[2 * kk];
-            w.part = a.xpiece[2 * kk + 1];
+            g = a.xpiece[2 * kk];
+            part = a.xpiece[2 * kk + 1];
+            mode = 1;
+            if (g < 0) { g = 0; mode = 0; }
         }
-        w.gs = a.group_rbase[w.g];
-        w.ge = a.group_rbase[w.g + 1];
-    };
-    auto run_words = [&](const Words& w, int32_t& i3w, int32_t& xw) {
-        const int32_t s = w.gs + W * w.part, e = min(w.ge, s + W);
-        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[w.g])].o3;
-        i3w = a.run_i3[min(s + lane, e - 1)];
-        xw = pre(min(s + lane, e - 1), (int32_t)(o3 / CN) + i3w);
+        const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
+        if (mode == 2 && ge - gs > W && a.gdone[g] >= 0) mode = 0;   // listed: done piece by piece
+        w.g = g;
+        w.mode = mode;
+        w.part = part;
+        w.s = mode == 1 ? gs + W * part : gs;
+        w.e = mode == 1 ? min(ge, w.s + W) : ge;
     };
     int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (k >= npieces) return;
+    if (k >= nunits) return;
     Words cur;
-    int32_t i3l, xl;   // lane j: i3 and add3's word of run s + j of the current piece
+    int32_t i3l;   // lane j: i3 of run s + j of the runs being walked
     words_of(k, cur);
-    run_words(cur, i3l, xl);
-    for (; k < npieces; k += nw) {
+    i3l = a.run_i3[min(cur.s + lane, cur.e - 1)];
+    for (; k < nunits; k += nw) {
         Words nxt;
-        words_of(min(k + nw, npieces - 1), nxt);
+        words_of(min(k + nw, nunits - 1), nxt);
         const int64_t g = cur.g;
+        if (cur.mode != 0) {
         // P: its address needs only g
         floatx4 preg[RT][KQ];
         const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
@@ -623,10 +637,6 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
-        const int32_t gs = cur.gs, ge = cur.ge, part = cur.part;
-        const bool split = ge - gs > W;
-        if (!split || k < X) {   // a split group is done piece by piece from the list
-        const int32_t s = gs + W * part, e = min(ge, s + W);
         const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
         doublex4 dacc[MT][RT];
 #pragma unroll
@@ -638,12 +648,13 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
         struct TileOps {
             floatx4 av[MT], bq[RT];
             float bv[KSP];
-            int32_t i3q, xq;
+            int32_t i3q;
         };
+        for (int32_t s = cur.s;;) {
+        const int32_t e = min(cur.e, s + W);
         auto load_tile = [&](int32_t t0, TileOps& o) {
             const int32_t rq = t0 + q < e ? t0 + q : t0;
             o.i3q = __shfl(i3l, rq - s);
-            o.xq = __shfl(xl, rq - s);
             const float* Sq = a.S + (int64_t)rq * D;
             const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
 #pragma unroll
@@ -664,7 +675,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
 #pragma unroll
                 for (int s2 = 0; s2 < KSP; ++s2)
                     cc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
-                if (okq) add3(o3 + (int64_t)o.i3q * CN, (16 * rt + col) * N3, o.xq, cc);
+                if (okq) add3(o3 + (int64_t)o.i3q * CN, (16 * rt + col) * N3, t0 + q, cc);
             }
             // dP: K = (run q, j3 = step), fp64 products and sums (a hot
             // group's dP adds up hundreds of runs of large S); a run past the
@@ -690,9 +701,14 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
             tile(t0 + 4, TB);
             if (t0 + 8 >= e) break;
         }
+        s = e;
+        if (s >= cur.e) break;
+        i3l = a.run_i3[min(s + lane, cur.e - 1)];   // a whole group's next kRunRange runs
+        }
         // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col];
-        // a piece of a split group keeps its fp64 partial in its own slot
-        float* dst = a.dpg + g * PR;
+        // a listed piece keeps its fp64 partial in its own slot
+        const bool piece = cur.mode == 1;
+        float* dst = a.pbuf + g * PR;
         double* dpp = a.dpart + k * PR;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -701,21 +717,22 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int idx = (16 * mt + q + 4 * v) * R + 16 * nt + col;
-                    if (split)   // device-scope stores: written through to the level all XCDs share
+                    if (piece)   // device-scope stores: written through to the level all XCDs share
                         __hip_atomic_store(dpp + idx, dacc[mt][nt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     else
                         dst[idx] = (float)dacc[mt][nt][v];
                 }
-        if (split) {
+        if (piece) {
             // count the piece once its slot's stores have completed (a wait,
             // not a device-scope fence: that one writes back the whole L2)
+            const int32_t gs = a.group_rbase[g], ge = a.group_rbase[g + 1];
             const int32_t np = (ge - gs + W - 1) / W;
             wait_vmem_done();
             int32_t done = 0;
             if (lane == 0) done = atomicAdd(a.gdone + g, 1) == np - 1 ? 1 : 0;
             if (__builtin_amdgcn_readfirstlane(done)) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                const double* first = a.dpart + (k - part) * PR;   // the group's pieces are listed in order
+                const double* first = a.dpart + (k - cur.part) * PR;   // the group's pieces are listed in order
                 for (int e0 = 0; e0 < PR; e0 += 64 * 4) {
                     double t[4] = {0.0, 0.0, 0.0, 0.0};
                     for (int32_t j = 0; j < np; ++j) {
@@ -730,45 +747,43 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Pre pre, Add3 add3)
             }
         }
         }
-        run_words(nxt, i3l, xl);
+        i3l = a.run_i3[min(nxt.s + lane, nxt.e - 1)];
         cur = nxt;
     }
 }
 
 // dG3 added straight to the fp64 accumulator with device atomics (tables
-// sharing their G3 slices' rows make this the general path)
+// whose G3 rows are not aligned to R*n3, or too many G3 rows)
 template <int N1, int N2, int R, int N3>
 __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
-    runs_body<N1, N2, R, N3>(a, [](int32_t, int32_t) { return 0; },
-                             [&](int64_t row, int within, int32_t, const floatx4& c) {
+    runs_body<N1, N2, R, N3>(a, [&](int64_t row, int within, int32_t, const floatx4& c) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) atomicAdd(a.dg3 + row + within + v, (double)c[v]);
     });
 }
 
-// One table: each run's dG3 term P^T S is stored as its own row, in the
-// bucket of its i3 (the planner ranked the runs inside their buckets), and
-// k_bwd_dg3 sums each bucket. Device atomics from every CU on the
-// same few hundred G3 slices saturate the memory-side atomic units, and LDS
-// float atomics are slow on the CU; plain stores avoid both.
+// Each run's dG3 term P^T S is stored as a row of its own: row r of c3 (at
+// row stride c3s; c3 is the S buffer itself when an S row holds R*n3 floats,
+// each run's term then replacing its S, which only this wave reads), and
+// k_bwd_dg3 sums the rows of each G3 row's bucket. Device atomics from every
+// CU on the same few hundred G3 slices saturate the memory-side atomic
+// units, and LDS float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256, 3) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3,
-                                                        const int32_t* __restrict__ run_slot) {
-    constexpr int CN = R * N3;
-    // add3's word: the run's c3 row in the bucket of its G3 row
-    runs_body<N1, N2, R, N3>(a, [&](int32_t run, int32_t) { return run_slot[run]; },
-                             [&](int64_t, int within, int32_t slot, const floatx4& c) {
-        *reinterpret_cast<floatx4*>(c3 + (int64_t)slot * CN + within) = c;
+__global__ __launch_bounds__(256, 3) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3, int64_t c3s) {
+    runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
+        *reinterpret_cast<floatx4*>(c3 + (int64_t)run * c3s + within) = c;
     });
 }
 
-// dG3[i3] = sum of the c3 rows of bucket i3 (the rows of the runs with that
-// i3, contiguous), in fp64: one workgroup per G3 slice, wave w on rows w,
-// w + 16, ... of the bucket, GB rows in flight; the 16 waves' sums are added
-// in LDS at the end.
+// dG3[i3] = sum of the c3 rows of the runs in bucket i3 (bucket_runs lists
+// them), in fp64: one workgroup per G3 row, wave w on rows w, w + 16, ... of
+// the bucket, GB rows in flight; the 16 waves' sums are added in LDS at the
+// end.
 template <int CN>
 __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3start,
-                                                  const float* __restrict__ c3, float* __restrict__ dg3) {
+                                                  const int32_t* __restrict__ bucket_runs,
+                                                  const float* __restrict__ c3, int64_t c3s,
+                                                  float* __restrict__ dg3) {
     constexpr int PL = CN / 64, WAVES = 16, GB = 16;
     static_assert(CN % 64 == 0, "shape");
     __shared__ double red[WAVES][CN];
@@ -779,10 +794,12 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3
 #pragma unroll
     for (int k = 0; k < PL; ++k) acc[k] = 0.0;
     for (int32_t j0 = b + w; j0 < e; j0 += WAVES * GB) {
+        // lane j < GB: the run of bucket row j0 + WAVES * j
+        const int32_t rl = bucket_runs[min(j0 + WAVES * min(lane, GB - 1), e - 1)];
         float x[GB][PL];
 #pragma unroll
         for (int j = 0; j < GB; ++j) {
-            const float* src = c3 + (int64_t)min(j0 + WAVES * j, e - 1) * CN + lane * PL;
+            const float* src = c3 + (int64_t)__builtin_amdgcn_readlane(rl, j) * c3s + lane * PL;
 #pragma unroll
             for (int k = 0; k < PL; ++k) x[j][k] = src[k];
         }
@@ -974,7 +991,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
 template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
-                                 float* dg3, hipStream_t s) {
+                                 float* dg3, bool kept, hipStream_t s) {
     // dG3 reduced per G3 row from per-run terms (k_bwd_dg3 writes every row
     // of the buffer, gaps included), unless some table's G3 rows are not
     // aligned to R*n3: then device atomics into an fp64 accumulator
@@ -984,66 +1001,70 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         tt_status st = fill32(dg2, 0u, p->extent[1], s);
         if (st != TT_OK) return st;
     }
-    constexpr int DL = N1 * N2 * N3 / 64;
+    constexpr int DL = N1 * N2 * N3 / 64, D = N1 * N2 * N3, CN = R * N3;
     double* acc1 = p->at<double>(p->lay.acc1);
     double* acc3 = p->at<double>(p->lay.acc3);
     double* xpart = p->at<double>(p->lay.xsum);
+    float* S = p->at<float>(p->lay.stage);
+    float* pbuf = p->at<float>(p->lay.pbuf);
     const CrossRef xr{p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                       p->at<int32_t>(p->lay.run_start), p->L};
     const int64_t nwin = (p->L + kWin - 1) / kWin;
     // set-up (first kPrepBlocks workgroups) and the grad-row sums in one launch
     const PrepArgs pa{acc1, p->extent[0], acc3, bucket3 ? 0 : p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
                       p->at<int32_t>(p->lay.i3cnt), bucket3 ? p->nb3 : 0, p->at<int32_t>(p->lay.i3start),
-                      p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece),
+                      p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                       p->at<int32_t>(p->lay.gdone), p->ctrl()};
     const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
-                     p->at<int32_t>(p->lay.run_start), p->L, gout, p->at<float>(p->lay.stage), xpart};
+                     p->at<int32_t>(p->lay.run_start), p->L, gout, S, xpart};
     hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
                        sa, pa);
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
-        const bool kept = p->p_kept && p->kept_g1 == g1 && p->kept_g2 == g2;
-        // cut-run sums (nspan workgroups) and, with buckets, the runs' c3 rows
+        // cut-run sums (nspan workgroups) and, with buckets, the bucket lists
         const int64_t nspan = std::min<int64_t>(std::max<int64_t>((nwin + 15) / 16, 1), 1024);
         const SlotArgs sl{p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.run_bkt),
-                          p->at<int32_t>(p->lay.run_rank), p->at<int32_t>(p->lay.run_slot)};
+                          p->at<int32_t>(p->lay.run_rank), p->at<int32_t>(p->lay.bucket_runs)};
         const int64_t nslot = bucket3 ? (p->L + 1023) / 1024 : 0;
         hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)(nspan + nslot)), dim3(1024), 0, s, xpart,
-                           p->at<int32_t>(p->lay.xcnt), xr, p->at<float>(p->lay.stage), p->ctrl(), nspan, sl);
+                           p->at<int32_t>(p->lay.xcnt), xr, S, p->ctrl(), nspan, sl);
         TT_LAUNCH_CHECK();
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
             const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
             hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
-                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2,
-                               p->at<float>(p->lay.pbuf));
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
             TT_LAUNCH_CHECK();
         }
-        RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece),
+        RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
-                    p->at<int32_t>(p->lay.run_i3), p->at<float>(p->lay.stage), p->at<float>(p->lay.pbuf), g3,
-                    acc3, p->at<float>(p->lay.dpg), p->at<double>(p->lay.dpart), p->at<int32_t>(p->lay.gdone)};
+                    p->at<int32_t>(p->lay.run_i3), S, pbuf, g3, acc3, p->at<double>(p->lay.dpart),
+                    p->at<int32_t>(p->lay.gdone)};
         if (bucket3) {
-            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra,
-                               p->at<float>(p->lay.c3), p->at<int32_t>(p->lay.run_slot));
+            // each run's dG3 term over its own S row when the row holds it
+            float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);
+            const int64_t c3s = CN <= D ? D : CN;
+            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra, c3,
+                               c3s);
             TT_LAUNCH_CHECK();
-            hipLaunchKernelGGL((k_bwd_dg3<R * N3>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
-                               p->at<int32_t>(p->lay.i3start), p->at<float>(p->lay.c3), dg3);
+            hipLaunchKernelGGL((k_bwd_dg3<CN>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
+                               p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3);
         } else {
             hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
         TT_LAUNCH_CHECK();
     }
     {
+        // dP of every group now sits over its P
         const int64_t w2 = p->n_i2 * (N2 * R / 16);
         hipLaunchKernelGGL((k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(), p->T,
                            p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key),
-                           p->at<float>(p->lay.dpg), g1, dg2, p->n_i2);
+                           pbuf, g1, dg2, p->n_i2);
         TT_LAUNCH_CHECK();
         const int64_t w1 = p->n_fb;
         if (w1 > 0) {
             hipLaunchKernelGGL((k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
-                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<float>(p->lay.dpg), g2, acc1);
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, pbuf, g2, acc1);
             TT_LAUNCH_CHECK();
         }
     }
@@ -1053,9 +1074,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     return TT_OK;
 }
 
-static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
-                         const float* gout, float* dg1, float* dg2, float* dg3, hipStream_t s,
-                         tt_status* st) {
+// The plan's shape and the cores' alignment admit the matrix-core backward.
+bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // k_bwd_dg2 stores each table's slices once: tables sharing G2 take the
@@ -1063,24 +1083,27 @@ static bool try_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
     if (p->g2_overlap) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
-    const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
-    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
-    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, s); return true; }
-    return false;
+    return p->n1 == 4 && p->n3 == 4 && p->R == 32 && (p->n2 == 8 || p->n2 == 4);
+}
+
+static tt_status launch_bwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
+                            const float* gout, float* dg1, float* dg2, float* dg3, bool kept, hipStream_t s) {
+    if (p->n2 == 8) return launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, s);
+    return launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, s);
 }
 
 }  // namespace tt
 
 using namespace tt;
 
-extern "C" tt_status tt_emb_backward(tt_emb_plan_t p, const float* g1, const float* g2,
-                                     const float* g3, const float* grad_out, float* dg1,
-                                     float* dg2, float* dg3, void* stream) {
-    if (!p || !g1 || !g2 || !g3 || !dg1 || !dg2 || !dg3 || (!grad_out && p->TB > 0))
-        return TT_ERR_INVALID_ARG;
+static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3,
+                               const float* grad_out, float* dg1, float* dg2, float* dg3, bool kept,
+                               void* stream) {
     hipStream_t s = (hipStream_t)stream;
+    // the backward overwrites the kept products (P, then dP over it)
+    p->kept_token = 0;
+    if (bwd_mfma_ok(p, g1, g2)) return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, s);
     tt_status st = TT_OK;
-    if (try_bwd_mfma(p, g1, g2, g3, grad_out, dg1, dg2, dg3, s, &st)) return st;
     if ((st = fill32(dg1, 0u, p->extent[0], s)) != TT_OK) return st;
     if ((st = fill32(dg2, 0u, p->extent[1], s)) != TT_OK) return st;
     if ((st = fill32(dg3, 0u, p->extent[2], s)) != TT_OK) return st;
@@ -1098,12 +1121,34 @@ extern "C" tt_status tt_emb_backward(tt_emb_plan_t p, const float* g1, const flo
     return TT_OK;
 }
 
+static bool backward_args_ok(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3,
+                             const float* grad_out, const float* dg1, const float* dg2, const float* dg3) {
+    return p && g1 && g2 && g3 && dg1 && dg2 && dg3 && (grad_out || p->TB == 0);
+}
+
+extern "C" tt_status tt_emb_backward(tt_emb_plan_t p, const float* g1, const float* g2,
+                                     const float* g3, const float* grad_out, float* dg1,
+                                     float* dg2, float* dg3, void* stream) {
+    if (!backward_args_ok(p, g1, g2, g3, grad_out, dg1, dg2, dg3)) return TT_ERR_INVALID_ARG;
+    return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, false, stream);
+}
+
+extern "C" tt_status tt_emb_backward_kept(tt_emb_plan_t p, uint64_t kept_token, const float* g1,
+                                          const float* g2, const float* g3, const float* grad_out,
+                                          float* dg1, float* dg2, float* dg3, void* stream) {
+    if (!backward_args_ok(p, g1, g2, g3, grad_out, dg1, dg2, dg3)) return TT_ERR_INVALID_ARG;
+    if (kept_token == 0 || kept_token != p->kept_token || g1 != p->kept_g1 || g2 != p->kept_g2 ||
+        !bwd_mfma_ok(p, g1, g2))
+        return TT_ERR_STALE;
+    return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, true, stream);
+}
+
 extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3,
                                 const float* dg1, const float* dg2, const float* dg3, float lr,
                                 void* stream) {
     if (!p || !g1 || !g2 || !g3 || !dg1 || !dg2 || !dg3) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    p->p_kept = false;   // the cores change: a kept P no longer matches them
+    p->kept_token = 0;   // the cores change: kept products no longer match them
     const SgdArgs a{{g1, g2, g3}, {dg1, dg2, dg3}, {p->extent[0], p->extent[1], p->extent[2]}};
     const int64_t nmax = std::max(p->extent[0], std::max(p->extent[1], p->extent[2]));
     if (nmax <= 0) return TT_OK;

@@ -314,18 +314,22 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     return TT_OK;
 }
 
-// Returns true (and launches) when the plan's shape has a matrix-core kernel.
-static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
-                         float* out, bool keep, hipStream_t s, tt_status* st) {
+// The plan's shape and the cores' alignment admit the matrix-core kernels.
+bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
-    if (n1 == 4 && n2 == 8 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, keep, s); return true; }
-    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 32) { *st = launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, keep, s); return true; }
-    if (n1 == 4 && n2 == 4 && n3 == 4 && R == 16) { *st = launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, false, s); return true; }
-    return false;
+    return n1 == 4 && n3 == 4 && ((n2 == 8 && R == 32) || (n2 == 4 && R == 32) || (n2 == 4 && R == 16));
+}
+
+static tt_status launch_fwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
+                            float* out, bool keep, hipStream_t s) {
+    const int n2 = p->n2, R = p->R;
+    if (n2 == 8 && R == 32) return launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, keep, s);
+    if (n2 == 4 && R == 32) return launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, keep, s);
+    return launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, false, s);
 }
 
 }  // namespace tt
@@ -333,20 +337,24 @@ static bool try_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g
 using namespace tt;
 
 static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3, float* out,
-                              bool keep, void* stream) {
+                              bool keep, uint64_t* token, void* stream) {
+    if (token) *token = 0;
     if (!p || !g1 || !g2 || !g3 || (!out && p->TB > 0)) return TT_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    tt_status st = TT_OK;
-    if (try_fwd_mfma(p, g1, g2, g3, out, keep, s, &st)) {
-        // the backward's shapes (R = 32) are the ones whose prefix lanes are kept
-        if (keep && st == TT_OK && p->R == 32 && p->L > 0) {
-            p->p_kept = true;
+    if (fwd_mfma_ok(p, g1, g2)) {
+        // P is kept only where the backward's matrix-core path will read it
+        const bool k = keep && bwd_mfma_ok(p, g1, g2) && p->L > 0;
+        if (k) p->kept_token = 0;   // pbuf is being rewritten
+        const tt_status st = launch_fwd(p, g1, g2, g3, out, k, s);
+        if (k && st == TT_OK) {
+            p->kept_token = ++p->next_token;
             p->kept_g1 = g1;
             p->kept_g2 = g2;
+            if (token) *token = p->kept_token;
         }
         return st;
     }
-    st = fill32(out, 0u, p->TB * p->D, s);
+    tt_status st = fill32(out, 0u, p->TB * p->D, s);
     if (st != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;
@@ -363,10 +371,11 @@ static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2,
 
 extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const float* g2,
                                     const float* g3, float* out, void* stream) {
-    return forward_impl(p, g1, g2, g3, out, false, stream);
+    return forward_impl(p, g1, g2, g3, out, false, nullptr, stream);
 }
 
 extern "C" tt_status tt_emb_forward_train(tt_emb_plan_t p, const float* g1, const float* g2,
-                                          const float* g3, float* out, void* stream) {
-    return forward_impl(p, g1, g2, g3, out, true, stream);
+                                          const float* g3, float* out, uint64_t* kept_token,
+                                          void* stream) {
+    return forward_impl(p, g1, g2, g3, out, true, kept_token, stream);
 }

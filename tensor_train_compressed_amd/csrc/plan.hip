@@ -66,8 +66,10 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_of = take(l4);
     y.run_start = take(l4);
     // pieces of the groups with more than kRunRange row runs: a group of n > W
-    // runs has ceil(n / W) < 2n / W of them, so fewer than 2L / W in all
-    const size_t xcap = 2 * (size_t)(L / kRunRange) + 1;
+    // runs has ceil(n / W) < 2n / W of them, so fewer than 2L / W in all; at
+    // most kMaxXPieces are listed (the groups past that run whole)
+    y.xcap = std::min<int64_t>(2 * (L / kRunRange) + 1, kMaxXPieces);
+    const size_t xcap = (size_t)y.xcap;
     y.xpiece = take(sizeof(int32_t) * 2 * xcap);
     y.dpart = take(sizeof(double) * xcap * (size_t)PR);
     // one row per row run, plus kStageSpare rows that take the writes of
@@ -95,14 +97,15 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
-    // dL/dP per group, only for shapes the matrix-core backward serves
-    y.dpg = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.gdone = take(sizeof(int32_t) * (size_t)y.Gmax);
+    // P per group (kept from the training forward, or formed by the
+    // backward), then dL/dP per group written over it by the run kernel
     y.pbuf = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
     y.acc1 = take(sizeof(double) * (size_t)E1);
     y.acc3 = take(sizeof(double) * (size_t)E3);
-    // per run, P^T S (the run's dG3 term), for the single-table reduction of dG3
-    y.c3 = take(NB3 > 0 ? sizeof(float) * (size_t)L * (size_t)CN : 0);
+    // each run's dG3 term P^T S (R*n3 floats) goes over the run's S row when
+    // that row is long enough, else into a buffer of its own
+    y.c3 = take(NB3 > 0 && CN > D ? sizeof(float) * (size_t)L * (size_t)CN : 0);
     // fp64 pieces of the row runs cut by the backward's 64-position windows:
     // two slots per window (its start piece and its end piece)
     y.xsum = take(sizeof(double) * 2 * (size_t)((L + 63) / 64) * (size_t)D);
@@ -112,7 +115,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.i3start = take(sizeof(int32_t) * (size_t)(NB3 + 1));
     y.run_rank = take(sizeof(int32_t) * (size_t)L);
     y.run_bkt = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
-    y.run_slot = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
+    y.bucket_runs = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.NFB = NFB;
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
@@ -1007,7 +1010,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
     for (int k = 0; k < 3; ++k) p->extent[k] = 0;
     p->packed = true;
-    p->p_kept = false;
+    p->kept_token = 0;
+    p->next_token = 0;
     p->kept_g1 = nullptr;
     p->kept_g2 = nullptr;
     p->off4 = true;
@@ -1211,6 +1215,18 @@ extern "C" tt_status tt_emb_plan_counts(tt_emb_plan_t p, int64_t* num_groups, in
     return TT_OK;
 }
 
+extern "C" tt_status tt_emb_query_paths(tt_emb_plan_t p, const float* g1, const float* g2,
+                                        tt_emb_path_info* info) {
+    if (!p || !info) return TT_ERR_INVALID_ARG;
+    const bool f = fwd_mfma_ok(p, g1, g2), b = bwd_mfma_ok(p, g1, g2);
+    info->forward_path = f ? TT_PATH_MATRIX_CORE : TT_PATH_GENERIC;
+    info->backward_path = b ? TT_PATH_MATRIX_CORE : TT_PATH_GENERIC;
+    info->keeps_prefix = (f && b) ? 1 : 0;
+    info->dg3_by_rows = (b && p->nb3 > 0) ? 1 : 0;
+    info->workspace_bytes = (uint64_t)p->lay.total;
+    return TT_OK;
+}
+
 extern "C" tt_status tt_emb_plan_destroy(tt_emb_plan_t p) {
     delete p;
     return TT_OK;
@@ -1224,6 +1240,7 @@ extern "C" const char* tt_emb_status_string(tt_status s) {
         case TT_ERR_WORKSPACE: return "workspace too small";
         case TT_ERR_HIP: return "HIP runtime error";
         case TT_ERR_DEVICE_FLAG: return "device error flag set (bad index or offsets)";
+        case TT_ERR_STALE: return "kept prefix products are stale (token does not match the plan)";
     }
     return "unknown status";
 }

@@ -48,9 +48,14 @@ constexpr int kFwdPersistBlocks = 3 * 256;
 // The backward's run kernel hands out row runs in ranges of about this many
 // (a group of more runs is split; smaller groups are never split).
 constexpr int kRunRange = 32;
-// With one table of at most this many G3 slices, dG3 is reduced per slice
-// from per-run terms (one workgroup per slice scans the run list) instead of
-// with device atomics.
+// At most this many pieces of split groups are listed (each has an fp64 dP
+// slot in the workspace); the groups that would exceed it run whole, one
+// wave each.
+constexpr int64_t kMaxXPieces = 8192;
+// With at most this many G3 rows in all (any number of tables, each table's
+// G3 offset a whole number of R*n3 rows), dG3 is reduced per G3 row from
+// per-run terms (one workgroup per row sums its bucket) instead of with
+// device atomics.
 constexpr int kMaxBuckets3 = 8192;   // G3 rows whose runs the planner counts (see Layout::i3cnt)
 constexpr int kI3Pad = 32;   // int32 words per i3 counter (one 128-byte line each)
 // LDS the batch kernels may spend on the run i3 list of one batch
@@ -117,11 +122,12 @@ struct Layout {
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
     size_t run_start;                        // [L] int32: first sorted position of each row run
-    size_t xpiece;                           // [2*(L/kRunRange) + 1] int32 pairs: (group, piece) (backward)
-    size_t dpart;                            // [2*(L/kRunRange) + 1][n1*n2*R] double: dP of each listed piece
+    size_t xpiece;                           // [xcap] int32 pairs: (group, piece) (backward)
+    size_t dpart;                            // [xcap][n1*n2*R] double: dP of each listed piece
     size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
     size_t stage;                            // [L + kStageSpare][D] float, one row per row run: forward, the
-                                             //     run's embedding row; backward, its grad-row sum
+                                             //     run's embedding row; backward, its grad-row sum S,
+                                             //     then (bucketed dG3) its dG3 term P^T S over S
     size_t perm, sorted_i3, sorted_bag;      // [L]
     size_t skey, sort_k0, sort_v0, sort_b0, sort_k1, sort_v1, sort_b1;  // [L] radix ping-pong
     size_t hist;                             // [kRadixBins][hstride] uint32: digit counts per tile
@@ -131,11 +137,13 @@ struct Layout {
     size_t key_tiles;                        // [n_ktiles] uint64: key words per tile of keys
     size_t group_key, group_start, group_cbase;   // [Gmax], [Gmax+1], [Gmax+1]
     size_t chunk_group, chunk_begin, chunk_end;   // [Cmax]
-    size_t dpg;                              // [Gmax][n1*n2*R] float: dL/dP per group (backward)
-    size_t gdone;                            // [Gmax] int32: pieces of a split group finished (backward)
-    size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group (backward),
-                                             //     in the lane order of the matrix-core operands
-    size_t c3;                               // [L][R*n3] float (NB3 > 0): P^T S per run, by bucket
+    size_t gdone;                            // [Gmax] int32: pieces of a split group finished (backward);
+                                             //     -1: a group too large for the piece list, run whole
+    size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group, in the lane order of the
+                                             //     matrix-core operands; the backward's run kernel then
+                                             //     writes each group's dL/dP over it (row-major)
+    size_t c3;                               // [L][R*n3] float, only when R*n3 > D (and dG3 is bucketed):
+                                             //     each run's dG3 term P^T S (else written over its S row)
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
     size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
@@ -148,10 +156,10 @@ struct Layout {
     size_t i3start;                          // [NB3 + 1] int32: exclusive scan of the counts
     size_t run_rank;                         // [L] int32: rank of each run inside its bucket
     size_t run_bkt;                          // [L] int32: bucket (G3 row) of each run
-    size_t run_slot;                         // [L] int32: backward: each run's c3 row (start + rank)
+    size_t bucket_runs;                      // [L] int32: backward: the runs of each bucket, in rank order
     size_t batch;                            // [NFB] BatchRec
     size_t total;
-    int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles, NB3;
+    int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles, NB3, xcap;
     int passes;
 };
 
@@ -178,7 +186,9 @@ struct tt_emb_plan_s {
     bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
     bool off4;                // every table's G1 and G2 offsets are multiples of 4 floats
     bool g2_overlap;          // two tables' G2 ranges overlap (a shared core)
-    bool p_kept;              // pbuf holds P of every group for kept_g1/kept_g2 (forward_train)
+    uint64_t kept_token;      // nonzero: pbuf holds P of every group for kept_g1/kept_g2, kept by
+                              //     the tt_emb_forward_train call that returned this token
+    uint64_t next_token;      // last token handed out on this plan
     const float* kept_g1;
     const float* kept_g2;
     char* ws;                 // workspace base (device)
@@ -214,6 +224,11 @@ __device__ __forceinline__ void wait_vmem_done() {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// Whether the plan's calls take the matrix-core kernels with these cores
+// (forward.hip, backward.hip).
+bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
+bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
 
 inline unsigned grid_for(int64_t n, int threads) {
     int64_t g = (n + threads - 1) / threads;

@@ -68,5 +68,19 @@ def test_plan_rejects_bad_args_before_launch():
     assert lib.tt_emb_forward(None, P(1), P(1), P(1), P(1), None) == -1
     assert lib.tt_emb_backward(None, P(1), P(1), P(1), P(1), P(1), P(1), P(1), None) == -1
     assert lib.tt_emb_sgd(None, P(1), P(1), P(1), P(1), P(1), P(1), ctypes.c_float(0.1), None) == -1
+    tok = ctypes.c_uint64(7)
+    assert lib.tt_emb_forward_train(None, P(1), P(1), P(1), P(1), ctypes.byref(tok), None) == -1
+    assert tok.value == 0                      # no products kept
+    assert lib.tt_emb_backward_kept(None, 1, P(1), P(1), P(1), P(1), P(1), P(1), P(1), None) == -1
+    assert lib.tt_emb_query_paths(None, P(16), P(16), None) == -1
     assert lib.tt_emb_plan_destroy(None) == 0
     assert b"workspace" in lib.tt_emb_status_string(-3)
+    assert b"stale" in lib.tt_emb_status_string(-6)
+
+
+def test_workspace_size_skew11m():
+    """The 11M-row table's batch (656,601 lookups, 32,768 bags) plans in
+    under 700 MB of workspace."""
+    _lib()
+    good = _tabs((11_000_000, (200, 220, 250), (4, 8, 4), 32))
+    assert tte.tt_emb_workspace_bytes(good, 656_601, 32768, 256) < 700e6

@@ -2,9 +2,10 @@
 
 Planner tables must match bit for bit. Floats must satisfy
 |gpu - ref| <= 1e-4 * (1 + |ref|) elementwise, ref being the fp64 oracle.
-Small cases compare every output; the full-size workloads compare sampled
-bags (forward) and sampled core slices (backward), which the oracle computes
-one by one, in the launch configuration the benchmark times.
+Every case compares every output element, the full-size workloads included
+(the forward of all 32,768 and 851,968 bags; the training step exactly as the
+benchmark times it, with every gradient and every updated core element),
+except the 26-table backward, which compares sampled slices.
 """
 import json
 
@@ -181,24 +182,13 @@ def test_forward_ragged_shapes():
         run_forward_check(p, f"ragged chunk={chunk}", chunk=chunk)
 
 
-def _sample_bags(p, n=192, seed=0):
-    rng = np.random.default_rng(seed)
-    lens = np.diff(p.offsets)
-    big = np.argsort(lens)[-8:]
-    picks = np.concatenate([[0, p.T * p.batch - 1], big, rng.integers(0, p.T * p.batch, n)])
-    return np.unique(picks)
-
-
-@pytest.mark.parametrize("name", ["skew11m", "multi26"])
-def test_forward_full_size_sampled(name):
-    p = wl.make(name)
-    run_forward_check(p, f"{name} full", chunk=256, bags=_sample_bags(p))
-
-
-def test_forward_permuted_full_size_sampled():
-    # the skewed table with its rows permuted: far more, smaller prefix groups
-    p = wl.make("skew11m", permuted=True)
-    run_forward_check(p, "skew11m permuted full", chunk=256, bags=_sample_bags(p))
+@pytest.mark.parametrize("name,kw", [("skew11m", {}), ("skew11m", {"permuted": True}), ("multi26", {})])
+def test_forward_full_size_all_bags(name, kw):
+    """The full batches: 32,768 bags of the 11M-row table (unpermuted Zipf,
+    and with its rows permuted: far more, smaller prefix groups) and the
+    26-table batch (851,968 bags in one launch); every bag."""
+    p = wl.make(name, **kw)
+    run_forward_check(p, f"{name}{kw} full", chunk=256)
 
 
 def test_repeat_runs():
@@ -272,31 +262,151 @@ def test_backward_unaligned_dg2():
         assert_close(x.cpu().numpy(), ref[k], f"unaligned dG2: dG{k + 1}")
 
 
-def test_forward_train_keeps_prefix():
-    """tt_emb_forward_train gives the forward's output bit for bit and keeps
-    P for the next backward, which must match the oracle; tt_emb_sgd then
-    discards the kept P, so a backward on the updated cores (same pointers)
-    matches the oracle on those cores."""
+def _oracle_backward_sgd(p):
+    ref = oracle.backward_problem(p)
+    return ref, [oracle.sgd(c, r, p.lr) for c, r in zip((p.g1, p.g2, p.g3), ref)]
+
+
+def test_forward_train_token():
+    """tt_emb_forward_train gives the forward's output bit for bit and a
+    token; tt_emb_backward_kept with it matches the oracle. The token names
+    one use of the kept products: a second backward_kept, one after an SGD
+    step, after a plain backward (which overwrites them), after a newer
+    forward_train, or with other core pointers gets TT_ERR_STALE and
+    launches nothing."""
     import tensor_train_compressed_amd as tte
     p = wl.make("train11m", batch=1024)
     dp = DevProblem(p, 256)
     want_out = dp.forward().cpu().numpy()
-    out = torch.empty_like(torch.from_numpy(want_out)).to("cuda:0")
-    tte.tt_emb_forward_train(dp.plan, dp.g1, dp.g2, dp.g3, out)
+    out = torch.empty(want_out.shape, dtype=torch.float32, device="cuda:0")
+    d = [torch.empty_like(x) for x in (dp.g1, dp.g2, dp.g3)]
+    g = (dp.g1, dp.g2, dp.g3)
+
+    def stale(fn):
+        with pytest.raises(tte.TTEmbError) as ei:
+            fn()
+        assert ei.value.status == tte.TT_ERR_STALE
+
+    tok = tte.tt_emb_forward_train(dp.plan, *g, out)
+    assert tok != 0
     np.testing.assert_array_equal(out.cpu().numpy(), want_out, err_msg="forward_train output")
-    d = [x.cpu().numpy() for x in dp.backward()]
-    ref = oracle.backward_problem(p)
+    tte.tt_emb_backward_kept(dp.plan, tok, *g, dp.gout, *d)
+    ref, ref_sgd = _oracle_backward_sgd(p)
     for k in range(3):
-        assert_close(d[k], ref[k], f"backward after forward_train dG{k + 1}")
-    # an SGD step on the plan's cores, in place, then the backward again
-    dg = dp.backward()
-    tte.tt_emb_sgd(dp.plan, dp.g1, dp.g2, dp.g3, dg[0], dg[1], dg[2], p.lr)
-    p2 = wl.Problem(p.name, p.tables, p.batch, dp.g1.cpu().numpy(), dp.g2.cpu().numpy(),
-                    dp.g3.cpu().numpy(), p.goff, p.indices, p.offsets, p.grad_out, p.lr)
-    d2 = [x.cpu().numpy() for x in dp.backward()]
+        assert_close(d[k].cpu().numpy(), ref[k], f"backward_kept dG{k + 1}")
+    stale(lambda: tte.tt_emb_backward_kept(dp.plan, tok, *g, dp.gout, *d))       # consumed
+    # a newer forward_train invalidates the older token
+    t1 = tte.tt_emb_forward_train(dp.plan, *g, out)
+    t2 = tte.tt_emb_forward_train(dp.plan, *g, out)
+    assert t1 != t2
+    stale(lambda: tte.tt_emb_backward_kept(dp.plan, t1, *g, dp.gout, *d))
+    # other core pointers (same values)
+    g1c = dp.g1.clone()
+    stale(lambda: tte.tt_emb_backward_kept(dp.plan, t2, g1c, dp.g2, dp.g3, dp.gout, *d))
+    # forward_train(A), backward on other cores B (plain: forms B's products
+    # over the kept ones), then backward_kept(A's token): stale; a plain
+    # backward on A is still right
+    t3 = tte.tt_emb_forward_train(dp.plan, *g, out)
+    gb = [x * 1.5 for x in g]
+    db = [torch.empty_like(x) for x in g]
+    tte.tt_emb_backward(dp.plan, *gb, dp.gout, *db)
+    stale(lambda: tte.tt_emb_backward_kept(dp.plan, t3, *g, dp.gout, *d))
+    tte.tt_emb_backward(dp.plan, *g, dp.gout, *d)
+    for k in range(3):
+        assert_close(d[k].cpu().numpy(), ref[k], f"plain backward after another core set dG{k + 1}")
+    # an SGD step on the plan ends the token; then a second core set (the
+    # oracle's cores after a step of lr 1e-4: fresh inputs for both sides; at
+    # lr 0.01 the 1,024 bags' gradients, up to about 10^3, would blow the
+    # cores up until fp32 rows lose the tolerance to cancellation) matches
+    # the oracle again
+    t4 = tte.tt_emb_forward_train(dp.plan, *g, out)
+    tte.tt_emb_sgd(dp.plan, *[x.clone() for x in g], *d, p.lr)
+    stale(lambda: tte.tt_emb_backward_kept(dp.plan, t4, *g, dp.gout, *d))
+    new = [oracle.sgd(c, r, 1e-4).astype(np.float32) for c, r in zip((p.g1, p.g2, p.g3), ref)]
+    p2 = wl.Problem(p.name, p.tables, p.batch, *new, p.goff, p.indices, p.offsets, p.grad_out, p.lr)
+    for x, y in zip(g, (p2.g1, p2.g2, p2.g3)):
+        x.copy_(torch.from_numpy(y))
+    t5 = tte.tt_emb_forward_train(dp.plan, *g, out)
+    assert_close(out.cpu().numpy(), oracle.forward_problem(p2), "forward_train on updated cores")
+    tte.tt_emb_backward_kept(dp.plan, t5, *g, dp.gout, *d)
     ref2 = oracle.backward_problem(p2)
     for k in range(3):
-        assert_close(d2[k], ref2[k], f"backward after SGD dG{k + 1}")
+        assert_close(d[k].cpu().numpy(), ref2[k], f"backward_kept on updated cores dG{k + 1}")
+
+
+def test_training_step_full_size():
+    """The step the benchmark times, at full size (the 11M-row table, 32,768
+    bags, 656,601 lookups, chunk 256, one workspace for both steps): plan,
+    tt_emb_forward_train, tt_emb_backward_kept, tt_emb_sgd. Every output row,
+    every gradient element and every updated core element against the
+    oracle; the step runs twice on the same workspace, each time from the
+    workload's cores."""
+    import tensor_train_compressed_amd as tte
+    p = wl.make("train11m")
+    dp = DevProblem(p, 256)
+    ws = torch.empty(tte.tt_emb_workspace_bytes(dp.tables_c, p.L, p.batch, 256), dtype=torch.uint8,
+                     device="cuda:0")
+    say("full training step: oracle forward + backward (about a minute)")
+    ref_out = oracle.forward_problem(p)
+    ref, ref_sgd = _oracle_backward_sgd(p)
+    for step in range(2):
+        g = [torch.from_numpy(x).to("cuda:0") for x in (p.g1, p.g2, p.g3)]
+        d = [torch.empty_like(x) for x in g]
+        out = torch.empty((p.batch, p.dim), dtype=torch.float32, device="cuda:0")
+        pl = tte.tt_emb_plan(dp.tables_c, dp.idx, dp.off, p.batch, 256, workspace=ws)
+        tok = tte.tt_emb_forward_train(pl, *g, out)
+        assert tok != 0
+        tte.tt_emb_backward_kept(pl, tok, *g, dp.gout, *d)
+        tte.tt_emb_sgd(pl, *g, *d, p.lr)
+        assert tte.tt_emb_get_error(pl) == 0
+        say(f"step {step}: compare")
+        assert_close(out.cpu().numpy(), ref_out, f"step {step} forward")
+        for k in range(3):
+            assert_close(d[k].cpu().numpy(), ref[k], f"step {step} dG{k + 1}")
+            assert_close(g[k].cpu().numpy(), ref_sgd[k], f"step {step} SGD core {k + 1}")
+
+
+def test_query_paths():
+    import tensor_train_compressed_amd as tte
+    dp = DevProblem(wl.make("train11m", batch=64), 256)
+    dp.make_plan()
+    q = tte.tt_emb_query_paths(dp.plan, dp.g1, dp.g2)
+    assert q["forward_path"] == tte.TT_PATH_MATRIX_CORE and q["backward_path"] == tte.TT_PATH_MATRIX_CORE
+    assert q["keeps_prefix"] == 1 and q["dg3_by_rows"] == 1
+    assert q["workspace_bytes"] == dp.plan.workspace.numel()
+    # G1 at an address that is not 16-byte aligned: the generic kernels,
+    # still matching the oracle
+    buf = torch.empty(dp.g1.numel() + 1, dtype=torch.float32, device="cuda:0")
+    g1u = buf[1:]
+    g1u.copy_(dp.g1)
+    q = tte.tt_emb_query_paths(dp.plan, g1u, dp.g2)
+    assert q["forward_path"] == tte.TT_PATH_GENERIC and q["backward_path"] == tte.TT_PATH_GENERIC
+    assert q["keeps_prefix"] == 0
+    out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
+    assert tte.tt_emb_forward_train(dp.plan, g1u, dp.g2, dp.g3, out) == 0   # nothing kept
+    assert_close(out.cpu().numpy(), oracle.forward_problem(dp.p), "generic forward (unaligned G1)")
+    # a shape without matrix-core kernels
+    tabs = [wl.Table(5000, (17, 18, 17), (4, 2, 1), 5)]
+    dq = DevProblem(wl.make_custom(tabs, np.full(10, 3), seed=3), 16)
+    dq.make_plan()
+    q = tte.tt_emb_query_paths(dq.plan, dq.g1, dq.g2)
+    assert q["forward_path"] == tte.TT_PATH_GENERIC and q["backward_path"] == tte.TT_PATH_GENERIC
+
+
+def test_binding_checks_sizes():
+    import tensor_train_compressed_amd as tte
+    dp = DevProblem(wl.make("train11m", batch=64), 256)
+    dp.make_plan()
+    out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError):
+        tte.tt_emb_forward(dp.plan, dp.g1, dp.g2, dp.g3, out[:-1])
+    with pytest.raises(ValueError):
+        tte.tt_emb_forward(dp.plan, dp.g1[:-4], dp.g2, dp.g3, out)
+    with pytest.raises(ValueError):
+        tte.tt_emb_plan(dp.tables_c, dp.idx, dp.off[:-1], dp.p.batch, 256)
+    d = [torch.empty_like(x) for x in (dp.g1, dp.g2, dp.g3)]
+    with pytest.raises(ValueError):
+        tte.tt_emb_backward(dp.plan, dp.g1, dp.g2, dp.g3, dp.gout, d[0], d[1][:-1], d[2])
 
 
 def test_backward_multitable_small():
@@ -396,34 +506,19 @@ def test_backward_multitable_full_size_sampled():
                     slices=(np.concatenate(s1), np.concatenate(s2), np.concatenate(s3)))
 
 
-def _slice_mask(p, pl, which, picks):
-    """Mask of lookups whose core-`which` digit is in picks (single table)."""
-    t = p.tables[0]
-    key = pl["key"].astype(np.int64)
-    i1 = key % t.m[0]
-    i2 = key // t.m[0]
-    i3 = pl["i3"].astype(np.int64)
-    dig = {1: i1, 2: i2, 3: i3}[which]
-    return np.isin(dig, picks)
-
-
-def test_backward_full_size_sampled():
-    """train11m at full size: compare gradients of sampled slices; the oracle
-    sums only the lookups that touch them (which is exact for those slices)."""
-    p = wl.make("train11m")
-    t = p.tables[0]
-    R, (n1, n2, n3) = t.rank, t.n
-    pl = oracle.plan_problem(p, 256)
-    # the Zipf head is unpermuted: i2 = 1 and i3 = 1 pick up hot rows (row 1
-    # sits in the largest prefix group), while keeping the masked oracle short
-    i1s = np.array([3, 57, 199]); i2s = np.array([1, 100, 219]); i3s = np.array([1, 131, 249])
-    mask = (_slice_mask(p, pl, 1, i1s) | _slice_mask(p, pl, 2, i2s) |
-            _slice_mask(p, pl, 3, i3s)).astype(np.uint8)
-    say("sampled backward lookups", int(mask.sum()))
-    s1 = np.concatenate([np.arange(i * n1 * R, (i + 1) * n1 * R) for i in i1s])
-    s2 = np.concatenate([np.arange(i * R * n2 * R, (i + 1) * R * n2 * R) for i in i2s])
-    s3 = np.concatenate([np.arange(i * R * n3, (i + 1) * R * n3) for i in i3s])
-    _check_backward(p, "train11m full", chunk=256, mask=mask, slices=(s1, s2, s3))
+def test_backward_piece_list_overflow():
+    """More pieces of large groups than the piece list holds (8,192): 300
+    groups of 1,024 distinct rows each (32 pieces per group, 9,600 in all),
+    so the groups that do not fit run whole on one wave each; every
+    gradient element against the oracle. Shape (4, 4, 4), R 32: each run's
+    dG3 term (128 floats) is longer than its S row (64), so it goes to a
+    buffer of its own."""
+    t = wl.Table(20 * 15 * 1024, (20, 15, 1024), (4, 4, 4), 32)
+    L = 20 * 15 * 1024
+    p = wl.make_custom([t], np.full(L // 100, 100), seed=11, with_grad=True)
+    assert p.L == L
+    p.indices = np.random.default_rng(12).permutation(L).astype(np.int64)
+    _check_backward(p, "piece list overflow (9,600 pieces)", chunk=256)
 
 
 def test_backward_hot_slices_full_size():
