@@ -63,8 +63,10 @@ typedef enum {
     TT_ERR_WORKSPACE = -3,    /* workspace smaller than tt_emb_workspace_bytes      */
     TT_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed          */
     TT_ERR_DEVICE_FLAG = -5,  /* returned by tt_emb_get_error when the flag is set   */
-    TT_ERR_STALE = -6         /* tt_emb_backward_kept: the token does not name the   */
+    TT_ERR_STALE = -6,        /* tt_emb_backward_kept: the token does not name the   */
                               /* products the plan holds (see below)                 */
+    TT_ERR_SCRATCH = -7       /* tt_emb_forward_scratch: the batch needs more than   */
+                              /* the library's static scratch buffer holds           */
 } tt_status;
 
 /* Device error flag bits (tt_emb_get_error). */
@@ -197,6 +199,32 @@ tt_status tt_emb_plan_counts(tt_emb_plan_t plan, int64_t* num_groups, int64_t* n
 
 /* Frees the host handle (the workspace stays the caller's). NULL is a no-op. */
 tt_status tt_emb_plan_destroy(tt_emb_plan_t plan);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation): plans the batch and runs the forward in one call, with the
+ * same kernels and the same result as tt_emb_plan + tt_emb_forward, using a
+ * static device buffer of the library's own instead of a caller workspace.
+ * Arguments as for tt_emb_plan (tables, T, indices, offsets, L, B, chunk) and
+ * tt_emb_forward (cores, out, stream); tables is read during the call only.
+ * The buffer holds tt_emb_scratch_capacity() bytes (64 MiB) per device,
+ * taken when the library is loaded and held until the process ends; a
+ * forward-only plan of the 11M-row table (dim 128) fits about 100,000
+ * lookups. A batch that needs more returns TT_ERR_SCRATCH before any device
+ * work. Calls no allocator (device or host). All calls on one device share
+ * its buffer: calls that overlap in time on one device (different streams,
+ * different host threads) race and give undefined results; calls on one
+ * stream are ordered and safe. Device-found data errors (bad index or
+ * offsets) leave the output unspecified and are not reported (there is no
+ * plan to query): validate inputs with tt_emb_plan first where that
+ * matters. */
+tt_status tt_emb_forward_scratch(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                                 const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                                 const float* g1, const float* g2, const float* g3, float* out,
+                                 void* stream);
+
+/* Bytes of the static device buffer tt_emb_forward_scratch uses. */
+size_t tt_emb_scratch_capacity(void);
 
 /* Which kernels a call on this plan runs (pure host query, no launch).
  * The matrix-core path serves plans whose tables all share one shape among

@@ -21,13 +21,15 @@ __all__ = [
     "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
     "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
-    "tt_emb_query_paths", "TT_PATH_MATRIX_CORE", "TT_PATH_GENERIC", "TT_ERR_STALE", "Plan", "EXPORTS",
+    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "TT_PATH_MATRIX_CORE",
+    "TT_PATH_GENERIC", "TT_ERR_STALE", "TT_ERR_SCRATCH", "Plan", "EXPORTS",
 ]
 
 TT_OK = 0
 TT_ERR_INVALID_ARG = -1
 TT_ERR_DEVICE_FLAG = -5
 TT_ERR_STALE = -6
+TT_ERR_SCRATCH = -7
 TT_PATH_MATRIX_CORE = 1
 TT_PATH_GENERIC = 2
 TT_FLAG_BAD_INDEX = 1
@@ -38,7 +40,7 @@ EXPORTS = (
     "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train",
     "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
-    "tt_emb_query_paths", "tt_emb_status_string",
+    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +102,10 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_backward.argtypes = [P, P, P, P, P, P, P, P, P]
         lib.tt_emb_backward_kept.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, P, P]
         lib.tt_emb_query_paths.argtypes = [P, P, P, ctypes.POINTER(_PathInfo)]
+        lib.tt_emb_forward_scratch.argtypes = [P, i32, P, P, i64, i64, i32, P, P, P, P, P]
+        lib.tt_emb_forward_scratch.restype = ctypes.c_int
+        lib.tt_emb_scratch_capacity.argtypes = []
+        lib.tt_emb_scratch_capacity.restype = ctypes.c_size_t
         lib.tt_emb_sgd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P]
         lib.tt_emb_get_error.argtypes = [P, ctypes.POINTER(i32), P]
         lib.tt_emb_plan_get_view.argtypes = [P, ctypes.POINTER(_View)]
@@ -281,6 +287,26 @@ def tt_emb_query_paths(plan: Plan, g1, g2) -> dict:
                                              ctypes.c_void_p(g2.data_ptr()), ctypes.byref(info)),
            "tt_emb_query_paths")
     return {name: int(getattr(info, name)) for name, _ in _PathInfo._fields_}
+
+
+def tt_emb_scratch_capacity() -> int:
+    """Bytes of the library's static scratch buffer (per device)."""
+    return int(load_library().tt_emb_scratch_capacity())
+
+
+def tt_emb_forward_scratch(tables_c, indices, offsets, B: int, chunk: int, g1, g2, g3, out,
+                           stream=None):
+    """Plan + forward of one batch in the library's static scratch buffer:
+    no workspace and no allocation (raises TTEmbError with TT_ERR_SCRATCH
+    when the batch does not fit)."""
+    T = len(tables_c)
+    D = int(tables_c[0].n[0] * tables_c[0].n[1] * tables_c[0].n[2])
+    ext = core_extents(tables_c)
+    _check(load_library().tt_emb_forward_scratch(
+        tables_c, T, _dev_ptr(indices, "int64", "indices"), _dev_ptr(offsets, "int64", "offsets", T * B + 1),
+        int(indices.numel()), B, chunk, _dev_ptr(g1, "float32", "g1", ext[0], at_least=True),
+        _dev_ptr(g2, "float32", "g2", ext[1], at_least=True), _dev_ptr(g3, "float32", "g3", ext[2], at_least=True),
+        _dev_ptr(out, "float32", "out", T * B * D), _stream(stream)), "tt_emb_forward_scratch")
 
 
 def tt_emb_get_error(plan: Plan, stream=None) -> int:

@@ -1109,7 +1109,7 @@ static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2
     if ((st = fill32(dg3, 0u, p->extent[2], s)) != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;
-    for (const auto& x : p->tables) maxp = std::max(maxp, x.n[0] * x.n[1] * x.rank);
+    for (int32_t t = 0; t < p->T; ++t) maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
     const size_t lds = 2 * sizeof(float) * (size_t)maxp;
     hipLaunchKernelGGL(k_bwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
                        p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),

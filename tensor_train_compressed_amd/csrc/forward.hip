@@ -336,14 +336,13 @@ static tt_status launch_fwd(const tt_emb_plan_s* p, const float* g1, const float
 
 using namespace tt;
 
-static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3, float* out,
-                              bool keep, uint64_t* token, void* stream) {
+tt_status tt::forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3, float* out,
+                          bool keep, uint64_t* token, hipStream_t s) {
     if (token) *token = 0;
     if (!p || !g1 || !g2 || !g3 || (!out && p->TB > 0)) return TT_ERR_INVALID_ARG;
-    hipStream_t s = (hipStream_t)stream;
     if (fwd_mfma_ok(p, g1, g2)) {
         // P is kept only where the backward's matrix-core path will read it
-        const bool k = keep && bwd_mfma_ok(p, g1, g2) && p->L > 0;
+        const bool k = keep && !p->fwd_only && bwd_mfma_ok(p, g1, g2) && p->L > 0;
         if (k) p->kept_token = 0;   // pbuf is being rewritten
         const tt_status st = launch_fwd(p, g1, g2, g3, out, k, s);
         if (k && st == TT_OK) {
@@ -358,7 +357,7 @@ static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2,
     if (st != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;
-    for (const auto& x : p->tables) maxp = std::max(maxp, x.n[0] * x.n[1] * x.rank);
+    for (int32_t t = 0; t < p->T; ++t) maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
     const size_t lds = sizeof(float) * (size_t)maxp;
     hipLaunchKernelGGL(k_fwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
                        p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
@@ -371,11 +370,11 @@ static tt_status forward_impl(tt_emb_plan_t p, const float* g1, const float* g2,
 
 extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const float* g2,
                                     const float* g3, float* out, void* stream) {
-    return forward_impl(p, g1, g2, g3, out, false, nullptr, stream);
+    return forward_run(p, g1, g2, g3, out, false, nullptr, (hipStream_t)stream);
 }
 
 extern "C" tt_status tt_emb_forward_train(tt_emb_plan_t p, const float* g1, const float* g2,
                                           const float* g3, float* out, uint64_t* kept_token,
                                           void* stream) {
-    return forward_impl(p, g1, g2, g3, out, true, kept_token, stream);
+    return forward_run(p, g1, g2, g3, out, true, kept_token, (hipStream_t)stream);
 }

@@ -37,8 +37,11 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3) {
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3,
+                   bool fwd_only) {
     Layout y{};
+    // a forward-only plan carries none of the backward's buffers
+    const int64_t LB = fwd_only ? 0 : L;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + (bytes ? bytes : 1)); return o; };
     y.K = K;
@@ -68,7 +71,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     // pieces of the groups with more than kRunRange row runs: a group of n > W
     // runs has ceil(n / W) < 2n / W of them, so fewer than 2L / W in all; at
     // most kMaxXPieces are listed (the groups past that run whole)
-    y.xcap = std::min<int64_t>(2 * (L / kRunRange) + 1, kMaxXPieces);
+    y.xcap = fwd_only ? 0 : std::min<int64_t>(2 * (L / kRunRange) + 1, kMaxXPieces);
     const size_t xcap = (size_t)y.xcap;
     y.xpiece = take(sizeof(int32_t) * 2 * xcap);
     y.dpart = take(sizeof(double) * xcap * (size_t)PR);
@@ -97,23 +100,24 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.chunk_group = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_begin = take(sizeof(int32_t) * (size_t)y.Cmax);
     y.chunk_end = take(sizeof(int32_t) * (size_t)y.Cmax);
-    y.gdone = take(sizeof(int32_t) * (size_t)y.Gmax);
+    const int64_t GB = fwd_only ? 0 : y.Gmax;
+    y.gdone = take(sizeof(int32_t) * (size_t)GB);
     // P per group (kept from the training forward, or formed by the
     // backward), then dL/dP per group written over it by the run kernel
-    y.pbuf = take(sizeof(float) * (size_t)y.Gmax * (size_t)PR);
-    y.acc1 = take(sizeof(double) * (size_t)E1);
-    y.acc3 = take(sizeof(double) * (size_t)E3);
+    y.pbuf = take(sizeof(float) * (size_t)GB * (size_t)PR);
+    y.acc1 = take(fwd_only ? 0 : sizeof(double) * (size_t)E1);
+    y.acc3 = take(fwd_only ? 0 : sizeof(double) * (size_t)E3);
     // each run's dG3 term P^T S (R*n3 floats) goes over the run's S row when
     // that row is long enough, else into a buffer of its own
     y.c3 = take(NB3 > 0 && CN > D ? sizeof(float) * (size_t)L * (size_t)CN : 0);
     // fp64 pieces of the row runs cut by the backward's 64-position windows:
     // two slots per window (its start piece and its end piece)
-    y.xsum = take(sizeof(double) * 2 * (size_t)((L + 63) / 64) * (size_t)D);
-    y.xcnt = take(sizeof(int32_t) * (size_t)((L + 63) / 64));
+    y.xsum = take(sizeof(double) * 2 * (size_t)((LB + 63) / 64) * (size_t)D);
+    y.xcnt = take(sizeof(int32_t) * (size_t)((LB + 63) / 64));
     y.NB3 = NB3;
     y.i3cnt = take(sizeof(int32_t) * (size_t)NB3 * kI3Pad);
     y.i3start = take(sizeof(int32_t) * (size_t)(NB3 + 1));
-    y.run_rank = take(sizeof(int32_t) * (size_t)L);
+    y.run_rank = take(sizeof(int32_t) * (size_t)LB);
     y.run_bkt = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.bucket_runs = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.NFB = NFB;
@@ -965,21 +969,27 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
     return TT_OK;
 }
 
-extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
-                                         int64_t B, int32_t chunk) {
+namespace tt {
+size_t workspace_bytes_for(const tt_emb_table* tables, int32_t T, int64_t L, int64_t B, int32_t chunk,
+                           bool fwd_only) {
     int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
     if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3, fwd_only).total;
+}
+}  // namespace tt
+
+extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, int64_t L,
+                                         int64_t B, int32_t chunk) {
+    return workspace_bytes_for(tables, T, L, B, chunk, false);
 }
 
-extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
-                                 const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
-                                 void* workspace, size_t workspace_bytes, void* stream,
-                                 tt_emb_plan_t* plan_out) {
-    if (!plan_out) return TT_ERR_INVALID_ARG;
-    *plan_out = nullptr;
+// Plans into the host object *p (filled here; nothing is allocated). The
+// caller keeps `tables` alive as long as p uses it.
+tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                        const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
+                        size_t workspace_bytes, bool fwd_only, hipStream_t s) {
     int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
     tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3);
@@ -988,11 +998,10 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3);
+    if (fwd_only) NB3 = 0;
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3, fwd_only);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
-    tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
-    if (!p) return TT_ERR_INVALID_ARG;
     p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;
     p->M3 = M3;
     p->nb3 = (int32_t)NB3;
@@ -1005,7 +1014,8 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     }
     p->ws = (char*)workspace;
     p->lay = lay;
-    p->tables.assign(tables, tables + T);
+    p->tables = tables;
+    p->fwd_only = fwd_only;
     p->uniform = true;
     p->n1 = tables[0].n[0]; p->n2 = tables[0].n[1]; p->n3 = tables[0].n[2]; p->R = tables[0].rank;
     for (int k = 0; k < 3; ++k) p->extent[k] = 0;
@@ -1029,20 +1039,15 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     }
     // tables may share a core; a shared G2 needs a backward that adds the
     // tables' dG2 terms (the matrix-core dG2 kernel stores each slice once)
-    {
-        std::vector<std::pair<int64_t, int64_t>> r2((size_t)T);
-        for (int32_t t = 0; t < T; ++t) {
-            const tt_emb_table& x = tables[t];
-            r2[t] = {x.g_offset[1], x.g_offset[1] + (int64_t)x.m[1] * x.rank * x.n[1] * x.rank};
+    p->g2_overlap = false;
+    for (int32_t a = 0; a < T && !p->g2_overlap; ++a)
+        for (int32_t b = a + 1; b < T; ++b) {
+            const tt_emb_table& x = tables[a];
+            const tt_emb_table& y = tables[b];
+            const int64_t xe = x.g_offset[1] + (int64_t)x.m[1] * x.rank * x.n[1] * x.rank;
+            const int64_t ye = y.g_offset[1] + (int64_t)y.m[1] * y.rank * y.n[1] * y.rank;
+            if (x.g_offset[1] < ye && y.g_offset[1] < xe) { p->g2_overlap = true; break; }
         }
-        std::sort(r2.begin(), r2.end());
-        p->g2_overlap = false;
-        for (size_t t = 1; t < r2.size(); ++t)
-            if (r2[t].first < r2[t - 1].second) p->g2_overlap = true;
-    }
-    hipStream_t s = (hipStream_t)stream;
-
-    auto fail = [&](tt_status e) { delete p; return e; };
     // control words and descriptors
     // control words and the scans' tile status words (adjacent in the workspace)
     // are cleared by the launch that writes the first descriptors
@@ -1072,7 +1077,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                reinterpret_cast<uint32_t*>(p->ctrl()), nzero, p->at<TabDev>(lay.desc), b);
         else
             hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
-        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
     }
 
     int32_t* ctrl = p->ctrl();
@@ -1089,7 +1094,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                            p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
                            p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
                            ctrl, p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt);
-        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
     }
     // stable radix sort: key -> (skey, perm)
     if (L > 0) {
@@ -1107,18 +1112,18 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             const int shift = pass * kRadixBits;
             hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
                                kin, L, shift, lay.n_tiles, lay.hstride, hist);
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
             if (lay.n_tiles <= kDirectTiles) {
                 hipLaunchKernelGGL(k_radix_scatter<true>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                    s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
             } else {
                 if (scan_exclusive<uint32_t>(p, ++nscan, hist, (int64_t)kRadixBins * lay.hstride, nullptr, s) !=
                     TT_OK)
-                    return fail(TT_ERR_HIP);
+                    return TT_ERR_HIP;
                 hipLaunchKernelGGL(k_radix_scatter<false>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                    s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
             }
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
             kin = kout;
             vin = vout;
             bin = bout;
@@ -1135,23 +1140,23 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
             hipLaunchKernelGGL(k_gather, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
                                p->at<int32_t>(lay.skey), L, p->M3, p->at<int32_t>(lay.sorted_i3), key_start,
                                key_end, run_tiles);
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
         hipLaunchKernelGGL(k_key_tiles, dim3((unsigned)lay.n_ktiles), dim3(kSortThreads), 0, s, key_start,
                            key_end, K, chunk, key_tiles);
-        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         const bool kdirect = lay.n_ktiles <= kDirectTiles;
         if (!kdirect && scan_exclusive<uint64_t>(p, ++nscan, key_tiles, lay.n_ktiles, nullptr, s) != TT_OK)
-            return fail(TT_ERR_HIP);
+            return TT_ERR_HIP;
         hipLaunchKernelGGL(kdirect ? k_groups<true> : k_groups<false>, dim3((unsigned)lay.n_ktiles),
                            dim3(kSortThreads), 0, s, key_start, key_end, K, L, chunk, key_tiles, kscan,
                            p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
                            p->at<int32_t>(lay.group_cbase), ctrl);
-        if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+        if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         if (L > 0) {
             const bool rdirect = lay.n_tiles <= kDirectTiles;
             if (!rdirect && scan_exclusive<uint32_t>(p, ++nscan, run_tiles, lay.n_tiles, nullptr, s) != TT_OK)
-                return fail(TT_ERR_HIP);
+                return TT_ERR_HIP;
             hipLaunchKernelGGL(rdirect ? k_runs<true> : k_runs<false>, dim3((unsigned)lay.n_tiles),
                                dim3(kSortThreads), 0, s, p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
                                p->at<uint64_t>(lay.key_scan), key_start, key_end, run_tiles, L, p->M3, chunk,
@@ -1161,15 +1166,34 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
                                p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank),
                                p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN);
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
         if (lay.NFB > 0) {
             hipLaunchKernelGGL(k_batches, dim3(grid_for(lay.NFB, 256)), dim3(256), 0, s, p->desc(), T, K,
                                lay.NFB, kscan, p->at<int32_t>(lay.group_key),
                                p->at<int32_t>(lay.group_rbase), ctrl, p->at<BatchRec>(lay.batch));
-            if (hipGetLastError() != hipSuccess) return fail(TT_ERR_HIP);
+            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
     }
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                                 const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 tt_emb_plan_t* plan_out) {
+    if (!plan_out) return TT_ERR_INVALID_ARG;
+    *plan_out = nullptr;
+    if (!tables || T < 1) return TT_ERR_INVALID_ARG;
+    if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
+    tt_emb_plan_s* p = new (std::nothrow) tt_emb_plan_s();
+    if (!p) return TT_ERR_INVALID_ARG;
+    p->owned_tables = new (std::nothrow) tt_emb_table[T];
+    if (!p->owned_tables) { delete p; return TT_ERR_INVALID_ARG; }
+    std::memcpy(p->owned_tables, tables, sizeof(tt_emb_table) * (size_t)T);
+    const tt_status st = plan_into(p, p->owned_tables, T, indices, offsets, L, B, chunk, workspace,
+                                   workspace_bytes, false, (hipStream_t)stream);
+    if (st != TT_OK) { delete p; return st; }
     *plan_out = p;
     return TT_OK;
 }
@@ -1241,6 +1265,7 @@ extern "C" const char* tt_emb_status_string(tt_status s) {
         case TT_ERR_HIP: return "HIP runtime error";
         case TT_ERR_DEVICE_FLAG: return "device error flag set (bad index or offsets)";
         case TT_ERR_STALE: return "kept prefix products are stale (token does not match the plan)";
+        case TT_ERR_SCRATCH: return "batch needs more than the library's static scratch buffer holds";
     }
     return "unknown status";
 }

@@ -7,7 +7,6 @@
 #include <stddef.h>
 
 #include <algorithm>
-#include <vector>
 
 #include "tt_emb.h"
 
@@ -164,7 +163,8 @@ struct Layout {
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3);
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3,
+                   bool fwd_only);
 
 }  // namespace tt
 
@@ -191,9 +191,13 @@ struct tt_emb_plan_s {
     uint64_t next_token;      // last token handed out on this plan
     const float* kept_g1;
     const float* kept_g2;
+    bool fwd_only;            // the layout holds no backward buffers (forward calls only)
     char* ws;                 // workspace base (device)
     tt::Layout lay;
-    std::vector<tt_emb_table> tables;
+    const tt_emb_table* tables = nullptr;     // T descriptors (owned_tables, or the caller's
+    tt_emb_table* owned_tables = nullptr;     //     array for the length of one call)
+
+    ~tt_emb_plan_s() { delete[] owned_tables; }
 
     template <class P>
     P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
@@ -224,6 +228,16 @@ __device__ __forceinline__ void wait_vmem_done() {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// Plans into *p without allocating (plan.hip); the workspace size of a layout.
+tt_status plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                    const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
+                    size_t workspace_bytes, bool fwd_only, hipStream_t s);
+size_t workspace_bytes_for(const tt_emb_table* tables, int32_t T, int64_t L, int64_t B, int32_t chunk,
+                           bool fwd_only);
+// The forward on a plan (forward.hip); keep: also keep P (needs a full layout).
+tt_status forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3, float* out,
+                      bool keep, uint64_t* token, hipStream_t s);
 
 // Whether the plan's calls take the matrix-core kernels with these cores
 // (forward.hip, backward.hip).
