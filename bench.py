@@ -14,14 +14,19 @@ each phase (HIP events around back-to-back calls on the stream the kernels run
 on); the forward call's roofline figures; and the CPU oracle timed on a
 bounded sample of the same batch as `cpu_baseline`.
 
-Roofline of the forward call (the planner's output is an input to it): the
-work counted is the work the kernels execute. The forward contracts each
-distinct table row of a prefix group once, so its FLOP count is
-U * 2*n1*n2*R^2 (prefixes) + U_row * 2*n1*n2*n3*R (suffixes of distinct rows)
-+ L * D (pooling adds); the per-lookup count of the plain method (every lookup
-contracted) is reported beside it as context. HBM traffic per call comes from
-rocprofv3 counter passes kept under profiles/ and is reported only while the
-kernel sources still match the hash recorded there.
+Rooflines: every kernel's average duration comes from HIP events the
+library records around each launch on the stream it launches on
+(tt_emb_set_timing), in an instrumented pass after the timed region. The work
+counted is the work the kernels execute: the forward contracts each distinct
+table row of a prefix group once, so k_fwd_batch does U * 2*n1*n2*R^2
+(prefixes) + U_row * 2*n1*n2*n3*R (suffixes of distinct rows) FLOP, k_pool
+L * D adds; the per-lookup count of the plain method is reported beside it
+as context. `roofline` is k_fwd_batch (the forward's dominant kernel);
+`roofline_forward_call` adds pooling; `roofline_step` lists every kernel of
+the training step with its fp32 and fp64 FLOP (fractions of 157.3 and 78.6
+TFLOP/s) or its algorithmic bytes (fraction of 8 TB/s). HBM traffic comes
+from rocprofv3 counter passes kept under profiles/ and is reported only while
+the kernel sources still match the hash recorded there.
 """
 from __future__ import annotations
 
@@ -172,15 +177,74 @@ def main():
                                                 stream=stream), reps)
     torch.cuda.synchronize()
 
-    # executed work of one forward call (distinct rows of a group contracted once)
+    # per-kernel times, measured live: the library brackets every kernel it
+    # launches with HIP events on the stream it launches it on
+    # (tt_emb_set_timing); one instrumented pass of `reps` whole steps and
+    # `reps` plain forward calls on the same inputs, after the timed region
+    def kernel_avgs(records, calls):
+        agg = {}
+        for k, ms in records:
+            agg.setdefault(k, []).append(ms)
+        return {k: {"us": 1e3 * sum(v) / len(v), "per_call": len(v) / calls} for k, v in agg.items()}
+
+    tte.tt_emb_set_timing(None, True)
+    recs = []
+    for _ in range(reps):
+        recs += tte.tt_emb_kernel_times(step(), stream)
+    tte.tt_emb_set_timing(None, False)
+    step_kernels = kernel_avgs(recs, reps)
+    pl = plan()
+    tte.tt_emb_set_timing(pl, True)
+    for _ in range(reps):
+        tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream)
+    fwd_kernels = kernel_avgs(tte.tt_emb_kernel_times(pl, stream), reps)
+    tte.tt_emb_set_timing(pl, False)
+
+    # executed work (distinct rows of a group are contracted once)
     key_i3 = np.unique(p.indices)            # one table: a distinct index is a distinct (key, i3) row
     U_row = int(key_i3.size)
-    fwd_flop = U * 2 * n1 * n2 * R * R + U_row * 2 * n1 * n2 * n3 * R + L * D
-    fwd_flop_per_lookup = U * 2 * n1 * n2 * R * R + L * (2 * n1 * n2 * n3 * R + D)
-    core_bytes = 4 * (p.g1.size + p.g2.size + p.g3.size)
+    pre = U * 2 * n1 * n2 * R * R            # prefix products, per call
+    suf = U_row * 2 * n1 * n2 * n3 * R       # one suffix-sized product per distinct row
+    core_elems = p.g1.size + p.g2.size + p.g3.size
+    # kernel -> (fp32 FLOP, fp64 FLOP, algorithmic bytes) per launch
+    work = {
+        "k_fwd_batch": (pre + suf, 0, 0), "k_fwd_batch_keep": (pre + suf, 0, 0),
+        "k_pool": (L * D, 0, 4 * L * D + 4 * B * D),
+        "k_bwd_sum": (0, L * D, 4 * L * D + 4 * U_row * D),
+        "k_bwd_runs_c3": (suf, suf, 0), "k_bwd_dg3": (0, U_row * R * n3, 4 * U_row * R * n3),
+        "k_bwd_dg2": (0, pre, 0), "k_bwd_dg1": (0, pre, 0),
+        "k_sgd": (2 * core_elems, 0, 12 * core_elems),
+    }
+    PEAK_FP64_TFLOPS = 78.6
+
+    def kernel_roofline(name, rec):
+        f32, f64, by = work.get(name, (0, 0, 0))
+        sec = rec["us"] * 1e-6
+        out_ = {"kernel": name, "us": round(rec["us"], 2), "launches_per_call": rec["per_call"]}
+        if f32 or f64:
+            out_["fp32_tflops"] = round(f32 / sec / 1e12, 2)
+            out_["fp64_tflops"] = round(f64 / sec / 1e12, 2)
+            out_["frac"] = round(f32 / sec / 1e12 / PEAK_FP32_TFLOPS + f64 / sec / 1e12 / PEAK_FP64_TFLOPS, 4)
+            out_["bound"] = "mfma"
+        if by and not (f32 > 1e9 or f64 > 1e9):
+            out_["bound"] = "hbm"
+            out_["gbs"] = round(by / sec / 1e9, 1)
+            out_["frac"] = round(by / sec / 1e9 / PEAK_HBM_GBS, 4)
+        return out_
+
+    kb = fwd_kernels["k_fwd_batch"]["us"] * 1e-6
+    kpool = fwd_kernels["k_pool"]["us"] * 1e-6
+    achieved_tflops = (pre + suf) / kb / 1e12
+    fwd_flop = pre + suf + L * D
+    fwd_flop_per_lookup = pre + L * (2 * n1 * n2 * n3 * R + D)
+    core_bytes = 4 * core_elems
     fwd_bytes = 8 * L + 8 * (B + 1) + core_bytes + 4 * B * D
-    achieved_tflops = fwd_flop / (fwd_ms * 1e-3) / 1e12
     traffic = forward_traffic()
+    step_rows = sorted((kernel_roofline(k, v) for k, v in step_kernels.items()),
+                       key=lambda r: -r["us"] * r["launches_per_call"])
+    step_kernel_ms = sum(r["us"] * r["launches_per_call"] for r in step_rows) * 1e-3
+    f32_step = sum(work.get(k, (0, 0, 0))[0] * v["per_call"] for k, v in step_kernels.items())
+    f64_step = sum(work.get(k, (0, 0, 0))[1] * v["per_call"] for k, v in step_kernels.items())
 
     if args.calibrate_copy:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter values
@@ -221,15 +285,26 @@ def main():
         "forward_bags_per_s": round(B / (fwd_ms * 1e-3), 1),
         "plan_forward_bags_per_s": round(B / ((plan_ms + fwd_ms) * 1e-3), 1),
         "forward_rows_per_s": round(L / (fwd_ms * 1e-3), 1),
-        "roofline": {"kernel": "tt_emb_forward call (k_fwd_batch + k_pool)",
+        "workspace_bytes": int(ws.numel()),
+        "roofline": {"kernel": "k_fwd_batch (the forward's dominant kernel: prefix and suffix products)",
                      "bound": "mfma", "achieved": round(achieved_tflops, 3),
                      "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
                      "traffic": traffic,
-                     "flop_per_call": int(fwd_flop),
-                     "flop_per_call_if_every_lookup_contracted": int(fwd_flop_per_lookup),
-                     "algorithmic_bytes_per_call": int(fwd_bytes),
-                     "hbm_frac_algorithmic": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                     "avg_launch_us": round(kb * 1e6, 2),
+                     "flop_per_launch": int(pre + suf),
+                     "flop_per_launch_if_every_lookup_contracted": int(pre + L * 2 * n1 * n2 * n3 * R)},
+        "roofline_forward_call": {"kernels": "k_fwd_batch + k_pool", "us": round((kb + kpool) * 1e6, 2),
+                                  "flop": int(fwd_flop), "flop_if_every_lookup_contracted": int(fwd_flop_per_lookup),
+                                  "achieved": round(fwd_flop / (kb + kpool) / 1e12, 3), "unit": "TFLOP/s",
+                                  "frac": round(fwd_flop / (kb + kpool) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                                  "algorithmic_bytes": int(fwd_bytes),
+                                  "hbm_frac_algorithmic": round(fwd_bytes / (kb + kpool) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline_step": {"kernel_ms_per_step": round(step_kernel_ms, 4),
+                          "fp32_flop": int(f32_step), "fp64_flop": int(f64_step),
+                          "fp32_frac": round(f32_step / (step_kernel_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                          "fp64_frac": round(f64_step / (step_kernel_ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4),
+                          "kernels": step_rows},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

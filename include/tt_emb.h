@@ -248,6 +248,23 @@ typedef struct {
 tt_status tt_emb_query_paths(tt_emb_plan_t plan, const float* g1, const float* g2,
                              tt_emb_path_info* info);
 
+/* Kernel timing, for measurement. With timing on, every kernel that a call
+ * on this plan enqueues is bracketed by two HIP events recorded on that
+ * call's stream (the first 1024 launches since the last read are kept).
+ * tt_emb_kernel_times synchronises `stream`, writes up to `max` records in
+ * launch order (kernel name, static storage; milliseconds between the two
+ * events), sets *count, and clears the records. Timing adds two event
+ * records per launch; it is off unless enabled. tt_emb_set_timing(NULL, on)
+ * sets it for every plan created afterwards (from its planning kernels on). */
+typedef struct {
+    const char* kernel;
+    float ms;
+} tt_emb_kernel_time;
+
+tt_status tt_emb_set_timing(tt_emb_plan_t plan, int32_t enable);
+tt_status tt_emb_kernel_times(tt_emb_plan_t plan, tt_emb_kernel_time* out, int32_t max,
+                              int32_t* count, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* tt_emb_status_string(tt_status s);
 

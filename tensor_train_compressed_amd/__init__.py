@@ -21,7 +21,8 @@ __all__ = [
     "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
     "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
-    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "TT_PATH_MATRIX_CORE",
+    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
+    "tt_emb_kernel_times", "TT_PATH_MATRIX_CORE",
     "TT_PATH_GENERIC", "TT_ERR_STALE", "TT_ERR_SCRATCH", "Plan", "EXPORTS",
 ]
 
@@ -40,7 +41,8 @@ EXPORTS = (
     "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train",
     "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
-    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_status_string",
+    "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
+    "tt_emb_kernel_times", "tt_emb_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +76,10 @@ class _PathInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float)]
+
+
 class _View(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "key", "i3", "bag_of", "perm", "sorted_i3", "sorted_bag", "group_key", "group_start",
@@ -104,6 +110,10 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_query_paths.argtypes = [P, P, P, ctypes.POINTER(_PathInfo)]
         lib.tt_emb_forward_scratch.argtypes = [P, i32, P, P, i64, i64, i32, P, P, P, P, P]
         lib.tt_emb_forward_scratch.restype = ctypes.c_int
+        lib.tt_emb_set_timing.argtypes = [P, i32]
+        lib.tt_emb_set_timing.restype = ctypes.c_int
+        lib.tt_emb_kernel_times.argtypes = [P, ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32), P]
+        lib.tt_emb_kernel_times.restype = ctypes.c_int
         lib.tt_emb_scratch_capacity.argtypes = []
         lib.tt_emb_scratch_capacity.restype = ctypes.c_size_t
         lib.tt_emb_sgd.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P]
@@ -287,6 +297,23 @@ def tt_emb_query_paths(plan: Plan, g1, g2) -> dict:
                                              ctypes.c_void_p(g2.data_ptr()), ctypes.byref(info)),
            "tt_emb_query_paths")
     return {name: int(getattr(info, name)) for name, _ in _PathInfo._fields_}
+
+
+def tt_emb_set_timing(plan: Optional[Plan], enable: bool = True):
+    """Bracket every kernel the plan's calls launch with HIP events (plan
+    None: every plan created from now on, its planning kernels included)."""
+    _check(load_library().tt_emb_set_timing(None if plan is None else plan.handle, 1 if enable else 0),
+           "tt_emb_set_timing")
+
+
+def tt_emb_kernel_times(plan: Plan, stream=None, max_records: int = 1024) -> list:
+    """[(kernel name, ms)] of the launches recorded since the last read, in
+    launch order (synchronises the stream)."""
+    buf = (_KernelTime * max_records)()
+    n = ctypes.c_int32(0)
+    _check(load_library().tt_emb_kernel_times(plan.handle, buf, max_records, ctypes.byref(n),
+                                              _stream(stream)), "tt_emb_kernel_times")
+    return [(buf[i].kernel.decode(), float(buf[i].ms)) for i in range(n.value)]
 
 
 def tt_emb_scratch_capacity() -> int:

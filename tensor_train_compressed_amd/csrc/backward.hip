@@ -518,7 +518,8 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
 // lane order the run kernel reads it (store_prefix_lanes). Skipped when the
 // forward kept P on this plan for the same G1 and G2.
 template <int N1, int N2, int R>
-__global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t nb,
+__global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ recs, int64_t cap,
+                                                 const int32_t* __restrict__ ctrl,
                                                  const int32_t* __restrict__ run_i3,
                                                  const float* __restrict__ g1, const float* __restrict__ g2,
                                                  float* __restrict__ pbuf) {
@@ -528,14 +529,14 @@ __global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ re
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];
-    const int64_t G = gridDim.x;
-    int64_t b = blockIdx.x;
-    int32_t rwA = rec_word(recs, b, nb);
-    int32_t rwB = rec_word(recs, b + G, nb);
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    const int64_t nl = ctrl[CTRL_NUM_BATCHES];
+    int32_t rwA = rec_word(recs, snake(0, w, G), cap, nl);
+    int32_t rwB = rec_word(recs, snake(1, w, G), cap, nl);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, run_i3, g1, g2, f);
-    for (; b < nb; b += G) {
-        const int32_t rwC = rec_word(recs, b + 2 * G, nb);
+    for (int64_t r = 0; snake(r, w, G) < nl; ++r) {
+        const int32_t rwC = rec_word(recs, snake(r + 2, w, G), cap, nl);
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) batch_prefix<N1, N2, R>(rwA, run_i3, f, sU, sRb, sI3, c);
@@ -917,16 +918,25 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
 // element takes one fp64 atomic per group (groups of every slice add to the
 // same i1). A wave per half batch read the 32 KB G2 slice twice per batch,
 // and that L2 traffic set its time.
+// Waves take the batch slots in slice-major order (the planner's place map),
+// so waves that run together work on different i1 rows of dG1 rather than
+// piling atomics on the same ones.
 template <int N1, int N2, int R>
-__global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ recs, int64_t nb,
+__global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ recs, int64_t cap,
+                                                 const int32_t* __restrict__ ctrl,
+                                                 const int32_t* __restrict__ place,
                                                  const float* __restrict__ dpg, const float* __restrict__ g2,
                                                  double* __restrict__ dg1) {
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2, MT = kFwdBatch / 4;
     static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0 && MT == 2, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (b >= nb) return;
-    const int32_t rw = rec_word(recs, b, nb);
+    const int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (k >= cap) return;
+    const int32_t pos = place[k];
+    const int64_t nl = ctrl[CTRL_NUM_BATCHES];
+    if (pos < 0 || pos >= nl) return;
+    const int64_t b = pos;
+    const int32_t rw = rec_word(recs, b, cap, nl);
     const int ng = rec_field(rw, RW_NG);
     if (ng <= 0) return;
     const int32_t g0 = rec_field(rw, RW_G0);
@@ -998,7 +1008,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     const bool bucket3 = p->nb3 > 0 && p->L > 0;
     if (!p->packed) {
         // elements outside every table's slices are zero in the gradients
-        tt_status st = fill32(dg2, 0u, p->extent[1], s);
+        tt_status st = fill32(p, dg2, 0u, p->extent[1], s);
         if (st != TT_OK) return st;
     }
     constexpr int DL = N1 * N2 * N3 / 64, D = N1 * N2 * N3, CN = R * N3;
@@ -1017,7 +1027,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                       p->at<int32_t>(p->lay.gdone), p->ctrl()};
     const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                      p->at<int32_t>(p->lay.run_start), p->L, gout, S, xpart};
-    hipLaunchKernelGGL(k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
+    TT_LAUNCH(p, "k_bwd_sum", s, k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
                        sa, pa);
     TT_LAUNCH_CHECK();
     if (p->L > 0) {
@@ -1026,14 +1036,14 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         const SlotArgs sl{p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.run_bkt),
                           p->at<int32_t>(p->lay.run_rank), p->at<int32_t>(p->lay.bucket_runs)};
         const int64_t nslot = bucket3 ? (p->L + 1023) / 1024 : 0;
-        hipLaunchKernelGGL(k_bwd_cross<DL>, dim3((unsigned)(nspan + nslot)), dim3(1024), 0, s, xpart,
+        TT_LAUNCH(p, "k_bwd_cross", s, k_bwd_cross<DL>, dim3((unsigned)(nspan + nslot)), dim3(1024), 0, s, xpart,
                            p->at<int32_t>(p->lay.xcnt), xr, S, p->ctrl(), nspan, sl);
         TT_LAUNCH_CHECK();
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
             const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
-            hipLaunchKernelGGL((k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
-                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
+            TT_LAUNCH(p, "k_bwd_pfx", s, (k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
             TT_LAUNCH_CHECK();
         }
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
@@ -1044,31 +1054,32 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
             // each run's dG3 term over its own S row when the row holds it
             float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);
             const int64_t c3s = CN <= D ? D : CN;
-            hipLaunchKernelGGL((k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra, c3,
+            TT_LAUNCH(p, "k_bwd_runs_c3", s, (k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra, c3,
                                c3s);
             TT_LAUNCH_CHECK();
-            hipLaunchKernelGGL((k_bwd_dg3<CN>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
+            TT_LAUNCH(p, "k_bwd_dg3", s, (k_bwd_dg3<CN>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
                                p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3);
         } else {
-            hipLaunchKernelGGL((k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
+            TT_LAUNCH(p, "k_bwd_runs", s, (k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
         TT_LAUNCH_CHECK();
     }
     {
         // dP of every group now sits over its P
         const int64_t w2 = p->n_i2 * (N2 * R / 16);
-        hipLaunchKernelGGL((k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(), p->T,
+        TT_LAUNCH(p, "k_bwd_dg2", s, (k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(), p->T,
                            p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key),
                            pbuf, g1, dg2, p->n_i2);
         TT_LAUNCH_CHECK();
         const int64_t w1 = p->n_fb;
         if (w1 > 0) {
-            hipLaunchKernelGGL((k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
-                               p->at<BatchRec>(p->lay.batch), p->n_fb, pbuf, g2, acc1);
+            TT_LAUNCH(p, "k_bwd_dg1", s, (k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
+                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.batch_place),
+                               pbuf, g2, acc1);
             TT_LAUNCH_CHECK();
         }
     }
-    hipLaunchKernelGGL(k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
+    TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
                        bucket3 ? 0 : p->extent[2], p->ctrl());
     TT_LAUNCH_CHECK();
     return TT_OK;
@@ -1104,14 +1115,14 @@ static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2
     p->kept_token = 0;
     if (bwd_mfma_ok(p, g1, g2)) return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, s);
     tt_status st = TT_OK;
-    if ((st = fill32(dg1, 0u, p->extent[0], s)) != TT_OK) return st;
-    if ((st = fill32(dg2, 0u, p->extent[1], s)) != TT_OK) return st;
-    if ((st = fill32(dg3, 0u, p->extent[2], s)) != TT_OK) return st;
+    if ((st = fill32(p, dg1, 0u, p->extent[0], s)) != TT_OK) return st;
+    if ((st = fill32(p, dg2, 0u, p->extent[1], s)) != TT_OK) return st;
+    if ((st = fill32(p, dg3, 0u, p->extent[2], s)) != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;
     for (int32_t t = 0; t < p->T; ++t) maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
     const size_t lds = 2 * sizeof(float) * (size_t)maxp;
-    hipLaunchKernelGGL(k_bwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
+    TT_LAUNCH(p, "k_bwd_generic", s, k_bwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
                        p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
                        p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
                        p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
@@ -1152,7 +1163,7 @@ extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3
     const SgdArgs a{{g1, g2, g3}, {dg1, dg2, dg3}, {p->extent[0], p->extent[1], p->extent[2]}};
     const int64_t nmax = std::max(p->extent[0], std::max(p->extent[1], p->extent[2]));
     if (nmax <= 0) return TT_OK;
-    hipLaunchKernelGGL(k_sgd, dim3(std::min<unsigned>(grid_for(nmax / 4 + 1, 256), 2048u)), dim3(256), 0, s, a, lr);
+    TT_LAUNCH(p, "k_sgd", s, k_sgd, dim3(std::min<unsigned>(grid_for(nmax / 4 + 1, 256), 2048u)), dim3(256), 0, s, a, lr);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }

@@ -202,14 +202,15 @@ struct FwdTiles {
     }
 };
 
-// Persistent workgroups (a few per CU) walk the batch slots b = blockIdx.x,
-// blockIdx.x + gridDim.x, ... . While a workgroup runs the tiles of one batch,
-// the loads of its next batch (G2 slice, G1 rows, run i3 list) are in flight,
-// and the records of the next two batches are already in registers, so a
-// batch's prologue costs no exposed memory round trip; slots without a group
-// cost a record read.
+// Persistent workgroups (a few per CU) walk the planner's batch list in a
+// snake (round r: batch snake(r, blockIdx.x, gridDim.x)); the list holds only
+// batches with groups and starts with the heaviest, so every workgroup gets
+// four or five batches of mixed weight. While a workgroup runs the tiles of
+// one batch, the loads of its next batch (G2 slice, G1 rows, run i3 list)
+// are in flight, and the records of the next two batches are already in
+// registers, so a batch's prologue costs no exposed memory round trip.
 template <int N1, int N2, int R, int N3, bool KEEP>
-__global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t nb) {
+__global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, const int32_t* __restrict__ ctrl) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int SG = B::SG;
     static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 256, "shape");
@@ -217,15 +218,15 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t nb) {
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
-    const int64_t G = gridDim.x;
-    int64_t b = blockIdx.x;
-    int32_t rwA = rec_word(a.recs, b, nb);
-    int32_t rwB = rec_word(a.recs, b + G, nb);
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    const int64_t nl = ctrl[CTRL_NUM_BATCHES];
+    int32_t rwA = rec_word(a.recs, snake(0, w, G), cap, nl);
+    int32_t rwB = rec_word(a.recs, snake(1, w, G), cap, nl);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, a.run_i3, a.g1, a.g2, f);
     FwdTiles<N1, N2, R, N3> tl;
-    for (; b < nb; b += G) {
-        const int32_t rwC = rec_word(a.recs, b + 2 * G, nb);
+    for (int64_t r = 0; snake(r, w, G) < nl; ++r) {
+        const int32_t rwC = rec_word(a.recs, snake(r + 2, w, G), cap, nl);
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) {
@@ -298,15 +299,15 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
         if (keep)
-            hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
-                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
+            TT_LAUNCH(p, "k_fwd_batch_keep", s, (k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
+                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
         else
-            hipLaunchKernelGGL((k_fwd_batch<N1, N2, R, N3, false>), dim3((unsigned)grid),
-                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb);
+            TT_LAUNCH(p, "k_fwd_batch", s, (k_fwd_batch<N1, N2, R, N3, false>), dim3((unsigned)grid),
+                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
         TT_LAUNCH_CHECK();
     }
     if (p->TB > 0) {
-        hipLaunchKernelGGL(k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
+        TT_LAUNCH(p, "k_pool", s, k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
                            p->at<float>(p->lay.stage), out, p->ctrl());
         TT_LAUNCH_CHECK();
@@ -353,13 +354,13 @@ tt_status tt::forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, co
         }
         return st;
     }
-    tt_status st = fill32(out, 0u, p->TB * p->D, s);
+    tt_status st = fill32(p, out, 0u, p->TB * p->D, s);
     if (st != TT_OK) return st;
     if (p->lay.Cmax == 0) return TT_OK;
     int maxp = 0;
     for (int32_t t = 0; t < p->T; ++t) maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
     const size_t lds = sizeof(float) * (size_t)maxp;
-    hipLaunchKernelGGL(k_fwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
+    TT_LAUNCH(p, "k_fwd_generic", s, k_fwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
                        p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
                        p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
                        p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),

@@ -23,12 +23,15 @@
 //   k_key_tiles       present keys and chunks per tile of keys
 //   k_groups          key scan (group id and first chunk of every key), group tables
 //   k_runs            row-run ids and tables, chunk table; runs per G3 row
-//   k_batches         one record per forward batch (kFwdBatch groups of one slice)
+//   k_runs            (also counts the forward batch slots that hold a group, per tile)
+//   k_batches         the records of the batch slots (kFwdBatch groups of one slice) that
+//                     hold a group, compacted into the batch list
 // A device-wide scan of the tile totals runs before k_radix_scatter, k_groups
 // or k_runs only when there are more than kDirectTiles tiles.
 #include "tt_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <new>
 
@@ -121,6 +124,8 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_bkt = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.bucket_runs = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.NFB = NFB;
+    y.batch_tiles = take(sizeof(uint32_t) * (size_t)((NFB + kSlotTile - 1) / kSlotTile));
+    y.batch_place = take(sizeof(int32_t) * (size_t)NFB);
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
     return y;
@@ -135,12 +140,47 @@ __global__ void k_fill32(uint32_t* p, uint32_t v, int64_t n) {
     for (; i < n; i += stride) p[i] = v;
 }
 
-tt_status fill32(void* p, uint32_t v, int64_t n, hipStream_t s) {
+tt_status fill32(const tt_emb_plan_s* p, void* ptr, uint32_t v, int64_t n, hipStream_t s) {
     if (n <= 0) return TT_OK;
     unsigned g = std::min<unsigned>(grid_for(n, 256), 4096u);
-    hipLaunchKernelGGL(k_fill32, dim3(g), dim3(256), 0, s, (uint32_t*)p, v, n);
+    TT_LAUNCH(p, "k_fill32", s, k_fill32, dim3(g), dim3(256), 0, s, (uint32_t*)ptr, v, n);
     TT_LAUNCH_CHECK();
     return TT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+
+void timing_free(Timing* t) {
+    if (!t) return;
+    for (int i = 0; i < t->created; ++i) {
+        (void)hipEventDestroy(t->ev[i][0]);
+        (void)hipEventDestroy(t->ev[i][1]);
+    }
+    delete t;
+}
+
+int kt_begin(const tt_emb_plan_s* p, const char* name, hipStream_t s) {
+    Timing* t = p ? p->timing : nullptr;
+    if (!t || t->n >= Timing::kCap) return -1;
+    const int i = t->n;
+    if (i >= t->created) {
+        if (hipEventCreate(&t->ev[i][0]) != hipSuccess) return -1;
+        if (hipEventCreate(&t->ev[i][1]) != hipSuccess) {
+            (void)hipEventDestroy(t->ev[i][0]);
+            return -1;
+        }
+        t->created = i + 1;
+    }
+    if (hipEventRecord(t->ev[i][0], s) != hipSuccess) return -1;
+    t->name[i] = name;
+    return i;
+}
+
+void kt_end(const tt_emb_plan_s* p, int slot, hipStream_t s) {
+    if (slot < 0) return;
+    Timing* t = p->timing;
+    if (hipEventRecord(t->ev[slot][1], s) == hipSuccess) t->n = slot + 1;
 }
 
 struct DescBatch {
@@ -592,13 +632,13 @@ template <class V>
 static tt_status scan_exclusive(const tt_emb_plan_s* p, int seq, V* data, int64_t n, V* total_out,
                                 hipStream_t s) {
     if (n <= 4 * (int64_t)kScanTile) {
-        hipLaunchKernelGGL(k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, data, n, total_out);
+        TT_LAUNCH(p, "k_scan_single", s, k_scan_single<V>, dim3(1), dim3(kScanThreads), 0, s, data, n, total_out);
         TT_LAUNCH_CHECK();
         return TT_OK;
     }
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
     if (seq < 1 || seq >= CTRL_SCAN_MAX || nb > p->lay.scan_tiles) return TT_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(k_scan_lookback<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n,
+    TT_LAUNCH(p, "k_scan_lookback", s, k_scan_lookback<V>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, data, n,
                        p->at<ScanTileStatus>(p->lay.scan_st),
                        reinterpret_cast<uint32_t*>(p->ctrl() + CTRL_SCAN_CTR + seq), (uint32_t)seq,
                        total_out, p->ctrl());
@@ -774,6 +814,31 @@ __device__ __forceinline__ int32_t bucket3(const TabDev* __restrict__ desc, int3
 // of row-run heads before s), and the chunk table: position s opens a chunk
 // when it lies a multiple of `chunk` past its group's start (chunk c of group
 // g starts `chunk` lookups after the previous one of g).
+// Forward batch slot b (layer-major): its table, slice and layer, and the
+// slice's groups [gs0, gs1).
+struct SlotOf {
+    TabDev d;
+    int32_t i2, jb, gs0, gs1;
+    int64_t kb;
+};
+__device__ __forceinline__ SlotOf slot_of(const TabDev* __restrict__ desc, int32_t T, int64_t K, int64_t b,
+                                          const uint64_t* __restrict__ key_scan, const int32_t* __restrict__ ctrl) {
+    int lo = 0, hi = T;   // last table with fb_base <= b
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
+    }
+    SlotOf o;
+    o.d = desc[lo];
+    o.i2 = (int32_t)((b - o.d.fb_base) % o.d.m2);
+    o.jb = (int32_t)((b - o.d.fb_base) / o.d.m2);
+    o.kb = (int64_t)o.d.key_base + (int64_t)o.i2 * o.d.m1;
+    const int64_t ke = o.kb + o.d.m1;
+    o.gs0 = (int32_t)(key_scan[o.kb] >> 32);
+    o.gs1 = ke < K ? (int32_t)(key_scan[ke] >> 32) : ctrl[CTRL_NUM_GROUPS];
+    return o;
+}
+
 template <bool DIRECT>
 __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ skey,
@@ -793,7 +858,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int32_t* __restrict__ i3cnt, int32_t n3cnt,
                                                        int32_t* __restrict__ run_rank,
                                                        int32_t* __restrict__ run_bkt,
-                                                       const TabDev* __restrict__ desc, int32_t T, int32_t CN) {
+                                                       const TabDev* __restrict__ desc, int32_t T, int32_t CN,
+                                                       int64_t K, int64_t NFB,
+                                                       uint32_t* __restrict__ batch_tiles) {
     __shared__ uint32_t sh3[kMaxBuckets3];
     for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
     const int64_t tile = blockIdx.x;
@@ -865,46 +932,85 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
             r += hr[j];
         }
     }
+    // forward batch slots holding a group, per tile of kSlotTile slots (the
+    // group tables are complete: k_groups ran before); kSortThreads slots per
+    // round, each tile's count added up over its waves in LDS
+    constexpr int TPR = kSortThreads / kSlotTile, WPT = kSlotTile / 64;
+    static_assert(kSortThreads % kSlotTile == 0 && kSlotTile % 64 == 0, "slot tiles");
+    __shared__ uint32_t wcnt[kSortWaves];
+    const int64_t nst = (NFB + kSlotTile - 1) / kSlotTile;
+    for (int64_t jt0 = (int64_t)blockIdx.x * TPR; jt0 < nst; jt0 += (int64_t)gridDim.x * TPR) {
+        const int64_t b = jt0 * kSlotTile + threadIdx.x;
+        bool live = false;
+        if (b < NFB) {
+            const SlotOf o = slot_of(desc, T, K, b, key_scan, ctrl);
+            live = o.gs1 - (o.gs0 + kFwdBatch * o.jb) > 0;
+        }
+        const uint64_t m = __ballot(live);
+        if ((threadIdx.x & 63) == 0) wcnt[threadIdx.x >> 6] = (uint32_t)__popcll(m);
+        __syncthreads();
+        if (threadIdx.x < TPR && jt0 + threadIdx.x < nst) {
+            uint32_t c = 0;
+            for (int w = 0; w < WPT; ++w) c += wcnt[threadIdx.x * WPT + w];
+            batch_tiles[jt0 + threadIdx.x] = c;
+        }
+        __syncthreads();   // wcnt is reused by the next round
+    }
 }
 
-// One thread per forward batch slot (table t, i2, j): the j-th run of
-// kFwdBatch groups among the groups of slice (t, i2), which are consecutive in
-// key order. Writes the batch's record; ng = 0 when the slot has no group.
-__global__ __launch_bounds__(256) void k_batches(const TabDev* __restrict__ desc, int32_t T, int64_t K,
-                                                 int64_t NFB, const uint64_t* __restrict__ key_scan,
-                                                 const int32_t* __restrict__ group_key,
-                                                 const int32_t* __restrict__ group_rbase,
-                                                 const int32_t* __restrict__ ctrl,
-                                                 BatchRec* __restrict__ rec) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= NFB) return;
-    int lo = 0, hi = T;   // last table with fb_base <= b
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
-    }
-    const TabDev d = desc[lo];
-    const int32_t nb = (d.m1 + kFwdBatch - 1) / kFwdBatch;
-    const int32_t i2 = (int32_t)((b - d.fb_base) / nb), jb = (int32_t)((b - d.fb_base) % nb);
-    const int64_t kb = (int64_t)d.key_base + (int64_t)i2 * d.m1, ke = kb + d.m1;
-    const int32_t gs0 = (int32_t)(key_scan[kb] >> 32);
-    const int32_t gs1 = ke < K ? (int32_t)(key_scan[ke] >> 32) : ctrl[CTRL_NUM_GROUPS];
+// One workgroup per tile of kSlotTile batch slots, one slot per thread: the
+// record of a slot that holds a group (the jb-th run of kFwdBatch groups
+// among its slice's groups, consecutive in key order), written at the slot's
+// place in the batch list: the slots holding a group in earlier tiles (the
+// workgroup adds up k_runs' per-tile counts itself) plus those before it in
+// the tile. The record's loads are issued before the counts are added up.
+// Every slot's place (-1: no group) goes to `place`, indexed slice-major
+// (fb_base + i2*ceil(m1/kFwdBatch) + jb); the last tile writes the list's
+// length.
+__global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict__ desc, int32_t T, int64_t K,
+                                                       int64_t NFB, const uint64_t* __restrict__ key_scan,
+                                                       const int32_t* __restrict__ group_key,
+                                                       const int32_t* __restrict__ group_rbase,
+                                                       int32_t* __restrict__ ctrl,
+                                                       const uint32_t* __restrict__ batch_tiles,
+                                                       int32_t* __restrict__ place,
+                                                       BatchRec* __restrict__ rec) {
+    __shared__ uint32_t wsum[17];   // (block_exclusive_scan's per-wave sums)
+    const int64_t jt = blockIdx.x;
+    const int64_t b = jt * kSlotTile + threadIdx.x;
     BatchRec r;
     memset(&r, 0, sizeof(r));
-    r.g0 = gs0 + kFwdBatch * jb;
-    r.ng = max(0, min(kFwdBatch, gs1 - r.g0));
-    r.i2 = i2;
-    r.o1 = d.o1; r.o2 = d.o2; r.o3 = d.o3;
-    if (r.ng > 0) {
-        r.rb0 = group_rbase[r.g0];
-        for (int j = 0; j < kFwdBatch; ++j) {
-            if (j < r.ng) r.i1[j] = (int32_t)(group_key[r.g0 + j] - kb);
-            r.rbase[j] = group_rbase[r.g0 + min(j, r.ng)] - r.rb0;
+    SlotOf o{};
+    if (b < NFB) {
+        o = slot_of(desc, T, K, b, key_scan, ctrl);
+        r.g0 = o.gs0 + kFwdBatch * o.jb;
+        r.ng = max(0, min(kFwdBatch, o.gs1 - r.g0));
+        if (r.ng > 0) {
+            r.i2 = o.i2;
+            r.o1 = o.d.o1; r.o2 = o.d.o2; r.o3 = o.d.o3;
+            r.rb0 = group_rbase[r.g0];
+            for (int j = 0; j < kFwdBatch; ++j) {
+                if (j < r.ng) r.i1[j] = (int32_t)(group_key[r.g0 + j] - o.kb);
+                r.rbase[j] = group_rbase[r.g0 + min(j, r.ng)] - r.rb0;
+            }
+            r.nr = group_rbase[r.g0 + r.ng] - r.rb0;
+            r.rbase[kFwdBatch] = r.nr;
         }
-        r.nr = group_rbase[r.g0 + r.ng] - r.rb0;
-        r.rbase[kFwdBatch] = r.nr;
     }
-    rec[b] = r;
+    uint32_t base = 0;
+    for (int64_t j0 = 0; j0 < jt; j0 += kSlotTile) {
+        const uint32_t v = j0 + threadIdx.x < jt ? batch_tiles[j0 + threadIdx.x] : 0u;
+        uint32_t tot;
+        (void)block_exclusive_scan<uint32_t>(v, wsum, &tot);   // synchronises
+        base += tot;
+    }
+    uint32_t tot;
+    const uint32_t pos = base + block_exclusive_scan<uint32_t>(r.ng > 0 ? 1u : 0u, wsum, &tot);
+    if (jt == (NFB - 1) / kSlotTile && threadIdx.x == 0) ctrl[CTRL_NUM_BATCHES] = (int32_t)(base + tot);
+    if (b >= NFB) return;
+    const int64_t nb1 = (o.d.m1 + kFwdBatch - 1) / kFwdBatch;
+    place[o.d.fb_base + (int64_t)o.i2 * nb1 + o.jb] = r.ng > 0 ? (int32_t)pos : -1;
+    if (r.ng > 0) rec[pos] = r;
 }
 
 }  // namespace tt
@@ -913,6 +1019,9 @@ using namespace tt;
 
 // ---------------------------------------------------------------------------
 // host side
+
+// Plans created while this is set time their kernels from the start.
+static std::atomic<int> g_timing_default{0};
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
                               int32_t* M3_out, int64_t* PR_out, int64_t* CN_out, int64_t* E1_out,
@@ -1073,10 +1182,10 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             kb += x.m[0] * x.m[1];
         }
         if (first == 0)
-            hipLaunchKernelGGL(k_init, dim3(std::min<unsigned>(grid_for(nzero, 256), 64u)), dim3(256), 0, s,
+            TT_LAUNCH(p, "k_init", s, k_init, dim3(std::min<unsigned>(grid_for(nzero, 256), 64u)), dim3(256), 0, s,
                                reinterpret_cast<uint32_t*>(p->ctrl()), nzero, p->at<TabDev>(lay.desc), b);
         else
-            hipLaunchKernelGGL(k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
+            TT_LAUNCH(p, "k_write_desc", s, k_write_desc, dim3(1), dim3(16), 0, s, p->at<TabDev>(lay.desc), b);
         if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
     }
 
@@ -1090,7 +1199,7 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     // lookup, per offset and per key)
     {
         const int64_t n = std::max<int64_t>(std::max<int64_t>(std::max<int64_t>(L, p->TB + 1), K), n3cnt);
-        hipLaunchKernelGGL(k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
+        TT_LAUNCH(p, "k_split", s, k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
                            p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
                            p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
                            ctrl, p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt);
@@ -1110,17 +1219,17 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             int32_t* vout = p->at<int32_t>(to_final ? lay.sort_v1 : lay.sort_v0);
             int32_t* bout = p->at<int32_t>(to_final ? lay.sort_b1 : lay.sort_b0);
             const int shift = pass * kRadixBits;
-            hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
+            TT_LAUNCH(p, "k_radix_hist", s, k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
                                kin, L, shift, lay.n_tiles, lay.hstride, hist);
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
             if (lay.n_tiles <= kDirectTiles) {
-                hipLaunchKernelGGL(k_radix_scatter<true>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
+                TT_LAUNCH(p, "k_radix_scatter", s, k_radix_scatter<true>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                    s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
             } else {
                 if (scan_exclusive<uint32_t>(p, ++nscan, hist, (int64_t)kRadixBins * lay.hstride, nullptr, s) !=
                     TT_OK)
                     return TT_ERR_HIP;
-                hipLaunchKernelGGL(k_radix_scatter<false>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
+                TT_LAUNCH(p, "k_radix_scatter", s, k_radix_scatter<false>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                    s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
             }
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
@@ -1137,18 +1246,18 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
         uint32_t* run_tiles = p->at<uint32_t>(lay.run_tiles);
         uint64_t* key_tiles = p->at<uint64_t>(lay.key_tiles);
         if (L > 0) {
-            hipLaunchKernelGGL(k_gather, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
+            TT_LAUNCH(p, "k_gather", s, k_gather, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
                                p->at<int32_t>(lay.skey), L, p->M3, p->at<int32_t>(lay.sorted_i3), key_start,
                                key_end, run_tiles);
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
-        hipLaunchKernelGGL(k_key_tiles, dim3((unsigned)lay.n_ktiles), dim3(kSortThreads), 0, s, key_start,
+        TT_LAUNCH(p, "k_key_tiles", s, k_key_tiles, dim3((unsigned)lay.n_ktiles), dim3(kSortThreads), 0, s, key_start,
                            key_end, K, chunk, key_tiles);
         if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         const bool kdirect = lay.n_ktiles <= kDirectTiles;
         if (!kdirect && scan_exclusive<uint64_t>(p, ++nscan, key_tiles, lay.n_ktiles, nullptr, s) != TT_OK)
             return TT_ERR_HIP;
-        hipLaunchKernelGGL(kdirect ? k_groups<true> : k_groups<false>, dim3((unsigned)lay.n_ktiles),
+        TT_LAUNCH(p, "k_groups", s, kdirect ? k_groups<true> : k_groups<false>, dim3((unsigned)lay.n_ktiles),
                            dim3(kSortThreads), 0, s, key_start, key_end, K, L, chunk, key_tiles, kscan,
                            p->at<int32_t>(lay.group_key), p->at<int32_t>(lay.group_start),
                            p->at<int32_t>(lay.group_cbase), ctrl);
@@ -1157,7 +1266,7 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             const bool rdirect = lay.n_tiles <= kDirectTiles;
             if (!rdirect && scan_exclusive<uint32_t>(p, ++nscan, run_tiles, lay.n_tiles, nullptr, s) != TT_OK)
                 return TT_ERR_HIP;
-            hipLaunchKernelGGL(rdirect ? k_runs<true> : k_runs<false>, dim3((unsigned)lay.n_tiles),
+            TT_LAUNCH(p, "k_runs", s, rdirect ? k_runs<true> : k_runs<false>, dim3((unsigned)lay.n_tiles),
                                dim3(kSortThreads), 0, s, p->at<int32_t>(lay.perm), p->at<int32_t>(lay.skey),
                                p->at<uint64_t>(lay.key_scan), key_start, key_end, run_tiles, L, p->M3, chunk,
                                ctrl, p->at<int32_t>(lay.rid), p->at<int32_t>(lay.run_i3),
@@ -1165,13 +1274,16 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
                                p->at<int32_t>(lay.group_rbase), p->at<int32_t>(lay.chunk_group),
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
                                p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank),
-                               p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN);
+                               p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN, K, lay.NFB,
+                               p->at<uint32_t>(lay.batch_tiles));
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
-        if (lay.NFB > 0) {
-            hipLaunchKernelGGL(k_batches, dim3(grid_for(lay.NFB, 256)), dim3(256), 0, s, p->desc(), T, K,
-                               lay.NFB, kscan, p->at<int32_t>(lay.group_key),
-                               p->at<int32_t>(lay.group_rbase), ctrl, p->at<BatchRec>(lay.batch));
+        if (lay.NFB > 0 && L > 0) {   // (no lookups: the list stays empty, its length 0 from k_init)
+            // the batch list: slots that hold a group, compacted in slot order
+            TT_LAUNCH(p, "k_batches", s, k_batches, dim3((unsigned)((lay.NFB + kSlotTile - 1) / kSlotTile)),
+                      dim3(kSlotTile), 0, s, p->desc(), T, K, lay.NFB, kscan, p->at<int32_t>(lay.group_key),
+                      p->at<int32_t>(lay.group_rbase), ctrl, p->at<uint32_t>(lay.batch_tiles),
+                      p->at<int32_t>(lay.batch_place), p->at<BatchRec>(lay.batch));
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
     }
@@ -1190,6 +1302,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     if (!p) return TT_ERR_INVALID_ARG;
     p->owned_tables = new (std::nothrow) tt_emb_table[T];
     if (!p->owned_tables) { delete p; return TT_ERR_INVALID_ARG; }
+    if (g_timing_default.load()) p->timing = new (std::nothrow) Timing();
     std::memcpy(p->owned_tables, tables, sizeof(tt_emb_table) * (size_t)T);
     const tt_status st = plan_into(p, p->owned_tables, T, indices, offsets, L, B, chunk, workspace,
                                    workspace_bytes, false, (hipStream_t)stream);
@@ -1248,6 +1361,40 @@ extern "C" tt_status tt_emb_query_paths(tt_emb_plan_t p, const float* g1, const 
     info->keeps_prefix = (f && b) ? 1 : 0;
     info->dg3_by_rows = (b && p->nb3 > 0) ? 1 : 0;
     info->workspace_bytes = (uint64_t)p->lay.total;
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_set_timing(tt_emb_plan_t p, int32_t enable) {
+    if (!p) {
+        g_timing_default.store(enable ? 1 : 0);
+        return TT_OK;
+    }
+    if (enable && !p->timing) {
+        p->timing = new (std::nothrow) Timing();
+        if (!p->timing) return TT_ERR_INVALID_ARG;
+    } else if (!enable && p->timing) {
+        timing_free(p->timing);
+        p->timing = nullptr;
+    }
+    return TT_OK;
+}
+
+extern "C" tt_status tt_emb_kernel_times(tt_emb_plan_t p, tt_emb_kernel_time* out, int32_t max,
+                                         int32_t* count, void* stream) {
+    if (!p || !count || (max > 0 && !out) || max < 0) return TT_ERR_INVALID_ARG;
+    *count = 0;
+    Timing* t = p->timing;
+    if (!t) return TT_OK;
+    TT_HIP_CHECK(hipStreamSynchronize((hipStream_t)stream));
+    const int n = std::min<int>(t->n, max);
+    for (int i = 0; i < n; ++i) {
+        float ms = 0.f;
+        TT_HIP_CHECK(hipEventElapsedTime(&ms, t->ev[i][0], t->ev[i][1]));
+        out[i].kernel = t->name[i];
+        out[i].ms = ms;
+    }
+    *count = n;
+    t->n = 0;
     return TT_OK;
 }
 

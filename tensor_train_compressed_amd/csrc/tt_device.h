@@ -60,15 +60,25 @@ struct PrefixBatch {
     static_assert(N1 == 4 && MR % 16 == 0 && N2R % 16 == 0 && R % 4 == 0, "prefix batch shape");
 };
 
-// The record of batch b as one word per lane (lane k holds word k of the
-// BatchRec; lanes past it hold word 0); all zero (ng = 0) for b >= nb.
+// The record of batch b of the list as one word per lane (lane k holds word k
+// of the BatchRec; lanes past it hold word 0); all zero (ng = 0) for b >= nl,
+// the list's length. The address depends only on b and the list's capacity,
+// so the load need not wait for nl (a zero record reads slice 0 only).
 constexpr int kRecWords = (int)(sizeof(BatchRec) / 4);
 static_assert(kRecWords <= 64, "BatchRec fits one wave");
-__device__ __forceinline__ int32_t rec_word(const BatchRec* __restrict__ recs, int64_t b, int64_t nb) {
+__device__ __forceinline__ int32_t rec_word(const BatchRec* __restrict__ recs, int64_t b, int64_t cap, int64_t nl) {
     const int lane = threadIdx.x & 63;
-    const int32_t* w = reinterpret_cast<const int32_t*>(recs + (b < nb ? b : 0));
+    const int32_t* w = reinterpret_cast<const int32_t*>(recs + (b < cap ? b : 0));
     const int32_t x = w[lane < kRecWords ? lane : 0];
-    return b < nb ? x : 0;
+    return b < nl ? x : 0;
+}
+
+// The batch of round r of workgroup w among G persistent workgroups: a snake
+// over the list (r*G + w on even rounds, r*G + G-1-w on odd ones), so that the
+// workgroups given the list's first, heaviest batches get its lighter ones
+// next.
+__device__ __forceinline__ int64_t snake(int64_t r, int64_t w, int64_t G) {
+    return r * G + ((r & 1) ? G - 1 - w : w);
 }
 __device__ __forceinline__ int32_t rec_field(int32_t rw, int k) { return __builtin_amdgcn_readlane(rw, k); }
 __device__ __forceinline__ int64_t rec_field64(int32_t rw, int k) {
@@ -199,21 +209,6 @@ __device__ __forceinline__ void batch_prefix(int32_t rw, const int32_t* __restri
         }
     }
     __syncthreads();
-}
-
-// One batch per workgroup (blockIdx): fetch and prefix. Returns false (for the
-// whole block) when the batch holds no group.
-template <int N1, int N2, int R>
-__device__ __forceinline__ bool batch_begin(const BatchRec* __restrict__ recs, int64_t nb,
-                                            const int32_t* __restrict__ run_i3,
-                                            const float* __restrict__ g1, const float* __restrict__ g2,
-                                            float* sU, int32_t* sRb, int32_t* sI3, BatchCtx& c) {
-    const int32_t rw = rec_word(recs, blockIdx.x, nb);
-    if (rec_field(rw, RW_NG) <= 0) return false;
-    BatchPf<N1, N2, R> f;
-    batch_fetch<N1, N2, R>(rw, run_i3, g1, g2, f);
-    batch_prefix<N1, N2, R>(rw, run_i3, f, sU, sRb, sI3, c);
-    return true;
 }
 
 // Stores the batch's P (in LDS, row gi*NP + p at stride AS) to pbuf in the

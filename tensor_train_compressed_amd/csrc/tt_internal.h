@@ -31,6 +31,7 @@ enum CtrlSlot : int {
     CTRL_NUM_CHUNKS = 2,
     CTRL_NUM_RUNS = 4,    // row runs
     CTRL_NUM_XPIECES = 5, // backward: extra run pieces of the groups split over several waves
+    CTRL_NUM_BATCHES = 6, // forward batches that hold a group (the compacted batch list's length)
     CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
     CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
     CTRL_WORDS = 64
@@ -62,7 +63,12 @@ constexpr int kI3Pad = 32;   // int32 words per i3 counter (one 128-byte line ea
 constexpr int kMaxBatchI3Bytes = 32768;
 
 // One forward batch as the planner describes it to the batch kernels: up to
-// kFwdBatch groups of one (table, i2) slice, consecutive in key order.
+// kFwdBatch groups of one (table, i2) slice, consecutive in key order. Slot j
+// of slice i2 of table t is batch slot fb_base_t + j*m2_t + i2 (layer-major:
+// the first kFwdBatch groups of every slice, then the next ones, ...); the
+// planner keeps the slots that hold a group, in that order, as the batch
+// list (under skew the first layer holds the low i1 and the heaviest groups,
+// so the list starts with its heaviest batches).
 struct alignas(16) BatchRec {
     int32_t ng;                    // groups in the batch (0: nothing to do)
     int32_t g0;                    // first group
@@ -77,6 +83,8 @@ struct alignas(16) BatchRec {
     int32_t pad2[7];
 };
 static_assert(sizeof(BatchRec) == 160, "BatchRec layout");
+
+constexpr int kSlotTile = 256;   // batch slots per workgroup of the planner's batch-list kernel
 
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
@@ -156,7 +164,12 @@ struct Layout {
     size_t run_rank;                         // [L] int32: rank of each run inside its bucket
     size_t run_bkt;                          // [L] int32: bucket (G3 row) of each run
     size_t bucket_runs;                      // [L] int32: backward: the runs of each bucket, in rank order
-    size_t batch;                            // [NFB] BatchRec
+    size_t batch_tiles;                      // [ceil(NFB/kSlotTile)] uint32: slots holding a group per tile
+                                             //     of kSlotTile batch slots
+    size_t batch_place;                      // [NFB] int32: each slot's place in the batch list (-1: none),
+                                             //     indexed slice-major (fb_base + i2*ceil(m1/kFwdBatch) + jb)
+    size_t batch;                            // [NFB] BatchRec: the batches that hold a group,
+                                             //     compacted (CTRL_NUM_BATCHES of them)
     size_t total;
     int64_t n_tiles, hstride, n_ktiles, K, Gmax, Cmax, NFB, scan_tiles, NB3, xcap;
     int passes;
@@ -165,6 +178,17 @@ struct Layout {
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
                    int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3,
                    bool fwd_only);
+
+// Kernel timing of a plan (tt_emb_set_timing): a start and an end event per
+// launch, recorded on the launch's stream, read back by tt_emb_kernel_times.
+struct Timing {
+    static constexpr int kCap = 1024;
+    const char* name[kCap];
+    hipEvent_t ev[kCap][2];
+    int n = 0;         // launches recorded since the last read
+    int created = 0;   // event pairs created so far (slots [0, created))
+};
+void timing_free(Timing* t);
 
 }  // namespace tt
 
@@ -196,8 +220,12 @@ struct tt_emb_plan_s {
     tt::Layout lay;
     const tt_emb_table* tables = nullptr;     // T descriptors (owned_tables, or the caller's
     tt_emb_table* owned_tables = nullptr;     //     array for the length of one call)
+    tt::Timing* timing = nullptr;             // non-null while kernel timing is on
 
-    ~tt_emb_plan_s() { delete[] owned_tables; }
+    ~tt_emb_plan_s() {
+        delete[] owned_tables;
+        tt::timing_free(timing);
+    }
 
     template <class P>
     P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
@@ -244,10 +272,25 @@ tt_status forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const 
 bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
 bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
 
+// Kernel timing hooks around one launch (no-ops unless the plan times its
+// kernels): kt_begin records the start event and returns the record's slot
+// (-1: not recorded), kt_end records the end event.
+int kt_begin(const tt_emb_plan_s* p, const char* name, hipStream_t s);
+void kt_end(const tt_emb_plan_s* p, int slot, hipStream_t s);
+
 inline unsigned grid_for(int64_t n, int threads) {
     int64_t g = (n + threads - 1) / threads;
     return (unsigned)(g < 1 ? 1 : g);
 }
-// Fill `n` 32-bit words at `p` with `v` (stream-ordered, capture-safe).
-tt_status fill32(void* p, uint32_t v, int64_t n, hipStream_t s);
+// Fill `n` 32-bit words at `ptr` with `v` (stream-ordered, capture-safe).
+tt_status fill32(const tt_emb_plan_s* p, void* ptr, uint32_t v, int64_t n, hipStream_t s);
 }  // namespace tt
+
+// A kernel launch on stream `s` for plan `p`, bracketed by the plan's timing
+// events when timing is on.
+#define TT_LAUNCH(p, name, s, ...)                              \
+    do {                                                        \
+        const int _kt_slot = tt::kt_begin((p), (name), (s));    \
+        hipLaunchKernelGGL(__VA_ARGS__);                        \
+        tt::kt_end((p), _kt_slot, (s));                         \
+    } while (0)

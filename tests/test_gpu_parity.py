@@ -540,3 +540,26 @@ def test_backward_hot_slices_full_size():
         assert_close(d[0][:n1 * R], g["dg1_i1_0"], f"hot dG1[i1=0] run {run}")
         assert_close(d[1][:R * n2 * R], g["dg2_i2_0"], f"hot dG2[i2=0] run {run}")
         assert_close(d[2][:R * n3], g["dg3_i3_0"], f"hot dG3[i3=0] run {run}")
+
+
+def test_kernel_timing():
+    """tt_emb_set_timing brackets every launch with events: a forward records
+    the batch and pooling kernels once each, with positive times; a plan made
+    while the process-wide default is on records its planning kernels."""
+    import tensor_train_compressed_amd as tte
+    dp = DevProblem(wl.make("train11m", batch=256), 256)
+    tte.tt_emb_set_timing(None, True)
+    try:
+        pl = tte.tt_emb_plan(dp.tables_c, dp.idx, dp.off, dp.p.batch, 256)
+    finally:
+        tte.tt_emb_set_timing(None, False)
+    names = [k for k, _ in tte.tt_emb_kernel_times(pl)]
+    assert "k_split" in names and "k_batches" in names and "k_radix_scatter" in names
+    out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
+    tte.tt_emb_forward(pl, dp.g1, dp.g2, dp.g3, out)
+    t = tte.tt_emb_kernel_times(pl)
+    assert [k for k, _ in t] == ["k_fwd_batch", "k_pool"] and all(ms > 0 for _, ms in t)
+    tte.tt_emb_set_timing(pl, False)
+    tte.tt_emb_forward(pl, dp.g1, dp.g2, dp.g3, out)
+    assert tte.tt_emb_kernel_times(pl) == []
+    assert_close(out.cpu().numpy(), oracle.forward_problem(dp.p), "forward with timing toggled")
