@@ -6,8 +6,10 @@ TT rank 32, fp32 cores; a batch of 32,768 bags with Poisson(20) lengths
 clipped to [1,100] and unpermuted Zipf(1.1) indices; grad_out ~ N(0,1) and an
 SGD step with lr 0.01. One step is the whole path on one batch: plan (split,
 prefix grouping, chunking, row runs), forward (the training call, which keeps
-each group's prefix product for the backward), backward, SGD, with every
-input already resident in HBM.
+each group's prefix product for the backward), then the backward fused with
+the SGD step (the cores updated in place on the slices the batch touches;
+bit for bit the separate backward and SGD calls, whose times are reported
+too), with every input already resident in HBM.
 
 Prints one JSON line: whole-step pooled bags/s as `value`; per-call times of
 each phase (HIP events around back-to-back calls on the stream the kernels run
@@ -52,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--chunk", type=int, default=256)
-    ap.add_argument("--cpu-bags", type=int, default=6144,
+    ap.add_argument("--cpu-bags", type=int, default=32768,
                     help="bags of the batch the CPU oracle baseline runs on (0: skip)")
     ap.add_argument("--phase-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -118,8 +120,7 @@ def main():
     def step():
         pl = plan()
         tok = tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
-        tte.tt_emb_backward_kept(pl, tok, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2], stream=stream)
-        tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr, stream=stream)
+        tte.tt_emb_backward_sgd(pl, tok, g[0], g[1], g[2], gout, p.lr, stream=stream)
         return pl
 
     for _ in range(args.warmup):
@@ -175,6 +176,20 @@ def main():
     bwd_ms = bwd_after_fwd_train_ms(reps)
     sgd_ms = per_call_ms(lambda: tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr,
                                                 stream=stream), reps)
+
+    # the fused backward + SGD step as the timed step runs it
+    def bwd_sgd_ms(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            tok = tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
+            e0.record(stream)
+            tte.tt_emb_backward_sgd(pl, tok, g[0], g[1], g[2], gout, p.lr, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+
+    bwd_sgd = bwd_sgd_ms(reps)
     torch.cuda.synchronize()
 
     # per-kernel times, measured live: the library brackets every kernel it
@@ -281,7 +296,8 @@ def main():
         "phases_ms_per_call": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4),
                                "forward_train": round(fwd_train_ms, 4),
                                "backward_after_forward_train": round(bwd_ms, 4),
-                               "sgd": round(sgd_ms, 4)},
+                               "sgd": round(sgd_ms, 4),
+                               "backward_sgd_after_forward_train": round(bwd_sgd, 4)},
         "forward_bags_per_s": round(B / (fwd_ms * 1e-3), 1),
         "plan_forward_bags_per_s": round(B / ((plan_ms + fwd_ms) * 1e-3), 1),
         "forward_rows_per_s": round(L / (fwd_ms * 1e-3), 1),

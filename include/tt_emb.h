@@ -165,6 +165,21 @@ tt_status tt_emb_backward_kept(tt_emb_plan_t plan, uint64_t kept_token, const fl
                                const float* g2, const float* g3, const float* grad_out,
                                float* dg1, float* dg2, float* dg3, void* stream);
 
+/* Backward fused with the SGD step: G_k <- G_k - lr * dG_k in place, for
+ * the slices that some lookup of the batch touches (the others are neither
+ * read nor written), without writing the gradients out. The result is bit
+ * for bit that of the backward followed by tt_emb_sgd (untouched slices
+ * have zero gradients, so the plain step leaves them unchanged too).
+ *   kept_token  a token from tt_emb_forward_train to reuse its prefix
+ *               products (rules as for tt_emb_backward_kept), or 0 to form
+ *               them again
+ *   g1, g2, g3  the cores, read and then updated in place
+ * Returns TT_ERR_UNSUPPORTED for plans whose backward takes the generic
+ * kernels (tt_emb_query_paths), TT_ERR_STALE for a token that does not name
+ * the plan's kept products. Ends the validity of any kept token. */
+tt_status tt_emb_backward_sgd(tt_emb_plan_t plan, uint64_t kept_token, float* g1, float* g2,
+                              float* g3, const float* grad_out, float lr, void* stream);
+
 /* SGD step on every core element: G <- G - lr * dG (device buffers). */
 tt_status tt_emb_sgd(tt_emb_plan_t plan, float* g1, float* g2, float* g3, const float* dg1,
                      const float* dg2, const float* dg3, float lr, void* stream);

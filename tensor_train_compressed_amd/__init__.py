@@ -19,7 +19,8 @@ from typing import Optional, Sequence
 __all__ = [
     "TTEmbError", "TTEmbLibraryMissing", "TT_OK", "TT_FLAG_BAD_INDEX", "TT_FLAG_BAD_OFFSETS",
     "library_path", "load_library", "make_tables", "tt_emb_workspace_bytes", "tt_emb_plan",
-    "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
+    "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_backward_sgd",
+    "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
     "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
     "tt_emb_kernel_times", "TT_PATH_MATRIX_CORE",
@@ -39,7 +40,7 @@ TT_FLAG_BAD_OFFSETS = 2
 # Every symbol include/tt_emb.h declares.
 EXPORTS = (
     "tt_emb_workspace_bytes", "tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train",
-    "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_sgd",
+    "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_backward_sgd", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
     "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
     "tt_emb_kernel_times", "tt_emb_status_string",
@@ -107,6 +108,8 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_forward_train.argtypes = [P, P, P, P, P, ctypes.POINTER(ctypes.c_uint64), P]
         lib.tt_emb_backward.argtypes = [P, P, P, P, P, P, P, P, P]
         lib.tt_emb_backward_kept.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, P, P]
+        lib.tt_emb_backward_sgd.argtypes = [P, ctypes.c_uint64, P, P, P, P, ctypes.c_float, P]
+        lib.tt_emb_backward_sgd.restype = ctypes.c_int
         lib.tt_emb_query_paths.argtypes = [P, P, P, ctypes.POINTER(_PathInfo)]
         lib.tt_emb_forward_scratch.argtypes = [P, i32, P, P, i64, i64, i32, P, P, P, P, P]
         lib.tt_emb_forward_scratch.restype = ctypes.c_int
@@ -282,6 +285,16 @@ def tt_emb_backward_kept(plan: Plan, kept_token: int, g1, g2, g3, grad_out, dg1,
         plan.handle, ctypes.c_uint64(int(kept_token)), *plan.cores(g1, g2, g3),
         _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D),
         *plan.cores(dg1, dg2, dg3, ("dg1", "dg2", "dg3")), _stream(stream)), "tt_emb_backward_kept")
+
+
+def tt_emb_backward_sgd(plan: Plan, kept_token: int, g1, g2, g3, grad_out, lr: float, stream=None):
+    """Backward fused with the SGD step: the cores are updated in place on
+    the slices the batch touches (kept_token 0: form the prefix products
+    again)."""
+    _check(load_library().tt_emb_backward_sgd(
+        plan.handle, ctypes.c_uint64(int(kept_token)), *plan.cores(g1, g2, g3),
+        _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D), float(lr), _stream(stream)),
+        "tt_emb_backward_sgd")
 
 
 def tt_emb_sgd(plan: Plan, g1, g2, g3, dg1, dg2, dg3, lr: float, stream=None):

@@ -86,15 +86,37 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     }
 }
 
-// dG1 (and dG3 when n3 > 0) from their fp64 accumulators.
+// Where the backward's gradient elements go: into the gradient buffers, or,
+// for the backward fused with the SGD step, into the cores themselves,
+// G <- G - lr * dG with dG rounded to fp32 first (the same operations as the
+// SGD kernel, so the same bits). The fused form writes only the slices that
+// some lookup touches.
+struct GradOut {
+    float neg_lr;
+    int32_t sgd;
+};
+__device__ __forceinline__ void put_grad(float* p, float g, GradOut o) {
+    if (o.sgd) *p = fmaf(o.neg_lr, g, *p);
+    else *p = g;
+}
+
+// dG1 (and dG3 when n3 > 0) from their fp64 accumulators (fused SGD: an
+// element whose sum is zero, untouched, is left alone).
 __global__ __launch_bounds__(256) void k_bwd_finish(const double* __restrict__ a1, float* __restrict__ dg1,
                                                     int64_t n1, const double* __restrict__ a3,
-                                                    float* __restrict__ dg3, int64_t n3, int32_t* ctrl) {
+                                                    float* __restrict__ dg3, int64_t n3, int32_t* ctrl,
+                                                    GradOut go) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     if (tid == 0) ctrl[CTRL_NUM_XPIECES] = 0;   // the next backward on this plan appends from 0
-    for (int64_t i = tid; i < n1; i += nth) dg1[i] = (float)a1[i];
-    for (int64_t i = tid; i < n3; i += nth) dg3[i] = (float)a3[i];
+    for (int64_t i = tid; i < n1; i += nth) {
+        const double a = a1[i];
+        if (!go.sgd || a != 0.0) put_grad(dg1 + i, (float)a, go);
+    }
+    for (int64_t i = tid; i < n3; i += nth) {
+        const double a = a3[i];
+        if (!go.sgd || a != 0.0) put_grad(dg3 + i, (float)a, go);
+    }
 }
 
 // G_k <- G_k - lr * dG_k for the three cores in one launch (16-byte accesses
@@ -784,12 +806,13 @@ template <int CN>
 __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3start,
                                                   const int32_t* __restrict__ bucket_runs,
                                                   const float* __restrict__ c3, int64_t c3s,
-                                                  float* __restrict__ dg3) {
+                                                  float* __restrict__ dg3, GradOut go) {
     constexpr int PL = CN / 64, WAVES = 16, GB = 16;
     static_assert(CN % 64 == 0, "shape");
     __shared__ double red[WAVES][CN];
     const int32_t row = blockIdx.x;
     const int32_t b = i3start[row], e = i3start[row + 1];
+    if (go.sgd && b == e) return;   // an untouched G3 row keeps its values
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     double acc[PL];
 #pragma unroll
@@ -818,7 +841,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3
         double x = 0.0;
 #pragma unroll
         for (int k = 0; k < WAVES; ++k) x += red[k][t];
-        dg3[(int64_t)row * CN + t] = (float)x;
+        put_grad(dg3 + (int64_t)row * CN + t, (float)x, go);
     }
 }
 
@@ -834,7 +857,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
                                                  const uint64_t* __restrict__ key_scan,
                                                  const int32_t* __restrict__ group_key,
                                                  const float* __restrict__ dpg, const float* __restrict__ g1,
-                                                 float* __restrict__ dg2, int64_t n_i2) {
+                                                 float* __restrict__ dg2, int64_t n_i2, GradOut go) {
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, CT = N2R / 16, UNR = 8;
     static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
@@ -859,6 +882,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
     const int32_t U = ctrl[CTRL_NUM_GROUPS];
     const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
     const int32_t ge = kb + d.m1 < K ? (int32_t)(key_scan[kb + d.m1] >> 32) : U;
+    if (go.sgd && g0 >= ge) return;   // an untouched G2 slice keeps its values
     const float* G1c = g1 + d.o1 + q * R + col;               // + i1*N1*R + 16*rt: G1[i1][j1 = q][r1]
     const float* dPc = dpg + q * N2R + 16 * ct + col;          // + g * PR: dP_g[j1 = q][c]
     // two accumulator sets (even and odd steps of a group pair) keep two
@@ -907,7 +931,8 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) D2[(int64_t)(16 * rt + q + 4 * v) * N2R] = (float)(acc[0][rt][v] + acc[1][rt][v]);
+        for (int v = 0; v < 4; ++v)
+            put_grad(D2 + (int64_t)(16 * rt + q + 4 * v) * N2R, (float)(acc[0][rt][v] + acc[1][rt][v]), go);
 }
 
 // dG1[i1] += dP_g G2[i2]^T, one wave per prefix batch (up to 8 groups of one
@@ -998,15 +1023,19 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
             }
 }
 
+// Fused SGD (go.sgd): dg1/dg2/dg3 are the cores g1/g2/g3 themselves. Every
+// kernel reads the cores it needs before any kernel updates them: the run
+// kernel (G3) precedes k_bwd_dg3, k_bwd_dg1 (G2) precedes k_bwd_dg2, which
+// (G1) precedes k_bwd_finish.
 template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
-                                 float* dg3, bool kept, hipStream_t s) {
+                                 float* dg3, bool kept, GradOut go, hipStream_t s) {
     // dG3 reduced per G3 row from per-run terms (k_bwd_dg3 writes every row
     // of the buffer, gaps included), unless some table's G3 rows are not
     // aligned to R*n3: then device atomics into an fp64 accumulator
     const bool bucket3 = p->nb3 > 0 && p->L > 0;
-    if (!p->packed) {
+    if (!p->packed && !go.sgd) {
         // elements outside every table's slices are zero in the gradients
         tt_status st = fill32(p, dg2, 0u, p->extent[1], s);
         if (st != TT_OK) return st;
@@ -1058,19 +1087,16 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                                c3s);
             TT_LAUNCH_CHECK();
             TT_LAUNCH(p, "k_bwd_dg3", s, (k_bwd_dg3<CN>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
-                               p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3);
+                               p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3,
+                               go);
         } else {
             TT_LAUNCH(p, "k_bwd_runs", s, (k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
         TT_LAUNCH_CHECK();
     }
     {
-        // dP of every group now sits over its P
-        const int64_t w2 = p->n_i2 * (N2 * R / 16);
-        TT_LAUNCH(p, "k_bwd_dg2", s, (k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(), p->T,
-                           p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key),
-                           pbuf, g1, dg2, p->n_i2);
-        TT_LAUNCH_CHECK();
+        // dP of every group now sits over its P; dG1 first: it reads G2,
+        // which the fused SGD updates in k_bwd_dg2
         const int64_t w1 = p->n_fb;
         if (w1 > 0) {
             TT_LAUNCH(p, "k_bwd_dg1", s, (k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
@@ -1078,9 +1104,14 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                                pbuf, g2, acc1);
             TT_LAUNCH_CHECK();
         }
+        const int64_t w2 = p->n_i2 * (N2 * R / 16);
+        TT_LAUNCH(p, "k_bwd_dg2", s, (k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(),
+                  p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key), pbuf, g1,
+                  dg2, p->n_i2, go);
+        TT_LAUNCH_CHECK();
     }
     TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
-                       bucket3 ? 0 : p->extent[2], p->ctrl());
+                       bucket3 ? 0 : p->extent[2], p->ctrl(), go);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }
@@ -1098,9 +1129,10 @@ bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
 }
 
 static tt_status launch_bwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
-                            const float* gout, float* dg1, float* dg2, float* dg3, bool kept, hipStream_t s) {
-    if (p->n2 == 8) return launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, s);
-    return launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, s);
+                            const float* gout, float* dg1, float* dg2, float* dg3, bool kept, GradOut go,
+                            hipStream_t s) {
+    if (p->n2 == 8) return launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
+    return launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
 }
 
 }  // namespace tt
@@ -1113,7 +1145,7 @@ static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2
     hipStream_t s = (hipStream_t)stream;
     // the backward overwrites the kept products (P, then dP over it)
     p->kept_token = 0;
-    if (bwd_mfma_ok(p, g1, g2)) return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, s);
+    if (bwd_mfma_ok(p, g1, g2)) return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, GradOut{0.f, 0}, s);
     tt_status st = TT_OK;
     if ((st = fill32(p, dg1, 0u, p->extent[0], s)) != TT_OK) return st;
     if ((st = fill32(p, dg2, 0u, p->extent[1], s)) != TT_OK) return st;
@@ -1152,6 +1184,17 @@ extern "C" tt_status tt_emb_backward_kept(tt_emb_plan_t p, uint64_t kept_token, 
         !bwd_mfma_ok(p, g1, g2))
         return TT_ERR_STALE;
     return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, true, stream);
+}
+
+extern "C" tt_status tt_emb_backward_sgd(tt_emb_plan_t p, uint64_t kept_token, float* g1, float* g2,
+                                         float* g3, const float* grad_out, float lr, void* stream) {
+    if (!p || !g1 || !g2 || !g3 || (!grad_out && p->TB > 0)) return TT_ERR_INVALID_ARG;
+    if (!bwd_mfma_ok(p, g1, g2)) return TT_ERR_UNSUPPORTED;
+    if (kept_token != 0 && (kept_token != p->kept_token || g1 != p->kept_g1 || g2 != p->kept_g2))
+        return TT_ERR_STALE;
+    const bool kept = kept_token != 0;
+    p->kept_token = 0;   // consumed, and the cores change
+    return launch_bwd(p, g1, g2, g3, grad_out, g1, g2, g3, kept, GradOut{-lr, 1}, (hipStream_t)stream);
 }
 
 extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3,

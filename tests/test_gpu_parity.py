@@ -349,6 +349,10 @@ def test_training_step_full_size():
     say("full training step: oracle forward + backward (about a minute)")
     ref_out = oracle.forward_problem(p)
     ref, ref_sgd = _oracle_backward_sgd(p)
+    # step 0: backward into gradient buffers, then tt_emb_sgd; step 1: the
+    # fused tt_emb_backward_sgd (the benchmark's step), whose updated cores
+    # must equal step 0's bit for bit
+    first = None
     for step in range(2):
         g = [torch.from_numpy(x).to("cuda:0") for x in (p.g1, p.g2, p.g3)]
         d = [torch.empty_like(x) for x in g]
@@ -356,14 +360,24 @@ def test_training_step_full_size():
         pl = tte.tt_emb_plan(dp.tables_c, dp.idx, dp.off, p.batch, 256, workspace=ws)
         tok = tte.tt_emb_forward_train(pl, *g, out)
         assert tok != 0
-        tte.tt_emb_backward_kept(pl, tok, *g, dp.gout, *d)
-        tte.tt_emb_sgd(pl, *g, *d, p.lr)
+        if step == 0:
+            tte.tt_emb_backward_kept(pl, tok, *g, dp.gout, *d)
+            tte.tt_emb_sgd(pl, *g, *d, p.lr)
+        else:
+            tte.tt_emb_backward_sgd(pl, tok, *g, dp.gout, p.lr)
         assert tte.tt_emb_get_error(pl) == 0
         say(f"step {step}: compare")
         assert_close(out.cpu().numpy(), ref_out, f"step {step} forward")
         for k in range(3):
-            assert_close(d[k].cpu().numpy(), ref[k], f"step {step} dG{k + 1}")
+            if step == 0:
+                assert_close(d[k].cpu().numpy(), ref[k], f"step {step} dG{k + 1}")
             assert_close(g[k].cpu().numpy(), ref_sgd[k], f"step {step} SGD core {k + 1}")
+        cores = [x.cpu().numpy() for x in g]
+        if first is None:
+            first = cores
+        else:
+            for k in range(3):
+                np.testing.assert_array_equal(cores[k], first[k], err_msg=f"fused step core {k + 1}")
 
 
 def test_query_paths():
@@ -563,3 +577,55 @@ def test_kernel_timing():
     tte.tt_emb_forward(pl, dp.g1, dp.g2, dp.g3, out)
     assert tte.tt_emb_kernel_times(pl) == []
     assert_close(out.cpu().numpy(), oracle.forward_problem(dp.p), "forward with timing toggled")
+
+
+@pytest.mark.parametrize("case", ["single", "multi6", "shared_g3", "no_lookups", "recompute"])
+def test_backward_sgd_fused(case):
+    """tt_emb_backward_sgd against tt_emb_backward + tt_emb_sgd on the same
+    inputs: the updated cores bit for bit (untouched slices unchanged), and
+    against the oracle's step; with a kept token and (recompute) without."""
+    import tensor_train_compressed_amd as tte
+    if case == "single":
+        p = wl.make("train11m", batch=256)
+    elif case == "recompute":
+        p = wl.make("train11m", batch=300)
+    elif case == "multi6":
+        p = wl.make("multi26", batch=32, tables=6)
+        p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
+        p.lr = 0.01
+    else:
+        t1 = wl.Table(4 * 5 * 300, (4, 5, 300), (4, 8, 4), 32)
+        t2 = wl.Table(3 * 6 * 300, (3, 6, 300), (4, 8, 4), 32)
+        lens = np.full(2 * 60, 7) if case == "shared_g3" else np.zeros(2 * 16, np.int64)
+        p = wl.make_custom([t1, t2], lens, seed=7, zipf_alpha=1.1, with_grad=True)
+        p.g3 = p.g3[:300 * 32 * 4].copy()
+        p.goff = p.goff.copy()
+        p.goff[1, 2] = 0
+    dp = DevProblem(p, 32)
+    dp.make_plan()
+    out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
+    g = [x.clone() for x in (dp.g1, dp.g2, dp.g3)]
+    d = [torch.empty_like(x) for x in g]
+    tok = tte.tt_emb_forward_train(dp.plan, *g, out)
+    if tok:
+        tte.tt_emb_backward_kept(dp.plan, tok, *g, dp.gout, *d)
+    else:   # no lookups: nothing is kept
+        assert p.L == 0
+        tte.tt_emb_backward(dp.plan, *g, dp.gout, *d)
+    tte.tt_emb_sgd(dp.plan, *g, *d, p.lr)
+    want = [x.cpu().numpy() for x in g]
+    f = [x.clone() for x in (dp.g1, dp.g2, dp.g3)]
+    tok = tte.tt_emb_forward_train(dp.plan, *f, out) if case != "recompute" else 0
+    tte.tt_emb_backward_sgd(dp.plan, tok, *f, dp.gout, p.lr)
+    ref, ref_sgd = _oracle_backward_sgd(p)
+    touched = [np.asarray(r) != 0 for r in ref]
+    for k in range(3):
+        got = f[k].cpu().numpy()
+        np.testing.assert_array_equal(got, want[k], err_msg=f"{case}: fused core {k + 1}")
+        assert_close(got, ref_sgd[k], f"{case}: fused core {k + 1} vs oracle")
+        orig = (p.g1, p.g2, p.g3)[k]
+        np.testing.assert_array_equal(got[~touched[k]], orig[~touched[k]], err_msg=f"{case}: untouched {k + 1}")
+    # a stale token is refused before any launch, the cores untouched
+    with pytest.raises(tte.TTEmbError) as ei:
+        tte.tt_emb_backward_sgd(dp.plan, 12345, *f, dp.gout, p.lr)
+    assert ei.value.status == tte.TT_ERR_STALE
