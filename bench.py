@@ -44,8 +44,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3      # MI355X published dense FP32 (matrix cores and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_traffic_skew11m.json")
-FORWARD_SOURCES = ("forward.hip", "tt_device.h", "tt_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic_skew11m.json")
+CSRC = os.path.join(ROOT, "tensor_train_compressed_amd", "csrc")
 
 
 def parse():
@@ -62,25 +62,26 @@ def parse():
     return ap.parse_args()
 
 
-def forward_source_hash() -> str:
+def kernel_source_hash() -> str:
+    """sha256 prefix over every kernel source file (sorted by name)."""
     h = hashlib.sha256()
-    for f in FORWARD_SOURCES:
-        with open(os.path.join(ROOT, "tensor_train_compressed_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def forward_traffic():
-    """HBM bytes per forward call from the committed counter passes, or None
-    when the forward kernels changed since they were taken."""
+def kernel_traffic():
+    """HBM bytes per launch of each kernel from the committed counter passes,
+    or {} when the kernel sources changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
-        return None
-    if rec.get("source_hash") != forward_source_hash():
-        return None
-    return rec.get("bytes_per_call")
+        return {}
+    if rec.get("source_hash") != kernel_source_hash():
+        return {}
+    return {k: v["fetch_bytes"] + v["write_bytes"] for k, v in rec.get("kernels", {}).items()}
 
 
 def main():
@@ -236,6 +237,9 @@ def main():
         f32, f64, by = work.get(name, (0, 0, 0))
         sec = rec["us"] * 1e-6
         out_ = {"kernel": name, "us": round(rec["us"], 2), "launches_per_call": rec["per_call"]}
+        tb = traffic_of(name)
+        if tb is not None:
+            out_["traffic"] = tb
         if f32 or f64:
             out_["fp32_tflops"] = round(f32 / sec / 1e12, 2)
             out_["fp64_tflops"] = round(f64 / sec / 1e12, 2)
@@ -254,7 +258,24 @@ def main():
     fwd_flop_per_lookup = pre + L * (2 * n1 * n2 * n3 * R + D)
     core_bytes = 4 * core_elems
     fwd_bytes = 8 * L + 8 * (B + 1) + core_bytes + 4 * B * D
-    traffic = forward_traffic()
+    traffic_by_kernel = kernel_traffic()
+
+    def traffic_of(name):
+        """Counter bytes of the kernel a timing record names (the training
+        forward's batch kernel is the KEEP instantiation)."""
+        for k, v in traffic_by_kernel.items():
+            base = k.split("<")[0]
+            if name == "k_fwd_batch_keep":
+                if base == "k_fwd_batch" and k.rstrip(">").endswith("true"):
+                    return v
+            elif name == "k_fwd_batch":
+                if base == "k_fwd_batch" and k.rstrip(">").endswith("false"):
+                    return v
+            elif base == name:
+                return v
+        return None
+
+    traffic = traffic_of("k_fwd_batch")
     step_rows = sorted((kernel_roofline(k, v) for k, v in step_kernels.items()),
                        key=lambda r: -r["us"] * r["launches_per_call"])
     step_kernel_ms = sum(r["us"] * r["launches_per_call"] for r in step_rows) * 1e-3

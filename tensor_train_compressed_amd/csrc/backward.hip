@@ -551,14 +551,14 @@ __global__ __launch_bounds__(256) void k_bwd_pfx(const BatchRec* __restrict__ re
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];
-    const int64_t G = gridDim.x, w = blockIdx.x;
-    const int64_t nl = ctrl[CTRL_NUM_BATCHES];
-    int32_t rwA = rec_word(recs, snake(0, w, G), cap, nl);
-    int32_t rwB = rec_word(recs, snake(1, w, G), cap, nl);
+    const BatchWalk bw = batch_walk(ctrl);
+    const int64_t end = bw.base + bw.n;
+    int32_t rwA = rec_word(recs, bw.at(0), cap, end);
+    int32_t rwB = rec_word(recs, bw.at(1), cap, end);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, run_i3, g1, g2, f);
-    for (int64_t r = 0; snake(r, w, G) < nl; ++r) {
-        const int32_t rwC = rec_word(recs, snake(r + 2, w, G), cap, nl);
+    for (int64_t r = 0; bw.has(r); ++r) {
+        const int32_t rwC = rec_word(recs, bw.at(r + 2), cap, end);
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) batch_prefix<N1, N2, R>(rwA, run_i3, f, sU, sRb, sI3, c);
@@ -644,50 +644,59 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     };
     int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (k >= nunits) return;
+    auto o3_of = [&](int64_t g) { return a.desc[find_table(a.desc, a.T, a.group_key[g])].o3; };
+    // a tile's operands (S rows in both layouts, G3 rows of its runs) for the
+    // runs t0 .. t0+3 of the walked range [s, e) (i3w: lane j holds the i3 of
+    // run s + j; lanes past e read run t0 or e - 1, whose results go unused)
+    struct TileOps {
+        floatx4 av[MT], bq[RT];
+        float bv[KSP];
+        int32_t i3q;
+    };
+    auto load_tile = [&](int32_t t0, int32_t s, int32_t e, int32_t i3w, int64_t o3, TileOps& o) {
+        const int32_t rq = t0 + q < e ? t0 + q : t0;
+        o.i3q = __shfl(i3w, rq - s);
+        const float* Sq = a.S + (int64_t)rq * D;
+        const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o.av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
+#pragma unroll
+        for (int nt = 0; nt < RT; ++nt) o.bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
+        const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
+#pragma unroll
+        for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = Sl[(4 * s2 + q) * N3];
+    };
     Words cur;
-    int32_t i3l;   // lane j: i3 of run s + j of the runs being walked
     words_of(k, cur);
-    i3l = a.run_i3[min(cur.s + lane, cur.e - 1)];
+    int64_t o3 = o3_of(cur.g);
+    int32_t i3l = a.run_i3[min(cur.s + lane, cur.e - 1)];   // lane j: i3 of run s + j
     for (; k < nunits; k += nw) {
+        const int64_t g = cur.g;
+        const bool work = cur.mode != 0;
+        // this unit's P and first tile go out first; the next unit's words,
+        // G3 offset and run i3 values are fetched while they are in flight
+        floatx4 preg[RT][KQ];
+        TileOps TA, TB;
+        if (work) {
+            const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
+            load_tile(cur.s, cur.s, min(cur.e, cur.s + W), i3l, o3, TA);
+        }
         Words nxt;
         words_of(min(k + nw, nunits - 1), nxt);
-        const int64_t g = cur.g;
-        if (cur.mode != 0) {
-        // P: its address needs only g
-        floatx4 preg[RT][KQ];
-        const floatx4* Pp = reinterpret_cast<const floatx4*>(a.pbuf + g * PR) + 16 * q + col;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
-        const int64_t o3 = a.desc[find_table(a.desc, a.T, a.group_key[g])].o3;
+        const int64_t o3n = o3_of(nxt.g);
+        const int32_t i3n = a.run_i3[min(nxt.s + lane, nxt.e - 1)];
+        if (work) {
         doublex4 dacc[MT][RT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < RT; ++nt) dacc[mt][nt] = doublex4{0.0, 0.0, 0.0, 0.0};
-        // a tile's operands (S rows in both layouts, G3 rows of its runs) are
-        // loaded one tile ahead, before the current tile's products and stores
-        struct TileOps {
-            floatx4 av[MT], bq[RT];
-            float bv[KSP];
-            int32_t i3q;
-        };
         for (int32_t s = cur.s;;) {
         const int32_t e = min(cur.e, s + W);
-        auto load_tile = [&](int32_t t0, TileOps& o) {
-            const int32_t rq = t0 + q < e ? t0 + q : t0;
-            o.i3q = __shfl(i3l, rq - s);
-            const float* Sq = a.S + (int64_t)rq * D;
-            const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) o.av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
-#pragma unroll
-            for (int nt = 0; nt < RT; ++nt) o.bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
-            const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
-#pragma unroll
-            for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = Sl[(4 * s2 + q) * N3];
-        };
         auto tile = [&](int32_t t0, TileOps& o) {
             const bool okq = t0 + q < e;
             // dG3: rows (run t0 + lk, j3) of P^T S; lane (col, q) gets run
@@ -714,19 +723,19 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
                                                                             dacc[mt][nt], 0, 0, 0);
             }
         };
-        TileOps TA, TB;
-        load_tile(s, TA);
         for (int32_t t0 = s;; t0 += 8) {
-            load_tile(min(t0 + 4, e - 1), TB);
+            load_tile(min(t0 + 4, e - 1), s, e, i3l, o3, TB);
             tile(t0, TA);
             if (t0 + 4 >= e) break;
-            load_tile(min(t0 + 8, e - 1), TA);
+            load_tile(min(t0 + 8, e - 1), s, e, i3l, o3, TA);
             tile(t0 + 4, TB);
             if (t0 + 8 >= e) break;
         }
         s = e;
         if (s >= cur.e) break;
-        i3l = a.run_i3[min(s + lane, cur.e - 1)];   // a whole group's next kRunRange runs
+        // a whole group's next kRunRange runs
+        i3l = a.run_i3[min(s + lane, cur.e - 1)];
+        load_tile(s, s, min(cur.e, s + W), i3l, o3, TA);
         }
         // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col];
         // a listed piece keeps its fp64 partial in its own slot
@@ -770,7 +779,8 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             }
         }
         }
-        i3l = a.run_i3[min(nxt.s + lane, nxt.e - 1)];
+        i3l = i3n;
+        o3 = o3n;
         cur = nxt;
     }
 }
@@ -1070,7 +1080,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         TT_LAUNCH_CHECK();
         if (!kept) {
             const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
-            const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
+            const int64_t grid = batch_grid(p->n_fb, kFwdPersistBlocks);
             TT_LAUNCH(p, "k_bwd_pfx", s, (k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
             TT_LAUNCH_CHECK();

@@ -202,10 +202,10 @@ struct FwdTiles {
     }
 };
 
-// Persistent workgroups (a few per CU) walk the planner's batch list in a
-// snake (round r: batch snake(r, blockIdx.x, gridDim.x)); the list holds only
-// batches with groups and starts with the heaviest, so every workgroup gets
-// four or five batches of mixed weight. While a workgroup runs the tiles of
+// Persistent workgroups (a few per CU) walk the planner's batch list, each the
+// part of its XCD class in a snake over that class's workgroups (batch_walk);
+// the list holds only batches with groups and each part starts with its
+// heaviest, so every workgroup gets four or five batches of mixed weight. While a workgroup runs the tiles of
 // one batch, the loads of its next batch (G2 slice, G1 rows, run i3 list)
 // are in flight, and the records of the next two batches are already in
 // registers, so a batch's prologue costs no exposed memory round trip.
@@ -218,15 +218,15 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, co
     __shared__ int32_t sRb[SG + 1];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
-    const int64_t G = gridDim.x, w = blockIdx.x;
-    const int64_t nl = ctrl[CTRL_NUM_BATCHES];
-    int32_t rwA = rec_word(a.recs, snake(0, w, G), cap, nl);
-    int32_t rwB = rec_word(a.recs, snake(1, w, G), cap, nl);
+    const BatchWalk bw = batch_walk(ctrl);
+    const int64_t end = bw.base + bw.n;
+    int32_t rwA = rec_word(a.recs, bw.at(0), cap, end);
+    int32_t rwB = rec_word(a.recs, bw.at(1), cap, end);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, a.run_i3, a.g1, a.g2, f);
     FwdTiles<N1, N2, R, N3> tl;
-    for (int64_t r = 0; snake(r, w, G) < nl; ++r) {
-        const int32_t rwC = rec_word(a.recs, snake(r + 2, w, G), cap, nl);
+    for (int64_t r = 0; bw.has(r); ++r) {
+        const int32_t rwC = rec_word(a.recs, bw.at(r + 2), cap, end);
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) {
@@ -297,7 +297,7 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
               p->at<float>(p->lay.stage), p->L, keep ? p->at<float>(p->lay.pbuf) : nullptr};
     if (p->L > 0 && p->n_fb > 0) {
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
-        const int64_t grid = std::min<int64_t>(p->n_fb, kFwdPersistBlocks);
+        const int64_t grid = batch_grid(p->n_fb, kFwdPersistBlocks);
         if (keep)
             TT_LAUNCH(p, "k_fwd_batch_keep", s, (k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
                                dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());

@@ -124,7 +124,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_bkt = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.bucket_runs = take(NB3 > 0 ? sizeof(int32_t) * (size_t)L : 0);
     y.NFB = NFB;
-    y.batch_tiles = take(sizeof(uint32_t) * (size_t)((NFB + kSlotTile - 1) / kSlotTile));
+    y.batch_tiles = take(sizeof(uint32_t) * kXcds * (size_t)((NFB + kSlotTile - 1) / kSlotTile));
     y.batch_place = take(sizeof(int32_t) * (size_t)NFB);
     y.batch = take(sizeof(BatchRec) * (size_t)NFB);
     y.total = off;
@@ -819,6 +819,7 @@ __device__ __forceinline__ int32_t bucket3(const TabDev* __restrict__ desc, int3
 struct SlotOf {
     TabDev d;
     int32_t i2, jb, gs0, gs1;
+    int32_t cls;   // XCD class: the slice's global index mod kXcds
     int64_t kb;
 };
 __device__ __forceinline__ SlotOf slot_of(const TabDev* __restrict__ desc, int32_t T, int64_t K, int64_t b,
@@ -836,6 +837,7 @@ __device__ __forceinline__ SlotOf slot_of(const TabDev* __restrict__ desc, int32
     const int64_t ke = o.kb + o.d.m1;
     o.gs0 = (int32_t)(key_scan[o.kb] >> 32);
     o.gs1 = ke < K ? (int32_t)(key_scan[ke] >> 32) : ctrl[CTRL_NUM_GROUPS];
+    o.cls = (o.d.i2_base + o.i2) % kXcds;
     return o;
 }
 
@@ -932,41 +934,39 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
             r += hr[j];
         }
     }
-    // forward batch slots holding a group, per tile of kSlotTile slots (the
-    // group tables are complete: k_groups ran before); kSortThreads slots per
-    // round, each tile's count added up over its waves in LDS
-    constexpr int TPR = kSortThreads / kSlotTile, WPT = kSlotTile / 64;
-    static_assert(kSortThreads % kSlotTile == 0 && kSlotTile % 64 == 0, "slot tiles");
-    __shared__ uint32_t wcnt[kSortWaves];
+    // forward batch slots holding a group, per tile of kSlotTile slots and
+    // XCD class (the group tables are complete: k_groups ran before);
+    // kSortThreads slots per round, counted in LDS
+    constexpr int TPR = kSortThreads / kSlotTile;
+    static_assert(kSortThreads % kSlotTile == 0, "slot tiles");
+    __shared__ uint32_t ccnt[TPR][kXcds];
     const int64_t nst = (NFB + kSlotTile - 1) / kSlotTile;
     for (int64_t jt0 = (int64_t)blockIdx.x * TPR; jt0 < nst; jt0 += (int64_t)gridDim.x * TPR) {
+        if (threadIdx.x < TPR * kXcds) ccnt[threadIdx.x / kXcds][threadIdx.x % kXcds] = 0u;
+        __syncthreads();
         const int64_t b = jt0 * kSlotTile + threadIdx.x;
-        bool live = false;
         if (b < NFB) {
             const SlotOf o = slot_of(desc, T, K, b, key_scan, ctrl);
-            live = o.gs1 - (o.gs0 + kFwdBatch * o.jb) > 0;
+            if (o.gs1 - (o.gs0 + kFwdBatch * o.jb) > 0) atomicAdd(&ccnt[threadIdx.x / kSlotTile][o.cls], 1u);
         }
-        const uint64_t m = __ballot(live);
-        if ((threadIdx.x & 63) == 0) wcnt[threadIdx.x >> 6] = (uint32_t)__popcll(m);
         __syncthreads();
-        if (threadIdx.x < TPR && jt0 + threadIdx.x < nst) {
-            uint32_t c = 0;
-            for (int w = 0; w < WPT; ++w) c += wcnt[threadIdx.x * WPT + w];
-            batch_tiles[jt0 + threadIdx.x] = c;
-        }
-        __syncthreads();   // wcnt is reused by the next round
+        if (threadIdx.x < TPR * kXcds && jt0 + threadIdx.x / kXcds < nst)
+            batch_tiles[(jt0 + threadIdx.x / kXcds) * kXcds + threadIdx.x % kXcds] =
+                ccnt[threadIdx.x / kXcds][threadIdx.x % kXcds];
+        __syncthreads();   // ccnt is reused by the next round
     }
 }
 
 // One workgroup per tile of kSlotTile batch slots, one slot per thread: the
 // record of a slot that holds a group (the jb-th run of kFwdBatch groups
 // among its slice's groups, consecutive in key order), written at the slot's
-// place in the batch list: the slots holding a group in earlier tiles (the
-// workgroup adds up k_runs' per-tile counts itself) plus those before it in
-// the tile. The record's loads are issued before the counts are added up.
-// Every slot's place (-1: no group) goes to `place`, indexed slice-major
-// (fb_base + i2*ceil(m1/kFwdBatch) + jb); the last tile writes the list's
-// length.
+// place in the batch list: its class's part starts after the parts of the
+// lower classes, and inside it come the class's slots holding a group in
+// earlier tiles and then those before it in the tile (the workgroup adds up
+// k_runs' per-tile, per-class counts itself). The record's loads are issued
+// first. Every slot's place (-1: no group) goes to `place`, indexed
+// slice-major (fb_base + i2*ceil(m1/kFwdBatch) + jb); workgroup 0 writes the
+// parts' starts and the list's length.
 __global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict__ desc, int32_t T, int64_t K,
                                                        int64_t NFB, const uint64_t* __restrict__ key_scan,
                                                        const int32_t* __restrict__ group_key,
@@ -975,9 +975,11 @@ __global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict_
                                                        const uint32_t* __restrict__ batch_tiles,
                                                        int32_t* __restrict__ place,
                                                        BatchRec* __restrict__ rec) {
-    __shared__ uint32_t wsum[17];   // (block_exclusive_scan's per-wave sums)
+    __shared__ uint32_t sbase[kXcds], stot[kXcds];
+    __shared__ uint32_t wc[kSlotTile / 64][kXcds];
     const int64_t jt = blockIdx.x;
     const int64_t b = jt * kSlotTile + threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     BatchRec r;
     memset(&r, 0, sizeof(r));
     SlotOf o{};
@@ -997,20 +999,43 @@ __global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict_
             r.rbase[kFwdBatch] = r.nr;
         }
     }
-    uint32_t base = 0;
-    for (int64_t j0 = 0; j0 < jt; j0 += kSlotTile) {
-        const uint32_t v = j0 + threadIdx.x < jt ? batch_tiles[j0 + threadIdx.x] : 0u;
-        uint32_t tot;
-        (void)block_exclusive_scan<uint32_t>(v, wsum, &tot);   // synchronises
-        base += tot;
+    if (threadIdx.x < kXcds) { sbase[threadIdx.x] = 0u; stot[threadIdx.x] = 0u; }
+    __syncthreads();
+    // per class: the counts of the earlier tiles, and the total of all tiles
+    const int64_t nst = (NFB + kSlotTile - 1) / kSlotTile;
+    for (int64_t i = threadIdx.x; i < nst * kXcds; i += kSlotTile) {
+        const uint32_t c = batch_tiles[i];
+        if (c) {
+            atomicAdd(&stot[i % kXcds], c);
+            if (i / kXcds < jt) atomicAdd(&sbase[i % kXcds], c);
+        }
     }
-    uint32_t tot;
-    const uint32_t pos = base + block_exclusive_scan<uint32_t>(r.ng > 0 ? 1u : 0u, wsum, &tot);
-    if (jt == (NFB - 1) / kSlotTile && threadIdx.x == 0) ctrl[CTRL_NUM_BATCHES] = (int32_t)(base + tot);
-    if (b >= NFB) return;
-    const int64_t nb1 = (o.d.m1 + kFwdBatch - 1) / kFwdBatch;
-    place[o.d.fb_base + (int64_t)o.i2 * nb1 + o.jb] = r.ng > 0 ? (int32_t)pos : -1;
-    if (r.ng > 0) rec[pos] = r;
+    // rank of the slot among the tile's slots of its class that hold a group
+    const bool live = r.ng > 0;
+    uint32_t rank = 0;
+#pragma unroll
+    for (int c = 0; c < kXcds; ++c) {
+        const uint64_t m = __ballot(live && o.cls == c);
+        if (lane == 0) wc[w][c] = (uint32_t)__popcll(m);
+        if (live && o.cls == c) rank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    }
+    __syncthreads();
+    if (live) {
+        for (int ww = 0; ww < w; ++ww) rank += wc[ww][o.cls];
+        uint32_t start = 0;
+        for (int c = 0; c < o.cls; ++c) start += stot[c];
+        const uint32_t pos = start + sbase[o.cls] + rank;
+        rec[pos] = r;
+        place[o.d.fb_base + (int64_t)o.i2 * ((o.d.m1 + kFwdBatch - 1) / kFwdBatch) + o.jb] = (int32_t)pos;
+    } else if (b < NFB) {
+        place[o.d.fb_base + (int64_t)o.i2 * ((o.d.m1 + kFwdBatch - 1) / kFwdBatch) + o.jb] = -1;
+    }
+    if (jt == 0 && threadIdx.x <= kXcds) {
+        uint32_t start = 0;
+        for (int c = 0; c < (int)threadIdx.x; ++c) start += stot[c];
+        ctrl[CTRL_CLASS_BASE + threadIdx.x] = (int32_t)start;   // the last one: the list's length
+        if (threadIdx.x == kXcds) ctrl[CTRL_NUM_BATCHES] = (int32_t)start;
+    }
 }
 
 }  // namespace tt

@@ -80,6 +80,43 @@ __device__ __forceinline__ int32_t rec_word(const BatchRec* __restrict__ recs, i
 __device__ __forceinline__ int64_t snake(int64_t r, int64_t w, int64_t G) {
     return r * G + ((r & 1) ? G - 1 - w : w);
 }
+
+// The part of the batch list a persistent workgroup walks, and its place
+// among the workgroups walking it. When the list's XCD-class parts are about
+// equal (and the grid is a multiple of kXcds), workgroup w walks the part of
+// its own class, w mod kXcds (it runs on that XCD, whose L2 then holds that
+// class's G2 slices), in a snake over that class's workgroups; otherwise (a
+// few slices hold most batches) the whole list, in a snake over all.
+struct BatchWalk {
+    int64_t base, n, wi, G;
+    __device__ __forceinline__ int64_t at(int64_t r) const { return base + snake(r, wi, G); }
+    __device__ __forceinline__ bool has(int64_t r) const { return snake(r, wi, G) < n; }
+};
+__device__ __forceinline__ BatchWalk batch_walk(const int32_t* __restrict__ ctrl) {
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    int32_t cb[kXcds + 1];
+#pragma unroll
+    for (int c = 0; c <= kXcds; ++c) cb[c] = ctrl[CTRL_CLASS_BASE + c];
+    const int64_t nl = cb[kXcds];
+    int64_t mx = 0;
+#pragma unroll
+    for (int c = 0; c < kXcds; ++c) mx = max(mx, (int64_t)(cb[c + 1] - cb[c]));
+    BatchWalk bw{0, nl, w, G};
+    if (G % kXcds == 0 && mx * kXcds <= nl + nl / 4 + 4 * kXcds) {
+        const int c = (int)(w % kXcds);
+        bw.base = cb[c];
+        bw.n = cb[c + 1] - cb[c];
+        bw.wi = w / kXcds;
+        bw.G = G / kXcds;
+    }
+    return bw;
+}
+
+// Persistent grid of a batch kernel: a multiple of kXcds, at most `cap`.
+inline unsigned batch_grid(int64_t slots, int64_t cap) {
+    const int64_t g = std::min<int64_t>(cap, (slots + kXcds - 1) / kXcds * kXcds);
+    return (unsigned)std::max<int64_t>(g, kXcds);
+}
 __device__ __forceinline__ int32_t rec_field(int32_t rw, int k) { return __builtin_amdgcn_readlane(rw, k); }
 __device__ __forceinline__ int64_t rec_field64(int32_t rw, int k) {
     return (int64_t)(uint32_t)__builtin_amdgcn_readlane(rw, k) |

@@ -32,7 +32,9 @@ enum CtrlSlot : int {
     CTRL_NUM_RUNS = 4,    // row runs
     CTRL_NUM_XPIECES = 5, // backward: extra run pieces of the groups split over several waves
     CTRL_NUM_BATCHES = 6, // forward batches that hold a group (the compacted batch list's length)
-    CTRL_SCAN_CTR = 16,   // tile counters of the single-pass scans, one per scan of a plan
+    CTRL_CLASS_BASE = 8,  // 8 words: start of each XCD class's part of the batch list (class c:
+                          //     slices with global index = c mod 8); the list's length after them
+    CTRL_SCAN_CTR = 24,   // tile counters of the single-pass scans, one per scan of a plan
     CTRL_SCAN_MAX = 16,   //   (at most this many scans per plan)
     CTRL_WORDS = 64
 };
@@ -65,10 +67,13 @@ constexpr int kMaxBatchI3Bytes = 32768;
 // One forward batch as the planner describes it to the batch kernels: up to
 // kFwdBatch groups of one (table, i2) slice, consecutive in key order. Slot j
 // of slice i2 of table t is batch slot fb_base_t + j*m2_t + i2 (layer-major:
-// the first kFwdBatch groups of every slice, then the next ones, ...); the
-// planner keeps the slots that hold a group, in that order, as the batch
-// list (under skew the first layer holds the low i1 and the heaviest groups,
-// so the list starts with its heaviest batches).
+// the first kFwdBatch groups of every slice, then the next ones, ...). The
+// planner keeps the slots that hold a group as the batch list, in 8 parts by
+// XCD class (the slice's global index mod 8), each part in slot order (under
+// skew the first layer holds the low i1 and the heaviest groups, so each
+// part starts with its heaviest batches). Workgroups run on XCD blockIdx mod
+// 8, so a workgroup that walks the part of its own class reads the G2 slices
+// that its XCD's L2 already holds.
 struct alignas(16) BatchRec {
     int32_t ng;                    // groups in the batch (0: nothing to do)
     int32_t g0;                    // first group
@@ -164,8 +169,8 @@ struct Layout {
     size_t run_rank;                         // [L] int32: rank of each run inside its bucket
     size_t run_bkt;                          // [L] int32: bucket (G3 row) of each run
     size_t bucket_runs;                      // [L] int32: backward: the runs of each bucket, in rank order
-    size_t batch_tiles;                      // [ceil(NFB/kSlotTile)] uint32: slots holding a group per tile
-                                             //     of kSlotTile batch slots
+    size_t batch_tiles;                      // [ceil(NFB/kSlotTile)][kXcds] uint32: slots holding a group
+                                             //     per tile of kSlotTile batch slots and XCD class
     size_t batch_place;                      // [NFB] int32: each slot's place in the batch list (-1: none),
                                              //     indexed slice-major (fb_base + i2*ceil(m1/kFwdBatch) + jb)
     size_t batch;                            // [NFB] BatchRec: the batches that hold a group,
