@@ -213,6 +213,7 @@ struct PrepArgs {
     int64_t n3;
     int32_t* xcnt;
     int64_t nwin;
+    int32_t* claims;
     const int32_t* i3cnt;
     int32_t m3;
     int32_t* i3start;
@@ -275,6 +276,7 @@ __device__ __forceinline__ void bwd_prep(const PrepArgs& pa, int64_t blk) {
     for (int64_t i = tid; i < n1; i += nth) dg1[i] = 0.0;
     for (int64_t i = tid; i < n3; i += nth) dg3[i] = 0.0;
     for (int64_t i = tid; i < nwin; i += nth) pa.xcnt[i] = 0;
+    if (tid < kRunCounters) pa.claims[tid * 32] = 0;
     // groups of more than kRunRange runs are split into pieces of kRunRange
     // runs: list their pieces, a group's pieces together and in order (the
     // run kernel takes these first, then one piece per other group)
@@ -593,9 +595,18 @@ struct RunsArgs {
     double* dg3;
     double* dpart;
     int32_t* gdone;            // per group: pieces finished (zeroed by bwd_prep); -1: not listed
+    int32_t* claims;           // [kRunCounters][32]: unit counters (zeroed by bwd_prep)
 };
 
-// One wave per unit (persistent, static stride), the group's P in registers;
+// One wave per unit, the group's P in registers. Persistent waves claim their
+// units: the waves of workgroup b from counter c = b mod kRunCounters, whose
+// j-th claim is unit j*kRunCounters + c (the list's order inside each
+// counter's share: listed pieces, the largest work, first). A wave claims its
+// next unit when it starts the current one, so the claim's round trip hides
+// behind the unit's work. A fixed stride over the units left the last wave
+// ending 29% after the median one; the claims spread over kRunCounters
+// addresses keep each counter's serialised atomics well inside the kernel's
+// run time.
 // four runs at a time (lane group q takes run t0 + q):
 //   dG3[i3] += P^T S          fp32 products over p, handed to add3 (device
 //                              atomics, or the run's own row, reduced later)
@@ -616,7 +627,10 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     const int32_t U = a.ctrl[CTRL_NUM_GROUPS];
     const int32_t X = (int32_t)min((int64_t)a.ctrl[CTRL_NUM_XPIECES], a.xcap);
     const int64_t nunits = (int64_t)X + U;
-    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int cidx = (int)(blockIdx.x % kRunCounters);
+    int32_t* ctr = a.claims + cidx * 32;
+    auto claim_issue = [&]() { int32_t v = 0; if (lane == 0) v = atomicAdd(ctr, 1); return v; };
+    auto claim_unit = [&](int32_t v) { return (int64_t)__builtin_amdgcn_readfirstlane(v) * kRunCounters + cidx; };
     // A unit's words (group, mode, runs) and, per lane j, the i3 of its run
     // s + j are fetched during the unit before it: the words at that unit's
     // start, the run i3 values after its tiles.
@@ -642,8 +656,9 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         w.s = mode == 1 ? gs + W * part : gs;
         w.e = mode == 1 ? min(ge, w.s + W) : ge;
     };
-    int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t k = claim_unit(claim_issue());
     if (k >= nunits) return;
+    int32_t kn_raw = claim_issue();   // the next unit's claim, read at the next unit
     auto o3_of = [&](int64_t g) { return a.desc[find_table(a.desc, a.T, a.group_key[g])].o3; };
     // a tile's operands (S rows in both layouts, G3 rows of its runs) for the
     // runs t0 .. t0+3 of the walked range [s, e) (i3w: lane j holds the i3 of
@@ -670,7 +685,9 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     words_of(k, cur);
     int64_t o3 = o3_of(cur.g);
     int32_t i3l = a.run_i3[min(cur.s + lane, cur.e - 1)];   // lane j: i3 of run s + j
-    for (; k < nunits; k += nw) {
+    for (;;) {
+        const int64_t kn = claim_unit(kn_raw);
+        kn_raw = claim_issue();
         const int64_t g = cur.g;
         const bool work = cur.mode != 0;
         // this unit's P and first tile go out first; the next unit's words,
@@ -686,7 +703,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             load_tile(cur.s, cur.s, min(cur.e, cur.s + W), i3l, o3, TA);
         }
         Words nxt;
-        words_of(min(k + nw, nunits - 1), nxt);
+        words_of(min(kn, nunits - 1), nxt);
         const int64_t o3n = o3_of(nxt.g);
         const int32_t i3n = a.run_i3[min(nxt.s + lane, nxt.e - 1)];
         if (work) {
@@ -779,9 +796,11 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             }
         }
         }
+        if (kn >= nunits) break;
         i3l = i3n;
         o3 = o3n;
         cur = nxt;
+        k = kn;
     }
 }
 
@@ -1061,9 +1080,11 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     const int64_t nwin = (p->L + kWin - 1) / kWin;
     // set-up (first kPrepBlocks workgroups) and the grad-row sums in one launch
     const PrepArgs pa{acc1, p->extent[0], acc3, bucket3 ? 0 : p->extent[2], p->at<int32_t>(p->lay.xcnt), nwin,
+                      p->at<int32_t>(p->lay.claims),
                       p->at<int32_t>(p->lay.i3cnt), bucket3 ? p->nb3 : 0, p->at<int32_t>(p->lay.i3start),
                       p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                       p->at<int32_t>(p->lay.gdone), p->ctrl()};
+    static_assert(kPrepBlocks * 256 >= kRunCounters, "prep zeroes the counters");
     const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                      p->at<int32_t>(p->lay.run_start), p->L, gout, S, xpart};
     TT_LAUNCH(p, "k_bwd_sum", s, k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
@@ -1088,7 +1109,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), S, pbuf, g3, acc3, p->at<double>(p->lay.dpart),
-                    p->at<int32_t>(p->lay.gdone)};
+                    p->at<int32_t>(p->lay.gdone), p->at<int32_t>(p->lay.claims)};
         if (bucket3) {
             // each run's dG3 term over its own S row when the row holds it
             float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);

@@ -71,15 +71,37 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 // input order and writes the bag's output row: no atomics, and the same bits
 // on every run.
 
+// Every table's G3 slices transposed to [n3][R] (g3t, same packing as G3),
+// so that a tile lane's suffix operand, eight consecutive r2 of one j3, is two
+// 16-byte loads instead of eight 4-byte loads 16 bytes apart. One thread per
+// G3 element the tables use (tables sharing a G3 write the same values).
+__global__ __launch_bounds__(256) void k_g3t(const TabDev* __restrict__ desc, int32_t T, int64_t n,
+                                             const float* __restrict__ g3, float* __restrict__ g3t) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    int lo = 0, hi = T;   // last table with g3_base <= e
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (desc[mid].g3_base <= e) lo = mid; else hi = mid;
+    }
+    const TabDev d = desc[lo];
+    const int64_t cn = (int64_t)d.R * d.n3, local = e - d.g3_base;
+    const int64_t slice = d.o3 + (local / cn) * cn;
+    const int64_t w = local % cn;          // destination: [j3][r2]
+    const int64_t j3 = w / d.R, r2 = w % d.R;
+    g3t[slice + w] = g3[slice + r2 * d.n3 + j3];
+}
+
 struct FwdArgs {
     const BatchRec* recs;
     const int32_t* run_i3;
     const float* g1;
     const float* g2;
-    const float* g3;
+    const float* g3t;      // G3 with each slice transposed to [n3][R]
     float* stage;
     int64_t L;             // first spare stage row
     float* pbuf;           // when set, each group's P is also kept here (for the backward)
+    int32_t* claims;       // [kFwdCounters][32]: batch claim counters (zero at the launch)
 };
 
 // The runs of one batch: tiles of LK = 4 runs of one group. The suffix
@@ -114,7 +136,7 @@ struct FwdTiles {
     struct Ops {
         int g;
         int32_t r;
-        float bv[KS];      // G3[i3 of run lk][r2][j3], K = r2
+        floatx4 bv[KS / 4];   // G3[i3 of run lk][r2 = KS*q + 4h + u][j3], K = r2
     };
     int32_t tpl;           // lane g <= ng: the batch's first tile of group g (lane ng: the tile count)
     int t0, n, gs;
@@ -136,9 +158,9 @@ struct FwdTiles {
     __device__ __forceinline__ void load_ops(const FwdArgs& a, const BatchCtx& c, const Ids& o, Ops& x) {
         const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4, j3 = col % N3;
         x.g = o.g; x.r = o.r;
-        const float* gb = a.g3 + c.o3 + j3 + KS * q * N3 + (int64_t)o.i3 * R * N3;
+        const floatx4* gb = reinterpret_cast<const floatx4*>(a.g3t + c.o3 + (int64_t)o.i3 * R * N3 + j3 * R + KS * q);
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) x.bv[s2] = gb[s2 * N3];
+        for (int h = 0; h < KS / 4; ++h) x.bv[h] = gb[h];
     }
 
     // After the prologue (sRb, sI3 and P in LDS, visible to every wave): the
@@ -189,7 +211,7 @@ struct FwdTiles {
                 floatx4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < KS; ++s2)
-                    e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2], bp[mt][s2], e, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2 / 4][s2 % 4], bp[mt][s2], e, 0, 0, 0);
                 *reinterpret_cast<floatx4*>(dst + 16 * mt * N3) = e;
             }
         };
@@ -202,13 +224,17 @@ struct FwdTiles {
     }
 };
 
-// Persistent workgroups (a few per CU) walk the planner's batch list, each the
-// part of its XCD class in a snake over that class's workgroups (batch_walk);
+// Persistent workgroups (a few per CU) claim their batches from the planner's
+// batch list, each in the part of its XCD class (batch_walk, batch_claims):
 // the list holds only batches with groups and each part starts with its
-// heaviest, so every workgroup gets four or five batches of mixed weight. While a workgroup runs the tiles of
-// one batch, the loads of its next batch (G2 slice, G1 rows, run i3 list)
-// are in flight, and the records of the next two batches are already in
-// registers, so a batch's prologue costs no exposed memory round trip.
+// heaviest, so the claims hand out the heaviest batches first and the last
+// ones to finish are light. Thread 0 claims two batches ahead; while a
+// workgroup runs the tiles of one batch, the loads of its next batch (G2
+// slice, G1 rows, run i3 list) are in flight and the record of the one after
+// is in registers, so a batch's prologue costs no exposed memory round trip.
+// A fixed walk of the list left the last workgroup ending about 20% after
+// the median one; the claims, spread over kFwdCounters addresses, cost a few
+// hundred serialised atomics per counter.
 template <int N1, int N2, int R, int N3, bool KEEP>
 __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, const int32_t* __restrict__ ctrl) {
     using B = PrefixBatch<N1, N2, R>;
@@ -216,17 +242,24 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, co
     static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 256, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
+    __shared__ int32_t sClaim[2];
     extern __shared__ int32_t sI3[];   // the batch's run i3 list
 
-    const BatchWalk bw = batch_walk(ctrl);
-    const int64_t end = bw.base + bw.n;
-    int32_t rwA = rec_word(a.recs, bw.at(0), cap, end);
-    int32_t rwB = rec_word(a.recs, bw.at(1), cap, end);
+    const BatchClaims bc = batch_claims(batch_walk(ctrl), a.claims);
+    if (threadIdx.x == 0) {
+        sClaim[0] = atomicAdd(bc.ctr, 1);
+        sClaim[1] = atomicAdd(bc.ctr, 1);
+    }
+    __syncthreads();
+    int64_t pA = bc.pos(sClaim[0]), pB = bc.pos(sClaim[1]);
+    int32_t rwA = rec_word(a.recs, pA, cap, bc.end);
+    int32_t rwB = rec_word(a.recs, pB, cap, bc.end);
     BatchPf<N1, N2, R> f;
     batch_fetch<N1, N2, R>(rwA, a.run_i3, a.g1, a.g2, f);
     FwdTiles<N1, N2, R, N3> tl;
-    for (int64_t r = 0; bw.has(r); ++r) {
-        const int32_t rwC = rec_word(a.recs, bw.at(r + 2), cap, end);
+    while (pA < bc.end) {
+        int32_t cc = 0;
+        if (threadIdx.x == 0) cc = atomicAdd(bc.ctr, 1);   // read at the batch's end
         BatchCtx c;
         const bool live = rec_field(rwA, RW_NG) > 0;
         if (live) {
@@ -237,8 +270,13 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, co
         if (live) {
             if (KEEP) store_prefix_lanes<N1, N2, R, 256>(sU, c.g0, c.ng, a.pbuf);
             tl.run(a, c, sU, sRb, sI3);
-            __syncthreads();   // sU is the next prologue's
         }
+        if (threadIdx.x == 0) sClaim[0] = cc;
+        __syncthreads();   // sU is the next prologue's; the claim is every wave's
+        const int64_t pC = bc.pos(__builtin_amdgcn_readfirstlane(sClaim[0]));
+        const int32_t rwC = rec_word(a.recs, pC, cap, bc.end);
+        pA = pB;
+        pB = pC;
         rwA = rwB;
         rwB = rwC;
     }
@@ -253,7 +291,11 @@ template <int D>
 __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_start, int64_t TB,
                                               const int32_t* __restrict__ run_of,
                                               const float* __restrict__ stage,
-                                              float* __restrict__ out, int32_t* ctrl) {
+                                              float* __restrict__ out, int32_t* ctrl,
+                                              int32_t* __restrict__ fwd_claims) {
+    // the batch kernel has finished: its claim counters start from zero at
+    // the next forward call
+    if (blockIdx.x == 0 && threadIdx.x < kFwdCounters) fwd_claims[threadIdx.x * 32] = 0;
     constexpr int LPR = D / 4, RPI = 64 / LPR, U = 8;   // U loads in flight
     static_assert(D % 4 == 0 && 64 % LPR == 0, "row shape");
     // wave-uniform bag: its loops are scalar control flow
@@ -293,9 +335,14 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 template <int N1, int N2, int R, int N3>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, bool keep, hipStream_t s) {
-    FwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3,
-              p->at<float>(p->lay.stage), p->L, keep ? p->at<float>(p->lay.pbuf) : nullptr};
+    int32_t* fwd_claims = p->at<int32_t>(p->lay.claims) + 32 * kRunCounters;
+    float* g3t = p->at<float>(p->lay.g3t);
+    FwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3t,
+              p->at<float>(p->lay.stage), p->L, keep ? p->at<float>(p->lay.pbuf) : nullptr, fwd_claims};
     if (p->L > 0 && p->n_fb > 0) {
+        TT_LAUNCH(p, "k_g3t", s, k_g3t, dim3(grid_for(p->g3_total, 256)), dim3(256), 0, s, p->desc(), p->T,
+                  p->g3_total, g3, g3t);
+        TT_LAUNCH_CHECK();
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = batch_grid(p->n_fb, kFwdPersistBlocks);
         if (keep)
@@ -309,7 +356,7 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     if (p->TB > 0) {
         TT_LAUNCH(p, "k_pool", s, k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
-                           p->at<float>(p->lay.stage), out, p->ctrl());
+                           p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims);
         TT_LAUNCH_CHECK();
     }
     return TT_OK;

@@ -108,6 +108,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     // P per group (kept from the training forward, or formed by the
     // backward), then dL/dP per group written over it by the run kernel
     y.pbuf = take(sizeof(float) * (size_t)GB * (size_t)PR);
+    y.g3t = take(sizeof(float) * (size_t)E3);
     y.acc1 = take(fwd_only ? 0 : sizeof(double) * (size_t)E1);
     y.acc3 = take(fwd_only ? 0 : sizeof(double) * (size_t)E3);
     // each run's dG3 term P^T S (R*n3 floats) goes over the run's S row when
@@ -117,6 +118,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     // two slots per window (its start piece and its end piece)
     y.xsum = take(sizeof(double) * 2 * (size_t)((LB + 63) / 64) * (size_t)D);
     y.xcnt = take(sizeof(int32_t) * (size_t)((LB + 63) / 64));
+    y.claims = take(sizeof(int32_t) * 32 * (kRunCounters + kFwdCounters));
     y.NB3 = NB3;
     y.i3cnt = take(sizeof(int32_t) * (size_t)NB3 * kI3Pad);
     y.i3start = take(sizeof(int32_t) * (size_t)(NB3 + 1));
@@ -974,8 +976,10 @@ __global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict_
                                                        int32_t* __restrict__ ctrl,
                                                        const uint32_t* __restrict__ batch_tiles,
                                                        int32_t* __restrict__ place,
-                                                       BatchRec* __restrict__ rec) {
+                                                       BatchRec* __restrict__ rec,
+                                                       int32_t* __restrict__ fwd_claims) {
     __shared__ uint32_t sbase[kXcds], stot[kXcds];
+    if (blockIdx.x == 0 && threadIdx.x < kFwdCounters) fwd_claims[threadIdx.x * 32] = 0;   // the forward's counters
     __shared__ uint32_t wc[kSlotTile / 64][kXcds];
     const int64_t jt = blockIdx.x;
     const int64_t b = jt * kSlotTile + threadIdx.x;
@@ -1159,8 +1163,11 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     p->kept_g1 = nullptr;
     p->kept_g2 = nullptr;
     p->off4 = true;
+    p->g3_total = 0;
     for (int32_t t = 0; t < T; ++t) {
-        if (tables[t].g_offset[0] % 4 != 0 || tables[t].g_offset[1] % 4 != 0) p->off4 = false;
+        if (tables[t].g_offset[0] % 4 != 0 || tables[t].g_offset[1] % 4 != 0 || tables[t].g_offset[2] % 4 != 0)
+            p->off4 = false;
+        p->g3_total += (int64_t)tables[t].m[2] * tables[t].rank * tables[t].n[2];
         const tt_emb_table& x = tables[t];
         if (x.n[0] != p->n1 || x.n[1] != p->n2 || x.n[2] != p->n3 || x.rank != p->R) p->uniform = false;
         const int64_t R = x.rank;
@@ -1188,6 +1195,7 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     const int64_t nzero = (int64_t)((lay.scan_st - lay.ctrl) + sizeof(ScanTileStatus) * lay.scan_tiles) / 4;
     int nscan = 0;   // scans issued so far (each gets its own epoch and tile counter)
     int32_t kb = 0, i2b = 0, fbb = 0;
+    int64_t g3b = 0;
     for (int32_t first = 0; first < T; first += 16) {
         DescBatch b{};
         b.first = first;
@@ -1204,6 +1212,8 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             i2b += x.m[1];
             d.fb_base = fbb;
             fbb += x.m[1] * ((x.m[0] + kFwdBatch - 1) / kFwdBatch);
+            d.g3_base = g3b;
+            g3b += (int64_t)x.m[2] * x.rank * x.n[2];
             kb += x.m[0] * x.m[1];
         }
         if (first == 0)
@@ -1308,7 +1318,8 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             TT_LAUNCH(p, "k_batches", s, k_batches, dim3((unsigned)((lay.NFB + kSlotTile - 1) / kSlotTile)),
                       dim3(kSlotTile), 0, s, p->desc(), T, K, lay.NFB, kscan, p->at<int32_t>(lay.group_key),
                       p->at<int32_t>(lay.group_rbase), ctrl, p->at<uint32_t>(lay.batch_tiles),
-                      p->at<int32_t>(lay.batch_place), p->at<BatchRec>(lay.batch));
+                      p->at<int32_t>(lay.batch_place), p->at<BatchRec>(lay.batch),
+                      p->at<int32_t>(lay.claims) + 32 * kRunCounters);
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
     }

@@ -89,6 +89,7 @@ __device__ __forceinline__ int64_t snake(int64_t r, int64_t w, int64_t G) {
 // few slices hold most batches) the whole list, in a snake over all.
 struct BatchWalk {
     int64_t base, n, wi, G;
+    bool classed;
     __device__ __forceinline__ int64_t at(int64_t r) const { return base + snake(r, wi, G); }
     __device__ __forceinline__ bool has(int64_t r) const { return snake(r, wi, G) < n; }
 };
@@ -101,21 +102,45 @@ __device__ __forceinline__ BatchWalk batch_walk(const int32_t* __restrict__ ctrl
     int64_t mx = 0;
 #pragma unroll
     for (int c = 0; c < kXcds; ++c) mx = max(mx, (int64_t)(cb[c + 1] - cb[c]));
-    BatchWalk bw{0, nl, w, G};
+    BatchWalk bw{0, nl, w, G, false};
     if (G % kXcds == 0 && mx * kXcds <= nl + nl / 4 + 4 * kXcds) {
         const int c = (int)(w % kXcds);
         bw.base = cb[c];
         bw.n = cb[c + 1] - cb[c];
         bw.wi = w / kXcds;
         bw.G = G / kXcds;
+        bw.classed = true;
     }
     return bw;
 }
 
-// Persistent grid of a batch kernel: a multiple of kXcds, at most `cap`.
+// Claimed batches: workgroup b claims from counter cidx = b mod kFwdCounters;
+// claim j of that counter is batch base + j*stride + off of the walked part
+// (classed: the kFwdCounters/kXcds counters of the part's class interleave
+// over it; otherwise all kFwdCounters over the whole list), so each counter
+// hands out its share in list order, heaviest first.
+struct BatchClaims {
+    int64_t base, end, stride, off;
+    int32_t* ctr;
+    __device__ __forceinline__ int64_t pos(int32_t j) const { return base + (int64_t)j * stride + off; }
+};
+__device__ __forceinline__ BatchClaims batch_claims(const BatchWalk& bw, int32_t* __restrict__ counters) {
+    const int cidx = (int)(blockIdx.x % kFwdCounters);
+    BatchClaims c;
+    c.base = bw.base;
+    c.end = bw.base + bw.n;
+    c.stride = bw.classed ? kFwdCounters / kXcds : kFwdCounters;
+    c.off = bw.classed ? cidx / kXcds : cidx;
+    c.ctr = counters + cidx * 32;
+    return c;
+}
+
+// Persistent grid of a batch kernel: a multiple of kFwdCounters (so every
+// counter, and every class, has its workgroups), at most `cap`.
 inline unsigned batch_grid(int64_t slots, int64_t cap) {
-    const int64_t g = std::min<int64_t>(cap, (slots + kXcds - 1) / kXcds * kXcds);
-    return (unsigned)std::max<int64_t>(g, kXcds);
+    static_assert(kFwdPersistBlocks % kFwdCounters == 0, "grid of whole counter sets");
+    const int64_t g = std::min<int64_t>(cap, (slots + kFwdCounters - 1) / kFwdCounters * kFwdCounters);
+    return (unsigned)std::max<int64_t>(g, kFwdCounters);
 }
 __device__ __forceinline__ int32_t rec_field(int32_t rw, int k) { return __builtin_amdgcn_readlane(rw, k); }
 __device__ __forceinline__ int64_t rec_field64(int32_t rw, int k) {

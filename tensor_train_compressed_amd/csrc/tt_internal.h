@@ -20,7 +20,8 @@ struct alignas(16) TabDev {
     int32_t key_base;           // first prefix key of this table
     int32_t i2_base;            // first (table, i2) slice index of this table
     int32_t fb_base;            // first forward batch (kFwdBatch groups of one slice) of this table
-    int32_t pad_[3];
+    int32_t pad_;
+    int64_t g3_base;            // first element of this table's G3 in a walk over every table's G3
 };
 static_assert(sizeof(TabDev) == 80, "TabDev layout");
 
@@ -54,6 +55,15 @@ constexpr int kRunRange = 32;
 // slot in the workspace); the groups that would exceed it run whole, one
 // wave each.
 constexpr int64_t kMaxXPieces = 8192;
+// The run kernel's waves claim their units from this many counters (each on a
+// 128-byte line of its own; counter c hands out units c, c + kRunCounters,
+// ...), the waves of workgroup b from counter b mod kRunCounters.
+constexpr int kRunCounters = 32;
+// The forward batch kernel's workgroups claim their batches from this many
+// counters (after the run kernel's in the same array): workgroup b from
+// counter b mod kFwdCounters, whose XCD class is b mod kXcds.
+constexpr int kFwdCounters = 32;
+static_assert(kFwdCounters % kXcds == 0, "each counter serves one XCD class");
 // With at most this many G3 rows in all (any number of tables, each table's
 // G3 offset a whole number of R*n3 rows), dG3 is reduced per G3 row from
 // per-run terms (one workgroup per row sums its bucket) instead of with
@@ -154,6 +164,8 @@ struct Layout {
     size_t pbuf;                             // [Gmax][n1*n2*R] float: P per group, in the lane order of the
                                              //     matrix-core operands; the backward's run kernel then
                                              //     writes each group's dL/dP over it (row-major)
+    size_t g3t;                              // [extent of G3] float: each G3 slice transposed to [n3][R]
+                                             //     (the forward's suffix operand, written per forward call)
     size_t c3;                               // [L][R*n3] float, only when R*n3 > D (and dG3 is bucketed):
                                              //     each run's dG3 term P^T S (else written over its S row)
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
@@ -161,6 +173,8 @@ struct Layout {
     size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
                                              //     cut by the backward's windows
     size_t xcnt;                             // [ceil(L/64)] int32: spans done per long cut run
+    size_t claims;                           // [kRunCounters + kFwdCounters][32] int32: the run kernel's and
+                                             //     the forward batch kernel's claim counters
     // the backward's c3 rows, bucketed by G3 row (table's G3 offset / (R*n3) + i3),
     // when every table's G3 offset is a whole number of rows and there are at
     // most kMaxBuckets3 rows (NB3 of them; else NB3 = 0 and dG3 takes atomics)
@@ -212,6 +226,7 @@ struct tt_emb_plan_s {
     bool uniform;             // all tables share (n1, n2, n3, R)
     int32_t n1, n2, n3, R;    // the shared shape when uniform
     int64_t extent[3];        // elements of the packed G1/G2/G3 buffers in use
+    int64_t g3_total;         // sum over tables of m3*R*n3 (the G3 elements the tables use)
     bool packed;              // tables' cores sit back to back from offset 0 (no gaps)
     bool off4;                // every table's G1 and G2 offsets are multiples of 4 floats
     bool g2_overlap;          // two tables' G2 ranges overlap (a shared core)

@@ -558,7 +558,7 @@ def test_backward_hot_slices_full_size():
 
 def test_kernel_timing():
     """tt_emb_set_timing brackets every launch with events: a forward records
-    the batch and pooling kernels once each, with positive times; a plan made
+    the G3 transpose, batch and pooling kernels once each, with positive times; a plan made
     while the process-wide default is on records its planning kernels."""
     import tensor_train_compressed_amd as tte
     dp = DevProblem(wl.make("train11m", batch=256), 256)
@@ -572,7 +572,7 @@ def test_kernel_timing():
     out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
     tte.tt_emb_forward(pl, dp.g1, dp.g2, dp.g3, out)
     t = tte.tt_emb_kernel_times(pl)
-    assert [k for k, _ in t] == ["k_fwd_batch", "k_pool"] and all(ms > 0 for _, ms in t)
+    assert [k for k, _ in t] == ["k_g3t", "k_fwd_batch", "k_pool"] and all(ms > 0 for _, ms in t)
     tte.tt_emb_set_timing(pl, False)
     tte.tt_emb_forward(pl, dp.g1, dp.g2, dp.g3, out)
     assert tte.tt_emb_kernel_times(pl) == []
