@@ -3,10 +3,9 @@
 // The pages evaluate training through the TT lookup (FlowTT abstract: training
 // latency at batch 32,768) but give no formulas; the gradients here are those
 // of the loss <grad_out, out> with respect to each core, by multilinear
-// calculus on the TT chain. Per chunk, the shared prefix P = G1[i1] x G2[i2]
-// is recomputed on chip; each lookup adds to dP (kept in LDS for the whole
-// chunk) and to its dG3 slice; the chunk then turns dP into its dG1 and dG2
-// contributions.
+// calculus on the TT chain. The generic kernel below works per chunk with
+// fp32 atomics; the matrix-core kernels further down work per row run and per
+// group, with fp64 sums where long cancelling sequences meet.
 #include "tt_device.h"
 
 namespace tt {
@@ -158,10 +157,11 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 // group, the same runs the forward contracts):
 //
 // bwd_prep      (the first workgroups of the k_bwd_sum launch) zeroes the
-//               fp64 accumulators of dG1 and dG3 (the targets added with
-//               atomics; fp64 keeps a sum of many cancelling terms within the
-//               fp32 tolerance) and the completion counters, scans the runs
-//               per i3, and lists the pieces of the large groups
+//               fp64 accumulators (dG1; dG3 when it is added with atomics),
+//               the completion and claim counters, scans the dG3 buckets'
+//               run counts, and lists the pieces of the groups of more than
+//               kRunRange runs (a group whose pieces would not fit the list
+//               runs whole)
 // k_bwd_sum     one wave per window of 64 sorted positions: for every run,
 //               S = sum of the grad_out rows of its lookups, accumulated in
 //               fp64. A run inside one window is stored once, rounded to fp32;
@@ -170,22 +170,31 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 // k_bwd_cross   adds up the pieces of the cut runs in fp64 and rounds them
 //               into their S rows (a hot row's run spans many windows: an
 //               fp32 sum of its pieces would lose the fp32 tolerance on the
-//               slices it feeds)
-// k_bwd_pfx     recomputes P of every group (persistent workgroups over the
-//               planner's prefix batches, as the forward) into a global buffer
-// k_bwd_runs    one wave per piece of up to kRunRange runs of one group, the
-//               group's P in registers;
-//               per run, on the matrix cores,
-//                 dG3[i3] += P^T S          (R x n3, added with fp64 atomics)
-//                 dP_g    += S G3[i3]^T     (n1*n2 x R, summed in registers)
-//               and stores each group's dL/dP row once (atomics only for the
-//               few groups large enough to be split into pieces)
-// k_bwd_dg2     one wave per (slice, 16x16 tile of dG2[i2]):
-//                 dG2[i2] += G1[i1]^T dP    (fp64 products, plain stores, owned)
-// k_bwd_dg1     one wave per (4 groups of a slice, 16 r1 columns):
+//               slices it feeds); its extra workgroups write the dG3 bucket
+//               lists
+// k_bwd_pfx     forms P of every group (persistent workgroups over the
+//               forward's batch list) into the P buffer; skipped when the
+//               training forward kept P
+// k_bwd_runs_c3 one wave per unit (a listed piece of up to kRunRange runs of
+//               one group, or a whole group), claimed from 32 counters, the
+//               group's P in registers; per tile of 4 runs, on the matrix
+//               cores,
+//                 c3[run]  = P^T S          (R x n3, fp32; over the run's S)
+//                 dP_g    += S G3[i3]^T     (n1*n2 x R, fp64, in registers)
+//               dP is stored over the group's P (a split group's pieces go to
+//               fp64 slots, the last piece adds them); k_bwd_runs adds P^T S
+//               to the fp64 dG3 accumulator with atomics instead
+// k_bwd_dg3     one workgroup per G3 row: dG3[i3] = sum of its runs' c3 rows
+// k_bwd_dg1     one wave per batch slot, slice-major:
 //                 dG1[i1] += dP G2[i2]^T    (fp64 products, one fp64 atomic
 //                                            per element and group)
-// k_bwd_finish  dG1, dG3 <- their fp64 accumulators, rounded to fp32
+// k_bwd_dg2     one wave per (slice, 16-column tile of dG2[i2]):
+//                 dG2[i2] = sum G1[i1]^T dP (fp64 products, plain stores, owned)
+// k_bwd_finish  dG1 (and atomics-mode dG3) <- their fp64 accumulators, rounded
+//               to fp32
+// With the fused SGD (GradOut::sgd) dG3, dG2 and dG1 are not stored: each
+// kernel applies G <- G - lr * dG to the core element instead, and only on
+// the slices and rows the batch touches.
 
 __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64_t s) {
     return s == 0 || skey[s - 1] != skey[s];
