@@ -37,32 +37,41 @@ from .planner import PlanError, plan, plan_problem  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tt_oracle.c")
-_LIB = os.path.join(_HERE, "libtt_oracle.so")
+_LIB = os.environ.get("TT_ORACLE_LIB") or os.path.join(_HERE, "libtt_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
 OK, BAD_ARG, BAD_INDEX, BAD_OFFSETS, NO_MEMORY = 0, -1, -2, -3, -4
+
+# AddressSanitizer + UndefinedBehaviorSanitizer build (gcc); the process that
+# loads it must preload gcc's libasan (LD_PRELOAD) and set TT_ORACLE_LIB.
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
 
 
 class OracleError(RuntimeError):
     pass
 
 
-def build(force: bool = True) -> str:
-    """Compile tt_oracle.c with gcc (-O2, OpenMP) into oracle/libtt_oracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+def build(force: bool = True, sanitize: bool = False, out: Optional[str] = None) -> str:
+    """Compile tt_oracle.c with gcc (OpenMP) into oracle/libtt_oracle.so (-O2),
+    or, with sanitize=True, an ASan/UBSan build into `out`."""
+    lib = out or _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + f".tmp{os.getpid()}"
+        opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+        subprocess.run(["gcc", *opt, "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
                         "-o", tmp, _SRC], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
+            if not os.environ.get("TT_ORACLE_LIB"):
+                build(force=False)
             lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p
             i32, i64 = ctypes.c_int32, ctypes.c_int64

@@ -62,7 +62,9 @@ class TTEmbLibraryMissing(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libtt_emb.so")
+    """The in-tree libtt_emb.so, or the file TT_EMB_LIBRARY names (an
+    instrumented build of the same sources, e.g. with host sanitizers)."""
+    return os.environ.get("TT_EMB_LIBRARY") or os.path.join(_HERE, "libtt_emb.so")
 
 
 class _Table(ctypes.Structure):

@@ -47,6 +47,49 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer flags: every
+# -fsanitize goes to the host compilation only (device code is not
+# instrumented). A process that loads this build must preload clang's ASan
+# runtime (asan_runtime()) and point TT_EMB_LIBRARY at it.
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime (it also carries the UBSan handlers)."""
+    llvm = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm")
+    hits = sorted(glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang's ASan runtime was not found next to hipcc")
+    return os.path.realpath(hits[-1])
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Build the same sources with host-side sanitizers (device code at -O1,
+    never run by the host checks) into out_dir/libtt_emb_san.so."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [a for a in COMMON if a != "-O3"] + ["-O1", "-g"] + HOST_SANITIZE
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources()))) as ex:
+        objs = list(ex.map(one, sources()))
+    lib = os.path.join(out_dir, "libtt_emb_san.so")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return lib
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()

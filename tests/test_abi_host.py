@@ -84,3 +84,21 @@ def test_workspace_size_skew11m():
     _lib()
     good = _tabs((11_000_000, (200, 220, 250), (4, 8, 4), 32))
     assert tte.tt_emb_workspace_bytes(good, 656_601, 32768, 256) < 700e6
+
+
+def test_more_entry_points_reject_bad_args_on_host():
+    lib = _lib()
+    P = ctypes.c_void_p
+    assert lib.tt_emb_backward_sgd(None, 1, P(1), P(1), P(1), P(1), ctypes.c_float(0.1), None) == -1
+    n = ctypes.c_int32(-1)
+    assert lib.tt_emb_kernel_times(None, None, 0, ctypes.byref(n), None) == -1
+    assert lib.tt_emb_set_timing(None, 1) == 0 and lib.tt_emb_set_timing(None, 0) == 0
+    assert lib.tt_emb_scratch_capacity() == 64 << 20
+    big = _tabs((11_000_000, (200, 220, 250), (4, 8, 4), 32))
+    # a batch beyond the static buffer is refused before any device call
+    assert lib.tt_emb_forward_scratch(big, 1, P(16), P(16), 2_000_000, 32768, 256,
+                                      P(16), P(16), P(16), P(16), None) == -7
+    # a batch that fits, with a null core: refused before the buffer is touched
+    assert lib.tt_emb_forward_scratch(big, 1, P(16), P(16), 1000, 64, 256,
+                                      None, P(16), P(16), P(16), None) == -1
+    assert b"scratch" in lib.tt_emb_status_string(-7)
