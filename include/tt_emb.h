@@ -242,12 +242,15 @@ tt_status tt_emb_forward_scratch(const tt_emb_table* tables, int32_t T, const in
 size_t tt_emb_scratch_capacity(void);
 
 /* Which kernels a call on this plan runs (pure host query, no launch).
- * The matrix-core path serves plans whose tables all share one shape among
- * those this build instantiates, with G1 and G2 offsets that are multiples
- * of 4 floats, 16-byte aligned g1 and g2, and m3 <= 1024; the backward's
- * matrix-core path also needs tables that do not share a G2 core. Other
- * plans take the generic kernels (scalar FMA, one workgroup per chunk, fp32
- * atomics whose summation order varies from run to run). */
+ * The matrix-core path serves plans whose tables all share one shape
+ * (n1, n2, n3, R) among those the library is built for, with G1 and G2
+ * offsets that are multiples of 4 floats, 16-byte aligned g1 and g2, and
+ * m3 <= 1024. Forward shapes: (4,8,4,32), (4,4,4,32), (4,4,4,16),
+ * (2,8,4,32), (8,4,4,32), (4,4,4,64), (4,4,8,32), (4,4,2,32), (4,4,1,32);
+ * the backward's matrix-core kernels serve the first six (n3 = 4) for tables
+ * that do not share a G2 core. Other plans take the generic kernels (scalar
+ * FMA, one workgroup per chunk, fp32 atomics whose summation order varies
+ * from run to run). */
 #define TT_PATH_MATRIX_CORE 1
 #define TT_PATH_GENERIC 2
 typedef struct {

@@ -830,7 +830,7 @@ __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
 // CU on the same few hundred G3 slices saturate the memory-side atomic
 // units, and LDS float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
-__global__ __launch_bounds__(256, 3) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3, int64_t c3s) {
+__global__ __launch_bounds__(256, R >= 64 ? 2 : 3) void k_bwd_runs_c3(RunsArgs a, float* __restrict__ c3, int64_t c3s) {
     runs_body<N1, N2, R, N3>(a, [&](int64_t, int within, int32_t run, const floatx4& c) {
         *reinterpret_cast<floatx4*>(c3 + (int64_t)run * c3s + within) = c;
     });
@@ -884,11 +884,11 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3
 }
 
 // dG2[i2] = sum over the slice's groups of G1[i1]^T dP_g, one wave per
-// (slice, 16-column tile of the n2*R columns), every r1 tile: K = j1, one
-// fp64 matrix-core step per group and r1 tile, operands read straight from
-// memory (each dP element once; the next UNR groups' loads issued before the
-// current ones' products), no LDS and no barrier. The wave owns its columns:
-// plain stores.
+// (slice, 16-column tile of the n2*R columns), every r1 tile: K = the
+// (group, j1) pairs taken four at a time (one group per fp64 matrix-core step
+// when n1 = 4), operands read straight from memory (each dP element once;
+// the next UNR steps' loads issued before the current ones' products), no
+// LDS and no barrier. The wave owns its columns: plain stores.
 template <int N1, int N2, int R>
 __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc, int32_t T,
                                                  const int32_t* __restrict__ ctrl, int64_t K,
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
                                                  const float* __restrict__ dpg, const float* __restrict__ g1,
                                                  float* __restrict__ dg2, int64_t n_i2, GradOut go) {
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, CT = N2R / 16, UNR = 8;
-    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0, "shape");
+    static_assert(16 % N1 == 0 && R % 16 == 0 && N2R % 16 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     // wave-uniform task: the group loop is scalar control flow (no exec-mask
     // loop, whose head waits for every load in flight)
@@ -921,10 +921,10 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
     const int32_t g0 = (int32_t)(key_scan[kb] >> 32);
     const int32_t ge = kb + d.m1 < K ? (int32_t)(key_scan[kb + d.m1] >> 32) : U;
     if (go.sgd && g0 >= ge) return;   // an untouched G2 slice keeps its values
-    const float* G1c = g1 + d.o1 + q * R + col;               // + i1*N1*R + 16*rt: G1[i1][j1 = q][r1]
-    const float* dPc = dpg + q * N2R + 16 * ct + col;          // + g * PR: dP_g[j1 = q][c]
-    // two accumulator sets (even and odd steps of a group pair) keep two
-    // independent product chains per r1 tile in flight
+    const float* G1c = g1 + d.o1 + col;          // + i1*N1*R + j1*R + 16*rt: G1[i1][j1][r1]
+    const float* dPc = dpg + 16 * ct + col;      // + g*PR + j1*N2R: dP_g[j1][c]
+    // two accumulator sets (even and odd steps) keep two independent product
+    // chains per r1 tile in flight
     doublex4 acc[2][RT];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
@@ -933,21 +933,36 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
     for (int32_t gb = g0; gb < ge; gb += 64) {
         const int32_t i1l = group_key[min(gb + lane, ge - 1)] - (int32_t)kb;   // lane j: i1 of group gb + j
         const int n = min(64, ge - gb);
+        const int ns = (n * N1 + 3) / 4;   // steps: lane q of step st takes pair 4st + q
         float av[2][UNR][RT], bv[2][UNR];
         auto load = [&](int j0, float (&a)[UNR][RT], float (&b)[UNR]) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
-                const int j = min(j0 + u, n - 1);
-                const float* ga = G1c + (int64_t)__builtin_amdgcn_readlane(i1l, j) * N1 * R;
+                const unsigned st = (unsigned)min(j0 + u, ns - 1);
+                int gl, j1, i1;
+                bool ok = true;
+                if constexpr (N1 >= 4) {   // the lanes of a step share its group: wave-uniform
+                    gl = (int)((4u * st) / N1);
+                    j1 = (int)((4u * st) % N1) + q;
+                    i1 = __builtin_amdgcn_readlane(i1l, gl);
+                } else {
+                    const unsigned f = 4u * st + (unsigned)q;
+                    ok = (int)(f / N1) < n;   // a pair past the last group adds zero
+                    gl = min((int)(f / N1), n - 1);
+                    j1 = (int)(f % N1);
+                    i1 = __shfl(i1l, gl);
+                }
+                const float* ga = G1c + (int64_t)i1 * N1 * R + j1 * R;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) a[u][rt] = ga[16 * rt];
-                b[u] = dPc[(int64_t)(gb + j) * PR];
+                const float x = dPc[(int64_t)(gb + gl) * PR + j1 * N2R];
+                b[u] = ok ? x : 0.f;
             }
         };
         auto math = [&](int j0, const float (&a)[UNR][RT], const float (&b)[UNR]) {
 #pragma unroll
             for (int u = 0; u < UNR; ++u)
-                if (j0 + u < n) {
+                if (j0 + u < ns) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
                         acc[u & 1][rt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[u][rt], (double)b[u],
@@ -956,12 +971,12 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
         };
         load(0, av[0], bv[0]);
         for (int j0 = 0;; j0 += 2 * UNR) {
-            load(min(j0 + UNR, n - 1), av[1], bv[1]);
+            load(min(j0 + UNR, ns - 1), av[1], bv[1]);
             math(j0, av[0], bv[0]);
-            if (j0 + UNR >= n) break;
-            load(min(j0 + 2 * UNR, n - 1), av[0], bv[0]);
+            if (j0 + UNR >= ns) break;
+            load(min(j0 + 2 * UNR, ns - 1), av[0], bv[0]);
             math(j0 + UNR, av[1], bv[1]);
-            if (j0 + 2 * UNR >= n) break;
+            if (j0 + 2 * UNR >= ns) break;
         }
     }
     // the fp64 product's lane (col, q) holds rows r1 = 16rt + q + 4v, column c = 16ct + col
@@ -974,13 +989,13 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
 }
 
 // dG1[i1] += dP_g G2[i2]^T, one wave per prefix batch (up to 8 groups of one
-// slice: two row tiles of 4 groups), every r1 tile: rows (group, j1), K = the
-// n2*R columns, taken 16 at a time as 16-byte loads per lane (dP once, G2 once
-// per r1 tile for both row tiles) feeding four fp64 matrix-core steps per row
-// and r1 tile. A group's sum over K is complete in the wave, so each dG1
-// element takes one fp64 atomic per group (groups of every slice add to the
-// same i1). A wave per half batch read the 32 KB G2 slice twice per batch,
-// and that L2 traffic set its time.
+// slice: n1/2 row tiles of 16 (group, j1) rows), every r1 tile: rows (group,
+// j1), K = the n2*R columns, taken 16 at a time as 16-byte loads per lane (dP
+// once, G2 once per r1 tile for all row tiles) feeding four fp64
+// matrix-core steps per row and r1 tile. A group's sum over K is complete in
+// the wave, so each dG1 element takes one fp64 atomic per group (groups of
+// every slice add to the same i1). A wave per half batch read the 32 KB G2
+// slice twice per batch, and that L2 traffic set its time.
 // Waves take the batch slots in slice-major order (the planner's place map),
 // so waves that run together work on different i1 rows of dG1 rather than
 // piling atomics on the same ones.
@@ -990,8 +1005,8 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
                                                  const int32_t* __restrict__ place,
                                                  const float* __restrict__ dpg, const float* __restrict__ g2,
                                                  double* __restrict__ dg1) {
-    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2, MT = kFwdBatch / 4;
-    static_assert(N1 == 4 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0 && MT == 2, "shape");
+    constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2, MT = kFwdBatch * N1 / 16;
+    static_assert(16 % N1 == 0 && MT >= 1 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     const int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (k >= cap) return;
@@ -1003,12 +1018,14 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
     const int ng = rec_field(rw, RW_NG);
     if (ng <= 0) return;
     const int32_t g0 = rec_field(rw, RW_G0);
-    // A row i of row tile mt = (group 4mt + i / 4, j1 = i % 4): lane (col, q) reads row col
+    // A row i of row tile mt = (group, j1) of row 16mt + i: lane (col, q) reads row col
     const floatx4* A[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        A[mt] = reinterpret_cast<const floatx4*>(dpg + (int64_t)(g0 + min(4 * mt + col / 4, ng - 1)) * PR +
-                                                 (col % 4) * N2R) + q;
+    for (int mt = 0; mt < MT; ++mt) {
+        const int rho = 16 * mt + col;
+        A[mt] = reinterpret_cast<const floatx4*>(dpg + (int64_t)(g0 + min(rho / N1, ng - 1)) * PR +
+                                                 (rho % N1) * N2R) + q;
+    }
     const floatx4* Bm = reinterpret_cast<const floatx4*>(g2 + rec_field64(rw, RW_O2) +
                                                           (int64_t)rec_field(rw, RW_I2) * R * N2R +
                                                           (int64_t)col * N2R) + q;   // + 16*rt rows
@@ -1047,18 +1064,26 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
         if (s0 + 2 * UNR < KS) load(s0 + 2 * UNR, a4[0], b4[0]);
         math(a4[1], b4[1]);
     }
-    // the fp64 product's lane (col, q) holds rows q + 4v of tile mt = (group 4mt + v, j1 = q),
-    // column r1 = 16rt + col
-    double* D1 = dg1 + rec_field64(rw, RW_O1) + q * R + col;
+    // the fp64 product's lane (col, q) holds rows q + 4v of tile mt, that is
+    // (group, j1) of row 16mt + q + 4v, column r1 = 16rt + col
+    double* D1 = dg1 + rec_field64(rw, RW_O1) + col;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (4 * mt + v < ng) {
-                double* dst = D1 + (int64_t)__builtin_amdgcn_readlane(rw, RW_I1 + 4 * mt + v) * N1 * R;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[mt][rt][v]);
+        for (int v = 0; v < 4; ++v) {
+            const int rho = 16 * mt + q + 4 * v, gi = rho / N1, j1 = rho % N1;
+            int32_t i1;
+            if constexpr (N1 >= 4) {   // gi = (16mt + 4v) / N1: wave-uniform
+                if ((16 * mt + 4 * v) / N1 >= ng) continue;
+                i1 = __builtin_amdgcn_readlane(rw, RW_I1 + (16 * mt + 4 * v) / N1);
+            } else {
+                i1 = __shfl(rw, RW_I1 + min(gi, kFwdBatch - 1));
+                if (gi >= ng) continue;
             }
+            double* dst = D1 + (int64_t)i1 * N1 * R + j1 * R;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) atomicAdd(dst + 16 * rt, acc[mt][rt][v]);
+        }
 }
 
 // Fused SGD (go.sgd): dg1/dg2/dg3 are the cores g1/g2/g3 themselves. Every
@@ -1165,14 +1190,33 @@ bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
     if (p->g2_overlap) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
-    return p->n1 == 4 && p->n3 == 4 && p->R == 32 && (p->n2 == 8 || p->n2 == 4);
+    return mfma_shape(p->n1, p->n2, p->n3, p->R, true);
+}
+
+// One entry of the shape list: launches the backward when the plan has this
+// shape (instantiated only for the shapes the backward's kernels serve).
+template <int N1, int N2, int R, int N3, bool BW>
+static bool bwd_case(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
+                     const float* gout, float* dg1, float* dg2, float* dg3, bool kept, GradOut go,
+                     hipStream_t s, tt_status* st) {
+    if constexpr (BW) {
+        if (p->n1 == N1 && p->n2 == N2 && p->n3 == N3 && p->R == R) {
+            *st = launch_bwd_mfma<N1, N2, R, N3>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
+            return true;
+        }
+    }
+    return false;
 }
 
 static tt_status launch_bwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                             const float* gout, float* dg1, float* dg2, float* dg3, bool kept, GradOut go,
                             hipStream_t s) {
-    if (p->n2 == 8) return launch_bwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
-    return launch_bwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
+    tt_status st = TT_ERR_UNSUPPORTED;
+#define TT_BWD_CASE(a, b, c, d, bw) \
+    if (bwd_case<a, b, d, c, bw>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s, &st)) return st;
+    TT_MFMA_SHAPES(TT_BWD_CASE)
+#undef TT_BWD_CASE
+    return st;
 }
 
 }  // namespace tt

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256) void k_fwd_generic(
 
 
 // ---------------------------------------------------------------------------
-// Matrix-core path for the common shapes (n1 = 4, n3 = 4, shared n2 and R).
+// Matrix-core path for the shapes the library is built for (every table of
+// the plan with the same n1, n2, n3 and R).
 //
 // One workgroup (4 waves) per batch of up to kFwdBatch prefix groups of one
 // (table, i2) slice: groups that share a G2 slice are adjacent in key order.
@@ -104,11 +105,13 @@ struct FwdArgs {
     int32_t* claims;       // [kFwdCounters][32]: batch claim counters (zero at the launch)
 };
 
-// The runs of one batch: tiles of LK = 4 runs of one group. The suffix
+// The runs of one batch: tiles of LK = 16/n3 runs of one group. The suffix
 // product of a tile is E^T = G3[i3]^T P^T: rows (run, j3), columns p, K = r2.
-// Lane (col, q) feeds G3 of run col/4 as the A operand and P row 16mt + col as
-// the B operand, and receives E[run q][p = 16mt + col][j3 = 0..3]: four
-// consecutive floats of that run's row, written with one 16-byte store.
+// Lane (col, q) feeds G3 of run col/n3 (its column j3 = col%n3) as the A
+// operand and P row 16mt + col as the B operand, and receives rows 4q..4q+3
+// of the tile's E^T at p = 16mt + col: with n3 >= 4, four consecutive j3 of
+// one run (one 16-byte store); with n3 = 2, two j3 of each of two runs; with
+// n3 = 1, one value of each of four runs.
 // Wave w takes a contiguous range of tiles (consecutive tiles mostly share a
 // group, so P is reloaded once per group). Every wave forms the batch's tile
 // prefix itself, in registers (lane g: first tile of group g), so begin() can
@@ -119,7 +122,7 @@ struct FwdArgs {
 // stores: loads and stores share one in-order completion counter, so a load
 // can only be waited for alone if every memory access issued after it is
 // certain to have been issued. The loop body therefore holds no conditional
-// access (lanes past the group's last run store to a spare row, the
+// access (lanes past the group's last run store to spare rows, the
 // look-ahead tile is clamped to the last one, run i3 values come from LDS),
 // it is unrolled by two with ping-pong operand sets, and no register that a
 // load is still filling is ever copied.
@@ -128,15 +131,18 @@ struct FwdTiles {
     using B = PrefixBatch<N1, N2, R>;
     static constexpr int NP = B::NP, D = NP * N3, KS = B::KS, AS = B::AS, WAVES = B::WAVES;
     static constexpr int MT = NP / 16, LK = 16 / N3;
+    static constexpr int RPL = N3 >= 4 ? 1 : 4 / N3;   // runs of a lane's four results
+    static constexpr int VPR = 4 / RPL;                // results per run (consecutive j3)
+    static_assert(16 % N3 == 0 && LK <= kStageSpare, "suffix tile shape");
     struct Ids {
         int g;
-        int32_t r;         // stage row of run q of the tile (a spare row past the group's end)
-        int32_t i3;        // i3 of run lk of the tile (run 0's past the end)
+        int32_t r[RPL];    // stage rows of the lane's result runs (spare rows past the group's end)
+        int32_t i3;        // i3 of the lane's operand run col/n3 (the tile's first run's past the end)
     };
     struct Ops {
         int g;
-        int32_t r;
-        floatx4 bv[KS / 4];   // G3[i3 of run lk][r2 = KS*q + 4h + u][j3], K = r2
+        int32_t r[RPL];
+        floatx4 bv[KS / 4];   // G3[i3 of run col/n3][j3 = col%n3][r2 = KS*q + 4h + u], K = r2
     };
     int32_t tpl;           // lane g <= ng: the batch's first tile of group g (lane ng: the tile count)
     int t0, n, gs;
@@ -152,12 +158,18 @@ struct FwdTiles {
         while (tp(gs + 1) <= tt) ++gs;
         o.g = gs;
         const int32_t rb = sRb[gs] + LK * (tt - tp(gs)), re = sRb[gs + 1];   // relative to rb0
-        o.r = rb + q < re ? c.rb0 + rb + q : (int32_t)a.L + q;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+            const int lr = (4 * q) / N3 + u;
+            o.r[u] = rb + lr < re ? c.rb0 + rb + lr : (int32_t)a.L + lr;
+        }
         o.i3 = sI3[rb + lk < re ? rb + lk : rb];
     }
     __device__ __forceinline__ void load_ops(const FwdArgs& a, const BatchCtx& c, const Ids& o, Ops& x) {
         const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4, j3 = col % N3;
-        x.g = o.g; x.r = o.r;
+        x.g = o.g;
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) x.r[u] = o.r[u];
         const floatx4* gb = reinterpret_cast<const floatx4*>(a.g3t + c.o3 + (int64_t)o.i3 * R * N3 + j3 * R + KS * q);
 #pragma unroll
         for (int h = 0; h < KS / 4; ++h) x.bv[h] = gb[h];
@@ -193,6 +205,7 @@ struct FwdTiles {
                                         const int32_t* sI3) {
         if (n <= 0) return;
         const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
+        const int jb = N3 >= 4 ? (4 * q) % N3 : 0;   // first j3 of the lane's results
         int cur = -1;
         float bp[MT][KS];      // P[16mt + col][KS*q + s2]
         auto step = [&](int k, Ops& C, Ops& Nx, Ids& Inew, const Ids& Inext) {
@@ -205,14 +218,24 @@ struct FwdTiles {
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) bp[mt][s2] = sP[(cur * NP + 16 * mt + col) * AS + KS * q + s2];
             }
-            float* dst = a.stage + (int64_t)C.r * D + col * N3;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 floatx4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < KS; ++s2)
                     e = __builtin_amdgcn_mfma_f32_16x16x4f32(C.bv[s2 / 4][s2 % 4], bp[mt][s2], e, 0, 0, 0);
-                *reinterpret_cast<floatx4*>(dst + 16 * mt * N3) = e;
+#pragma unroll
+                for (int u = 0; u < RPL; ++u) {
+                    float* dst = a.stage + (int64_t)C.r[u] * D + (16 * mt + col) * N3 + jb;
+                    if constexpr (VPR == 4) {
+                        *reinterpret_cast<floatx4*>(dst) = e;
+                    } else if constexpr (VPR == 2) {
+                        typedef float floatx2 __attribute__((ext_vector_type(2)));
+                        *reinterpret_cast<floatx2*>(dst) = floatx2{e[2 * u], e[2 * u + 1]};
+                    } else {
+                        *dst = e[u];
+                    }
+                }
             }
         };
         int k = 0;
@@ -239,7 +262,7 @@ template <int N1, int N2, int R, int N3, bool KEEP>
 __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, const int32_t* __restrict__ ctrl) {
     using B = PrefixBatch<N1, N2, R>;
     constexpr int SG = B::SG;
-    static_assert(N3 == 4 && B::NP % 16 == 0 && 64 * B::WAVES == 256, "shape");
+    static_assert(B::NP % 16 == 0 && 64 * B::WAVES == 256, "shape");
     __shared__ __attribute__((aligned(16))) float sU[B::U_FLOATS];   // prologue, then P
     __shared__ int32_t sRb[SG + 1];
     __shared__ int32_t sClaim[2];
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
     if (h == 0) *reinterpret_cast<floatx4*>(out + q * D + c4) = acc;
 }
 
-template <int N1, int N2, int R, int N3>
+template <int N1, int N2, int R, int N3, bool BW>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, bool keep, hipStream_t s) {
     int32_t* fwd_claims = p->at<int32_t>(p->lay.claims) + 32 * kRunCounters;
@@ -345,12 +368,17 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         TT_LAUNCH_CHECK();
         const size_t lds = sizeof(int32_t) * (size_t)kFwdBatch * (size_t)p->M3;
         const int64_t grid = batch_grid(p->n_fb, kFwdPersistBlocks);
-        if (keep)
-            TT_LAUNCH(p, "k_fwd_batch_keep", s, (k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
-                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
-        else
+        bool kept = false;
+        if constexpr (BW) {
+            if (keep) {
+                TT_LAUNCH(p, "k_fwd_batch_keep", s, (k_fwd_batch<N1, N2, R, N3, true>), dim3((unsigned)grid),
+                          dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
+                kept = true;
+            }
+        }
+        if (!kept)
             TT_LAUNCH(p, "k_fwd_batch", s, (k_fwd_batch<N1, N2, R, N3, false>), dim3((unsigned)grid),
-                               dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
+                      dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s, a, p->n_fb, p->ctrl());
         TT_LAUNCH_CHECK();
     }
     if (p->TB > 0) {
@@ -362,22 +390,31 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     return TT_OK;
 }
 
+bool mfma_shape(int n1, int n2, int n3, int R, bool backward) {
+#define TT_SHAPE_IS(a, b, c, d, bw) \
+    if (n1 == a && n2 == b && n3 == c && R == d) return bw || !backward;
+    TT_MFMA_SHAPES(TT_SHAPE_IS)
+#undef TT_SHAPE_IS
+    return false;
+}
+
 // The plan's shape and the cores' alignment admit the matrix-core kernels.
 bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
     // the batch's run i3 list is staged in LDS
     if ((int64_t)sizeof(int32_t) * kFwdBatch * p->M3 > kMaxBatchI3Bytes) return false;
-    const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
-    return n1 == 4 && n3 == 4 && ((n2 == 8 && R == 32) || (n2 == 4 && R == 32) || (n2 == 4 && R == 16));
+    return mfma_shape(p->n1, p->n2, p->n3, p->R, false);
 }
 
 static tt_status launch_fwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                             float* out, bool keep, hipStream_t s) {
-    const int n2 = p->n2, R = p->R;
-    if (n2 == 8 && R == 32) return launch_fwd_mfma<4, 8, 32, 4>(p, g1, g2, g3, out, keep, s);
-    if (n2 == 4 && R == 32) return launch_fwd_mfma<4, 4, 32, 4>(p, g1, g2, g3, out, keep, s);
-    return launch_fwd_mfma<4, 4, 16, 4>(p, g1, g2, g3, out, false, s);
+    const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
+#define TT_FWD_CASE(a, b, c, d, bw) \
+    if (n1 == a && n2 == b && n3 == c && R == d) return launch_fwd_mfma<a, b, d, c, bw>(p, g1, g2, g3, out, keep, s);
+    TT_MFMA_SHAPES(TT_FWD_CASE)
+#undef TT_FWD_CASE
+    return TT_ERR_UNSUPPORTED;
 }
 
 }  // namespace tt

@@ -36,7 +36,7 @@ inline unsigned persistent_grid(int blocks_per_cu) { return (unsigned)(256 * blo
 // then issues every load the batch needs at once (G2 slice and G1 rows as
 // coalesced 16-byte loads, the run i3 list), so the prologue costs two
 // dependent round trips. The G2 slice and the G1 rows go to LDS; every group's
-// P = G1[i1] x G2[i2] is then formed as one (4*batch) x (n2*R) x R product on
+// P = G1[i1] x G2[i2] is then formed as one (n1*batch) x (n2*R) x R product on
 // the matrix cores, and P is written over the same LDS (sP[g][p][AS]).
 
 struct BatchCtx {
@@ -57,7 +57,7 @@ struct PrefixBatch {
     static constexpr int P_FLOATS = SG * NP * AS;
     // LDS of the prologue: G2 slice then G1 rows; P is written over them
     static constexpr int U_FLOATS = (G2_FLOATS + G1_FLOATS) > P_FLOATS ? (G2_FLOATS + G1_FLOATS) : P_FLOATS;
-    static_assert(N1 == 4 && MR % 16 == 0 && N2R % 16 == 0 && R % 4 == 0, "prefix batch shape");
+    static_assert(16 % N1 == 0 && MR % 16 == 0 && N2R % 16 == 0 && R % 16 == 0, "prefix batch shape");
 };
 
 // The record of batch b of the list as one word per lane (lane k holds word k
@@ -238,7 +238,7 @@ __device__ __forceinline__ void batch_prefix(int32_t rw, const int32_t* __restri
     if (tid <= kFwdBatch) sRb[tid] = rbw;
     __syncthreads();
     // wave w: column tiles nt = w + WAVES*k, every row tile mt (row 16mt + i =
-    // group 4mt + i/N1, j1 = i%N1); K = r1
+    // group (16mt + i)/N1, j1 = (16mt + i)%N1); K = r1
     floatx4 acc[NTW][MTP];
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
@@ -263,10 +263,14 @@ __device__ __forceinline__ void batch_prefix(int32_t rw, const int32_t* __restri
         if (nt < NT2) {
 #pragma unroll
             for (int mt = 0; mt < MTP; ++mt) {
-                // C row 4q+v2 = (group 4mt+q, j1 v2); column cc = 16nt + col = (j2, r2)
-                const int gi = 4 * mt + q, cc = 16 * nt + col;
+                // C row 4q+v2 of tile mt = (group, j1) of row 16mt + 4q + v2;
+                // column cc = 16nt + col = (j2, r2)
+                const int cc = 16 * nt + col;
 #pragma unroll
-                for (int v2 = 0; v2 < 4; ++v2) sP[(gi * NP + v2 * N2 + cc / R) * AS + cc % R] = acc[k][mt][v2];
+                for (int v2 = 0; v2 < 4; ++v2) {
+                    const int rho = 16 * mt + 4 * q + v2, gi = rho / N1, j1 = rho % N1;
+                    sP[(gi * NP + j1 * N2 + cc / R) * AS + cc % R] = acc[k][mt][v2];
+                }
             }
         }
     }

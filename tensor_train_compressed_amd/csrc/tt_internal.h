@@ -41,10 +41,19 @@ enum CtrlSlot : int {
 };
 
 constexpr int kXcds = 8;
+// Table shapes (n1, n2, n3, R) the matrix-core kernels are built for, every
+// table of a plan having the same one; the last field says whether the
+// backward's matrix-core kernels serve the shape too (they need n3 = 4 and
+// a dim that is a multiple of 64). Other shapes take the generic kernels.
+#define TT_MFMA_SHAPES(X)                                                                         \
+    X(4, 8, 4, 32, true) X(4, 4, 4, 32, true) X(4, 4, 4, 16, true) X(2, 8, 4, 32, true)           \
+    X(8, 4, 4, 32, true) X(4, 4, 4, 64, true) X(4, 4, 8, 32, false) X(4, 4, 2, 32, false)         \
+    X(4, 4, 1, 32, false)
+
 // Forward work unit: up to this many prefix groups of one (table, i2) slice.
 constexpr int kFwdBatch = 8;
 // Spare stage rows after the L run rows (targets of inactive lanes' stores).
-constexpr int kStageSpare = 4;
+constexpr int kStageSpare = 16;
 // Workgroups (four waves each) of the persistent forward batch kernel: three
 // per CU (the kernel's registers and LDS allow no more).
 constexpr int kFwdPersistBlocks = 3 * 256;
@@ -289,6 +298,7 @@ tt_status forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const 
 
 // Whether the plan's calls take the matrix-core kernels with these cores
 // (forward.hip, backward.hip).
+bool mfma_shape(int n1, int n2, int n3, int R, bool backward);
 bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
 bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2);
 
