@@ -221,56 +221,147 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
 
 // ---------------------------------------------------------------------------
 // split
+//
+// Workgroups 0 .. n_tiles-1 take one tile of kSortTile lookups each (the
+// sort's tiles), kSortItems per thread: each lookup's table, digits and
+// prefix key, and the tile's counts of the sort key's lowest digit (the
+// first radix pass's histogram, as k_radix_hist writes it for the later
+// passes). The workgroups after them, running alongside, take kSortThreads
+// offsets, kSortTile keys and kSortTile G3 buckets each: bag_start and the
+// offsets check; every wave labels the lookups of its 64 bags, consecutive
+// lanes on consecutive lookups (lane j holds bag j's offset; a lookup's bag is
+// the last lane whose offset is not past it, found by a binary search over
+// the lanes); keys marked absent; bucket run counters cleared.
 
-__global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
-                                               const int64_t* __restrict__ off, int64_t L,
-                                               int64_t TB, int64_t B,
-                                               const TabDev* __restrict__ desc,
-                                               int32_t* __restrict__ key, int32_t* __restrict__ i3o,
-                                               int32_t* __restrict__ bag_of,
-                                               int32_t* __restrict__ bag_start,
-                                               int32_t* __restrict__ ckey, int32_t M3,
-                                               int32_t* ctrl, int32_t* __restrict__ key_start,
-                                               int64_t K, int32_t* __restrict__ i3cnt, int32_t n3cnt) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < K) key_start[i] = -1;   // k_gather records each present key's first position
-    if (i < n3cnt) i3cnt[i * kI3Pad] = 0;   // k_runs counts the runs of each i3
-    if (i <= TB) {
-        const int64_t a = off[i];
-        bag_start[i] = (int32_t)(a < 0 ? 0 : (a > L ? L : a));
-        bool bad = (i == 0 && a != 0) || (i == TB && a != L) || (i < TB && off[i + 1] < a);
-        if (bad) atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_OFFSETS);
+__device__ __forceinline__ uint32_t sort_digit(int32_t k, int shift) {
+    return ((uint32_t)k >> shift) & (kRadixBins - 1);
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restrict__ idx,
+                                                        const int64_t* __restrict__ off, int64_t L,
+                                                        int64_t TB, int64_t B,
+                                                        const TabDev* __restrict__ desc,
+                                                        int32_t* __restrict__ key, int32_t* __restrict__ i3o,
+                                                        int32_t* __restrict__ bag_of,
+                                                        int32_t* __restrict__ bag_start,
+                                                        int32_t* __restrict__ ckey, int32_t M3,
+                                                        int32_t* ctrl, int32_t* __restrict__ key_start,
+                                                        int64_t K, int32_t* __restrict__ i3cnt, int32_t n3cnt,
+                                                        int64_t n_tiles, int64_t hstride,
+                                                        uint32_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[kSortWaves][kRadixBins];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((int64_t)blockIdx.x >= n_tiles) {
+        const int64_t x = blockIdx.x - n_tiles;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const int64_t i = x * kSortTile + j * kSortThreads + threadIdx.x;
+            if (i < K) key_start[i] = -1;              // k_gather records each present key's first position
+            if (i < n3cnt) i3cnt[i * kI3Pad] = 0;       // k_runs counts the runs of each bucket
+        }
+        const int64_t q0 = x * kSortThreads + 64 * w;   // this wave's bags q0 .. q0+63
+        if (q0 > TB) return;   // wave-uniform
+        const int64_t i = q0 + lane;
+        const int64_t x0 = off[i < TB ? i : TB], x1 = off[i < TB ? i + 1 : TB];
+        int64_t a = L, an = L;   // bag i's offset and the next one, clamped into [0, L]
+        if (i <= TB) {
+            a = x0 < 0 ? 0 : (x0 > L ? L : x0);
+            bag_start[i] = (int32_t)a;
+            const int64_t xn = i < TB ? x1 : L;
+            an = xn < 0 ? 0 : (xn > L ? L : xn);
+            const bool bad = (i == 0 && x0 != 0) || (i == TB && x0 != L) || (i < TB && xn < x0);
+            if (bad) atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_OFFSETS);
+        }
+        if (q0 >= TB) return;
+        // lookups [lo, hi) belong to these bags (bags past TB start at L)
+        const int32_t o = (int32_t)a;
+        const int32_t lo = __builtin_amdgcn_readfirstlane(o);
+        const int32_t hi = __builtin_amdgcn_readlane((int32_t)an, 63);
+        for (int32_t l0 = lo; l0 < hi; l0 += 64) {
+            const int32_t l = l0 + lane;
+            int jj = 0;   // last lane whose offset is <= l (lane 0's is lo <= l)
+#pragma unroll
+            for (int st = 32; st >= 1; st >>= 1) {
+                const int32_t y = __shfl(o, jj + st);
+                if (y <= l) jj += st;
+            }
+            if (l < hi) bag_of[l] = (int32_t)(q0 + jj);
+        }
+        return;
     }
-    if (i < TB) {
-        // bag i labels its own lookups (clamped: bad offsets may leave some
-        // unlabelled; their readers clamp the label into [0, TB))
-        const int64_t a = min(max(off[i], (int64_t)0), L);
-        const int64_t b = min(max(off[i + 1], a), L);
-        for (int64_t l = a; l < b; ++l) bag_of[l] = (int32_t)i;
-    }
-    if (i >= L) return;
-    // table of lookup i: last t with off[t*B] <= i (in range for any offsets)
+    const int64_t tile = blockIdx.x;
+    for (int i = lane; i < kRadixBins; i += 64) cnt[w][i] = 0;   // own row, so no barrier
+    // lookups: wave w takes the w-th sixteenth of the tile, 64 at a time;
+    // every index load is issued before the first is used
     const int64_t T = TB / B;
-    int64_t lo = 0, hi = T;
-    while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (off[mid * B] <= i) lo = mid; else hi = mid;
+    const int64_t base = tile * kSortTile + (int64_t)w * (kSortTile / kSortWaves);
+    int64_t xv[kSortItems];
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const int64_t e = base + slot * 64 + lane;
+        xv[slot] = idx[e < L ? e : L - 1];   // L > 0: there is a lookup tile
     }
-    const TabDev d = desc[lo];
-    int64_t x = idx[i];
-    if (x < 0 || x >= d.N) {
-        atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_INDEX);
-        x = 0;
+
+    // one lookup: its key, sort key and i3 (a bad index reads as row 0)
+    auto split_one = [&](int64_t e, int64_t x, const TabDev& dd) {
+        if (x < 0 || x >= dd.N) {
+            atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_INDEX);
+            x = 0;
+        }
+        const uint32_t xi = (uint32_t)x;
+        const uint32_t r3 = xi % (uint32_t)dd.m3;
+        const uint32_t p = xi / (uint32_t)dd.m3;
+        const uint32_t r2 = p % (uint32_t)dd.m2;
+        const uint32_t r1 = p / (uint32_t)dd.m2;
+        const int32_t k = dd.key_base + (int32_t)(r2 * (uint32_t)dd.m1 + r1);
+        const int32_t ck = k * M3 + (int32_t)r3;
+        key[e] = k;
+        ckey[e] = ck;
+        i3o[e] = (int32_t)r3;
+        return sort_digit(ck, 0);
+    };
+    uint32_t dg[kSortItems];
+    if (T == 1) {   // one table: its descriptor read once (uniform)
+        const TabDev d0 = desc[0];
+#pragma unroll
+        for (int slot = 0; slot < kSortItems; ++slot) {
+            const int64_t e = base + slot * 64 + lane;
+            dg[slot] = e < L ? split_one(e, xv[slot], d0) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int slot = 0; slot < kSortItems; ++slot) {
+            const int64_t e = base + slot * 64 + lane;
+            dg[slot] = 0u;
+            if (e < L) {
+                // table of lookup e: last t with off[t*B] <= e (in range for any offsets)
+                int64_t lo = 0, hi = T;
+                while (hi - lo > 1) {
+                    const int64_t mid = (lo + hi) >> 1;
+                    if (off[mid * B] <= e) lo = mid; else hi = mid;
+                }
+                dg[slot] = split_one(e, xv[slot], desc[lo]);
+            }
+        }
     }
-    const uint32_t xi = (uint32_t)x;
-    const uint32_t r3 = xi % (uint32_t)d.m3;
-    const uint32_t p = xi / (uint32_t)d.m3;
-    const uint32_t r2 = p % (uint32_t)d.m2;
-    const uint32_t r1 = p / (uint32_t)d.m2;
-    const int32_t k = d.key_base + (int32_t)(r2 * (uint32_t)d.m1 + r1);
-    key[i] = k;
-    ckey[i] = k * M3 + (int32_t)r3;
-    i3o[i] = (int32_t)r3;
+#pragma unroll
+    for (int slot = 0; slot < kSortItems; ++slot) {
+        const bool valid = base + slot * 64 + lane < L;
+        const uint64_t peers = match_digit(dg[slot], __ballot(valid));
+        if (valid && popc_below(peers) == 0) cnt[w][dg[slot]] += (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kRadixBins; i += kSortThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) c += cnt[ww][i];
+        hist[(int64_t)i * hstride + tile] = c;
+    }
+    if (tile == n_tiles - 1) {
+        const int64_t pad = hstride - n_tiles;
+        for (int64_t i = threadIdx.x; i < pad * kRadixBins; i += kSortThreads)
+            hist[(i / pad) * hstride + n_tiles + i % pad] = 0u;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -280,10 +371,6 @@ __global__ __launch_bounds__(256) void k_split(const int64_t* __restrict__ idx,
 // w-th sixteenth, 64 at a time, so ranks in (wave, slot, lane) order are ranks
 // in sequence order. Digit counts are kept per wave (no LDS atomics: in a
 // slot, one leader lane per distinct digit adds its peers' count).
-
-__device__ __forceinline__ uint32_t sort_digit(int32_t k, int shift) {
-    return ((uint32_t)k >> shift) & (kRadixBins - 1);
-}
 
 // Per-tile digit counts: hist[d * hstride + tile]; the last tile also zeroes
 // the padding columns [n_tiles, hstride).
@@ -1230,14 +1317,17 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     int32_t* key = p->at<int32_t>(lay.key);
     int32_t* i3 = p->at<int32_t>(lay.i3);
     int32_t* bag = p->at<int32_t>(lay.bag_of);
-    // split (also checks the offsets and marks every key absent; one thread per
-    // lookup, per offset and per key)
+    // split (also checks the offsets, labels the bags, marks every key absent
+    // and counts the first radix pass's digits per tile)
     {
-        const int64_t n = std::max<int64_t>(std::max<int64_t>(std::max<int64_t>(L, p->TB + 1), K), n3cnt);
-        TT_LAUNCH(p, "k_split", s, k_split, dim3(grid_for(n, 256)), dim3(256), 0, s, indices, offsets, L,
-                           p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
-                           p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3,
-                           ctrl, p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt);
+        const int64_t nx = std::max<int64_t>(std::max<int64_t>((p->TB + 1 + kSortThreads - 1) / kSortThreads,
+                                                               (K + kSortTile - 1) / kSortTile),
+                                             ((int64_t)n3cnt + kSortTile - 1) / kSortTile);
+        TT_LAUNCH(p, "k_split", s, k_split, dim3((unsigned)(lay.n_tiles + nx)), dim3(kSortThreads), 0,
+                  s, indices, offsets, L, p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
+                  p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3, ctrl,
+                  p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt, lay.n_tiles, lay.hstride,
+                  p->at<uint32_t>(lay.hist));
         if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
     }
     // stable radix sort: key -> (skey, perm)
@@ -1254,9 +1344,11 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
             int32_t* vout = p->at<int32_t>(to_final ? lay.sort_v1 : lay.sort_v0);
             int32_t* bout = p->at<int32_t>(to_final ? lay.sort_b1 : lay.sort_b0);
             const int shift = pass * kRadixBits;
-            TT_LAUNCH(p, "k_radix_hist", s, k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
-                               kin, L, shift, lay.n_tiles, lay.hstride, hist);
-            if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
+            if (pass > 0) {   // the first pass's counts come from k_split
+                TT_LAUNCH(p, "k_radix_hist", s, k_radix_hist, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0, s,
+                          kin, L, shift, lay.n_tiles, lay.hstride, hist);
+                if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
+            }
             if (lay.n_tiles <= kDirectTiles) {
                 TT_LAUNCH(p, "k_radix_scatter", s, k_radix_scatter<true>, dim3((unsigned)lay.n_tiles), dim3(kSortThreads), 0,
                                    s, kin, vin, bin, L, (int32_t)p->TB, shift, lay.hstride, hist, kout, vout, bout);
