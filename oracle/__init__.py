@@ -18,6 +18,11 @@ Parity status of each function (pins live in tests/, marked "not gpu"):
   backward     pinned: exact adjoint identity against the forward oracle,
                brute-force chain rule on tiny shapes, rank-1 closed form
   sgd          pinned by its arithmetic definition on hand-made values
+  cache        (hot-row cache) pinned: an empty hot set changes nothing; a hot
+               set holding the rows' own TT values reproduces the plain
+               forward; the adjoint identity for dW against the forward; the
+               cores' gradients add up with those of the hot lookups alone to
+               the plain backward
   planner      pinned: exact digit identity over every row of a table,
                pure-Python brute-force stable sort on small inputs, and the
                partition invariants of groups and chunks
@@ -165,3 +170,74 @@ def forward_problem(p, bags=None) -> np.ndarray:
 def backward_problem(p, mask=None):
     return backward(p.tables, p.g1, p.g2, p.g3, p.goff, p.indices, p.offsets, p.batch,
                     p.grad_out, mask)
+
+
+# ---------------------------------------------------------------------------
+# Hot-row cache (TT-Rec abstract: caching strategies for the embedding
+# lookups; TT-Rec news article, method paragraph: a cache structure that uses
+# the skewed, sparse feature distribution and changes accuracy). Reading: a
+# set of hot rows per table is kept uncompressed, as trainable vectors W[s];
+# a lookup of a hot row takes W[s] in place of the TT contraction, its grad
+# row goes to dW[s], and the TT cores get gradients from the other lookups
+# only. Hot entry s is the pair (hot_table[s], hot_row[s]); when a pair is
+# listed twice its first slot serves it (the later slot gets no lookups).
+
+def _bag_of(offsets: np.ndarray, L: int) -> np.ndarray:
+    off = np.asarray(offsets, dtype=np.int64)
+    return np.repeat(np.arange(off.size - 1, dtype=np.int64), np.diff(off))[:L]
+
+
+def cache_slots(p, hot_table, hot_row) -> np.ndarray:
+    """Slot of every lookup's row in the hot set (int64 [L]; -1: not hot)."""
+    bag = _bag_of(p.offsets, p.L)
+    t = bag // p.batch
+    key = t * (np.int64(1) << 40) + np.asarray(p.indices, dtype=np.int64)
+    hk = np.asarray(hot_table, dtype=np.int64) * (np.int64(1) << 40) + np.asarray(hot_row, dtype=np.int64)
+    if hk.size == 0:
+        return np.full(p.L, -1, np.int64)
+    uk, first = np.unique(hk, return_index=True)   # first slot of each distinct pair
+    pos = np.searchsorted(uk, key)
+    pos_c = np.minimum(pos, uk.size - 1)
+    hit = uk[pos_c] == key
+    return np.where(hit, first[pos_c], -1).astype(np.int64)
+
+
+def forward_cached(p, hot_table, hot_row, W) -> np.ndarray:
+    """Pooled outputs (float64) with the hot rows taken from W [n_hot][D]."""
+    slot = cache_slots(p, hot_table, hot_row)
+    bag = _bag_of(p.offsets, p.L)
+    cold = slot < 0
+    TB = p.T * p.batch
+    counts = np.bincount(bag[cold], minlength=TB)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    out = forward(p.tables, p.g1, p.g2, p.g3, p.goff, np.asarray(p.indices)[cold], off, p.batch)
+    np.add.at(out, bag[~cold], np.asarray(W, dtype=np.float64)[slot[~cold]])
+    return out
+
+
+def backward_cached(p, hot_table, hot_row, n_hot: int):
+    """(dG1, dG2, dG3, dW) in float64: the cores' gradients from the lookups
+    of rows outside the hot set, and dW [n_hot][D] from the hot ones."""
+    slot = cache_slots(p, hot_table, hot_row)
+    bag = _bag_of(p.offsets, p.L)
+    cold = slot < 0
+    d1, d2, d3 = backward_problem(p, mask=cold.astype(np.uint8))
+    dW = np.zeros((n_hot, p.dim), np.float64)
+    np.add.at(dW, slot[~cold], np.asarray(p.grad_out, dtype=np.float64)[bag[~cold]])
+    return d1, d2, d3, dW
+
+
+def materialise_rows(p, hot_table, hot_row) -> np.ndarray:
+    """TT rows of the listed (table, row) pairs (float64 [n][D]): the forward
+    of one-lookup bags."""
+    ht = np.asarray(hot_table, dtype=np.int64)
+    hr = np.asarray(hot_row, dtype=np.int64)
+    out = np.empty((ht.size, p.dim), np.float64)
+    for t in np.unique(ht):
+        sel = np.nonzero(ht == t)[0]
+        tab = [p.tables[t]]
+        goff = np.asarray(p.goff).reshape(-1, 3)[t:t + 1]
+        o = forward(tab, p.g1, p.g2, p.g3, goff, hr[sel], np.arange(sel.size + 1, dtype=np.int64),
+                    sel.size)
+        out[sel] = o
+    return out
