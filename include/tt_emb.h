@@ -65,8 +65,10 @@ typedef enum {
     TT_ERR_DEVICE_FLAG = -5,  /* returned by tt_emb_get_error when the flag is set   */
     TT_ERR_STALE = -6,        /* tt_emb_backward_kept: the token does not name the   */
                               /* products the plan holds (see below)                 */
-    TT_ERR_SCRATCH = -7       /* tt_emb_forward_scratch: the batch needs more than   */
+    TT_ERR_SCRATCH = -7,      /* tt_emb_forward_scratch: the batch needs more than   */
                               /* the library's static scratch buffer holds           */
+    TT_ERR_CACHE = -8         /* a plan with a hot-row cache given to a call without */
+                              /* the hot rows, or the reverse (see below)            */
 } tt_status;
 
 /* Device error flag bits (tt_emb_get_error). */
@@ -282,6 +284,59 @@ typedef struct {
 tt_status tt_emb_set_timing(tt_emb_plan_t plan, int32_t enable);
 tt_status tt_emb_kernel_times(tt_emb_plan_t plan, tt_emb_kernel_time* out, int32_t max,
                               int32_t* count, void* stream);
+
+/* Hot-row cache. TT-Rec pairs the TT table with caching for the lookups
+ * (TT-Rec abstract: caching strategies; news article, method paragraph: a
+ * cache structure that exploits the skewed sparse-feature distribution and
+ * changes accuracy). Here a set of hot rows is kept uncompressed, as
+ * trainable fp32 vectors: hot entry s is the pair (hot_table[s],
+ * hot_row[s]) with its vector W[s] (D floats, a caller buffer [n_hot][D]).
+ * A lookup of a hot row takes W[s] in place of the TT contraction; in the
+ * backward its grad row goes to dW[s], and the cores get gradients from the
+ * other lookups only. A pair listed twice is served by its first slot (the
+ * later slot gets no lookups); a pair naming no valid row matches nothing.
+ * Which rows are hot, and how W[s] starts (for instance the row's TT value,
+ * from a forward of one-lookup bags), is the caller's choice.
+ *
+ * The cache is a device hash table in caller memory: tt_emb_cache_bytes(n)
+ * bytes (256-byte aligned), filled by tt_emb_cache_build from device arrays
+ * hot_table (int32 [n_hot]) and hot_row (int64 [n_hot]) on `stream`; it is
+ * read by tt_emb_plan_cached (and must stay unchanged while plans made with
+ * it are used). A plan made with a cache takes only the _cached compute calls
+ * (the others return TT_ERR_CACHE), and only shapes with the matrix-core
+ * kernels in both directions (tt_emb_query_paths; else TT_ERR_UNSUPPORTED at
+ * the compute call). n_hot = 0 is allowed and changes nothing. */
+size_t tt_emb_cache_bytes(int64_t n_hot);
+tt_status tt_emb_cache_build(const int32_t* hot_table, const int64_t* hot_row, int64_t n_hot,
+                             void* cache, size_t cache_bytes, void* stream);
+
+/* As tt_emb_plan, for a batch served with the hot-row cache `cache` of
+ * n_hot entries (built by tt_emb_cache_build with the same n_hot). */
+tt_status tt_emb_plan_cached(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                             const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                             const void* cache, int64_t n_hot, void* workspace,
+                             size_t workspace_bytes, void* stream, tt_emb_plan_t* plan_out);
+
+/* Forward with the hot rows W (fp32 [n_hot][D], read only). kept_token NULL:
+ * as tt_emb_forward; non-NULL: as tt_emb_forward_train (the token names the
+ * kept products). */
+tt_status tt_emb_forward_cached(tt_emb_plan_t plan, const float* g1, const float* g2,
+                                const float* g3, const float* hot_w, float* out,
+                                uint64_t* kept_token, void* stream);
+
+/* Backward: dG1..dG3 as tt_emb_backward (from the lookups of rows outside
+ * the hot set) and dW (fp32 [n_hot][D], every row written: zero for hot rows
+ * the batch does not look up). kept_token 0: P is formed again; otherwise
+ * as tt_emb_backward_kept (TT_ERR_STALE for a stale token). */
+tt_status tt_emb_backward_cached(tt_emb_plan_t plan, uint64_t kept_token, const float* g1,
+                                 const float* g2, const float* g3, const float* grad_out,
+                                 float* dg1, float* dg2, float* dg3, float* hot_dw, void* stream);
+
+/* Backward fused with the SGD step on the cores and on W (in place, W[s]
+ * updated only for hot rows the batch looks up), as tt_emb_backward_sgd. */
+tt_status tt_emb_backward_sgd_cached(tt_emb_plan_t plan, uint64_t kept_token, float* g1, float* g2,
+                                     float* g3, float* hot_w, const float* grad_out, float lr,
+                                     void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* tt_emb_status_string(tt_status s);

@@ -23,8 +23,10 @@ __all__ = [
     "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
     "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
-    "tt_emb_kernel_times", "TT_PATH_MATRIX_CORE",
-    "TT_PATH_GENERIC", "TT_ERR_STALE", "TT_ERR_SCRATCH", "Plan", "EXPORTS",
+    "tt_emb_kernel_times", "tt_emb_cache_bytes", "tt_emb_cache_build", "tt_emb_plan_cached",
+    "tt_emb_forward_cached", "tt_emb_backward_cached", "tt_emb_backward_sgd_cached", "HotCache",
+    "TT_PATH_MATRIX_CORE", "TT_PATH_GENERIC", "TT_ERR_STALE", "TT_ERR_SCRATCH", "TT_ERR_CACHE", "Plan",
+    "EXPORTS",
 ]
 
 TT_OK = 0
@@ -32,6 +34,7 @@ TT_ERR_INVALID_ARG = -1
 TT_ERR_DEVICE_FLAG = -5
 TT_ERR_STALE = -6
 TT_ERR_SCRATCH = -7
+TT_ERR_CACHE = -8
 TT_PATH_MATRIX_CORE = 1
 TT_PATH_GENERIC = 2
 TT_FLAG_BAD_INDEX = 1
@@ -43,7 +46,8 @@ EXPORTS = (
     "tt_emb_backward", "tt_emb_backward_kept", "tt_emb_backward_sgd", "tt_emb_sgd",
     "tt_emb_get_error", "tt_emb_plan_get_view", "tt_emb_plan_counts", "tt_emb_plan_destroy",
     "tt_emb_query_paths", "tt_emb_forward_scratch", "tt_emb_scratch_capacity", "tt_emb_set_timing",
-    "tt_emb_kernel_times", "tt_emb_status_string",
+    "tt_emb_kernel_times", "tt_emb_cache_bytes", "tt_emb_cache_build", "tt_emb_plan_cached",
+    "tt_emb_forward_cached", "tt_emb_backward_cached", "tt_emb_backward_sgd_cached", "tt_emb_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -126,11 +130,21 @@ def load_library() -> ctypes.CDLL:
         lib.tt_emb_plan_get_view.argtypes = [P, ctypes.POINTER(_View)]
         lib.tt_emb_plan_counts.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64), P]
         lib.tt_emb_plan_destroy.argtypes = [P]
+        lib.tt_emb_cache_bytes.argtypes = [i64]
+        lib.tt_emb_cache_bytes.restype = ctypes.c_size_t
+        lib.tt_emb_cache_build.argtypes = [P, P, i64, P, ctypes.c_size_t, P]
+        lib.tt_emb_plan_cached.argtypes = [P, i32, P, P, i64, i64, i32, P, i64, P, ctypes.c_size_t, P,
+                                           ctypes.POINTER(P)]
+        lib.tt_emb_forward_cached.argtypes = [P, P, P, P, P, P, ctypes.POINTER(ctypes.c_uint64), P]
+        lib.tt_emb_backward_cached.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, P, P, P]
+        lib.tt_emb_backward_sgd_cached.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, ctypes.c_float, P]
         lib.tt_emb_status_string.argtypes = [ctypes.c_int]
         lib.tt_emb_status_string.restype = ctypes.c_char_p
         for name in ("tt_emb_plan", "tt_emb_forward", "tt_emb_forward_train", "tt_emb_backward",
                      "tt_emb_backward_kept", "tt_emb_sgd", "tt_emb_get_error", "tt_emb_plan_get_view",
-                     "tt_emb_plan_counts", "tt_emb_plan_destroy", "tt_emb_query_paths"):
+                     "tt_emb_plan_counts", "tt_emb_plan_destroy", "tt_emb_query_paths",
+                     "tt_emb_cache_build", "tt_emb_plan_cached", "tt_emb_forward_cached",
+                     "tt_emb_backward_cached", "tt_emb_backward_sgd_cached"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -233,10 +247,10 @@ def tt_emb_workspace_bytes(tables_c, L: int, B: int, chunk: int) -> int:
 
 
 def tt_emb_plan(tables_c, indices, offsets, B: int, chunk: int, workspace=None,
-                stream=None) -> Plan:
+                stream=None, cache=None) -> Plan:
     """Plan a batch. `tables_c` from make_tables; indices int64[L] and offsets
     int64[T*B+1] device tensors; workspace a uint8 device tensor (allocated
-    here with torch if None)."""
+    here with torch if None); cache a HotCache (tt_emb_plan_cached)."""
     lib = load_library()
     L = int(indices.numel())
     T = len(tables_c)
@@ -247,13 +261,89 @@ def tt_emb_plan(tables_c, indices, offsets, B: int, chunk: int, workspace=None,
         import torch
         workspace = torch.empty(need, dtype=torch.uint8, device=indices.device)
     h = ctypes.c_void_p()
-    st = lib.tt_emb_plan(tables_c, T, _dev_ptr(indices, "int64", "indices"),
-                         _dev_ptr(offsets, "int64", "offsets", T * B + 1), L, B, chunk,
-                         _dev_ptr(workspace, "uint8", "workspace"), workspace.numel(),
-                         _stream(stream), ctypes.byref(h))
-    _check(st, "tt_emb_plan")
+    args = (tables_c, T, _dev_ptr(indices, "int64", "indices"),
+            _dev_ptr(offsets, "int64", "offsets", T * B + 1), L, B, chunk)
+    tail = (_dev_ptr(workspace, "uint8", "workspace"), workspace.numel(), _stream(stream), ctypes.byref(h))
+    if cache is None:
+        _check(lib.tt_emb_plan(*args, *tail), "tt_emb_plan")
+    else:
+        _check(lib.tt_emb_plan_cached(*args, _dev_ptr(cache.mem, "uint8", "cache"), cache.n_hot, *tail),
+               "tt_emb_plan_cached")
     D = int(tables_c[0].n[0] * tables_c[0].n[1] * tables_c[0].n[2])
-    return Plan(h.value, workspace, L, T * B, D, core_extents(tables_c))
+    pl = Plan(h.value, workspace, L, T * B, D, core_extents(tables_c))
+    pl.cache = cache   # kept alive with the plan
+    return pl
+
+
+class HotCache:
+    """A hot-row cache's hash table (device memory, owned here) for the
+    entries (hot_table[s], hot_row[s]), built on `stream`."""
+
+    def __init__(self, hot_table, hot_row, stream=None):
+        import torch
+        lib = load_library()
+        n = int(hot_row.numel())
+        if int(hot_table.numel()) != n:
+            raise ValueError("hot_table and hot_row differ in length")
+        self.n_hot = n
+        nbytes = int(lib.tt_emb_cache_bytes(n))
+        if nbytes == 0:
+            raise TTEmbError(-2, "tt_emb_cache_bytes")
+        self.mem = torch.empty(nbytes, dtype=torch.uint8, device=hot_row.device)
+        _check(lib.tt_emb_cache_build(_dev_ptr(hot_table, "int32", "hot_table") if n else None,
+                                      _dev_ptr(hot_row, "int64", "hot_row") if n else None, n,
+                                      _dev_ptr(self.mem, "uint8", "cache"), nbytes, _stream(stream)),
+               "tt_emb_cache_build")
+
+
+def tt_emb_cache_bytes(n_hot: int) -> int:
+    return int(load_library().tt_emb_cache_bytes(int(n_hot)))
+
+
+def tt_emb_cache_build(hot_table, hot_row, stream=None) -> HotCache:
+    return HotCache(hot_table, hot_row, stream)
+
+
+def tt_emb_plan_cached(tables_c, indices, offsets, B: int, chunk: int, cache: HotCache,
+                       workspace=None, stream=None) -> Plan:
+    return tt_emb_plan(tables_c, indices, offsets, B, chunk, workspace, stream, cache)
+
+
+def _hot(plan: Plan, w, what: str):
+    if getattr(plan, "cache", None) is None:   # the library refuses the call (TT_ERR_CACHE)
+        return _dev_ptr(w, "float32", what)
+    n = plan.cache.n_hot
+    if n == 0 and w is None:
+        return None
+    return _dev_ptr(w, "float32", what, n * plan.D)
+
+
+def tt_emb_forward_cached(plan: Plan, g1, g2, g3, hot_w, out, keep: bool = False, stream=None) -> int:
+    """Forward with the hot rows hot_w [n_hot][D]; keep: also keep the
+    prefix products (returns their token, else 0)."""
+    tok = ctypes.c_uint64(0)
+    _check(load_library().tt_emb_forward_cached(
+        plan.handle, *plan.cores(g1, g2, g3), _hot(plan, hot_w, "hot_w"),
+        _dev_ptr(out, "float32", "out", plan.TB * plan.D), ctypes.byref(tok) if keep else None,
+        _stream(stream)), "tt_emb_forward_cached")
+    return int(tok.value)
+
+
+def tt_emb_backward_cached(plan: Plan, kept_token: int, g1, g2, g3, grad_out, dg1, dg2, dg3, hot_dw,
+                           stream=None):
+    _check(load_library().tt_emb_backward_cached(
+        plan.handle, ctypes.c_uint64(int(kept_token)), *plan.cores(g1, g2, g3),
+        _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D),
+        *plan.cores(dg1, dg2, dg3, ("dg1", "dg2", "dg3")), _hot(plan, hot_dw, "hot_dw"), _stream(stream)),
+        "tt_emb_backward_cached")
+
+
+def tt_emb_backward_sgd_cached(plan: Plan, kept_token: int, g1, g2, g3, hot_w, grad_out, lr: float,
+                               stream=None):
+    _check(load_library().tt_emb_backward_sgd_cached(
+        plan.handle, ctypes.c_uint64(int(kept_token)), *plan.cores(g1, g2, g3), _hot(plan, hot_w, "hot_w"),
+        _dev_ptr(grad_out, "float32", "grad_out", plan.TB * plan.D), float(lr), _stream(stream)),
+        "tt_emb_backward_sgd_cached")
 
 
 def tt_emb_forward(plan: Plan, g1, g2, g3, out, stream=None):

@@ -605,6 +605,9 @@ struct RunsArgs {
     double* dpart;
     int32_t* gdone;            // per group: pieces finished (zeroed by bwd_prep); -1: not listed
     int32_t* claims;           // [kRunCounters][32]: unit counters (zeroed by bwd_prep)
+    const int32_t* run_cslot;  // hot-row cache: each run's slot (-1: not hot); null without a cache
+    float* hot;                // the hot rows' gradients dW [n_hot][D], or (fused SGD) W itself
+    GradOut hgo;               // how a hot run's S goes into `hot`
 };
 
 // One wave per unit, the group's P in registers. Persistent waves claim their
@@ -676,10 +679,12 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         floatx4 av[MT], bq[RT];
         float bv[KSP];
         int32_t i3q;
+        int32_t csq;           // hot-row slot of run t0 + q (-1: not hot)
     };
     auto load_tile = [&](int32_t t0, int32_t s, int32_t e, int32_t i3w, int64_t o3, TileOps& o) {
         const int32_t rq = t0 + q < e ? t0 + q : t0;
         o.i3q = __shfl(i3w, rq - s);
+        o.csq = a.run_cslot ? a.run_cslot[rq] : -1;
         const float* Sq = a.S + (int64_t)rq * D;
         const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
 #pragma unroll
@@ -725,6 +730,9 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         const int32_t e = min(cur.e, s + W);
         auto tile = [&](int32_t t0, TileOps& o) {
             const bool okq = t0 + q < e;
+            // a hot row's run: its S is the hot row's gradient, and it adds
+            // nothing to the cores' gradients
+            const bool hotq = okq && o.csq >= 0;
             // dG3: rows (run t0 + lk, j3) of P^T S; lane (col, q) gets run
             // t0 + q, r2 = 16rt + col, j3 = v
 #pragma unroll
@@ -733,14 +741,23 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
 #pragma unroll
                 for (int s2 = 0; s2 < KSP; ++s2)
                     cc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.bv[s2], preg[rt][s2 / 4][s2 % 4], cc, 0, 0, 0);
-                if (okq) add3(o3 + (int64_t)o.i3q * CN, (16 * rt + col) * N3, t0 + q, cc);
+                if (okq) add3(o3 + (int64_t)o.i3q * CN, (16 * rt + col) * N3, t0 + q,
+                              hotq ? floatx4{0.f, 0.f, 0.f, 0.f} : cc);
+            }
+            if (hotq) {
+                // lane (col, q) holds S[run t0 + q][(16mt + col)*n3 + 0..3]
+                float* hr = a.hot + (int64_t)o.csq * D + col * N3;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) put_grad(hr + 16 * mt * N3 + v, o.av[mt][v], a.hgo);
             }
             // dP: K = (run q, j3 = step), fp64 products and sums (a hot
             // group's dP adds up hundreds of runs of large S); a run past the
             // piece adds zeros
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const floatx4 av = okq ? o.av[mt] : floatx4{0.f, 0.f, 0.f, 0.f};
+                const floatx4 av = okq && !hotq ? o.av[mt] : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int nt = 0; nt < RT; ++nt)
 #pragma unroll
@@ -1093,7 +1110,7 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
 template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
-                                 float* dg3, bool kept, GradOut go, hipStream_t s) {
+                                 float* dg3, bool kept, GradOut go, hipStream_t s, float* hot) {
     // dG3 reduced per G3 row from per-run terms (k_bwd_dg3 writes every row
     // of the buffer, gaps included), unless some table's G3 rows are not
     // aligned to R*n3: then device atomics into an fp64 accumulator
@@ -1140,10 +1157,17 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
             TT_LAUNCH_CHECK();
         }
+        // hot rows: dW starts at zero (every row written); the fused step
+        // updates W in place
+        if (p->cached && !go.sgd && p->n_hot > 0) {
+            tt_status st = fill32(p, hot, 0u, p->n_hot * (int64_t)D, s);
+            if (st != TT_OK) return st;
+        }
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), S, pbuf, g3, acc3, p->at<double>(p->lay.dpart),
-                    p->at<int32_t>(p->lay.gdone), p->at<int32_t>(p->lay.claims)};
+                    p->at<int32_t>(p->lay.gdone), p->at<int32_t>(p->lay.claims),
+                    p->cached ? p->at<int32_t>(p->lay.run_cslot) : nullptr, hot, go};
         if (bucket3) {
             // each run's dG3 term over its own S row when the row holds it
             float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);
@@ -1198,10 +1222,10 @@ bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
 template <int N1, int N2, int R, int N3, bool BW>
 static bool bwd_case(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                      const float* gout, float* dg1, float* dg2, float* dg3, bool kept, GradOut go,
-                     hipStream_t s, tt_status* st) {
+                     hipStream_t s, tt_status* st, float* hot) {
     if constexpr (BW) {
         if (p->n1 == N1 && p->n2 == N2 && p->n3 == N3 && p->R == R) {
-            *st = launch_bwd_mfma<N1, N2, R, N3>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s);
+            *st = launch_bwd_mfma<N1, N2, R, N3>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s, hot);
             return true;
         }
     }
@@ -1210,10 +1234,10 @@ static bool bwd_case(const tt_emb_plan_s* p, const float* g1, const float* g2, c
 
 static tt_status launch_bwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
                             const float* gout, float* dg1, float* dg2, float* dg3, bool kept, GradOut go,
-                            hipStream_t s) {
+                            hipStream_t s, float* hot = nullptr) {
     tt_status st = TT_ERR_UNSUPPORTED;
 #define TT_BWD_CASE(a, b, c, d, bw) \
-    if (bwd_case<a, b, d, c, bw>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s, &st)) return st;
+    if (bwd_case<a, b, d, c, bw>(p, g1, g2, g3, gout, dg1, dg2, dg3, kept, go, s, &st, hot)) return st;
     TT_MFMA_SHAPES(TT_BWD_CASE)
 #undef TT_BWD_CASE
     return st;
@@ -1225,11 +1249,13 @@ using namespace tt;
 
 static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2, const float* g3,
                                const float* grad_out, float* dg1, float* dg2, float* dg3, bool kept,
-                               void* stream) {
+                               void* stream, float* hot_dw = nullptr) {
     hipStream_t s = (hipStream_t)stream;
     // the backward overwrites the kept products (P, then dP over it)
     p->kept_token = 0;
-    if (bwd_mfma_ok(p, g1, g2)) return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, GradOut{0.f, 0}, s);
+    if (bwd_mfma_ok(p, g1, g2))
+        return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, GradOut{0.f, 0}, s, hot_dw);
+    if (p->cached) return TT_ERR_UNSUPPORTED;   // hot rows need the matrix-core kernels
     tt_status st = TT_OK;
     if ((st = fill32(p, dg1, 0u, p->extent[0], s)) != TT_OK) return st;
     if ((st = fill32(p, dg2, 0u, p->extent[1], s)) != TT_OK) return st;
@@ -1253,10 +1279,16 @@ static bool backward_args_ok(tt_emb_plan_t p, const float* g1, const float* g2, 
     return p && g1 && g2 && g3 && dg1 && dg2 && dg3 && (grad_out || p->TB == 0);
 }
 
+// A kept token names the products the plan holds for these G1 and G2.
+static bool token_ok(tt_emb_plan_t p, uint64_t tok, const float* g1, const float* g2) {
+    return tok != 0 && tok == p->kept_token && g1 == p->kept_g1 && g2 == p->kept_g2;
+}
+
 extern "C" tt_status tt_emb_backward(tt_emb_plan_t p, const float* g1, const float* g2,
                                      const float* g3, const float* grad_out, float* dg1,
                                      float* dg2, float* dg3, void* stream) {
     if (!backward_args_ok(p, g1, g2, g3, grad_out, dg1, dg2, dg3)) return TT_ERR_INVALID_ARG;
+    if (p->cached) return TT_ERR_CACHE;
     return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, false, stream);
 }
 
@@ -1264,21 +1296,44 @@ extern "C" tt_status tt_emb_backward_kept(tt_emb_plan_t p, uint64_t kept_token, 
                                           const float* g2, const float* g3, const float* grad_out,
                                           float* dg1, float* dg2, float* dg3, void* stream) {
     if (!backward_args_ok(p, g1, g2, g3, grad_out, dg1, dg2, dg3)) return TT_ERR_INVALID_ARG;
-    if (kept_token == 0 || kept_token != p->kept_token || g1 != p->kept_g1 || g2 != p->kept_g2 ||
-        !bwd_mfma_ok(p, g1, g2))
-        return TT_ERR_STALE;
+    if (p->cached) return TT_ERR_CACHE;
+    if (!token_ok(p, kept_token, g1, g2) || !bwd_mfma_ok(p, g1, g2)) return TT_ERR_STALE;
     return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, true, stream);
+}
+
+extern "C" tt_status tt_emb_backward_cached(tt_emb_plan_t p, uint64_t kept_token, const float* g1,
+                                            const float* g2, const float* g3, const float* grad_out,
+                                            float* dg1, float* dg2, float* dg3, float* hot_dw, void* stream) {
+    if (!backward_args_ok(p, g1, g2, g3, grad_out, dg1, dg2, dg3)) return TT_ERR_INVALID_ARG;
+    if (!p->cached) return TT_ERR_CACHE;
+    if (!hot_dw && p->n_hot > 0) return TT_ERR_INVALID_ARG;
+    if (!bwd_mfma_ok(p, g1, g2)) return TT_ERR_UNSUPPORTED;
+    if (kept_token != 0 && !token_ok(p, kept_token, g1, g2)) return TT_ERR_STALE;
+    return backward_impl(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept_token != 0, stream, hot_dw);
+}
+
+static tt_status backward_sgd(tt_emb_plan_t p, uint64_t kept_token, float* g1, float* g2, float* g3,
+                              float* hot_w, const float* grad_out, float lr, void* stream) {
+    if (!p || !g1 || !g2 || !g3 || (!grad_out && p->TB > 0)) return TT_ERR_INVALID_ARG;
+    if (!bwd_mfma_ok(p, g1, g2)) return TT_ERR_UNSUPPORTED;
+    if (kept_token != 0 && !token_ok(p, kept_token, g1, g2)) return TT_ERR_STALE;
+    const bool kept = kept_token != 0;
+    p->kept_token = 0;   // consumed, and the cores change
+    return launch_bwd(p, g1, g2, g3, grad_out, g1, g2, g3, kept, GradOut{-lr, 1}, (hipStream_t)stream, hot_w);
 }
 
 extern "C" tt_status tt_emb_backward_sgd(tt_emb_plan_t p, uint64_t kept_token, float* g1, float* g2,
                                          float* g3, const float* grad_out, float lr, void* stream) {
-    if (!p || !g1 || !g2 || !g3 || (!grad_out && p->TB > 0)) return TT_ERR_INVALID_ARG;
-    if (!bwd_mfma_ok(p, g1, g2)) return TT_ERR_UNSUPPORTED;
-    if (kept_token != 0 && (kept_token != p->kept_token || g1 != p->kept_g1 || g2 != p->kept_g2))
-        return TT_ERR_STALE;
-    const bool kept = kept_token != 0;
-    p->kept_token = 0;   // consumed, and the cores change
-    return launch_bwd(p, g1, g2, g3, grad_out, g1, g2, g3, kept, GradOut{-lr, 1}, (hipStream_t)stream);
+    if (p && p->cached) return TT_ERR_CACHE;
+    return backward_sgd(p, kept_token, g1, g2, g3, nullptr, grad_out, lr, stream);
+}
+
+extern "C" tt_status tt_emb_backward_sgd_cached(tt_emb_plan_t p, uint64_t kept_token, float* g1, float* g2,
+                                                float* g3, float* hot_w, const float* grad_out, float lr,
+                                                void* stream) {
+    if (p && !p->cached) return TT_ERR_CACHE;
+    if (p && !hot_w && p->n_hot > 0) return TT_ERR_INVALID_ARG;
+    return backward_sgd(p, kept_token, g1, g2, g3, hot_w, grad_out, lr, stream);
 }
 
 extern "C" tt_status tt_emb_sgd(tt_emb_plan_t p, float* g1, float* g2, float* g3,

@@ -307,7 +307,8 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, co
 
 // One wave per bag: sum the rows of the bag's lookups (in input order) from
 // the stage buffer (one row per run id) and write the bag's output row. Empty
-// bags get zeros. Rows are read as 16-byte vectors, LPR = D/4 lanes per row,
+// bags get zeros. With a hot-row cache, a hot row's lookups carry -(slot + 1)
+// in place of a run id and take the row from `hot`. Rows are read as 16-byte vectors, LPR = D/4 lanes per row,
 // so one load instruction covers RPI = 64/LPR rows; lane group h takes rows
 // h, h + RPI, ... of the bag and the RPI partial sums are added at the end.
 template <int D>
@@ -315,7 +316,8 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
                                               const int32_t* __restrict__ run_of,
                                               const float* __restrict__ stage,
                                               float* __restrict__ out, int32_t* ctrl,
-                                              int32_t* __restrict__ fwd_claims) {
+                                              int32_t* __restrict__ fwd_claims,
+                                              const float* __restrict__ hot) {
     // the batch kernel has finished: its claim counters start from zero at
     // the next forward call
     if (blockIdx.x == 0 && threadIdx.x < kFwdCounters) fwd_claims[threadIdx.x * 32] = 0;
@@ -338,7 +340,8 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
             for (int u = 0; u < U; ++u) {
                 const int j = j0 + RPI * u + h;
                 const int32_t slot = __shfl(rv, min(j, n - 1));
-                v[u] = *reinterpret_cast<const floatx4*>(stage + (int64_t)slot * D + c4);
+                const float* src = slot >= 0 ? stage + (int64_t)slot * D : hot + (int64_t)(-1 - slot) * D;
+                v[u] = *reinterpret_cast<const floatx4*>(src + c4);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
 
 template <int N1, int N2, int R, int N3, bool BW>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
-                                 const float* g3, float* out, bool keep, hipStream_t s) {
+                                 const float* g3, float* out, bool keep, hipStream_t s, const float* hot) {
     int32_t* fwd_claims = p->at<int32_t>(p->lay.claims) + 32 * kRunCounters;
     float* g3t = p->at<float>(p->lay.g3t);
     FwdArgs a{p->at<BatchRec>(p->lay.batch), p->at<int32_t>(p->lay.run_i3), g1, g2, g3t,
@@ -384,7 +387,7 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     if (p->TB > 0) {
         TT_LAUNCH(p, "k_pool", s, k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
                            p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
-                           p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims);
+                           p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims, hot);
         TT_LAUNCH_CHECK();
     }
     return TT_OK;
@@ -408,10 +411,10 @@ bool fwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
 }
 
 static tt_status launch_fwd(const tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3,
-                            float* out, bool keep, hipStream_t s) {
+                            float* out, bool keep, hipStream_t s, const float* hot) {
     const int n1 = p->n1, n2 = p->n2, n3 = p->n3, R = p->R;
 #define TT_FWD_CASE(a, b, c, d, bw) \
-    if (n1 == a && n2 == b && n3 == c && R == d) return launch_fwd_mfma<a, b, d, c, bw>(p, g1, g2, g3, out, keep, s);
+    if (n1 == a && n2 == b && n3 == c && R == d) return launch_fwd_mfma<a, b, d, c, bw>(p, g1, g2, g3, out, keep, s, hot);
     TT_MFMA_SHAPES(TT_FWD_CASE)
 #undef TT_FWD_CASE
     return TT_ERR_UNSUPPORTED;
@@ -422,14 +425,19 @@ static tt_status launch_fwd(const tt_emb_plan_s* p, const float* g1, const float
 using namespace tt;
 
 tt_status tt::forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3, float* out,
-                          bool keep, uint64_t* token, hipStream_t s) {
+                          bool keep, uint64_t* token, hipStream_t s, const float* hot_w) {
     if (token) *token = 0;
     if (!p || !g1 || !g2 || !g3 || (!out && p->TB > 0)) return TT_ERR_INVALID_ARG;
+    if (p->cached) {
+        // hot rows take the matrix-core path in both directions
+        if (!hot_w && p->n_hot > 0) return TT_ERR_INVALID_ARG;
+        if (!fwd_mfma_ok(p, g1, g2) || !bwd_mfma_ok(p, g1, g2)) return TT_ERR_UNSUPPORTED;
+    }
     if (fwd_mfma_ok(p, g1, g2)) {
         // P is kept only where the backward's matrix-core path will read it
         const bool k = keep && !p->fwd_only && bwd_mfma_ok(p, g1, g2) && p->L > 0;
         if (k) p->kept_token = 0;   // pbuf is being rewritten
-        const tt_status st = launch_fwd(p, g1, g2, g3, out, k, s);
+        const tt_status st = launch_fwd(p, g1, g2, g3, out, k, s, hot_w);
         if (k && st == TT_OK) {
             p->kept_token = ++p->next_token;
             p->kept_g1 = g1;
@@ -455,11 +463,22 @@ tt_status tt::forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, co
 
 extern "C" tt_status tt_emb_forward(tt_emb_plan_t p, const float* g1, const float* g2,
                                     const float* g3, float* out, void* stream) {
+    if (p && p->cached) return TT_ERR_CACHE;
     return forward_run(p, g1, g2, g3, out, false, nullptr, (hipStream_t)stream);
 }
 
 extern "C" tt_status tt_emb_forward_train(tt_emb_plan_t p, const float* g1, const float* g2,
                                           const float* g3, float* out, uint64_t* kept_token,
                                           void* stream) {
+    if (kept_token) *kept_token = 0;
+    if (p && p->cached) return TT_ERR_CACHE;
     return forward_run(p, g1, g2, g3, out, true, kept_token, (hipStream_t)stream);
+}
+
+extern "C" tt_status tt_emb_forward_cached(tt_emb_plan_t p, const float* g1, const float* g2,
+                                           const float* g3, const float* hot_w, float* out,
+                                           uint64_t* kept_token, void* stream) {
+    if (kept_token) *kept_token = 0;
+    if (p && !p->cached) return TT_ERR_CACHE;
+    return forward_run(p, g1, g2, g3, out, kept_token != nullptr, kept_token, (hipStream_t)stream, hot_w);
 }

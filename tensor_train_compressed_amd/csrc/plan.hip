@@ -66,6 +66,9 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     const size_t l4 = sizeof(int32_t) * (size_t)L;
     y.key = take(l4); y.i3 = take(l4); y.bag_of = take(l4);
     y.ckey = take(l4);
+    // hot-row slots (plans with a hot-row cache; always carved in full layouts)
+    y.cslot = take(sizeof(int32_t) * (size_t)LB);
+    y.run_cslot = take(sizeof(int32_t) * (size_t)LB);
     y.bag_start = take(sizeof(int32_t) * (size_t)((int64_t)T * B + 1));
     y.rid = take(l4);
     y.run_i3 = take(l4);
@@ -248,7 +251,10 @@ __global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restric
                                                         int32_t* ctrl, int32_t* __restrict__ key_start,
                                                         int64_t K, int32_t* __restrict__ i3cnt, int32_t n3cnt,
                                                         int64_t n_tiles, int64_t hstride,
-                                                        uint32_t* __restrict__ hist) {
+                                                        uint32_t* __restrict__ hist,
+                                                        const int64_t* __restrict__ hot_keys,
+                                                        const int32_t* __restrict__ hot_slots, int hot_lg,
+                                                        int32_t* __restrict__ cslot) {
     __shared__ uint32_t cnt[kSortWaves][kRadixBins];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if ((int64_t)blockIdx.x >= n_tiles) {
@@ -302,12 +308,14 @@ __global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restric
         xv[slot] = idx[e < L ? e : L - 1];   // L > 0: there is a lookup tile
     }
 
-    // one lookup: its key, sort key and i3 (a bad index reads as row 0)
-    auto split_one = [&](int64_t e, int64_t x, const TabDev& dd) {
+    // one lookup: its key, sort key and i3 (a bad index reads as row 0), and
+    // with a hot-row cache its row's slot
+    auto split_one = [&](int64_t e, int64_t x, const TabDev& dd, int64_t t) {
         if (x < 0 || x >= dd.N) {
             atomicOr(&ctrl[CTRL_FLAG], TT_FLAG_BAD_INDEX);
             x = 0;
         }
+        if (cslot) cslot[e] = cache_probe(hot_keys, hot_slots, hot_lg, (t << 40) | x);
         const uint32_t xi = (uint32_t)x;
         const uint32_t r3 = xi % (uint32_t)dd.m3;
         const uint32_t p = xi / (uint32_t)dd.m3;
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restric
 #pragma unroll
         for (int slot = 0; slot < kSortItems; ++slot) {
             const int64_t e = base + slot * 64 + lane;
-            dg[slot] = e < L ? split_one(e, xv[slot], d0) : 0u;
+            dg[slot] = e < L ? split_one(e, xv[slot], d0, 0) : 0u;
         }
     } else {
 #pragma unroll
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restric
                     const int64_t mid = (lo + hi) >> 1;
                     if (off[mid * B] <= e) lo = mid; else hi = mid;
                 }
-                dg[slot] = split_one(e, xv[slot], desc[lo]);
+                dg[slot] = split_one(e, xv[slot], desc[lo], lo);
             }
         }
     }
@@ -951,7 +959,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int32_t* __restrict__ run_bkt,
                                                        const TabDev* __restrict__ desc, int32_t T, int32_t CN,
                                                        int64_t K, int64_t NFB,
-                                                       uint32_t* __restrict__ batch_tiles) {
+                                                       uint32_t* __restrict__ batch_tiles,
+                                                       const int32_t* __restrict__ cslot,
+                                                       int32_t* __restrict__ run_cslot) {
     __shared__ uint32_t sh3[kMaxBuckets3];
     for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
     const int64_t tile = blockIdx.x;
@@ -986,7 +996,14 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                 run_start[rr] = (int32_t)s;
                 if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3)], 1u);   // rank in the tile
             }
-            run_of[perm[s]] = rr + (int32_t)hr[j] - 1;
+            const int32_t pl = perm[s];
+            int32_t ro = rr + (int32_t)hr[j] - 1;
+            if (cslot) {   // a hot row's lookups: -(slot + 1), its run: the slot
+                const int32_t cs = cslot[pl];
+                if (hr[j]) run_cslot[rr] = cs;
+                if (cs >= 0) ro = -(cs + 1);
+            }
+            run_of[pl] = ro;
             const int32_t off = (int32_t)s - key_start[k];
             if (off % chunk == 0) {
                 const uint64_t ks = key_scan[k];
@@ -1214,7 +1231,8 @@ extern "C" size_t tt_emb_workspace_bytes(const tt_emb_table* tables, int32_t T, 
 // caller keeps `tables` alive as long as p uses it.
 tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T, const int64_t* indices,
                         const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
-                        size_t workspace_bytes, bool fwd_only, hipStream_t s) {
+                        size_t workspace_bytes, bool fwd_only, hipStream_t s, const void* cache,
+                        int64_t n_hot) {
     int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
     tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3);
@@ -1223,6 +1241,7 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     if (st != TT_OK) return st;
     if (!offsets || !workspace || (L > 0 && !indices)) return TT_ERR_INVALID_ARG;
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
+    if (cache && (fwd_only || n_hot < 0 || ((uintptr_t)cache & 255) != 0)) return TT_ERR_INVALID_ARG;
     if (fwd_only) NB3 = 0;
     const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3, fwd_only);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
@@ -1239,6 +1258,12 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     }
     p->ws = (char*)workspace;
     p->lay = lay;
+    p->cached = cache != nullptr;
+    p->n_hot = cache ? n_hot : 0;
+    p->hot_lg = cache ? cache_lg(n_hot) : 0;
+    p->hot_keys = cache ? reinterpret_cast<const int64_t*>((const char*)cache + kHotHeader) : nullptr;
+    p->hot_slots = cache ? reinterpret_cast<const int32_t*>((const char*)cache + cache_slots_offset(p->hot_lg))
+                         : nullptr;
     p->tables = tables;
     p->fwd_only = fwd_only;
     p->uniform = true;
@@ -1327,7 +1352,8 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
                   s, indices, offsets, L, p->TB, B > 0 ? B : 1, p->desc(), key, i3, bag,
                   p->at<int32_t>(lay.bag_start), p->at<int32_t>(lay.ckey), p->M3, ctrl,
                   p->at<int32_t>(lay.key_start), K, p->at<int32_t>(lay.i3cnt), n3cnt, lay.n_tiles, lay.hstride,
-                  p->at<uint32_t>(lay.hist));
+                  p->at<uint32_t>(lay.hist), p->hot_keys, p->hot_slots, p->hot_lg,
+                  p->cached ? p->at<int32_t>(lay.cslot) : nullptr);
         if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
     }
     // stable radix sort: key -> (skey, perm)
@@ -1402,7 +1428,8 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
                                p->at<int32_t>(lay.chunk_begin), p->at<int32_t>(lay.chunk_end),
                                p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank),
                                p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN, K, lay.NFB,
-                               p->at<uint32_t>(lay.batch_tiles));
+                               p->at<uint32_t>(lay.batch_tiles), p->cached ? p->at<int32_t>(lay.cslot) : nullptr,
+                               p->cached ? p->at<int32_t>(lay.run_cslot) : nullptr);
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
         if (lay.NFB > 0 && L > 0) {   // (no lookups: the list stays empty, its length 0 from k_init)
@@ -1418,10 +1445,33 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     return TT_OK;
 }
 
+static tt_status plan_new(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                          const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
+                          size_t workspace_bytes, void* stream, tt_emb_plan_t* plan_out, const void* cache,
+                          int64_t n_hot);
+
 extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const int64_t* indices,
                                  const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  tt_emb_plan_t* plan_out) {
+    return plan_new(tables, T, indices, offsets, L, B, chunk, workspace, workspace_bytes, stream, plan_out,
+                    nullptr, 0);
+}
+
+extern "C" tt_status tt_emb_plan_cached(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                                        const int64_t* offsets, int64_t L, int64_t B, int32_t chunk,
+                                        const void* cache, int64_t n_hot, void* workspace,
+                                        size_t workspace_bytes, void* stream, tt_emb_plan_t* plan_out) {
+    if (plan_out) *plan_out = nullptr;
+    if (!cache || n_hot < 0) return TT_ERR_INVALID_ARG;
+    return plan_new(tables, T, indices, offsets, L, B, chunk, workspace, workspace_bytes, stream, plan_out,
+                    cache, n_hot);
+}
+
+static tt_status plan_new(const tt_emb_table* tables, int32_t T, const int64_t* indices,
+                          const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
+                          size_t workspace_bytes, void* stream, tt_emb_plan_t* plan_out, const void* cache,
+                          int64_t n_hot) {
     if (!plan_out) return TT_ERR_INVALID_ARG;
     *plan_out = nullptr;
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
@@ -1433,7 +1483,7 @@ extern "C" tt_status tt_emb_plan(const tt_emb_table* tables, int32_t T, const in
     if (g_timing_default.load()) p->timing = new (std::nothrow) Timing();
     std::memcpy(p->owned_tables, tables, sizeof(tt_emb_table) * (size_t)T);
     const tt_status st = plan_into(p, p->owned_tables, T, indices, offsets, L, B, chunk, workspace,
-                                   workspace_bytes, false, (hipStream_t)stream);
+                                   workspace_bytes, false, (hipStream_t)stream, cache, n_hot);
     if (st != TT_OK) { delete p; return st; }
     *plan_out = p;
     return TT_OK;
@@ -1541,6 +1591,7 @@ extern "C" const char* tt_emb_status_string(tt_status s) {
         case TT_ERR_DEVICE_FLAG: return "device error flag set (bad index or offsets)";
         case TT_ERR_STALE: return "kept prefix products are stale (token does not match the plan)";
         case TT_ERR_SCRATCH: return "batch needs more than the library's static scratch buffer holds";
+        case TT_ERR_CACHE: return "hot-row cache mismatch (a plan with a cache takes only the _cached calls, which need one)";
     }
     return "unknown status";
 }

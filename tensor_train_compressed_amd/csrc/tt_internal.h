@@ -148,6 +148,9 @@ struct Layout {
                                              //     scans, right after ctrl (cleared with it)
     size_t key, i3, bag_of;                  // [L]
     size_t ckey;                             // [L] sort key = key * M3 + i3
+    size_t cslot;                            // [L] int32: each lookup's hot-row slot (-1: not hot),
+                                             //     cached plans only (full layouts)
+    size_t run_cslot;                        // [L] int32: each row run's hot-row slot (-1: not hot)
     size_t bag_start;                        // [TB+1] int32 copy of the offsets
     size_t rid;                              // [L] int32, sorted order: number of row-run heads before s
     size_t run_i3;                           // [L] int32: i3 of each run
@@ -245,6 +248,11 @@ struct tt_emb_plan_s {
     const float* kept_g1;
     const float* kept_g2;
     bool fwd_only;            // the layout holds no backward buffers (forward calls only)
+    bool cached = false;      // planned with a hot-row cache (tt_emb_plan_cached)
+    int64_t n_hot = 0;        // the cache's entries
+    const int64_t* hot_keys = nullptr;    // the cache's hash table (device): keys, then slots
+    const int32_t* hot_slots = nullptr;
+    int32_t hot_lg = 0;       // log2 of the table's capacity
     char* ws;                 // workspace base (device)
     tt::Layout lay;
     const tt_emb_table* tables = nullptr;     // T descriptors (owned_tables, or the caller's
@@ -289,12 +297,13 @@ __device__ __forceinline__ void wait_vmem_done() {
 // Plans into *p without allocating (plan.hip); the workspace size of a layout.
 tt_status plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T, const int64_t* indices,
                     const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
-                    size_t workspace_bytes, bool fwd_only, hipStream_t s);
+                    size_t workspace_bytes, bool fwd_only, hipStream_t s, const void* cache = nullptr,
+                    int64_t n_hot = 0);
 size_t workspace_bytes_for(const tt_emb_table* tables, int32_t T, int64_t L, int64_t B, int32_t chunk,
                            bool fwd_only);
 // The forward on a plan (forward.hip); keep: also keep P (needs a full layout).
 tt_status forward_run(tt_emb_plan_s* p, const float* g1, const float* g2, const float* g3, float* out,
-                      bool keep, uint64_t* token, hipStream_t s);
+                      bool keep, uint64_t* token, hipStream_t s, const float* hot_w = nullptr);
 
 // Whether the plan's calls take the matrix-core kernels with these cores
 // (forward.hip, backward.hip).
@@ -314,6 +323,41 @@ inline unsigned grid_for(int64_t n, int threads) {
 }
 // Fill `n` 32-bit words at `ptr` with `v` (stream-ordered, capture-safe).
 tt_status fill32(const tt_emb_plan_s* p, void* ptr, uint32_t v, int64_t n, hipStream_t s);
+
+// Hot-row cache: an open-addressing hash table (linear probing, at most half
+// full) of 2^lg int64 keys (table << 40 | row; -1: empty) and int32 slots,
+// after a 256-byte header, in caller memory.
+constexpr int64_t kHotEmpty = -1;
+constexpr int kHotHeader = 256;
+inline int cache_lg(int64_t n_hot) {
+    int lg = 6;
+    while ((int64_t(1) << lg) < 2 * n_hot) ++lg;
+    return lg;
+}
+inline size_t cache_bytes_lg(int lg) {
+    const size_t c = size_t(1) << lg;
+    return (size_t)kHotHeader + ((8 * c + 255) & ~size_t(255)) + ((4 * c + 255) & ~size_t(255));
+}
+__host__ __device__ inline size_t cache_slots_offset(int lg) {
+    return (size_t)kHotHeader + ((8 * (size_t(1) << lg) + 255) & ~size_t(255));
+}
+__device__ __forceinline__ uint64_t cache_hash(int64_t key, int lg) {
+    return ((uint64_t)key * 0x9E3779B97F4A7C15ull) >> (64 - lg);
+}
+// Slot of `key` in the table, or -1 (the probe ends at the first empty entry;
+// the table always has one).
+__device__ __forceinline__ int32_t cache_probe(const int64_t* __restrict__ keys, const int32_t* __restrict__ slots,
+                                               int lg, int64_t key) {
+    const uint64_t mask = (uint64_t(1) << lg) - 1;
+    uint64_t h = cache_hash(key, lg);
+    for (uint64_t n = 0; n <= mask; ++n) {
+        const int64_t k = keys[h];
+        if (k == key) return slots[h];
+        if (k == kHotEmpty) return -1;
+        h = (h + 1) & mask;
+    }
+    return -1;
+}
 }  // namespace tt
 
 // A kernel launch on stream `s` for plan `p`, bracketed by the plan's timing

@@ -678,3 +678,77 @@ def test_matrix_core_shapes(n1, n2, n3, R, bw):
         tte.tt_emb_backward_sgd(dp.plan, tok, *g, dp.gout, p.lr)
         for k, (c, r) in enumerate(zip((p.g1, p.g2, p.g3), ref)):
             assert_close(g[k].cpu().numpy(), oracle.sgd(c, r, p.lr), f"{label} fused SGD core {k + 1}")
+
+
+def _top_pairs(p, k):
+    """The k most frequent (table, row) pairs of the batch."""
+    bag = np.repeat(np.arange(p.T * p.batch), np.diff(p.offsets))
+    key = (bag // p.batch) * (1 << 40) + p.indices
+    u, c = np.unique(key, return_counts=True)
+    top = u[np.argsort(-c, kind="stable")[:k]]
+    return (top >> 40).astype(np.int32), (top & ((1 << 40) - 1)).astype(np.int64)
+
+
+@pytest.mark.parametrize("case", ["single", "multi6", "empty"])
+def test_hot_row_cache(case):
+    """Hot rows kept uncompressed (the TT-Rec cache): forward, backward (kept
+    and recomputed prefixes) and the fused step against the oracle's cached
+    model on every element; a cache holding the rows' own TT values gives the
+    plain forward; the plain calls refuse a cached plan and the reverse."""
+    import tensor_train_compressed_amd as tte
+    if case == "multi6":
+        p = wl.make("multi26", batch=32, tables=6)
+        p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
+        p.lr = 0.01
+    else:
+        p = wl.make("train11m", batch=512)
+    if case == "empty":
+        ht, hr = np.zeros(0, np.int32), np.zeros(0, np.int64)
+    else:
+        ht, hr = _top_pairs(p, 96)
+        # a duplicate (served by its first slot) and a pair naming no row
+        ht = np.concatenate([ht, ht[:1], [0]]).astype(np.int32)
+        hr = np.concatenate([hr, hr[:1], [p.tables[0].num_rows + 5]]).astype(np.int64)
+    n = hr.size
+    say(case, f"L={p.L} hot entries={n}")
+    dp = DevProblem(p, 64)
+    cache = tte.HotCache(torch.from_numpy(ht).to("cuda:0"), torch.from_numpy(hr).to("cuda:0"))
+    plan = tte.tt_emb_plan(dp.tables_c, dp.idx, dp.off, p.batch, 64, cache=cache)
+    W = np.random.default_rng(2).standard_normal((n, p.dim)).astype(np.float32)
+    Wd = torch.from_numpy(W).to("cuda:0")
+    out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
+    tok = tte.tt_emb_forward_cached(plan, dp.g1, dp.g2, dp.g3, Wd, out, keep=True)
+    assert tok != 0
+    assert_close(out.cpu().numpy(), oracle.forward_cached(p, ht, hr, W), f"{case}: cached forward")
+    ref = oracle.backward_cached(p, ht, hr, n)
+    d = [torch.empty_like(x) for x in (dp.g1, dp.g2, dp.g3)]
+    dW = torch.full_like(Wd, 7.0)
+    for t in (tok, 0):
+        tte.tt_emb_backward_cached(plan, t, dp.g1, dp.g2, dp.g3, dp.gout, *d, dW)
+        for k in range(3):
+            assert_close(d[k].cpu().numpy(), ref[k], f"{case}: cached dG{k + 1} (token {t})")
+        assert_close(dW.cpu().numpy(), ref[3], f"{case}: dW (token {t})")
+    # the fused step: cores and hot rows updated in place
+    g = [x.clone() for x in (dp.g1, dp.g2, dp.g3)]
+    Wf = Wd.clone()
+    tok = tte.tt_emb_forward_cached(plan, *g, Wf, out, keep=True)
+    tte.tt_emb_backward_sgd_cached(plan, tok, *g, Wf, dp.gout, p.lr)
+    for k, c in enumerate((p.g1, p.g2, p.g3)):
+        assert_close(g[k].cpu().numpy(), oracle.sgd(c, ref[k], p.lr), f"{case}: fused core {k + 1}")
+    assert_close(Wf.cpu().numpy(), oracle.sgd(W, ref[3], p.lr), f"{case}: fused hot rows")
+    # a cache holding the rows' own TT values: the plain model's output
+    if n:
+        Wt = torch.from_numpy(oracle.materialise_rows(p, ht[:-1], hr[:-1]).astype(np.float32))
+        Wt = torch.cat([Wt, torch.zeros(1, p.dim)]).to("cuda:0")
+    else:
+        Wt = Wd
+    tte.tt_emb_forward_cached(plan, dp.g1, dp.g2, dp.g3, Wt, out)
+    assert_close(out.cpu().numpy(), oracle.forward_problem(p), f"{case}: TT-valued cache")
+    # the plain calls refuse the cached plan, the cached ones a plain plan
+    with pytest.raises(tte.TTEmbError) as ei:
+        tte.tt_emb_forward(plan, dp.g1, dp.g2, dp.g3, out)
+    assert ei.value.status == tte.TT_ERR_CACHE
+    dp.make_plan()
+    with pytest.raises(tte.TTEmbError) as ei:
+        tte.tt_emb_backward_cached(dp.plan, 0, dp.g1, dp.g2, dp.g3, dp.gout, *d, dW)
+    assert ei.value.status == tte.TT_ERR_CACHE
