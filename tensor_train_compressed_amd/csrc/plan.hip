@@ -980,6 +980,22 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
         hr[j] = (s0 + j < L && (s0 + j == 0 || ck[j] != ck[j + 1])) ? 1u : 0u;
         sum += hr[j];
     }
+    // every per-position load goes out before the scan's barriers: the
+    // lookup, its key's first and last position and scan word (a position
+    // past L reads key 0's), and with a hot-row cache the lookup's slot
+    int32_t pl[kSortItems], kst[kSortItems], kend[kSortItems], csv[kSortItems];
+    uint64_t ksc[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const int64_t s = min(s0 + j, L - 1);
+        const int32_t k = max(ck[j + 1], 0) / M3;
+        pl[j] = perm[s];
+        kst[j] = key_start[k];
+        kend[j] = key_end[k];
+        ksc[j] = key_scan[k];
+    }
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) csv[j] = cslot ? cslot[pl[j]] : -1;
     uint32_t tot;
     uint32_t run = block_exclusive_scan<uint32_t>(sum, wsum, &tot) + sbase;   // synchronises
     uint32_t lrank[kSortItems];
@@ -996,22 +1012,20 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                 run_start[rr] = (int32_t)s;
                 if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3)], 1u);   // rank in the tile
             }
-            const int32_t pl = perm[s];
             int32_t ro = rr + (int32_t)hr[j] - 1;
             if (cslot) {   // a hot row's lookups: -(slot + 1), its run: the slot
-                const int32_t cs = cslot[pl];
-                if (hr[j]) run_cslot[rr] = cs;
-                if (cs >= 0) ro = -(cs + 1);
+                if (hr[j]) run_cslot[rr] = csv[j];
+                if (csv[j] >= 0) ro = -(csv[j] + 1);
             }
-            run_of[pl] = ro;
-            const int32_t off = (int32_t)s - key_start[k];
+            run_of[pl[j]] = ro;
+            const int32_t off = (int32_t)s - kst[j];
             if (off % chunk == 0) {
-                const uint64_t ks = key_scan[k];
+                const uint64_t ks = ksc[j];
                 const int32_t g = (int32_t)(ks >> 32);
                 const int32_t c = (int32_t)(ks & 0xffffffffu) + off / chunk;
                 chunk_group[c] = g;
                 chunk_begin[c] = (int32_t)s;
-                chunk_end[c] = min((int32_t)s + chunk, key_end[k]);
+                chunk_end[c] = min((int32_t)s + chunk, kend[j]);
                 if (off == 0) group_rbase[g] = rr;
             }
             if (s == L - 1) {
