@@ -16,9 +16,9 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     const int32_t* __restrict__ chunk_begin, const int32_t* __restrict__ chunk_end,
     const int32_t* __restrict__ sorted_i3, const int32_t* __restrict__ sorted_bag,
     const float* __restrict__ g1, const float* __restrict__ g2, const float* __restrict__ g3,
-    const float* __restrict__ gout, float* __restrict__ dg1, float* __restrict__ dg2,
-    float* __restrict__ dg3, int32_t D) {
-    extern __shared__ float sm[];
+    const float* __restrict__ gout, double* __restrict__ a1, double* __restrict__ a2,
+    double* __restrict__ a3, int32_t D) {
+    extern __shared__ double smd[];
     const int32_t c = blockIdx.x;
     if (c >= ctrl[CTRL_NUM_CHUNKS]) return;
     const int32_t g = chunk_group[c];
@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     const int32_t i2 = local / d.m1, i1 = local % d.m1;
     const int32_t R = d.R, n1 = d.n1, n2 = d.n2, n3 = d.n3;
     const int32_t np = n1 * n2;
-    float* P = sm;            // [np][R]
-    float* dP = sm + np * R;  // [np][R]
+    double* dP = smd;                                      // [np][R]
+    float* P = reinterpret_cast<float*>(smd + np * R);     // [np][R]
     const float* A = g1 + d.o1 + (int64_t)i1 * n1 * R;
     const float* Bc = g2 + d.o2 + (int64_t)i2 * R * n2 * R;
     const float* C0 = g3 + d.o3;
@@ -43,13 +43,14 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
     __syncthreads();
     const int32_t b = chunk_begin[c], e_end = chunk_end[c];
     // dP[p][r2] = sum over the chunk's lookups of sum_j3 g[p*n3+j3] G3[i3][r2][j3]
+    // (fp64: a hot row's lookups add up many large, cancelling terms)
     for (int e = threadIdx.x; e < np * R; e += blockDim.x) {
         const int p = e / R, r2 = e % R;
-        float s = 0.f;
+        double s = 0.0;
         for (int32_t l = b; l < e_end; ++l) {
             const float* gr = gout + (int64_t)sorted_bag[l] * D + p * n3;
             const float* Cs = C0 + (int64_t)sorted_i3[l] * R * n3 + r2 * n3;
-            for (int j3 = 0; j3 < n3; ++j3) s = fmaf(gr[j3], Cs[j3], s);
+            for (int j3 = 0; j3 < n3; ++j3) s = fma((double)gr[j3], (double)Cs[j3], s);
         }
         dP[e] = s;
     }
@@ -60,28 +61,28 @@ __global__ __launch_bounds__(256) void k_bwd_generic(
         const int32_t rem = (int32_t)(w % (R * n3));
         const int r2 = rem / n3, j3 = rem % n3;
         const float* gr = gout + (int64_t)sorted_bag[l] * D;
-        float s = 0.f;
-        for (int p = 0; p < np; ++p) s = fmaf(P[p * R + r2], gr[p * n3 + j3], s);
-        atomicAdd(&dg3[d.o3 + (int64_t)sorted_i3[l] * R * n3 + r2 * n3 + j3], s);
+        double s = 0.0;
+        for (int p = 0; p < np; ++p) s = fma((double)P[p * R + r2], (double)gr[p * n3 + j3], s);
+        atomicAdd(&a3[d.o3 + (int64_t)sorted_i3[l] * R * n3 + r2 * n3 + j3], s);
     }
     __syncthreads();
     // dG1[i1][j1][r1] += sum_{j2,r2} dP[j1*n2+j2][r2] G2[i2][r1][j2][r2]
     for (int e = threadIdx.x; e < n1 * R; e += blockDim.x) {
         const int j1 = e / R, r1 = e % R;
-        float s = 0.f;
+        double s = 0.0;
         for (int j2 = 0; j2 < n2; ++j2)
             for (int r2 = 0; r2 < R; ++r2)
-                s = fmaf(dP[(j1 * n2 + j2) * R + r2], Bc[(r1 * n2 + j2) * R + r2], s);
-        atomicAdd(&dg1[d.o1 + (int64_t)i1 * n1 * R + e], s);
+                s = fma(dP[(j1 * n2 + j2) * R + r2], (double)Bc[(r1 * n2 + j2) * R + r2], s);
+        atomicAdd(&a1[d.o1 + (int64_t)i1 * n1 * R + e], s);
     }
     // dG2[i2][r1][j2][r2] += sum_j1 G1[i1][j1][r1] dP[j1*n2+j2][r2]
     for (int e = threadIdx.x; e < R * n2 * R; e += blockDim.x) {
         const int r1 = e / (n2 * R);
         const int rem = e % (n2 * R);
         const int j2 = rem / R, r2 = rem % R;
-        float s = 0.f;
-        for (int j1 = 0; j1 < n1; ++j1) s = fmaf(A[j1 * R + r1], dP[(j1 * n2 + j2) * R + r2], s);
-        atomicAdd(&dg2[d.o2 + (int64_t)i2 * R * n2 * R + e], s);
+        double s = 0.0;
+        for (int j1 = 0; j1 < n1; ++j1) s = fma((double)A[j1 * R + r1], dP[(j1 * n2 + j2) * R + r2], s);
+        atomicAdd(&a2[d.o2 + (int64_t)i2 * R * n2 * R + e], s);
     }
 }
 
@@ -1256,20 +1257,33 @@ static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2
     if (bwd_mfma_ok(p, g1, g2))
         return launch_bwd(p, g1, g2, g3, grad_out, dg1, dg2, dg3, kept, GradOut{0.f, 0}, s, hot_dw);
     if (p->cached) return TT_ERR_UNSUPPORTED;   // hot rows need the matrix-core kernels
+    // generic kernels: every core's gradient summed in fp64 accumulators
+    // (cleared here), then rounded into the caller's buffers
+    double* a1 = p->at<double>(p->lay.acc1);
+    double* a2 = p->at<double>(p->lay.acc2);
+    double* a3 = p->at<double>(p->lay.acc3);
     tt_status st = TT_OK;
-    if ((st = fill32(p, dg1, 0u, p->extent[0], s)) != TT_OK) return st;
-    if ((st = fill32(p, dg2, 0u, p->extent[1], s)) != TT_OK) return st;
-    if ((st = fill32(p, dg3, 0u, p->extent[2], s)) != TT_OK) return st;
-    if (p->lay.Cmax == 0) return TT_OK;
-    int maxp = 0;
-    for (int32_t t = 0; t < p->T; ++t) maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
-    const size_t lds = 2 * sizeof(float) * (size_t)maxp;
-    TT_LAUNCH(p, "k_bwd_generic", s, k_bwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
-                       p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key),
-                       p->at<int32_t>(p->lay.chunk_group), p->at<int32_t>(p->lay.chunk_begin),
-                       p->at<int32_t>(p->lay.chunk_end), p->at<int32_t>(p->lay.sorted_i3),
-                       p->at<int32_t>(p->lay.sorted_bag), g1, g2, g3, grad_out, dg1, dg2, dg3,
-                       p->D);
+    if ((st = fill32(p, a1, 0u, 2 * p->extent[0], s)) != TT_OK) return st;
+    if ((st = fill32(p, a2, 0u, 2 * p->extent[1], s)) != TT_OK) return st;
+    if ((st = fill32(p, a3, 0u, 2 * p->extent[2], s)) != TT_OK) return st;
+    if (p->lay.Cmax > 0) {
+        int maxp = 0;
+        for (int32_t t = 0; t < p->T; ++t)
+            maxp = std::max(maxp, p->tables[t].n[0] * p->tables[t].n[1] * p->tables[t].rank);
+        const size_t lds = (sizeof(double) + sizeof(float)) * (size_t)maxp;
+        TT_LAUNCH(p, "k_bwd_generic", s, k_bwd_generic, dim3((unsigned)p->lay.Cmax), dim3(256), lds, s, p->desc(),
+                  p->T, p->ctrl(), p->at<int32_t>(p->lay.group_key), p->at<int32_t>(p->lay.chunk_group),
+                  p->at<int32_t>(p->lay.chunk_begin), p->at<int32_t>(p->lay.chunk_end),
+                  p->at<int32_t>(p->lay.sorted_i3), p->at<int32_t>(p->lay.sorted_bag), g1, g2, g3, grad_out, a1,
+                  a2, a3, p->D);
+        TT_LAUNCH_CHECK();
+    }
+    const GradOut go{0.f, 0};
+    TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, a1, dg1, p->extent[0], a3, dg3,
+              p->extent[2], p->ctrl(), go);
+    TT_LAUNCH_CHECK();
+    TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, a2, dg2, p->extent[1], a3, dg3,
+              (int64_t)0, p->ctrl(), go);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }

@@ -40,8 +40,8 @@ namespace tt {
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3,
-                   bool fwd_only) {
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E2, int64_t E3, int64_t NFB,
+                   int64_t NB3, bool fwd_only) {
     Layout y{};
     // a forward-only plan carries none of the backward's buffers
     const int64_t LB = fwd_only ? 0 : L;
@@ -113,6 +113,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.pbuf = take(sizeof(float) * (size_t)GB * (size_t)PR);
     y.g3t = take(sizeof(float) * (size_t)E3);
     y.acc1 = take(fwd_only ? 0 : sizeof(double) * (size_t)E1);
+    y.acc2 = take(fwd_only ? 0 : sizeof(double) * (size_t)E2);   // the generic backward only
     y.acc3 = take(fwd_only ? 0 : sizeof(double) * (size_t)E3);
     // each run's dG3 term P^T S (R*n3 floats) goes over the run's S row when
     // that row is long enough, else into a buffer of its own
@@ -1172,10 +1173,10 @@ static std::atomic<int> g_timing_default{0};
 
 static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_out, int32_t* D_out,
                               int32_t* M3_out, int64_t* PR_out, int64_t* CN_out, int64_t* E1_out,
-                              int64_t* E3_out, int64_t* NFB_out, int64_t* NB3_out) {
+                              int64_t* E2_out, int64_t* E3_out, int64_t* NFB_out, int64_t* NB3_out) {
     if (!tables || T < 1) return TT_ERR_INVALID_ARG;
     if (T > kMaxTables) return TT_ERR_UNSUPPORTED;
-    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E2 = 0, E3 = 0, NFB = 0;
     int32_t D = -1, M3 = 1;
     for (int32_t t = 0; t < T; ++t) {
         const tt_emb_table& x = tables[t];
@@ -1198,6 +1199,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
         PR = std::max<int64_t>(PR, (int64_t)x.n[0] * x.n[1] * x.rank);
         CN = std::max<int64_t>(CN, (int64_t)x.rank * x.n[2]);
         E1 = std::max<int64_t>(E1, x.g_offset[0] + (int64_t)x.m[0] * x.n[0] * x.rank);
+        E2 = std::max<int64_t>(E2, x.g_offset[1] + (int64_t)x.m[1] * x.rank * x.n[1] * x.rank);
         E3 = std::max<int64_t>(E3, x.g_offset[2] + (int64_t)x.m[2] * x.rank * x.n[2]);
     }
     if (K * M3 >= (int64_t(1) << 31)) return TT_ERR_UNSUPPORTED;
@@ -1212,6 +1214,7 @@ static tt_status check_tables(const tt_emb_table* tables, int32_t T, int64_t* K_
     *PR_out = PR;
     *CN_out = CN;
     *E1_out = E1;
+    *E2_out = E2;
     *E3_out = E3;
     *NFB_out = NFB;
     return TT_OK;
@@ -1228,11 +1231,11 @@ static tt_status check_sizes(int32_t T, int64_t L, int64_t B, int32_t chunk) {
 namespace tt {
 size_t workspace_bytes_for(const tt_emb_table* tables, int32_t T, int64_t L, int64_t B, int32_t chunk,
                            bool fwd_only) {
-    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E2 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
-    if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3) != TT_OK) return 0;
+    if (check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E2, &E3, &NFB, &NB3) != TT_OK) return 0;
     if (check_sizes(T, L, B, chunk) != TT_OK) return 0;
-    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3, fwd_only).total;
+    return make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E2, E3, NFB, NB3, fwd_only).total;
 }
 }  // namespace tt
 
@@ -1247,9 +1250,9 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
                         const int64_t* offsets, int64_t L, int64_t B, int32_t chunk, void* workspace,
                         size_t workspace_bytes, bool fwd_only, hipStream_t s, const void* cache,
                         int64_t n_hot) {
-    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E3 = 0, NFB = 0, NB3 = 0;
+    int64_t K = 0, PR = 1, CN = 1, E1 = 0, E2 = 0, E3 = 0, NFB = 0, NB3 = 0;
     int32_t D = 0, M3 = 1;
-    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E3, &NFB, &NB3);
+    tt_status st = check_tables(tables, T, &K, &D, &M3, &PR, &CN, &E1, &E2, &E3, &NFB, &NB3);
     if (st != TT_OK) return st;
     st = check_sizes(T, L, B, chunk);
     if (st != TT_OK) return st;
@@ -1257,7 +1260,7 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
     if (((uintptr_t)workspace & 255) != 0) return TT_ERR_INVALID_ARG;
     if (cache && (fwd_only || n_hot < 0 || ((uintptr_t)cache & 255) != 0)) return TT_ERR_INVALID_ARG;
     if (fwd_only) NB3 = 0;
-    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E3, NFB, NB3, fwd_only);
+    const Layout lay = make_layout(T, L, B, chunk, K, D, M3, PR, CN, E1, E2, E3, NFB, NB3, fwd_only);
     if (workspace_bytes < lay.total) return TT_ERR_WORKSPACE;
 
     p->T = T; p->L = L; p->B = B; p->TB = (int64_t)T * B; p->chunk = chunk; p->D = D; p->K = K;

@@ -182,6 +182,7 @@ struct Layout {
                                              //     each run's dG3 term P^T S (else written over its S row)
     size_t acc1, acc3;                       // [extent of G1], [extent of G3] double: dG1 and
                                              //     dG3 accumulated in fp64 by the backward
+    size_t acc2;                             // [extent of G2] double: dG2 of the generic backward
     size_t xsum;                             // [2*ceil(L/64)][D] double: pieces of the row runs
                                              //     cut by the backward's windows
     size_t xcnt;                             // [ceil(L/64)] int32: spans done per long cut run
@@ -207,8 +208,8 @@ struct Layout {
 };
 
 Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, int32_t D,
-                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E3, int64_t NFB, int64_t NB3,
-                   bool fwd_only);
+                   int64_t M3, int64_t PR, int64_t CN, int64_t E1, int64_t E2, int64_t E3, int64_t NFB,
+                   int64_t NB3, bool fwd_only);
 
 // Kernel timing of a plan (tt_emb_set_timing): a start and an end event per
 // launch, recorded on the launch's stream, read back by tt_emb_kernel_times.

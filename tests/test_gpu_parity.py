@@ -752,3 +752,23 @@ def test_hot_row_cache(case):
     with pytest.raises(tte.TTEmbError) as ei:
         tte.tt_emb_backward_cached(dp.plan, 0, dp.g1, dp.g2, dp.g3, dp.gout, *d, dW)
     assert ei.value.status == tte.TT_ERR_CACHE
+
+
+def test_generic_path_realistic_size():
+    """A shape without matrix-core kernels (rank 12) at a realistic size
+    (1M rows, 4,096 Zipf-skewed bags of Poisson(20) lookups): the query
+    reports the generic kernels, and forward and backward match the oracle
+    on every element."""
+    import tensor_train_compressed_amd as tte
+    t = wl.Table(100 ** 3, (100, 100, 100), (4, 4, 4), 12)
+    lens = np.minimum(np.random.default_rng(5).poisson(20, 4096), 100)
+    p = wl.make_custom([t], lens, seed=13, zipf_alpha=1.05, with_grad=True)
+    dp = DevProblem(p, 256)
+    dp.make_plan()
+    q = tte.tt_emb_query_paths(dp.plan, dp.g1, dp.g2)
+    assert q["forward_path"] == tte.TT_PATH_GENERIC and q["backward_path"] == tte.TT_PATH_GENERIC
+    say("generic path", f"L={p.L}")
+    assert_close(dp.forward().cpu().numpy(), oracle.forward_problem(p), "generic forward")
+    ref = oracle.backward_problem(p)
+    for k, x in enumerate(dp.backward()):
+        assert_close(x.cpu().numpy(), ref[k], f"generic dG{k + 1}")
