@@ -239,7 +239,9 @@ def main():
         out_ = {"kernel": name, "us": round(rec["us"], 2), "launches_per_call": rec["per_call"]}
         tb = traffic_of(name)
         if tb is not None:
+            # measured HBM bytes (counters) over the event-timed launch
             out_["traffic"] = tb
+            out_["hbm_frac_measured"] = round(tb / sec / 1e9 / PEAK_HBM_GBS, 4)
         if f32 or f64:
             out_["fp32_tflops"] = round(f32 / sec / 1e12, 2)
             out_["fp64_tflops"] = round(f64 / sec / 1e12, 2)

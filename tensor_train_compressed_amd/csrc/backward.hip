@@ -1139,6 +1139,12 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     static_assert(kPrepBlocks * 256 >= kRunCounters, "prep zeroes the counters");
     const SumArgs sa{p->at<int32_t>(p->lay.sorted_bag), p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                      p->at<int32_t>(p->lay.run_start), p->L, gout, S, xpart};
+    // hot rows: dW starts at zero (every row written, also with no lookups);
+    // the fused step updates W in place
+    if (p->cached && !go.sgd && p->n_hot > 0) {
+        tt_status st = fill32(p, hot, 0u, p->n_hot * (int64_t)D, s);
+        if (st != TT_OK) return st;
+    }
     TT_LAUNCH(p, "k_bwd_sum", s, k_bwd_sum<DL>, dim3(kPrepBlocks + (p->L > 0 ? persistent_grid(4) : 0u)), dim3(256), 0, s,
                        sa, pa);
     TT_LAUNCH_CHECK();
@@ -1157,12 +1163,6 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
             TT_LAUNCH(p, "k_bwd_pfx", s, (k_bwd_pfx<N1, N2, R>), dim3((unsigned)grid), dim3(64 * PrefixBatch<N1, N2, R>::WAVES), lds, s,
                                p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.run_i3), g1, g2, pbuf);
             TT_LAUNCH_CHECK();
-        }
-        // hot rows: dW starts at zero (every row written); the fused step
-        // updates W in place
-        if (p->cached && !go.sgd && p->n_hot > 0) {
-            tt_status st = fill32(p, hot, 0u, p->n_hot * (int64_t)D, s);
-            if (st != TT_OK) return st;
         }
         RunsArgs ra{p->desc(), p->T, p->ctrl(), p->at<int32_t>(p->lay.xpiece), p->lay.xcap,
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),

@@ -689,7 +689,7 @@ def _top_pairs(p, k):
     return (top >> 40).astype(np.int32), (top & ((1 << 40) - 1)).astype(np.int64)
 
 
-@pytest.mark.parametrize("case", ["single", "multi6", "empty"])
+@pytest.mark.parametrize("case", ["single", "multi6", "empty", "all_hot", "no_lookups"])
 def test_hot_row_cache(case):
     """Hot rows kept uncompressed (the TT-Rec cache): forward, backward (kept
     and recomputed prefixes) and the fused step against the oracle's cached
@@ -700,10 +700,17 @@ def test_hot_row_cache(case):
         p = wl.make("multi26", batch=32, tables=6)
         p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
         p.lr = 0.01
+    elif case == "no_lookups":
+        t = wl.Table(4 * 5 * 300, (4, 5, 300), (4, 8, 4), 32)
+        p = wl.make_custom([t], np.zeros(16, np.int64), seed=7, with_grad=True)
     else:
         p = wl.make("train11m", batch=512)
     if case == "empty":
         ht, hr = np.zeros(0, np.int32), np.zeros(0, np.int64)
+    elif case == "all_hot":   # every row the batch looks up is hot: the cores get no gradient
+        ht, hr = _top_pairs(p, 1 << 30)
+    elif case == "no_lookups":
+        ht, hr = np.array([0, 0], np.int32), np.array([3, 4], np.int64)
     else:
         ht, hr = _top_pairs(p, 96)
         # a duplicate (served by its first slot) and a pair naming no row
@@ -718,7 +725,7 @@ def test_hot_row_cache(case):
     Wd = torch.from_numpy(W).to("cuda:0")
     out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
     tok = tte.tt_emb_forward_cached(plan, dp.g1, dp.g2, dp.g3, Wd, out, keep=True)
-    assert tok != 0
+    assert (tok != 0) == (p.L > 0)
     assert_close(out.cpu().numpy(), oracle.forward_cached(p, ht, hr, W), f"{case}: cached forward")
     ref = oracle.backward_cached(p, ht, hr, n)
     d = [torch.empty_like(x) for x in (dp.g1, dp.g2, dp.g3)]
@@ -737,7 +744,9 @@ def test_hot_row_cache(case):
         assert_close(g[k].cpu().numpy(), oracle.sgd(c, ref[k], p.lr), f"{case}: fused core {k + 1}")
     assert_close(Wf.cpu().numpy(), oracle.sgd(W, ref[3], p.lr), f"{case}: fused hot rows")
     # a cache holding the rows' own TT values: the plain model's output
-    if n:
+    if case in ("all_hot", "no_lookups"):
+        Wt = torch.from_numpy(oracle.materialise_rows(p, ht, hr).astype(np.float32)).to("cuda:0")
+    elif n:
         Wt = torch.from_numpy(oracle.materialise_rows(p, ht[:-1], hr[:-1]).astype(np.float32))
         Wt = torch.cat([Wt, torch.zeros(1, p.dim)]).to("cuda:0")
     else:
