@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
     TT_OK = 0,
     TT_ERR_INVALID_ARG = -1,  /* null pointer, bad dims, inconsistent sizes          */
-    TT_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits (see below)   */
+    TT_ERR_UNSUPPORTED = -2,  /* valid but outside the library's limits (see below)  */
     TT_ERR_WORKSPACE = -3,    /* workspace smaller than tt_emb_workspace_bytes      */
     TT_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed          */
     TT_ERR_DEVICE_FLAG = -5,  /* returned by tt_emb_get_error when the flag is set   */
@@ -76,7 +76,7 @@ typedef enum {
 #define TT_FLAG_BAD_OFFSETS 2 /* offsets[0] != 0, offsets[T*B] != L or a decrease   */
 #define TT_FLAG_INTERNAL 4    /* a scan's wait for an earlier tile hit its bound     */
 
-/* Limits of this build: N_t < 2^31, L < 2^31, T*B < 2^31, sum over tables of
+/* Limits of the library: N_t < 2^31, L < 2^31, T*B < 2^31, sum over tables of
  * m1*m2 < 2^30, R <= 64, n1*n2 <= 64, n3 <= 16, D <= 1024, T <= 4096. */
 
 /* One table (host memory). All tables of a call must have the same D. */

@@ -49,7 +49,7 @@ def _compile(src: str) -> str:
 
 # Host-side AddressSanitizer + UndefinedBehaviorSanitizer flags: every
 # -fsanitize goes to the host compilation only (device code is not
-# instrumented). A process that loads this build must preload clang's ASan
+# instrumented). A process that loads this library must preload clang's ASan
 # runtime (asan_runtime()) and point TT_EMB_LIBRARY at it.
 HOST_SANITIZE = [
     "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",

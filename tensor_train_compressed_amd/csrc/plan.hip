@@ -1602,7 +1602,7 @@ extern "C" const char* tt_emb_status_string(tt_status s) {
     switch (s) {
         case TT_OK: return "ok";
         case TT_ERR_INVALID_ARG: return "invalid argument";
-        case TT_ERR_UNSUPPORTED: return "unsupported (outside this build's limits)";
+        case TT_ERR_UNSUPPORTED: return "unsupported (outside the library's limits)";
         case TT_ERR_WORKSPACE: return "workspace too small";
         case TT_ERR_HIP: return "HIP runtime error";
         case TT_ERR_DEVICE_FLAG: return "device error flag set (bad index or offsets)";
