@@ -59,7 +59,98 @@ def parse():
     ap.add_argument("--phase-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB (reference for HBM counters)")
+    ap.add_argument("--forward-workload", default=None, choices=["multi26"],
+                    help="instead of the training step: plan and forward of this workload only "
+                         "(one JSON line with its forward rooflines)")
     return ap.parse_args()
+
+
+def forward_only(args):
+    """Plan and forward of the 26-table batch (26 tables of 10^3 to 4*10^7
+    rows, dim 64 = 4x4x4, rank 32, 32,768 bags per table, 8.5 M lookups):
+    per-call times and the forward kernels' rooflines, as for the main
+    workload."""
+    import numpy as np
+    import torch
+
+    import tensor_train_compressed_amd as tte
+    import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    p = wl.make(args.forward_workload)
+    t0 = p.tables[0]
+    n1, n2, n3 = t0.n
+    R, D = t0.rank, t0.dim
+    T, B, L = p.T, p.batch, p.L
+    tabs = tte.make_tables(p.tables, p.goff)
+    g = [torch.from_numpy(x).to(dev) for x in (p.g1, p.g2, p.g3)]
+    idx = torch.from_numpy(p.indices).to(dev)
+    off = torch.from_numpy(p.offsets).to(dev)
+    out = torch.empty((T * B, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tte.tt_emb_workspace_bytes(tabs, L, B, args.chunk), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    plan = lambda: tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream)
+    pl = plan()
+    q = tte.tt_emb_query_paths(pl, g[0], g[1])
+    for _ in range(args.warmup):
+        pl = plan()
+        tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream)
+    torch.cuda.synchronize()
+    assert tte.tt_emb_get_error(pl) == 0
+
+    def per_call_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = args.steps
+    plan_ms = per_call_ms(plan, reps)
+    pl = plan()
+    fwd_ms = per_call_ms(lambda: tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream), reps)
+    tte.tt_emb_set_timing(pl, True)
+    for _ in range(reps):
+        tte.tt_emb_forward(pl, g[0], g[1], g[2], out, stream=stream)
+    recs = tte.tt_emb_kernel_times(pl, stream)
+    tte.tt_emb_set_timing(pl, False)
+    agg = {}
+    for k, ms in recs:
+        agg.setdefault(k, []).append(ms)
+    us = {k: 1e3 * sum(v) / len(v) for k, v in agg.items()}
+    # executed work: one prefix product per (table, i1, i2) group, one suffix
+    # product per distinct (table, row), one add per lookup
+    bag = np.repeat(np.arange(T * B), np.diff(p.offsets))
+    tab = bag // B
+    m3 = np.array([t.m[2] for t in p.tables], dtype=np.int64)[tab]
+    U = int(np.unique(tab * (1 << 40) + p.indices // m3).size)
+    U_row = int(np.unique(tab * (1 << 40) + p.indices).size)
+    pre = U * 2 * n1 * n2 * R * R
+    suf = U_row * 2 * n1 * n2 * n3 * R
+    kb, kp = us.get("k_fwd_batch", 0.0) * 1e-6, us.get("k_pool", 0.0) * 1e-6
+    res = {
+        "metric": f"pooled bags/s, TT-EmbeddingBag forward of the {args.forward_workload} batch",
+        "value": round(T * B / (fwd_ms * 1e-3), 1), "unit": "bags/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic (seeded Zipf/Poisson indices, Gaussian cores)",
+        "config": {"workload": f"{args.forward_workload}: {T} tables, dim {D}={n1}x{n2}x{n3}, rank {R}, "
+                               f"B={B} bags per table", "lookups": L, "prefix_groups": U, "distinct_rows": U_row},
+        "paths": {"forward": q["forward_path"], "workspace_bytes": q["workspace_bytes"]},
+        "phases_ms_per_call": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4)},
+        "kernels_us": {k: round(v, 2) for k, v in sorted(us.items(), key=lambda x: -x[1])},
+        "roofline": {"kernel": "k_fwd_batch", "bound": "mfma", "achieved": round((pre + suf) / kb / 1e12, 3),
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round((pre + suf) / kb / 1e12 / PEAK_FP32_TFLOPS, 4), "flop_per_launch": int(pre + suf)},
+        "roofline_forward_call": {"kernels": "k_fwd_batch + k_pool", "us": round((kb + kp) * 1e6, 2),
+                                  "flop": int(pre + suf + L * D),
+                                  "frac": round((pre + suf + L * D) / (kb + kp) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+    }
+    print(json.dumps(res))
 
 
 def kernel_source_hash() -> str:
@@ -90,6 +181,9 @@ def main():
         print("bench.py runs on one GPU only: the library has no multi-GPU path; "
               "rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.forward_workload:
+        forward_only(args)
+        return
 
     import numpy as np
     import torch

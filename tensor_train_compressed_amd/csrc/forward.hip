@@ -305,6 +305,10 @@ __global__ __launch_bounds__(256, 3) void k_fwd_batch(FwdArgs a, int64_t cap, co
     }
 }
 
+// Bags of at most this many lookups on average take the several-bags-per-wave
+// pooling kernel.
+constexpr int64_t kShortBag = 16;
+
 // One wave per bag: sum the rows of the bag's lookups (in input order) from
 // the stage buffer (one row per run id) and write the bag's output row. Empty
 // bags get zeros. With a hot-row cache, a hot row's lookups carry -(slot + 1)
@@ -358,6 +362,54 @@ __global__ __launch_bounds__(256) void k_pool(const int32_t* __restrict__ bag_st
     if (h == 0) *reinterpret_cast<floatx4*>(out + q * D + c4) = acc;
 }
 
+// Short bags (a few lookups each): one wave takes BPW = 64/LPR bags, lane
+// group h (LPR lanes, a row's 16-byte pieces) owning bag BPW*wave + h and
+// summing its rows in input order. A wave pays its bag-bounds, run-id and
+// row round trips once for BPW bags, where the one-bag-per-wave kernel is
+// bound by those round trips when bags are short. Rows the group's bag does
+// not have are loaded (clamped) and not added.
+template <int D>
+__global__ __launch_bounds__(256) void k_pool_short(const int32_t* __restrict__ bag_start, int64_t TB,
+                                                    const int32_t* __restrict__ run_of,
+                                                    const float* __restrict__ stage,
+                                                    float* __restrict__ out, int32_t* ctrl,
+                                                    int32_t* __restrict__ fwd_claims,
+                                                    const float* __restrict__ hot) {
+    if (blockIdx.x == 0 && threadIdx.x < kFwdCounters) fwd_claims[threadIdx.x * 32] = 0;
+    constexpr int LPR = D / 4, BPW = 64 / LPR, U = 8;
+    static_assert(D % 4 == 0 && 64 % LPR == 0, "row shape");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int h = lane / LPR, i = lane % LPR, c4 = 4 * i;
+    const int64_t q = ((int64_t)blockIdx.x * 4 + w) * BPW + h;   // this lane group's bag
+    const bool qv = q < TB;
+    const int32_t b0 = qv ? bag_start[q] : 0;
+    const int32_t b1 = qv ? max(b0, bag_start[q + 1]) : b0;
+    const int32_t n = b1 - b0;
+    int32_t nmax = n;   // the wave's longest bag (wave-uniform)
+#pragma unroll
+    for (int m = LPR; m < 64; m *= 2) nmax = max(nmax, __shfl_xor(nmax, m));
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t base = 0; base < nmax; base += LPR) {
+        // lane i of the group: the run id of its bag's lookup base + i
+        const int32_t rv = base + i < n ? run_of[b0 + base + i] : 0;
+        const int jn = min(LPR, nmax - base);
+        for (int j0 = 0; j0 < jn; j0 += U) {
+            floatx4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t slot = __shfl(rv, h * LPR + min(j0 + u, LPR - 1));
+                const float* src = slot >= 0 ? stage + (int64_t)slot * D : hot + (int64_t)(-1 - slot) * D;
+                v[u] = *reinterpret_cast<const floatx4*>(src + c4);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (j0 + u < jn && base + j0 + u < n) acc += v[u];
+        }
+    }
+    if (qv) *reinterpret_cast<floatx4*>(out + q * D + c4) = acc;
+}
+
 template <int N1, int N2, int R, int N3, bool BW>
 static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, float* out, bool keep, hipStream_t s, const float* hot) {
@@ -385,9 +437,15 @@ static tt_status launch_fwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
         TT_LAUNCH_CHECK();
     }
     if (p->TB > 0) {
-        TT_LAUNCH(p, "k_pool", s, k_pool<N1 * N2 * N3>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
-                           p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
-                           p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims, hot);
+        constexpr int D = N1 * N2 * N3, BPW = 64 / (D / 4);
+        if (BPW > 1 && p->L <= kShortBag * p->TB)   // short bags: several per wave
+            TT_LAUNCH(p, "k_pool", s, k_pool_short<D>, dim3(grid_for(p->TB, 4 * BPW)), dim3(256), 0, s,
+                      p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
+                      p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims, hot);
+        else
+            TT_LAUNCH(p, "k_pool", s, k_pool<D>, dim3(grid_for(p->TB, 4)), dim3(256), 0, s,
+                      p->at<int32_t>(p->lay.bag_start), p->TB, p->at<int32_t>(p->lay.run_of),
+                      p->at<float>(p->lay.stage), out, p->ctrl(), fwd_claims, hot);
         TT_LAUNCH_CHECK();
     }
     return TT_OK;
