@@ -330,12 +330,37 @@ __global__ __launch_bounds__(kSortThreads) void k_split(const int64_t* __restric
         return sort_digit(ck, 0);
     };
     uint32_t dg[kSortItems];
-    if (T == 1) {   // one table: its descriptor read once (uniform)
-        const TabDev d0 = desc[0];
+    // the tables of the tile's first and last lookups: the number of table
+    // starts (tables 1 .. T-1) at or before each (every thread counts a
+    // share, added across the block); when they agree, every lookup of the
+    // tile is in that table
+    int64_t tu = 0;   // the tile's table, or -1: the tile spans tables
+    if (T > 1) {
+        __shared__ int32_t sTab[2];
+        if (threadIdx.x == 0) { sTab[0] = 0; sTab[1] = 0; }
+        __syncthreads();
+        const int64_t ef = tile * kSortTile, el = min<int64_t>(L, ef + kSortTile) - 1;
+        int32_t cf = 0, cl = 0;
+        for (int64_t t = 1 + threadIdx.x; t < T; t += kSortThreads) {
+            const int64_t st = off[t * B];
+            cf += st <= ef ? 1 : 0;
+            cl += st <= el ? 1 : 0;
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            cf += __shfl_xor(cf, m);
+            cl += __shfl_xor(cl, m);
+        }
+        if (lane == 0 && (cf | cl)) { atomicAdd(&sTab[0], cf); atomicAdd(&sTab[1], cl); }
+        __syncthreads();
+        tu = sTab[0] == sTab[1] ? sTab[0] : -1;
+    }
+    if (tu >= 0) {   // one table for the whole tile: its descriptor read once (uniform)
+        const TabDev d0 = desc[tu];
 #pragma unroll
         for (int slot = 0; slot < kSortItems; ++slot) {
             const int64_t e = base + slot * 64 + lane;
-            dg[slot] = e < L ? split_one(e, xv[slot], d0, 0) : 0u;
+            dg[slot] = e < L ? split_one(e, xv[slot], d0, tu) : 0u;
         }
     } else {
 #pragma unroll
@@ -897,13 +922,48 @@ __global__ __launch_bounds__(kSortThreads) void k_groups(const int32_t* __restri
     }
 }
 
-// G3 row of a run of key k and digit i3: its table's first G3 row plus i3.
+// The table holding both `first` and `last`, values of a per-table start
+// field that grows with the table index (key_base, fb_base), or -1 when they
+// lie in different tables: the number of starts of tables 1 .. T-1 at or
+// before each, counted by every thread of the block (the block's threads all
+// call it; it synchronises the block).
+template <class Start>
+__device__ int32_t block_table_of(const TabDev* __restrict__ desc, int32_t T, int64_t first, int64_t last,
+                                  Start start) {
+    if (T <= 1) return 0;
+    __shared__ int32_t sTab[2];
+    if (threadIdx.x == 0) { sTab[0] = 0; sTab[1] = 0; }
+    __syncthreads();
+    int32_t cf = 0, cl = 0;
+    for (int64_t t = 1 + threadIdx.x; t < T; t += blockDim.x) {
+        const int64_t st = start(desc[t]);
+        cf += st <= first ? 1 : 0;
+        cl += st <= last ? 1 : 0;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        cf += __shfl_xor(cf, m);
+        cl += __shfl_xor(cl, m);
+    }
+    if ((threadIdx.x & 63) == 0 && (cf | cl)) { atomicAdd(&sTab[0], cf); atomicAdd(&sTab[1], cl); }
+    __syncthreads();
+    const int32_t a = sTab[0], b = sTab[1];
+    __syncthreads();   // sTab is free for the next call
+    return a == b ? a : -1;
+}
+
+// G3 row of a run of key k and digit i3: its table's first G3 row plus i3
+// (tu >= 0: the caller knows the table).
 __device__ __forceinline__ int32_t bucket3(const TabDev* __restrict__ desc, int32_t T, int32_t CN, int32_t k,
-                                           int32_t i3) {
-    int lo = 0, hi = T;   // last table with key_base <= k
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (desc[mid].key_base <= k) lo = mid; else hi = mid;
+                                           int32_t i3, int32_t tu = -1) {
+    int lo = tu;
+    if (lo < 0) {
+        lo = 0;
+        int hi = T;   // last table with key_base <= k
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (desc[mid].key_base <= k) lo = mid; else hi = mid;
+        }
     }
     return (int32_t)(desc[lo].o3 / CN) + i3;
 }
@@ -921,11 +981,16 @@ struct SlotOf {
     int64_t kb;
 };
 __device__ __forceinline__ SlotOf slot_of(const TabDev* __restrict__ desc, int32_t T, int64_t K, int64_t b,
-                                          const uint64_t* __restrict__ key_scan, const int32_t* __restrict__ ctrl) {
-    int lo = 0, hi = T;   // last table with fb_base <= b
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
+                                          const uint64_t* __restrict__ key_scan, const int32_t* __restrict__ ctrl,
+                                          int32_t tu = -1) {
+    int lo = tu;
+    if (lo < 0) {
+        lo = 0;
+        int hi = T;   // last table with fb_base <= b
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (desc[mid].fb_base <= b) lo = mid; else hi = mid;
+        }
     }
     SlotOf o;
     o.d = desc[lo];
@@ -981,6 +1046,11 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
         hr[j] = (s0 + j < L && (s0 + j == 0 || ck[j] != ck[j + 1])) ? 1u : 0u;
         sum += hr[j];
     }
+    // the tile's keys lie in one table (usually): its index for the G3 rows
+    const int32_t tuk = n3cnt ? block_table_of(desc, T, skey[tile * kSortTile] / M3,
+                                               skey[min<int64_t>(L, (tile + 1) * kSortTile) - 1] / M3,
+                                               [](const TabDev& d) { return (int64_t)d.key_base; })
+                              : -1;
     // every per-position load goes out before the scan's barriers: the
     // lookup, its key's first and last position and scan word (a position
     // past L reads key 0's), and with a hot-row cache the lookup's slot
@@ -1011,7 +1081,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                 const int32_t r3 = ck[j + 1] - k * M3;
                 run_i3[rr] = r3;
                 run_start[rr] = (int32_t)s;
-                if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3)], 1u);   // rank in the tile
+                if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3, tuk)], 1u);   // rank in the tile
             }
             int32_t ro = rr + (int32_t)hr[j] - 1;
             if (cslot) {   // a hot row's lookups: -(slot + 1), its run: the slot
@@ -1048,7 +1118,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
         for (int j = 0; j < kSortItems; ++j) {
             if (s0 + j < L && hr[j]) {
                 const int32_t k = ck[j + 1] / M3;
-                const int32_t b = bucket3(desc, T, CN, k, ck[j + 1] - k * M3);
+                const int32_t b = bucket3(desc, T, CN, k, ck[j + 1] - k * M3, tuk);
                 run_rank[r] = (int32_t)(sh3[b] + lrank[j]);
                 run_bkt[r] = b;
             }
@@ -1064,10 +1134,12 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
     const int64_t nst = (NFB + kSlotTile - 1) / kSlotTile;
     for (int64_t jt0 = (int64_t)blockIdx.x * TPR; jt0 < nst; jt0 += (int64_t)gridDim.x * TPR) {
         if (threadIdx.x < TPR * kXcds) ccnt[threadIdx.x / kXcds][threadIdx.x % kXcds] = 0u;
-        __syncthreads();
         const int64_t b = jt0 * kSlotTile + threadIdx.x;
+        const int32_t tus = block_table_of(desc, T, jt0 * kSlotTile, min<int64_t>(NFB, (jt0 + TPR) * kSlotTile) - 1,
+                                           [](const TabDev& d) { return (int64_t)d.fb_base; });
+        __syncthreads();   // ccnt cleared
         if (b < NFB) {
-            const SlotOf o = slot_of(desc, T, K, b, key_scan, ctrl);
+            const SlotOf o = slot_of(desc, T, K, b, key_scan, ctrl, tus);
             if (o.gs1 - (o.gs0 + kFwdBatch * o.jb) > 0) atomicAdd(&ccnt[threadIdx.x / kSlotTile][o.cls], 1u);
         }
         __syncthreads();
@@ -1106,8 +1178,10 @@ __global__ __launch_bounds__(kSlotTile) void k_batches(const TabDev* __restrict_
     BatchRec r;
     memset(&r, 0, sizeof(r));
     SlotOf o{};
+    const int32_t tus = block_table_of(desc, T, jt * kSlotTile, min<int64_t>(NFB, (jt + 1) * kSlotTile) - 1,
+                                       [](const TabDev& d) { return (int64_t)d.fb_base; });
     if (b < NFB) {
-        o = slot_of(desc, T, K, b, key_scan, ctrl);
+        o = slot_of(desc, T, K, b, key_scan, ctrl, tus);
         r.g0 = o.gs0 + kFwdBatch * o.jb;
         r.ng = max(0, min(kFwdBatch, o.gs1 - r.g0));
         if (r.ng > 0) {
