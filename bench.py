@@ -321,8 +321,9 @@ def main():
         "k_fwd_batch": (pre + suf, 0, 0), "k_fwd_batch_keep": (pre + suf, 0, 0),
         "k_pool": (L * D, 0, 4 * L * D + 4 * B * D),
         "k_bwd_sum": (0, L * D, 4 * L * D + 4 * U_row * D),
-        "k_bwd_runs_c3": (suf, suf, 0), "k_bwd_dg3": (0, U_row * R * n3, 4 * U_row * R * n3),
-        "k_bwd_dg2": (0, pre, 0), "k_bwd_dg1": (0, pre, 0),
+        "k_bwd_runs_c3": (suf, suf, 0),
+        # dG3 (c3 row sums), dG1 and dG2 in one launch
+        "k_bwd_dg123": (0, 2 * pre + U_row * R * n3, 0),
         "k_sgd": (2 * core_elems, 0, 12 * core_elems),
     }
     PEAK_FP64_TFLOPS = 78.6

@@ -105,13 +105,38 @@ __device__ __forceinline__ void put_grad(float* p, float g, GradOut o) {
 __global__ __launch_bounds__(256) void k_bwd_finish(const double* __restrict__ a1, float* __restrict__ dg1,
                                                     int64_t n1, const double* __restrict__ a3,
                                                     float* __restrict__ dg3, int64_t n3, int32_t* ctrl,
-                                                    GradOut go) {
+                                                    GradOut go, const float* __restrict__ b2,
+                                                    float* __restrict__ g2, int64_t n2) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     if (tid == 0) ctrl[CTRL_NUM_XPIECES] = 0;   // the next backward on this plan appends from 0
     for (int64_t i = tid; i < n1; i += nth) {
         const double a = a1[i];
         if (!go.sgd || a != 0.0) put_grad(dg1 + i, (float)a, go);
+    }
+    // fused SGD: G2 from the dG2 buffer (rounded to fp32 already; zero on the
+    // slices no lookup touched, which keep their values), four elements per
+    // thread and step when both buffers are 16-byte aligned
+    int64_t done = 0;
+    if ((((uintptr_t)b2 | (uintptr_t)g2) & 15) == 0) {
+        const int64_t n4 = n2 / 4;
+        const floatx4* b4 = reinterpret_cast<const floatx4*>(b2);
+        floatx4* g4 = reinterpret_cast<floatx4*>(g2);
+        for (int64_t i = tid; i < n4; i += nth) {
+            const floatx4 b = b4[i];
+            if (b[0] != 0.f || b[1] != 0.f || b[2] != 0.f || b[3] != 0.f) {
+                floatx4 g = g4[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (b[e] != 0.f) g[e] = fmaf(go.neg_lr, b[e], g[e]);
+                g4[i] = g;
+            }
+        }
+        done = n4 * 4;
+    }
+    for (int64_t i = done + tid; i < n2; i += nth) {
+        const float b = b2[i];
+        if (b != 0.f) put_grad(g2 + i, b, go);
     }
     for (int64_t i = tid; i < n3; i += nth) {
         const double a = a3[i];
@@ -185,17 +210,20 @@ __global__ __launch_bounds__(256) void k_sgd(SgdArgs a, float lr) {
 //               dP is stored over the group's P (a split group's pieces go to
 //               fp64 slots, the last piece adds them); k_bwd_runs adds P^T S
 //               to the fp64 dG3 accumulator with atomics instead
-// k_bwd_dg3     one workgroup per G3 row: dG3[i3] = sum of its runs' c3 rows
-// k_bwd_dg1     one wave per batch slot, slice-major:
+// k_bwd_dg123   three kinds of workgroups in one launch:
+//               dG3: one per G3 row, dG3[i3] = sum of its runs' c3 rows
+//               dG1: one wave per batch slot, slice-major,
 //                 dG1[i1] += dP G2[i2]^T    (fp64 products, one fp64 atomic
 //                                            per element and group)
-// k_bwd_dg2     one wave per (slice, 16-column tile of dG2[i2]):
+//               dG2: one wave per (slice, 16-column tile of dG2[i2]),
 //                 dG2[i2] = sum G1[i1]^T dP (fp64 products, plain stores, owned)
 // k_bwd_finish  dG1 (and atomics-mode dG3) <- their fp64 accumulators, rounded
 //               to fp32
-// With the fused SGD (GradOut::sgd) dG3, dG2 and dG1 are not stored: each
-// kernel applies G <- G - lr * dG to the core element instead, and only on
-// the slices and rows the batch touches.
+// With the fused SGD (GradOut::sgd) the gradients are not stored: dG3's
+// workgroups and k_bwd_finish apply G <- G - lr * dG to the core elements
+// instead, only on the rows and slices the batch touches; dG2 goes to a
+// buffer (zero on untouched slices) that k_bwd_finish applies to G2, since
+// G2 is read for dG1 in the same launch.
 
 __device__ __forceinline__ bool row_head(const int32_t* __restrict__ skey, int64_t s) {
     return s == 0 || skey[s - 1] != skey[s];
@@ -331,7 +359,7 @@ struct SlotArgs {
 
 // Workgroups past the first nspan (when bucketing dG3): each run's place in
 // the list of its bucket's runs (its bucket's start plus its rank in the
-// bucket), read by k_bwd_dg3.
+// bucket), read by dG3's workgroups of k_bwd_dg123.
 template <int DL>
 __global__ __launch_bounds__(1024) void k_bwd_cross(double* __restrict__ xpart, int32_t* __restrict__ xcnt,
                                                     CrossRef x, float* __restrict__ S,
@@ -844,7 +872,7 @@ __global__ __launch_bounds__(256) void k_bwd_runs(RunsArgs a) {
 // Each run's dG3 term P^T S is stored as a row of its own: row r of c3 (at
 // row stride c3s; c3 is the S buffer itself when an S row holds R*n3 floats,
 // each run's term then replacing its S, which only this wave reads), and
-// k_bwd_dg3 sums the rows of each G3 row's bucket. Device atomics from every
+// k_bwd_dg123 sums the rows of each G3 row's bucket. Device atomics from every
 // CU on the same few hundred G3 slices saturate the memory-side atomic
 // units, and LDS float atomics are slow on the CU; plain stores avoid both.
 template <int N1, int N2, int R, int N3>
@@ -855,31 +883,35 @@ __global__ __launch_bounds__(256, R >= 64 ? 2 : 3) void k_bwd_runs_c3(RunsArgs a
 }
 
 // dG3[i3] = sum of the c3 rows of the runs in bucket i3 (bucket_runs lists
-// them), in fp64: one workgroup per G3 row, wave w on rows w, w + 16, ... of
-// the bucket, GB rows in flight; the 16 waves' sums are added in LDS at the
-// end.
-template <int CN>
-__global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3start,
-                                                  const int32_t* __restrict__ bucket_runs,
-                                                  const float* __restrict__ c3, int64_t c3s,
-                                                  float* __restrict__ dg3, GradOut go) {
-    constexpr int PL = CN / 64, WAVES = 16, GB = 16;
+// them), in fp64: one workgroup of WAVES waves per G3 row, wave w on rows w,
+// w + WAVES, ... of the bucket, GB rows in flight; the waves' sums are added
+// in LDS at the end.
+struct Dg3Args {
+    const int32_t* i3start;
+    const int32_t* bucket_runs;
+    const float* c3;
+    int64_t c3s;
+    float* dg3;
+    GradOut go;
+};
+
+template <int CN, int WAVES>
+__device__ __forceinline__ void dg3_body(const Dg3Args& a, int32_t row, double (&red)[WAVES][CN]) {
+    constexpr int PL = CN / 64, GB = 16;
     static_assert(CN % 64 == 0, "shape");
-    __shared__ double red[WAVES][CN];
-    const int32_t row = blockIdx.x;
-    const int32_t b = i3start[row], e = i3start[row + 1];
-    if (go.sgd && b == e) return;   // an untouched G3 row keeps its values
+    const int32_t b = a.i3start[row], e = a.i3start[row + 1];
+    if (a.go.sgd && b == e) return;   // an untouched G3 row keeps its values
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     double acc[PL];
 #pragma unroll
     for (int k = 0; k < PL; ++k) acc[k] = 0.0;
     for (int32_t j0 = b + w; j0 < e; j0 += WAVES * GB) {
         // lane j < GB: the run of bucket row j0 + WAVES * j
-        const int32_t rl = bucket_runs[min(j0 + WAVES * min(lane, GB - 1), e - 1)];
+        const int32_t rl = a.bucket_runs[min(j0 + WAVES * min(lane, GB - 1), e - 1)];
         float x[GB][PL];
 #pragma unroll
         for (int j = 0; j < GB; ++j) {
-            const float* src = c3 + (int64_t)__builtin_amdgcn_readlane(rl, j) * c3s + lane * PL;
+            const float* src = a.c3 + (int64_t)__builtin_amdgcn_readlane(rl, j) * a.c3s + lane * PL;
 #pragma unroll
             for (int k = 0; k < PL; ++k) x[j][k] = src[k];
         }
@@ -893,11 +925,11 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3
 #pragma unroll
     for (int k = 0; k < PL; ++k) red[w][lane * PL + k] = acc[k];
     __syncthreads();
-    for (int t = threadIdx.x; t < CN; t += 1024) {
+    for (int t = threadIdx.x; t < CN; t += 64 * WAVES) {
         double x = 0.0;
 #pragma unroll
         for (int k = 0; k < WAVES; ++k) x += red[k][t];
-        put_grad(dg3 + (int64_t)row * CN + t, (float)x, go);
+        put_grad(a.dg3 + (int64_t)row * CN + t, (float)x, a.go);
     }
 }
 
@@ -907,19 +939,39 @@ __global__ __launch_bounds__(1024) void k_bwd_dg3(const int32_t* __restrict__ i3
 // when n1 = 4), operands read straight from memory (each dP element once;
 // the next UNR steps' loads issued before the current ones' products), no
 // LDS and no barrier. The wave owns its columns: plain stores.
+struct Dg2Args {
+    const TabDev* desc;
+    int32_t T;
+    const int32_t* ctrl;
+    int64_t K;
+    const uint64_t* key_scan;
+    const int32_t* group_key;
+    const float* dpg;
+    const float* g1;
+    float* dg2;
+    int64_t n_i2;
+    GradOut go;
+};
+
 template <int N1, int N2, int R>
-__global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc, int32_t T,
-                                                 const int32_t* __restrict__ ctrl, int64_t K,
-                                                 const uint64_t* __restrict__ key_scan,
-                                                 const int32_t* __restrict__ group_key,
-                                                 const float* __restrict__ dpg, const float* __restrict__ g1,
-                                                 float* __restrict__ dg2, int64_t n_i2, GradOut go) {
+__device__ __forceinline__ void dg2_body(const Dg2Args& x, int64_t blk) {
+    const TabDev* __restrict__ desc = x.desc;
+    const int32_t T = x.T;
+    const int32_t* __restrict__ ctrl = x.ctrl;
+    const int64_t K = x.K;
+    const uint64_t* __restrict__ key_scan = x.key_scan;
+    const int32_t* __restrict__ group_key = x.group_key;
+    const float* __restrict__ dpg = x.dpg;
+    const float* __restrict__ g1 = x.g1;
+    float* __restrict__ dg2 = x.dg2;
+    const int64_t n_i2 = x.n_i2;
+    const GradOut go = x.go;
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, CT = N2R / 16, UNR = 8;
     static_assert(16 % N1 == 0 && R % 16 == 0 && N2R % 16 == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
     // wave-uniform task: the group loop is scalar control flow (no exec-mask
     // loop, whose head waits for every load in flight)
-    const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t task = blk * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (task >= n_i2 * CT) return;
     const int32_t bi = (int32_t)(task / CT);
     const int ct = (int)(task % CT);
@@ -1017,16 +1069,29 @@ __global__ __launch_bounds__(256) void k_bwd_dg2(const TabDev* __restrict__ desc
 // Waves take the batch slots in slice-major order (the planner's place map),
 // so waves that run together work on different i1 rows of dG1 rather than
 // piling atomics on the same ones.
+struct Dg1Args {
+    const BatchRec* recs;
+    int64_t cap;
+    const int32_t* ctrl;
+    const int32_t* place;
+    const float* dpg;
+    const float* g2;
+    double* dg1;
+};
+
 template <int N1, int N2, int R>
-__global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ recs, int64_t cap,
-                                                 const int32_t* __restrict__ ctrl,
-                                                 const int32_t* __restrict__ place,
-                                                 const float* __restrict__ dpg, const float* __restrict__ g2,
-                                                 double* __restrict__ dg1) {
+__device__ __forceinline__ void dg1_body(const Dg1Args& x, int64_t blk) {
+    const BatchRec* __restrict__ recs = x.recs;
+    const int64_t cap = x.cap;
+    const int32_t* __restrict__ ctrl = x.ctrl;
+    const int32_t* __restrict__ place = x.place;
+    const float* __restrict__ dpg = x.dpg;
+    const float* __restrict__ g2 = x.g2;
+    double* __restrict__ dg1 = x.dg1;
     constexpr int N2R = N2 * R, PR = N1 * N2R, RT = R / 16, KS = N2R / 16, UNR = 2, MT = kFwdBatch * N1 / 16;
     static_assert(16 % N1 == 0 && MT >= 1 && R % 16 == 0 && N2R % 16 == 0 && KS % (2 * UNR) == 0, "shape");
     const int lane = threadIdx.x & 63, col = lane & 15, q = lane >> 4;
-    const int64_t k = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t k = blk * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (k >= cap) return;
     const int32_t pos = place[k];
     const int64_t nl = ctrl[CTRL_NUM_BATCHES];
@@ -1104,21 +1169,40 @@ __global__ __launch_bounds__(256) void k_bwd_dg1(const BatchRec* __restrict__ re
         }
 }
 
+// dG3, dG1 and dG2 in one launch: workgroups below nb3 reduce one G3 row's
+// c3 rows each, the next nb1 take dG1's batch slots, the rest dG2's (slice,
+// column tile) tasks. None reads what another writes (with the fused SGD,
+// dG2 goes to a buffer of its own that k_bwd_finish applies, as G2 is read
+// for dG1; G3, updated here, is read by none of them). The dG1 and dG2 waves
+// run chains of loads and fp64 matrix-core steps, the dG3 waves stream c3
+// rows: together they keep more waves on each SIMD than any one of them.
+template <int N1, int N2, int R, int CN>
+__global__ __launch_bounds__(256, 5) void k_bwd_dg123(Dg3Args a3, Dg1Args a1, Dg2Args a2, int64_t nb3, int64_t nb1) {
+    __shared__ double red[4][CN];
+    const int64_t blk = blockIdx.x;
+    if (blk < nb3) dg3_body<CN, 4>(a3, (int32_t)blk, red);
+    else if (blk < nb3 + nb1) dg1_body<N1, N2, R>(a1, blk - nb3);
+    else dg2_body<N1, N2, R>(a2, blk - nb3 - nb1);
+}
+
 // Fused SGD (go.sgd): dg1/dg2/dg3 are the cores g1/g2/g3 themselves. Every
 // kernel reads the cores it needs before any kernel updates them: the run
-// kernel (G3) precedes k_bwd_dg3, k_bwd_dg1 (G2) precedes k_bwd_dg2, which
-// (G1) precedes k_bwd_finish.
+// kernel (G3) precedes k_bwd_dg123, which updates G3, reads G1 and G2 and
+// writes dG2 to a buffer; k_bwd_finish then updates G1 and G2.
 template <int N1, int N2, int R, int N3>
 static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const float* g2,
                                  const float* g3, const float* gout, float* dg1, float* dg2,
                                  float* dg3, bool kept, GradOut go, hipStream_t s, float* hot) {
-    // dG3 reduced per G3 row from per-run terms (k_bwd_dg3 writes every row
+    // dG3 reduced per G3 row from per-run terms (k_bwd_dg123 writes every row
     // of the buffer, gaps included), unless some table's G3 rows are not
     // aligned to R*n3: then device atomics into an fp64 accumulator
     const bool bucket3 = p->nb3 > 0 && p->L > 0;
-    if (!p->packed && !go.sgd) {
+    // dG2's destination: the gradient, or, with the fused SGD, a buffer that
+    // k_bwd_finish applies to G2 (k_bwd_dg123 reads G2 for dG1 meanwhile)
+    float* d2 = go.sgd ? p->at<float>(p->lay.acc2) : dg2;
+    if (!p->packed) {
         // elements outside every table's slices are zero in the gradients
-        tt_status st = fill32(p, dg2, 0u, p->extent[1], s);
+        tt_status st = fill32(p, d2, 0u, p->extent[1], s);
         if (st != TT_OK) return st;
     }
     constexpr int DL = N1 * N2 * N3 / 64, D = N1 * N2 * N3, CN = R * N3;
@@ -1127,6 +1211,9 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
     double* xpart = p->at<double>(p->lay.xsum);
     float* S = p->at<float>(p->lay.stage);
     float* pbuf = p->at<float>(p->lay.pbuf);
+    // each run's dG3 term over its own S row when the row holds it
+    float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);
+    const int64_t c3s = CN <= D ? D : CN;
     const CrossRef xr{p->at<int32_t>(p->lay.skey), p->at<int32_t>(p->lay.rid),
                       p->at<int32_t>(p->lay.run_start), p->L};
     const int64_t nwin = (p->L + kWin - 1) / kWin;
@@ -1170,38 +1257,33 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     p->at<int32_t>(p->lay.gdone), p->at<int32_t>(p->lay.claims),
                     p->cached ? p->at<int32_t>(p->lay.run_cslot) : nullptr, hot, go};
         if (bucket3) {
-            // each run's dG3 term over its own S row when the row holds it
-            float* c3 = CN <= D ? S : p->at<float>(p->lay.c3);
-            const int64_t c3s = CN <= D ? D : CN;
             TT_LAUNCH(p, "k_bwd_runs_c3", s, (k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra, c3,
                                c3s);
             TT_LAUNCH_CHECK();
-            TT_LAUNCH(p, "k_bwd_dg3", s, (k_bwd_dg3<CN>), dim3((unsigned)p->nb3), dim3(1024), 0, s,
-                               p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3,
-                               go);
         } else {
             TT_LAUNCH(p, "k_bwd_runs", s, (k_bwd_runs<N1, N2, R, N3>), dim3(persistent_grid(4)), dim3(256), 0, s, ra);
         }
         TT_LAUNCH_CHECK();
     }
     {
-        // dP of every group now sits over its P; dG1 first: it reads G2,
-        // which the fused SGD updates in k_bwd_dg2
-        const int64_t w1 = p->n_fb;
-        if (w1 > 0) {
-            TT_LAUNCH(p, "k_bwd_dg1", s, (k_bwd_dg1<N1, N2, R>), dim3((unsigned)((w1 + 3) / 4)), dim3(256), 0, s,
-                               p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.batch_place),
-                               pbuf, g2, acc1);
+        // dP of every group now sits over its P, each run's c3 row over its
+        // S: dG3, dG1 and dG2 in one launch
+        const int64_t nb3 = bucket3 ? p->nb3 : 0;
+        const int64_t nb1 = (p->n_fb + 3) / 4;
+        const int64_t nb2 = (p->n_i2 * (N2 * R / 16) + 3) / 4;
+        const Dg3Args a3{p->at<int32_t>(p->lay.i3start), p->at<int32_t>(p->lay.bucket_runs), c3, c3s, dg3, go};
+        const Dg1Args a1{p->at<BatchRec>(p->lay.batch), p->n_fb, p->ctrl(), p->at<int32_t>(p->lay.batch_place),
+                         pbuf, g2, acc1};
+        const Dg2Args a2{p->desc(), p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan),
+                         p->at<int32_t>(p->lay.group_key), pbuf, g1, d2, p->n_i2, GradOut{0.f, 0}};
+        if (nb3 + nb1 + nb2 > 0) {
+            TT_LAUNCH(p, "k_bwd_dg123", s, (k_bwd_dg123<N1, N2, R, CN>), dim3((unsigned)(nb3 + nb1 + nb2)), dim3(256), 0,
+                      s, a3, a1, a2, nb3, nb1);
             TT_LAUNCH_CHECK();
         }
-        const int64_t w2 = p->n_i2 * (N2 * R / 16);
-        TT_LAUNCH(p, "k_bwd_dg2", s, (k_bwd_dg2<N1, N2, R>), dim3((unsigned)((w2 + 3) / 4)), dim3(256), 0, s, p->desc(),
-                  p->T, p->ctrl(), p->K, p->at<uint64_t>(p->lay.key_scan), p->at<int32_t>(p->lay.group_key), pbuf, g1,
-                  dg2, p->n_i2, go);
-        TT_LAUNCH_CHECK();
     }
-    TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, acc1, dg1, p->extent[0], acc3, dg3,
-                       bucket3 ? 0 : p->extent[2], p->ctrl(), go);
+    TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(go.sgd ? 1024 : 256), dim3(256), 0, s, acc1, dg1, p->extent[0],
+              acc3, dg3, bucket3 ? 0 : p->extent[2], p->ctrl(), go, d2, dg2, go.sgd ? p->extent[1] : 0);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }
@@ -1210,7 +1292,7 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
 bool bwd_mfma_ok(const tt_emb_plan_s* p, const float* g1, const float* g2) {
     // the prologue reads G1 rows and the G2 slice as 16-byte vectors
     if (!p->uniform || !p->off4 || ((uintptr_t)g1 & 15) != 0 || ((uintptr_t)g2 & 15) != 0) return false;
-    // k_bwd_dg2 stores each table's slices once: tables sharing G2 take the
+    // dG2 is stored once per table slice: tables sharing G2 take the
     // general path, which adds every table's terms
     if (p->g2_overlap) return false;
     // the batch's run i3 list is staged in LDS
@@ -1280,10 +1362,10 @@ static tt_status backward_impl(tt_emb_plan_t p, const float* g1, const float* g2
     }
     const GradOut go{0.f, 0};
     TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, a1, dg1, p->extent[0], a3, dg3,
-              p->extent[2], p->ctrl(), go);
+              p->extent[2], p->ctrl(), go, nullptr, nullptr, (int64_t)0);
     TT_LAUNCH_CHECK();
     TT_LAUNCH(p, "k_bwd_finish", s, k_bwd_finish, dim3(256), dim3(256), 0, s, a2, dg2, p->extent[1], a3, dg3,
-              (int64_t)0, p->ctrl(), go);
+              (int64_t)0, p->ctrl(), go, nullptr, nullptr, (int64_t)0);
     TT_LAUNCH_CHECK();
     return TT_OK;
 }
