@@ -36,7 +36,13 @@
  * Streams: every call that takes `stream` enqueues its kernels on that HIP
  * stream (a hipStream_t passed as void*; NULL is the null stream) and returns
  * without waiting, except tt_emb_get_error and tt_emb_plan_counts, which
- * synchronise that stream. Calls on one plan must be ordered on one stream.
+ * synchronise that stream. Calls on one plan must be ordered: on one stream,
+ * or across streams with events. Plans on separate workspaces share no device
+ * state, so their calls may run at the same time on different streams: a
+ * training loop can build the next batch's plan on a second stream, in a
+ * second workspace, while the current batch's forward and backward run
+ * (the caller orders every call that reads cores after the update that
+ * writes them, and each plan after the last call on its workspace).
  *
  * Errors: every call returns a tt_status. Arguments that can be checked on
  * the host (null pointers, non-positive or inconsistent dims, sizes beyond
@@ -214,7 +220,9 @@ tt_status tt_emb_plan_get_view(tt_emb_plan_t plan, tt_emb_plan_view* view);
 tt_status tt_emb_plan_counts(tt_emb_plan_t plan, int64_t* num_groups, int64_t* num_chunks,
                              void* stream);
 
-/* Frees the host handle (the workspace stays the caller's). NULL is a no-op. */
+/* Frees the host handle (the workspace stays the caller's). NULL is a no-op.
+ * Kernels of the plan that are already enqueued run to completion: they use
+ * their launch arguments and caller-owned buffers only, not the handle. */
 tt_status tt_emb_plan_destroy(tt_emb_plan_t plan);
 
 /* Allocation-free forward, for callers that cannot allocate device memory

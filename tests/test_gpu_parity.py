@@ -631,6 +631,61 @@ def test_backward_sgd_fused(case):
     assert ei.value.status == tte.TT_ERR_STALE
 
 
+def test_pipelined_steps_match_serial():
+    """Training steps on four different batches, run one after another on one
+    stream, and run as the benchmark runs them: each batch's plan built on a
+    second stream into the other of two workspaces while the previous batch
+    computes. The cores after the last step and its forward output agree bit
+    for bit (plans on separate workspaces share no device state)."""
+    import tensor_train_compressed_amd as tte
+    base = wl.make("train11m", batch=2048)
+    batches = [wl.make("train11m", seed=s, batch=2048) for s in (1, 2, 3, 4)]
+    tabs = tte.make_tables(base.tables, base.goff)
+    dev = "cuda:0"
+    ins = [(torch.from_numpy(b.indices).to(dev), torch.from_numpy(b.offsets).to(dev),
+            torch.from_numpy(b.grad_out).to(dev)) for b in batches]
+    nws = tte.tt_emb_workspace_bytes(tabs, max(b.L for b in batches), 2048, 256)
+    wss = [torch.empty(nws, dtype=torch.uint8, device=dev) for _ in range(2)]
+    out = torch.empty((2048, base.dim), dtype=torch.float32, device=dev)
+
+    def cores():
+        return [torch.from_numpy(x).to(dev) for x in (base.g1, base.g2, base.g3)]
+
+    g = cores()
+    for idx, off, gout in ins:
+        pl = tte.tt_emb_plan(tabs, idx, off, 2048, 256, workspace=wss[0])
+        tok = tte.tt_emb_forward_train(pl, *g, out)
+        tte.tt_emb_backward_sgd(pl, tok, *g, gout, base.lr)
+    torch.cuda.synchronize()
+    want = [x.cpu().numpy() for x in g] + [out.cpu().numpy()]
+
+    out.fill_(0)
+    g = cores()
+    sc, sp = torch.cuda.current_stream(), torch.cuda.Stream()
+    planned = [torch.cuda.Event(), torch.cuda.Event()]
+    used = [torch.cuda.Event(), torch.cuda.Event()]
+    plans = [None, None]
+    sp.wait_stream(sc)
+    plans[0] = tte.tt_emb_plan(tabs, ins[0][0], ins[0][1], 2048, 256, workspace=wss[0], stream=sp)
+    planned[0].record(sp)
+    for i in range(len(ins)):
+        c, n = i % 2, (i + 1) % 2
+        sc.wait_event(planned[c])
+        tok = tte.tt_emb_forward_train(plans[c], *g, out, stream=sc)
+        tte.tt_emb_backward_sgd(plans[c], tok, *g, ins[i][2], base.lr, stream=sc)
+        used[c].record(sc)
+        if i + 1 < len(ins):
+            if i >= 1:
+                sp.wait_event(used[n])
+            plans[n] = tte.tt_emb_plan(tabs, ins[i + 1][0], ins[i + 1][1], 2048, 256, workspace=wss[n], stream=sp)
+            planned[n].record(sp)
+    torch.cuda.synchronize()
+    assert tte.tt_emb_get_error(plans[(len(ins) - 1) % 2]) == 0
+    got = [x.cpu().numpy() for x in g] + [out.cpu().numpy()]
+    for k, name in enumerate(("G1", "G2", "G3", "last forward")):
+        np.testing.assert_array_equal(got[k], want[k], err_msg=name)
+
+
 # (n1, n2, n3, R, backward on the matrix cores too): every shape the
 # matrix-core kernels are built for, beyond the benchmark's (4, 8, 4, 32)
 MFMA_SHAPES = [(4, 4, 4, 32, True), (4, 4, 4, 16, True), (2, 8, 4, 32, True), (8, 4, 4, 32, True),
