@@ -528,14 +528,16 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
         const uint64_t m = __ballot(hr);
         const int32_t bagv = a.sorted_bag[valid ? sl : s0];
         const int32_t rrv = valid ? a.rid[sl] + (hr ? 1 : 0) - 1 : 0;
-        int32_t cur = 0;
+        int32_t cur = 0, cur_r = 0;
         bool cur_head = false;
         double sacc[DL];
 #pragma unroll
         for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
         // a piece that starts at a head and ends inside the window (or at its
-        // end, the next window starting a new run) is the whole run
-        auto flush = [&](bool ends_here) {
+        // end, the next window starting a new run) is the whole run; a run of
+        // one lookup is not stored (the run kernel reads its grad row)
+        auto flush = [&](bool ends_here, int r_end) {
+            if (cur_head && ends_here && r_end - cur_r == 1) return;
             if (cur_head && ends_here) {
                 float* dst = a.S + (int64_t)cur * D + lane * DL;
 #pragma unroll
@@ -559,8 +561,9 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
                 const int r = r0 + u;
                 if (r < n) {
                     if (r == 0 || ((m >> r) & 1ull)) {
-                        if (r != 0) flush(true);   // the previous piece ends at a row head
+                        if (r != 0) flush(true, r);   // the previous piece ends at a row head
                         cur = __builtin_amdgcn_readlane(rrv, r);
+                        cur_r = r;
                         cur_head = ((m >> r) & 1ull) != 0;
 #pragma unroll
                         for (int k = 0; k < DL; ++k) sacc[k] = 0.0;
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
                 }
             }
         }
-        flush(tail_whole);
+        flush(tail_whole, n);
     }
 }
 
@@ -637,6 +640,8 @@ struct RunsArgs {
     const int32_t* run_cslot;  // hot-row cache: each run's slot (-1: not hot); null without a cache
     float* hot;                // the hot rows' gradients dW [n_hot][D], or (fused SGD) W itself
     GradOut hgo;               // how a hot run's S goes into `hot`
+    const int32_t* run_bag1;   // per run: the bag of a run of one lookup, else -1
+    const float* gout;         // grad rows: S of a run of one lookup
 };
 
 // One wave per unit, the group's P in registers. Persistent waves claim their
@@ -710,17 +715,23 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         int32_t i3q;
         int32_t csq;           // hot-row slot of run t0 + q (-1: not hot)
     };
-    auto load_tile = [&](int32_t t0, int32_t s, int32_t e, int32_t i3w, int64_t o3, TileOps& o) {
+    // (b1w: lane j holds run s + j's bag when the run has one lookup, else -1:
+    // then the run's S is that grad row)
+    auto srow = [&](int32_t r, int32_t b1) {
+        return b1 >= 0 ? a.gout + (int64_t)b1 * D : a.S + (int64_t)r * D;
+    };
+    auto load_tile = [&](int32_t t0, int32_t s, int32_t e, int32_t i3w, int32_t b1w, int64_t o3, TileOps& o) {
         const int32_t rq = t0 + q < e ? t0 + q : t0;
         o.i3q = __shfl(i3w, rq - s);
         o.csq = a.run_cslot ? a.run_cslot[rq] : -1;
-        const float* Sq = a.S + (int64_t)rq * D;
+        const float* Sq = srow(rq, __shfl(b1w, rq - s));
         const float* G3q = a.g3 + o3 + (int64_t)o.i3q * CN;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o.av[mt] = *reinterpret_cast<const floatx4*>(Sq + (16 * mt + col) * N3);
 #pragma unroll
         for (int nt = 0; nt < RT; ++nt) o.bq[nt] = *reinterpret_cast<const floatx4*>(G3q + (16 * nt + col) * N3);
-        const float* Sl = a.S + (int64_t)min(t0 + lk, e - 1) * D + j3;
+        const int32_t rl = min(t0 + lk, e - 1);
+        const float* Sl = srow(rl, __shfl(b1w, rl - s)) + j3;
 #pragma unroll
         for (int s2 = 0; s2 < KSP; ++s2) o.bv[s2] = Sl[(4 * s2 + q) * N3];
     };
@@ -728,6 +739,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
     words_of(k, cur);
     int64_t o3 = o3_of(cur.g);
     int32_t i3l = a.run_i3[min(cur.s + lane, cur.e - 1)];   // lane j: i3 of run s + j
+    int32_t b1l = a.run_bag1[min(cur.s + lane, cur.e - 1)];  // lane j: bag of run s + j (one lookup)
     for (;;) {
         const int64_t kn = claim_unit(kn_raw);
         kn_raw = claim_issue();
@@ -743,12 +755,13 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int h = 0; h < KQ; ++h) preg[rt][h] = Pp[(rt * KQ + h) * 64];
-            load_tile(cur.s, cur.s, min(cur.e, cur.s + W), i3l, o3, TA);
+            load_tile(cur.s, cur.s, min(cur.e, cur.s + W), i3l, b1l, o3, TA);
         }
         Words nxt;
         words_of(min(kn, nunits - 1), nxt);
         const int64_t o3n = o3_of(nxt.g);
         const int32_t i3n = a.run_i3[min(nxt.s + lane, nxt.e - 1)];
+        const int32_t b1n = a.run_bag1[min(nxt.s + lane, nxt.e - 1)];
         if (work) {
         doublex4 dacc[MT][RT];
 #pragma unroll
@@ -796,10 +809,10 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
             }
         };
         for (int32_t t0 = s;; t0 += 8) {
-            load_tile(min(t0 + 4, e - 1), s, e, i3l, o3, TB);
+            load_tile(min(t0 + 4, e - 1), s, e, i3l, b1l, o3, TB);
             tile(t0, TA);
             if (t0 + 4 >= e) break;
-            load_tile(min(t0 + 8, e - 1), s, e, i3l, o3, TA);
+            load_tile(min(t0 + 8, e - 1), s, e, i3l, b1l, o3, TA);
             tile(t0 + 4, TB);
             if (t0 + 8 >= e) break;
         }
@@ -807,7 +820,8 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         if (s >= cur.e) break;
         // a whole group's next kRunRange runs
         i3l = a.run_i3[min(s + lane, cur.e - 1)];
-        load_tile(s, s, min(cur.e, s + W), i3l, o3, TA);
+        b1l = a.run_bag1[min(s + lane, cur.e - 1)];
+        load_tile(s, s, min(cur.e, s + W), i3l, b1l, o3, TA);
         }
         // the fp64 product's lane (col, q) holds dP[16mt + q + 4v][16nt + col];
         // a listed piece keeps its fp64 partial in its own slot
@@ -853,6 +867,7 @@ __device__ __forceinline__ void runs_body(const RunsArgs& a, Add3 add3) {
         }
         if (kn >= nunits) break;
         i3l = i3n;
+        b1l = b1n;
         o3 = o3n;
         cur = nxt;
         k = kn;
@@ -1255,7 +1270,8 @@ static tt_status launch_bwd_mfma(const tt_emb_plan_s* p, const float* g1, const 
                     p->at<int32_t>(p->lay.group_rbase), p->at<int32_t>(p->lay.group_key),
                     p->at<int32_t>(p->lay.run_i3), S, pbuf, g3, acc3, p->at<double>(p->lay.dpart),
                     p->at<int32_t>(p->lay.gdone), p->at<int32_t>(p->lay.claims),
-                    p->cached ? p->at<int32_t>(p->lay.run_cslot) : nullptr, hot, go};
+                    p->cached ? p->at<int32_t>(p->lay.run_cslot) : nullptr, hot, go,
+                    p->at<int32_t>(p->lay.run_bag1), gout};
         if (bucket3) {
             TT_LAUNCH(p, "k_bwd_runs_c3", s, (k_bwd_runs_c3<N1, N2, R, N3>), dim3(persistent_grid(3)), dim3(256), 0, s, ra, c3,
                                c3s);

@@ -74,6 +74,7 @@ Layout make_layout(int32_t T, int64_t L, int64_t B, int32_t chunk, int64_t K, in
     y.run_i3 = take(l4);
     y.run_of = take(l4);
     y.run_start = take(l4);
+    y.run_bag1 = take(sizeof(int32_t) * (size_t)LB);
     // pieces of the groups with more than kRunRange row runs: a group of n > W
     // runs has ceil(n / W) < 2n / W of them, so fewer than 2L / W in all; at
     // most kMaxXPieces are listed (the groups past that run whole)
@@ -1027,7 +1028,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                                                        int64_t K, int64_t NFB,
                                                        uint32_t* __restrict__ batch_tiles,
                                                        const int32_t* __restrict__ cslot,
-                                                       int32_t* __restrict__ run_cslot) {
+                                                       int32_t* __restrict__ run_cslot,
+                                                       const int32_t* __restrict__ sorted_bag,
+                                                       int32_t* __restrict__ run_bag1) {
     __shared__ uint32_t sh3[kMaxBuckets3];
     for (int i = threadIdx.x; i < n3cnt; i += kSortThreads) sh3[i] = 0u;   // ordered by the scan's barriers
     const int64_t tile = blockIdx.x;
@@ -1036,10 +1039,12 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
     tile_base<DIRECT, uint32_t>(run_tiles, tile, &sbase);
     // thread t takes positions 4t .. 4t+3 of the tile
     const int64_t s0 = tile * kSortTile + (int64_t)threadIdx.x * kSortItems;
-    int32_t ck[kSortItems + 1];
+    // ck[j + 1] = key at position s0 + j, ck[0] the one before, ck[kSortItems + 1]
+    // the one after (-1 outside [0, L))
+    int32_t ck[kSortItems + 2];
     ck[0] = s0 > 0 && s0 <= L ? skey[s0 - 1] : -1;
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) ck[j + 1] = s0 + j < L ? skey[s0 + j] : -1;
+    for (int j = 0; j <= kSortItems; ++j) ck[j + 1] = s0 + j < L ? skey[s0 + j] : -1;
     uint32_t hr[kSortItems], sum = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
@@ -1067,6 +1072,9 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
     }
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) csv[j] = cslot ? cslot[pl[j]] : -1;
+    int32_t sbg[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) sbg[j] = run_bag1 ? sorted_bag[min(s0 + j, L - 1)] : 0;
     uint32_t tot;
     uint32_t run = block_exclusive_scan<uint32_t>(sum, wsum, &tot) + sbase;   // synchronises
     uint32_t lrank[kSortItems];
@@ -1081,6 +1089,7 @@ __global__ __launch_bounds__(kSortThreads) void k_runs(const int32_t* __restrict
                 const int32_t r3 = ck[j + 1] - k * M3;
                 run_i3[rr] = r3;
                 run_start[rr] = (int32_t)s;
+                if (run_bag1) run_bag1[rr] = ck[j + 2] != ck[j + 1] ? sbg[j] : -1;   // one lookup: its bag
                 if (n3cnt) lrank[j] = atomicAdd(&sh3[bucket3(desc, T, CN, k, r3, tuk)], 1u);   // rank in the tile
             }
             int32_t ro = rr + (int32_t)hr[j] - 1;
@@ -1520,7 +1529,8 @@ tt_status tt::plan_into(tt_emb_plan_s* p, const tt_emb_table* tables, int32_t T,
                                p->at<int32_t>(lay.i3cnt), n3cnt, p->at<int32_t>(lay.run_rank),
                                p->at<int32_t>(lay.run_bkt), p->desc(), T, (int32_t)CN, K, lay.NFB,
                                p->at<uint32_t>(lay.batch_tiles), p->cached ? p->at<int32_t>(lay.cslot) : nullptr,
-                               p->cached ? p->at<int32_t>(lay.run_cslot) : nullptr);
+                               p->cached ? p->at<int32_t>(lay.run_cslot) : nullptr, p->at<int32_t>(lay.sorted_bag),
+                               p->fwd_only ? nullptr : p->at<int32_t>(lay.run_bag1));
             if (hipGetLastError() != hipSuccess) return TT_ERR_HIP;
         }
         if (lay.NFB > 0 && L > 0) {   // (no lookups: the list stays empty, its length 0 from k_init)

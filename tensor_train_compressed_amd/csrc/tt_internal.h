@@ -156,6 +156,8 @@ struct Layout {
     size_t run_i3;                           // [L] int32: i3 of each run
     size_t run_of;                           // [L] int32, input order: run id of each lookup
     size_t run_start;                        // [L] int32: first sorted position of each row run
+    size_t run_bag1;                         // [L] int32 (plans with the backward): the bag of a run
+                                             //     of one lookup (its S is that grad row), else -1
     size_t xpiece;                           // [xcap] int32 pairs: (group, piece) (backward)
     size_t dpart;                            // [xcap][n1*n2*R] double: dP of each listed piece
     size_t group_rbase;                      // [Gmax+1] int32: first row run of each group
