@@ -33,7 +33,9 @@ L * D adds; the per-lookup count of the plain method is reported beside it
 as context. `roofline` is k_fwd_batch (the forward's dominant kernel);
 `roofline_forward_call` adds pooling; `roofline_step` lists every kernel of
 the training step with its fp32 and fp64 FLOP (fractions of 157.3 and 78.6
-TFLOP/s) or its algorithmic bytes (fraction of 8 TB/s). HBM traffic comes
+TFLOP/s) or its algorithmic bytes (each datum counted once, a fraction of
+8 TB/s; the gather kernels also give their rate of per-lookup row reads,
+most of which hit L2 or the Infinity Cache). HBM traffic comes
 from rocprofv3 counter passes kept under profiles/ and is reported only while
 the kernel sources still match the hash recorded there.
 """
@@ -351,22 +353,30 @@ def main():
     tte.tt_emb_set_timing(pl, False)
 
     # executed work (distinct rows of a group are contracted once)
-    key_i3 = np.unique(p.indices)            # one table: a distinct index is a distinct (key, i3) row
+    key_i3, row_n = np.unique(p.indices, return_counts=True)   # one table: a distinct index is a row run
     U_row = int(key_i3.size)
+    U_one = int((row_n == 1).sum())         # runs of one lookup: no S row (their grad row serves)
     pre = U * 2 * n1 * n2 * R * R            # prefix products, per call
     suf = U_row * 2 * n1 * n2 * n3 * R       # one suffix-sized product per distinct row
     core_elems = p.g1.size + p.g2.size + p.g3.size
-    # kernel -> (fp32 FLOP, fp64 FLOP, algorithmic bytes) per launch
+    # kernel -> (fp32 FLOP, fp64 FLOP, algorithmic HBM bytes) per launch; the
+    # bytes count each datum once (a gathered row that many lookups share is
+    # read from HBM once at best; its other reads hit L2 or the Infinity
+    # Cache), and `gathered` below gives the per-lookup row reads
     work = {
         "k_fwd_batch": (pre + suf, 0, 0), "k_fwd_batch_keep": (pre + suf, 0, 0),
-        "k_pool": (L * D, 0, 4 * L * D + 4 * B * D),
-        "k_bwd_sum": (0, L * D, 4 * L * D + 4 * U_row * D),
+        # stage rows of the distinct rows, run ids, offsets in; pooled rows out
+        "k_pool": (L * D, 0, 4 * U_row * D + 4 * L + 8 * (B + 1) + 4 * B * D),
+        # grad rows, sorted bags / run ids / keys in; S rows of the runs of
+        # more than one lookup out
+        "k_bwd_sum": (0, L * D, 4 * B * D + 12 * L + 4 * (U_row - U_one) * D),
         "k_bwd_runs_c3": (suf, suf, 0),
         # dG3 (c3 row sums), dG1 and dG2 in one launch
         "k_bwd_dg123": (0, 2 * pre + U_row * R * n3, 0),
         "k_sgd": (2 * core_elems, 0, 12 * core_elems),
     }
     PEAK_FP64_TFLOPS = 78.6
+    gathered = {"k_pool": 4 * L * D, "k_bwd_sum": 4 * L * D}
 
     def kernel_roofline(name, rec):
         f32, f64, by = work.get(name, (0, 0, 0))
@@ -386,6 +396,9 @@ def main():
             out_["bound"] = "hbm"
             out_["gbs"] = round(by / sec / 1e9, 1)
             out_["frac"] = round(by / sec / 1e9 / PEAK_HBM_GBS, 4)
+        if name in gathered:
+            # one D-row read per lookup, most from L2 / the Infinity Cache
+            out_["gathered_row_gbs"] = round(gathered[name] / sec / 1e9, 1)
         return out_
 
     kb = fwd_kernels["k_fwd_batch"]["us"] * 1e-6
