@@ -68,17 +68,18 @@ def parse():
     ap.add_argument("--phase-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB (reference for HBM counters)")
-    ap.add_argument("--forward-workload", default=None, choices=["multi26"],
+    ap.add_argument("--forward-workload", default=None, choices=["tiny", "table1m", "skew11m", "multi26"],
                     help="instead of the training step: plan and forward of this workload only "
                          "(one JSON line with its forward rooflines)")
     return ap.parse_args()
 
 
 def forward_only(args):
-    """Plan and forward of the 26-table batch (26 tables of 10^3 to 4*10^7
-    rows, dim 64 = 4x4x4, rank 32, 32,768 bags per table, 8.5 M lookups):
-    per-call times and the forward kernels' rooflines, as for the main
-    workload."""
+    """Plan and forward of one workload (tiny: 1,000 rows, rank 4; table1m:
+    1M rows, rank 16, 4,096 bags; skew11m: the training workload's table and
+    batch; multi26: 26 tables of 10^3 to 4*10^7 rows, dim 64 = 4x4x4, rank
+    32, 32,768 bags per table, 8.5 M lookups): per-call times and the forward
+    kernels' rooflines, as for the main workload."""
     import numpy as np
     import torch
 
@@ -142,7 +143,10 @@ def forward_only(args):
     U_row = int(np.unique(tab * (1 << 40) + p.indices).size)
     pre = U * 2 * n1 * n2 * R * R
     suf = U_row * 2 * n1 * n2 * n3 * R
-    kb, kp = us.get("k_fwd_batch", 0.0) * 1e-6, us.get("k_pool", 0.0) * 1e-6
+    # the matrix-core kernels, or the generic one (which pools as it goes)
+    kname = "k_fwd_batch" if "k_fwd_batch" in us else "k_fwd_generic"
+    kb, kp = us.get(kname, 0.0) * 1e-6, us.get("k_pool", 0.0) * 1e-6
+    fwd_bytes = 8 * L + 8 * (T * B + 1) + 4 * (p.g1.size + p.g2.size + p.g3.size) + 4 * T * B * D
     res = {
         "metric": f"pooled bags/s, TT-EmbeddingBag forward of the {args.forward_workload} batch",
         "value": round(T * B / (fwd_ms * 1e-3), 1), "unit": "bags/s", "n_gpus": 1, "higher_is_better": True,
@@ -152,12 +156,19 @@ def forward_only(args):
         "paths": {"forward": q["forward_path"], "workspace_bytes": q["workspace_bytes"]},
         "phases_ms_per_call": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4)},
         "kernels_us": {k: round(v, 2) for k, v in sorted(us.items(), key=lambda x: -x[1])},
-        "roofline": {"kernel": "k_fwd_batch", "bound": "mfma", "achieved": round((pre + suf) / kb / 1e12, 3),
+        "roofline": {"kernel": kname, "bound": "mfma" if kname == "k_fwd_batch" else "alu",
+                     "achieved": round((pre + suf) / kb / 1e12, 3),
                      "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round((pre + suf) / kb / 1e12 / PEAK_FP32_TFLOPS, 4), "flop_per_launch": int(pre + suf)},
-        "roofline_forward_call": {"kernels": "k_fwd_batch + k_pool", "us": round((kb + kp) * 1e6, 2),
+        "roofline_forward_call": {"kernels": f"{kname} + k_pool" if kp > 0 else kname, "us": round((kb + kp) * 1e6, 2),
                                   "flop": int(pre + suf + L * D),
-                                  "frac": round((pre + suf + L * D) / (kb + kp) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+                                  "frac": round((pre + suf + L * D) / (kb + kp) / 1e12 / PEAK_FP32_TFLOPS, 4)
+                                  if kb + kp > 0 else None},
+        "plan_forward_bags_per_s": round(T * B / ((plan_ms + fwd_ms) * 1e-3), 1),
+        "forward_rows_per_s": round(L / (fwd_ms * 1e-3), 1),
+        # indices, offsets, cores once, pooled rows out
+        "forward_algorithmic_bytes": int(fwd_bytes),
+        "forward_hbm_gbs_algorithmic": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
     }
     print(json.dumps(res))
 
