@@ -548,11 +548,19 @@ __global__ __launch_bounds__(256) void k_bwd_sum(SumArgs a, PrepArgs pa) {
                 for (int k = 0; k < DL; ++k) dst[k] = sacc[k];
             }
         };
+        // the runs of one lookup (heads followed by a head or the window's
+        // whole end): their sums are not kept, so their row loads read the
+        // window's first row again (an L1 hit) instead of a grad row
+        const uint64_t nexth = (m >> 1) | (tail_whole ? (1ull << (n - 1)) : 0ull);
+        const uint64_t one = m & nexth;
+        const int32_t bag0 = __builtin_amdgcn_readfirstlane(bagv);
         for (int r0 = 0; r0 < n; r0 += FL) {
             float v[FL][DL];
 #pragma unroll
             for (int u = 0; u < FL; ++u) {
-                const float* row = a.gout + (int64_t)__builtin_amdgcn_readlane(bagv, min(r0 + u, 63)) * D + lane * DL;
+                const int r = min(r0 + u, 63);
+                const int32_t bg = ((one >> r) & 1ull) ? bag0 : __builtin_amdgcn_readlane(bagv, r);
+                const float* row = a.gout + (int64_t)bg * D + lane * DL;
 #pragma unroll
                 for (int k = 0; k < DL; ++k) v[u][k] = row[k];
             }
