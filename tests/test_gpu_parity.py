@@ -579,11 +579,13 @@ def test_kernel_timing():
     assert_close(out.cpu().numpy(), oracle.forward_problem(dp.p), "forward with timing toggled")
 
 
-@pytest.mark.parametrize("case", ["single", "multi6", "shared_g3", "no_lookups", "recompute"])
+@pytest.mark.parametrize("case", ["single", "multi6", "shared_g3", "no_lookups", "recompute", "gap_g2"])
 def test_backward_sgd_fused(case):
     """tt_emb_backward_sgd against tt_emb_backward + tt_emb_sgd on the same
     inputs: the updated cores bit for bit (untouched slices unchanged), and
-    against the oracle's step; with a kept token and (recompute) without."""
+    against the oracle's step; with a kept token and (recompute) without;
+    gap_g2: the second table's G2 slices start 1,000 floats past the first's
+    end (the gap belongs to no table and must keep its values)."""
     import tensor_train_compressed_amd as tte
     if case == "single":
         p = wl.make("train11m", batch=256)
@@ -593,6 +595,17 @@ def test_backward_sgd_fused(case):
         p = wl.make("multi26", batch=32, tables=6)
         p.grad_out = np.random.default_rng(1).standard_normal((p.T * p.batch, p.dim)).astype(np.float32)
         p.lr = 0.01
+    elif case == "gap_g2":
+        t1 = wl.Table(20 * 30 * 40, (20, 30, 40), (4, 8, 4), 32)
+        t2 = wl.Table(25 * 12 * 40, (25, 12, 40), (4, 8, 4), 32)
+        p = wl.make_custom([t1, t2], np.full(2 * 64, 9), seed=11, zipf_alpha=1.1, with_grad=True)
+        gap, e1 = 1000, int(p.goff[1, 1])
+        g2 = np.random.default_rng(5).standard_normal(p.g2.size + gap).astype(np.float32)
+        g2[:e1] = p.g2[:e1]
+        g2[e1 + gap:] = p.g2[e1:]
+        p.g2 = g2
+        p.goff = p.goff.copy()
+        p.goff[1, 1] += gap
     else:
         t1 = wl.Table(4 * 5 * 300, (4, 5, 300), (4, 8, 4), 32)
         t2 = wl.Table(3 * 6 * 300, (3, 6, 300), (4, 8, 4), 32)
@@ -603,6 +616,8 @@ def test_backward_sgd_fused(case):
         p.goff[1, 2] = 0
     dp = DevProblem(p, 32)
     dp.make_plan()
+    if case == "gap_g2":   # the matrix-core backward, with its dG2 buffer over a gapped G2
+        assert tte.tt_emb_query_paths(dp.plan, dp.g1, dp.g2)["backward_path"] == 1
     out = torch.empty((dp.TB, dp.D), dtype=torch.float32, device="cuda:0")
     g = [x.clone() for x in (dp.g1, dp.g2, dp.g3)]
     d = [torch.empty_like(x) for x in g]
