@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--phase-reps", type=int, default=50)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB (reference for HBM counters)")
+    ap.add_argument("--hot-rows", type=int, default=0,
+                    help="instead of the main line: the training step with a hot-row cache of the batch's "
+                         "N most frequent rows, beside the same step without it (one JSON line)")
     ap.add_argument("--forward-workload", default=None, choices=["tiny", "table1m", "skew11m", "multi26"],
                     help="instead of the training step: plan and forward of this workload only "
                          "(one JSON line with its forward rooflines)")
@@ -173,6 +176,76 @@ def forward_only(args):
     print(json.dumps(res))
 
 
+def hot_rows_step(args):
+    """The training step (plan, training forward, backward fused with SGD)
+    on the main workload with a hot-row cache of the batch's N most frequent
+    rows (uncompressed, trainable, started at their TT values), against the
+    same step without the cache, both one step after another on one
+    stream."""
+    import numpy as np
+    import torch
+
+    import tensor_train_compressed_amd as tte
+    import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    p = wl.make("train11m")
+    B, L, D = p.batch, p.L, p.tables[0].dim
+    tabs = tte.make_tables(p.tables, p.goff)
+    g = [torch.from_numpy(x).to(dev) for x in (p.g1, p.g2, p.g3)]
+    idx = torch.from_numpy(p.indices).to(dev)
+    off = torch.from_numpy(p.offsets).to(dev)
+    gout = torch.from_numpy(p.grad_out).to(dev)
+    out = torch.empty((B, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    rows, cnt = np.unique(p.indices, return_counts=True)
+    top = rows[np.argsort(-cnt, kind="stable")[:args.hot_rows]]
+    n_hot = int(top.size)
+    served = float(cnt[np.argsort(-cnt, kind="stable")[:args.hot_rows]].sum()) / L
+    cache = tte.HotCache(torch.zeros(n_hot, dtype=torch.int32, device=dev), torch.from_numpy(top).to(dev))
+    # W starts at the rows' TT values: a plain forward of one-lookup bags
+    hot_w = torch.empty((n_hot, D), dtype=torch.float32, device=dev)
+    tp = tte.tt_emb_plan(tabs, torch.from_numpy(top).to(dev),
+                         torch.arange(n_hot + 1, dtype=torch.int64, device=dev), n_hot, args.chunk)
+    tte.tt_emb_forward(tp, g[0], g[1], g[2], hot_w)
+    ws = torch.empty(tte.tt_emb_workspace_bytes(tabs, L, B, args.chunk), dtype=torch.uint8, device=dev)
+
+    def step_cached():
+        pl = tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream, cache=cache)
+        tok = tte.tt_emb_forward_cached(pl, g[0], g[1], g[2], hot_w, out, keep=True, stream=stream)
+        tte.tt_emb_backward_sgd_cached(pl, tok, g[0], g[1], g[2], hot_w, gout, p.lr, stream=stream)
+        return pl
+
+    def step_plain():
+        pl = tte.tt_emb_plan(tabs, idx, off, B, args.chunk, workspace=ws, stream=stream)
+        tok = tte.tt_emb_forward_train(pl, g[0], g[1], g[2], out, stream=stream)
+        tte.tt_emb_backward_sgd(pl, tok, g[0], g[1], g[2], gout, p.lr, stream=stream)
+        return pl
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            pl = fn()
+        torch.cuda.synchronize()
+        assert tte.tt_emb_get_error(pl) == 0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / args.steps
+
+    ms_cached = timed(step_cached)
+    ms_plain = timed(step_plain)
+    print(json.dumps({
+        "metric": f"pooled bags/s, TT-EmbeddingBag training step at batch {B} with a hot-row cache",
+        "value": round(B / (ms_cached * 1e-3), 1), "unit": "bags/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic (seeded Zipf/Poisson indices, Gaussian cores)",
+        "config": {"workload": "skew11m-train, one step after another on one stream", "hot_rows": n_hot,
+                   "lookups_served_by_cache": round(served, 4)},
+        "ms_per_step_cached": round(ms_cached, 4), "ms_per_step_uncached": round(ms_plain, 4),
+    }))
+
+
 def kernel_source_hash() -> str:
     """sha256 prefix over every kernel source file (sorted by name)."""
     h = hashlib.sha256()
@@ -203,6 +276,9 @@ def main():
         sys.exit(2)
     if args.forward_workload:
         forward_only(args)
+        return
+    if args.hot_rows > 0:
+        hot_rows_step(args)
         return
 
     import numpy as np
@@ -322,6 +398,9 @@ def main():
         return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
 
     bwd_ms = bwd_after_fwd_train_ms(reps)
+    # the backward that forms P again (no kept products): the checkpoint's worth
+    bwd_recompute_ms = per_call_ms(lambda: tte.tt_emb_backward(pl, g[0], g[1], g[2], gout, dg[0], dg[1], dg[2],
+                                                               stream=stream), reps)
     sgd_ms = per_call_ms(lambda: tte.tt_emb_sgd(pl, g[0], g[1], g[2], dg[0], dg[1], dg[2], p.lr,
                                                 stream=stream), reps)
 
@@ -481,6 +560,7 @@ def main():
         "phases_ms_per_call": {"plan": round(plan_ms, 4), "forward": round(fwd_ms, 4),
                                "forward_train": round(fwd_train_ms, 4),
                                "backward_after_forward_train": round(bwd_ms, 4),
+                               "backward_forming_p_again": round(bwd_recompute_ms, 4),
                                "sgd": round(sgd_ms, 4),
                                "backward_sgd_after_forward_train": round(bwd_sgd, 4)},
         "forward_bags_per_s": round(B / (fwd_ms * 1e-3), 1),
